@@ -1,0 +1,22 @@
+"""f64 CPU oracle for paged, folded causal attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it; the attention library never does.  It shares no code
+with the GPU path.
+"""
+
+from .oracle import (  # noqa: F401
+    HostView,
+    attend,
+    build,
+    dequant_f32,
+    int4_codes,
+    logical_kv,
+    merge_splits,
+    reference,
+    regen_values,
+    row_info,
+    splitmix64,
+    widen,
+    widen_bits,
+)

@@ -1,0 +1,312 @@
+"""Python side of the f64 CPU oracle.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the attention library.  It shares
+no code with the GPU path: it has its own widening of stored values, its own
+int8/int4 decoding, its own page-table walk and its own SplitMix64 (in
+attention.c).
+
+Definitions followed:
+  * attention: RustAttention README, "Mathematical Framework Covered"
+    (softmax(QK^T / sqrt(d_k) + Mask) V), causal mask and max subtraction from
+    its "Architectural Features Included" list;
+  * causal alignment of a chunk of new queries: the n_q new rows are the last
+    n_q positions of the context, so row t of a sequence with context c sees
+    keys 0 .. c - n_q + t (the chunk's own earlier tokens included);
+  * paging: logical token j of sequence s lives in block table[s][j // P], row
+    j % P (CFR-Atlas README, PageKey + token_range per page);
+  * cold tiers: ARGUS "Visual Architecture" (INT8; INT4 2-way bit-packed),
+    symmetric: value = code * scale, one scale per (page, kv head) for K and
+    one for V; int4 element 2i in the low nibble, two's complement;
+  * regenerated pages: the value definition in attention.c;
+  * split merge: log-sum-exp combination of normalised partial results
+    (attnres AGENTS.md, "online softmax merge").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attention.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+TIER_SHIFT = 30
+SLOT_MASK = (1 << TIER_SHIFT) - 1
+
+
+def build(force: bool = False) -> str:
+    """Compile attention.c with gcc (-O2, OpenMP) into liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+            "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, dbl, p = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        L.oracle_attend.argtypes = [i64, i64, i64, p, p, p, p, dbl, p, p]
+        L.oracle_attend.restype = None
+        L.oracle_attend_folded.argtypes = [i64, i64, i64, p, p, p, p, dbl, i64, p, p]
+        L.oracle_attend_folded.restype = None
+        L.oracle_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.oracle_splitmix64.restype = ctypes.c_uint64
+        L.oracle_regen_values.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_uint64, i64, i64, i64, i64, p]
+        L.oracle_regen_values.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------------------
+# Core definitions
+# ---------------------------------------------------------------------------
+
+def attend(q, k, v, visible, scale, page_tokens=None):
+    """Exact causal attention of rows `q` [n][d] over one head's keys.
+
+    k, v: [n_keys][d]; visible[r] = number of leading keys row r may see.
+    Returns (out [n][d] f64, lse [n] f64, natural log).  With `page_tokens`
+    the folded (page-by-page online softmax) variant is used instead.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    vis = np.ascontiguousarray(visible, dtype=np.int64)
+    n, d = q.shape
+    n_keys = k.shape[0]
+    assert k.shape == (n_keys, d) and v.shape == (n_keys, d) and vis.shape == (n,)
+    out = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    if page_tokens is None:
+        lib().oracle_attend(n, d, n_keys, _ptr(q), _ptr(k), _ptr(v), _ptr(vis),
+                            float(scale), _ptr(out), _ptr(lse))
+    else:
+        lib().oracle_attend_folded(n, d, n_keys, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(vis), float(scale), int(page_tokens),
+                                   _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def merge_splits(part_out, part_lse):
+    """Log-sum-exp merge of normalised partials.
+
+    part_out [splits][rows][d], part_lse [splits][rows] (natural log; -inf for
+    an empty split).  lse = log sum_s exp(lse_s); out = sum_s exp(lse_s - lse)
+    o_s.  All-empty rows give out 0 and lse -inf.
+    """
+    po = np.asarray(part_out, dtype=np.float64)
+    pl = np.asarray(part_lse, dtype=np.float64)
+    m = pl.max(axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(pl), np.exp(pl - m_safe[None, :]), 0.0)
+    z = w.sum(axis=0)
+    out = np.where(finite[:, None],
+                   (w[:, :, None] * po).sum(axis=0) / np.where(z > 0, z, 1.0)[:, None],
+                   0.0)
+    lse = np.where(finite, m_safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    return out, lse
+
+
+def splitmix64(seed: int, n: int) -> int:
+    """n-th output (n >= 1) of SplitMix64 seeded with `seed`."""
+    return int(lib().oracle_splitmix64(seed & (2**64 - 1), n))
+
+
+def regen_values(seed, layer, kv_head, token0, n_tokens, d, kv) -> np.ndarray:
+    """Regenerated K (kv=0) or V (kv=1) rows [n_tokens][d] as f32 (bf16-exact)."""
+    dst = np.empty((int(n_tokens), int(d)), dtype=np.float32)
+    if n_tokens:
+        lib().oracle_regen_values(int(seed), int(layer), int(kv_head), int(token0),
+                                  int(n_tokens), int(d), int(kv), _ptr(dst))
+    return dst
+
+
+# ---------------------------------------------------------------------------
+# Stored values -> exact f64 (or f32 for the bit-exact decode checks)
+# ---------------------------------------------------------------------------
+
+def _np(t):
+    """torch tensor (any device) -> numpy array of the same bits."""
+    import torch
+    t = t.detach()
+    if t.device.type != "cpu":
+        t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16), "bf16"
+    if t.dtype == torch.float16:
+        return t.numpy(), "f16"
+    if t.dtype == torch.float32:
+        return t.numpy(), "f32"
+    return t.numpy(), str(t.dtype)
+
+
+def widen_bits(a: np.ndarray, kind: str) -> np.ndarray:
+    """Exact f64 value of stored f32 / bf16 (raw uint16 bits) / f16 numbers."""
+    if kind == "bf16":
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def widen(t) -> np.ndarray:
+    a, kind = _np(t)
+    return widen_bits(a, kind)
+
+
+def int4_codes(packed: np.ndarray) -> np.ndarray:
+    """Unpack two's-complement nibbles: byte i holds element 2i (low nibble)
+    and element 2i+1 (high nibble)."""
+    b = packed.astype(np.int16)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.int16)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def dequant_f32(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """f32(code * scale) with one scale per leading index pair [n][Hkv]."""
+    return (codes.astype(np.float32) * scale.astype(np.float32)[:, :, None, None]
+            ).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Paged problems (synth.Paged) -> logical per-sequence K/V and references
+# ---------------------------------------------------------------------------
+
+class HostView:
+    """Host copies of a problem's stored arrays, made once."""
+
+    def __init__(self, w):
+        self.w = w
+        self.k = None
+        self.v = None
+        self.tiers = None
+
+    def pools(self):
+        if self.k is None:
+            self.k = _np(self.w.k_pool)
+            self.v = _np(self.w.v_pool)
+        return self.k, self.v
+
+    def tier_arrays(self):
+        if self.tiers is None and self.w.tiers is not None:
+            self.tiers = {}
+            for key, val in self.w.tiers.items():
+                if key == "counts":
+                    continue
+                self.tiers[key] = _np(val)[0]
+        return self.tiers
+
+
+def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
+    """Logical K, V of sequence s, kv head g: ([n][d] f64, [n][d] f64).
+
+    Walks the page table page by page; each page comes from its storage tier
+    or from the resident pool.  In a regenerated problem every K/V value is
+    defined by the regenerator (its resident pages hold the same values by
+    construction), so all pages are taken from the regenerator."""
+    host = host or HostView(w)
+    P, D = w.page_tokens, w.head_dim
+    ctx = int(w.context_lens[s]) if n_tokens is None else int(n_tokens)
+    K = np.zeros((ctx, D), dtype=np.float64)
+    V = np.zeros((ctx, D), dtype=np.float64)
+    n_regen = -(-ctx // P) if w.regen is not None else 0
+    for p in range(-(-ctx // P)):
+        t0, t1 = p * P, min(ctx, (p + 1) * P)
+        rows = t1 - t0
+        if p < n_regen:
+            rs = w.regen
+            K[t0:t1] = regen_values(rs["seed"], rs["layer"], g, t0, rows, D, 0)
+            V[t0:t1] = regen_values(rs["seed"], rs["layer"], g, t0, rows, D, 1)
+            continue
+        entry = int(w.page_table[s, p]) & 0xFFFFFFFF
+        if w.tiers is None:
+            (ka, kind), (va, _) = host.pools()
+            K[t0:t1] = widen_bits(ka[entry, g, :rows], kind)
+            V[t0:t1] = widen_bits(va[entry, g, :rows], kind)
+            continue
+        tier, slot = entry >> TIER_SHIFT, entry & SLOT_MASK
+        if tier == 0:
+            (ka, kind), (va, _) = host.pools()
+            K[t0:t1] = widen_bits(ka[slot, g, :rows], kind)
+            V[t0:t1] = widen_bits(va[slot, g, :rows], kind)
+            continue
+        ta = host.tier_arrays()
+        key = "i8" if tier == 1 else "i4"
+        for dst, kv in ((K, "k"), (V, "v")):
+            codes = ta[f"{key}_{kv}"][slot, g, :rows]
+            if key == "i4":
+                codes = int4_codes(codes)
+            sc = np.float64(ta[f"{key}_{kv}_scale"][slot, g])
+            dst[t0:t1] = codes.astype(np.float64) * sc
+    return K, V
+
+
+def row_info(w):
+    """For each query row: (sequence, visible key count)."""
+    qs = w.query_start
+    seqs = np.zeros(w.total_q, dtype=np.int64)
+    vis = np.zeros(w.total_q, dtype=np.int64)
+    for s in range(w.num_seqs):
+        n_q = int(w.query_lens[s])
+        ctx = int(w.context_lens[s])
+        for t in range(n_q):
+            seqs[qs[s] + t] = s
+            vis[qs[s] + t] = max(0, ctx - n_q + t + 1)
+    return seqs, vis
+
+
+def reference(w, rows=None, heads=None, host=None, page_tokens=None):
+    """Oracle out / lse for the chosen query rows and heads.
+
+    Returns (out [len(rows)][len(heads)][d] f64, lse [len(rows)][len(heads)]).
+    rows defaults to every query row, heads to every head.  GQA/MQA: query
+    head h reads kv head h // (num_heads // num_kv_heads).
+    """
+    host = host or HostView(w)
+    rows = np.arange(w.total_q) if rows is None else np.asarray(rows)
+    heads = np.arange(w.num_heads) if heads is None else np.asarray(heads)
+    G = w.num_heads // w.num_kv_heads
+    seqs, vis = row_info(w)
+    qh = widen(w.q)  # [total_q][H][D]
+    out = np.zeros((rows.size, heads.size, w.head_dim))
+    lse = np.zeros((rows.size, heads.size))
+    for s in sorted(set(int(seqs[r]) for r in rows)):
+        sel = [i for i, r in enumerate(rows) if seqs[r] == s]
+        n_keys = int(max(vis[rows[i]] for i in sel))
+        for g in sorted(set(int(h) // G for h in heads)):
+            K, V = logical_kv(w, s, g, n_tokens=n_keys, host=host)
+            hsel = [j for j, h in enumerate(heads) if int(h) // G == g]
+            qq = np.stack([qh[rows[i], heads[j]] for i in sel for j in hsel])
+            vv = np.array([vis[rows[i]] for i in sel for j in hsel])
+            o, l = attend(qq, K, V, vv, w.scale, page_tokens=page_tokens)
+            k = 0
+            for i in sel:
+                for j in hsel:
+                    out[i, j] = o[k]
+                    lse[i, j] = l[k]
+                    k += 1
+    return out, lse
