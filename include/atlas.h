@@ -1,0 +1,269 @@
+/*
+ * atlas.h - C ABI of the paged, folded attention library (libatlas.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact causal scaled-dot-product attention
+ *     out = softmax(scale * q K^T + causal mask) V,   lse = log sum exp(scale * q K^T)
+ * (RustAttention README, "Mathematical Framework Covered") over a paged K/V
+ * cache, folding the keys page by page with an online softmax (CFR-Atlas
+ * README, overview: "exact folded online-softmax attention"; ARGUS,
+ * "Latency & Throughput Impact": page-by-page online softmax without a
+ * concatenated K/V tensor).  Long contexts are split over pages across
+ * workgroups and the partial results merged by log-sum-exp (cortiq README,
+ * "split-K flash-decoding"; attnres AGENTS.md, "online softmax merge").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers unless a field says "host".
+ *    Every layout is dense row-major with the shape given; the caller owns
+ *    all memory.  The library never allocates device memory; temporary
+ *    storage comes from the caller's `workspace`.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Buffers must stay valid until the stream's work completes.
+ *  - Every argument check runs on the host before anything is launched, so a
+ *    call that returns an error has written nothing (CFR-Atlas README, test
+ *    list: rejection of invalid configs and ranges, transactional behaviour).
+ *    Launch failures return ATLAS_EDEVICE; faults surface at the caller's
+ *    next synchronisation.
+ *  - Device-side guards: a page-table entry that names a block outside the
+ *    pool, or a context length outside [0, max_pages_per_seq * page_tokens]
+ *    or above max_context_len, never causes an out-of-bounds read; the rows
+ *    it affects are written as NaN (out and lse), so such inputs fail loudly
+ *    rather than silently (attnres AGENTS.md, "Non-Negotiable Invariants").
+ *  - The library is stateless and thread-safe.  Results are bitwise
+ *    deterministic run to run; split boundaries are fixed in tokens, so the
+ *    page size and the physical placement of pages do not change the result
+ *    bits.
+ */
+#ifndef ATLAS_H
+#define ATLAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATLAS_ABI_VERSION 1u
+
+typedef int32_t atlas_status;
+#define ATLAS_OK 0           /* success (work enqueued) */
+#define ATLAS_EINVAL 1       /* invalid argument: null pointer, bad size, ... */
+#define ATLAS_EUNSUPPORTED 2 /* valid but not implemented: head_dim, dtype, ... */
+#define ATLAS_EWORKSPACE 3   /* workspace missing or smaller than required */
+#define ATLAS_EDEVICE 4      /* the HIP runtime reported an error */
+
+/* Element types of q and of resident K/V pages. */
+#define ATLAS_F32 0
+#define ATLAS_BF16 1
+#define ATLAS_F16 2
+
+/* Tiered page-table entries (atlas_paged_attention_tiered): the top two bits
+ * hold the tier, the low 30 bits the slot in that tier's pool. */
+#define ATLAS_TIER_SHIFT 30
+#define ATLAS_TIER_HOT 0  /* f16 / bf16 page in the hot pool (args k_pool/v_pool) */
+#define ATLAS_TIER_INT8 1 /* int8 codes, one f32 scale per (page, kv head) */
+#define ATLAS_TIER_INT4 2 /* int4 codes, two per byte, same scale layout */
+
+/*
+ * One attention call (decode or chunked prefill).  CFR-Atlas README,
+ * "Config::builder(page_tokens, head_dim)" and "AttentionRequest::new(layer,
+ * head, query, context_tokens)" name the same quantities for one head.
+ *
+ * Query rows.  With query_start == NULL every sequence has exactly one query
+ * row (decode) and total_q == num_seqs.  Otherwise sequence s owns rows
+ * query_start[s] .. query_start[s+1]-1 (chunked prefill), which are the last
+ * n_q = query_start[s+1]-query_start[s] positions of its context: row t of
+ * the chunk sees keys 0 .. context_lens[s] - n_q + t.  A decode row sees all
+ * context_lens[s] keys, its own included.
+ *
+ * Heads.  Query head h reads kv head h / (num_heads / num_kv_heads): MHA when
+ * the counts are equal, MQA when num_kv_heads == 1, GQA otherwise (CFR-Atlas
+ * README, module list: "MHA/MQA/GQA head mapping").
+ *
+ * Paging.  Logical token j of sequence s is row j % page_tokens of block
+ * page_table[s * max_pages_per_seq + j / page_tokens] (CFR-Atlas README,
+ * PageKey and token_range of a regenerated page).
+ */
+typedef struct atlas_attn_args {
+    uint32_t struct_size;       /* = sizeof(atlas_attn_args); ABI guard */
+    int32_t q_dtype;            /* ATLAS_F32 / ATLAS_BF16 / ATLAS_F16 */
+    int32_t kv_dtype;           /* element type of k_pool / v_pool */
+    int32_t num_seqs;           /* >= 1 */
+    int32_t num_heads;          /* query heads, multiple of num_kv_heads */
+    int32_t num_kv_heads;       /* >= 1 */
+    int32_t head_dim;           /* 64 or 128 */
+    int32_t page_tokens;        /* tokens per page, multiple of 16 */
+    int32_t max_pages_per_seq;  /* row length of page_table */
+    int32_t num_blocks;         /* blocks in k_pool / v_pool */
+    int32_t max_context_len;    /* host: >= every context_lens[s] */
+    int32_t max_query_len;      /* host: >= every chunk length (1 for decode) */
+    int32_t total_q;            /* query rows (== num_seqs for decode) */
+    int32_t split_tokens;       /* keys per split-K work item (multiple of 64);
+                                   0 = the library chooses from the shape */
+    float scale;                /* softmax scale, finite (e.g. 1/sqrt(head_dim)) */
+    const void *q;              /* [total_q][num_heads][head_dim], q_dtype */
+    const void *k_pool;         /* [num_blocks][num_kv_heads][page_tokens][head_dim] */
+    const void *v_pool;         /* same shape and type as k_pool */
+    const int32_t *page_table;  /* [num_seqs][max_pages_per_seq] block ids */
+    const int32_t *context_lens;/* [num_seqs] keys per sequence, >= 0 */
+    const int32_t *query_start; /* [num_seqs + 1] prefix sums, or NULL (decode) */
+    float *out;                 /* [total_q][num_heads][head_dim] f32 */
+    float *lse;                 /* [total_q][num_heads] f32, natural log;
+                                   -inf (and out = 0) for a row with no keys */
+    void *workspace;            /* device scratch, >= atlas_workspace_size() */
+    size_t workspace_bytes;
+    void *stream;               /* hipStream_t, NULL = default stream */
+} atlas_attn_args;
+
+/*
+ * Cold-tier pools of atlas_paged_attention_tiered (ARGUS, "Visual
+ * Architecture": FP16 hot pool, INT8, INT4 "2-way Bit-Packed"; pages are
+ * reconstructed in registers just before the dot products, ARGUS "Why It
+ * Works: Storage vs. Computation").  Value = code * scale, symmetric, one f32
+ * scale per (page, kv head), separately for K and V.  int4 byte i of a row
+ * holds element 2i in its low nibble and element 2i+1 in its high nibble,
+ * two's complement.  A pool with zero slots may pass NULL pointers.
+ */
+typedef struct atlas_tier_pools {
+    uint32_t struct_size;       /* = sizeof(atlas_tier_pools) */
+    int32_t num_int8;           /* slots in the int8 pool */
+    int32_t num_int4;           /* slots in the int4 pool */
+    int32_t reserved;
+    const int8_t *int8_k;       /* [num_int8][num_kv_heads][page_tokens][head_dim] */
+    const int8_t *int8_v;
+    const float *int8_k_scale;  /* [num_int8][num_kv_heads] */
+    const float *int8_v_scale;
+    const uint8_t *int4_k;      /* [num_int4][num_kv_heads][page_tokens][head_dim/2] */
+    const uint8_t *int4_v;
+    const float *int4_k_scale;  /* [num_int4][num_kv_heads] */
+    const float *int4_v_scale;
+} atlas_tier_pools;
+
+/*
+ * Regenerated pages (CFR-Atlas README: cold pages are "regenerated
+ * deterministically into scratch buffers" and the fold stays exact when the
+ * regenerator reproduces the stored rows).  Logical pages
+ * 0 .. regen_pages[s]-1 of sequence s are not read from the pool (their
+ * page-table entries are ignored); their K/V values are
+ *     c  = layer<<48 | kv_head<<40 | token<<9 | dim<<1 | kv   (kv: 0 = K, 1 = V)
+ *     z  = mix64(seed + (c + 1) * 0x9E3779B97F4A7C15)   (SplitMix64 output c+1)
+ *     x  = (z >> 40) * 2^-23 - 1                         (uniform on [-1, 1))
+ *     value = bf16(x), round to nearest even.
+ * Bounds: layer < 2^16, kv_head < 2^8, token < 2^31, dim < 2^8.  Requires
+ * kv_dtype == ATLAS_BF16.  Resident pages must hold the same values for the
+ * result to equal full-KV attention (atlas_regenerate_pages writes them).
+ */
+typedef struct atlas_regen_spec {
+    uint32_t struct_size;       /* = sizeof(atlas_regen_spec) */
+    uint32_t layer;
+    uint64_t seed;
+    const int32_t *regen_pages; /* [num_seqs] regenerated leading pages */
+    int32_t max_regen_pages;    /* host: >= every regen_pages[s] */
+    int32_t reserved;
+} atlas_regen_spec;
+
+/* ABI version of the loaded library (ATLAS_ABI_VERSION it was built with). */
+uint32_t atlas_abi_version(void);
+
+/* Static description of a status code. */
+const char *atlas_status_string(atlas_status status);
+
+/* Human-readable reason of the last error returned on this host thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char *atlas_last_error(void);
+
+/*
+ * Workspace bytes needed by atlas_paged_attention (regen == NULL) or
+ * atlas_paged_attention_regen (regen != NULL) for these arguments.  Reads host
+ * fields only.  The workspace holds the split-K partials (one f32 vector of
+ * head_dim plus one lse per (row, head, split)) and, for chunked prefill with
+ * regenerated pages, one bf16 copy of every regenerated page (each regenerated
+ * value is computed once per call and shared by every query tile).
+ */
+atlas_status atlas_workspace_size(const atlas_attn_args *args,
+                                  const atlas_regen_spec *regen,
+                                  size_t *bytes);
+
+/*
+ * Paged causal attention: decode (query_start == NULL) or chunked prefill.
+ * kv_dtype F32, BF16 or F16; q_dtype F32 with F32 K/V, otherwise BF16 or F16.
+ * head_dim 64 or 128; num_heads / num_kv_heads in {1, 2, 4, 8}.  Decode rows
+ * (and every row of f32 problems) use the vector-ALU kernel with split-K over
+ * pages and a log-sum-exp merge; chunked prefill over BF16/F16 K/V with
+ * head_dim 128 runs QK^T and PV on matrix cores (MFMA).
+ */
+atlas_status atlas_paged_attention(const atlas_attn_args *args);
+
+/*
+ * Decode over tiered pages: page_table entries are (tier << 30) | slot.  Hot
+ * pages come from args->k_pool / v_pool (kv_dtype F16 or BF16, num_blocks
+ * slots); int8 and int4 pages from `pools`.  Decode only (query_start must be
+ * NULL).  Codes are decoded in registers and the per-page scales are applied
+ * to the dot products and to the probabilities, never written back.
+ */
+atlas_status atlas_paged_attention_tiered(const atlas_attn_args *args,
+                                          const atlas_tier_pools *pools);
+
+/*
+ * Attention with regenerated leading pages (see atlas_regen_spec).  Decode
+ * rows regenerate each value inside the attention kernel, where it is used
+ * once.  Chunked prefill first regenerates every value of the regenerated
+ * pages once into the workspace and then runs the matrix-core kernel over
+ * resident and regenerated pages alike.
+ */
+atlas_status atlas_paged_attention_regen(const atlas_attn_args *args,
+                                         const atlas_regen_spec *regen);
+
+/*
+ * Log-sum-exp merge of split-K partials (attnres AGENTS.md, "online softmax
+ * merge"):  lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * o_s.
+ *   part_out [splits][rows][head_dim] f32: normalised partial outputs
+ *   part_lse [splits][rows] f32, natural log; -inf marks an empty split
+ *   out [rows][head_dim] f32, lse [rows] f32
+ * A row whose splits are all empty gets out = 0 and lse = -inf.  Splits are
+ * combined in index order (deterministic).  head_dim <= 256, splits >= 1.
+ */
+atlas_status atlas_fold_partials(const float *part_out, const float *part_lse,
+                                 int32_t splits, int32_t rows, int32_t head_dim,
+                                 float *out, float *lse, void *stream);
+
+/*
+ * Inspection entry points.  Each copies or decodes stored values without
+ * attention arithmetic so that the page walk and the encodings can be checked
+ * bit for bit against an independent implementation.
+ */
+
+/* Gather tokens 0 .. num_tokens-1 of sequence `seq` through the page table
+ * into contiguous [num_tokens][num_kv_heads][head_dim] arrays of kv_dtype
+ * (plain pools; tiered tables are rejected).  num_tokens <= max_pages_per_seq
+ * * page_tokens. */
+atlas_status atlas_gather_pages(const atlas_attn_args *args, int32_t seq,
+                                int32_t num_tokens, void *k_out, void *v_out);
+
+/* Write the regenerated K/V values of logical pages logical_pages[i] into
+ * pool blocks dst_blocks[i] (i < n), pools of shape [*][num_kv_heads]
+ * [page_tokens][head_dim] and type kv_dtype (BF16 or F32; the values are
+ * bf16-exact either way).  Both index arrays are device int32. */
+atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t page_tokens, int32_t kv_dtype,
+                                    const int32_t *logical_pages,
+                                    const int32_t *dst_blocks, int32_t n,
+                                    int32_t num_blocks, void *k_pool,
+                                    void *v_pool, void *stream);
+
+/* Decode tier-tagged pages entries[i] (i < n, device int32, (tier << 30) |
+ * slot) to f32 K/V [n][num_kv_heads][page_tokens][head_dim]: hot pages are
+ * widened exactly, int8 / int4 pages give f32(code * scale). */
+atlas_status atlas_dequant_pages(const atlas_attn_args *args,
+                                 const atlas_tier_pools *pools,
+                                 const int32_t *entries, int32_t n,
+                                 float *k_out, float *v_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATLAS_H */

@@ -1,0 +1,460 @@
+// C ABI of libatlas.so: host-side argument checks, split planning, workspace
+// layout and kernel dispatch.  No device memory is read or allocated here;
+// every check runs before the first launch, so an error leaves all outputs
+// untouched (CFR-Atlas README, test list: rejection of invalid configs and
+// ranges, transactional behaviour).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "atlas.h"
+#include "internal.h"
+
+using namespace atlas;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+atlas_status fail(atlas_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+atlas_status ok() {
+    g_last_error.clear();
+    return ATLAS_OK;
+}
+
+atlas_status device_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(ATLAS_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Everything a call needs that follows from the host-side arguments.
+struct Plan {
+    int group = 1;
+    int split_tokens = 0;
+    int max_splits = 1;
+    bool direct = true;      // one split per row: the decode kernel writes out/lse
+    bool mfma = false;       // chunked prefill on matrix cores
+    size_t part_o_bytes = 0;
+    size_t part_lse_bytes = 0;
+    size_t regen_bytes = 0;  // one K and one V copy of the regenerated pages
+    size_t total = 0;
+};
+
+int env_split_tokens() {
+    const char *s = std::getenv("ATLAS_SPLIT_TOKENS");
+    if (!s || !*s) return 0;
+    return std::atoi(s);
+}
+
+// Tokens per split-K work item.  Fixed in tokens (never derived from the page
+// size or placement) so the arithmetic order, hence the result bits, depend
+// only on the logical problem.  The largest power of two in [256, 2048] that
+// still yields about 16 workgroups per compute unit for the largest context.
+int choose_split_tokens(const atlas_attn_args *a) {
+    int t = a->split_tokens > 0 ? a->split_tokens : env_split_tokens();
+    if (t > 0) return t;
+    const int64_t rows = (int64_t)a->total_q * a->num_kv_heads;
+    const int64_t want = 4096;
+    for (int cand = 2048; cand >= 256; cand >>= 1) {
+        const int64_t items = rows * ((a->max_context_len + cand - 1) / cand);
+        if (items >= want) return cand;
+    }
+    return 256;
+}
+
+bool dtype_ok(int32_t d) { return d == ATLAS_F32 || d == ATLAS_BF16 || d == ATLAS_F16; }
+
+atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_regen_spec *rg,
+                          Plan *plan) {
+    if (!a) return fail(ATLAS_EINVAL, "args is NULL");
+    if (a->struct_size != sizeof(atlas_attn_args))
+        return fail(ATLAS_EINVAL, "args->struct_size %u != %zu", a->struct_size,
+                    sizeof(atlas_attn_args));
+    if (!dtype_ok(a->q_dtype) || !dtype_ok(a->kv_dtype))
+        return fail(ATLAS_EINVAL, "unknown dtype (q %d, kv %d)", a->q_dtype, a->kv_dtype);
+    if (a->num_seqs < 1) return fail(ATLAS_EINVAL, "num_seqs %d < 1", a->num_seqs);
+    if (a->num_heads < 1 || a->num_kv_heads < 1)
+        return fail(ATLAS_EINVAL, "num_heads %d / num_kv_heads %d must be >= 1", a->num_heads,
+                    a->num_kv_heads);
+    if (a->num_heads % a->num_kv_heads)
+        return fail(ATLAS_EINVAL, "num_heads %d is not a multiple of num_kv_heads %d",
+                    a->num_heads, a->num_kv_heads);
+    const int group = a->num_heads / a->num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(ATLAS_EUNSUPPORTED, "heads per kv head %d not in {1, 2, 4, 8}", group);
+    if (a->head_dim < 1) return fail(ATLAS_EINVAL, "head_dim %d < 1", a->head_dim);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(ATLAS_EUNSUPPORTED, "head_dim %d not in {64, 128}", a->head_dim);
+    if (a->page_tokens < 1) return fail(ATLAS_EINVAL, "page_tokens %d < 1", a->page_tokens);
+    if (a->page_tokens % 16)
+        return fail(ATLAS_EUNSUPPORTED, "page_tokens %d is not a multiple of 16", a->page_tokens);
+    if (a->max_pages_per_seq < 1)
+        return fail(ATLAS_EINVAL, "max_pages_per_seq %d < 1", a->max_pages_per_seq);
+    if (a->num_blocks < (tiered ? 0 : 1))
+        return fail(ATLAS_EINVAL, "num_blocks %d out of range", a->num_blocks);
+    const int64_t max_keys = (int64_t)a->max_pages_per_seq * a->page_tokens;
+    if (max_keys > INT32_MAX)
+        return fail(ATLAS_EINVAL, "max_pages_per_seq * page_tokens overflows int32");
+    if (a->max_context_len < 0 || a->max_context_len > max_keys)
+        return fail(ATLAS_EINVAL, "max_context_len %d outside [0, %lld]", a->max_context_len,
+                    (long long)max_keys);
+    if (a->query_start == nullptr) {
+        if (a->total_q != a->num_seqs)
+            return fail(ATLAS_EINVAL, "decode needs total_q (%d) == num_seqs (%d)", a->total_q,
+                        a->num_seqs);
+    } else {
+        if (a->total_q < 1) return fail(ATLAS_EINVAL, "total_q %d < 1", a->total_q);
+        if (a->max_query_len < 1 || a->max_query_len > a->total_q ||
+            a->max_query_len > a->max_context_len)
+            return fail(ATLAS_EINVAL, "max_query_len %d outside [1, min(total_q, max_context_len)]",
+                        a->max_query_len);
+    }
+    if (!std::isfinite(a->scale)) return fail(ATLAS_EINVAL, "scale is not finite");
+    if (a->split_tokens < 0 || (a->split_tokens > 0 && a->split_tokens % 64))
+        return fail(ATLAS_EINVAL, "split_tokens %d must be 0 or a positive multiple of 64",
+                    a->split_tokens);
+    if (!a->q || !a->page_table || !a->context_lens || !a->out || !a->lse)
+        return fail(ATLAS_EINVAL, "NULL q, page_table, context_lens, out or lse");
+    if (!tiered && (!a->k_pool || !a->v_pool))
+        return fail(ATLAS_EINVAL, "NULL k_pool or v_pool");
+    if (tiered && a->num_blocks > 0 && (!a->k_pool || !a->v_pool))
+        return fail(ATLAS_EINVAL, "NULL hot k_pool or v_pool with num_blocks > 0");
+    if ((int64_t)a->total_q * a->num_heads * a->head_dim > ((int64_t)1 << 40))
+        return fail(ATLAS_EINVAL, "output too large");
+
+    plan->group = group;
+    const bool prefill = a->query_start != nullptr;
+    const bool sixteen = a->kv_dtype == ATLAS_BF16 || a->kv_dtype == ATLAS_F16;
+    plan->mfma = prefill && !tiered && sixteen && a->q_dtype == a->kv_dtype &&
+                 a->head_dim == 128 && std::getenv("ATLAS_NO_MFMA") == nullptr && false;
+
+    if (!plan->mfma) {
+        int st = choose_split_tokens(a);
+        if (st < 64 || st % 64)
+            return fail(ATLAS_EINVAL, "split tokens %d must be a positive multiple of 64", st);
+        plan->split_tokens = st;
+        plan->max_splits = a->max_context_len > 0 ? (a->max_context_len + st - 1) / st : 1;
+        if (plan->max_splits < 1) plan->max_splits = 1;
+        plan->direct = plan->max_splits == 1;
+        const int64_t blocks = (int64_t)a->total_q * a->num_kv_heads * plan->max_splits;
+        if (blocks > INT32_MAX)
+            return fail(ATLAS_EUNSUPPORTED, "too many split-K work items (%lld)",
+                        (long long)blocks);
+        if (!plan->direct) {
+            const int64_t parts = (int64_t)a->total_q * a->num_heads * plan->max_splits;
+            plan->part_o_bytes = align_up((size_t)parts * a->head_dim * sizeof(float));
+            plan->part_lse_bytes = align_up((size_t)parts * sizeof(float));
+        }
+    }
+
+    if (rg) {
+        if (rg->struct_size != sizeof(atlas_regen_spec))
+            return fail(ATLAS_EINVAL, "regen->struct_size %u != %zu", rg->struct_size,
+                        sizeof(atlas_regen_spec));
+        if (a->kv_dtype != ATLAS_BF16)
+            return fail(ATLAS_EUNSUPPORTED, "regenerated pages need kv_dtype BF16");
+        if (rg->layer >= (1u << 16)) return fail(ATLAS_EINVAL, "layer %u >= 2^16", rg->layer);
+        if (a->num_kv_heads > 256) return fail(ATLAS_EINVAL, "num_kv_heads > 256 with regen");
+        if (!rg->regen_pages) return fail(ATLAS_EINVAL, "NULL regen_pages");
+        if (rg->max_regen_pages < 0 || rg->max_regen_pages > a->max_pages_per_seq)
+            return fail(ATLAS_EINVAL, "max_regen_pages %d outside [0, max_pages_per_seq]",
+                        rg->max_regen_pages);
+        if (plan->mfma) {
+            plan->regen_bytes = align_up((size_t)a->num_seqs * rg->max_regen_pages *
+                                         a->num_kv_heads * a->page_tokens * a->head_dim * 2);
+        }
+    }
+    plan->total = plan->part_o_bytes + plan->part_lse_bytes + 2 * plan->regen_bytes;
+    return ok();
+}
+
+atlas_status check_workspace(const atlas_attn_args *a, const Plan &plan) {
+    if (plan.total == 0) return ok();
+    if (!a->workspace) return fail(ATLAS_EWORKSPACE, "workspace is NULL, %zu bytes needed",
+                                   plan.total);
+    if (a->workspace_bytes < plan.total)
+        return fail(ATLAS_EWORKSPACE, "workspace %zu bytes < %zu needed", a->workspace_bytes,
+                    plan.total);
+    if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign)
+        return fail(ATLAS_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+    return ok();
+}
+
+RowMap row_map(const atlas_attn_args *a) {
+    RowMap m;
+    m.context_lens = a->context_lens;
+    m.query_start = a->query_start;
+    m.num_seqs = a->num_seqs;
+    m.max_context_len = a->max_context_len;
+    m.max_keys = a->max_pages_per_seq * a->page_tokens;
+    return m;
+}
+
+DecodeParams decode_params(const atlas_attn_args *a, const Plan &plan) {
+    DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.rows = row_map(a);
+    p.q = a->q;
+    p.q_dtype = a->q_dtype;
+    p.k_pool = a->k_pool;
+    p.v_pool = a->v_pool;
+    p.page_table = a->page_table;
+    p.num_heads = a->num_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.page_tokens = a->page_tokens;
+    p.max_pages = a->max_pages_per_seq;
+    p.num_blocks = a->num_blocks;
+    p.total_q = a->total_q;
+    p.split_tokens = plan.split_tokens;
+    p.max_splits = plan.max_splits;
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    char *ws = reinterpret_cast<char *>(a->workspace);
+    p.part_o = plan.direct ? nullptr : reinterpret_cast<float *>(ws);
+    p.part_lse = plan.direct ? nullptr : reinterpret_cast<float *>(ws + plan.part_o_bytes);
+    p.out = a->out;
+    p.lse = a->lse;
+    p.direct = plan.direct ? 1 : 0;
+    return p;
+}
+
+atlas_status run_decode(const atlas_attn_args *a, const Plan &plan, DecodeParams &p, int mode) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
+    hipError_t e = launch_decode(p, a->kv_dtype, a->head_dim, plan.group, mode, stream);
+    if (e != hipSuccess) return device_status(e, "decode launch");
+    if (!plan.direct) {
+        FoldParams f;
+        std::memset(&f, 0, sizeof(f));
+        f.part_o = p.part_o;
+        f.part_lse = p.part_lse;
+        f.out = a->out;
+        f.lse = a->lse;
+        f.o_row_stride = (int64_t)plan.max_splits * a->head_dim;
+        f.o_split_stride = a->head_dim;
+        f.l_row_stride = plan.max_splits;
+        f.l_split_stride = 1;
+        f.rows = a->total_q * a->num_heads;
+        f.head_dim = a->head_dim;
+        f.fixed_splits = 0;
+        f.map = p.rows;
+        f.num_heads = a->num_heads;
+        f.split_tokens = plan.split_tokens;
+        e = launch_fold(f, stream);
+        if (e != hipSuccess) return device_status(e, "fold launch");
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t atlas_abi_version(void) { return ATLAS_ABI_VERSION; }
+
+const char *atlas_status_string(atlas_status s) {
+    switch (s) {
+        case ATLAS_OK: return "ok";
+        case ATLAS_EINVAL: return "invalid argument";
+        case ATLAS_EUNSUPPORTED: return "unsupported configuration";
+        case ATLAS_EWORKSPACE: return "workspace missing or too small";
+        case ATLAS_EDEVICE: return "device error";
+        default: return "unknown status";
+    }
+}
+
+const char *atlas_last_error(void) { return g_last_error.c_str(); }
+
+atlas_status atlas_workspace_size(const atlas_attn_args *args, const atlas_regen_spec *regen,
+                                  size_t *bytes) {
+    if (!bytes) return fail(ATLAS_EINVAL, "bytes is NULL");
+    Plan plan;
+    atlas_status st = check_common(args, false, regen, &plan);
+    if (st != ATLAS_OK) return st;
+    *bytes = plan.total;
+    return ok();
+}
+
+atlas_status atlas_paged_attention(const atlas_attn_args *args) {
+    Plan plan;
+    atlas_status st = check_common(args, false, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if ((st = check_workspace(args, plan)) != ATLAS_OK) return st;
+    DecodeParams p = decode_params(args, plan);
+    return run_decode(args, plan, p, MODE_PLAIN);
+}
+
+atlas_status atlas_paged_attention_tiered(const atlas_attn_args *args,
+                                          const atlas_tier_pools *pools) {
+    Plan plan;
+    atlas_status st = check_common(args, true, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if (!pools) return fail(ATLAS_EINVAL, "pools is NULL");
+    if (pools->struct_size != sizeof(atlas_tier_pools))
+        return fail(ATLAS_EINVAL, "pools->struct_size %u != %zu", pools->struct_size,
+                    sizeof(atlas_tier_pools));
+    if (args->query_start != nullptr)
+        return fail(ATLAS_EUNSUPPORTED, "tiered pages support decode only (query_start NULL)");
+    if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
+        return fail(ATLAS_EUNSUPPORTED, "tiered hot pages must be F16 or BF16");
+    if (pools->num_int8 < 0 || pools->num_int4 < 0)
+        return fail(ATLAS_EINVAL, "negative tier pool size");
+    if (pools->num_int8 > 0 && (!pools->int8_k || !pools->int8_v || !pools->int8_k_scale ||
+                                !pools->int8_v_scale))
+        return fail(ATLAS_EINVAL, "NULL int8 pool pointer");
+    if (pools->num_int4 > 0 && (!pools->int4_k || !pools->int4_v || !pools->int4_k_scale ||
+                                !pools->int4_v_scale))
+        return fail(ATLAS_EINVAL, "NULL int4 pool pointer");
+    if ((st = check_workspace(args, plan)) != ATLAS_OK) return st;
+    DecodeParams p = decode_params(args, plan);
+    p.i8_k = pools->int8_k;
+    p.i8_v = pools->int8_v;
+    p.i8_ks = pools->int8_k_scale;
+    p.i8_vs = pools->int8_v_scale;
+    p.i4_k = pools->int4_k;
+    p.i4_v = pools->int4_v;
+    p.i4_ks = pools->int4_k_scale;
+    p.i4_vs = pools->int4_v_scale;
+    p.n_i8 = pools->num_int8;
+    p.n_i4 = pools->num_int4;
+    return run_decode(args, plan, p, MODE_TIERED);
+}
+
+atlas_status atlas_paged_attention_regen(const atlas_attn_args *args,
+                                         const atlas_regen_spec *regen) {
+    if (!regen) return fail(ATLAS_EINVAL, "regen is NULL");
+    Plan plan;
+    atlas_status st = check_common(args, false, regen, &plan);
+    if (st != ATLAS_OK) return st;
+    if ((st = check_workspace(args, plan)) != ATLAS_OK) return st;
+    DecodeParams p = decode_params(args, plan);
+    p.seed = regen->seed;
+    p.layer = regen->layer;
+    p.regen_pages = regen->regen_pages;
+    return run_decode(args, plan, p, MODE_REGEN);
+}
+
+atlas_status atlas_fold_partials(const float *part_out, const float *part_lse, int32_t splits,
+                                 int32_t rows, int32_t head_dim, float *out, float *lse,
+                                 void *stream) {
+    if (!part_out || !part_lse || !out || !lse)
+        return fail(ATLAS_EINVAL, "NULL pointer argument");
+    if (splits < 1) return fail(ATLAS_EINVAL, "splits %d < 1", splits);
+    if (rows < 0) return fail(ATLAS_EINVAL, "rows %d < 0", rows);
+    if (head_dim < 1 || head_dim > 256)
+        return fail(ATLAS_EUNSUPPORTED, "head_dim %d outside [1, 256]", head_dim);
+    FoldParams f;
+    std::memset(&f, 0, sizeof(f));
+    f.part_o = part_out;
+    f.part_lse = part_lse;
+    f.out = out;
+    f.lse = lse;
+    f.o_row_stride = head_dim;
+    f.o_split_stride = (int64_t)rows * head_dim;
+    f.l_row_stride = 1;
+    f.l_split_stride = rows;
+    f.rows = rows;
+    f.head_dim = head_dim;
+    f.fixed_splits = splits;
+    f.num_heads = 1;
+    f.split_tokens = 1;
+    return device_status(launch_fold(f, reinterpret_cast<hipStream_t>(stream)), "fold launch");
+}
+
+atlas_status atlas_gather_pages(const atlas_attn_args *args, int32_t seq, int32_t num_tokens,
+                                void *k_out, void *v_out) {
+    Plan plan;
+    atlas_status st = check_common(args, false, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if (seq < 0 || seq >= args->num_seqs)
+        return fail(ATLAS_EINVAL, "seq %d outside [0, %d)", seq, args->num_seqs);
+    if (num_tokens < 0 || (int64_t)num_tokens > (int64_t)args->max_pages_per_seq * args->page_tokens)
+        return fail(ATLAS_EINVAL, "num_tokens %d outside [0, max_pages * page_tokens]",
+                    num_tokens);
+    if (!k_out || !v_out) return fail(ATLAS_EINVAL, "NULL output");
+    const int eb = args->kv_dtype == ATLAS_F32 ? 4 : 2;
+    return device_status(
+        launch_gather(args->k_pool, args->v_pool,
+                      args->page_table + (int64_t)seq * args->max_pages_per_seq,
+                      args->num_kv_heads, args->head_dim, args->page_tokens, args->num_blocks, eb,
+                      num_tokens, k_out, v_out, reinterpret_cast<hipStream_t>(args->stream)),
+        "gather launch");
+}
+
+atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t page_tokens, int32_t kv_dtype,
+                                    const int32_t *logical_pages, const int32_t *dst_blocks,
+                                    int32_t n, int32_t num_blocks, void *k_pool, void *v_pool,
+                                    void *stream) {
+    if (layer >= (1u << 16)) return fail(ATLAS_EINVAL, "layer %u >= 2^16", layer);
+    if (num_kv_heads < 1 || num_kv_heads > 256)
+        return fail(ATLAS_EINVAL, "num_kv_heads %d outside [1, 256]", num_kv_heads);
+    if (head_dim < 2 || head_dim > 256 || head_dim % 2)
+        return fail(ATLAS_EINVAL, "head_dim %d must be even and in [2, 256]", head_dim);
+    if (page_tokens < 1) return fail(ATLAS_EINVAL, "page_tokens %d < 1", page_tokens);
+    if (kv_dtype != ATLAS_BF16 && kv_dtype != ATLAS_F32)
+        return fail(ATLAS_EUNSUPPORTED, "regenerated pages are written as BF16 or F32");
+    if (n < 0 || num_blocks < 0) return fail(ATLAS_EINVAL, "negative n or num_blocks");
+    if (n > 0 && (!logical_pages || !dst_blocks || !k_pool || !v_pool))
+        return fail(ATLAS_EINVAL, "NULL pointer argument");
+    RegenFillParams r;
+    std::memset(&r, 0, sizeof(r));
+    r.seed = seed;
+    r.layer = layer;
+    r.num_kv_heads = num_kv_heads;
+    r.head_dim = head_dim;
+    r.page_tokens = page_tokens;
+    r.logical_pages = logical_pages;
+    r.dst_blocks = dst_blocks;
+    r.n = n;
+    r.num_blocks = num_blocks;
+    r.kv_f32 = kv_dtype == ATLAS_F32;
+    r.k_dst = k_pool;
+    r.v_dst = v_pool;
+    return device_status(launch_regen_fill(r, reinterpret_cast<hipStream_t>(stream)),
+                         "regenerate launch");
+}
+
+atlas_status atlas_dequant_pages(const atlas_attn_args *args, const atlas_tier_pools *pools,
+                                 const int32_t *entries, int32_t n, float *k_out, float *v_out) {
+    Plan plan;
+    atlas_status st = check_common(args, true, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if (!pools || pools->struct_size != sizeof(atlas_tier_pools))
+        return fail(ATLAS_EINVAL, "pools NULL or wrong struct_size");
+    if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
+        return fail(ATLAS_EUNSUPPORTED, "tiered hot pages must be F16 or BF16");
+    if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
+    if (n > 0 && (!entries || !k_out || !v_out)) return fail(ATLAS_EINVAL, "NULL pointer");
+    DecodeParams p = decode_params(args, plan);
+    p.i8_k = pools->int8_k;
+    p.i8_v = pools->int8_v;
+    p.i8_ks = pools->int8_k_scale;
+    p.i8_vs = pools->int8_v_scale;
+    p.i4_k = pools->int4_k;
+    p.i4_v = pools->int4_v;
+    p.i4_ks = pools->int4_k_scale;
+    p.i4_vs = pools->int4_v_scale;
+    p.n_i8 = pools->num_int8;
+    p.n_i4 = pools->num_int4;
+    return device_status(launch_dequant(p, args->kv_dtype, args->head_dim, entries, n, k_out,
+                                        v_out, reinterpret_cast<hipStream_t>(args->stream)),
+                         "dequant launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Device helpers for gfx950 kernels: storage-type widening, 16-lane DPP
+// reductions, the page regenerator's value function and the row map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace atlas {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Widening of stored 16-bit values packed two to a 32-bit word.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Element i of a row slice held as 32-bit words, for each storage type.
+template <int KV>
+__device__ __forceinline__ float widen_word(const uint32_t *w, int i) {
+    if constexpr (KV == KV_F32) {
+        return __uint_as_float(w[i]);
+    } else if constexpr (KV == KV_BF16) {
+        return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+    } else {
+        return (i & 1) ? f16_hi(w[i >> 1]) : f16_lo(w[i >> 1]);
+    }
+}
+
+__device__ __forceinline__ float load_elem(const void *base, int64_t idx, int dtype) {
+    if (dtype == KV_F32) return reinterpret_cast<const float *>(base)[idx];
+    uint16_t b = reinterpret_cast<const uint16_t *>(base)[idx];
+    if (dtype == KV_BF16) return __uint_as_float(((uint32_t)b) << 16);
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Sign-extended bit field: the `bits`-wide field that ends at bit 31 after a
+// left shift by `sh` (shift done unsigned, then an arithmetic right shift).
+__device__ __forceinline__ int32_t sext_field(uint32_t w, int sh, int bits) {
+    return ((int32_t)(w << sh)) >> (32 - bits);
+}
+
+// ---------------------------------------------------------------------------
+// Vector loads of NB bytes (NB in {2, 4, 8, 16, 32}) into 32-bit words.
+// ---------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ void load_words(uint32_t *dst, const void *src) {
+    if constexpr (NB == 32) {
+        const uint4 *s = reinterpret_cast<const uint4 *>(src);
+        uint4 a = s[0], b = s[1];
+        dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+        dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+    } else if constexpr (NB == 16) {
+        uint4 a = *reinterpret_cast<const uint4 *>(src);
+        dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+    } else if constexpr (NB == 8) {
+        uint2 a = *reinterpret_cast<const uint2 *>(src);
+        dst[0] = a.x; dst[1] = a.y;
+    } else if constexpr (NB == 4) {
+        dst[0] = *reinterpret_cast<const uint32_t *>(src);
+    } else {
+        static_assert(NB == 2, "unsupported load width");
+        dst[0] = *reinterpret_cast<const uint16_t *>(src);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums within a row of 16 lanes (DPP row_ror).  Rotations by 8, 4,
+// 2 and 1 leave the full row sum in every lane, and every lane adds the same
+// pairs in the same tree, so all 16 lanes hold bit-identical sums.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0x128>(x);  // row_ror:8
+    x += dpp_f<0x124>(x);  // row_ror:4
+    x += dpp_f<0x122>(x);  // row_ror:2
+    x += dpp_f<0x121>(x);  // row_ror:1
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Page regenerator (counter-based SplitMix64, Steele-Lea-Flood 2014).
+// Counter c = layer<<48 | kv_head<<40 | token<<9 | dim<<1 | kv addresses
+// output c+1 of the stream seeded with `seed`; the value is bf16(2u - 1) with
+// u = top 24 bits / 2^24.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t regen_counter(uint32_t layer, int kv_head, int token,
+                                                  int dim, int kv) {
+    return ((uint64_t)layer << 48) | ((uint64_t)(uint32_t)kv_head << 40) |
+           ((uint64_t)(uint32_t)token << 9) | ((uint64_t)(uint32_t)dim << 1) | (uint64_t)kv;
+}
+
+__device__ __forceinline__ uint32_t regen_bf16_bits(uint64_t seed, uint64_t ctr) {
+    uint64_t z = seed + (ctr + 1ull) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    const int32_t u = (int32_t)(uint32_t)(z >> 40) - (1 << 23);
+    const float x = (float)u * (1.0f / 8388608.0f);   // exact: |u| < 2^24
+    uint32_t b = __float_as_uint(x);
+    b += 0x7FFFu + ((b >> 16) & 1u);                   // round to nearest even
+    return b >> 16;
+}
+
+__device__ __forceinline__ float regen_value(uint64_t seed, uint64_t ctr) {
+    return __uint_as_float(regen_bf16_bits(seed, ctr) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Row map: sequence of a query row and the number of keys it sees.  Returns
+// false when the sequence's context length is outside what the page table
+// and the host bound allow (the caller then writes NaN for the row).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool map_row(const RowMap &m, int row, int &seq, int &visible) {
+    int n_q = 1, t = 0;
+    if (m.query_start == nullptr) {
+        seq = row;
+    } else {
+        int lo = 0, hi = m.num_seqs - 1;   // last s with query_start[s] <= row
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (m.query_start[mid] <= row) lo = mid; else hi = mid - 1;
+        }
+        seq = lo;
+        const int q0 = m.query_start[seq];
+        n_q = m.query_start[seq + 1] - q0;
+        t = row - q0;
+    }
+    const int ctx = m.context_lens[seq];
+    // A chunk's rows are the last n_q tokens of the context, so a chunk longer
+    // than its context is malformed; a decode row may see zero keys.
+    const bool ok = ctx >= 0 && ctx <= m.max_context_len && ctx <= m.max_keys &&
+                    n_q >= 1 && t < n_q && (m.query_start == nullptr || n_q <= ctx);
+    visible = ok ? ctx - n_q + t + 1 : 0;
+    if (visible < 0) visible = 0;
+    return ok;
+}
+
+__device__ __forceinline__ int splits_of(int visible, int split_tokens) {
+    const int n = (visible + split_tokens - 1) / split_tokens;
+    return n < 1 ? 1 : n;
+}
+
+}  // namespace atlas

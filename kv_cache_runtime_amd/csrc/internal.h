@@ -1,0 +1,115 @@
+// Internal launch parameters shared by the host dispatcher (api.hip) and the
+// kernels.  Plain structs of pointers and sizes, passed by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace atlas {
+
+enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_F16 = 2 };
+enum Mode : int { MODE_PLAIN = 0, MODE_TIERED = 1, MODE_REGEN = 2 };
+
+// Where a query row sits: its sequence and how many leading keys it sees.
+// Shared by the decode kernel and the fold kernel so both agree on the
+// number of splits of every row.
+struct RowMap {
+    const int32_t *context_lens;  // [num_seqs]
+    const int32_t *query_start;   // [num_seqs + 1] or nullptr (one row per sequence)
+    int32_t num_seqs;
+    int32_t max_context_len;      // host bound
+    int32_t max_keys;             // max_pages_per_seq * page_tokens
+};
+
+struct DecodeParams {
+    RowMap rows;
+    const void *q;            // [total_q][H][D]
+    int32_t q_dtype;
+    const void *k_pool;       // [num_blocks][Hkv][P][D] (hot pool in tiered mode)
+    const void *v_pool;
+    const int32_t *page_table;
+    int32_t num_heads, num_kv_heads, page_tokens, max_pages, num_blocks, total_q;
+    int32_t split_tokens, max_splits;
+    float scale_log2;         // softmax scale * log2(e)
+    float *part_o;            // [total_q * H][max_splits][D]
+    float *part_lse;          // [total_q * H][max_splits], natural log
+    float *out;               // [total_q][H][D]  (written directly if direct != 0)
+    float *lse;               // [total_q][H]
+    int32_t direct;
+    // tiered pools
+    const int8_t *i8_k, *i8_v;
+    const float *i8_ks, *i8_vs;
+    const uint8_t *i4_k, *i4_v;
+    const float *i4_ks, *i4_vs;
+    int32_t n_i8, n_i4;
+    // regenerated pages
+    uint64_t seed;
+    uint32_t layer;
+    const int32_t *regen_pages;  // [num_seqs]
+};
+
+struct FoldParams {
+    const float *part_o;
+    const float *part_lse;
+    float *out;
+    float *lse;
+    int64_t o_row_stride, o_split_stride;   // in floats
+    int64_t l_row_stride, l_split_stride;
+    int32_t rows;          // rows to merge (total_q * H internally)
+    int32_t head_dim;
+    int32_t fixed_splits;  // > 0: every row has this many splits
+    // otherwise the split count of a row comes from its visible keys
+    RowMap map;
+    int32_t num_heads;
+    int32_t split_tokens;
+};
+
+struct PrefillParams {
+    RowMap rows;
+    const void *q;            // [total_q][H][D] bf16 / f16
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *page_table;
+    const void *regen_k;      // [num_seqs][max_regen][Hkv][P][D] regenerated pages, or null
+    const void *regen_v;
+    const int32_t *regen_pages;
+    int32_t max_regen;
+    int32_t num_heads, num_kv_heads, page_tokens, max_pages, num_blocks, total_q;
+    int32_t max_query_len;
+    int32_t q_blocks;         // query tiles per sequence (grid)
+    float scale_log2;
+    float *out;
+    float *lse;
+};
+
+struct RegenFillParams {
+    uint64_t seed;
+    uint32_t layer;
+    int32_t num_kv_heads, head_dim, page_tokens;
+    const int32_t *logical_pages;  // [n] or null (then page index = i % pages_per_seq)
+    const int32_t *dst_blocks;     // [n] or null (then block = i)
+    const int32_t *regen_pages;    // per-sequence limit for scratch fills, or null
+    int32_t pages_per_seq;         // scratch fill: max_regen
+    int32_t n;
+    int32_t num_blocks;
+    int32_t kv_f32;                // 1: write f32 values, 0: bf16
+    void *k_dst;
+    void *v_dst;
+};
+
+// Launchers (defined next to their kernels).  Each returns the HIP error of
+// the launch.
+hipError_t launch_decode(const DecodeParams &p, int kv_type, int head_dim, int group,
+                         int mode, hipStream_t stream);
+hipError_t launch_fold(const FoldParams &f, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream);
+hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream);
+hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t page_tokens,
+                         int32_t num_blocks, int32_t elem_bytes, int32_t num_tokens,
+                         void *k_out, void *v_out, hipStream_t stream);
+hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,
+                          const int32_t *entries, int32_t n, float *k_out, float *v_out,
+                          hipStream_t stream);
+
+}  // namespace atlas

@@ -1,0 +1,369 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 oracle.
+
+Tolerances (max-abs on out and on lse): 2e-5 for f32 K/V, 2e-3 for bf16 /
+f16 / int8 / int4 / regenerated K/V, all with f32 accumulation.  Integer and
+byte-level steps (page gather, regenerated values, tier decoding) must match
+bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from kv_cache_runtime_amd import atlas
+from tests.paging import relayout
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-5, "bf16": 2e-3, "f16": 2e-3}
+
+
+def _tol(w):
+    if w.tiers is not None or w.regen is not None:
+        return 2e-3
+    return TOL[w.kv_dtype]
+
+
+def run(w, split_tokens=0, fill=True):
+    prob = atlas.Problem(w, split_tokens=split_tokens)
+    if w.regen is not None and fill:
+        prob.fill_resident_from_regenerator()
+    out, lse = prob.run()
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def check(w, out, lse, rows=None, heads=None, tol=None, host=None):
+    tol = _tol(w) if tol is None else tol
+    rows = np.arange(w.total_q) if rows is None else np.asarray(rows)
+    heads = np.arange(w.num_heads) if heads is None else np.asarray(heads)
+    ref_o, ref_l = oracle.reference(w, rows=rows, heads=heads, host=host)
+    got_o = out[rows][:, heads]
+    got_l = lse[rows][:, heads]
+    assert np.all(np.isfinite(got_o)), "non-finite output"
+    finite = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(got_l), finite)
+    eo = float(np.max(np.abs(got_o - ref_o))) if got_o.size else 0.0
+    el = float(np.max(np.abs(got_l[finite] - ref_l[finite]))) if finite.any() else 0.0
+    print(f"[{w.name or 'case'}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e} tol={tol:g}",
+          flush=True)
+    assert eo <= tol and el <= tol
+    return eo, el
+
+
+def cuda():
+    return torch.device("cuda:0")
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+def test_config1_full(gpu):
+    w = synth.config(1, device=gpu)
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+def test_config2_reduced_all_heads(gpu):
+    w = synth.config(2, device=gpu, context_lens=5000)
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+def test_config2_full_sampled_heads(gpu):
+    w = synth.config(2, device=gpu)
+    out, lse = run(w)
+    check(w, out, lse, heads=[0, 7, 19, 31])
+
+
+def test_config3_reduced(gpu):
+    w = synth.config(3, device=gpu, num_seqs=10,
+                     context_lens=[1, 15, 16, 17, 300, 1023, 1024, 2049, 4000, 777])
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+def test_config3_full_sampled(gpu):
+    w = synth.config(3, device=gpu)
+    out, lse = run(w)
+    seqs = [0, 13, 37, 63, int(np.argmax(w.context_lens))]
+    check(w, out, lse, rows=seqs, heads=[0, 5, 17, 31])
+
+
+def test_config4_reduced(gpu):
+    w = synth.config(4, device=gpu, num_seqs=6, context_lens=[5, 1000, 1030, 2500, 4097, 3000])
+    counts = w.tiers["counts"]
+    assert counts[1] > 0 and counts[2] > 0
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+def test_config4_full_sampled(gpu):
+    w = synth.config(4, device=gpu)
+    out, lse = run(w)
+    seqs = [1, 22, 50, int(np.argmax(w.context_lens))]
+    check(w, out, lse, rows=seqs, heads=[0, 9, 30])
+
+
+def test_config5_reduced_prefill_with_regen(gpu):
+    w = synth.config(5, device=gpu, context_lens=3000, query_lens=200, num_heads=16,
+                     num_kv_heads=2)
+    out, lse = run(w)
+    check(w, out, lse, rows=[0, 1, 57, 100, 199])
+
+
+# ---------------------------------------------------------------------------
+# Shapes, head maps, splits, prefill rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 4), (8, 2), (8, 1)])
+def test_head_maps_dtypes_dims(gpu, kv, D, H, Hkv):
+    w = synth.build(dict(num_seqs=3, context_lens=[70, 513, 1200], num_heads=H,
+                         num_kv_heads=Hkv, head_dim=D, page_tokens=32, kv_dtype=kv,
+                         placement="permuted"), device=gpu, seed=D + H + Hkv,
+                    name=f"{kv}-D{D}-H{H}/{Hkv}")
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+@pytest.mark.parametrize("split", [64, 128, 512, 2048])
+def test_split_sizes(gpu, split):
+    w = synth.build(dict(num_seqs=2, context_lens=[3001, 64], num_heads=8, num_kv_heads=2,
+                         head_dim=128, page_tokens=16, kv_dtype="bf16"), device=gpu, seed=5,
+                    name=f"split{split}")
+    out, lse = run(w, split_tokens=split)
+    check(w, out, lse)
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_chunked_prefill_rows(gpu, kv):
+    w = synth.build(dict(num_seqs=3, context_lens=[50, 700, 333], query_lens=[50, 37, 5],
+                         num_heads=8, num_kv_heads=2, head_dim=64, page_tokens=16,
+                         kv_dtype=kv), device=gpu, seed=9, name=f"prefill-{kv}")
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+def test_regen_decode_rows(gpu):
+    w = synth.build(dict(num_seqs=3, context_lens=[900, 17, 2050], num_heads=8,
+                         num_kv_heads=2, head_dim=128, page_tokens=64, kv_dtype="bf16",
+                         regen=dict(seed=7, layer=3, fraction=0.75)), device=gpu, seed=3,
+                    name="regen-decode")
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+# ---------------------------------------------------------------------------
+# Invariants: determinism, page size, placement, regen vs resident
+# ---------------------------------------------------------------------------
+
+def test_determinism_bitwise(gpu):
+    w = synth.config(3, device=gpu, num_seqs=6, context_lens=("uniform", 100, 5000))
+    o1, l1 = run(w)
+    o2, l2 = run(w)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+@pytest.mark.parametrize("kv,D", [("bf16", 128), ("f32", 64)])
+def test_page_size_and_placement_do_not_change_bits(gpu, kv, D):
+    w = synth.build(dict(num_seqs=4, context_lens=[1, 100, 1500, 2600], num_heads=8,
+                         num_kv_heads=2, head_dim=D, page_tokens=16, kv_dtype=kv),
+                    device=gpu, seed=21, name="pagesize")
+    o0, l0 = run(w, split_tokens=512)
+    check(w, o0, l0)
+    for P, seed, spare in ((16, 1, 5), (32, 2, 0), (64, 3, 9), (256, 4, 1), (512, 5, 0)):
+        w2 = relayout(w, P, seed, spare_blocks=spare)
+        o2, l2 = run(w2, split_tokens=512)
+        assert np.array_equal(o0.view(np.uint32), o2.view(np.uint32)), P
+        assert np.array_equal(l0.view(np.uint32), l2.view(np.uint32)), P
+
+
+def test_regenerated_equals_resident_bitwise(gpu):
+    # CFR-Atlas contract: when regeneration reproduces the stored rows, the
+    # folded result equals the all-resident result.
+    base = dict(num_seqs=2, context_lens=[1000, 2100], num_heads=8, num_kv_heads=2,
+                head_dim=128, page_tokens=64, kv_dtype="bf16")
+    w_regen = synth.build(dict(base, regen=dict(seed=11, layer=1, fraction=0.75)),
+                          device=gpu, seed=4)
+    w_res = synth.build(dict(base, regen=dict(seed=11, layer=1, fraction=0.0)),
+                        device=gpu, seed=4)
+    o1, l1 = run(w_regen, split_tokens=512)
+    o2, l2 = run(w_res, split_tokens=512)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+    check(w_regen, o1, l1)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases and loud failures
+# ---------------------------------------------------------------------------
+
+def test_empty_and_single_token_contexts(gpu):
+    w = synth.build(dict(num_seqs=3, context_lens=[0, 1, 2], num_heads=4, num_kv_heads=2,
+                         head_dim=64, page_tokens=16, kv_dtype="f32"), device=gpu, seed=2)
+    out, lse = run(w)
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf)
+    v0 = w.v_pool[int(w.page_table[1, 0])][:, 0].cpu().numpy()  # [Hkv][D]
+    assert np.array_equal(out[1], v0[np.arange(4) // 2])
+    check(w, out, lse, rows=[1, 2])
+
+
+def test_identical_v_rows_return_that_row(gpu):
+    w = synth.build(dict(num_seqs=2, context_lens=[3000, 50], num_heads=4, num_kv_heads=1,
+                         head_dim=128, page_tokens=16, kv_dtype="bf16"), device=gpu, seed=8)
+    row = torch.randn(128, device=gpu).to(torch.bfloat16)
+    w.v_pool[:] = row
+    out, _ = run(w)
+    np.testing.assert_allclose(out, np.broadcast_to(row.float().cpu().numpy(), out.shape),
+                               rtol=0, atol=1e-6)
+
+
+def test_bad_page_ids_and_context_lengths_give_nan(gpu):
+    w = synth.build(dict(num_seqs=3, context_lens=[100, 200, 300], num_heads=4,
+                         num_kv_heads=2, head_dim=64, page_tokens=16, kv_dtype="f32"),
+                    device=gpu, seed=6)
+    w.page_table[1, 3] = w.num_blocks + 7   # outside the pool: guarded, row -> NaN
+    w.page_table[2, 0] = -5
+    out, lse = run(w)
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(lse[1]))
+    assert np.all(np.isnan(out[2])) and np.all(np.isnan(lse[2]))
+    check(w, out, lse, rows=[0])
+    # a context longer than the host bound: guarded, row -> NaN, others intact
+    w2 = synth.build(dict(num_seqs=2, context_lens=[100, 200], num_heads=4, num_kv_heads=2,
+                          head_dim=64, page_tokens=16, kv_dtype="f32", max_pages=16),
+                     device=gpu, seed=6)
+    prob = atlas.Problem(w2)
+    prob.args.max_context_len = 150
+    prob.ctx[1] = 200
+    out2, lse2 = prob.run()
+    torch.cuda.synchronize()
+    assert torch.isnan(out2[1]).all() and torch.isnan(lse2[1]).all()
+    assert torch.isfinite(out2[0]).all()
+
+
+# ---------------------------------------------------------------------------
+# Bit-exact inspection entry points
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f16"])
+def test_gather_pages_bit_exact(gpu, kv):
+    w = synth.build(dict(num_seqs=3, context_lens=[33, 1000, 517], num_heads=8,
+                         num_kv_heads=4, head_dim=64, page_tokens=16, kv_dtype=kv),
+                    device=gpu, seed=31)
+    prob = atlas.Problem(w)
+    host = oracle.HostView(w)
+    for s in range(3):
+        n = int(w.context_lens[s])
+        k = torch.empty((n, 4, 64), device=gpu, dtype=w.k_pool.dtype)
+        v = torch.empty_like(k)
+        atlas.atlas_gather_pages(prob.args, s, n, k, v)
+        torch.cuda.synchronize()
+        for g in range(4):
+            K, V = oracle.logical_kv(w, s, g, host=host)
+            assert np.array_equal(k[:, g].double().cpu().numpy(), K)
+            assert np.array_equal(v[:, g].double().cpu().numpy(), V)
+
+
+@pytest.mark.parametrize("kv_name,code", [("bf16", atlas.BF16), ("f32", atlas.F32)])
+def test_regenerate_pages_bit_exact(gpu, kv_name, code):
+    Hkv, D, P = 3, 128, 32
+    logical = torch.tensor([0, 5, 2, 1000], dtype=torch.int32, device=gpu)
+    blocks = torch.tensor([3, 0, 1, 2], dtype=torch.int32, device=gpu)
+    dt = synth.DTYPES[kv_name]
+    kp = torch.full((4, Hkv, P, D), float("nan"), dtype=dt, device=gpu)
+    vp = torch.full_like(kp, float("nan"))
+    atlas.atlas_regenerate_pages(123456789, 5, Hkv, D, P, code, logical, blocks, 4, kp, vp)
+    torch.cuda.synchronize()
+    for lp, b in zip(logical.tolist(), blocks.tolist()):
+        for g in range(Hkv):
+            for kv, pool in ((0, kp), (1, vp)):
+                ref = oracle.regen_values(123456789, 5, g, lp * P, P, D, kv)
+                got = pool[b, g].float().cpu().numpy()
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_regenerate_config5_pages_bit_exact(gpu):
+    # every value of four of config 5's regenerated pages, all kv heads
+    Hkv, D, P = 8, 128, 256
+    lps = [0, 1, 200, 383]
+    logical = torch.tensor(lps, dtype=torch.int32, device=gpu)
+    blocks = torch.arange(4, dtype=torch.int32, device=gpu)
+    kp = torch.empty((4, Hkv, P, D), dtype=torch.bfloat16, device=gpu)
+    vp = torch.empty_like(kp)
+    atlas.atlas_regenerate_pages(42, 0, Hkv, D, P, atlas.BF16, logical, blocks, 4, kp, vp)
+    torch.cuda.synchronize()
+    for i, lp in enumerate(lps):
+        for g in range(Hkv):
+            for kv, pool in ((0, kp), (1, vp)):
+                ref = oracle.regen_values(42, 0, g, lp * P, P, D, kv)
+                got = pool[i, g].float().cpu().numpy()
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_pages_bit_exact(gpu):
+    w = synth.config(4, device=gpu, num_seqs=3, context_lens=[3000, 2000, 1500])
+    prob = atlas.Problem(w)
+    entries_np = np.concatenate([w.page_table[s, :w.pages_of(s)] for s in range(3)])
+    entries = torch.from_numpy(entries_np).to(gpu)
+    n = entries.numel()
+    k = torch.empty((n, 8, 16, 128), device=gpu)
+    v = torch.empty_like(k)
+    atlas.atlas_dequant_pages(prob.args, prob.tiers, entries, k, v)
+    torch.cuda.synchronize()
+    host = oracle.HostView(w)
+    ta = host.tier_arrays()
+    (hk, kind), (hv, _) = host.pools()
+    kc, vc = k.cpu().numpy(), v.cpu().numpy()
+    for i, e in enumerate(entries_np.view(np.uint32)):
+        tier, slot = int(e) >> 30, int(e) & ((1 << 30) - 1)
+        if tier == 0:
+            rk = oracle.widen_bits(hk[slot], kind).astype(np.float32)
+            rv = oracle.widen_bits(hv[slot], kind).astype(np.float32)
+        else:
+            key = "i8" if tier == 1 else "i4"
+            ck, cv = ta[f"{key}_k"][slot], ta[f"{key}_v"][slot]
+            if key == "i4":
+                ck, cv = oracle.int4_codes(ck), oracle.int4_codes(cv)
+            rk = oracle.dequant_f32(ck[None], ta[f"{key}_k_scale"][slot][None])[0]
+            rv = oracle.dequant_f32(cv[None], ta[f"{key}_v_scale"][slot][None])[0]
+        ok_k = np.array_equal(kc[i].view(np.uint32), rk.view(np.uint32)) or \
+            (tier == 0 and np.array_equal(np.isnan(kc[i]), np.isnan(rk)) and
+             np.array_equal(kc[i][~np.isnan(rk)], rk[~np.isnan(rk)]))
+        ok_v = np.array_equal(vc[i].view(np.uint32), rv.view(np.uint32)) or \
+            (tier == 0 and np.array_equal(np.isnan(vc[i]), np.isnan(rv)) and
+             np.array_equal(vc[i][~np.isnan(rv)], rv[~np.isnan(rv)]))
+        assert ok_k and ok_v, (i, tier)
+
+
+def test_fold_partials_matches_oracle_merge(gpu):
+    rng = np.random.default_rng(17)
+    splits, rows, D = 7, 300, 128
+    po = rng.standard_normal((splits, rows, D)).astype(np.float32)
+    pl = (rng.standard_normal((splits, rows)) * 20).astype(np.float32)
+    pl[rng.random((splits, rows)) < 0.3] = -np.inf
+    pl[:, 5] = -np.inf   # an all-empty row
+    out = torch.empty((rows, D), device=gpu)
+    lse = torch.empty(rows, device=gpu)
+    atlas.atlas_fold_partials(torch.from_numpy(po).to(gpu), torch.from_numpy(pl).to(gpu),
+                              out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.merge_splits(po, pl)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(o[5] == 0) and l[5] == -np.inf
+    fin = np.isfinite(ref_l)
+    assert np.max(np.abs(o - ref_o)) <= 2e-5 * max(1.0, float(np.max(np.abs(ref_o))))
+    assert np.max(np.abs(l[fin] - ref_l[fin])) <= 2e-5 * max(1.0, float(np.max(np.abs(ref_l[fin]))))
+    # a single split is the identity
+    out1 = torch.empty((rows, D), device=gpu)
+    lse1 = torch.empty(rows, device=gpu)
+    atlas.atlas_fold_partials(torch.from_numpy(po[:1]).to(gpu),
+                              torch.from_numpy(np.where(np.isfinite(pl[:1]), pl[:1], 0.0)
+                                               .astype(np.float32)).to(gpu), out1, lse1)
+    torch.cuda.synchronize()
+    assert np.array_equal(out1.cpu().numpy(), po[0])
