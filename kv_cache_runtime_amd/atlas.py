@@ -54,6 +54,7 @@ class AttnArgs(ctypes.Structure):
         ("workspace", _p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", _p),
+        ("profile_events", _p * 2),
     ]
 
 

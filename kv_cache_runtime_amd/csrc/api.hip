@@ -5,6 +5,7 @@
 // ranges, transactional behaviour).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -53,6 +54,7 @@ struct Plan {
     bool mfma = false;       // chunked prefill on matrix cores
     size_t part_o_bytes = 0;
     size_t part_lse_bytes = 0;
+    size_t counter_bytes = 0;
     size_t regen_bytes = 0;  // one K and one V copy of the regenerated pages
     size_t total = 0;
 };
@@ -161,6 +163,7 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
             const int64_t parts = (int64_t)a->total_q * a->num_heads * plan->max_splits;
             plan->part_o_bytes = align_up((size_t)parts * a->head_dim * sizeof(float));
             plan->part_lse_bytes = align_up((size_t)parts * sizeof(float));
+            plan->counter_bytes = align_up((size_t)a->total_q * a->num_kv_heads * 8);
         }
     }
 
@@ -181,7 +184,8 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
                                          a->num_kv_heads * a->page_tokens * a->head_dim * 2);
         }
     }
-    plan->total = plan->part_o_bytes + plan->part_lse_bytes + 2 * plan->regen_bytes;
+    plan->total = plan->part_o_bytes + plan->part_lse_bytes + plan->counter_bytes +
+                  2 * plan->regen_bytes;
     return ok();
 }
 
@@ -195,6 +199,18 @@ atlas_status check_workspace(const atlas_attn_args *a, const Plan &plan) {
     if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign)
         return fail(ATLAS_EINVAL, "workspace must be %zu-byte aligned", kAlign);
     return ok();
+}
+
+// Tag of one call for the split arrival counters in the workspace.  Any
+// value left in a counter by an earlier call carries another tag and reads as
+// zero arrivals; 0 is never used as a tag.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> epoch{0x5EED0000u};
+    uint32_t e;
+    do {
+        e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (e == 0);
+    return e;
 }
 
 RowMap row_map(const atlas_attn_args *a) {
@@ -231,33 +247,27 @@ DecodeParams decode_params(const atlas_attn_args *a, const Plan &plan) {
     p.out = a->out;
     p.lse = a->lse;
     p.direct = plan.direct ? 1 : 0;
+    p.counters = plan.direct ? nullptr
+                             : reinterpret_cast<unsigned long long *>(
+                                   ws + plan.part_o_bytes + plan.part_lse_bytes);
+    p.epoch = next_epoch();
     return p;
+}
+
+// Optional caller events around the main kernel (profiling hook).
+hipError_t mark(const atlas_attn_args *a, int which, hipStream_t stream) {
+    if (!a->profile_events[which]) return hipSuccess;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(a->profile_events[which]), stream);
 }
 
 atlas_status run_decode(const atlas_attn_args *a, const Plan &plan, DecodeParams &p, int mode) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
-    hipError_t e = launch_decode(p, a->kv_dtype, a->head_dim, plan.group, mode, stream);
+    hipError_t e = mark(a, 0, stream);
+    if (e != hipSuccess) return device_status(e, "profile event record");
+    e = launch_decode(p, a->kv_dtype, a->head_dim, plan.group, mode, stream);
     if (e != hipSuccess) return device_status(e, "decode launch");
-    if (!plan.direct) {
-        FoldParams f;
-        std::memset(&f, 0, sizeof(f));
-        f.part_o = p.part_o;
-        f.part_lse = p.part_lse;
-        f.out = a->out;
-        f.lse = a->lse;
-        f.o_row_stride = (int64_t)plan.max_splits * a->head_dim;
-        f.o_split_stride = a->head_dim;
-        f.l_row_stride = plan.max_splits;
-        f.l_split_stride = 1;
-        f.rows = a->total_q * a->num_heads;
-        f.head_dim = a->head_dim;
-        f.fixed_splits = 0;
-        f.map = p.rows;
-        f.num_heads = a->num_heads;
-        f.split_tokens = plan.split_tokens;
-        e = launch_fold(f, stream);
-        if (e != hipSuccess) return device_status(e, "fold launch");
-    }
+    e = mark(a, 1, stream);
+    if (e != hipSuccess) return device_status(e, "profile event record");
     return ok();
 }
 

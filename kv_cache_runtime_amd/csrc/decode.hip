@@ -7,8 +7,9 @@
 // rescaled by exp(m_old - m_new) whenever the max grows -- so the K/V pages
 // are never concatenated.  The context is cut into splits of a fixed number
 // of tokens (cortiq README, "split-K flash-decoding"); every split is one
-// workgroup and writes a normalised partial (o, lse) that fold_kernel merges
-// (attnres AGENTS.md, "online softmax merge").
+// workgroup and writes a normalised partial (o, lse); the last workgroup of a
+// (row, kv head) to finish merges the partials by log-sum-exp (attnres
+// AGENTS.md, "online softmax merge").
 //
 // gfx950 mapping.  A workgroup is 4 wave64s and owns one (row, kv head,
 // split).  Inside a wave the 64 lanes form 4 row-slots of 16 lanes; a
@@ -154,6 +155,104 @@ __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry,
         }
     }
     return false;
+}
+
+// Arrival counter of a (row, kv head) for one call.  The 64-bit word holds
+// (epoch << 32) | arrivals; a word left by an earlier call (another epoch)
+// counts as zero arrivals, so the counters never need clearing between
+// calls.  Returns nonzero for the workgroup whose arrival completes `n`.
+__device__ __forceinline__ int arrive_last(unsigned long long *ctr, uint32_t epoch, int n) {
+    unsigned long long old = *reinterpret_cast<volatile unsigned long long *>(ctr);
+    unsigned long long want;
+    while (true) {
+        const bool same = (uint32_t)(old >> 32) == epoch;
+        want = same ? old + 1ull : (((unsigned long long)epoch << 32) | 1ull);
+        const unsigned long long prev = atomicCAS(ctr, old, want);
+        if (prev == old) break;
+        old = prev;
+    }
+    const int arrived = (int)(uint32_t)want;
+    if (arrived == n) atomicExch(ctr, 0ull);  // no one else touches it in this call
+    return arrived == n;
+}
+
+// Log-sum-exp merge of `nsplit` normalised partials of one output row
+// (attnres AGENTS.md, "online softmax merge"): lse = M + log sum_s
+// exp(lse_s - M), out = sum_s exp(lse_s - lse) o_s.  Whole workgroup (256
+// threads).  Weights go through LDS in chunks of kMergeChunk splits; each
+// wave sums a fixed quarter of a chunk and the quarters are added in wave
+// order, so the arithmetic order is fixed.  Any NaN partial makes the row NaN;
+// a row whose splits are all empty gets out 0 and lse -inf.  head_dim <= 256.
+constexpr int kMergeChunk = 1024;
+
+__device__ void merge_row(const float *pl, int64_t l_stride, const float *po, int64_t o_stride,
+                          int nsplit, int D, float *out, float *lse_out) {
+    __shared__ float s_w[kMergeChunk];
+    __shared__ float s_red[kWaves][256];
+    __shared__ float s_sum[kWaves];
+    const float kNegInf = -__builtin_inff();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    float M = kNegInf;
+    int nan = 0;
+    for (int s = tid; s < nsplit; s += 256) {
+        const float x = pl[s * l_stride];
+        nan |= (x != x);
+        M = fmaxf(M, x);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) s_sum[wave] = M;
+    const bool any_nan = __syncthreads_or(nan) != 0;
+    M = fmaxf(fmaxf(s_sum[0], s_sum[1]), fmaxf(s_sum[2], s_sum[3]));
+    const float M_use = (M == kNegInf) ? 0.0f : M;
+    __syncthreads();
+
+    float lsum = 0.0f;
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = 0; c0 < nsplit; c0 += kMergeChunk) {
+        const int cn = min(kMergeChunk, nsplit - c0);
+        for (int s = tid; s < cn; s += 256) {
+            const float x = pl[(c0 + s) * l_stride];
+            const float w = (x == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((x - M_use) * kLog2e);
+            s_w[s] = w;
+            lsum += w;
+        }
+        __syncthreads();
+        const int per = (cn + kWaves - 1) / kWaves;
+        const int s0 = wave * per, s1 = min(cn, s0 + per);
+        for (int s = s0; s < s1; ++s) {
+            const float w = s_w[s];
+            const float *row = po + (int64_t)(c0 + s) * o_stride;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = lane + 64 * i;
+                if (col < D) a[i] = fmaf(w, row[col], a[i]);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int col = lane + 64 * i;
+        if (col < D) s_red[wave][col] = a[i];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) s_sum[wave] = lsum;
+    __syncthreads();
+    const float L = ((s_sum[0] + s_sum[1]) + s_sum[2]) + s_sum[3];
+    const float qnan = __builtin_nanf("");
+    for (int col = tid; col < D; col += 256) {
+        float o = ((s_red[0][col] + s_red[1][col]) + s_red[2][col]) + s_red[3][col];
+        o = (L > 0.0f) ? o / L : 0.0f;
+        out[col] = any_nan ? qnan : o;
+    }
+    if (tid == 0) {
+        const float l = (L > 0.0f) ? M + logf(L) : kNegInf;
+        *lse_out = any_nan ? qnan : l;
+    }
+    __syncthreads();
 }
 
 template <int KV, int D, int G, int MODE>
@@ -302,7 +401,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     }
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
 
-    // merge the waves in a fixed order and write the split's result
+    // merge the waves in a fixed order: this split's normalised result
+    const int nsplit = splits_of(nvis, T);
+    const bool final_here = p.direct || nsplit == 1;
     if (wave == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -325,76 +426,45 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
                 for (int w = 0; w < kWaves; ++w) o = fmaf(fw[w], s_acc[w][h][col], o);
                 o = L > 0.0f ? o / L : 0.0f;
                 if (any_bad) o = qnan;
-                if (p.direct) p.out[orow * D + col] = o;
+                if (final_here) p.out[orow * D + col] = o;
                 else p.part_o[(orow * p.max_splits + split) * D + col] = o;
             }
             if (lane == 0) {
                 float lse = L > 0.0f ? (M + log2f(L)) * kLn2 : kNegInf;
                 if (any_bad) lse = qnan;
-                if (p.direct) p.lse[orow] = lse;
+                if (final_here) p.lse[orow] = lse;
                 else p.part_lse[orow * p.max_splits + split] = lse;
             }
         }
     }
+    if (final_here) return;
+
+    // Split-K merge inside the kernel: the last workgroup to finish a
+    // (row, kv head) merges all of its splits.  The merge reads the splits in
+    // index order, so the result does not depend on which workgroup is last.
+    __shared__ int s_last;
+    __threadfence();  // release this split's partial to the whole device
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = arrive_last(p.counters + (int64_t)row * p.num_kv_heads + g, p.epoch, nsplit);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire the other splits' partials
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {
+        const int64_t orow = (int64_t)row * p.num_heads + g * G + h;
+        merge_row(p.part_lse + orow * p.max_splits, 1, p.part_o + orow * p.max_splits * D, D,
+                  nsplit, D, p.out + orow * D, p.lse + orow);
+    }
 }
 
-// One wave per merged row; splits combined in index order.
+// Public split merge: one workgroup per row.
 __global__ __launch_bounds__(256) void fold_kernel(const FoldParams f) {
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int idx = blockIdx.x * 4 + wave;
+    const int idx = blockIdx.x;
     if (idx >= f.rows) return;
-    const float kNegInf = -__builtin_inff();
-    int nsplit = f.fixed_splits;
-    if (nsplit <= 0) {
-        int seq, vis;
-        map_row(f.map, idx / f.num_heads, seq, vis);
-        nsplit = splits_of(vis, f.split_tokens);
-    }
-    const float *pl = f.part_lse + (int64_t)idx * f.l_row_stride;
-    const float *po = f.part_o + (int64_t)idx * f.o_row_stride;
-
-    float M = kNegInf;
-    int nan = 0;
-    for (int s = lane; s < nsplit; s += 64) {
-        const float x = pl[(int64_t)s * f.l_split_stride];
-        nan |= (x != x);
-        M = fmaxf(M, x);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const bool any_nan = __any(nan);
-    const float M_use = (M == kNegInf) ? 0.0f : M;
-
-    float L = 0.0f;
-    float accv[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // head_dim <= 256
-    for (int s = 0; s < nsplit; ++s) {
-        const float x = pl[(int64_t)s * f.l_split_stride];
-        const float w = (x == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((x - M_use) * kLog2e);
-        L += w;
-        if (w != 0.0f) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = lane + 64 * i;
-                if (col < f.head_dim) accv[i] = fmaf(w, po[(int64_t)s * f.o_split_stride + col], accv[i]);
-            }
-        }
-    }
-    const float qnan = __builtin_nanf("");
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int col = lane + 64 * i;
-        if (col < f.head_dim) {
-            float o = (L > 0.0f) ? accv[i] / L : 0.0f;
-            if (any_nan) o = qnan;
-            f.out[(int64_t)idx * f.head_dim + col] = o;
-        }
-    }
-    if (lane == 0) {
-        float lse = (L > 0.0f) ? M + logf(L) : kNegInf;
-        if (any_nan) lse = qnan;
-        f.lse[idx] = lse;
-    }
+    merge_row(f.part_lse + (int64_t)idx * f.l_row_stride, f.l_split_stride,
+              f.part_o + (int64_t)idx * f.o_row_stride, f.o_split_stride, f.fixed_splits,
+              f.head_dim, f.out + (int64_t)idx * f.head_dim, f.lse + idx);
 }
 
 template <int KV, int D, int G, int MODE>
@@ -449,7 +519,7 @@ hipError_t launch_decode(const DecodeParams &p, int kv_type, int head_dim, int g
 
 hipError_t launch_fold(const FoldParams &f, hipStream_t stream) {
     if (f.rows <= 0) return hipSuccess;
-    const unsigned blocks = (unsigned)((f.rows + 3) / 4);
+    const unsigned blocks = (unsigned)f.rows;
     hipLaunchKernelGGL(fold_kernel, dim3(blocks), dim3(256), 0, stream, f);
     return hipGetLastError();
 }
