@@ -118,8 +118,8 @@ typedef struct atlas_attn_args {
     void *profile_events[2];    /* optional hipEvent_t pair (or NULLs): recorded on
                                    `stream` just before and just after the main
                                    attention kernel, so a caller can time that
-                                   kernel alone (a regeneration pre-pass, if any,
-                                   falls outside the pair) */
+                                   kernel alone (the split merge and a
+                                   regeneration pre-pass fall outside the pair) */
 } atlas_attn_args;
 
 /*
@@ -183,12 +183,11 @@ const char *atlas_last_error(void);
  * Workspace bytes needed by atlas_paged_attention (regen == NULL) or
  * atlas_paged_attention_regen (regen != NULL) for these arguments.  Reads host
  * fields only.  The workspace holds the split-K partials (one f32 vector of
- * head_dim plus one lse per (row, head, split)), one 64-bit arrival counter
- * per (row, kv head) and, for chunked prefill with regenerated pages, one bf16
- * copy of every regenerated page (each regenerated value is computed once per
- * call and shared by every query tile).  Its contents need no initialisation
- * and are not meaningful between calls; two calls in flight at the same time
- * must not share a workspace.
+ * head_dim plus one lse per (row, head, split)) and, for chunked prefill with
+ * regenerated pages, one bf16 copy of every regenerated page (each
+ * regenerated value is computed once per call and shared by every query
+ * tile).  Its contents need no initialisation and are not meaningful between
+ * calls; two calls in flight at the same time must not share a workspace.
  */
 atlas_status atlas_workspace_size(const atlas_attn_args *args,
                                   const atlas_regen_spec *regen,

@@ -52,9 +52,9 @@ struct Plan {
     int max_splits = 1;
     bool direct = true;      // one split per row: the decode kernel writes out/lse
     bool mfma = false;       // chunked prefill on matrix cores
+    int q_blocks = 0;        // query tiles per sequence (matrix-core prefill)
     size_t part_o_bytes = 0;
     size_t part_lse_bytes = 0;
-    size_t counter_bytes = 0;
     size_t regen_bytes = 0;  // one K and one V copy of the regenerated pages
     size_t total = 0;
 };
@@ -145,7 +145,7 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
     const bool prefill = a->query_start != nullptr;
     const bool sixteen = a->kv_dtype == ATLAS_BF16 || a->kv_dtype == ATLAS_F16;
     plan->mfma = prefill && !tiered && sixteen && a->q_dtype == a->kv_dtype &&
-                 a->head_dim == 128 && std::getenv("ATLAS_NO_MFMA") == nullptr && false;
+                 a->head_dim == 128 && std::getenv("ATLAS_NO_MFMA") == nullptr;
 
     if (!plan->mfma) {
         int st = choose_split_tokens(a);
@@ -163,7 +163,6 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
             const int64_t parts = (int64_t)a->total_q * a->num_heads * plan->max_splits;
             plan->part_o_bytes = align_up((size_t)parts * a->head_dim * sizeof(float));
             plan->part_lse_bytes = align_up((size_t)parts * sizeof(float));
-            plan->counter_bytes = align_up((size_t)a->total_q * a->num_kv_heads * 8);
         }
     }
 
@@ -184,8 +183,13 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
                                          a->num_kv_heads * a->page_tokens * a->head_dim * 2);
         }
     }
-    plan->total = plan->part_o_bytes + plan->part_lse_bytes + plan->counter_bytes +
-                  2 * plan->regen_bytes;
+    if (plan->mfma) {
+        plan->q_blocks = (a->max_query_len + 128 / group - 1) / (128 / group);
+        const int64_t blocks = (int64_t)a->num_kv_heads * plan->q_blocks * a->num_seqs;
+        if (blocks > INT32_MAX)
+            return fail(ATLAS_EUNSUPPORTED, "too many prefill workgroups (%lld)", (long long)blocks);
+    }
+    plan->total = plan->part_o_bytes + plan->part_lse_bytes + 2 * plan->regen_bytes;
     return ok();
 }
 
@@ -199,18 +203,6 @@ atlas_status check_workspace(const atlas_attn_args *a, const Plan &plan) {
     if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign)
         return fail(ATLAS_EINVAL, "workspace must be %zu-byte aligned", kAlign);
     return ok();
-}
-
-// Tag of one call for the split arrival counters in the workspace.  Any
-// value left in a counter by an earlier call carries another tag and reads as
-// zero arrivals; 0 is never used as a tag.
-uint32_t next_epoch() {
-    static std::atomic<uint32_t> epoch{0x5EED0000u};
-    uint32_t e;
-    do {
-        e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-    } while (e == 0);
-    return e;
 }
 
 RowMap row_map(const atlas_attn_args *a) {
@@ -247,10 +239,6 @@ DecodeParams decode_params(const atlas_attn_args *a, const Plan &plan) {
     p.out = a->out;
     p.lse = a->lse;
     p.direct = plan.direct ? 1 : 0;
-    p.counters = plan.direct ? nullptr
-                             : reinterpret_cast<unsigned long long *>(
-                                   ws + plan.part_o_bytes + plan.part_lse_bytes);
-    p.epoch = next_epoch();
     return p;
 }
 
@@ -266,6 +254,83 @@ atlas_status run_decode(const atlas_attn_args *a, const Plan &plan, DecodeParams
     if (e != hipSuccess) return device_status(e, "profile event record");
     e = launch_decode(p, a->kv_dtype, a->head_dim, plan.group, mode, stream);
     if (e != hipSuccess) return device_status(e, "decode launch");
+    e = mark(a, 1, stream);
+    if (e != hipSuccess) return device_status(e, "profile event record");
+    if (!plan.direct) {
+        FoldParams f;
+        std::memset(&f, 0, sizeof(f));
+        f.part_o = p.part_o;
+        f.part_lse = p.part_lse;
+        f.out = a->out;
+        f.lse = a->lse;
+        f.o_row_stride = (int64_t)plan.max_splits * a->head_dim;
+        f.o_split_stride = a->head_dim;
+        f.l_row_stride = plan.max_splits;
+        f.l_split_stride = 1;
+        f.rows = a->total_q * a->num_heads;
+        f.head_dim = a->head_dim;
+        f.fixed_splits = 0;
+        f.map = p.rows;
+        f.num_heads = a->num_heads;
+        f.split_tokens = plan.split_tokens;
+        e = launch_fold(f, stream);
+        if (e != hipSuccess) return device_status(e, "fold launch");
+    }
+    return ok();
+}
+
+// Chunked prefill on the matrix cores, after regenerating the regenerated
+// pages once into the workspace.
+atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas_regen_spec *rg) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
+    PrefillParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.rows = row_map(a);
+    p.q = a->q;
+    p.k_pool = a->k_pool;
+    p.v_pool = a->v_pool;
+    p.page_table = a->page_table;
+    p.num_heads = a->num_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.page_tokens = a->page_tokens;
+    p.max_pages = a->max_pages_per_seq;
+    p.num_blocks = a->num_blocks;
+    p.total_q = a->total_q;
+    p.max_query_len = a->max_query_len;
+    p.q_blocks = plan.q_blocks;
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    p.out = a->out;
+    p.lse = a->lse;
+    hipError_t e;
+    if (rg) {
+        char *ws = reinterpret_cast<char *>(a->workspace);
+        p.regen_k = ws;
+        p.regen_v = ws + plan.regen_bytes;
+        p.regen_pages = rg->regen_pages;
+        p.max_regen = rg->max_regen_pages;
+        if (rg->max_regen_pages > 0) {
+            RegenFillParams r;
+            std::memset(&r, 0, sizeof(r));
+            r.seed = rg->seed;
+            r.layer = rg->layer;
+            r.num_kv_heads = a->num_kv_heads;
+            r.head_dim = a->head_dim;
+            r.page_tokens = a->page_tokens;
+            r.regen_pages = rg->regen_pages;
+            r.pages_per_seq = rg->max_regen_pages;
+            r.n = a->num_seqs * rg->max_regen_pages;
+            r.num_blocks = r.n;
+            r.kv_f32 = 0;
+            r.k_dst = const_cast<void *>(p.regen_k);
+            r.v_dst = const_cast<void *>(p.regen_v);
+            e = launch_regen_fill(r, stream);
+            if (e != hipSuccess) return device_status(e, "regenerate launch");
+        }
+    }
+    e = mark(a, 0, stream);
+    if (e != hipSuccess) return device_status(e, "profile event record");
+    e = launch_prefill(p, a->kv_dtype, plan.group, stream);
+    if (e != hipSuccess) return device_status(e, "prefill launch");
     e = mark(a, 1, stream);
     if (e != hipSuccess) return device_status(e, "profile event record");
     return ok();
@@ -305,6 +370,7 @@ atlas_status atlas_paged_attention(const atlas_attn_args *args) {
     atlas_status st = check_common(args, false, nullptr, &plan);
     if (st != ATLAS_OK) return st;
     if ((st = check_workspace(args, plan)) != ATLAS_OK) return st;
+    if (plan.mfma) return run_prefill(args, plan, nullptr);
     DecodeParams p = decode_params(args, plan);
     return run_decode(args, plan, p, MODE_PLAIN);
 }
@@ -352,10 +418,12 @@ atlas_status atlas_paged_attention_regen(const atlas_attn_args *args,
     atlas_status st = check_common(args, false, regen, &plan);
     if (st != ATLAS_OK) return st;
     if ((st = check_workspace(args, plan)) != ATLAS_OK) return st;
+    if (plan.mfma) return run_prefill(args, plan, regen);
     DecodeParams p = decode_params(args, plan);
     p.seed = regen->seed;
     p.layer = regen->layer;
     p.regen_pages = regen->regen_pages;
+    p.max_regen = regen->max_regen_pages;
     return run_decode(args, plan, p, MODE_REGEN);
 }
 

@@ -7,9 +7,11 @@
 // rescaled by exp(m_old - m_new) whenever the max grows -- so the K/V pages
 // are never concatenated.  The context is cut into splits of a fixed number
 // of tokens (cortiq README, "split-K flash-decoding"); every split is one
-// workgroup and writes a normalised partial (o, lse); the last workgroup of a
-// (row, kv head) to finish merges the partials by log-sum-exp (attnres
-// AGENTS.md, "online softmax merge").
+// workgroup and writes a normalised partial (o, lse); a second kernel merges
+// the partials of every row by log-sum-exp (attnres AGENTS.md, "online
+// softmax merge").  Merging inside the attention kernel would need a
+// device-scope release per workgroup, which on this chip writes back the L2
+// and costs far more than the extra launch.
 //
 // gfx950 mapping.  A workgroup is 4 wave64s and owns one (row, kv head,
 // split).  Inside a wave the 64 lanes form 4 row-slots of 16 lanes; a
@@ -157,25 +159,6 @@ __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry,
     return false;
 }
 
-// Arrival counter of a (row, kv head) for one call.  The 64-bit word holds
-// (epoch << 32) | arrivals; a word left by an earlier call (another epoch)
-// counts as zero arrivals, so the counters never need clearing between
-// calls.  Returns nonzero for the workgroup whose arrival completes `n`.
-__device__ __forceinline__ int arrive_last(unsigned long long *ctr, uint32_t epoch, int n) {
-    unsigned long long old = *reinterpret_cast<volatile unsigned long long *>(ctr);
-    unsigned long long want;
-    while (true) {
-        const bool same = (uint32_t)(old >> 32) == epoch;
-        want = same ? old + 1ull : (((unsigned long long)epoch << 32) | 1ull);
-        const unsigned long long prev = atomicCAS(ctr, old, want);
-        if (prev == old) break;
-        old = prev;
-    }
-    const int arrived = (int)(uint32_t)want;
-    if (arrived == n) atomicExch(ctr, 0ull);  // no one else touches it in this call
-    return arrived == n;
-}
-
 // Log-sum-exp merge of `nsplit` normalised partials of one output row
 // (attnres AGENTS.md, "online softmax merge"): lse = M + log sum_s
 // exp(lse_s - M), out = sum_s exp(lse_s - lse) o_s.  Whole workgroup (256
@@ -304,7 +287,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     const int n_tiles = t1 > t0 ? (t1 - t0 + TILE - 1) / TILE : 0;
     const int32_t *trow = p.page_table + (int64_t)seq * p.max_pages;
     int n_regen = 0;
-    if constexpr (MODE == MODE_REGEN) n_regen = row_ok ? p.regen_pages[seq] : 0;
+    if constexpr (MODE == MODE_REGEN) {
+        n_regen = row_ok ? p.regen_pages[seq] : 0;
+        if (n_regen < 0 || n_regen > p.max_regen) {  // outside the host bound: fail loudly
+            bad = true;
+            n_regen = 0;
+        }
+    }
 
     for (int tile = wave; tile < n_tiles; tile += kWaves) {
         const int tok0 = t0 + tile * TILE + r * U;  // first token of this row-slot
@@ -437,33 +426,22 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
             }
         }
     }
-    if (final_here) return;
-
-    // Split-K merge inside the kernel: the last workgroup to finish a
-    // (row, kv head) merges all of its splits.  The merge reads the splits in
-    // index order, so the result does not depend on which workgroup is last.
-    __shared__ int s_last;
-    __threadfence();  // release this split's partial to the whole device
-    __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = arrive_last(p.counters + (int64_t)row * p.num_kv_heads + g, p.epoch, nsplit);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();  // acquire the other splits' partials
-#pragma unroll 1
-    for (int h = 0; h < G; ++h) {
-        const int64_t orow = (int64_t)row * p.num_heads + g * G + h;
-        merge_row(p.part_lse + orow * p.max_splits, 1, p.part_o + orow * p.max_splits * D, D,
-                  nsplit, D, p.out + orow * D, p.lse + orow);
-    }
 }
 
-// Public split merge: one workgroup per row.
+// Split merge: one workgroup per merged row.  With fixed_splits == 0 the
+// number of splits of a row follows from its visible keys (decode path).
 __global__ __launch_bounds__(256) void fold_kernel(const FoldParams f) {
     const int idx = blockIdx.x;
     if (idx >= f.rows) return;
+    int nsplit = f.fixed_splits;
+    if (nsplit <= 0) {
+        int seq, vis;
+        map_row(f.map, idx / f.num_heads, seq, vis);
+        nsplit = splits_of(vis, f.split_tokens);
+        if (nsplit == 1) return;  // written directly by the attention kernel
+    }
     merge_row(f.part_lse + (int64_t)idx * f.l_row_stride, f.l_split_stride,
-              f.part_o + (int64_t)idx * f.o_row_stride, f.o_split_stride, f.fixed_splits,
+              f.part_o + (int64_t)idx * f.o_row_stride, f.o_split_stride, nsplit,
               f.head_dim, f.out + (int64_t)idx * f.head_dim, f.lse + idx);
 }
 

@@ -36,8 +36,6 @@ struct DecodeParams {
     float *out;               // [total_q][H][D]  (written directly if direct != 0)
     float *lse;               // [total_q][H]
     int32_t direct;
-    unsigned long long *counters;  // [total_q * Hkv] split arrival counters
-    uint32_t epoch;                // this call's tag for the counters (never 0)
     // tiered pools
     const int8_t *i8_k, *i8_v;
     const float *i8_ks, *i8_vs;
@@ -48,6 +46,7 @@ struct DecodeParams {
     uint64_t seed;
     uint32_t layer;
     const int32_t *regen_pages;  // [num_seqs]
+    int32_t max_regen;           // host bound on regen_pages[s]
 };
 
 struct FoldParams {

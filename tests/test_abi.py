@@ -91,9 +91,7 @@ def test_workspace_size_of_a_valid_call():
     # max_context_len 1000 over 4 rows x 8 kv heads: splits of 256 tokens,
     # ceil(1000 / 256) = 4 splits per (row, head)
     parts = 4 * 32 * 4
-    counters = 4 * 8 * 8  # one 64-bit arrival counter per (row, kv head)
-    assert n == ((parts * 128 * 4 + 255) // 256 * 256) + ((parts * 4 + 255) // 256 * 256) + \
-        ((counters + 255) // 256 * 256)
+    assert n == ((parts * 128 * 4 + 255) // 256 * 256) + ((parts * 4 + 255) // 256 * 256)
     st, n1 = _ws(_args(split_tokens=1024))
     assert st == atlas.OK and n1 == 0  # one split: results are written directly
 

@@ -367,3 +367,60 @@ def test_fold_partials_matches_oracle_merge(gpu):
                                                .astype(np.float32)).to(gpu), out1, lse1)
     torch.cuda.synchronize()
     assert np.array_equal(out1.cpu().numpy(), po[0])
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill on the matrix cores (bf16 / f16, head_dim 128)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (8, 4), (8, 2), (16, 2)])
+def test_mfma_prefill_shapes(gpu, kv, H, Hkv):
+    w = synth.build(dict(num_seqs=3, context_lens=[300, 77, 1500], query_lens=[300, 20, 133],
+                         num_heads=H, num_kv_heads=Hkv, head_dim=128, page_tokens=16,
+                         kv_dtype=kv), device=gpu, seed=H * 10 + Hkv, name=f"mfma-{kv}-{H}/{Hkv}")
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+@pytest.mark.parametrize("P", [16, 64, 256])
+def test_mfma_prefill_regen_page_sizes(gpu, P):
+    w = synth.build(dict(num_seqs=2, context_lens=[2000, 900], query_lens=[257, 64],
+                         num_heads=16, num_kv_heads=2, head_dim=128, page_tokens=P,
+                         kv_dtype="bf16", regen=dict(seed=5, layer=2, fraction=0.75)),
+                    device=gpu, seed=P, name=f"mfma-regen-P{P}")
+    out, lse = run(w)
+    check(w, out, lse)
+
+
+def test_mfma_prefill_page_size_and_placement_do_not_change_bits(gpu):
+    w = synth.build(dict(num_seqs=2, context_lens=[1111, 700], query_lens=[150, 700],
+                         num_heads=16, num_kv_heads=4, head_dim=128, page_tokens=16,
+                         kv_dtype="bf16"), device=gpu, seed=77, name="mfma-pagesize")
+    o0, l0 = run(w)
+    check(w, o0, l0)
+    for P, seed in ((32, 1), (64, 2), (256, 3)):
+        w2 = relayout(w, P, seed, spare_blocks=3)
+        w2.query_lens = w.query_lens
+        o2, l2 = run(w2)
+        assert np.array_equal(o0.view(np.uint32), o2.view(np.uint32)), P
+        assert np.array_equal(l0.view(np.uint32), l2.view(np.uint32)), P
+
+
+def test_config5_regenerated_equals_resident_bitwise(gpu):
+    # CFR-Atlas contract on the prefill path: 75 % regenerated vs all pages
+    # resident (filled by the regenerator) give identical bits.
+    kw = dict(context_lens=4096, query_lens=512, num_heads=16, num_kv_heads=2)
+    w_regen = synth.config(5, device=gpu, **kw)
+    w_res = synth.config(5, device=gpu, regen=dict(seed=42, layer=0, fraction=0.0), **kw)
+    o1, l1 = run(w_regen)
+    o2, l2 = run(w_res)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+    check(w_regen, o1, l1, rows=[0, 100, 511])
+
+
+def test_config5_full_sampled(gpu):
+    w = synth.config(5, device=gpu)
+    out, lse = run(w)
+    check(w, out, lse, rows=[0, 1, 777, 1500, 2047], heads=[0, 13, 40, 63])
