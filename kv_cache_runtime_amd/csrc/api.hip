@@ -298,6 +298,14 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
     p.total_q = a->total_q;
     p.max_query_len = a->max_query_len;
     p.q_blocks = plan.q_blocks;
+    {
+        // division by page_tokens as a multiply-high (valid for keys < 2^31)
+        uint32_t sh = 0;
+        while ((1u << sh) < (uint32_t)a->page_tokens) ++sh;
+        p.p_shift = sh;
+        p.p_magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << sh) - a->page_tokens)) /
+                               a->page_tokens + 1);
+    }
     p.scale_log2 = a->scale * 1.4426950408889634f;
     p.out = a->out;
     p.lse = a->lse;

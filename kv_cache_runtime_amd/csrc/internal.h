@@ -78,6 +78,7 @@ struct PrefillParams {
     int32_t num_heads, num_kv_heads, page_tokens, max_pages, num_blocks, total_q;
     int32_t max_query_len;
     int32_t q_blocks;         // query tiles per sequence (grid)
+    uint32_t p_magic, p_shift;  // key / page_tokens == (umulhi(key, p_magic) + key) >> p_shift
     float scale_log2;
     float *out;
     float *lse;

@@ -39,6 +39,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;              // head_dim
 constexpr int kTile = 64;            // keys per tile
@@ -57,54 +58,42 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
     }
 }
 
-// Round two finite f32 values to f16 (nearest even) and pack them, `lo` in
-// the low half.  Also returns the rounded values.
-__device__ __forceinline__ uint32_t pack_f16(float lo, float hi, float &rlo, float &rhi) {
-    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    rlo = (float)a;
-    rhi = (float)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 // Two packed bf16 values -> two packed f16 values (exact for magnitudes in
 // the f16 normal range; values above 65504 become inf and poison the row).
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-    const _Float16 a = (_Float16)__uint_as_float(w << 16);
-    const _Float16 b = (_Float16)__uint_as_float(w & 0xFFFF0000u);
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f16x2_t h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xFFFF0000u)};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
-// Address of K or V row `key` of (seq, kv head g): a regenerated page in the
-// workspace copy, or a resident page through the page table.  Sets `bad` for
-// a block id outside the pool (the row is then read from block 0).
-__device__ __forceinline__ const uint16_t *kv_row(const PrefillParams &p, const void *pool,
-                                                  const void *regen, int seq, int g, int key,
-                                                  int n_regen, bool &bad) {
+// Base of K or V rows [key, key + 4) of (seq, kv head g) (four consecutive
+// keys never straddle a page since page_tokens is a multiple of 16): a
+// regenerated page in the workspace copy, or a resident page through the page
+// table.  Sets `bad` for a block id outside the pool (rows of block 0 are
+// read instead).
+__device__ __forceinline__ int64_t kv_row_index(const PrefillParams &p, int seq, int g, int key,
+                                                int n_regen, bool &in_regen, bool &bad) {
     const int P = p.page_tokens;
-    const int lp = key / P, row = key - lp * P;
-    int64_t blk_row;
-    const uint16_t *base;
-    if (lp < n_regen) {
-        blk_row = (((int64_t)seq * p.max_regen + lp) * p.num_kv_heads + g) * P + row;
-        base = reinterpret_cast<const uint16_t *>(regen);
-    } else {
-        int blk = p.page_table[(int64_t)seq * p.max_pages + lp];
-        if (blk < 0 || blk >= p.num_blocks) {
-            bad = true;
-            blk = 0;
-        }
-        blk_row = ((int64_t)blk * p.num_kv_heads + g) * P + row;
-        base = reinterpret_cast<const uint16_t *>(pool);
+    const uint32_t lp = (__umulhi((uint32_t)key, p.p_magic) + (uint32_t)key) >> p.p_shift;
+    const int row = key - (int)lp * P;
+    in_regen = (int)lp < n_regen;
+    if (in_regen) return (((int64_t)seq * p.max_regen + lp) * p.num_kv_heads + g) * P + row;
+    int blk = p.page_table[(int64_t)seq * p.max_pages + lp];
+    if (blk < 0 || blk >= p.num_blocks) {
+        bad = true;
+        blk = 0;
     }
-    return base + blk_row * kD;
+    return ((int64_t)blk * p.num_kv_heads + g) * P + row;
 }
 
 template <int KV, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
     constexpr int kPosWave = 32 / G;       // positions per wave (32 rows)
     constexpr int kPosWg = 4 * kPosWave;   // positions per workgroup
+    // Lazy rescale: the reference max of a row moves only when a tile's max
+    // exceeds it by more than 2^8, so probabilities (scaled by 2^7) stay
+    // below 2^15 and fit f16.
+    constexpr float kSlack = 8.0f;
+    constexpr float kPScale = 7.0f;
     const float kNegInf = -__builtin_inff();
 
     __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * kKStride];
@@ -136,6 +125,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const int t_last = min(n_q - 1, t_base + kPosWg - 1);
     const int key_limit = ctx_ok ? ctx - n_q + t_last + 1 : 0;
     const int wave_min_pos = ctx - n_q + t_base + wave * kPosWave;
+    const bool wave_rows_ok = __all(row_ok);
     int n_regen = 0;
     bool regen_bad = false;
     if (p.regen_pages != nullptr && ctx_ok) {
@@ -161,38 +151,38 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[b][j] = 0.0f;
-    float m = kNegInf, l = 0.0f;
+    float m_ref = kNegInf, l = 0.0f;
     bool bad = false;
 
-    // cooperative staging: K as 16-byte chunks (key = chunk / 16, dims 8 * (chunk % 16));
-    // V as 4 consecutive keys x 8 dims per thread
+    // cooperative staging: thread (kg, dc) moves keys 4 kg .. 4 kg + 3, dims
+    // 8 dc .. 8 dc + 7 of both K and V (one page lookup per thread and tile)
     const int dc = tid & 15;
     const int kg = tid >> 4;
     uint4 kreg[4], vreg[4];
     auto fetch = [&](int k0) {
+        const int key = k0 + 4 * kg;
+        if (key < key_limit) {
+            bool in_regen;
+            const int64_t row = kv_row_index(p, seq, g, key, n_regen, in_regen, bad);
+            const uint16_t *kb = reinterpret_cast<const uint16_t *>(in_regen ? p.regen_k : p.k_pool) +
+                                 row * kD + 8 * dc;
+            const uint16_t *vb = reinterpret_cast<const uint16_t *>(in_regen ? p.regen_v : p.v_pool) +
+                                 row * kD + 8 * dc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = k0 + ((tid + 256 * i) >> 4);
-            kreg[i] = make_uint4(0, 0, 0, 0);
-            if (key < key_limit)
-                kreg[i] = *reinterpret_cast<const uint4 *>(
-                    kv_row(p, p.k_pool, p.regen_k, seq, g, key, n_regen, bad) + 8 * dc);
-        }
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = key + i < key_limit;
+                kreg[i] = ok ? *reinterpret_cast<const uint4 *>(kb + i * kD) : make_uint4(0, 0, 0, 0);
+                vreg[i] = ok ? *reinterpret_cast<const uint4 *>(vb + i * kD) : make_uint4(0, 0, 0, 0);
+            }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 4 * kg + i;
-            vreg[i] = make_uint4(0, 0, 0, 0);
-            if (key < key_limit)
-                vreg[i] = *reinterpret_cast<const uint4 *>(
-                    kv_row(p, p.v_pool, p.regen_v, seq, g, key, n_regen, bad) + 8 * dc);
+            for (int i = 0; i < 4; ++i) kreg[i] = vreg[i] = make_uint4(0, 0, 0, 0);
         }
     };
     auto stage = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kl = (tid + 256 * i) >> 4;
-            *reinterpret_cast<uint4 *>(&sK[kl * kKStride + 8 * dc]) = kreg[i];
-        }
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(&sK[(4 * kg + i) * kKStride + 8 * dc]) = kreg[i];
         // transpose V (as f16): dims 8 dc + e, keys 4 kg .. 4 kg + 3
         if constexpr (KV == KV_BF16) {
 #pragma unroll
@@ -228,73 +218,80 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         __syncthreads();
         if (tile + 1 < n_tiles) fetch(k0 + kTile);  // in flight during the math below
 
-        // S^T for keys k0 .. k0 + 63 (two 32-key blocks)
+        // S^T for keys k0 .. k0 + 63 (two 32-key blocks), unscaled q.k
         f32x16_t s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
                 const uint4 a = *reinterpret_cast<const uint4 *>(
                     &sK[(32 * kb + r) * kKStride + 16 * ks + 8 * half]);
                 s[kb] = mfma32<KV>(a, qf[ks], s[kb]);
             }
         }
 
-        // scale into the log2 domain, causal mask, tile max
-        const bool need_mask = !row_ok || (k0 + kTile - 1 > wave_min_pos);
-        float mt = kNegInf;
+        // causal mask only on tiles that reach past some row's position
+        if (!wave_rows_ok || k0 + kTile - 1 > wave_min_pos) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float x = s[kb][j] * p.scale_log2;
-                if (need_mask) {
+                for (int j = 0; j < 16; ++j) {
                     const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * half + (j & 3);
-                    x = (row_ok && key <= pos) ? x : kNegInf;
+                    s[kb][j] = (row_ok && key <= pos) ? s[kb][j] : kNegInf;
                 }
-                s[kb][j] = x;
-                mt = fmaxf(mt, x);
             }
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m, mt);
-        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        m = m_new;
-        l *= alpha;
+        float mraw = kNegInf;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
+            for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, s[kb][j]);
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+        const float mt = mraw * p.scale_log2;  // scale > 0 keeps the order
 
-        // P^T operands (f16, scaled by 2^15 so that small weights stay
-        // normal): PV step st covers keys 16 st .. 16 st + 15 of the tile
+        const bool move = mt > m_ref + kSlack;  // also true on the first finite tile
+        if (__any(move)) {
+            const float m_new = move ? mt : m_ref;
+            const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+            m_ref = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
+        }
+
+        // P^T operands (f16, p * 2^7 relative to the reference max): PV step
+        // st covers keys 16 st .. 16 st + 15 of the tile
+        const float m_off = (m_ref == kNegInf) ? 0.0f : m_ref - kPScale;
         uint4 pb[4];
-        const float m_off = m_use - 15.0f;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int kb = st >> 1, j0 = 8 * (st & 1);
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float r0, r1;
-                w[i] = pack_f16(__builtin_amdgcn_exp2f(s[kb][j0 + 2 * i] - m_off),
-                                __builtin_amdgcn_exp2f(s[kb][j0 + 2 * i + 1] - m_off), r0, r1);
-                l += r0 + r1;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][j0 + 2 * i], p.scale_log2, -m_off));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][j0 + 2 * i + 1], p.scale_log2, -m_off));
+                l += p0 + p1;
+                const f16x2_t h = {(_Float16)p0, (_Float16)p1};
+                w[i] = __builtin_bit_cast(uint32_t, h);
             }
             pb[st] = make_uint4(w[0], w[1], w[2], w[3]);
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T (consecutive MFMAs use different accumulators)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint16_t *vrow = &sV[(32 * b + r) * kVStride + 4 * half];
+        for (int st = 0; st < 4; ++st) {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const uint2 va = *reinterpret_cast<const uint2 *>(vrow + 16 * st);
-                const uint2 vb = *reinterpret_cast<const uint2 *>(vrow + 16 * st + 8);
+            for (int b = 0; b < 4; ++b) {
+                const uint16_t *vrow = &sV[(32 * b + r) * kVStride + 4 * half + 16 * st];
+                const uint2 va = *reinterpret_cast<const uint2 *>(vrow);
+                const uint2 vb = *reinterpret_cast<const uint2 *>(vrow + 8);
                 o[b] = mfma32<KV_F16>(make_uint4(va.x, va.y, vb.x, vb.y), pb[st], o[b]);
             }
         }
@@ -320,7 +317,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
             }
         }
         if (half == 0) {
-            float lse = l_row > 0.0f ? (m + log2f(l_row) - 15.0f) * kLn2 : kNegInf;
+            const float m_off = (m_ref == kNegInf) ? 0.0f : m_ref - kPScale;
+            float lse = l_row > 0.0f ? (m_off + log2f(l_row)) * kLn2 : kNegInf;
             p.lse[orow] = any_bad ? qnan : lse;
         }
     }
