@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run a plain device-to-device copy of this many "
+                         "bytes three times (calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -207,6 +210,14 @@ def main():
     roof["kernel_avg_ms"] = round(kern_avg, 5)
     roof["kernel_median_ms"] = round(kern_ms[K // 2], 5)
     roof["algorithmic_per_launch"] = work["flops"] if prefill else work["kv_bytes"]
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu:

@@ -55,7 +55,8 @@ struct Plan {
     int q_blocks = 0;        // query tiles per sequence (matrix-core prefill)
     size_t part_o_bytes = 0;
     size_t part_lse_bytes = 0;
-    size_t regen_bytes = 0;  // one K and one V copy of the regenerated pages
+    size_t regen_bytes = 0;  // K copy of the regenerated pages (matrix-core prefill)
+    size_t vt_bytes = 0;     // transposed f16 V of every page (matrix-core prefill)
     size_t total = 0;
 };
 
@@ -184,12 +185,16 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
         }
     }
     if (plan->mfma) {
-        plan->q_blocks = (a->max_query_len + 128 / group - 1) / (128 / group);
+        // transposed f16 copy of every page's V, written once per call
+        plan->vt_bytes = align_up((size_t)a->num_seqs * a->max_pages_per_seq * a->num_kv_heads *
+                                  a->page_tokens * a->head_dim * 2);
+        const int pos_per_block = 4 * 32 * kPrefillHalves / group;
+        plan->q_blocks = (a->max_query_len + pos_per_block - 1) / pos_per_block;
         const int64_t blocks = (int64_t)a->num_kv_heads * plan->q_blocks * a->num_seqs;
         if (blocks > INT32_MAX)
             return fail(ATLAS_EUNSUPPORTED, "too many prefill workgroups (%lld)", (long long)blocks);
     }
-    plan->total = plan->part_o_bytes + plan->part_lse_bytes + 2 * plan->regen_bytes;
+    plan->total = plan->part_o_bytes + plan->part_lse_bytes + plan->regen_bytes + plan->vt_bytes;
     return ok();
 }
 
@@ -310,10 +315,10 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
     p.out = a->out;
     p.lse = a->lse;
     hipError_t e;
+    char *ws = reinterpret_cast<char *>(a->workspace);
+    p.vt = ws + plan.regen_bytes;
     if (rg) {
-        char *ws = reinterpret_cast<char *>(a->workspace);
         p.regen_k = ws;
-        p.regen_v = ws + plan.regen_bytes;
         p.regen_pages = rg->regen_pages;
         p.max_regen = rg->max_regen_pages;
         if (rg->max_regen_pages > 0) {
@@ -329,11 +334,31 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
             r.n = a->num_seqs * rg->max_regen_pages;
             r.num_blocks = r.n;
             r.kv_f32 = 0;
-            r.k_dst = const_cast<void *>(p.regen_k);
-            r.v_dst = const_cast<void *>(p.regen_v);
+            r.k_dst = ws;
+            r.vt_dst = const_cast<void *>(p.vt);
+            r.vt_pages_per_seq = a->max_pages_per_seq;
             e = launch_regen_fill(r, stream);
             if (e != hipSuccess) return device_status(e, "regenerate launch");
         }
+    }
+    {
+        VtCopyParams v;
+        std::memset(&v, 0, sizeof(v));
+        v.v_pool = a->v_pool;
+        v.v_bf16 = a->kv_dtype == ATLAS_BF16;
+        v.page_table = a->page_table;
+        v.context_lens = a->context_lens;
+        v.regen_pages = rg ? rg->regen_pages : nullptr;
+        v.num_seqs = a->num_seqs;
+        v.num_kv_heads = a->num_kv_heads;
+        v.page_tokens = a->page_tokens;
+        v.max_pages = a->max_pages_per_seq;
+        v.num_blocks = a->num_blocks;
+        v.max_context_len = a->max_context_len;
+        v.max_regen = rg ? rg->max_regen_pages : 0;
+        v.vt = const_cast<void *>(p.vt);
+        e = launch_vt_copy(v, stream);
+        if (e != hipSuccess) return device_status(e, "V transpose launch");
     }
     e = mark(a, 0, stream);
     if (e != hipSuccess) return device_status(e, "profile event record");

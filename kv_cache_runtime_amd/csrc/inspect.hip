@@ -40,16 +40,19 @@ __global__ __launch_bounds__(128) void gather_kernel(const char *k_pool, const c
 }
 
 // One workgroup per (page entry, kv head); each thread writes pairs of
-// consecutive head_dim elements (one 32-bit bf16x2 or two f32 stores).
+// consecutive elements (one 32-bit bf16x2 / f16x2 or two f32 stores).  With
+// vt_dst set, V is written transposed ([D][P]) as f16 -- every regenerated
+// value is a multiple of 2^-23 in [-1, 1] with at most 8 significant bits, so
+// f16 holds it exactly.
 __global__ __launch_bounds__(256) void regen_fill_kernel(const RegenFillParams r) {
     const int i = blockIdx.x / r.num_kv_heads;
     const int g = blockIdx.x % r.num_kv_heads;
     if (i >= r.n) return;
-    int lp, blk;
+    int lp, blk, seq = 0;
     if (r.regen_pages != nullptr) {
         // workspace copy: block i holds logical page i % pages_per_seq of
         // sequence i / pages_per_seq, if that page is regenerated
-        const int seq = i / r.pages_per_seq;
+        seq = i / r.pages_per_seq;
         lp = i % r.pages_per_seq;
         if (lp >= r.regen_pages[seq]) return;
         blk = i;
@@ -65,20 +68,99 @@ __global__ __launch_bounds__(256) void regen_fill_kernel(const RegenFillParams r
         const int e = 2 * t;
         const int row = e / D, dim = e % D;
         const int tok = lp * P + row;
-        uint32_t k0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 0));
-        uint32_t k1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 0));
-        uint32_t v0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1));
-        uint32_t v1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 1));
+        const uint32_t k0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 0));
+        const uint32_t k1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 0));
         if (r.kv_f32) {
             float2 kk = make_float2(__uint_as_float(k0 << 16), __uint_as_float(k1 << 16));
-            float2 vv = make_float2(__uint_as_float(v0 << 16), __uint_as_float(v1 << 16));
             reinterpret_cast<float2 *>(reinterpret_cast<float *>(r.k_dst) + base)[t] = kk;
-            reinterpret_cast<float2 *>(reinterpret_cast<float *>(r.v_dst) + base)[t] = vv;
         } else {
             reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.k_dst) + base)[t] =
                 k0 | (k1 << 16);
-            reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.v_dst) + base)[t] =
-                v0 | (v1 << 16);
+        }
+        if (r.vt_dst == nullptr) {
+            const uint32_t v0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1));
+            const uint32_t v1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 1));
+            if (r.kv_f32) {
+                float2 vv = make_float2(__uint_as_float(v0 << 16), __uint_as_float(v1 << 16));
+                reinterpret_cast<float2 *>(reinterpret_cast<float *>(r.v_dst) + base)[t] = vv;
+            } else {
+                reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.v_dst) + base)[t] =
+                    v0 | (v1 << 16);
+            }
+        }
+    }
+    if (r.vt_dst != nullptr) {
+        // V^T: element pair (dim, rows row, row + 1)
+        const int64_t vbase =
+            (((int64_t)seq * r.vt_pages_per_seq + lp) * r.num_kv_heads + g) * (int64_t)D * P;
+        for (int t = threadIdx.x; t < pairs; t += blockDim.x) {
+            const int e = 2 * t;
+            const int dim = e / P, row = e % P;
+            const int tok = lp * P + row;
+            const float v0 = __uint_as_float(
+                regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1)) << 16);
+            const float v1 = __uint_as_float(
+                regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok + 1, dim, 1)) << 16);
+            typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+            const f16x2_t h = {(_Float16)v0, (_Float16)v1};
+            reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.vt_dst) + vbase)[t] =
+                __builtin_bit_cast(uint32_t, h);
+        }
+    }
+}
+
+// Transposed f16 copy of resident V pages: one workgroup per (sequence,
+// logical page, kv head), 64 rows at a time through LDS.  Rows past the
+// context end are written as zeros (a page's tail may hold anything), and a
+// block id outside the pool writes NaN so the rows that read it fail loudly.
+__global__ __launch_bounds__(256) void vt_copy_kernel(const VtCopyParams v) {
+    constexpr int D = 128;
+    constexpr int kRows = 64;
+    __shared__ uint16_t tile[kRows][D + 2];
+    const int g = blockIdx.x % v.num_kv_heads;
+    const int rest = blockIdx.x / v.num_kv_heads;
+    const int lp = rest % v.max_pages;
+    const int seq = rest / v.max_pages;
+    const int P = v.page_tokens;
+    const int ctx = v.context_lens[seq];
+    if (ctx < 0 || ctx > v.max_context_len || ctx > v.max_pages * P) return;
+    if (lp * P >= ctx) return;
+    if (v.regen_pages != nullptr) {
+        const int nr = v.regen_pages[seq];
+        if (nr >= 0 && nr <= v.max_regen && lp < nr) return;  // regenerated page
+    }
+    const int blk = v.page_table[(int64_t)seq * v.max_pages + lp];
+    const bool ok = blk >= 0 && blk < v.num_blocks;
+    const uint16_t *src = reinterpret_cast<const uint16_t *>(v.v_pool) +
+                          (((int64_t)(ok ? blk : 0) * v.num_kv_heads + g) * P) * D;
+    uint16_t *dst = reinterpret_cast<uint16_t *>(v.vt) +
+                    (((int64_t)seq * v.max_pages + lp) * v.num_kv_heads + g) * (int64_t)D * P;
+    const int valid = min(P, ctx - lp * P);
+    const uint16_t qnan = 0x7E00u;
+    for (int r0 = 0; r0 < P; r0 += kRows) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < kRows * D / 2; e += blockDim.x) {
+            const int row = (2 * e) / D, dim = (2 * e) % D;
+            uint32_t w = 0;
+            if (r0 + row < valid) {
+                w = *reinterpret_cast<const uint32_t *>(src + (int64_t)(r0 + row) * D + dim);
+                if (v.v_bf16) {
+                    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+                    const f16x2_t h = {(_Float16)__uint_as_float(w << 16),
+                                       (_Float16)__uint_as_float(w & 0xFFFF0000u)};
+                    w = __builtin_bit_cast(uint32_t, h);
+                }
+                if (!ok) w = qnan | ((uint32_t)qnan << 16);
+            }
+            tile[row][dim] = (uint16_t)w;
+            tile[row][dim + 1] = (uint16_t)(w >> 16);
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < kRows * D / 2; e += blockDim.x) {
+            const int dim = (2 * e) / kRows, row = (2 * e) % kRows;
+            if (r0 + row >= P) continue;  // pages shorter than the staging tile
+            const uint32_t w = (uint32_t)tile[row][dim] | ((uint32_t)tile[row + 1][dim] << 16);
+            *reinterpret_cast<uint32_t *>(dst + (int64_t)dim * P + r0 + row) = w;
         }
     }
 }
@@ -139,6 +221,13 @@ hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream) {
     const int64_t blocks = (int64_t)r.n * r.num_kv_heads;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(regen_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_vt_copy(const VtCopyParams &v, hipStream_t stream) {
+    const int64_t blocks = (int64_t)v.num_seqs * v.max_pages * v.num_kv_heads;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(vt_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, v);
     return hipGetLastError();
 }
 

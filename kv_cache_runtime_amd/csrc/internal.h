@@ -71,8 +71,8 @@ struct PrefillParams {
     const void *k_pool;
     const void *v_pool;
     const int32_t *page_table;
-    const void *regen_k;      // [num_seqs][max_regen][Hkv][P][D] regenerated pages, or null
-    const void *regen_v;
+    const void *regen_k;      // [num_seqs][max_regen][Hkv][P][D] regenerated K pages, or null
+    const void *vt;           // [num_seqs][max_pages][Hkv][D][P] f16: V of every page, transposed
     const int32_t *regen_pages;
     int32_t max_regen;
     int32_t num_heads, num_kv_heads, page_tokens, max_pages, num_blocks, total_q;
@@ -97,6 +97,21 @@ struct RegenFillParams {
     int32_t kv_f32;                // 1: write f32 values, 0: bf16
     void *k_dst;
     void *v_dst;
+    void *vt_dst;                  // if set: V goes here transposed, as f16
+                                   // [seq][vt_pages_per_seq][Hkv][D][P], not to v_dst
+    int32_t vt_pages_per_seq;
+};
+
+// Transposed f16 copy of the resident V pages of a chunked prefill.
+struct VtCopyParams {
+    const void *v_pool;            // [num_blocks][Hkv][P][D] bf16 or f16
+    int32_t v_bf16;
+    const int32_t *page_table;
+    const int32_t *context_lens;
+    const int32_t *regen_pages;    // pages below this count are skipped (regenerated), or null
+    int32_t num_seqs, num_kv_heads, page_tokens, max_pages, num_blocks, max_context_len;
+    int32_t max_regen;
+    void *vt;                      // [num_seqs][max_pages][Hkv][D][P] f16
 };
 
 // Launchers (defined next to their kernels).  Each returns the HIP error of
@@ -104,8 +119,14 @@ struct RegenFillParams {
 hipError_t launch_decode(const DecodeParams &p, int kv_type, int head_dim, int group,
                          int mode, hipStream_t stream);
 hipError_t launch_fold(const FoldParams &f, hipStream_t stream);
+// 32-row halves per wave of the matrix-core prefill kernel (1 or 2).
+#ifndef ATLAS_PREFILL_HALVES
+#define ATLAS_PREFILL_HALVES 1
+#endif
+constexpr int kPrefillHalves = ATLAS_PREFILL_HALVES;
 hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream);
 hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream);
+hipError_t launch_vt_copy(const VtCopyParams &v, hipStream_t stream);
 hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
                          int32_t num_kv_heads, int32_t head_dim, int32_t page_tokens,
                          int32_t num_blocks, int32_t elem_bytes, int32_t num_tokens,
