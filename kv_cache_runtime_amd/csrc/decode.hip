@@ -38,6 +38,7 @@ namespace atlas {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kStagedPages = 512;  // page-table entries staged in LDS per split
 
 template <int KV>
 constexpr int hot_bytes() { return KV == KV_F32 ? 4 : 2; }
@@ -250,8 +251,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     const int r = lane >> 4;
     const int c = lane & 15;
 
-    const int split = blockIdx.x % p.max_splits;
-    const int rg = blockIdx.x / p.max_splits;
+    // split index slowest: consecutive workgroups (which the dispatcher
+    // spreads over the XCDs) take the same split of different (row, kv head)
+    // pairs, so the mostly empty high splits of short contexts neither pile
+    // onto a subset of XCDs nor interleave with the busy ones
+    const int pairs = p.total_q * p.num_kv_heads;
+    const int split = blockIdx.x / pairs;
+    const int rg = blockIdx.x - split * pairs;
     const int g = rg % p.num_kv_heads;
     const int row = rg / p.num_kv_heads;
 
@@ -286,6 +292,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 
     const int n_tiles = t1 > t0 ? (t1 - t0 + TILE - 1) / TILE : 0;
     const int32_t *trow = p.page_table + (int64_t)seq * p.max_pages;
+    // page-table entries of this split, staged once (a dependent global load
+    // per tile would add a memory round trip before every K/V load)
+    __shared__ int32_t s_pages[kStagedPages];
+    const int lp_first = t0 / p.page_tokens;
+    const int lp_count = t1 > t0 ? (t1 - 1) / p.page_tokens - lp_first + 1 : 0;
+    const bool staged = lp_count <= kStagedPages;
+    if (staged)
+        for (int i = threadIdx.x; i < lp_count; i += 256) s_pages[i] = trow[lp_first + i];
+    __syncthreads();
     int n_regen = 0;
     if constexpr (MODE == MODE_REGEN) {
         n_regen = row_ok ? p.regen_pages[seq] : 0;
@@ -303,7 +318,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
         if (live) {
             const int lp = tok0 / p.page_tokens;
             uint32_t entry = 0;
-            if (!(MODE == MODE_REGEN && lp < n_regen)) entry = (uint32_t)trow[lp];
+            if (!(MODE == MODE_REGEN && lp < n_regen))
+                entry = (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]);
             if (!load_slot<KV, D, U, MODE>(p, entry, g, tok0, lp, n_regen, c, kf, vf, sd)) {
                 bad = true;
                 live = false;

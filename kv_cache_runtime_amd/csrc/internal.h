@@ -119,6 +119,10 @@ struct VtCopyParams {
 hipError_t launch_decode(const DecodeParams &p, int kv_type, int head_dim, int group,
                          int mode, hipStream_t stream);
 hipError_t launch_fold(const FoldParams &f, hipStream_t stream);
+// Matrix-core decode (QK^T on MFMA) for 16-bit and tiered pages.
+bool decode_mfma_supported(int kv_type, int head_dim, int group, int mode);
+hipError_t launch_decode_mfma(const DecodeParams &p, int kv_type, int group, int mode,
+                              hipStream_t stream);
 // 32-row halves per wave of the matrix-core prefill kernel (1 or 2).
 #ifndef ATLAS_PREFILL_HALVES
 #define ATLAS_PREFILL_HALVES 1
