@@ -121,6 +121,56 @@ __device__ __forceinline__ bool load_k_chunk(const DecodeParams &p, uint32_t ent
     return false;
 }
 
+// Tiered pages: loads dims 32 r .. 32 r + 31 of K row `row` of a page as the
+// four 16-bit operands kv[ks] = dims 32 r + 8 ks .. + 8 (hot: 64 bytes, int8:
+// 32, int4: 16, each one contiguous run) and returns the page's K scale.
+// Returns false for an invalid page-table entry.
+template <int KV>
+__device__ __forceinline__ bool load_k_row_tiered(const DecodeParams &p, uint32_t entry, int g,
+                                                  int row, int r, uint4 (&kv)[4], float &kscale) {
+    kscale = 1.0f;
+    const uint32_t tier = entry >> 30, slot = entry & ((1u << 30) - 1u);
+    const int P = p.page_tokens;
+    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * P + row;
+    if (tier == 0) {
+        if (slot >= (uint32_t)p.num_blocks) return false;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            reinterpret_cast<const uint16_t *>(p.k_pool) + r0 * kD + 32 * r);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kv[ks] = src[ks];
+        return true;
+    }
+    if (tier == 1) {
+        if (slot >= (uint32_t)p.n_i8) return false;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.i8_k + r0 * kD + 32 * r);
+        kscale = p.i8_ks[(int64_t)slot * p.num_kv_heads + g];
+        const uint4 a = src[0], b = src[1];
+        i8x4_to_f16x4(a.x, kv[0].x, kv[0].y);
+        i8x4_to_f16x4(a.y, kv[0].z, kv[0].w);
+        i8x4_to_f16x4(a.z, kv[1].x, kv[1].y);
+        i8x4_to_f16x4(a.w, kv[1].z, kv[1].w);
+        i8x4_to_f16x4(b.x, kv[2].x, kv[2].y);
+        i8x4_to_f16x4(b.y, kv[2].z, kv[2].w);
+        i8x4_to_f16x4(b.z, kv[3].x, kv[3].y);
+        i8x4_to_f16x4(b.w, kv[3].z, kv[3].w);
+        return true;
+    }
+    if (tier == 2) {
+        if (slot >= (uint32_t)p.n_i4) return false;
+        const uint4 w = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + 16 * r);
+        kscale = p.i4_ks[(int64_t)slot * p.num_kv_heads + g];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint32_t o[4];
+            i4x8_to_f16x8(ww[ks], o);
+            kv[ks] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        return true;
+    }
+    return false;
+}
+
 // Loads the raw V words of 16 tokens x 8 dims for this lane's row-slot (hot:
 // 4 words per token, int8: 2, int4: 1), its tier and V scale.  Returns false
 // for an invalid page-table entry.
@@ -204,19 +254,23 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     const int t1 = min(t0 + T, nvis);
 
     // page-table entries of this split, staged once (a dependent global load
-    // per tile would add a memory round trip before every K/V load)
+    // per tile would add a memory round trip before every K/V load); tiered
+    // splits stage them grouped by tier and walk the pages in that order
     __shared__ int32_t s_pages[kStagedPages];
+    __shared__ int16_t s_lp[MODE == MODE_TIERED ? kStagedPages : 1];
     const int32_t *trow = p.page_table + (int64_t)seq * p.max_pages;
     const int P = p.page_tokens;
     const int lp_first = t0 / P;
     const int lp_count = t1 > t0 ? (t1 - 1) / P - lp_first + 1 : 0;
     const bool staged = lp_count <= kStagedPages;
-    if (staged)
-        for (int i = tid; i < lp_count; i += 256) s_pages[i] = trow[lp_first + i];
-    __syncthreads();
-    auto entry_of = [&](int lp) -> uint32_t {
-        return (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]);
-    };
+    const bool by_tier = MODE == MODE_TIERED && staged;
+    if (by_tier) {
+        stage_pages_by_tier(trow + lp_first, lp_count, s_pages, s_lp);
+    } else {
+        if (staged)
+            for (int i = tid; i < lp_count; i += 256) s_pages[i] = trow[lp_first + i];
+        __syncthreads();
+    }
 
     // A operand: query head c (zero for c >= G), dims 32 ks + 8 r .. + 8
     uint4 qf[4];
@@ -224,7 +278,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     for (int ks = 0; ks < 4; ++ks) {
         uint32_t w[4] = {0u, 0u, 0u, 0u};
         if (c < G) {
-            const int64_t q0 = ((int64_t)row * p.num_heads + g * G + c) * kD + 32 * ks + 8 * r;
+            // operand ks, lane row r holds dims 32 ks + 8 r (16-bit pages) or
+            // 32 r + 8 ks (tiered pages, so each lane's K bytes are one run);
+            // a dot product does not depend on how its terms are dealt out
+            const int d0 = MODE == MODE_TIERED ? 32 * r + 8 * ks : 32 * ks + 8 * r;
+            const int64_t q0 = ((int64_t)row * p.num_heads + g * G + c) * kD + d0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float x0 = load_elem(p.q, q0 + 2 * i, p.q_dtype);
@@ -255,46 +313,81 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
     bool bad = !row_ok;
 
-    const int n_tiles = t1 > t0 ? (t1 - t0 + kTileTok - 1) / kTileTok : 0;
+    // positions walked: tokens t0 .. t1 - 1, or (by tier) every token slot of
+    // the split's pages, of which those outside [t0, t1) are masked
+    const int n_pos = by_tier ? lp_count * P : t1 - t0;
+    const int n_tiles = n_pos > 0 ? (n_pos + kTileTok - 1) / kTileTok : 0;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-    for (int tile = wave; tile < n_tiles; tile += kWaves) {
-        const int k0 = t0 + tile * kTileTok;
-        // ---- K: token 16 tg + c of the tile, dims 32 ks + 8 r .. + 8
-        uint4 kb[4][4];
-        float kscale[4];
+    for (int tile = wave_u; tile < n_tiles; tile += kWaves) {
+        // ---- the 16-position groups of the tile: the page size is a
+        // multiple of 16 and tiles start at multiples of 64 positions, so a
+        // group lies in one page; its first token, page-table entry and
+        // liveness are wave-uniform
+        int gtok[4];
+        uint32_t gent[4];
+        bool glive[4];
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-            const int tk = k0 + 16 * tg + c;
-            kscale[tg] = 1.0f;
-            bool ok = tk < t1;
-            if (ok) {
-                const int lp = tk / P;
-                const uint32_t e = entry_of(lp);
+            const int q = tile * kTileTok + 16 * tg;
+            if (by_tier) {
+                const int pi = q / P;
+                glive[tg] = pi < lp_count;
+                const int lp = lp_first + (glive[tg] ? s_lp[pi] : 0);
+                gtok[tg] = lp * P + (q - pi * P);
+                gent[tg] = glive[tg] ? (uint32_t)s_pages[pi] : 0u;
+            } else {
+                gtok[tg] = t0 + q;
+                glive[tg] = gtok[tg] < t1;
+                const int lp = gtok[tg] / P;
+                gent[tg] = glive[tg] ? (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]) : 0u;
+            }
+            gtok[tg] = __builtin_amdgcn_readfirstlane(gtok[tg]);
+            gent[tg] = __builtin_amdgcn_readfirstlane(gent[tg]);
+        }
+        auto in_range = [&](int tok) { return tok >= t0 && tok < t1; };
+
+        // ---- K: token gtok[tg] + c, dims 32 ks + 8 r .. + 8
+        uint4 kb[4][4];
+        float kscale[4];
+        bool kvalid[4];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    ok = ok && load_k_chunk<KV, MODE>(p, e, g, tk - lp * P, 32 * ks + 8 * r,
-                                                      kb[tg][ks], kscale[tg]);
-                if (!ok && tk < t1) bad = true;
+        for (int tg = 0; tg < 4; ++tg) {
+            const int tk = gtok[tg] + c;
+            kscale[tg] = 1.0f;
+            kvalid[tg] = glive[tg] && in_range(tk);
+            bool ok = glive[tg];
+            if (ok) {
+                const int row0 = gtok[tg] % P;
+                if constexpr (MODE == MODE_TIERED) {
+                    ok = load_k_row_tiered<KV>(p, gent[tg], g, row0 + c, r, kb[tg], kscale[tg]);
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        ok = ok && load_k_chunk<KV, MODE>(p, gent[tg], g, row0 + c,
+                                                          32 * ks + 8 * r, kb[tg][ks], kscale[tg]);
+                }
+                if (!ok) {
+                    bad = true;
+                    kvalid[tg] = false;
+                }
             }
             if (!ok) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) kb[tg][ks] = make_uint4(0u, 0u, 0u, 0u);
             }
         }
-        // ---- V rows of this lane's row-slot (in flight during QK)
-        const int v0 = k0 + kSlotTok * r;
-        const bool slot_live = v0 < t1;
+        // ---- V rows of this lane's row-slot r = group r (in flight during QK)
+        const int v0 = r == 0 ? gtok[0] : r == 1 ? gtok[1] : r == 2 ? gtok[2] : gtok[3];
+        const uint32_t vent = r == 0 ? gent[0] : r == 1 ? gent[1] : r == 2 ? gent[2] : gent[3];
+        bool slot_live = r == 0 ? glive[0] : r == 1 ? glive[1] : r == 2 ? glive[2] : glive[3];
         uint4 vr[kSlotTok];
         uint32_t vtier = 0;
         float vscale = 1.0f;
         if (slot_live) {
-            const int lp = v0 / P;
-            if (!load_v_slot<KV, MODE>(p, entry_of(lp), g, v0 - lp * P, c, vr, vtier, vscale)) {
+            if (!load_v_slot<KV, MODE>(p, vent, g, v0 % P, c, vr, vtier, vscale)) {
                 bad = true;
-                vscale = 0.0f;
-                vtier = 0;
-#pragma unroll
-                for (int u = 0; u < kSlotTok; ++u) vr[u] = make_uint4(0u, 0u, 0u, 0u);
+                slot_live = false;
             }
         }
 
@@ -306,9 +399,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) sc[tg] = mfma16<QT>(qf[ks], kb[tg][ks], sc[tg]);
             const float f = kscale[tg] * p.scale_log2;
-            const bool valid = k0 + 16 * tg + c < t1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[tg][i] = valid ? sc[tg][i] * f : kNegInf;
+            for (int i = 0; i < 4; ++i) sc[tg][i] = kvalid[tg] ? sc[tg][i] * f : kNegInf;
         }
 
         // ---- online softmax, one reference max per head (uniform in a row)
@@ -359,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             auto pv = [&](auto widen) {
 #pragma unroll
                 for (int u = 0; u < kSlotTok; ++u) {
-                    const bool valid = v0 + u < t1;
+                    const bool valid = in_range(v0 + u);
                     float pu[G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) pu[h] = sP[wave][kSlotTok * r + u][h] * vscale;

@@ -148,6 +148,53 @@ __device__ __forceinline__ bool map_row(const RowMap &m, int row, int &seq, int 
     return ok;
 }
 
+// Stages the page-table entries lp_first .. lp_first + n - 1 of a split into
+// LDS grouped by tier (entry >> 30: hot, int8, int4, and 3 = invalid), keeping
+// the logical order inside a tier; s_lp receives each staged entry's offset
+// from lp_first.  The ranks come from wave ballots, so the order is fixed
+// (no atomics).  Whole workgroup of 256 threads, n <= 512; ends with a barrier.
+// Folding keys with an online softmax does not depend on their order, so a
+// split may visit its pages in this order: the waves then mostly meet pages of
+// one tier and take one load path.
+__device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, int32_t *s_entry,
+                                                    int16_t *s_lp) {
+    __shared__ int s_cnt[2][4][4];  // chunk, wave, tier
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int32_t e[2];
+    int t[2], rank[2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const int i = ch * 256 + tid;
+        e[ch] = i < n ? trow[i] : 0;
+        t[ch] = i < n ? (int)((uint32_t)e[ch] >> 30) : 4;
+        rank[ch] = 0;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const uint64_t m = __ballot(t[ch] == tt);
+            if (lane == 0) s_cnt[ch][wave][tt] = __popcll(m);
+            if (t[ch] == tt)
+                rank[ch] = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const int i = ch * 256 + tid;
+        if (i >= n) continue;
+        const int tt = t[ch];
+        int pos = rank[ch];
+        for (int c2 = 0; c2 < 2; ++c2)
+            for (int w2 = 0; w2 < 4; ++w2) {
+                for (int u = 0; u < tt; ++u) pos += s_cnt[c2][w2][u];
+                if (c2 < ch || (c2 == ch && w2 < wave)) pos += s_cnt[c2][w2][tt];
+            }
+        s_entry[pos] = e[ch];
+        s_lp[pos] = (int16_t)i;
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ int splits_of(int visible, int split_tokens) {
     const int n = (visible + split_tokens - 1) / split_tokens;
     return n < 1 ? 1 : n;

@@ -162,6 +162,29 @@ def test_regen_decode_rows(gpu):
 # Invariants: determinism, page size, placement, regen vs resident
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("kernel", ["default", "valu"])
+@pytest.mark.parametrize("P,split", [(16, 0), (16, 64), (64, 128), (256, 64), (256, 0)])
+@pytest.mark.parametrize("H,Hkv,hot", [(8, 4, "f16"), (8, 2, "f16"), (16, 2, "f16"),
+                                       (8, 2, "bf16")])
+def test_tiered_page_walk(gpu, monkeypatch, kernel, P, split, H, Hkv, hot):
+    """Tiered splits visit their pages grouped by tier; splits that start
+    inside a page (page 256, split 64) mask the tokens before their start."""
+    if kernel == "valu":
+        monkeypatch.setenv("ATLAS_DECODE_VALU", "1")
+    w = synth.build(dict(num_seqs=4, context_lens=[37, 700, 1500, 2600], num_heads=H,
+                         num_kv_heads=Hkv, head_dim=128, page_tokens=P, q_dtype="bf16",
+                         kv_dtype=hot, placement="permuted",
+                         tiers=dict(hot_tokens=300, p_int8=0.5)),
+                    device=gpu, seed=P + split + H + Hkv, name=f"tiered-P{P}-s{split}-{H}/{Hkv}")
+    counts = w.tiers["counts"]
+    assert counts[1] > 0 and counts[2] > 0
+    o1, l1 = run(w, split_tokens=split)
+    check(w, o1, l1)
+    o2, l2 = run(w, split_tokens=split)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
 def test_determinism_bitwise(gpu):
     w = synth.config(3, device=gpu, num_seqs=6, context_lens=("uniform", 100, 5000))
     o1, l1 = run(w)
