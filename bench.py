@@ -69,6 +69,38 @@ def algorithmic_work(w):
                 regen_elems=regen_elems)
 
 
+def kernel_sources_digest() -> str:
+    """Digest of the HIP sources: HBM byte counts taken with an older build
+    no longer describe the kernels."""
+    import hashlib
+    csrc = os.path.join(ROOT, "kv_cache_runtime_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the main kernel for this workload, from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (each counter scaled
+    by its reading for a copy of known size), or None when the summary was
+    taken with other kernel sources or does not cover the workload."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_digest()
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or "=" not in line:
+                continue
+            fields = dict(kv.split("=", 1) for kv in line.split())
+            if fields.get("workload") == workload and fields.get("sources") == digest:
+                return int(fields["bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(w, work, budget_s: float = 20.0):
     """Time the f64 oracle on a bounded sample of the same workload, running
     independent (sequence, kv head) groups on the host cores."""
@@ -207,8 +239,11 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None}
+    roof["traffic"] = measured_traffic(w.name)
     roof["kernel_avg_ms"] = round(kern_avg, 5)
     roof["kernel_median_ms"] = round(kern_ms[K // 2], 5)
+    roof["kernel_min_ms"] = round(kern_ms[0], 5)
+    roof["kernel_max_ms"] = round(kern_ms[-1], 5)
     roof["algorithmic_per_launch"] = work["flops"] if prefill else work["kv_bytes"]
 
     if args.copy_bytes > 0:

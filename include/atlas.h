@@ -269,6 +269,30 @@ atlas_status atlas_dequant_pages(const atlas_attn_args *args,
                                  const int32_t *entries, int32_t n,
                                  float *k_out, float *v_out);
 
+/*
+ * Debug check of the tables behind a call (the CFR-Atlas README asks that
+ * invalid configurations and page ranges be rejected; attention kernels only
+ * turn a bad entry into NaN rows, this call counts them).  Same arguments as
+ * the attention call it guards: pools != NULL checks a tiered call, regen !=
+ * NULL a regenerated one (not both).  Reads only the visible keys of every
+ * sequence.  report_dev: caller-owned device buffer of 4 uint32 counters,
+ * overwritten:
+ *   [0] page-table entries of visible, non-regenerated pages that name no
+ *       page (slot beyond its pool, tier 3);
+ *   [1] sequences whose context length, query range or regenerated-page
+ *       count is out of bounds;
+ *   [2] non-finite K or V elements among visible tokens of resident pages
+ *       (check_values != 0 only; reads every such element);
+ *   [3] non-finite K or V scales of visible cold pages (check_values only).
+ * Asynchronous on args->stream; if report_host != NULL the counters are also
+ * copied there and the call waits for the stream.  Allocates nothing.
+ */
+atlas_status atlas_validate_tables(const atlas_attn_args *args,
+                                   const atlas_tier_pools *pools,
+                                   const atlas_regen_spec *regen,
+                                   int32_t check_values, uint32_t *report_dev,
+                                   uint32_t *report_host);
+
 #ifdef __cplusplus
 }
 #endif

@@ -90,7 +90,7 @@ EXPORTS = [
     "atlas_abi_version", "atlas_status_string", "atlas_last_error", "atlas_workspace_size",
     "atlas_paged_attention", "atlas_paged_attention_tiered", "atlas_paged_attention_regen",
     "atlas_fold_partials", "atlas_gather_pages", "atlas_regenerate_pages",
-    "atlas_dequant_pages",
+    "atlas_dequant_pages", "atlas_validate_tables",
 ]
 
 _lib = None
@@ -136,6 +136,9 @@ def load(path: str = LIB_PATH):
     L.atlas_dequant_pages.restype = _i32
     L.atlas_dequant_pages.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools), _p,
                                       _i32, _p, _p]
+    L.atlas_validate_tables.restype = _i32
+    L.atlas_validate_tables.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools),
+                                        ctypes.POINTER(RegenSpec), _i32, _p, _p]
     if L.atlas_abi_version() != 1:
         raise RuntimeError("libatlas ABI version mismatch")
     _lib = L
@@ -289,6 +292,22 @@ def atlas_dequant_pages(args: AttnArgs, pools: TierPools, entries, k_out, v_out)
            "atlas_dequant_pages")
 
 
+def atlas_validate_tables(args: AttnArgs, pools=None, regen=None, check_values: bool = False,
+                          report_dev=None):
+    """Counts of invalid entries / lengths / non-finite values / scales (a
+    list of 4 ints); waits for the stream.  report_dev: device uint32-sized
+    buffer of 4 elements (allocated here if None)."""
+    if report_dev is None:
+        report_dev = torch.zeros(4, dtype=torch.int32, device="cuda")
+    host = (ctypes.c_uint32 * 4)()
+    _check(load().atlas_validate_tables(ctypes.byref(args),
+                                        ctypes.byref(pools) if pools is not None else None,
+                                        ctypes.byref(regen) if regen is not None else None,
+                                        1 if check_values else 0, _ptr(report_dev), host),
+           "atlas_validate_tables")
+    return [int(x) for x in host]
+
+
 # ---------------------------------------------------------------------------
 # Convenience: run a synth.Paged problem end to end
 # ---------------------------------------------------------------------------
@@ -351,6 +370,9 @@ class Problem:
         atlas_regenerate_pages(w.regen["seed"], w.regen["layer"], w.num_kv_heads, w.head_dim,
                                w.page_tokens, _NAME_CODE[w.kv_dtype], lp, bl, w.num_blocks,
                                w.k_pool, w.v_pool)
+
+    def validate(self, check_values: bool = False):
+        return atlas_validate_tables(self.args, self.tiers, self.regen, check_values)
 
     def run(self):
         if self.kind == "tiered":

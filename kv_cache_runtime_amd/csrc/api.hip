@@ -572,4 +572,54 @@ atlas_status atlas_dequant_pages(const atlas_attn_args *args, const atlas_tier_p
                          "dequant launch");
 }
 
+atlas_status atlas_validate_tables(const atlas_attn_args *args, const atlas_tier_pools *pools,
+                                   const atlas_regen_spec *regen, int32_t check_values,
+                                   uint32_t *report_dev, uint32_t *report_host) {
+    if (pools && regen) return fail(ATLAS_EINVAL, "pools and regen are exclusive");
+    Plan plan;
+    atlas_status st = check_common(args, pools != nullptr, regen, &plan);
+    if (st != ATLAS_OK) return st;
+    if (!report_dev) return fail(ATLAS_EINVAL, "report_dev is NULL");
+    if (pools && pools->struct_size != sizeof(atlas_tier_pools))
+        return fail(ATLAS_EINVAL, "pools->struct_size mismatch");
+    if (pools && (pools->num_int8 < 0 || pools->num_int4 < 0))
+        return fail(ATLAS_EINVAL, "negative tier pool size");
+    ValidateParams v;
+    std::memset(&v, 0, sizeof(v));
+    v.p = decode_params(args, plan);
+    v.p.part_o = nullptr;
+    v.p.part_lse = nullptr;
+    v.mode = pools ? MODE_TIERED : regen ? MODE_REGEN : MODE_PLAIN;
+    if (pools) {
+        v.p.i8_ks = pools->int8_k_scale;
+        v.p.i8_vs = pools->int8_v_scale;
+        v.p.i4_ks = pools->int4_k_scale;
+        v.p.i4_vs = pools->int4_v_scale;
+        v.p.n_i8 = pools->num_int8;
+        v.p.n_i4 = pools->num_int4;
+        if (check_values && ((v.p.n_i8 > 0 && (!v.p.i8_ks || !v.p.i8_vs)) ||
+                             (v.p.n_i4 > 0 && (!v.p.i4_ks || !v.p.i4_vs))))
+            return fail(ATLAS_EINVAL, "NULL tier scale pointer");
+    }
+    if (regen) {
+        v.p.regen_pages = regen->regen_pages;
+        v.p.max_regen = regen->max_regen_pages;
+    }
+    v.kv_type = args->kv_dtype;
+    v.head_dim = args->head_dim;
+    v.check_values = check_values ? 1 : 0;
+    v.max_query_len = args->max_query_len;
+    v.report = report_dev;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(args->stream);
+    hipError_t e = launch_validate(v, stream);
+    if (e != hipSuccess) return device_status(e, "validate launch");
+    if (report_host) {
+        e = hipMemcpyAsync(report_host, report_dev, 4 * sizeof(uint32_t), hipMemcpyDeviceToHost,
+                           stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return device_status(e, "validate report copy");
+    }
+    return ok();
+}
+
 }  // extern "C"

@@ -205,13 +205,27 @@ __device__ void merge_row(const float *pl, int64_t l_stride, const float *po, in
         __syncthreads();
         const int per = (cn + kWaves - 1) / kWaves;
         const int s0 = wave * per, s1 = min(cn, s0 + per);
-        for (int s = s0; s < s1; ++s) {
-            const float w = s_w[s];
-            const float *row = po + (int64_t)(c0 + s) * o_stride;
+        // batches of 8 partial rows: their loads are all issued before the
+        // first use, so the loop pays one memory latency per batch, not per row
+        constexpr int kBatch = 8;
+        for (int sb = s0; sb < s1; sb += kBatch) {
+            float x[kBatch][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = lane + 64 * i;
-                if (col < D) a[i] = fmaf(w, row[col], a[i]);
+            for (int j = 0; j < kBatch; ++j) {
+                const int s = sb + j;
+                const float *row = po + (int64_t)(c0 + min(s, s1 - 1)) * o_stride;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = lane + 64 * i;
+                    x[j][i] = (col < D) ? row[col] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (sb + j >= s1) break;
+                const float w = s_w[sb + j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = fmaf(w, x[j][i], a[i]);
             }
         }
         __syncthreads();

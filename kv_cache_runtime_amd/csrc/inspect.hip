@@ -202,6 +202,108 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DecodeParams p, int 
     }
 }
 
+
+// ---- debug validation of the tables and pools behind a call --------------
+constexpr int kValidatePages = 64;  // logical pages per workgroup
+
+__global__ void zero_report_kernel(uint32_t *report) {
+    if (threadIdx.x < 4) report[threadIdx.x] = 0u;
+}
+
+__device__ __forceinline__ float elem_as_float(const void *base, int64_t i, int kv_type) {
+    if (kv_type == KV_F32) return reinterpret_cast<const float *>(base)[i];
+    const uint32_t h = reinterpret_cast<const uint16_t *>(base)[i];
+    return kv_type == KV_BF16 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Workgroup (seq, chunk of kValidatePages logical pages).  Counts, over the
+// visible keys of every sequence: entries naming no page, out-of-bounds
+// lengths / query ranges / regenerated-page counts, and (optionally)
+// non-finite resident K/V values and cold-page scales.
+__global__ __launch_bounds__(256) void validate_kernel(const ValidateParams v) {
+    const DecodeParams &p = v.p;
+    const int s = blockIdx.x;
+    const int lp0 = blockIdx.y * kValidatePages;
+    const int P = p.page_tokens;
+    const int64_t max_keys = (int64_t)p.max_pages * P;
+    __shared__ uint32_t s_cnt[4];
+    if (threadIdx.x < 4) s_cnt[threadIdx.x] = 0u;
+    __syncthreads();
+
+    const int ctx_raw = p.rows.context_lens[s];
+    const int ctx = ctx_raw < 0 ? 0 : (int)min((int64_t)ctx_raw, max_keys);
+    int n_regen = 0;
+    if (v.mode == MODE_REGEN && p.regen_pages) {
+        n_regen = p.regen_pages[s];
+        n_regen = n_regen < 0 ? 0 : min(n_regen, p.max_pages);
+    }
+    if (blockIdx.y == 0 && threadIdx.x == 0) {
+        bool bad = ctx_raw < 0 || ctx_raw > p.rows.max_context_len || (int64_t)ctx_raw > max_keys;
+        if (p.rows.query_start) {
+            const int q0 = p.rows.query_start[s], q1 = p.rows.query_start[s + 1];
+            const int n_q = q1 - q0;
+            bad = bad || n_q < 1 || n_q > ctx_raw || n_q > v.max_query_len || q0 < 0 ||
+                  q1 > p.total_q;
+            if (s == 0) bad = bad || q0 != 0;
+            if (s == p.rows.num_seqs - 1) bad = bad || q1 != p.total_q;
+        }
+        if (v.mode == MODE_REGEN && p.regen_pages) {
+            const int r = p.regen_pages[s];
+            bad = bad || r < 0 || r > p.max_regen;
+        }
+        if (bad) s_cnt[1] = 1u;
+    }
+
+    const int n_pages = (ctx + P - 1) / P;
+    const int lp_end = min(n_pages, lp0 + kValidatePages);
+    const int32_t *trow = p.page_table + (int64_t)s * p.max_pages;
+    const int D = v.head_dim;
+    uint32_t bad_entry = 0, bad_val = 0, bad_scale = 0;
+    for (int lp = max(lp0, n_regen); lp < lp_end; ++lp) {
+        const uint32_t e = (uint32_t)trow[lp];
+        uint32_t tier = 0, slot = e;
+        if (v.mode == MODE_TIERED) {
+            tier = e >> 30;
+            slot = e & ((1u << 30) - 1u);
+        }
+        const bool ok = tier == 0   ? slot < (uint32_t)p.num_blocks
+                        : tier == 1 ? slot < (uint32_t)p.n_i8
+                        : tier == 2 ? slot < (uint32_t)p.n_i4
+                                    : false;
+        if (!ok) {
+            if (threadIdx.x == 0) ++bad_entry;
+            continue;
+        }
+        if (!v.check_values) continue;
+        const int rows = min(P, ctx - lp * P);
+        if (tier == 0) {
+            const int64_t n = (int64_t)p.num_kv_heads * rows * D;
+            for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+                const int g = (int)(i / ((int64_t)rows * D));
+                const int64_t rem = i - (int64_t)g * rows * D;
+                const int64_t idx = (((int64_t)slot * p.num_kv_heads + g) * P) * D + rem;
+                const float a = elem_as_float(p.k_pool, idx, v.kv_type);
+                const float b = elem_as_float(p.v_pool, idx, v.kv_type);
+                if (!__builtin_isfinite(a)) ++bad_val;
+                if (!__builtin_isfinite(b)) ++bad_val;
+            }
+        } else {
+            const float *ks = tier == 1 ? p.i8_ks : p.i4_ks;
+            const float *vs = tier == 1 ? p.i8_vs : p.i4_vs;
+            for (int g = threadIdx.x; g < p.num_kv_heads; g += blockDim.x) {
+                const int64_t i = (int64_t)slot * p.num_kv_heads + g;
+                if (!__builtin_isfinite(ks[i])) ++bad_scale;
+                if (!__builtin_isfinite(vs[i])) ++bad_scale;
+            }
+        }
+    }
+    if (bad_entry) atomicAdd(&s_cnt[0], bad_entry);
+    if (bad_val) atomicAdd(&s_cnt[2], bad_val);
+    if (bad_scale) atomicAdd(&s_cnt[3], bad_scale);
+    __syncthreads();
+    if (threadIdx.x < 4 && s_cnt[threadIdx.x]) atomicAdd(&v.report[threadIdx.x], s_cnt[threadIdx.x]);
+}
+
 }  // namespace
 
 hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
@@ -238,6 +340,17 @@ hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, kv_type,
                        head_dim, entries, n, k_out, v_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_validate(const ValidateParams &v, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_report_kernel, dim3(1), dim3(64), 0, stream, v.report);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int chunks = (v.p.max_pages + kValidatePages - 1) / kValidatePages;
+    if (v.p.rows.num_seqs <= 0 || chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)v.p.rows.num_seqs, (unsigned)chunks),
+                       dim3(256), 0, stream, v);
     return hipGetLastError();
 }
 

@@ -114,6 +114,16 @@ struct VtCopyParams {
     void *vt;                      // [num_seqs][max_pages][Hkv][D][P] f16
 };
 
+// Debug check of the tables and pools behind a call.
+struct ValidateParams {
+    DecodeParams p;           // tables, lengths, pools, regen counts (regen_pages may be null)
+    int32_t mode;             // MODE_PLAIN / MODE_TIERED / MODE_REGEN
+    int32_t kv_type, head_dim;
+    int32_t check_values;
+    int32_t max_query_len;
+    uint32_t *report;         // [4] counters, zeroed by the launcher's first kernel
+};
+
 // Launchers (defined next to their kernels).  Each returns the HIP error of
 // the launch.
 hipError_t launch_decode(const DecodeParams &p, int kv_type, int head_dim, int group,
@@ -135,6 +145,7 @@ hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *
                          int32_t num_kv_heads, int32_t head_dim, int32_t page_tokens,
                          int32_t num_blocks, int32_t elem_bytes, int32_t num_tokens,
                          void *k_out, void *v_out, hipStream_t stream);
+hipError_t launch_validate(const ValidateParams &v, hipStream_t stream);
 hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,
                           const int32_t *entries, int32_t n, float *k_out, float *v_out,
                           hipStream_t stream);

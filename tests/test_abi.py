@@ -186,3 +186,19 @@ def test_fold_and_inspection_arguments_are_checked():
                                     FAKE, FAKE, None) == atlas.EUNSUPPORTED
     assert L.atlas_regenerate_pages(1, 0, 8, 127, 16, atlas.BF16, FAKE, FAKE, 1, 1,
                                     FAKE, FAKE, None) == atlas.EINVAL
+
+
+def test_validate_tables_arguments_are_checked():
+    L = atlas.load()
+    a = _args()
+    assert L.atlas_validate_tables(ctypes.byref(a), None, None, 0, None, None) == atlas.EINVAL
+    pools = atlas.TierPools()
+    pools.struct_size = ctypes.sizeof(atlas.TierPools)
+    r = atlas.make_regen(42, 0, FAKE, 10)
+    assert L.atlas_validate_tables(ctypes.byref(a), ctypes.byref(pools), ctypes.byref(r), 0,
+                                   FAKE, None) == atlas.EINVAL
+    bad = _args(num_heads=30)
+    assert L.atlas_validate_tables(ctypes.byref(bad), None, None, 0, FAKE, None) == atlas.EINVAL
+    pools.num_int8 = 2  # scales missing, values requested
+    assert L.atlas_validate_tables(ctypes.byref(_args(kv_dtype=atlas.F16)), ctypes.byref(pools),
+                                   None, 1, FAKE, None) == atlas.EINVAL

@@ -447,3 +447,46 @@ def test_config5_full_sampled(gpu):
     w = synth.config(5, device=gpu)
     out, lse = run(w)
     check(w, out, lse, rows=[0, 1, 777, 1500, 2047], heads=[0, 13, 40, 63])
+
+
+# ---------------------------------------------------------------------------
+# Debug table validation
+# ---------------------------------------------------------------------------
+
+def test_validate_tables_counts_planted_faults(gpu):
+    w = synth.config(3, device=gpu, num_seqs=4, context_lens=[1, 100, 1500, 2600])
+    prob = atlas.Problem(w)
+    # clean problem: the NaN poison sits only in unused entries and page tails
+    assert prob.validate(check_values=True) == [0, 0, 0, 0]
+    prob.table[2, 5] = w.num_blocks + 7        # visible entry naming no page
+    prob.table[3, 2] = -1
+    assert prob.validate() == [2, 0, 0, 0]
+    prob.table.copy_(torch.from_numpy(w.page_table).to(gpu))
+    blk = int(w.page_table[3, 4])
+    w.k_pool[blk, 1, 3, 7] = float("nan")      # visible token 4 * 16 + 3 of seq 3
+    w.v_pool[blk, 0, 0, 0] = float("inf")
+    assert prob.validate(check_values=True) == [0, 0, 2, 0]
+    assert prob.validate(check_values=False) == [0, 0, 0, 0]
+    prob.ctx[1] = w.max_context_len + 1        # beyond the host bound
+    assert prob.validate()[1] == 1
+
+
+def test_validate_tables_tiered_and_regen(gpu):
+    w = synth.config(4, device=gpu, num_seqs=3, context_lens=[1000, 2500, 3000])
+    prob = atlas.Problem(w)
+    assert prob.validate(check_values=True) == [0, 0, 0, 0]
+    e = int(w.page_table[1, 3]) & 0xFFFFFFFF
+    tier, slot = e >> 30, e & ((1 << 30) - 1)
+    assert tier in (1, 2)
+    scales = w.tiers["i8_k_scale" if tier == 1 else "i4_k_scale"]
+    scales[slot, 2] = float("inf")
+    assert prob.validate(check_values=True) == [0, 0, 0, 1]
+    prob.table[0, 1] = -(1 << 30)              # 0xC0000000: tier 3, names no pool
+    assert prob.validate()[0] == 1
+
+    w5 = synth.config(5, device=gpu, context_lens=3000, query_lens=200, num_heads=16,
+                      num_kv_heads=2)
+    p5 = atlas.Problem(w5)
+    assert p5.validate() == [0, 0, 0, 0]
+    p5.regen_pages[0] = int(w5.regen["regen_pages"].max()) + 1
+    assert p5.validate()[1] == 1
