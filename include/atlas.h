@@ -33,7 +33,9 @@
  *  - The library is stateless and thread-safe.  Results are bitwise
  *    deterministic run to run; split boundaries are fixed in tokens, so the
  *    page size and the physical placement of pages do not change the result
- *    bits.
+ *    bits.  (Tiered calls visit the pages of a split grouped by tier; there
+ *    the placement still leaves the bits alone, the page size -- which sets
+ *    the tier granularity -- may change the last bits.)
  */
 #ifndef ATLAS_H
 #define ATLAS_H
@@ -182,9 +184,11 @@ const char *atlas_last_error(void);
 /*
  * Workspace bytes needed by atlas_paged_attention (regen == NULL) or
  * atlas_paged_attention_regen (regen != NULL) for these arguments.  Reads host
- * fields only.  The workspace holds the split-K partials (one f32 vector of
- * head_dim plus one lse per (row, head, split)) and, for chunked prefill with
- * regenerated pages, one bf16 copy of every regenerated page (each
+ * fields only.  The workspace holds the split-K partials of decode (one f32
+ * vector of head_dim plus one lse per (row, head, split)); for matrix-core
+ * chunked prefill it holds an f16 copy of every page's V transposed to
+ * [head_dim][page_tokens] (num_seqs * max_pages_per_seq pages) and, with
+ * regenerated pages, one bf16 copy of every regenerated K page (each
  * regenerated value is computed once per call and shared by every query
  * tile).  Its contents need no initialisation and are not meaningful between
  * calls; two calls in flight at the same time must not share a workspace.
@@ -196,10 +200,14 @@ atlas_status atlas_workspace_size(const atlas_attn_args *args,
 /*
  * Paged causal attention: decode (query_start == NULL) or chunked prefill.
  * kv_dtype F32, BF16 or F16; q_dtype F32 with F32 K/V, otherwise BF16 or F16.
- * head_dim 64 or 128; num_heads / num_kv_heads in {1, 2, 4, 8}.  Decode rows
- * (and every row of f32 problems) use the vector-ALU kernel with split-K over
- * pages and a log-sum-exp merge; chunked prefill over BF16/F16 K/V with
- * head_dim 128 runs QK^T and PV on matrix cores (MFMA).
+ * head_dim 64 or 128; num_heads / num_kv_heads in {1, 2, 4, 8}.  Decode
+ * rows are split over pages (split-K) and merged by log-sum-exp; with 16-bit
+ * K/V, head_dim 128 and 2 or 4 query heads per kv head QK^T runs on matrix
+ * cores and PV on the vector ALUs, otherwise both run on the vector ALUs.
+ * Chunked prefill over BF16/F16 K/V (q of the same type) with head_dim 128
+ * runs QK^T and PV on matrix cores (MFMA); other prefill shapes use the
+ * vector-ALU kernel.  On matrix cores PV takes the probabilities and V in
+ * f16, so V must lie within the f16 range (|v| <= 65504).
  */
 atlas_status atlas_paged_attention(const atlas_attn_args *args);
 
@@ -208,7 +216,11 @@ atlas_status atlas_paged_attention(const atlas_attn_args *args);
  * pages come from args->k_pool / v_pool (kv_dtype F16 or BF16, num_blocks
  * slots); int8 and int4 pages from `pools`.  Decode only (query_start must be
  * NULL).  Codes are decoded in registers and the per-page scales are applied
- * to the dot products and to the probabilities, never written back.
+ * to the dot products and to the probabilities, never written back.  With
+ * F16 hot pages, head_dim 128 and 2 or 4 query heads per kv head, QK^T runs
+ * on matrix cores in f16: the codes convert exactly, q is rounded to f16
+ * (exact for bf16 q with 2^-14 <= |q| <= 65504; smaller magnitudes carry an
+ * absolute error of at most 2^-25, larger ones are out of range).
  */
 atlas_status atlas_paged_attention_tiered(const atlas_attn_args *args,
                                           const atlas_tier_pools *pools);
