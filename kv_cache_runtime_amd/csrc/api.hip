@@ -257,7 +257,8 @@ atlas_status run_decode(const atlas_attn_args *a, const Plan &plan, DecodeParams
     hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
     hipError_t e = mark(a, 0, stream);
     if (e != hipSuccess) return device_status(e, "profile event record");
-    if (decode_mfma_supported(a->kv_dtype, a->head_dim, plan.group, mode) &&
+    if (decode_mfma_supported(a->kv_dtype, a->head_dim, plan.group, mode, a->page_tokens,
+                              plan.split_tokens) &&
         std::getenv("ATLAS_DECODE_VALU") == nullptr)
         e = launch_decode_mfma(p, a->kv_dtype, plan.group, mode, stream);
     else

@@ -38,7 +38,7 @@ namespace atlas {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kStagedPages = 512;  // page-table entries staged in LDS per split
+constexpr int kStagedPages = kDecodeStagedPages;
 
 template <int KV>
 constexpr int hot_bytes() { return KV == KV_F32 ? 4 : 2; }

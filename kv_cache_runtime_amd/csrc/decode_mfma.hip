@@ -1,27 +1,36 @@
-// Paged decode attention with QK^T on the matrix cores (gfx950), for 16-bit
-// and tiered (f16 hot + int8 / int4 cold) pages, head_dim 128 and 2 or 4 query
-// heads per kv head.  Same method and split-K structure as decode.hip: keys
-// folded tile by tile with an online softmax (CFR-Atlas README, overview;
-// ARGUS "Latency & Throughput Impact"), splits merged by log-sum-exp.
+// Paged decode attention on the matrix cores (gfx950), for 16-bit and tiered
+// (f16 hot + int8 / int4 cold) pages, head_dim 128 and 2, 4 or 8 query heads
+// per kv head.  Same method and split-K structure as decode.hip: keys folded
+// tile by tile with an online softmax (CFR-Atlas README, overview; ARGUS
+// "Latency & Throughput Impact"), splits merged by log-sum-exp.
 //
 // gfx950 mapping.  A workgroup is 4 wave64s and owns one (row, kv head,
-// split); each wave walks 64-token tiles.  Scores come from
-// v_mfma_f32_16x16x32 with the query heads as A (rows, zero-padded to 16)
-// and the K rows of 16 tokens as B: lane l supplies 8 dims of token l % 16,
-// so every K load is 16 tokens x 64 contiguous bytes, and the result of 16
-// tokens x (up to) 16 heads lands with token l % 16 in lane l and heads
-// 4 (l / 16) .. + 3 in its four registers.  Four token groups per tile keep
-// four independent accumulators in flight.  The softmax keeps one reference
-// max per head (moved only when a tile's max exceeds it by 2^8) and reduces
-// within 16-lane rows only; probabilities go through LDS, and P.V runs on the
-// vector ALUs in the row-slot layout of decode.hip: 16-lane row-slots, each
-// lane owning 8 of the 128 dims of 16 consecutive tokens.
+// split); each wave walks 64-token tiles, four 16-token groups each (a group
+// lies in one page: pages are multiples of 16 tokens, tiles start at
+// multiples of 64 positions).
+//  * Scores: v_mfma_f32_16x16x32 with the query heads as A (rows, zero-padded
+//    to 16) and 16 tokens as B (lane l supplies 8 dims of token l % 16), so
+//    every K load is 16 tokens x 64 contiguous bytes; the result has token
+//    l % 16 in lane l and heads 4 (l / 16) .. + 3 in its four registers.
+//  * Softmax: one reference max per head, moved only when a tile's max
+//    exceeds it by 2^8, reduced within 16-lane rows by DPP.
+//  * P.V: O^T[dim][head] += V^T[dim][token] P^T[token][head], also on
+//    v_mfma_f32_16x16x32.  V rows are written to LDS as they are stored
+//    (token-major, int codes widened to f16 on the way) and read back as the
+//    token-contiguous operand by the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16); P goes through LDS the same way.  bf16 pages keep
+//    P as a bf16 pair (hi + lo, ~16 significant bits); f16 pages use f16 P.
+//  * The next tile's K and V are requested while the current tile computes
+//    (software pipeline), so HBM latency overlaps the softmax and P.V.
 //
-// Tiered pages: K int8 / int4 codes become f16 in registers (exact), the K
-// scale multiplies the finished score and the V scale the probability.  The
-// matrix-core operand type is bf16 for bf16 pages (query used as stored) and
-// f16 otherwise (the query converted to f16: exact for |q| in [2^-14, 65504],
-// smaller magnitudes round with absolute error at most 2^-25).
+// Tiered pages: the split's page-table entries are staged in LDS grouped by
+// tier, and each tier's run of pages is padded to whole tiles, so every tile
+// holds one tier and runs straight-line code for it.  K int8 / int4 codes
+// become f16 in registers (exact), the K scale multiplies the finished score
+// and the V scale the probability.  The matrix-core operand type is bf16 for
+// bf16 pages (query used as stored) and f16 otherwise (the query converted to
+// f16: exact for |q| in [2^-14, 65504], smaller magnitudes round with
+// absolute error at most 2^-25).
 #include "device.h"
 
 namespace atlas {
@@ -35,8 +44,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kTileTok = 64;  // tokens per wave tile (one per lane for QK)
-constexpr int kSlotTok = 16;  // tokens per row-slot for P.V
-constexpr int kStagedPages = 512;  // page-table entries staged in LDS per split
+constexpr int kStagedPages = kDecodeStagedPages;  // page-table entries staged per split
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -52,183 +60,217 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     }
 }
 
-// int8 codes (4 per word) -> f16 pairs, exact: bias to unsigned, place each
-// byte under the f16 exponent of 1024 (0x64xx == 1024 + byte), subtract 1152.
+// Byte permutes that take the constant byte 0x64 from a register: placing a
+// code byte u under it gives the f16 0x64uu = 1024 + u.
+constexpr uint32_t kMagic64 = 0x64646464u;
+
+// int8 codes (4 per word) -> f16 pairs, exact: bias to unsigned (u = c + 128),
+// form 0x64uu (= 1024 + u) with one byte permute per pair, subtract 1152.
 __device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
     const uint32_t u = w ^ 0x80808080u;
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const uint32_t a = __builtin_amdgcn_perm(0u, u, 0x0C010C00u) | 0x64006400u;  // bytes 0, 1
-    const uint32_t b = __builtin_amdgcn_perm(0u, u, 0x0C030C02u) | 0x64006400u;  // bytes 2, 3
+    const uint32_t a = __builtin_amdgcn_perm(kMagic64, u, 0x05010400u);  // bytes 0, 1
+    const uint32_t b = __builtin_amdgcn_perm(kMagic64, u, 0x05030402u);  // bytes 2, 3
     const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
     lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) - bias);
     hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - bias);
 }
 
-// int4 codes (8 per word, element e in nibble e) -> f16 pairs (e, e + 1), exact.
+// int4 codes (8 per word, element e in nibble e, two's complement) -> f16
+// pairs (e, e + 1), exact: bias to unsigned nibbles, gather the even and the
+// odd elements into bytes, interleave them, place each byte under 0x64 and
+// subtract 1032.
 __device__ __forceinline__ void i4x8_to_f16x8(uint32_t w, uint32_t (&out)[4]) {
-    const uint32_t u = w ^ 0x88888888u;  // two's complement nibble -> biased by 8
+    const uint32_t u = w ^ 0x88888888u;
+    const uint32_t ev = u & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
+    const uint32_t od = (u >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+    const uint32_t e03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // elements 0..3
+    const uint32_t e47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // elements 4..7
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t byte = (u >> (8 * i)) & 0xFFu;
-        const uint32_t pair = (byte & 0x0Fu) | ((byte & 0xF0u) << 12) | 0x64006400u;
-        out[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, pair) - bias);
-    }
+    const uint32_t p0 = __builtin_amdgcn_perm(kMagic64, e03, 0x05010400u);
+    const uint32_t p1 = __builtin_amdgcn_perm(kMagic64, e03, 0x05030402u);
+    const uint32_t p2 = __builtin_amdgcn_perm(kMagic64, e47, 0x05010400u);
+    const uint32_t p3 = __builtin_amdgcn_perm(kMagic64, e47, 0x05030402u);
+    out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p0) - bias);
+    out[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p1) - bias);
+    out[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p2) - bias);
+    out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p3) - bias);
 }
 
-// Loads dims d0 .. d0 + 7 of K row `row` of a page as one 16-bit operand
-// (uint4) and returns the page's K scale.  Returns false for an invalid
-// page-table entry.
-template <int KV, int MODE>
-__device__ __forceinline__ bool load_k_chunk(const DecodeParams &p, uint32_t entry, int g, int row,
-                                             int d0, uint4 &kv, float &kscale) {
-    kscale = 1.0f;
-    uint32_t tier = 0, slot = entry;
-    if constexpr (MODE == MODE_TIERED) {
-        tier = entry >> 30;
-        slot = entry & ((1u << 30) - 1u);
-    }
-    const int P = p.page_tokens;
-    if (tier == 0) {
-        if (slot >= (uint32_t)p.num_blocks) return false;
-        kv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.k_pool) +
-                                              (((int64_t)slot * p.num_kv_heads + g) * P + row) * kD +
-                                              d0);
-        return true;
-    }
-    if constexpr (MODE == MODE_TIERED) {
-        if (tier == 1) {
-            if (slot >= (uint32_t)p.n_i8) return false;
-            const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * P + row;
-            const uint2 w = *reinterpret_cast<const uint2 *>(p.i8_k + r0 * kD + d0);
-            kscale = p.i8_ks[(int64_t)slot * p.num_kv_heads + g];
-            i8x4_to_f16x4(w.x, kv.x, kv.y);
-            i8x4_to_f16x4(w.y, kv.z, kv.w);
-            return true;
-        }
-        if (tier == 2) {
-            if (slot >= (uint32_t)p.n_i4) return false;
-            const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * P + row;
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(p.i4_k + r0 * (kD / 2) + d0 / 2);
-            kscale = p.i4_ks[(int64_t)slot * p.num_kv_heads + g];
-            uint32_t o[4];
-            i4x8_to_f16x8(w, o);
-            kv = make_uint4(o[0], o[1], o[2], o[3]);
-            return true;
-        }
-    }
-    return false;
-}
+constexpr int kHot = 0, kInt8 = 1, kInt4 = 2;
+// 16-byte chunks per lane of one 16-token group, for K and for V
+template <int TIER>
+constexpr int chunks() { return TIER == kHot ? 4 : TIER == kInt8 ? 2 : 1; }
 
-// Tiered pages: loads dims 32 r .. 32 r + 31 of K row `row` of a page as the
-// four 16-bit operands kv[ks] = dims 32 r + 8 ks .. + 8 (hot: 64 bytes, int8:
-// 32, int4: 16, each one contiguous run) and returns the page's K scale.
-// Returns false for an invalid page-table entry.
-template <int KV>
-__device__ __forceinline__ bool load_k_row_tiered(const DecodeParams &p, uint32_t entry, int g,
-                                                  int row, int r, uint4 (&kv)[4], float &kscale) {
+// Raw K of row `row` of a page (slot) for this lane (row r of the 16-lane
+// rows).  Resident pages give the four operands directly (operand ks = dims
+// 32 ks + 8 r .. + 8); tiered pages give dims 32 r .. 32 r + 31 as one run
+// (hot: 64 bytes, int8: 32, int4: 16), widened by widen_k.  Returns the K
+// scale; false if the slot is outside its pool.
+template <int KV, int MODE, int TIER>
+__device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slot, int g, int row,
+                                             int r, uint4 (&kr)[chunks<TIER>()], float &kscale) {
     kscale = 1.0f;
-    const uint32_t tier = entry >> 30, slot = entry & ((1u << 30) - 1u);
-    const int P = p.page_tokens;
-    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * P + row;
-    if (tier == 0) {
+    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row;
+    if constexpr (TIER == kHot) {
         if (slot >= (uint32_t)p.num_blocks) return false;
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            reinterpret_cast<const uint16_t *>(p.k_pool) + r0 * kD + 32 * r);
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(p.k_pool) + r0 * kD;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kv[ks] = src[ks];
-        return true;
-    }
-    if (tier == 1) {
+        for (int ks = 0; ks < 4; ++ks) {
+            const int d0 = MODE == MODE_TIERED ? 32 * r + 8 * ks : 32 * ks + 8 * r;
+            kr[ks] = *reinterpret_cast<const uint4 *>(src + d0);
+        }
+    } else if constexpr (TIER == kInt8) {
         if (slot >= (uint32_t)p.n_i8) return false;
         const uint4 *src = reinterpret_cast<const uint4 *>(p.i8_k + r0 * kD + 32 * r);
         kscale = p.i8_ks[(int64_t)slot * p.num_kv_heads + g];
-        const uint4 a = src[0], b = src[1];
-        i8x4_to_f16x4(a.x, kv[0].x, kv[0].y);
-        i8x4_to_f16x4(a.y, kv[0].z, kv[0].w);
-        i8x4_to_f16x4(a.z, kv[1].x, kv[1].y);
-        i8x4_to_f16x4(a.w, kv[1].z, kv[1].w);
-        i8x4_to_f16x4(b.x, kv[2].x, kv[2].y);
-        i8x4_to_f16x4(b.y, kv[2].z, kv[2].w);
-        i8x4_to_f16x4(b.z, kv[3].x, kv[3].y);
-        i8x4_to_f16x4(b.w, kv[3].z, kv[3].w);
-        return true;
-    }
-    if (tier == 2) {
+        kr[0] = src[0];
+        kr[1] = src[1];
+    } else {
         if (slot >= (uint32_t)p.n_i4) return false;
-        const uint4 w = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + 16 * r);
+        kr[0] = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + 16 * r);
         kscale = p.i4_ks[(int64_t)slot * p.num_kv_heads + g];
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    }
+    return true;
+}
+
+// Raw K -> the four 16-bit operands (codes widened to f16, exact).
+template <int TIER>
+__device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4 (&kb)[4]) {
+    if constexpr (TIER == kHot) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = kr[ks];
+    } else if constexpr (TIER == kInt8) {
+        const uint32_t w[8] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w, kr[1].x, kr[1].y, kr[1].z, kr[1].w};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint32_t a, b, c, d;
+            i8x4_to_f16x4(w[2 * ks], a, b);
+            i8x4_to_f16x4(w[2 * ks + 1], c, d);
+            kb[ks] = make_uint4(a, b, c, d);
+        }
+    } else {
+        const uint32_t w[4] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             uint32_t o[4];
-            i4x8_to_f16x8(ww[ks], o);
-            kv[ks] = make_uint4(o[0], o[1], o[2], o[3]);
+            i4x8_to_f16x8(w[ks], o);
+            kb[ks] = make_uint4(o[0], o[1], o[2], o[3]);
         }
-        return true;
     }
-    return false;
 }
 
-// Loads the raw V words of 16 tokens x 8 dims for this lane's row-slot (hot:
-// 4 words per token, int8: 2, int4: 1), its tier and V scale.  Returns false
-// for an invalid page-table entry.
-template <int KV, int MODE>
-__device__ __forceinline__ bool load_v_slot(const DecodeParams &p, uint32_t entry, int g, int row0,
-                                            int c, uint4 (&vr)[kSlotTok], uint32_t &tier,
-                                            float &vscale) {
+// Raw V of one 16-token group (rows row0 .. row0 + 15 of a page, one
+// contiguous slab): lane l takes 16-byte chunks l, l + 64, ...  Returns the V
+// scale; false if the slot is outside its pool.
+template <int KV, int TIER>
+__device__ __forceinline__ bool load_v_group(const DecodeParams &p, uint32_t slot, int g, int row0,
+                                             int lane, uint4 (&vr)[chunks<TIER>()],
+                                             float &vscale) {
     vscale = 1.0f;
-    tier = 0;
-    uint32_t slot = entry;
-    if constexpr (MODE == MODE_TIERED) {
-        tier = entry >> 30;
-        slot = entry & ((1u << 30) - 1u);
-    }
-    const int P = p.page_tokens;
-    if (tier == 0) {
+    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row0;
+    if constexpr (TIER == kHot) {
         if (slot >= (uint32_t)p.num_blocks) return false;
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(p.v_pool) +
-                              (((int64_t)slot * p.num_kv_heads + g) * P + row0) * kD + 8 * c;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            reinterpret_cast<const uint16_t *>(p.v_pool) + r0 * kD);
 #pragma unroll
-        for (int u = 0; u < kSlotTok; ++u) vr[u] = *reinterpret_cast<const uint4 *>(src + u * kD);
-        return true;
+        for (int i = 0; i < 4; ++i) vr[i] = src[64 * i + lane];
+    } else if constexpr (TIER == kInt8) {
+        if (slot >= (uint32_t)p.n_i8) return false;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.i8_v + r0 * kD);
+        vscale = p.i8_vs[(int64_t)slot * p.num_kv_heads + g];
+        vr[0] = src[lane];
+        vr[1] = src[64 + lane];
+    } else {
+        if (slot >= (uint32_t)p.n_i4) return false;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.i4_v + r0 * (kD / 2));
+        vscale = p.i4_vs[(int64_t)slot * p.num_kv_heads + g];
+        vr[0] = src[lane];
     }
-    if constexpr (MODE == MODE_TIERED) {
-        if (tier == 1) {
-            if (slot >= (uint32_t)p.n_i8) return false;
-            const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * P + row0;
-            const uint2 *src = reinterpret_cast<const uint2 *>(p.i8_v + r0 * kD + 8 * c);
-            vscale = p.i8_vs[(int64_t)slot * p.num_kv_heads + g];
-#pragma unroll
-            for (int u = 0; u < kSlotTok; ++u) {
-                const uint2 w = src[u * (kD / 8)];
-                vr[u] = make_uint4(w.x, w.y, 0u, 0u);
-            }
-            return true;
-        }
-        if (tier == 2) {
-            if (slot >= (uint32_t)p.n_i4) return false;
-            const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * P + row0;
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(p.i4_v + r0 * (kD / 2) + 4 * c);
-            vscale = p.i4_vs[(int64_t)slot * p.num_kv_heads + g];
-#pragma unroll
-            for (int u = 0; u < kSlotTok; ++u) vr[u] = make_uint4(src[u * (kD / 8)], 0u, 0u, 0u);
-            return true;
-        }
-    }
-    return false;
+    return true;
 }
+
+constexpr int kVPitch = kD + 16;  // LDS row pitch of the V tile (16-bit elements, 72 words)
+
+// Component-wise select (a select of whole uint4 values can turn into a
+// select of addresses and a trip through scratch memory).
+__device__ __forceinline__ uint4 keep_if(bool ok, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return make_uint4(ok ? a : 0u, ok ? b : 0u, ok ? c : 0u, ok ? d : 0u);
+}
+
+// Writes the group's V rows, as 16-bit operands, into rows base .. base + 15
+// of the wave's LDS V tile; rows whose token is not visible (tok_ok false)
+// are written as zeros, so NaN garbage in page tails never meets a zero
+// probability.
+template <int TIER, typename TokOk>
+__device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
+                                              const uint4 (&vr)[chunks<TIER>()], int lane,
+                                              TokOk tok_ok) {
+    if constexpr (TIER == kHot) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // chunk 64 i + lane: token 4 i + lane / 16
+            const int tok = 4 * i + (lane >> 4);
+            *reinterpret_cast<uint4 *>(vt + (base + tok) * kVPitch + 8 * (lane & 15)) =
+                keep_if(tok_ok(tok), vr[i].x, vr[i].y, vr[i].z, vr[i].w);
+        }
+    } else if constexpr (TIER == kInt8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {  // chunk 64 i + lane: token 8 i + lane / 8
+            const int tok = 8 * i + (lane >> 3);
+            const bool ok = tok_ok(tok);
+            const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) i8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
+            uint16_t *dst = vt + (base + tok) * kVPitch + 16 * (lane & 7);
+            *reinterpret_cast<uint4 *>(dst) = keep_if(ok, h[0], h[1], h[2], h[3]);
+            *reinterpret_cast<uint4 *>(dst + 8) = keep_if(ok, h[4], h[5], h[6], h[7]);
+        }
+    } else {
+        const int tok = lane >> 2;  // chunk lane: token lane / 4, dims 32 (lane % 4) ..
+        const bool ok = tok_ok(tok);
+        const uint32_t w[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+        uint16_t *dst = vt + (base + tok) * kVPitch + 32 * (lane & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t o[4];
+            i4x8_to_f16x8(w[j], o);
+            *reinterpret_cast<uint4 *>(dst + 8 * j) = keep_if(ok, o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+typedef short s16x4_lds_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// s supplies the address of 4 consecutive 16-bit elements; lane i receives
+// element i % 4 of the chunks of lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.
+// With lane s of the group pointing at row k0 + s / 4, column n0 + 4 (s % 4)
+// of a row-major tile, lane i receives column n0 + i of rows k0 .. k0 + 3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *ptr) {
+    const s16x4_lds_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_lds_t *)(ptr));
+    return __builtin_bit_cast(uint2, v);
+}
+
+template <int V>
+struct TierC {  // compile-time int argument of the tile-run lambda
+    static constexpr int value = V;
+};
 
 template <int QT, int KV, int G, int MODE>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams p) {
     constexpr int NR = (G + 3) / 4;  // 16-lane rows holding score heads (4 heads per row)
     constexpr float kSlack = 8.0f;   // lazy rescale threshold (log2 units)
     constexpr float kPScale = 7.0f;  // probabilities kept relative to m_ref - 7
+    constexpr int NP = QT == KV_BF16 ? 2 : 1;  // P operand parts (bf16: hi + lo)
     const float kNegInf = -__builtin_inff();
 
-    __shared__ __attribute__((aligned(16))) float sP[kWaves][kTileTok][G];
-    __shared__ float s_acc[kWaves][G][kD];
+    // per wave: V tile of 32 tokens (one half of a 64-token tile at a time),
+    // reused for the wave's final accumulators; P of 64 tokens x 16 heads
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[kWaves][32 * kVPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t s_p[kWaves][NP][kTileTok * 16];
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[kWaves][G];
 
@@ -255,7 +297,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
 
     // page-table entries of this split, staged once (a dependent global load
     // per tile would add a memory round trip before every K/V load); tiered
-    // splits stage them grouped by tier and walk the pages in that order
+    // splits stage them grouped by tier (the host keeps every tiered split
+    // within kStagedPages pages)
     __shared__ int32_t s_pages[kStagedPages];
     __shared__ int16_t s_lp[MODE == MODE_TIERED ? kStagedPages : 1];
     const int32_t *trow = p.page_table + (int64_t)seq * p.max_pages;
@@ -263,16 +306,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     const int lp_first = t0 / P;
     const int lp_count = t1 > t0 ? (t1 - 1) / P - lp_first + 1 : 0;
     const bool staged = lp_count <= kStagedPages;
-    const bool by_tier = MODE == MODE_TIERED && staged;
-    if (by_tier) {
-        stage_pages_by_tier(trow + lp_first, lp_count, s_pages, s_lp);
+    int tier_count[4] = {0, 0, 0, 0};
+    if constexpr (MODE == MODE_TIERED) {
+        stage_pages_by_tier(trow + lp_first, min(lp_count, kStagedPages), s_pages, s_lp,
+                            tier_count);
     } else {
         if (staged)
             for (int i = tid; i < lp_count; i += 256) s_pages[i] = trow[lp_first + i];
         __syncthreads();
     }
 
-    // A operand: query head c (zero for c >= G), dims 32 ks + 8 r .. + 8
+    // A operand of the scores: query head c (zero for c >= G)
     uint4 qf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -299,214 +343,288 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         qf[ks] = make_uint4(w[0], w[1], w[2], w[3]);
     }
 
-    // m_ref / l of the heads 4 r + i held by this lane's row (score layout);
-    // acc of all G heads in the row-slot layout
-    float m_ref[4], l[4], acc[G][8];
+    // m_ref / l of heads 4 r + i (score layout); acc[mb][i] = O^T[dim
+    // 16 mb + 4 r + i][head c] (P.V result layout; columns c >= G unused)
+    float m_ref[4], l[4];
+    f32x4_t acc[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         m_ref[i] = kNegInf;
         l[i] = 0.0f;
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     bool bad = !row_ok;
 
-    // positions walked: tokens t0 .. t1 - 1, or (by tier) every token slot of
-    // the split's pages, of which those outside [t0, t1) are masked
-    const int n_pos = by_tier ? lp_count * P : t1 - t0;
-    const int n_tiles = n_pos > 0 ? (n_pos + kTileTok - 1) / kTileTok : 0;
+    uint16_t *vt = s_v[wave];
+    uint16_t *pt = s_p[wave][0];
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto in_range = [&](int tok) { return tok >= t0 && tok < t1; };
 
-    for (int tile = wave_u; tile < n_tiles; tile += kWaves) {
-        // ---- the 16-position groups of the tile: the page size is a
-        // multiple of 16 and tiles start at multiples of 64 positions, so a
-        // group lies in one page; its first token, page-table entry and
-        // liveness are wave-uniform
-        int gtok[4];
-        uint32_t gent[4];
-        bool glive[4];
-#pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
-            const int q = tile * kTileTok + 16 * tg;
-            if (by_tier) {
-                const int pi = q / P;
-                glive[tg] = pi < lp_count;
-                const int lp = lp_first + (glive[tg] ? s_lp[pi] : 0);
-                gtok[tg] = lp * P + (q - pi * P);
-                gent[tg] = glive[tg] ? (uint32_t)s_pages[pi] : 0u;
-            } else {
-                gtok[tg] = t0 + q;
-                glive[tg] = gtok[tg] < t1;
-                const int lp = gtok[tg] / P;
-                gent[tg] = glive[tg] ? (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]) : 0u;
-            }
-            gtok[tg] = __builtin_amdgcn_readfirstlane(gtok[tg]);
-            gent[tg] = __builtin_amdgcn_readfirstlane(gent[tg]);
-        }
-        auto in_range = [&](int tok) { return tok >= t0 && tok < t1; };
+    // Walks the tiles of one run of pages with one tier: the whole split in
+    // token order (natural), or the sp .. sp + np - 1 staged entries of a
+    // tier.  Each wave takes every fourth tile of the run.
+    auto run = [&](auto tier_c, auto natural_c, int sp, int np) {
+        constexpr int TIER = decltype(tier_c)::value;
+        constexpr bool natural = decltype(natural_c)::value != 0;
+        constexpr int NC = chunks<TIER>();
+        const int n_pos = natural ? t1 - t0 : np * P;
+        const int n_tiles = n_pos > 0 ? (n_pos + kTileTok - 1) / kTileTok : 0;
 
-        // ---- K: token gtok[tg] + c, dims 32 ks + 8 r .. + 8
-        uint4 kb[4][4];
-        float kscale[4];
-        bool kvalid[4];
-#pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
-            const int tk = gtok[tg] + c;
-            kscale[tg] = 1.0f;
-            kvalid[tg] = glive[tg] && in_range(tk);
-            bool ok = glive[tg];
-            if (ok) {
-                const int row0 = gtok[tg] % P;
-                if constexpr (MODE == MODE_TIERED) {
-                    ok = load_k_row_tiered<KV>(p, gent[tg], g, row0 + c, r, kb[tg], kscale[tg]);
-                } else {
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        ok = ok && load_k_chunk<KV, MODE>(p, gent[tg], g, row0 + c,
-                                                          32 * ks + 8 * r, kb[tg][ks], kscale[tg]);
-                }
-                if (!ok) {
-                    bad = true;
-                    kvalid[tg] = false;
-                }
-            }
-            if (!ok) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kb[tg][ks] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-        // ---- V rows of this lane's row-slot r = group r (in flight during QK)
-        const int v0 = r == 0 ? gtok[0] : r == 1 ? gtok[1] : r == 2 ? gtok[2] : gtok[3];
-        const uint32_t vent = r == 0 ? gent[0] : r == 1 ? gent[1] : r == 2 ? gent[2] : gent[3];
-        bool slot_live = r == 0 ? glive[0] : r == 1 ? glive[1] : r == 2 ? glive[2] : glive[3];
-        uint4 vr[kSlotTok];
-        uint32_t vtier = 0;
-        float vscale = 1.0f;
-        if (slot_live) {
-            if (!load_v_slot<KV, MODE>(p, vent, g, v0 % P, c, vr, vtier, vscale)) {
-                bad = true;
-                slot_live = false;
-            }
-        }
-
-        // ---- scores: sc[tg][i] = head 4 r + i, token 16 tg + c (log2 domain)
-        f32x4_t sc[4];
-#pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
-            sc[tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) sc[tg] = mfma16<QT>(qf[ks], kb[tg][ks], sc[tg]);
-            const float f = kscale[tg] * p.scale_log2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[tg][i] = kvalid[tg] ? sc[tg][i] * f : kNegInf;
-        }
-
-        // ---- online softmax, one reference max per head (uniform in a row)
-        bool move_any = false;
-        float alpha[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float mx = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
-            mx = fmaxf(mx, dpp_f<0x128>(mx));
-            mx = fmaxf(mx, dpp_f<0x124>(mx));
-            mx = fmaxf(mx, dpp_f<0x122>(mx));
-            mx = fmaxf(mx, dpp_f<0x121>(mx));
-            const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
-            const float m_new = move ? mx : m_ref[i];
-            alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;
-            move_any = move_any || move;
-            m_ref[i] = m_new;
-        }
-        if (__any(move_any)) {  // wave-uniform
-#pragma unroll
-            for (int i = 0; i < 4; ++i) l[i] *= alpha[i];
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float ah = __int_as_float(
-                    __builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * r + i;
-            const float m_off = (m_ref[i] == kNegInf) ? 0.0f : m_ref[i] - kPScale;
+        // the 16-position groups of a tile: first token, slot and liveness,
+        // all wave-uniform (a group lies in one page)
+        struct Groups {
+            int tok[4];
+            uint32_t slot[4];
+            bool live[4];
+        };
+        auto groups_of = [&](int tile, Groups &G_) {
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
-                const float pr = __builtin_amdgcn_exp2f(sc[tg][i] - m_off);
-                l[i] += pr;
-                if (r < NR && h < G) sP[wave][16 * tg + c][h] = pr;
+                const int q = tile * kTileTok + 16 * tg;
+                bool live;
+                int tok;
+                uint32_t ent;
+                if constexpr (natural) {
+                    tok = t0 + q;
+                    live = tile < n_tiles && tok < t1;
+                    const int lp = tok / P;
+                    ent = live ? (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]) : 0u;
+                } else {
+                    const int pi = q / P;
+                    live = tile < n_tiles && pi < np;
+                    const int lp = lp_first + (live ? s_lp[sp + pi] : 0);
+                    tok = lp * P + (q - pi * P);
+                    ent = live ? (uint32_t)s_pages[sp + pi] : 0u;
+                }
+                if constexpr (MODE == MODE_TIERED) ent &= (1u << 30) - 1u;
+                G_.tok[tg] = __builtin_amdgcn_readfirstlane(tok);
+                G_.slot[tg] = __builtin_amdgcn_readfirstlane(ent);
+                G_.live[tg] = live;
             }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        uint4 kr[4][NC], vr[4][NC];
+        float kscale[4], vscale[4];
+        bool kok[4], vok[4];
+        auto load_k = [&](const Groups &G_, int tg) {
+            kok[tg] = G_.live[tg];
+            kscale[tg] = 1.0f;
+            if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.tok[tg] % P + c, r,
+                                                         kr[tg], kscale[tg])) {
+                bad = true;
+                kok[tg] = false;
+            }
+            if (!kok[tg]) {  // uniform: a dead group scores zeros (masked below)
+#pragma unroll
+                for (int i = 0; i < NC; ++i) kr[tg][i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        };
+        auto load_v = [&](const Groups &G_, int tg) {
+            vok[tg] = G_.live[tg];
+            vscale[tg] = 1.0f;
+            if (vok[tg] && !load_v_group<KV, TIER>(p, G_.slot[tg], g, G_.tok[tg] % P, lane,
+                                                   vr[tg], vscale[tg])) {
+                bad = true;
+                vok[tg] = false;
+            }
+        };
 
-        // ---- P.V on the vector ALUs (row-slot layout); the tier is uniform
-        // within a row-slot, so each decode path runs straight-line
-        if (slot_live) {
-            auto pv = [&](auto widen) {
+        // software pipeline: the next tile's K is requested right after this
+        // tile's scores, its V groups as soon as this tile's are in LDS
+        Groups cur;
+        groups_of(wave_u, cur);
 #pragma unroll
-                for (int u = 0; u < kSlotTok; ++u) {
-                    const bool valid = in_range(v0 + u);
-                    float pu[G];
+        for (int tg = 0; tg < 4; ++tg) {
+            load_k(cur, tg);
+            load_v(cur, tg);
+        }
+
+        for (int tile = wave_u; tile < n_tiles; tile += kWaves) {
+            Groups nxt;
+            groups_of(tile + kWaves, nxt);
+
+            // ---- scores: sc[tg][i] = head 4 r + i, token tok[tg] + c
+            // (log2 domain)
+            f32x4_t sc[4];
+            bool kvalid[4];
 #pragma unroll
-                    for (int h = 0; h < G; ++h) pu[h] = sP[wave][kSlotTok * r + u][h] * vscale;
-                    float v[8];
-                    widen(vr[u], v);
+            for (int tg = 0; tg < 4; ++tg) {
+                kvalid[tg] = kok[tg] && in_range(cur.tok[tg] + c);
+                uint4 kb[4];
+                widen_k<TIER>(kr[tg], kb);
+                sc[tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float x = valid ? v[e] : 0.0f;
+                for (int ks = 0; ks < 4; ++ks) sc[tg] = mfma16<QT>(qf[ks], kb[ks], sc[tg]);
+            }
+            float kf[4];  // hot pages carry no scale
 #pragma unroll
-                        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pu[h], x, acc[h][e]);
+            for (int tg = 0; tg < 4; ++tg)
+                kf[tg] = TIER == kHot ? p.scale_log2 : kscale[tg] * p.scale_log2;
+            // next tile's K (its registers are free once the scores are issued)
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) load_k(nxt, tg);
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[tg][i] = kvalid[tg] ? sc[tg][i] * kf[tg] : kNegInf;
+            }
+
+            // ---- online softmax, one reference max per head (uniform in a row)
+            bool move_any = false;
+            float alpha[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float mx = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+                mx = fmaxf(mx, dpp_f<0x128>(mx));
+                mx = fmaxf(mx, dpp_f<0x124>(mx));
+                mx = fmaxf(mx, dpp_f<0x122>(mx));
+                mx = fmaxf(mx, dpp_f<0x121>(mx));
+                const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
+                const float m_new = move ? mx : m_ref[i];
+                alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;
+                move_any = move_any || move;
+                m_ref[i] = m_new;
+            }
+            if (__any(move_any)) {  // wave-uniform
+#pragma unroll
+                for (int i = 0; i < 4; ++i) l[i] *= alpha[i];
+                // alpha of head c, from the score layout (row c / 4, register c % 4)
+                float ac = 1.0f;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float ah = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+                    ac = c == h ? ah : ac;
+                }
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) acc[mb] *= ac;
+            }
+            // probabilities of token tok[tg] + c, heads 4 r .. 4 r + 3 -> P
+            // tile (token-major, 16 heads), scaled by the group's V scale.
+            // Resident pages add the rounded weights the matrix cores use to
+            // l, so the normalisation matches them exactly (a constant V row
+            // comes back unchanged); cold pages add the unscaled weights.
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) {
+                float pr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float m_off = (m_ref[i] == kNegInf) ? 0.0f : m_ref[i] - kPScale;
+                    pr[i] = __builtin_amdgcn_exp2f(sc[tg][i] - m_off);
+                    if constexpr (TIER != kHot) {
+                        l[i] += pr[i];
+                        pr[i] *= vscale[tg];
                     }
                 }
-            };
-            if (MODE != MODE_TIERED || vtier == 0) {
-                pv([](const uint4 &w, float (&v)[8]) {
-                    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                uint2 hi, lo;
+                if constexpr (QT == KV_BF16) {
+                    uint32_t hb[4], lb[4];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = widen_word<KV>(ww, e);
-                });
-            } else if (vtier == 1) {
-                pv([](const uint4 &w, float (&v)[8]) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v[e] = (float)sext_field(e < 4 ? w.x : w.y, 24 - 8 * (e & 3), 8);
-                });
-            } else {
-                pv([](const uint4 &w, float (&v)[8]) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = (float)sext_field(w.x, 28 - 4 * e, 4);
-                });
+                    for (int i = 0; i < 4; ++i) {
+                        // round to nearest even; the remainder is exact in
+                        // f32, and so is hi + lo
+                        const uint32_t u = __float_as_uint(pr[i]);
+                        const uint32_t h16 = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                        const float hf = __uint_as_float(h16 << 16);
+                        const uint32_t v = __float_as_uint(pr[i] - hf);
+                        const uint32_t l16 = (v + 0x7FFFu + ((v >> 16) & 1u)) >> 16;
+                        hb[i] = h16;
+                        lb[i] = l16;
+                        l[i] += hf + __uint_as_float(l16 << 16);
+                    }
+                    hi = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                    lo = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+                } else {
+                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                    const h2 a = {(_Float16)pr[0], (_Float16)pr[1]};
+                    const h2 b = {(_Float16)pr[2], (_Float16)pr[3]};
+                    if constexpr (TIER == kHot) {
+                        l[0] += (float)a[0];
+                        l[1] += (float)a[1];
+                        l[2] += (float)b[0];
+                        l[3] += (float)b[1];
+                    }
+                    hi = make_uint2(__builtin_bit_cast(uint32_t, a),
+                                    __builtin_bit_cast(uint32_t, b));
+                    lo = make_uint2(0u, 0u);
+                }
+                *reinterpret_cast<uint2 *>(pt + (16 * tg + c) * 16 + 4 * r) = hi;
+                if constexpr (NP == 2)
+                    *reinterpret_cast<uint2 *>(pt + kTileTok * 16 + (16 * tg + c) * 16 + 4 * r) = lo;
             }
+
+            // ---- P.V on the matrix cores, one 32-token half at a time
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int tg = 2 * half + j;
+                    const bool live = vok[tg];
+                    const int tb = cur.tok[tg];
+                    if (live && tb >= t0 && tb + 16 <= t1)  // whole group visible (uniform)
+                        store_v_group<TIER>(vt, 16 * j, vr[tg], lane, [](int) { return true; });
+                    else
+                        store_v_group<TIER>(vt, 16 * j, vr[tg], lane,
+                                            [&](int tok) { return live && in_range(tb + tok); });
+                    load_v(nxt, tg);  // this group's registers are free again
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // Contraction index k = 8 r + e of lane row r stands for
+                // token 4 r + e (e < 4) or 16 + 4 r + e - 4 (e >= 4) of the
+                // half, for A and B alike, so that the 32 lanes serviced
+                // together by one transposing read touch 8 consecutive tile
+                // rows (no bank conflicts with the 72-word row pitch).
+                // B = P^T: lane supplies those tokens of head c
+                const int s4 = c >> 2, s1 = c & 3;  // this lane's address in its group
+                uint4 bp[NP];
+#pragma unroll
+                for (int part = 0; part < NP; ++part) {
+                    const uint16_t *base = pt + part * kTileTok * 16;
+                    const uint2 x0 = lds_read_tr16(base + (32 * half + 4 * r + s4) * 16 + 4 * s1);
+                    const uint2 x1 =
+                        lds_read_tr16(base + (32 * half + 16 + 4 * r + s4) * 16 + 4 * s1);
+                    bp[part] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+                }
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) {
+                    // A = V^T: lane supplies dim 16 mb + c of the same tokens
+                    const uint2 y0 = lds_read_tr16(vt + (4 * r + s4) * kVPitch + 16 * mb + 4 * s1);
+                    const uint2 y1 =
+                        lds_read_tr16(vt + (16 + 4 * r + s4) * kVPitch + 16 * mb + 4 * s1);
+                    const uint4 av = make_uint4(y0.x, y0.y, y1.x, y1.y);
+#pragma unroll
+                    for (int part = 0; part < NP; ++part)
+                        acc[mb] = mfma16<QT>(av, bp[part], acc[mb]);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();  // P and V tiles are rewritten by the next tile
+            cur = nxt;
         }
-        __builtin_amdgcn_wave_barrier();  // sP is rewritten by the next tile
+    };
+
+    if constexpr (MODE == MODE_TIERED) {
+        // runs of hot, int8 and int4 pages; tier-3 entries name no pool
+        run(TierC<kHot>{}, TierC<0>{}, 0, tier_count[0]);
+        run(TierC<kInt8>{}, TierC<0>{}, tier_count[0], tier_count[1]);
+        run(TierC<kInt4>{}, TierC<0>{}, tier_count[0] + tier_count[1], tier_count[2]);
+        if (tier_count[3] > 0 || !staged) bad = true;
+    } else {
+        run(TierC<kHot>{}, TierC<1>{}, 0, 0);
     }
 
-    // ---- merge: all lanes share the reference max of a head, so the
-    // row-slot accumulators just add; l is summed over the 16 lanes of the
-    // row that holds the head
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = acc[h][e];
-            a += __shfl_xor(a, 16);
-            a += __shfl_xor(a, 32);
-            acc[h][e] = a;
-        }
-    }
+    // ---- merge the waves: l is summed over the 16 lanes of the row holding
+    // the head; the wave's accumulators go to its own (now unused) V tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) l[i] = row16_sum(l[i]);
-    if (r == 0) {
+    __builtin_amdgcn_wave_barrier();
+    float *s_acc = reinterpret_cast<float *>(vt);  // [G][kD] of this wave
+    if (c < G) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * c + e] = acc[h][e];
+            for (int i = 0; i < 4; ++i) s_acc[c * kD + 16 * mb + 4 * r + i] = acc[mb][i];
     }
     if (c == 0) {
 #pragma unroll
@@ -541,7 +659,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             for (int col = lane; col < kD; col += 64) {
                 float o = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) o = fmaf(fw[w], s_acc[w][h][col], o);
+                for (int w = 0; w < kWaves; ++w)
+                    o = fmaf(fw[w], reinterpret_cast<const float *>(s_v[w])[h * kD + col], o);
                 o = L > 0.0f ? o / L : 0.0f;
                 if (any_bad) o = qnan;
                 if (final_here) p.out[orow * kD + col] = o;
@@ -565,6 +684,7 @@ hipError_t by_group(const DecodeParams &p, int group, hipStream_t s) {
     switch (group) {
         case 2: hipLaunchKernelGGL((decode_mfma_kernel<QT, KV, 2, MODE>), grid, block, 0, s, p); break;
         case 4: hipLaunchKernelGGL((decode_mfma_kernel<QT, KV, 4, MODE>), grid, block, 0, s, p); break;
+        case 8: hipLaunchKernelGGL((decode_mfma_kernel<QT, KV, 8, MODE>), grid, block, 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -572,12 +692,14 @@ hipError_t by_group(const DecodeParams &p, int group, hipStream_t s) {
 
 }  // namespace
 
-bool decode_mfma_supported(int kv_type, int head_dim, int group, int mode) {
-    // G = 8 needs more registers than two waves per SIMD allow (spills):
-    // it stays on the vector-ALU kernel
-    if (head_dim != kD || (group != 2 && group != 4)) return false;
+bool decode_mfma_supported(int kv_type, int head_dim, int group, int mode, int page_tokens,
+                           int split_tokens) {
+    if (head_dim != kD || (group != 2 && group != 4 && group != 8)) return false;
     if (mode == MODE_PLAIN) return kv_type == KV_BF16 || kv_type == KV_F16;
-    if (mode == MODE_TIERED) return kv_type == KV_F16;
+    // a tiered split must fit the LDS staging of its page-table entries
+    // (a split starting inside a page touches one page more)
+    if (mode == MODE_TIERED)
+        return kv_type == KV_F16 && split_tokens / page_tokens + 2 <= kDecodeStagedPages;
     return false;
 }
 

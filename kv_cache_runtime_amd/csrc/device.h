@@ -151,13 +151,14 @@ __device__ __forceinline__ bool map_row(const RowMap &m, int row, int &seq, int 
 // Stages the page-table entries lp_first .. lp_first + n - 1 of a split into
 // LDS grouped by tier (entry >> 30: hot, int8, int4, and 3 = invalid), keeping
 // the logical order inside a tier; s_lp receives each staged entry's offset
-// from lp_first.  The ranks come from wave ballots, so the order is fixed
-// (no atomics).  Whole workgroup of 256 threads, n <= 512; ends with a barrier.
+// from lp_first and count[t] (every thread) the number of entries of tier t.
+// The ranks come from wave ballots, so the order is fixed (no atomics).
+// Whole workgroup of 256 threads, n <= 512; ends with a barrier.
 // Folding keys with an online softmax does not depend on their order, so a
 // split may visit its pages in this order: the waves then mostly meet pages of
 // one tier and take one load path.
 __device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, int32_t *s_entry,
-                                                    int16_t *s_lp) {
+                                                    int16_t *s_lp, int (&count)[4]) {
     __shared__ int s_cnt[2][4][4];  // chunk, wave, tier
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int32_t e[2];
@@ -178,6 +179,13 @@ __device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, 
         }
     }
     __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        int sum = 0;
+        for (int c2 = 0; c2 < 2; ++c2)
+            for (int w2 = 0; w2 < 4; ++w2) sum += s_cnt[c2][w2][tt];
+        count[tt] = sum;
+    }
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const int i = ch * 256 + tid;

@@ -124,13 +124,17 @@ struct ValidateParams {
     uint32_t *report;         // [4] counters, zeroed by the launcher's first kernel
 };
 
+// Page-table entries a decode workgroup stages in LDS for its split.
+constexpr int kDecodeStagedPages = 512;
+
 // Launchers (defined next to their kernels).  Each returns the HIP error of
 // the launch.
 hipError_t launch_decode(const DecodeParams &p, int kv_type, int head_dim, int group,
                          int mode, hipStream_t stream);
 hipError_t launch_fold(const FoldParams &f, hipStream_t stream);
 // Matrix-core decode (QK^T on MFMA) for 16-bit and tiered pages.
-bool decode_mfma_supported(int kv_type, int head_dim, int group, int mode);
+bool decode_mfma_supported(int kv_type, int head_dim, int group, int mode, int page_tokens,
+                           int split_tokens);
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_type, int group, int mode,
                               hipStream_t stream);
 // 32-row halves per wave of the matrix-core prefill kernel (1 or 2).
