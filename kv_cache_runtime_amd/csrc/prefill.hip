@@ -183,7 +183,43 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
     const int vk = tid & 7, vd = tid >> 3;
     const int64_t vt_seq = (int64_t)seq * p.max_pages;
     uint4 kreg[4], vreg[4];
+    // Pages of a multiple of 64 tokens hold whole tiles: a full tile then
+    // has one (wave-uniform) page, so its K and V^T bases are scalar and every
+    // thread adds a fixed offset.
+    const bool whole_tiles = p.page_tokens % kTile == 0;
+    const int k_off = 4 * kg * kD + 8 * dc;                  // elements from a K row base
+    const int v_off = 8 * vk + vd * p.page_tokens;           // elements from a V^T page base
+    const int64_t v_step = (int64_t)32 * p.page_tokens;      // dims vd + 32 i
+    auto fetch_whole = [&](int k0) {
+        const int P = p.page_tokens;
+        const int lp = k0 / P;
+        const int r0 = k0 - lp * P;
+        const uint16_t *kb;
+        if (lp < n_regen) {
+            kb = reinterpret_cast<const uint16_t *>(p.regen_k) +
+                 ((((int64_t)seq * p.max_regen + lp) * p.num_kv_heads + g) * P + r0) * kD;
+        } else {
+            int blk = p.page_table[(int64_t)seq * p.max_pages + lp];
+            if (blk < 0 || blk >= p.num_blocks) {
+                bad = true;
+                blk = 0;
+            }
+            kb = reinterpret_cast<const uint16_t *>(p.k_pool) +
+                 (((int64_t)blk * p.num_kv_heads + g) * P + r0) * kD;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kreg[i] = *reinterpret_cast<const uint4 *>(kb + k_off + i * kD);
+        const uint16_t *vb = reinterpret_cast<const uint16_t *>(p.vt) +
+                             ((vt_seq + lp) * p.num_kv_heads + g) * (int64_t)kD * P + r0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            vreg[i] = *reinterpret_cast<const uint4 *>(vb + v_off + i * v_step);
+    };
     auto fetch = [&](int k0) {
+        if (whole_tiles && k0 + kTile <= key_limit) {  // uniform
+            fetch_whole(k0);
+            return;
+        }
         const int key = k0 + 4 * kg;
         if (key < key_limit) {
             const int64_t row = k_row_index(p, seq, g, key, page_of(p, key), n_regen, bad);
@@ -315,8 +351,10 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
                         __builtin_amdgcn_exp2f(fmaf(s[hh][kb][j0 + 2 * i], p.scale_log2, -m_off));
                     const float p1 =
                         __builtin_amdgcn_exp2f(fmaf(s[hh][kb][j0 + 2 * i + 1], p.scale_log2, -m_off));
-                    l[hh] += p0 + p1;
                     const f16x2_t h = {(_Float16)p0, (_Float16)p1};
+                    // l sums the f16 weights the matrix cores use
+                    l[hh] = __builtin_amdgcn_fdot2(h, f16x2_t{(_Float16)1.0f, (_Float16)1.0f},
+                                                   l[hh], false);
                     w[i] = __builtin_bit_cast(uint32_t, h);
                 }
                 pb[hh][st] = make_uint4(w[0], w[1], w[2], w[3]);
