@@ -68,14 +68,17 @@ int env_split_tokens() {
 
 // Tokens per split-K work item.  Fixed in tokens (never derived from the page
 // size or placement) so the arithmetic order, hence the result bits, depend
-// only on the logical problem.  The largest power of two in [256, 2048] that
-// still yields about 16 workgroups per compute unit for the largest context.
+// only on the logical problem.  The largest power of two in [256, 4096] that
+// still yields about 4 workgroups per compute unit when every row has the
+// largest context (longer splits amortise each workgroup's setup and shrink
+// the merge; measured on the decode workloads, 2048-4096 is best whenever the
+// grid stays that full).
 int choose_split_tokens(const atlas_attn_args *a) {
     int t = a->split_tokens > 0 ? a->split_tokens : env_split_tokens();
     if (t > 0) return t;
     const int64_t rows = (int64_t)a->total_q * a->num_kv_heads;
-    const int64_t want = 4096;
-    for (int cand = 2048; cand >= 256; cand >>= 1) {
+    const int64_t want = 1024;
+    for (int cand = 4096; cand >= 256; cand >>= 1) {
         const int64_t items = rows * ((a->max_context_len + cand - 1) / cand);
         if (items >= want) return cand;
     }
@@ -220,6 +223,16 @@ RowMap row_map(const atlas_attn_args *a) {
     return m;
 }
 
+// Division by page_tokens as a multiply-high: x / P == (umulhi(x, magic) +
+// x) >> shift for every x < 2^31 (round-up reciprocal with a 2^shift >= P
+// pre-scale; the sum stays below 2^32 because magic < 2^32 and x < 2^31).
+void page_divider(int32_t page_tokens, uint32_t &magic, uint32_t &shift) {
+    uint32_t sh = 0;
+    while ((1u << sh) < (uint32_t)page_tokens) ++sh;
+    shift = sh;
+    magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << sh) - page_tokens)) / page_tokens + 1);
+}
+
 DecodeParams decode_params(const atlas_attn_args *a, const Plan &plan) {
     DecodeParams p;
     std::memset(&p, 0, sizeof(p));
@@ -237,6 +250,7 @@ DecodeParams decode_params(const atlas_attn_args *a, const Plan &plan) {
     p.total_q = a->total_q;
     p.split_tokens = plan.split_tokens;
     p.max_splits = plan.max_splits;
+    page_divider(a->page_tokens, p.p_magic, p.p_shift);
     p.scale_log2 = a->scale * 1.4426950408889634f;
     char *ws = reinterpret_cast<char *>(a->workspace);
     p.part_o = plan.direct ? nullptr : reinterpret_cast<float *>(ws);
@@ -308,14 +322,7 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
     p.total_q = a->total_q;
     p.max_query_len = a->max_query_len;
     p.q_blocks = plan.q_blocks;
-    {
-        // division by page_tokens as a multiply-high (valid for keys < 2^31)
-        uint32_t sh = 0;
-        while ((1u << sh) < (uint32_t)a->page_tokens) ++sh;
-        p.p_shift = sh;
-        p.p_magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << sh) - a->page_tokens)) /
-                               a->page_tokens + 1);
-    }
+    page_divider(a->page_tokens, p.p_magic, p.p_shift);
     p.scale_log2 = a->scale * 1.4426950408889634f;
     p.out = a->out;
     p.lse = a->lse;

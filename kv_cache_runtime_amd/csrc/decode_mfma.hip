@@ -374,31 +374,38 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         // the 16-position groups of a tile: first token, slot and liveness,
         // all wave-uniform (a group lies in one page)
         struct Groups {
-            int tok[4];
+            int tok[4];       // first token
+            int row[4];       // its row in the page
             uint32_t slot[4];
             bool live[4];
+        };
+        auto page_div = [&](int x) {  // x / P, x < 2^31
+            return (int)((__umulhi((uint32_t)x, p.p_magic) + (uint32_t)x) >> p.p_shift);
         };
         auto groups_of = [&](int tile, Groups &G_) {
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
                 const int q = tile * kTileTok + 16 * tg;
                 bool live;
-                int tok;
+                int tok, row0;
                 uint32_t ent;
                 if constexpr (natural) {
                     tok = t0 + q;
                     live = tile < n_tiles && tok < t1;
-                    const int lp = tok / P;
+                    const int lp = page_div(tok);
+                    row0 = tok - lp * P;
                     ent = live ? (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]) : 0u;
                 } else {
-                    const int pi = q / P;
+                    const int pi = page_div(q);
                     live = tile < n_tiles && pi < np;
                     const int lp = lp_first + (live ? s_lp[sp + pi] : 0);
-                    tok = lp * P + (q - pi * P);
+                    row0 = q - pi * P;
+                    tok = lp * P + row0;
                     ent = live ? (uint32_t)s_pages[sp + pi] : 0u;
                 }
                 if constexpr (MODE == MODE_TIERED) ent &= (1u << 30) - 1u;
                 G_.tok[tg] = __builtin_amdgcn_readfirstlane(tok);
+                G_.row[tg] = __builtin_amdgcn_readfirstlane(row0);
                 G_.slot[tg] = __builtin_amdgcn_readfirstlane(ent);
                 G_.live[tg] = live;
             }
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         auto load_k = [&](const Groups &G_, int tg) {
             kok[tg] = G_.live[tg];
             kscale[tg] = 1.0f;
-            if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.tok[tg] % P + c, r,
+            if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.row[tg] + c, r,
                                                          kr[tg], kscale[tg])) {
                 bad = true;
                 kok[tg] = false;
@@ -422,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         auto load_v = [&](const Groups &G_, int tg) {
             vok[tg] = G_.live[tg];
             vscale[tg] = 1.0f;
-            if (vok[tg] && !load_v_group<KV, TIER>(p, G_.slot[tg], g, G_.tok[tg] % P, lane,
+            if (vok[tg] && !load_v_group<KV, TIER>(p, G_.slot[tg], g, G_.row[tg], lane,
                                                    vr[tg], vscale[tg])) {
                 bad = true;
                 vok[tg] = false;

@@ -30,6 +30,7 @@ struct DecodeParams {
     const int32_t *page_table;
     int32_t num_heads, num_kv_heads, page_tokens, max_pages, num_blocks, total_q;
     int32_t split_tokens, max_splits;
+    uint32_t p_magic, p_shift;  // x / page_tokens == (umulhi(x, p_magic) + x) >> p_shift, x < 2^31
     float scale_log2;         // softmax scale * log2(e)
     float *part_o;            // [total_q * H][max_splits][D]
     float *part_lse;          // [total_q * H][max_splits], natural log
