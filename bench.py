@@ -69,6 +69,27 @@ def algorithmic_work(w):
                 regen_elems=regen_elems)
 
 
+def stream_read_gbps(torch, dev, nbytes: int = 2 << 30, reps: int = 10) -> float:
+    """Read bandwidth of the library's plain streaming-read probe over nbytes
+    (context for the fraction of the 8 TB/s peak)."""
+    from kv_cache_runtime_amd import atlas
+    blocks = 65536  # best of 1024 .. 65536 workgroups on MI355X (5.4-5.7 TB/s)
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    out = torch.empty(blocks, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        atlas.atlas_read_probe(x, out, blocks)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        atlas.atlas_read_probe(x, out, blocks)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps / 1e3
+    del x, out
+    return round(nbytes / t / 1e9, 1)
+
+
 def kernel_sources_digest() -> str:
     """Digest of the HIP sources: HBM byte counts taken with an older build
     no longer describe the kernels."""
@@ -175,6 +196,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--stream", type=int, default=1,
+                    help="also time a plain streaming read of 2 GiB (the library's read "
+                         "probe) as context for the HBM fraction (0 = skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device-to-device copy of this many "
                          "bytes three times (calibrates the HBM byte counters)")
@@ -246,6 +270,8 @@ def main():
     roof["kernel_max_ms"] = round(kern_ms[-1], 5)
     roof["algorithmic_per_launch"] = work["flops"] if prefill else work["kv_bytes"]
 
+    stream = stream_read_gbps(torch, dev) if args.stream else None
+
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -282,6 +308,7 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "context_tokens_per_s_per_head": round(ctx_per_head, 1),
         "roofline": roof,
+        "stream_read_GBps": stream,
         "cpu_baseline": cpu,
     }
     if prefill:

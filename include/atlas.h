@@ -305,6 +305,17 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args,
                                    int32_t check_values, uint32_t *report_dev,
                                    uint32_t *report_host);
 
+/*
+ * Measurement helper (not part of the attention method): reads `bytes`
+ * (multiple of 16, src 16-byte aligned) of device memory once with 16-byte
+ * loads spread over `blocks` workgroups of 256 threads, and writes one xor of
+ * the words read per workgroup to out[0 .. blocks-1] (device, caller-owned).
+ * Timing it gives the streaming read bandwidth the attention kernels are
+ * compared against.  Asynchronous on `stream`.
+ */
+atlas_status atlas_read_probe(const void *src, size_t bytes, uint32_t *out,
+                              int32_t blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

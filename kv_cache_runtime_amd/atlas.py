@@ -90,7 +90,7 @@ EXPORTS = [
     "atlas_abi_version", "atlas_status_string", "atlas_last_error", "atlas_workspace_size",
     "atlas_paged_attention", "atlas_paged_attention_tiered", "atlas_paged_attention_regen",
     "atlas_fold_partials", "atlas_gather_pages", "atlas_regenerate_pages",
-    "atlas_dequant_pages", "atlas_validate_tables",
+    "atlas_dequant_pages", "atlas_validate_tables", "atlas_read_probe",
 ]
 
 _lib = None
@@ -139,6 +139,8 @@ def load(path: str = LIB_PATH):
     L.atlas_validate_tables.restype = _i32
     L.atlas_validate_tables.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools),
                                         ctypes.POINTER(RegenSpec), _i32, _p, _p]
+    L.atlas_read_probe.restype = _i32
+    L.atlas_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, _p]
     if L.atlas_abi_version() != 1:
         raise RuntimeError("libatlas ABI version mismatch")
     _lib = L
@@ -306,6 +308,12 @@ def atlas_validate_tables(args: AttnArgs, pools=None, regen=None, check_values: 
                                         1 if check_values else 0, _ptr(report_dev), host),
            "atlas_validate_tables")
     return [int(x) for x in host]
+
+
+def atlas_read_probe(src, out, blocks: int, stream=None):
+    """Streaming read of the whole tensor `src` (measurement helper)."""
+    _check(load().atlas_read_probe(_ptr(src), int(src.numel() * src.element_size()), _ptr(out),
+                                   int(blocks), _stream(stream)), "atlas_read_probe")
 
 
 # ---------------------------------------------------------------------------

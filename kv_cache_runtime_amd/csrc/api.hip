@@ -630,4 +630,15 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args, const atlas_tier
     return ok();
 }
 
+atlas_status atlas_read_probe(const void *src, size_t bytes, uint32_t *out, int32_t blocks,
+                              void *stream) {
+    if (!src || !out) return fail(ATLAS_EINVAL, "NULL pointer argument");
+    if (bytes % 16) return fail(ATLAS_EINVAL, "bytes %zu is not a multiple of 16", bytes);
+    if (reinterpret_cast<uintptr_t>(src) % 16) return fail(ATLAS_EINVAL, "src is not 16-byte aligned");
+    if (blocks < 1 || blocks > (1 << 20)) return fail(ATLAS_EINVAL, "blocks %d outside [1, 2^20]", blocks);
+    return device_status(launch_read_probe(src, (int64_t)bytes, out, blocks,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                         "read probe launch");
+}
+
 }  // extern "C"

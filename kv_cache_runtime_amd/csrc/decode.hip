@@ -324,66 +324,159 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
         }
     }
 
-    for (int tile = wave; tile < n_tiles; tile += kWaves) {
-        const int tok0 = t0 + tile * TILE + r * U;  // first token of this row-slot
-        float kf[U][E], vf[U][E];
-        SlotData sd{1.0f, 1.0f};
-        bool live = tok0 < t1;
-        if (live) {
-            const int lp = tok0 / p.page_tokens;
-            uint32_t entry = 0;
-            if (!(MODE == MODE_REGEN && lp < n_regen))
-                entry = (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]);
-            if (!load_slot<KV, D, U, MODE>(p, entry, g, tok0, lp, n_regen, c, kf, vf, sd)) {
-                bad = true;
-                live = false;
+    // Resident pages with few registers per token (at most 16 bytes per row
+    // and lane, at most 8 accumulators per lane): software pipeline over
+    // 32-token tiles (8 tokens per row-slot), two register sets used in
+    // turn, so the next tile's K/V loads are in flight while this tile is
+    // folded.  Wider shapes keep the single-buffered loop (their second
+    // register set would halve the waves per SIMD).
+    constexpr int NB = E * hot_bytes<KV>();  // bytes per row and lane
+    constexpr int NW = (NB + 3) / 4;
+    constexpr bool kPipe = MODE == MODE_PLAIN && NW <= 4 && G * E <= 8;
+    if constexpr (kPipe) {
+        constexpr int UP = 8;
+        constexpr int TP = 4 * UP;
+        const int n_tiles_p = t1 > t0 ? (t1 - t0 + TP - 1) / TP : 0;
+        const int P = p.page_tokens;
+        struct Raw {
+            uint32_t k[UP][NW], v[UP][NW];
+            int tok0;
+            bool live;
+        };
+        auto load = [&](int tile, Raw &R) {
+            R.tok0 = t0 + tile * TP + r * UP;  // UP tokens of one page (P % 16 == 0)
+            R.live = tile < n_tiles_p && R.tok0 < t1;
+            if (R.live) {
+                const int lp = R.tok0 / P;
+                const uint32_t slot = (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]);
+                if (slot >= (uint32_t)p.num_blocks) {
+                    bad = true;
+                    R.live = false;
+                } else {
+                    const int64_t row0 = ((int64_t)slot * p.num_kv_heads + g) * P + (R.tok0 - lp * P);
+                    const char *kb = reinterpret_cast<const char *>(p.k_pool) +
+                                     (row0 * D + c * E) * hot_bytes<KV>();
+                    const char *vb = reinterpret_cast<const char *>(p.v_pool) +
+                                     (row0 * D + c * E) * hot_bytes<KV>();
+#pragma unroll
+                    for (int u = 0; u < UP; ++u) {
+                        load_words<NB>(R.k[u], kb + (int64_t)u * D * hot_bytes<KV>());
+                        load_words<NB>(R.v[u], vb + (int64_t)u * D * hot_bytes<KV>());
+                    }
+                }
             }
-        }
-        if (!live) {
+        };
+        auto fold = [&](const Raw &R) {
+            float s[G][UP];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < UP; ++u) {
+                const bool valid = R.live && (R.tok0 + u < t1);
 #pragma unroll
-                for (int e = 0; e < E; ++e) kf[u][e] = vf[u][e] = 0.0f;
-        }
-
-        // scores in the log2 domain, masked past the visible range
-        float s[G][U];
+                for (int h = 0; h < G; ++h) {
+                    float part = 0.0f;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool valid = live && (tok0 + u < t1);
+                    for (int e = 0; e < E; ++e)
+                        part = fmaf(qv[h][e], widen_word<KV>(R.k[u], e), part);
+                    const float dot = row16_sum(part);
+                    s[h][u] = valid ? dot : kNegInf;
+                }
+            }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float part = 0.0f;
+                float mt = s[h][0];
 #pragma unroll
-                for (int e = 0; e < E; ++e) part = fmaf(qv[h][e], kf[u][e], part);
-                const float dot = row16_sum(part) * sd.kscale;
-                s[h][u] = valid ? dot : kNegInf;
+                for (int u = 1; u < UP; ++u) mt = fmaxf(mt, s[h][u]);
+                const float m_new = fmaxf(m[h], mt);
+                const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m[h] - m_use);
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+#pragma unroll
+                for (int u = 0; u < UP; ++u) {
+                    const bool valid = R.live && (R.tok0 + u < t1);
+                    const float pr = __builtin_amdgcn_exp2f(s[h][u] - m_use);
+                    l[h] += pr;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float x = valid ? widen_word<KV>(R.v[u], e) : 0.0f;
+                        acc[h][e] = fmaf(pr, x, acc[h][e]);
+                    }
+                }
+                m[h] = m_new;
             }
-#pragma unroll
-            for (int e = 0; e < E; ++e) vf[u][e] = valid ? vf[u][e] : 0.0f;
+        };
+        Raw A, B;
+        load(wave, A);
+        for (int tile = wave; tile < n_tiles_p; tile += 2 * kWaves) {
+            load(tile + kWaves, B);
+            fold(A);
+            if (tile + kWaves >= n_tiles_p) break;
+            load(tile + 2 * kWaves, A);
+            fold(B);
         }
-
-        // online softmax update of this row-slot's state
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mt = s[h][0];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[h][u]);
-            const float m_new = fmaxf(m[h], mt);
-            const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m[h] - m_use);
-            l[h] *= alpha;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float pr = __builtin_amdgcn_exp2f(s[h][u] - m_use);
-                l[h] += pr;
-                const float pv = pr * sd.vscale;
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vf[u][e], acc[h][e]);
+    } else {
+        for (int tile = wave; tile < n_tiles; tile += kWaves) {
+            const int tok0 = t0 + tile * TILE + r * U;  // first token of this row-slot
+            float kf[U][E], vf[U][E];
+            SlotData sd{1.0f, 1.0f};
+            bool live = tok0 < t1;
+            if (live) {
+                const int lp = tok0 / p.page_tokens;
+                uint32_t entry = 0;
+                if (!(MODE == MODE_REGEN && lp < n_regen))
+                    entry = (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]);
+                if (!load_slot<KV, D, U, MODE>(p, entry, g, tok0, lp, n_regen, c, kf, vf, sd)) {
+                    bad = true;
+                    live = false;
+                }
             }
-            m[h] = m_new;
+            if (!live) {
+    #pragma unroll
+                for (int u = 0; u < U; ++u)
+    #pragma unroll
+                    for (int e = 0; e < E; ++e) kf[u][e] = vf[u][e] = 0.0f;
+            }
+
+            // scores in the log2 domain, masked past the visible range
+            float s[G][U];
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool valid = live && (tok0 + u < t1);
+    #pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float part = 0.0f;
+    #pragma unroll
+                    for (int e = 0; e < E; ++e) part = fmaf(qv[h][e], kf[u][e], part);
+                    const float dot = row16_sum(part) * sd.kscale;
+                    s[h][u] = valid ? dot : kNegInf;
+                }
+    #pragma unroll
+                for (int e = 0; e < E; ++e) vf[u][e] = valid ? vf[u][e] : 0.0f;
+            }
+
+            // online softmax update of this row-slot's state
+    #pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float mt = s[h][0];
+    #pragma unroll
+                for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[h][u]);
+                const float m_new = fmaxf(m[h], mt);
+                const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m[h] - m_use);
+                l[h] *= alpha;
+    #pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float pr = __builtin_amdgcn_exp2f(s[h][u] - m_use);
+                    l[h] += pr;
+                    const float pv = pr * sd.vscale;
+    #pragma unroll
+                    for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vf[u][e], acc[h][e]);
+                }
+                m[h] = m_new;
+            }
         }
     }
 

@@ -304,6 +304,33 @@ __global__ __launch_bounds__(256) void validate_kernel(const ValidateParams v) {
     if (threadIdx.x < 4 && s_cnt[threadIdx.x]) atomicAdd(&v.report[threadIdx.x], s_cnt[threadIdx.x]);
 }
 
+
+// ---- streaming read probe (measurement helper) ------------------------------
+// Every thread reads 16-byte words with a grid stride and folds them into one
+// xor; one word per workgroup is written so the loads cannot be dropped.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4 *src, int64_t n16,
+                                                         uint32_t *out) {
+    uint32_t x = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = src[i];
+        x ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    __shared__ uint32_t s_x[256];
+    s_x[threadIdx.x] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t y = 0;
+        for (int t = 0; t < 256; ++t) y ^= s_x[t];
+        out[blockIdx.x] = y;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
@@ -351,6 +378,14 @@ hipError_t launch_validate(const ValidateParams &v, hipStream_t stream) {
     if (v.p.rows.num_seqs <= 0 || chunks <= 0) return hipSuccess;
     hipLaunchKernelGGL(validate_kernel, dim3((unsigned)v.p.rows.num_seqs, (unsigned)chunks),
                        dim3(256), 0, stream, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int blocks,
+                             hipStream_t stream) {
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4 *>(src), bytes / 16, out);
     return hipGetLastError();
 }
 

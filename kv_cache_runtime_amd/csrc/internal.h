@@ -151,6 +151,8 @@ hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *
                          int32_t num_blocks, int32_t elem_bytes, int32_t num_tokens,
                          void *k_out, void *v_out, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams &v, hipStream_t stream);
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int blocks,
+                             hipStream_t stream);
 hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,
                           const int32_t *entries, int32_t n, float *k_out, float *v_out,
                           hipStream_t stream);

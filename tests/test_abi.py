@@ -202,3 +202,11 @@ def test_validate_tables_arguments_are_checked():
     pools.num_int8 = 2  # scales missing, values requested
     assert L.atlas_validate_tables(ctypes.byref(_args(kv_dtype=atlas.F16)), ctypes.byref(pools),
                                    None, 1, FAKE, None) == atlas.EINVAL
+
+
+def test_read_probe_arguments_are_checked():
+    L = atlas.load()
+    assert L.atlas_read_probe(None, 16, FAKE, 4, None) == atlas.EINVAL
+    assert L.atlas_read_probe(FAKE, 24, FAKE, 4, None) == atlas.EINVAL
+    assert L.atlas_read_probe(FAKE + 8, 32, FAKE, 4, None) == atlas.EINVAL
+    assert L.atlas_read_probe(FAKE, 32, FAKE, 0, None) == atlas.EINVAL

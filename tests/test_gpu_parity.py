@@ -490,3 +490,14 @@ def test_validate_tables_tiered_and_regen(gpu):
     assert p5.validate() == [0, 0, 0, 0]
     p5.regen_pages[0] = int(w5.regen["regen_pages"].max()) + 1
     assert p5.validate()[1] == 1
+
+
+def test_read_probe_reads_every_word(gpu):
+    n = (1 << 20) + 4 * 37  # words; not a multiple of the grid stride
+    x = torch.randint(0, 2**31 - 1, (n,), dtype=torch.int32, device=gpu)
+    out = torch.zeros(64, dtype=torch.int32, device=gpu)
+    atlas.atlas_read_probe(x, out, 64)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(x.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == want
