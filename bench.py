@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--stream", type=int, default=1,
                     help="also time a plain streaming read of 2 GiB (the library's read "
                          "probe) as context for the HBM fraction (0 = skip)")
+    ap.add_argument("--flush-mib", type=int, default=-1,
+                    help="after timing, time calls with this many MiB written between them "
+                         "(Infinity Cache flushed); -1 = 512 for config 1, else off")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device-to-device copy of this many "
                          "bytes three times (calibrates the HBM byte counters)")
@@ -272,6 +275,38 @@ def main():
 
     stream = stream_read_gbps(torch, dev) if args.stream else None
 
+    # cold calls: the Infinity Cache (MALL) is flushed by writing flush_mib
+    # MiB between calls, so a small working set is read from HBM again
+    flush_mib = args.flush_mib if args.flush_mib >= 0 else (512 if args.config == 1 else 0)
+    cold = None
+    if flush_mib > 0:
+        junk = torch.empty(flush_mib << 18, dtype=torch.float32, device=dev)
+        reps = min(K, 20)
+        calls, kerns = [], []
+        for i in range(reps):
+            junk.fill_(float(i))
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0.record()  # creates the HIP events; re-recorded by the library
+            k1.record()
+            c0.record()
+            prob.args.profile_events[0] = k0.cuda_event
+            prob.args.profile_events[1] = k1.cuda_event
+            prob.run()
+            c1.record()
+            torch.cuda.synchronize()
+            calls.append(c0.elapsed_time(c1))
+            kerns.append(k0.elapsed_time(k1))
+        prob.args.profile_events[0] = None
+        prob.args.profile_events[1] = None
+        del junk
+        calls.sort()
+        kerns.sort()
+        cold = {"flush_mib": flush_mib, "reps": reps,
+                "call_ms_median": round(calls[reps // 2], 5),
+                "kernel_ms_median": round(kerns[reps // 2], 5),
+                "kv_GBps_call": round(work["kv_bytes"] / (calls[reps // 2] / 1e3) / 1e9, 2)}
+
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -309,6 +344,7 @@ def main():
         "context_tokens_per_s_per_head": round(ctx_per_head, 1),
         "roofline": roof,
         "stream_read_GBps": stream,
+        "cold": cold,
         "cpu_baseline": cpu,
     }
     if prefill:
