@@ -162,95 +162,63 @@ __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry,
 
 // Log-sum-exp merge of `nsplit` normalised partials of one output row
 // (attnres AGENTS.md, "online softmax merge"): lse = M + log sum_s
-// exp(lse_s - M), out = sum_s exp(lse_s - lse) o_s.  Whole workgroup (256
-// threads).  Weights go through LDS in chunks of kMergeChunk splits; each
-// wave sums a fixed quarter of a chunk and the quarters are added in wave
-// order, so the arithmetic order is fixed.  Any NaN partial makes the row NaN;
-// a row whose splits are all empty gets out 0 and lse -inf.  head_dim <= 256.
-constexpr int kMergeChunk = 1024;
-
-__device__ void merge_row(const float *pl, int64_t l_stride, const float *po, int64_t o_stride,
-                          int nsplit, int D, float *out, float *lse_out) {
-    __shared__ float s_w[kMergeChunk];
-    __shared__ float s_red[kWaves][256];
-    __shared__ float s_sum[kWaves];
+// exp(lse_s - M), out = sum_s exp(lse_s - lse) o_s.  One wave per row: lane
+// l owns dims l + 64 k (k < KD).  The splits are folded in chunks of 32 / KD
+// with a running max, every load of a chunk issued before its first use, so
+// a row costs one memory round trip per chunk and no barrier.  The order is
+// fixed (deterministic).  Any NaN partial makes the row NaN; a row whose
+// splits are all empty gets out 0 and lse -inf.
+template <int KD>
+__device__ void merge_row_wave(const float *pl, int64_t l_stride, const float *po,
+                               int64_t o_stride, int nsplit, int D, float *out, float *lse_out,
+                               int lane) {
+    constexpr int C = 32 / KD;
     const float kNegInf = -__builtin_inff();
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    float M = kNegInf;
-    int nan = 0;
-    for (int s = tid; s < nsplit; s += 256) {
-        const float x = pl[s * l_stride];
-        nan |= (x != x);
-        M = fmaxf(M, x);
-    }
+    float M = kNegInf, L = 0.0f, acc[KD];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if (lane == 0) s_sum[wave] = M;
-    const bool any_nan = __syncthreads_or(nan) != 0;
-    M = fmaxf(fmaxf(s_sum[0], s_sum[1]), fmaxf(s_sum[2], s_sum[3]));
-    const float M_use = (M == kNegInf) ? 0.0f : M;
-    __syncthreads();
-
-    float lsum = 0.0f;
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c0 = 0; c0 < nsplit; c0 += kMergeChunk) {
-        const int cn = min(kMergeChunk, nsplit - c0);
-        for (int s = tid; s < cn; s += 256) {
-            const float x = pl[(c0 + s) * l_stride];
-            const float w = (x == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((x - M_use) * kLog2e);
-            s_w[s] = w;
-            lsum += w;
-        }
-        __syncthreads();
-        const int per = (cn + kWaves - 1) / kWaves;
-        const int s0 = wave * per, s1 = min(cn, s0 + per);
-        // batches of 8 partial rows: their loads are all issued before the
-        // first use, so the loop pays one memory latency per batch, not per row
-        constexpr int kBatch = 8;
-        for (int sb = s0; sb < s1; sb += kBatch) {
-            float x[kBatch][4];
+    for (int k = 0; k < KD; ++k) acc[k] = 0.0f;
+    bool nan = false;
+    for (int c0 = 0; c0 < nsplit; c0 += C) {
+        float ls[C], ov[C][KD];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int s = sb + j;
-                const float *row = po + (int64_t)(c0 + min(s, s1 - 1)) * o_stride;
+        for (int j = 0; j < C; ++j) {
+            const bool in = c0 + j < nsplit;
+            ls[j] = in ? pl[(int64_t)(c0 + j) * l_stride] : kNegInf;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int col = lane + 64 * i;
-                    x[j][i] = (col < D) ? row[col] : 0.0f;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (sb + j >= s1) break;
-                const float w = s_w[sb + j];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = fmaf(w, x[j][i], a[i]);
+            for (int k = 0; k < KD; ++k) {
+                const int d = lane + 64 * k;
+                ov[j][k] = (in && d < D) ? po[(int64_t)(c0 + j) * o_stride + d] : 0.0f;
             }
         }
-        __syncthreads();
-    }
+        float mc = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int col = lane + 64 * i;
-        if (col < D) s_red[wave][col] = a[i];
-    }
+        for (int j = 0; j < C; ++j) {
+            nan = nan || (ls[j] != ls[j]);
+            mc = fmaxf(mc, ls[j]);
+        }
+        const float m_new = fmaxf(M, mc);
+        if (m_new == kNegInf) continue;  // every split so far is empty
+        const float f = (M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((M - m_new) * kLog2e);
+        L *= f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
-    if (lane == 0) s_sum[wave] = lsum;
-    __syncthreads();
-    const float L = ((s_sum[0] + s_sum[1]) + s_sum[2]) + s_sum[3];
+        for (int k = 0; k < KD; ++k) acc[k] *= f;
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const float w =
+                (ls[j] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((ls[j] - m_new) * kLog2e);
+            L += w;
+#pragma unroll
+            for (int k = 0; k < KD; ++k) acc[k] = fmaf(w, ov[j][k], acc[k]);
+        }
+        M = m_new;
+    }
     const float qnan = __builtin_nanf("");
-    for (int col = tid; col < D; col += 256) {
-        float o = ((s_red[0][col] + s_red[1][col]) + s_red[2][col]) + s_red[3][col];
-        o = (L > 0.0f) ? o / L : 0.0f;
-        out[col] = any_nan ? qnan : o;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) out[d] = nan ? qnan : (L > 0.0f ? acc[k] / L : 0.0f);
     }
-    if (tid == 0) {
-        const float l = (L > 0.0f) ? M + logf(L) : kNegInf;
-        *lse_out = any_nan ? qnan : l;
-    }
-    __syncthreads();
+    if (lane == 0) *lse_out = nan ? qnan : (L > 0.0f ? M + logf(L) : kNegInf);
 }
 
 template <int KV, int D, int G, int MODE>
@@ -551,10 +519,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     }
 }
 
-// Split merge: one workgroup per merged row.  With fixed_splits == 0 the
-// number of splits of a row follows from its visible keys (decode path).
+// Split merge: one wave per merged row, four rows per workgroup.  With
+// fixed_splits == 0 the number of splits of a row follows from its visible
+// keys (decode path).
+template <int KD>
 __global__ __launch_bounds__(256) void fold_kernel(const FoldParams f) {
-    const int idx = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int idx = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (idx >= f.rows) return;
     int nsplit = f.fixed_splits;
     if (nsplit <= 0) {
@@ -563,9 +534,9 @@ __global__ __launch_bounds__(256) void fold_kernel(const FoldParams f) {
         nsplit = splits_of(vis, f.split_tokens);
         if (nsplit == 1) return;  // written directly by the attention kernel
     }
-    merge_row(f.part_lse + (int64_t)idx * f.l_row_stride, f.l_split_stride,
-              f.part_o + (int64_t)idx * f.o_row_stride, f.o_split_stride, nsplit,
-              f.head_dim, f.out + (int64_t)idx * f.head_dim, f.lse + idx);
+    merge_row_wave<KD>(f.part_lse + (int64_t)idx * f.l_row_stride, f.l_split_stride,
+                       f.part_o + (int64_t)idx * f.o_row_stride, f.o_split_stride, nsplit,
+                       f.head_dim, f.out + (int64_t)idx * f.head_dim, f.lse + idx, lane);
 }
 
 template <int KV, int D, int G, int MODE>
@@ -620,8 +591,13 @@ hipError_t launch_decode(const DecodeParams &p, int kv_type, int head_dim, int g
 
 hipError_t launch_fold(const FoldParams &f, hipStream_t stream) {
     if (f.rows <= 0) return hipSuccess;
-    const unsigned blocks = (unsigned)f.rows;
-    hipLaunchKernelGGL(fold_kernel, dim3(blocks), dim3(256), 0, stream, f);
+    const unsigned blocks = (unsigned)((f.rows + 3) / 4);
+    if (f.head_dim <= 64)
+        hipLaunchKernelGGL(fold_kernel<1>, dim3(blocks), dim3(256), 0, stream, f);
+    else if (f.head_dim <= 128)
+        hipLaunchKernelGGL(fold_kernel<2>, dim3(blocks), dim3(256), 0, stream, f);
+    else
+        hipLaunchKernelGGL(fold_kernel<4>, dim3(blocks), dim3(256), 0, stream, f);
     return hipGetLastError();
 }
 
