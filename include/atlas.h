@@ -202,12 +202,14 @@ atlas_status atlas_workspace_size(const atlas_attn_args *args,
  * kv_dtype F32, BF16 or F16; q_dtype F32 with F32 K/V, otherwise BF16 or F16.
  * head_dim 64 or 128; num_heads / num_kv_heads in {1, 2, 4, 8}.  Decode
  * rows are split over pages (split-K) and merged by log-sum-exp; with 16-bit
- * K/V, head_dim 128 and 2 or 4 query heads per kv head QK^T runs on matrix
- * cores and PV on the vector ALUs, otherwise both run on the vector ALUs.
- * Chunked prefill over BF16/F16 K/V (q of the same type) with head_dim 128
- * runs QK^T and PV on matrix cores (MFMA); other prefill shapes use the
- * vector-ALU kernel.  On matrix cores PV takes the probabilities and V in
- * f16, so V must lie within the f16 range (|v| <= 65504).
+ * K/V (q of the same type), head_dim 128 and 2, 4 or 8 query heads per kv
+ * head both products run on matrix cores (PV with P as f16 for F16 pages and
+ * as a bf16 hi + lo pair for BF16 pages, so decode has no range limit on V),
+ * otherwise on the vector ALUs.  Chunked prefill over BF16/F16 K/V (q of the
+ * same type) with head_dim 128 runs QK^T and PV on matrix cores; other
+ * prefill shapes use the vector-ALU kernel.  Prefill PV takes the
+ * probabilities and V in f16, so there V must lie within the f16 range
+ * (|v| <= 65504).
  */
 atlas_status atlas_paged_attention(const atlas_attn_args *args);
 
@@ -217,10 +219,11 @@ atlas_status atlas_paged_attention(const atlas_attn_args *args);
  * slots); int8 and int4 pages from `pools`.  Decode only (query_start must be
  * NULL).  Codes are decoded in registers and the per-page scales are applied
  * to the dot products and to the probabilities, never written back.  With
- * F16 hot pages, head_dim 128 and 2 or 4 query heads per kv head, QK^T runs
- * on matrix cores in f16: the codes convert exactly, q is rounded to f16
- * (exact for bf16 q with 2^-14 <= |q| <= 65504; smaller magnitudes carry an
- * absolute error of at most 2^-25, larger ones are out of range).
+ * F16 hot pages, head_dim 128 and 2, 4 or 8 query heads per kv head both
+ * products run on matrix cores in f16 (when a split spans at most 510
+ * pages): the codes convert exactly, q is rounded to f16 (exact for bf16 q
+ * with 2^-14 <= |q| <= 65504; smaller magnitudes carry an absolute error of
+ * at most 2^-25, larger ones are out of range).
  */
 atlas_status atlas_paged_attention_tiered(const atlas_attn_args *args,
                                           const atlas_tier_pools *pools);
