@@ -177,9 +177,18 @@ def cpu_baseline(w, work, budget_s: float = 20.0):
     frac = done_pairs / max(1, work["pairs"])
     kv_rate = work["kv_bytes"] * frac / dt / 1e9
     n_groups = len(chosen)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(kv_rate, 6), "unit": "GB/s",
-        "cores": cores, "kind": "oracle",
+        "cores": cores, "kind": "oracle", "cpu_model": cpu_model,
         "context_tokens_per_s_per_head": round(work["ctx_head_tokens"] * frac / dt, 1),
         "seconds": round(dt, 3),
         "sample": f"{n_groups} of {len(groups)} (sequence, kv head) groups "
