@@ -13,6 +13,8 @@ from .oracle import (  # noqa: F401
     int4_codes,
     logical_kv,
     merge_splits,
+    pack_int4,
+    quantize_block,
     reference,
     regen_values,
     row_info,

@@ -192,6 +192,32 @@ def dequant_f32(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
             ).astype(np.float32)
 
 
+def quantize_block(x: np.ndarray, qmax: int):
+    """Symmetric encoding of one (page, kv head) block of K or V into cold-tier
+    codes (argus-cache, "Visual Architecture": INT8 and INT4 tiers; reading:
+    one f32 scale per block, symmetric, round half to even).
+
+    scale = f32(max |x|) / qmax and code = clamp(rint(f32(x) / scale), -qmax,
+    qmax), both divisions in f32 with correct rounding, so that a device
+    computing in f32 takes the same integer decisions.  An all-zero block gets
+    scale 0 and codes 0.  Returns (int16 codes of x's shape, np.float32 scale).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    scale = np.float32(amax / np.float32(qmax))
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.int16), np.float32(0.0)
+    q = np.rint(np.divide(x, scale, dtype=np.float32))
+    return np.clip(q, -qmax, qmax).astype(np.int16), scale
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, element 2i in the low nibble of byte i (the
+    argus-cache INT4 "2-way bit-packed" layout as read here)."""
+    c = np.asarray(codes).astype(np.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
 # ---------------------------------------------------------------------------
 # Paged problems (synth.Paged) -> logical per-sequence K/V and references
 # ---------------------------------------------------------------------------

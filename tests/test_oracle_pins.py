@@ -436,3 +436,49 @@ def test_cfr_bench_byte_accounting():
     assert per_head_kv == int(g["baseline_kv_bytes"])
     assert scratch == int(g["cfr_scratch_bytes"])
     assert per_head_kv / scratch == float(g["estimated_memory_reduction"]) == ctx / P
+
+
+# ---------------------------------------------------------------------------
+# Cold-tier encoding (page demotion)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_quantize_block_is_the_nearest_code(qmax):
+    """Brute force: each code is the integer in [-qmax, qmax] nearest to
+    x / scale (ties to even), found by exhaustive search."""
+    rng = np.random.default_rng(qmax)
+    x = (rng.standard_normal(96) * 1.7).astype(np.float32)
+    codes, scale = oracle.quantize_block(x, qmax)
+    assert scale == np.float32(np.max(np.abs(x)) / np.float32(qmax))
+    cand = np.arange(-qmax, qmax + 1, dtype=np.float64)
+    for xi, ci in zip(x, codes):
+        t = np.float64(np.float32(xi / scale))
+        d = np.abs(cand - t)
+        best = cand[d == d.min()]
+        want = best[0] if best.size == 1 else best[np.argmin(np.abs(best) % 2)]
+        assert ci == want
+
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_quantize_block_extremes_symmetry_and_round_trip(qmax):
+    rng = np.random.default_rng(3 + qmax)
+    x = rng.standard_normal((16, 64)).astype(np.float32)
+    codes, scale = oracle.quantize_block(x, qmax)
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert abs(int(codes[i])) == qmax and np.sign(codes[i]) == np.sign(x[i])
+    assert np.all(np.abs(codes) <= qmax)
+    err = np.abs(x.astype(np.float64) - codes.astype(np.float64) * float(scale))
+    assert np.all(err <= 0.5 * float(scale) * (1 + 1e-5))
+    nc, ns = oracle.quantize_block(-x, qmax)
+    assert ns == scale and np.array_equal(nc, -codes)
+    pc, ps = oracle.quantize_block(x * np.float32(8.0), qmax)   # power-of-two scaling
+    assert ps == scale * np.float32(8.0) and np.array_equal(pc, codes)
+
+
+def test_quantize_block_zero_and_int4_packing():
+    codes, scale = oracle.quantize_block(np.zeros((4, 8), np.float32), 7)
+    assert scale == 0 and not codes.any()
+    c = np.array([[-7, 7, 0, -1, 3, -8, 5, 2]], dtype=np.int16)
+    packed = oracle.pack_int4(c)
+    assert packed.tolist() == [[0x79, 0xF0, 0x83, 0x25]]
+    assert np.array_equal(oracle.int4_codes(packed), c)
