@@ -309,6 +309,44 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args,
                                    uint32_t *report_host);
 
 /*
+ * KV write path (the write side of the cache the attention calls read).
+ *
+ * atlas_write_kv: every query row of `args` (a decode token, or a token of a
+ * prefill chunk) owns the key at its own position ctx - n_q + t; its K and V
+ * rows k_new / v_new[row][kv_head][head_dim] (kv_dtype, device, 16-byte
+ * aligned like the pools) are written to row pos % page_tokens of block
+ * page_table[s][pos / page_tokens] of args->k_pool / v_pool, so that the
+ * attention call on the same arguments sees them.  The pools are written
+ * through args' pointers.  Rows whose block id or context length is invalid
+ * are skipped (atlas_validate_tables counts them).  Same argument checks as
+ * atlas_paged_attention; asynchronous on args->stream.
+ */
+atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,
+                            const void *v_new);
+
+/*
+ * atlas_demote_pages: encodes hot pages into the cold tiers (argus-cache,
+ * "Visual Architecture": FP16 -> INT8 -> INT4).  For i < n, hot block
+ * src_slots[i] of args->k_pool / v_pool (kv_dtype F16 or BF16, every row
+ * finite) is encoded into dst_entries[i] = (tier << 30) | slot, tier 1 (int8)
+ * or 2 (int4) of `pools`: for each kv head, K and V separately,
+ *     scale = max|x| / qmax            (f32, correctly rounded; qmax 127 / 7)
+ *     code  = clamp(rint(x / scale), -qmax, qmax)   (round half to even)
+ * and an all-zero block gets scale 0 and codes 0.  Codes and scales are
+ * written through the pools' pointers; the caller then points its page-table
+ * entries at dst_entries.  A destination outside its pool rejects the page
+ * (nothing written); a source block outside the hot pool writes NaN scales,
+ * so rows reading the page fail loudly.  Each rejected page adds 1 to
+ * *rejected (device int32, optional).  The source and destination sets must
+ * not overlap between calls in flight.  Asynchronous on args->stream.
+ */
+atlas_status atlas_demote_pages(const atlas_attn_args *args,
+                                const atlas_tier_pools *pools,
+                                const int32_t *src_slots,
+                                const int32_t *dst_entries, int32_t n,
+                                int32_t *rejected);
+
+/*
  * Measurement helper (not part of the attention method): reads `bytes`
  * (multiple of 16, src 16-byte aligned) of device memory once with 16-byte
  * loads spread over `blocks` workgroups of 256 threads, and writes one xor of

@@ -91,6 +91,7 @@ EXPORTS = [
     "atlas_paged_attention", "atlas_paged_attention_tiered", "atlas_paged_attention_regen",
     "atlas_fold_partials", "atlas_gather_pages", "atlas_regenerate_pages",
     "atlas_dequant_pages", "atlas_validate_tables", "atlas_read_probe",
+    "atlas_write_kv", "atlas_demote_pages",
 ]
 
 _lib = None
@@ -139,6 +140,11 @@ def load(path: str = LIB_PATH):
     L.atlas_validate_tables.restype = _i32
     L.atlas_validate_tables.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools),
                                         ctypes.POINTER(RegenSpec), _i32, _p, _p]
+    L.atlas_write_kv.restype = _i32
+    L.atlas_write_kv.argtypes = [ctypes.POINTER(AttnArgs), _p, _p]
+    L.atlas_demote_pages.restype = _i32
+    L.atlas_demote_pages.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools), _p, _p,
+                                     _i32, _p]
     L.atlas_read_probe.restype = _i32
     L.atlas_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, _p]
     if L.atlas_abi_version() != 1:
@@ -308,6 +314,18 @@ def atlas_validate_tables(args: AttnArgs, pools=None, regen=None, check_values: 
                                         1 if check_values else 0, _ptr(report_dev), host),
            "atlas_validate_tables")
     return [int(x) for x in host]
+
+
+def atlas_write_kv(args: AttnArgs, k_new, v_new):
+    """Write each query row's K/V rows into the page of its own position."""
+    _check(load().atlas_write_kv(ctypes.byref(args), _ptr(k_new), _ptr(v_new)), "atlas_write_kv")
+
+
+def atlas_demote_pages(args: AttnArgs, pools: TierPools, src_slots, dst_entries, rejected=None):
+    """Encode hot blocks src_slots[i] into cold entries dst_entries[i]."""
+    _check(load().atlas_demote_pages(ctypes.byref(args), ctypes.byref(pools), _ptr(src_slots),
+                                     _ptr(dst_entries), int(src_slots.numel()), _ptr(rejected)),
+           "atlas_demote_pages")
 
 
 def atlas_read_probe(src, out, blocks: int, stream=None):

@@ -641,4 +641,81 @@ atlas_status atlas_read_probe(const void *src, size_t bytes, uint32_t *out, int3
                          "read probe launch");
 }
 
+atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new, const void *v_new) {
+    Plan plan;
+    atlas_status st = check_common(args, false, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if (!k_new || !v_new) return fail(ATLAS_EINVAL, "NULL k_new or v_new");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16 ||
+        reinterpret_cast<uintptr_t>(args->k_pool) % 16 ||
+        reinterpret_cast<uintptr_t>(args->v_pool) % 16)
+        return fail(ATLAS_EINVAL, "k_new, v_new and the pools must be 16-byte aligned");
+    WriteKvParams w;
+    std::memset(&w, 0, sizeof(w));
+    w.rows = row_map(args);
+    w.k_new = k_new;
+    w.v_new = v_new;
+    w.k_pool = const_cast<void *>(args->k_pool);
+    w.v_pool = const_cast<void *>(args->v_pool);
+    w.page_table = args->page_table;
+    w.num_kv_heads = args->num_kv_heads;
+    w.head_dim = args->head_dim;
+    w.page_tokens = args->page_tokens;
+    w.max_pages = args->max_pages_per_seq;
+    w.num_blocks = args->num_blocks;
+    w.total_q = args->total_q;
+    w.elem_bytes = args->kv_dtype == ATLAS_F32 ? 4 : 2;
+    return device_status(launch_write_kv(w, reinterpret_cast<hipStream_t>(args->stream)),
+                         "write launch");
+}
+
+atlas_status atlas_demote_pages(const atlas_attn_args *args, const atlas_tier_pools *pools,
+                                const int32_t *src_slots, const int32_t *dst_entries, int32_t n,
+                                int32_t *rejected) {
+    Plan plan;
+    atlas_status st = check_common(args, true, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if (!pools || pools->struct_size != sizeof(atlas_tier_pools))
+        return fail(ATLAS_EINVAL, "pools NULL or wrong struct_size");
+    if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
+        return fail(ATLAS_EUNSUPPORTED, "hot pages must be F16 or BF16");
+    if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
+    if (n == 0) return ok();
+    if (!src_slots || !dst_entries) return fail(ATLAS_EINVAL, "NULL src_slots or dst_entries");
+    if (pools->num_int8 < 0 || pools->num_int4 < 0)
+        return fail(ATLAS_EINVAL, "negative tier pool size");
+    if (pools->num_int8 > 0 && (!pools->int8_k || !pools->int8_v || !pools->int8_k_scale ||
+                                !pools->int8_v_scale))
+        return fail(ATLAS_EINVAL, "NULL int8 pool pointer");
+    if (pools->num_int4 > 0 && (!pools->int4_k || !pools->int4_v || !pools->int4_k_scale ||
+                                !pools->int4_v_scale))
+        return fail(ATLAS_EINVAL, "NULL int4 pool pointer");
+    if ((int64_t)n * args->num_kv_heads * 2 > INT32_MAX) return fail(ATLAS_EINVAL, "n too large");
+    DemoteParams d;
+    std::memset(&d, 0, sizeof(d));
+    d.k_pool = args->k_pool;
+    d.v_pool = args->v_pool;
+    d.kv_type = args->kv_dtype;
+    d.num_kv_heads = args->num_kv_heads;
+    d.head_dim = args->head_dim;
+    d.page_tokens = args->page_tokens;
+    d.num_blocks = args->num_blocks;
+    d.src_slots = src_slots;
+    d.dst_entries = dst_entries;
+    d.n = n;
+    d.i8_k = const_cast<int8_t *>(pools->int8_k);
+    d.i8_v = const_cast<int8_t *>(pools->int8_v);
+    d.i8_ks = const_cast<float *>(pools->int8_k_scale);
+    d.i8_vs = const_cast<float *>(pools->int8_v_scale);
+    d.i4_k = const_cast<uint8_t *>(pools->int4_k);
+    d.i4_v = const_cast<uint8_t *>(pools->int4_v);
+    d.i4_ks = const_cast<float *>(pools->int4_k_scale);
+    d.i4_vs = const_cast<float *>(pools->int4_v_scale);
+    d.n_i8 = pools->num_int8;
+    d.n_i4 = pools->num_int4;
+    d.rejected = rejected;
+    return device_status(launch_demote(d, reinterpret_cast<hipStream_t>(args->stream)),
+                         "demote launch");
+}
+
 }  // extern "C"

@@ -125,6 +125,32 @@ struct ValidateParams {
     uint32_t *report;         // [4] counters, zeroed by the launcher's first kernel
 };
 
+// New tokens' K/V rows written into their pages (one row per query row).
+struct WriteKvParams {
+    RowMap rows;
+    const void *k_new, *v_new;  // [total_q][Hkv][D]
+    void *k_pool, *v_pool;      // [num_blocks][Hkv][P][D]
+    const int32_t *page_table;
+    int32_t num_kv_heads, head_dim, page_tokens, max_pages, num_blocks, total_q;
+    int32_t elem_bytes;
+};
+
+// Hot pages encoded into int8 / int4 cold-tier slots.
+struct DemoteParams {
+    const void *k_pool, *v_pool;   // hot pool, bf16 or f16
+    int32_t kv_type;
+    int32_t num_kv_heads, head_dim, page_tokens, num_blocks;
+    const int32_t *src_slots;      // [n] hot blocks
+    const int32_t *dst_entries;    // [n] (tier << 30) | slot, tier 1 or 2
+    int32_t n;
+    int8_t *i8_k, *i8_v;
+    float *i8_ks, *i8_vs;
+    uint8_t *i4_k, *i4_v;
+    float *i4_ks, *i4_vs;
+    int32_t n_i8, n_i4;
+    int32_t *rejected;             // device counter or null
+};
+
 // Page-table entries a decode workgroup stages in LDS for its split.
 constexpr int kDecodeStagedPages = 512;
 
@@ -151,6 +177,8 @@ hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *
                          int32_t num_blocks, int32_t elem_bytes, int32_t num_tokens,
                          void *k_out, void *v_out, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams &v, hipStream_t stream);
+hipError_t launch_write_kv(const WriteKvParams &w, hipStream_t stream);
+hipError_t launch_demote(const DemoteParams &d, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int blocks,
                              hipStream_t stream);
 hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,

@@ -1,0 +1,145 @@
+// The KV write path: new tokens' K/V written into their pages, and hot pages
+// demoted into the int8 / int4 cold tiers.
+//
+// Writing: every query row of a call (a decode token, or a token of a prefill
+// chunk) owns the key at its own position, ctx - n_q + t; its K/V rows go to
+// row pos % P of block page_table[s][pos / P] of every kv head (CFR-Atlas
+// README, PageKey and token ranges; the pages are written in place, never
+// concatenated).
+//
+// Demotion (argus-cache, "Visual Architecture": FP16 -> INT8 -> INT4 tiers):
+// one block per (page, kv head, K|V) gets a symmetric f32 scale max|x| / qmax
+// and codes rint(x / scale) clamped to [-qmax, qmax]; both divisions are
+// correctly rounded f32 so the integer decisions are reproducible.  int4
+// codes are two's-complement nibbles, element 2i in the low nibble of byte i.
+#include "device.h"
+
+namespace atlas {
+
+namespace {
+
+// One thread per 16-byte chunk of a (row, kv head) K or V row.
+__global__ __launch_bounds__(256) void write_kv_kernel(const WriteKvParams w) {
+    const int64_t chunks_per_row = (int64_t)w.head_dim * w.elem_bytes / 16;
+    const int64_t total = (int64_t)w.total_q * w.num_kv_heads * chunks_per_row;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t ch = i % chunks_per_row;
+        const int64_t rg = i / chunks_per_row;
+        const int g = (int)(rg % w.num_kv_heads);
+        const int row = (int)(rg / w.num_kv_heads);
+        int seq, nvis;
+        if (!map_row(w.rows, row, seq, nvis) || nvis < 1) continue;  // nothing to own
+        const int pos = nvis - 1;                                      // the row's own key
+        const int lp = pos / w.page_tokens;
+        const int32_t blk = w.page_table[(int64_t)seq * w.max_pages + lp];
+        if (blk < 0 || blk >= w.num_blocks) continue;  // counted by atlas_validate_tables
+        const int64_t dst = (((int64_t)blk * w.num_kv_heads + g) * w.page_tokens +
+                             (pos - lp * w.page_tokens)) * chunks_per_row + ch;
+        const int64_t src = ((int64_t)row * w.num_kv_heads + g) * chunks_per_row + ch;
+        reinterpret_cast<uint4 *>(w.k_pool)[dst] = reinterpret_cast<const uint4 *>(w.k_new)[src];
+        reinterpret_cast<uint4 *>(w.v_pool)[dst] = reinterpret_cast<const uint4 *>(w.v_new)[src];
+    }
+}
+
+// One workgroup per (page i, kv head g, K or V).  Pass 1: max |x| of the
+// block; pass 2: codes.  Each thread owns runs of 8 consecutive elements, so
+// int4 pairs (2j, 2j + 1) never straddle threads.
+__global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
+    const int kv = blockIdx.x & 1;
+    const int g = (int)((blockIdx.x >> 1) % d.num_kv_heads);
+    const int i = (int)((blockIdx.x >> 1) / d.num_kv_heads);
+    const int32_t src_slot = d.src_slots[i];
+    const uint32_t dst = (uint32_t)d.dst_entries[i];
+    const uint32_t tier = dst >> 30, slot = dst & ((1u << 30) - 1u);
+    const bool dst_ok = (tier == 1 && slot < (uint32_t)d.n_i8) || (tier == 2 && slot < (uint32_t)d.n_i4);
+    const bool src_ok = src_slot >= 0 && src_slot < d.num_blocks;
+    if (!dst_ok || !src_ok) {
+        if (threadIdx.x == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
+        if (dst_ok && threadIdx.x == 0) {  // a bad source: the page turns its rows into NaN
+            float *sc = tier == 1 ? (kv ? d.i8_vs : d.i8_ks) : (kv ? d.i4_vs : d.i4_ks);
+            sc[(int64_t)slot * d.num_kv_heads + g] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int qmax = tier == 1 ? 127 : 7;
+    const int64_t n = (int64_t)d.page_tokens * d.head_dim;  // multiple of 8
+    const void *pool = kv ? d.v_pool : d.k_pool;
+    const int64_t base = ((int64_t)src_slot * d.num_kv_heads + g) * n;
+
+    float amax = 0.0f;
+    for (int64_t e = 8 * (int64_t)threadIdx.x; e < n; e += 8 * (int64_t)blockDim.x) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(pool) +
+                                                         base + e);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+            const float x = d.kv_type == KV_BF16 ? __uint_as_float((uint32_t)b << 16)
+                                                 : (float)__builtin_bit_cast(_Float16, b);
+            amax = fmaxf(amax, fabsf(x));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    __shared__ float s_max[4];
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    const float scale = __fdiv_rn(amax, (float)qmax);
+
+    const int64_t dst_base = ((int64_t)slot * d.num_kv_heads + g) * n;  // in elements
+    for (int64_t e = 8 * (int64_t)threadIdx.x; e < n; e += 8 * (int64_t)blockDim.x) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(pool) +
+                                                         base + e);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        int c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+            const float x = d.kv_type == KV_BF16 ? __uint_as_float((uint32_t)b << 16)
+                                                 : (float)__builtin_bit_cast(_Float16, b);
+            const float q = scale > 0.0f ? rintf(__fdiv_rn(x, scale)) : 0.0f;
+            c[j] = (int)fminf(fmaxf(q, (float)-qmax), (float)qmax);
+        }
+        if (tier == 1) {
+            int8_t *out = (kv ? d.i8_v : d.i8_k) + dst_base + e;
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo |= (uint32_t)(c[j] & 0xFF) << (8 * j);
+                hi |= (uint32_t)(c[4 + j] & 0xFF) << (8 * j);
+            }
+            *reinterpret_cast<uint2 *>(out) = make_uint2(lo, hi);
+        } else {
+            uint8_t *out = (kv ? d.i4_v : d.i4_k) + (dst_base + e) / 2;
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) word |= (uint32_t)(c[j] & 0xF) << (4 * j);
+            *reinterpret_cast<uint32_t *>(out) = word;
+        }
+    }
+    if (threadIdx.x == 0) {
+        float *sc = tier == 1 ? (kv ? d.i8_vs : d.i8_ks) : (kv ? d.i4_vs : d.i4_ks);
+        sc[(int64_t)slot * d.num_kv_heads + g] = scale;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_write_kv(const WriteKvParams &w, hipStream_t stream) {
+    const int64_t total = (int64_t)w.total_q * w.num_kv_heads * w.head_dim * w.elem_bytes / 16;
+    if (total <= 0) return hipSuccess;
+    const int64_t blocks = min((total + 255) / 256, (int64_t)65536);
+    hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_demote(const DemoteParams &d, hipStream_t stream) {
+    const int64_t blocks = (int64_t)d.n * d.num_kv_heads * 2;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(demote_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, d);
+    return hipGetLastError();
+}
+
+}  // namespace atlas

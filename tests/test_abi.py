@@ -210,3 +210,26 @@ def test_read_probe_arguments_are_checked():
     assert L.atlas_read_probe(FAKE, 24, FAKE, 4, None) == atlas.EINVAL
     assert L.atlas_read_probe(FAKE + 8, 32, FAKE, 4, None) == atlas.EINVAL
     assert L.atlas_read_probe(FAKE, 32, FAKE, 0, None) == atlas.EINVAL
+
+
+def test_write_and_demote_arguments_are_checked():
+    L = atlas.load()
+    a = _args()
+    assert L.atlas_write_kv(ctypes.byref(a), None, FAKE) == atlas.EINVAL
+    assert L.atlas_write_kv(ctypes.byref(a), FAKE + 8, FAKE) == atlas.EINVAL   # misaligned
+    assert L.atlas_write_kv(ctypes.byref(_args(num_heads=30)), FAKE, FAKE) == atlas.EINVAL
+    pools = atlas.TierPools()
+    pools.struct_size = ctypes.sizeof(atlas.TierPools)
+    f16 = _args(kv_dtype=atlas.F16)
+    assert L.atlas_demote_pages(ctypes.byref(f16), None, FAKE, FAKE, 1, None) == atlas.EINVAL
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, -1,
+                                None) == atlas.EINVAL
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), None, FAKE, 1,
+                                None) == atlas.EINVAL
+    pools.num_int4 = 2  # int4 pointers missing
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    assert L.atlas_demote_pages(ctypes.byref(_args(kv_dtype=atlas.F32, q_dtype=atlas.F32)),
+                                ctypes.byref(pools), FAKE, FAKE, 1, None) == atlas.EUNSUPPORTED
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), None, None, 0,
+                                None) == atlas.OK   # nothing to do
