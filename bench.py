@@ -198,6 +198,164 @@ def cpu_baseline(w, work, budget_s: float = 20.0):
     }
 
 
+def demote_plan(w, seed: int = 7):
+    """Every full hot page of every sequence, each sent to int8 or int4 by a
+    seeded fair coin (the cold split of the tiered workload), into fresh
+    consecutive slots.  Returns (src blocks, dst entries (tier << 30 | slot),
+    int8 count, int4 count)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    src, tiers = [], []
+    for s in range(w.num_seqs):
+        full = int(w.context_lens[s]) // w.page_tokens
+        src.extend(int(b) for b in w.page_table[s, :full])
+        tiers.extend(rng.integers(1, 3, size=full).tolist())
+    tiers = np.asarray(tiers, dtype=np.int64)
+    slot = np.zeros_like(tiers)
+    slot[tiers == 1] = np.arange(int((tiers == 1).sum()))
+    slot[tiers == 2] = np.arange(int((tiers == 2).sum()))
+    dst = ((tiers << 30) | slot).astype(np.uint32)
+    return (np.asarray(src, dtype=np.int32), dst.view(np.int32),
+            int((tiers == 1).sum()), int((tiers == 2).sum()))
+
+
+def write_path(args, torch, dev):
+    """Time the KV write path: atlas_write_kv (a chunk's new K/V rows into
+    their pages) or atlas_demote_pages (hot pages encoded into int8 / int4),
+    each against its HBM roofline, with the oracle's encoder timed on the host
+    for demotion."""
+    import numpy as np
+
+    import synth
+    from kv_cache_runtime_amd import atlas
+
+    w = synth.config(args.config, device=dev, seed=42)
+    if w.kv_dtype not in ("bf16", "f16") and args.op == "demote":
+        sys.exit("demote needs a bf16 or f16 hot pool (configs 3 and 5)")
+    prob = atlas.Problem(w)
+    D, Hkv, P = w.head_dim, w.num_kv_heads, w.page_tokens
+    eb = w.k_pool.element_size()
+    cpu = None
+    if args.op == "write_kv":
+        gen = torch.Generator(device=dev).manual_seed(5)
+        k_new = torch.randn((w.total_q, Hkv, D), generator=gen, device=dev).to(w.k_pool.dtype)
+        v_new = torch.randn((w.total_q, Hkv, D), generator=gen, device=dev).to(w.k_pool.dtype)
+        units = w.total_q * Hkv                      # (row, kv head) pairs
+        per_unit = 2 * 2 * D * eb                    # K and V: read the new row, write it
+
+        def call():
+            atlas.atlas_write_kv(prob.args, k_new, v_new)
+        sample = None
+        kernel = "write_kv_kernel"
+    else:
+        src, dst, n8, n4 = demote_plan(w)
+        tiers = {}
+        for kv in ("k", "v"):
+            tiers[f"i8_{kv}"] = torch.empty((n8, Hkv, P, D), dtype=torch.int8, device=dev)
+            tiers[f"i4_{kv}"] = torch.empty((n4, Hkv, P, D // 2), dtype=torch.uint8, device=dev)
+            tiers[f"i8_{kv}_scale"] = torch.empty((n8, Hkv), dtype=torch.float32, device=dev)
+            tiers[f"i4_{kv}_scale"] = torch.empty((n4, Hkv), dtype=torch.float32, device=dev)
+        pools = atlas.make_tiers(tiers)
+        src_t = torch.from_numpy(src).to(dev)
+        dst_t = torch.from_numpy(dst).to(dev)
+        rejected = torch.zeros(1, dtype=torch.int32, device=dev)
+        units = len(src) * Hkv                       # (page, kv head) blocks
+        # read K and V of the block, write their codes and two f32 scales
+        code_bytes = (n8 * 2 * P * D + n4 * P * D) * Hkv
+        per_unit = None
+
+        def call():
+            atlas.atlas_demote_pages(prob.args, pools, src_t, dst_t, rejected)
+        kernel = "demote_kernel"
+    alg_bytes = units * per_unit if per_unit else units * (2 * P * D * eb + 8) + code_bytes
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(K):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    # one kernel per call, launched on torch's current stream: per-call events
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    kern = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    kern_avg = sum(kern) / K
+    if args.op == "demote":
+        assert int(rejected) == 0
+
+    if args.op == "demote" and not args.no_cpu:
+        import oracle
+        host = oracle.HostView(w)
+        (ka, kind), (va, _) = host.pools()
+        order = np.random.default_rng(0).permutation(len(src))
+        t0, n_blocks, n_bytes = time.perf_counter(), 0, 0
+        for i in order:
+            e = int(np.uint32(dst[i]))
+            qmax = 127 if e >> 30 == 1 else 7
+            for arr in (ka, va):
+                for g in range(Hkv):
+                    x = oracle.widen_bits(arr[int(src[i]), g], kind).astype(np.float32)
+                    codes, _ = oracle.quantize_block(x, qmax)
+                    if qmax == 7:
+                        oracle.pack_int4(codes)
+                    n_bytes += P * D * eb + 4 + (P * D if qmax == 127 else P * D // 2)
+            n_blocks += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "seconds": round(dt, 3),
+               "sample": f"{n_blocks} of {len(src)} pages (all {Hkv} kv heads, K and V), "
+                         f"numpy f32 encoder, one host thread"}
+
+    # context: a plain device copy (read + write bytes), the practical roof of
+    # a kernel that streams reads and writes together
+    src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst_c = torch.empty_like(src_c)
+    dst_c.copy_(src_c)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst_c.copy_(src_c)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = round(2 * (1 << 30) * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
+    del src_c, dst_c
+
+    achieved = alg_bytes / (kern_avg / 1e3) / 1e9
+    line = {
+        "metric": {"write_kv": "KV write: bytes/s moved into the pages",
+                   "demote": "KV demotion: bytes/s of hot pages read + codes written"}[args.op],
+        "value": round(alg_bytes / (ms / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.kv_dtype if args.op == "write_kv" else f"{w.kv_dtype}->int8+int4",
+        "data": "synthetic",
+        "config": {"workload": f"{args.op} over {w.name}", "rows": w.total_q,
+                   "num_kv_heads": Hkv, "head_dim": D, "page_tokens": P,
+                   "units": units, "bytes": alg_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{args.op} over {w.name}"),
+                     "kernel": kernel, "kernel_avg_ms": round(kern_avg, 5),
+                     "kernel_median_ms": round(kern[K // 2], 5),
+                     "algorithmic_per_launch": alg_bytes},
+        "copy_GBps": copy_gbps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +373,10 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device-to-device copy of this many "
                          "bytes three times (calibrates the HBM byte counters)")
+    ap.add_argument("--op", choices=("attention", "write_kv", "demote"), default="attention",
+                    help="attention (default): the attention call of --config; write_kv: "
+                         "writing a chunk's new K/V into its pages; demote: encoding every "
+                         "full hot page of --config into the int8 / int4 tiers")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -230,6 +392,9 @@ def main():
 
     dev = torch.device("cuda:0")
     atlas.load()
+    if args.op != "attention":
+        write_path(args, torch, dev)
+        return
     w = synth.config(args.config, device=dev, seed=42)
     prob = atlas.Problem(w, split_tokens=args.split_tokens)
     if w.regen is not None:

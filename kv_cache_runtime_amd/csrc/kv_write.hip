@@ -42,87 +42,108 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteKvParams w) {
     }
 }
 
-// One workgroup per (page i, kv head g, K or V).  Pass 1: max |x| of the
-// block; pass 2: codes.  Each thread owns runs of 8 consecutive elements, so
-// int4 pairs (2j, 2j + 1) never straddle threads.
+// max |x| over the 8 16-bit elements of a chunk.
+__device__ inline float absmax8(const uint4 w, const bool bf16) {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+        const float x = bf16 ? __uint_as_float((uint32_t)b << 16)
+                             : (float)__builtin_bit_cast(_Float16, b);
+        m = fmaxf(m, fabsf(x));
+    }
+    return m;
+}
+
+// Codes of the 8 elements of chunk ch, stored at their place in the int8
+// (8 bytes per chunk) or int4 (one 32-bit word per chunk) block.
+__device__ inline void encode8(const uint4 w, const bool bf16, const float scale, const int qmax,
+                               const int tier, int8_t *i8, uint8_t *i4, const int64_t ch) {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    int c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+        const float x = bf16 ? __uint_as_float((uint32_t)b << 16)
+                             : (float)__builtin_bit_cast(_Float16, b);
+        const float q = scale > 0.0f ? rintf(__fdiv_rn(x, scale)) : 0.0f;
+        c[j] = (int)fminf(fmaxf(q, (float)-qmax), (float)qmax);
+    }
+    if (tier == 1) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo |= (uint32_t)(c[j] & 0xFF) << (8 * j);
+            hi |= (uint32_t)(c[4 + j] & 0xFF) << (8 * j);
+        }
+        reinterpret_cast<uint2 *>(i8)[ch] = make_uint2(lo, hi);
+    } else {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) word |= (uint32_t)(c[j] & 0xF) << (4 * j);
+        reinterpret_cast<uint32_t *>(i4)[ch] = word;
+    }
+}
+
+// One wave per (page i, kv head g, K or V) block, four blocks per
+// workgroup.  Lane l owns the 16-byte chunks l + 64 j.  A block of up to
+// 64 * R chunks (P * D <= 2048 at R = 4) is read once and kept in registers
+// between the max |x| pass and the encoding pass; a larger block is read a
+// second time for the encoding.  No barrier: the waves are independent.
+template <int R>
 __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
-    const int kv = blockIdx.x & 1;
-    const int g = (int)((blockIdx.x >> 1) % d.num_kv_heads);
-    const int i = (int)((blockIdx.x >> 1) / d.num_kv_heads);
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= (int64_t)d.n * d.num_kv_heads * 2) return;
+    const int kv = (int)(unit & 1);
+    const int g = (int)((unit >> 1) % d.num_kv_heads);
+    const int i = (int)((unit >> 1) / d.num_kv_heads);
     const int32_t src_slot = d.src_slots[i];
     const uint32_t dst = (uint32_t)d.dst_entries[i];
     const uint32_t tier = dst >> 30, slot = dst & ((1u << 30) - 1u);
     const bool dst_ok = (tier == 1 && slot < (uint32_t)d.n_i8) || (tier == 2 && slot < (uint32_t)d.n_i4);
     const bool src_ok = src_slot >= 0 && src_slot < d.num_blocks;
+    float *sc = tier == 1 ? (kv ? d.i8_vs : d.i8_ks) : (kv ? d.i4_vs : d.i4_ks);
     if (!dst_ok || !src_ok) {
-        if (threadIdx.x == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
-        if (dst_ok && threadIdx.x == 0) {  // a bad source: the page turns its rows into NaN
-            float *sc = tier == 1 ? (kv ? d.i8_vs : d.i8_ks) : (kv ? d.i4_vs : d.i4_ks);
-            sc[(int64_t)slot * d.num_kv_heads + g] = __builtin_nanf("");
-        }
+        if (lane == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
+        // a bad source: the page turns its rows into NaN
+        if (dst_ok && lane == 0) sc[(int64_t)slot * d.num_kv_heads + g] = __builtin_nanf("");
         return;
     }
+    const bool bf16 = d.kv_type == KV_BF16;
     const int qmax = tier == 1 ? 127 : 7;
     const int64_t n = (int64_t)d.page_tokens * d.head_dim;  // multiple of 8
-    const void *pool = kv ? d.v_pool : d.k_pool;
-    const int64_t base = ((int64_t)src_slot * d.num_kv_heads + g) * n;
+    const int64_t nch = n / 8;
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        reinterpret_cast<const uint16_t *>(kv ? d.v_pool : d.k_pool) +
+        ((int64_t)src_slot * d.num_kv_heads + g) * n);
 
+    uint4 keep[R];
     float amax = 0.0f;
-    for (int64_t e = 8 * (int64_t)threadIdx.x; e < n; e += 8 * (int64_t)blockDim.x) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(pool) +
-                                                         base + e);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
-            const float x = d.kv_type == KV_BF16 ? __uint_as_float((uint32_t)b << 16)
-                                                 : (float)__builtin_bit_cast(_Float16, b);
-            amax = fmaxf(amax, fabsf(x));
-        }
+    for (int j = 0; j < R; ++j) {
+        const int64_t ch = lane + 64 * j;
+        keep[j] = ch < nch ? src[ch] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
+    for (int j = 0; j < R; ++j) amax = fmaxf(amax, absmax8(keep[j], bf16));
+    for (int64_t ch = lane + 64 * R; ch < nch; ch += 64) amax = fmaxf(amax, absmax8(src[ch], bf16));
+#pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    __shared__ float s_max[4];
-    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     const float scale = __fdiv_rn(amax, (float)qmax);
 
     const int64_t dst_base = ((int64_t)slot * d.num_kv_heads + g) * n;  // in elements
-    for (int64_t e = 8 * (int64_t)threadIdx.x; e < n; e += 8 * (int64_t)blockDim.x) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(pool) +
-                                                         base + e);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        int c[8];
+    int8_t *i8 = tier == 1 ? (kv ? d.i8_v : d.i8_k) + dst_base : nullptr;
+    uint8_t *i4 = tier == 2 ? (kv ? d.i4_v : d.i4_k) + dst_base / 2 : nullptr;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
-            const float x = d.kv_type == KV_BF16 ? __uint_as_float((uint32_t)b << 16)
-                                                 : (float)__builtin_bit_cast(_Float16, b);
-            const float q = scale > 0.0f ? rintf(__fdiv_rn(x, scale)) : 0.0f;
-            c[j] = (int)fminf(fmaxf(q, (float)-qmax), (float)qmax);
-        }
-        if (tier == 1) {
-            int8_t *out = (kv ? d.i8_v : d.i8_k) + dst_base + e;
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                lo |= (uint32_t)(c[j] & 0xFF) << (8 * j);
-                hi |= (uint32_t)(c[4 + j] & 0xFF) << (8 * j);
-            }
-            *reinterpret_cast<uint2 *>(out) = make_uint2(lo, hi);
-        } else {
-            uint8_t *out = (kv ? d.i4_v : d.i4_k) + (dst_base + e) / 2;
-            uint32_t word = 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) word |= (uint32_t)(c[j] & 0xF) << (4 * j);
-            *reinterpret_cast<uint32_t *>(out) = word;
-        }
+    for (int j = 0; j < R; ++j) {
+        const int64_t ch = lane + 64 * j;
+        if (ch < nch) encode8(keep[j], bf16, scale, qmax, (int)tier, i8, i4, ch);
     }
-    if (threadIdx.x == 0) {
-        float *sc = tier == 1 ? (kv ? d.i8_vs : d.i8_ks) : (kv ? d.i4_vs : d.i4_ks);
-        sc[(int64_t)slot * d.num_kv_heads + g] = scale;
-    }
+    for (int64_t ch = lane + 64 * R; ch < nch; ch += 64)
+        encode8(src[ch], bf16, scale, qmax, (int)tier, i8, i4, ch);
+    if (lane == 0) sc[(int64_t)slot * d.num_kv_heads + g] = scale;
 }
 
 }  // namespace
@@ -136,9 +157,10 @@ hipError_t launch_write_kv(const WriteKvParams &w, hipStream_t stream) {
 }
 
 hipError_t launch_demote(const DemoteParams &d, hipStream_t stream) {
-    const int64_t blocks = (int64_t)d.n * d.num_kv_heads * 2;
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(demote_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, d);
+    const int64_t waves = (int64_t)d.n * d.num_kv_heads * 2;  // one per block
+    if (waves <= 0) return hipSuccess;
+    hipLaunchKernelGGL(demote_kernel<4>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
+                       d);
     return hipGetLastError();
 }
 

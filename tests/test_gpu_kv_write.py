@@ -160,3 +160,46 @@ def test_demote_rejects_bad_destinations_and_poisons_bad_sources(gpu):
     assert torch.isnan(w.tiers["i8_k_scale"][0]).all()          # bad source: NaN scales
     assert torch.isnan(w.tiers["i8_v_scale"][0]).all()
     assert w.tiers["i8_k_scale"].shape[1] == Hkv
+
+
+def test_demote_full_size_sampled(gpu):
+    """The benchmarked demotion (every full page of the 64-sequence bf16 GQA
+    decode workload, split int8 / int4 by a seeded coin), checked bit-exact on
+    sampled (page, kv head) blocks, including the first and the last."""
+    import bench
+    w = synth.config(3, device=gpu, seed=42)
+    Hkv, P, D = w.num_kv_heads, w.page_tokens, w.head_dim
+    src, dst, n8, n4 = bench.demote_plan(w)
+    tiers = {}
+    for kv in ("k", "v"):
+        tiers[f"i8_{kv}"] = torch.zeros((n8, Hkv, P, D), dtype=torch.int8, device=gpu)
+        tiers[f"i4_{kv}"] = torch.zeros((n4, Hkv, P, D // 2), dtype=torch.uint8, device=gpu)
+        tiers[f"i8_{kv}_scale"] = torch.full((n8, Hkv), -1.0, device=gpu)
+        tiers[f"i4_{kv}_scale"] = torch.full((n4, Hkv), -1.0, device=gpu)
+    prob = atlas.Problem(w)
+    rejected = torch.zeros(1, dtype=torch.int32, device=gpu)
+    atlas.atlas_demote_pages(prob.args, atlas.make_tiers(tiers), torch.from_numpy(src).to(gpu),
+                             torch.from_numpy(dst).to(gpu), rejected)
+    torch.cuda.synchronize()
+    assert int(rejected) == 0
+    # every destination scale was written (no -1 left)
+    for key in ("i8_k_scale", "i8_v_scale", "i4_k_scale", "i4_v_scale"):
+        assert bool((tiers[key] >= 0).all()), key
+
+    rng = np.random.default_rng(3)
+    pick = np.unique(np.concatenate([[0, len(src) - 1], rng.integers(0, len(src), 48)]))
+    host = oracle.HostView(w)
+    (ka, kind), (va, _) = host.pools()
+    for i in pick:
+        e = int(np.uint32(dst[i]))
+        tier, slot = e >> 30, e & ((1 << 30) - 1)
+        key, qmax = ("i8", 127) if tier == 1 else ("i4", 7)
+        for arr, kv in ((ka, "k"), (va, "v")):
+            got_codes = tiers[f"{key}_{kv}"][slot].cpu().numpy()
+            got_scale = tiers[f"{key}_{kv}_scale"][slot].cpu().numpy()
+            for g in range(Hkv):
+                x = oracle.widen_bits(arr[int(src[i]), g], kind).astype(np.float32)
+                codes, scale = oracle.quantize_block(x, qmax)
+                assert got_scale[g].tobytes() == scale.tobytes(), (i, kv, g)
+                want = codes.astype(np.int8) if tier == 1 else oracle.pack_int4(codes)
+                assert np.array_equal(got_codes[g].view(np.uint8), want.view(np.uint8)), (i, kv, g)
