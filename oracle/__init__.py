@@ -16,6 +16,7 @@ from .oracle import (  # noqa: F401
     pack_int4,
     quantize_block,
     reference,
+    rope,
     regen_values,
     row_info,
     splitmix64,

@@ -28,13 +28,20 @@
 #include <stdint.h>
 #include <string.h>
 
-/* Keys [0, visible[r]) are visible to row r; the rest are masked out. */
+/* Keys [0, visible[r]) are visible to row r; the rest are masked out.
+ *
+ * slope (NULL, or [n_rows]): ALiBi (Press, Smith, Lewis, "Train Short, Test
+ * Long", ICLR 2022), the positional policy the CFR-Atlas README lists beside
+ * RoPE: score j of row r gains -slope[r] * (pos_r - j), where pos_r =
+ * visible[r] - 1 is the row's own position, so a key i tokens back is
+ * penalised linearly in i. */
 void oracle_attend(int64_t n_rows, int64_t d, int64_t n_keys,
                    const double *q,      /* [n_rows][d] */
                    const double *k,      /* [n_keys][d] */
                    const double *v,      /* [n_keys][d] */
                    const int64_t *visible, /* [n_rows] */
                    double scale,
+                   const double *slope,  /* [n_rows] or NULL */
                    double *out,          /* [n_rows][d] */
                    double *lse)          /* [n_rows] */
 {
@@ -49,14 +56,17 @@ void oracle_attend(int64_t n_rows, int64_t d, int64_t n_keys,
             continue;
         }
         const double *qr = q + r * d;
-        /* m = max_j s_j with s_j = scale * q . k_j (scores are recomputed
-         * below rather than stored, so the memory stays O(d) per row) */
+        const double sl = slope ? slope[r] : 0.0;
+        const int64_t pos = visible[r] - 1;
+        /* m = max_j s_j with s_j = scale * q . k_j - slope * (pos - j)
+         * (scores are recomputed below rather than stored, so the memory
+         * stays O(d) per row) */
         double m = -INFINITY;
         for (int64_t j = 0; j < n; ++j) {
             double acc = 0.0;
             const double *kj = k + j * d;
             for (int64_t c = 0; c < d; ++c) acc += qr[c] * kj[c];
-            acc *= scale;
+            acc = acc * scale - sl * (double)(pos - j);
             if (acc > m) m = acc;
         }
         /* weights w_j = exp(s_j - m), their sum Z, and sum_j w_j v_j */
@@ -65,7 +75,7 @@ void oracle_attend(int64_t n_rows, int64_t d, int64_t n_keys,
             double acc = 0.0;
             const double *kj = k + j * d;
             for (int64_t c = 0; c < d; ++c) acc += qr[c] * kj[c];
-            double w = exp(acc * scale - m);
+            double w = exp(acc * scale - sl * (double)(pos - j) - m);
             z += w;
             const double *vj = v + j * d;
             for (int64_t c = 0; c < d; ++c) o[c] += w * vj[c];

@@ -58,7 +58,7 @@ def lib():
         build()
         L = ctypes.CDLL(_LIB_PATH)
         i64, dbl, p = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
-        L.oracle_attend.argtypes = [i64, i64, i64, p, p, p, p, dbl, p, p]
+        L.oracle_attend.argtypes = [i64, i64, i64, p, p, p, p, dbl, p, p, p]
         L.oracle_attend.restype = None
         L.oracle_attend_folded.argtypes = [i64, i64, i64, p, p, p, p, dbl, i64, p, p]
         L.oracle_attend_folded.restype = None
@@ -80,10 +80,12 @@ def _ptr(a: np.ndarray):
 # Core definitions
 # ---------------------------------------------------------------------------
 
-def attend(q, k, v, visible, scale, page_tokens=None):
+def attend(q, k, v, visible, scale, page_tokens=None, slope=None):
     """Exact causal attention of rows `q` [n][d] over one head's keys.
 
     k, v: [n_keys][d]; visible[r] = number of leading keys row r may see.
+    slope: optional [n] ALiBi slopes, one per row (score j of row r gains
+    -slope[r] * (visible[r] - 1 - j)).
     Returns (out [n][d] f64, lse [n] f64, natural log).  With `page_tokens`
     the folded (page-by-page online softmax) variant is used instead.
     """
@@ -97,13 +99,39 @@ def attend(q, k, v, visible, scale, page_tokens=None):
     out = np.zeros((n, d), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
     if page_tokens is None:
+        sl = None if slope is None else np.ascontiguousarray(slope, dtype=np.float64)
+        assert sl is None or sl.shape == (n,)
         lib().oracle_attend(n, d, n_keys, _ptr(q), _ptr(k), _ptr(v), _ptr(vis),
-                            float(scale), _ptr(out), _ptr(lse))
+                            float(scale), None if sl is None else _ptr(sl),
+                            _ptr(out), _ptr(lse))
     else:
+        assert slope is None, "the folded variant has no positional bias"
         lib().oracle_attend_folded(n, d, n_keys, _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(vis), float(scale), int(page_tokens),
                                    _ptr(out), _ptr(lse))
     return out, lse
+
+
+def rope(x, pos, theta):
+    """Rotary position embedding (Su et al., "RoFormer", 2021, section 3.4),
+    the other positional policy the CFR-Atlas README lists: dims (2i, 2i + 1)
+    of a row at position pos are rotated by the angle pos * theta^(-2i/d),
+    (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+
+    x: [..., d] (d even), pos: broadcastable to x[..., 0].  f64 throughout.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % 2 == 0
+    pos = np.asarray(pos, dtype=np.float64)[..., None]
+    freq = np.float64(theta) ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+    ang = pos * freq
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)), dtype=np.float64)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
 
 
 def merge_splits(part_out, part_lse):
@@ -253,8 +281,13 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
     Walks the page table page by page; each page comes from its storage tier
     or from the resident pool.  In a regenerated problem every K/V value is
     defined by the regenerator (its resident pages hold the same values by
-    construction), so all pages are taken from the regenerator."""
+    construction), so all pages are taken from the regenerator.
+
+    Positional policy: with a rotary embedding (w.rope_theta > 0) stored K
+    pages hold rotated keys, as a model caches them; regenerated keys are
+    produced unrotated and rotated here by their token position."""
     host = host or HostView(w)
+    theta = float(getattr(w, "rope_theta", 0.0) or 0.0)
     P, D = w.page_tokens, w.head_dim
     ctx = int(w.context_lens[s]) if n_tokens is None else int(n_tokens)
     K = np.zeros((ctx, D), dtype=np.float64)
@@ -267,6 +300,8 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
             rs = w.regen
             K[t0:t1] = regen_values(rs["seed"], rs["layer"], g, t0, rows, D, 0)
             V[t0:t1] = regen_values(rs["seed"], rs["layer"], g, t0, rows, D, 1)
+            if theta:  # the regenerator replays K before its rotation
+                K[t0:t1] = rope(K[t0:t1], np.arange(t0, t1), theta)
             continue
         entry = int(w.page_table[s, p]) & 0xFFFFFFFF
         if w.tiers is None:
@@ -311,8 +346,14 @@ def reference(w, rows=None, heads=None, host=None, page_tokens=None):
     Returns (out [len(rows)][len(heads)][d] f64, lse [len(rows)][len(heads)]).
     rows defaults to every query row, heads to every head.  GQA/MQA: query
     head h reads kv head h // (num_heads // num_kv_heads).
+
+    Positional policy: with w.rope_theta > 0 each query row is rotated by its
+    own position (its last visible key); with w.alibi_slopes (one per query
+    head) each score gains -slope_h * (position - key).
     """
     host = host or HostView(w)
+    theta = float(getattr(w, "rope_theta", 0.0) or 0.0)
+    slopes = getattr(w, "alibi_slopes", None)
     rows = np.arange(w.total_q) if rows is None else np.asarray(rows)
     heads = np.arange(w.num_heads) if heads is None else np.asarray(heads)
     G = w.num_heads // w.num_kv_heads
@@ -328,7 +369,12 @@ def reference(w, rows=None, heads=None, host=None, page_tokens=None):
             hsel = [j for j, h in enumerate(heads) if int(h) // G == g]
             qq = np.stack([qh[rows[i], heads[j]] for i in sel for j in hsel])
             vv = np.array([vis[rows[i]] for i in sel for j in hsel])
-            o, l = attend(qq, K, V, vv, w.scale, page_tokens=page_tokens)
+            if theta:
+                qq = rope(qq, vv - 1, theta)
+            sl = None
+            if slopes is not None:
+                sl = np.array([float(slopes[heads[j]]) for i in sel for j in hsel])
+            o, l = attend(qq, K, V, vv, w.scale, page_tokens=page_tokens, slope=sl)
             k = 0
             for i in sel:
                 for j in hsel:

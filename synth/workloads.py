@@ -62,6 +62,10 @@ class Paged:
     regen: Optional[dict] = None
     name: str = ""
     meta: dict = field(default_factory=dict)
+    # positional policy: ALiBi slopes (f32, one per query head) and the
+    # rotary base (0 = no rotary embedding)
+    alibi_slopes: Optional[np.ndarray] = None
+    rope_theta: float = 0.0
 
     @property
     def total_q(self) -> int:
@@ -114,7 +118,7 @@ class Paged:
             self.page_tokens, self.q_dtype, self.kv_dtype, self.context_lens,
             self.query_lens, self.scale, mv(self.q), mv(self.k_pool),
             mv(self.v_pool), self.page_table, tiers, self.regen, self.name,
-            dict(self.meta),
+            dict(self.meta), self.alibi_slopes, self.rope_theta,
         )
 
 
@@ -307,7 +311,16 @@ def build(spec: dict, device="cpu", seed: int = 42, name: str = "") -> Paged:
                 tiers[f"{key}_{kv}_scale"] = sc.contiguous()
         tiers["counts"] = counts
 
+    # Positional policy (inputs, not arithmetic): the geometric ALiBi slopes
+    # 2^(-8 (h + 1) / H) of Press et al. and a rotary base.
+    pos_spec = spec.get("positional") or {}
+    slopes = None
+    if pos_spec.get("alibi"):
+        slopes = np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
+    rope_theta = float(np.float32(pos_spec.get("rope_theta", 0.0)))
+
     return Paged(
+        alibi_slopes=slopes, rope_theta=rope_theta,
         num_seqs=S, num_heads=H, num_kv_heads=Hkv, head_dim=D, page_tokens=P,
         q_dtype=q_dtype, kv_dtype=kv_dtype, context_lens=ctx, query_lens=qlens,
         scale=scale, q=q.contiguous(), k_pool=k_pool.contiguous(),

@@ -482,3 +482,121 @@ def test_quantize_block_zero_and_int4_packing():
     packed = oracle.pack_int4(c)
     assert packed.tolist() == [[0x79, 0xF0, 0x83, 0x25]]
     assert np.array_equal(oracle.int4_codes(packed), c)
+
+
+# ---------------------------------------------------------------------------
+# 10. Positional policy: RoPE and ALiBi (CFR-Atlas README module list and
+#     test list name both; the definitions are those of their papers)
+# ---------------------------------------------------------------------------
+
+def test_rope_known_rotations():
+    # d = 4, theta = 10000: pair 0 turns by pos radians, pair 1 by pos / 100
+    e0 = np.array([1.0, 0.0, 0.0, 0.0])
+    e2 = np.array([0.0, 0.0, 1.0, 0.0])
+    np.testing.assert_allclose(oracle.rope(e0, 1, 10000.0),
+                               [0.5403023058681398, 0.8414709848078965, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(oracle.rope(e2, 1, 10000.0),
+                               [0, 0, 0.9999500004166653, 0.009999833334166664], atol=1e-15)
+    # pos = 3: pair 1 turns by 0.03 (the sign fixes the rotation direction)
+    e3 = np.array([0.0, 0.0, 0.0, 1.0])
+    np.testing.assert_allclose(oracle.rope(e3, 3, 10000.0),
+                               [0, 0, -math.sin(0.03), math.cos(0.03)], atol=1e-15)
+    # position 0 is the identity
+    x = np.random.default_rng(0).standard_normal((5, 8))
+    np.testing.assert_array_equal(oracle.rope(x, 0, 10000.0), x)
+
+
+def test_rope_equals_complex_multiplication():
+    # RoFormer's complex form: z_i = x_2i + i x_2i+1 times exp(i pos theta^(-2i/d))
+    rng = np.random.default_rng(1)
+    d, theta = 16, 500.0
+    x = rng.standard_normal((7, d))
+    pos = np.array([0, 1, 5, 77, 1000, 65535, 131071])
+    z = x[:, 0::2] + 1j * x[:, 1::2]
+    freq = np.array([theta ** (-(2.0 * i) / d) for i in range(d // 2)])
+    zr = z * np.exp(1j * pos[:, None] * freq[None, :])
+    want = np.empty_like(x)
+    want[:, 0::2], want[:, 1::2] = zr.real, zr.imag
+    np.testing.assert_allclose(oracle.rope(x, pos, theta), want, rtol=0, atol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position_and_keep_norms():
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((2, 64))
+    for m, n, shift in ((10, 3, 100), (5000, 4000, 77), (0, 9, 131000)):
+        a = oracle.rope(q, m, 10000.0) @ oracle.rope(k, n, 10000.0)
+        b = oracle.rope(q, m + shift, 10000.0) @ oracle.rope(k, n + shift, 10000.0)
+        assert abs(a - b) < 1e-9
+        np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, m, 10000.0)),
+                                   np.linalg.norm(q), rtol=1e-14)
+
+
+def test_alibi_matches_sdpa_with_additive_bias():
+    rng = np.random.default_rng(3)
+    ctx, n_q, d, scale = 23, 6, 8, 0.4
+    q, k, v = (rng.standard_normal(s) for s in ((n_q, d), (ctx, d), (ctx, d)))
+    slope = np.array([0.5, 0.25, 0.125, 2 ** -0.5, 1.0, 0.0])
+    vis = ctx - n_q + np.arange(n_q) + 1
+    out, lse = oracle.attend(q, k, v, vis, scale, slope=slope)
+    pos = vis - 1
+    bias = -slope[:, None] * (pos[:, None] - np.arange(ctx)[None, :])
+    mask = _bottom_right_mask(n_q, ctx, ctx)
+    add = torch.from_numpy(np.where(mask, bias, -np.inf))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=add[None], scale=scale)[0]
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
+    sc = torch.from_numpy(q) @ torch.from_numpy(k).T * scale + add
+    np.testing.assert_allclose(lse, torch.logsumexp(sc, -1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_alibi_zero_query_gives_geometric_weights():
+    # q = 0: weight of the key i tokens back is r^i, r = exp(-slope)
+    n, d, slope = 40, 40, 0.3
+    r = math.exp(-slope)
+    v = np.eye(n, d)  # one-hot rows expose the weights
+    out, lse = oracle.attend(np.zeros((1, d)), np.ones((n, d)), v, [n], 1.0, slope=[slope])
+    z = (1 - r ** n) / (1 - r)
+    np.testing.assert_allclose(out[0], [r ** (n - 1 - j) / z for j in range(n)], atol=1e-15)
+    assert abs(lse[0] - math.log(z)) < 1e-13
+    # slope 0 is the plain softmax
+    q = np.random.default_rng(4).standard_normal((3, d))
+    kk = np.random.default_rng(5).standard_normal((n, d))
+    a = oracle.attend(q, kk, v, [5, 20, 40], 0.2, slope=[0.0, 0.0, 0.0])
+    b = oracle.attend(q, kk, v, [5, 20, 40], 0.2)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_reference_positional_policy():
+    # decode and prefill rows: the reference rotates every query row by its
+    # own position and biases by head slope, which equals attending the
+    # rotated rows with the explicit bias; regenerated keys are rotated by
+    # their token position
+    w = synth.build(dict(num_seqs=2, context_lens=[45, 70], query_lens=[3, 1], num_heads=4,
+                         num_kv_heads=2, head_dim=8, page_tokens=16, kv_dtype="bf16",
+                         positional=dict(alibi=True, rope_theta=10000.0)), seed=17)
+    np.testing.assert_allclose(w.alibi_slopes, [2 ** -2, 2 ** -4, 2 ** -6, 2 ** -8])
+    out, lse = oracle.reference(w)
+    qh = oracle.widen(w.q)
+    seqs, vis = oracle.row_info(w)
+    for row in range(w.total_q):
+        s = int(seqs[row])
+        K, V = oracle.logical_kv(w, s, 0)
+        K1, V1 = oracle.logical_kv(w, s, 1)
+        for h in range(4):
+            Kh, Vh = (K, V) if h < 2 else (K1, V1)
+            n = int(vis[row])
+            qr = oracle.rope(qh[row, h], n - 1, 10000.0)
+            sc = Kh[:n] @ qr * w.scale - w.alibi_slopes[h] * (n - 1 - np.arange(n))
+            p = np.exp(sc - sc.max())
+            np.testing.assert_allclose(out[row, h], p @ Vh[:n] / p.sum(), atol=1e-12)
+            assert abs(lse[row, h] - (sc.max() + math.log(p.sum()))) < 1e-12
+    wr = synth.build(dict(num_seqs=1, context_lens=100, query_lens=4, num_heads=2,
+                          num_kv_heads=1, head_dim=8, page_tokens=32, kv_dtype="bf16",
+                          regen=dict(seed=5, layer=1, fraction=0.5),
+                          positional=dict(rope_theta=100.0)), seed=18)
+    K, V = oracle.logical_kv(wr, 0, 0)
+    raw = oracle.regen_values(5, 1, 0, 0, 100, 8, 0)
+    np.testing.assert_allclose(K, oracle.rope(raw, np.arange(100), 100.0), atol=1e-15)
+    np.testing.assert_array_equal(V, oracle.regen_values(5, 1, 0, 0, 100, 8, 1))
