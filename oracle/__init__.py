@@ -17,6 +17,7 @@ from .oracle import (  # noqa: F401
     quantize_block,
     reference,
     rope,
+    round_bf16,
     regen_values,
     row_info,
     splitmix64,

@@ -134,6 +134,15 @@ def rope(x, pos, theta):
     return out
 
 
+def round_bf16(x):
+    """Round f64 values to the nearest bfloat16 value (8 significant bits,
+    ties to even), directly from f64 (no intermediate f32).  Finite inputs
+    within the bf16 normal range, which is all this oracle feeds it."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)              # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 def merge_splits(part_out, part_lse):
     """Log-sum-exp merge of normalised partials.
 
@@ -285,7 +294,8 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
 
     Positional policy: with a rotary embedding (w.rope_theta > 0) stored K
     pages hold rotated keys, as a model caches them; regenerated keys are
-    produced unrotated and rotated here by their token position."""
+    produced unrotated, rotated here by their token position and rounded to
+    bf16, the value a bf16 cache holds for them."""
     host = host or HostView(w)
     theta = float(getattr(w, "rope_theta", 0.0) or 0.0)
     P, D = w.page_tokens, w.head_dim
@@ -300,8 +310,10 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
             rs = w.regen
             K[t0:t1] = regen_values(rs["seed"], rs["layer"], g, t0, rows, D, 0)
             V[t0:t1] = regen_values(rs["seed"], rs["layer"], g, t0, rows, D, 1)
-            if theta:  # the regenerator replays K before its rotation
-                K[t0:t1] = rope(K[t0:t1], np.arange(t0, t1), theta)
+            if theta:
+                # the regenerator replays K before its rotation; the cached
+                # key it must reproduce is the rotated key in bf16
+                K[t0:t1] = round_bf16(rope(K[t0:t1], np.arange(t0, t1), theta))
             continue
         entry = int(w.page_table[s, p]) & 0xFFFFFFFF
         if w.tiers is None:

@@ -598,5 +598,25 @@ def test_reference_positional_policy():
                           positional=dict(rope_theta=100.0)), seed=18)
     K, V = oracle.logical_kv(wr, 0, 0)
     raw = oracle.regen_values(5, 1, 0, 0, 100, 8, 0)
-    np.testing.assert_allclose(K, oracle.rope(raw, np.arange(100), 100.0), atol=1e-15)
+    rot = oracle.rope(raw, np.arange(100), 100.0)
+    assert np.all(np.abs(K - rot) <= np.abs(rot) * 2.0 ** -8)  # one bf16 rounding
+    bits = (K.astype(np.float32).view(np.uint32) & 0xFFFF).astype(np.int64)
+    assert not bits.any()  # bf16 values
     np.testing.assert_array_equal(V, oracle.regen_values(5, 1, 0, 0, 100, 8, 1))
+
+
+def test_round_bf16_is_nearest_even():
+    # agrees with torch's f32 -> bf16 conversion (nearest, ties to even) on
+    # f32 inputs, including exact ties
+    rng = np.random.default_rng(6)
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -100 * (1 + 2 ** -8),
+                     1.5 + 2 ** -8], dtype=np.float32)
+    x32 = np.concatenate([x32, ties])
+    want = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(x32.astype(np.float64)), want)
+    # directly from f64: a value just above a tie rounds up (f32 would round
+    # it onto the tie first and then to even, i.e. down)
+    x = 1 + 2 ** -8 + 2 ** -40
+    assert oracle.round_bf16(x) == 1 + 2 ** -7
+    assert oracle.round_bf16(1 + 2 ** -8) == 1.0
