@@ -373,6 +373,10 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device-to-device copy of this many "
                          "bytes three times (calibrates the HBM byte counters)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="attention with ALiBi slopes 2^(-8 (h + 1) / H)")
+    ap.add_argument("--rope-theta", type=float, default=0.0,
+                    help="attention with a rotary embedding of this base (0 = none)")
     ap.add_argument("--op", choices=("attention", "write_kv", "demote"), default="attention",
                     help="attention (default): the attention call of --config; write_kv: "
                          "writing a chunk's new K/V into its pages; demote: encoding every "
@@ -395,7 +399,13 @@ def main():
     if args.op != "attention":
         write_path(args, torch, dev)
         return
-    w = synth.config(args.config, device=dev, seed=42)
+    positional = {}
+    if args.alibi:
+        positional["alibi"] = True
+    if args.rope_theta:
+        positional["rope_theta"] = args.rope_theta
+    w = synth.config(args.config, device=dev, seed=42,
+                     **({"positional": positional} if positional else {}))
     prob = atlas.Problem(w, split_tokens=args.split_tokens)
     if w.regen is not None:
         prob.fill_resident_from_regenerator()
@@ -530,6 +540,8 @@ def main():
         "cold": cold,
         "cpu_baseline": cpu,
     }
+    if positional:
+        line["config"]["positional"] = positional
     if prefill:
         line["tflops"] = round(work["flops"] / t / 1e12, 3)
     print(json.dumps(line), flush=True)

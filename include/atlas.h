@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATLAS_ABI_VERSION 1u
+#define ATLAS_ABI_VERSION 2u
 
 typedef int32_t atlas_status;
 #define ATLAS_OK 0           /* success (work enqueued) */
@@ -87,6 +87,22 @@ typedef int32_t atlas_status;
  * Paging.  Logical token j of sequence s is row j % page_tokens of block
  * page_table[s * max_pages_per_seq + j / page_tokens] (CFR-Atlas README,
  * PageKey and token_range of a regenerated page).
+ *
+ * Positional policy (CFR-Atlas README, module list and test list: RoPE and
+ * ALiBi).  The position of a query row is its own key, i = (keys it sees)
+ * - 1.
+ *  - ALiBi (Press et al., 2022): with alibi_slopes != NULL the score of key j
+ *    for query head h becomes scale * q.k_j - alibi_slopes[h] * (i - j).
+ *  - RoPE (Su et al., RoFormer, 2021): with rope_theta > 0 dims (2m, 2m + 1)
+ *    of q are rotated by the angle i * rope_theta^(-2m / head_dim) before
+ *    the dot products.  K pages hold keys already rotated by their own
+ *    position, as a model caches them (atlas_write_kv rotates new keys);
+ *    regenerated keys are produced unrotated, rotated in the kernel by their
+ *    token position and rounded to bf16 (the value a bf16 cache holds, which
+ *    the regenerator must reproduce).  V is never rotated.  The angle is reduced in f64
+ *    turns and taken through the hardware sine and cosine (absolute error
+ *    about 1e-6); rotated q enters the 16-bit matrix-core paths as a
+ *    hi + lo pair, so its rounding stays near f32.
  */
 typedef struct atlas_attn_args {
     uint32_t struct_size;       /* = sizeof(atlas_attn_args); ABI guard */
@@ -122,6 +138,9 @@ typedef struct atlas_attn_args {
                                    attention kernel, so a caller can time that
                                    kernel alone (the split merge and a
                                    regeneration pre-pass fall outside the pair) */
+    const float *alibi_slopes;  /* [num_heads] f32 ALiBi slopes, finite, or NULL */
+    float rope_theta;           /* rotary base (e.g. 10000), finite and > 1, or 0 */
+    int32_t reserved;           /* 0 */
 } atlas_attn_args;
 
 /*
@@ -266,11 +285,15 @@ atlas_status atlas_gather_pages(const atlas_attn_args *args, int32_t seq,
 
 /* Write the regenerated K/V values of logical pages logical_pages[i] into
  * pool blocks dst_blocks[i] (i < n), pools of shape [*][num_kv_heads]
- * [page_tokens][head_dim] and type kv_dtype (BF16 or F32; the values are
- * bf16-exact either way).  Both index arrays are device int32. */
+ * [page_tokens][head_dim] and type kv_dtype (BF16 or F32; without a rotary
+ * embedding the values are bf16-exact either way).  Both index arrays are device int32.  With
+ * rope_theta > 0 the K rows are stored rotated by their token position (see
+ * the positional policy of atlas_attn_args), rounded to kv_dtype, so that
+ * resident pages hold what the regenerating kernels compute. */
 atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer,
                                     int32_t num_kv_heads, int32_t head_dim,
                                     int32_t page_tokens, int32_t kv_dtype,
+                                    float rope_theta,
                                     const int32_t *logical_pages,
                                     const int32_t *dst_blocks, int32_t n,
                                     int32_t num_blocks, void *k_pool,
@@ -317,8 +340,10 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args,
  * aligned like the pools) are written to row pos % page_tokens of block
  * page_table[s][pos / page_tokens] of args->k_pool / v_pool, so that the
  * attention call on the same arguments sees them.  The pools are written
- * through args' pointers.  Rows whose block id or context length is invalid
- * are skipped (atlas_validate_tables counts them).  Same argument checks as
+ * through args' pointers.  With args->rope_theta > 0 the K row is stored
+ * rotated by its position (rounded to kv_dtype); V is stored as given.  Rows
+ * whose block id or context length is invalid are skipped
+ * (atlas_validate_tables counts them).  Same argument checks as
  * atlas_paged_attention; asynchronous on args->stream.
  */
 atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,9 @@ class AttnArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", _p),
         ("profile_events", _p * 2),
+        ("alibi_slopes", _p),
+        ("rope_theta", ctypes.c_float),
+        ("reserved", _i32),
     ]
 
 
@@ -133,7 +137,7 @@ def load(path: str = LIB_PATH):
     L.atlas_gather_pages.argtypes = [ctypes.POINTER(AttnArgs), _i32, _i32, _p, _p]
     L.atlas_regenerate_pages.restype = _i32
     L.atlas_regenerate_pages.argtypes = [ctypes.c_uint64, ctypes.c_uint32, _i32, _i32, _i32, _i32,
-                                         _p, _p, _i32, _i32, _p, _p, _p]
+                                         ctypes.c_float, _p, _p, _i32, _i32, _p, _p, _p]
     L.atlas_dequant_pages.restype = _i32
     L.atlas_dequant_pages.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools), _p,
                                       _i32, _p, _p]
@@ -147,7 +151,7 @@ def load(path: str = LIB_PATH):
                                      _i32, _p]
     L.atlas_read_probe.restype = _i32
     L.atlas_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, _p]
-    if L.atlas_abi_version() != 1:
+    if L.atlas_abi_version() != 2:
         raise RuntimeError("libatlas ABI version mismatch")
     _lib = L
     return L
@@ -178,7 +182,8 @@ def _stream(stream):
 def make_args(*, q, k_pool, v_pool, page_table, context_lens, num_heads, num_kv_heads,
               head_dim, page_tokens, max_context_len, scale, out, lse, query_start=None,
               max_query_len=1, total_q=None, num_blocks=None, kv_dtype=None, q_dtype=None,
-              workspace=None, workspace_bytes=0, split_tokens=0, stream=None) -> AttnArgs:
+              workspace=None, workspace_bytes=0, split_tokens=0, stream=None,
+              alibi_slopes=None, rope_theta=0.0) -> AttnArgs:
     """Fill an atlas_attn_args from tensors (device pointers) and host ints."""
     a = AttnArgs()
     a.struct_size = ctypes.sizeof(AttnArgs)
@@ -207,6 +212,8 @@ def make_args(*, q, k_pool, v_pool, page_table, context_lens, num_heads, num_kv_
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace_bytes)
     a.stream = _stream(stream)
+    a.alibi_slopes = _ptr(alibi_slopes)
+    a.rope_theta = float(rope_theta)
     return a
 
 
@@ -285,11 +292,12 @@ def atlas_gather_pages(args: AttnArgs, seq: int, num_tokens: int, k_out, v_out):
 
 
 def atlas_regenerate_pages(seed, layer, num_kv_heads, head_dim, page_tokens, kv_dtype,
-                           logical_pages, dst_blocks, num_blocks, k_pool, v_pool, stream=None):
+                           logical_pages, dst_blocks, num_blocks, k_pool, v_pool, stream=None,
+                           rope_theta: float = 0.0):
     n = int(logical_pages.numel())
     _check(load().atlas_regenerate_pages(int(seed) & (2**64 - 1), int(layer), int(num_kv_heads),
                                          int(head_dim), int(page_tokens), int(kv_dtype),
-                                         _ptr(logical_pages), _ptr(dst_blocks), n,
+                                         float(rope_theta), _ptr(logical_pages), _ptr(dst_blocks), n,
                                          int(num_blocks), _ptr(k_pool), _ptr(v_pool),
                                          _stream(stream)), "atlas_regenerate_pages")
 
@@ -354,6 +362,10 @@ class Problem:
         self.out = torch.empty((w.total_q, w.num_heads, w.head_dim), device=dev,
                                dtype=torch.float32)
         self.lse = torch.empty((w.total_q, w.num_heads), device=dev, dtype=torch.float32)
+        self.alibi = None
+        if getattr(w, "alibi_slopes", None) is not None:
+            self.alibi = torch.from_numpy(np.ascontiguousarray(w.alibi_slopes,
+                                                               dtype=np.float32)).to(dev)
         self.kind = "plain"
         self.tiers = None
         self.regen = None
@@ -372,7 +384,8 @@ class Problem:
             scale=w.scale, out=self.out, lse=self.lse, query_start=self.qstart,
             max_query_len=w.max_query_len, total_q=w.total_q,
             kv_dtype=_NAME_CODE[w.kv_dtype], q_dtype=_NAME_CODE[w.q_dtype],
-            split_tokens=split_tokens, stream=stream)
+            split_tokens=split_tokens, stream=stream, alibi_slopes=self.alibi,
+            rope_theta=getattr(w, "rope_theta", 0.0))
         ws = atlas_workspace_size(self.args, self.regen)
         self.workspace = torch.empty(max(ws, 1), device=dev, dtype=torch.uint8)
         self.args.workspace = _ptr(self.workspace)
@@ -395,7 +408,7 @@ class Problem:
         bl = torch.tensor(blocks, dtype=torch.int32, device=dev)
         atlas_regenerate_pages(w.regen["seed"], w.regen["layer"], w.num_kv_heads, w.head_dim,
                                w.page_tokens, _NAME_CODE[w.kv_dtype], lp, bl, w.num_blocks,
-                               w.k_pool, w.v_pool)
+                               w.k_pool, w.v_pool, rope_theta=getattr(w, "rope_theta", 0.0))
 
     def validate(self, check_values: bool = False):
         return atlas_validate_tables(self.args, self.tiers, self.regen, check_values)

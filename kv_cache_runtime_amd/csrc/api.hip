@@ -133,6 +133,9 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
                         a->max_query_len);
     }
     if (!std::isfinite(a->scale)) return fail(ATLAS_EINVAL, "scale is not finite");
+    if (!std::isfinite(a->rope_theta) || (a->rope_theta != 0.0f && !(a->rope_theta > 1.0f)))
+        return fail(ATLAS_EINVAL, "rope_theta must be 0 or a finite value > 1");
+    if (a->reserved != 0) return fail(ATLAS_EINVAL, "reserved field must be 0");
     if (a->split_tokens < 0 || (a->split_tokens > 0 && a->split_tokens % 64))
         return fail(ATLAS_EINVAL, "split_tokens %d must be 0 or a positive multiple of 64",
                     a->split_tokens);
@@ -213,6 +216,15 @@ atlas_status check_workspace(const atlas_attn_args *a, const Plan &plan) {
     return ok();
 }
 
+PosParams pos_params(float rope_theta, const float *alibi) {
+    PosParams q;
+    std::memset(&q, 0, sizeof(q));
+    q.alibi = alibi;
+    q.rope = rope_theta > 0.0f ? 1 : 0;
+    q.rope_log2_theta = q.rope ? std::log2((double)rope_theta) : 0.0;
+    return q;
+}
+
 RowMap row_map(const atlas_attn_args *a) {
     RowMap m;
     m.context_lens = a->context_lens;
@@ -237,6 +249,7 @@ DecodeParams decode_params(const atlas_attn_args *a, const Plan &plan) {
     DecodeParams p;
     std::memset(&p, 0, sizeof(p));
     p.rows = row_map(a);
+    p.pos = pos_params(a->rope_theta, a->alibi_slopes);
     p.q = a->q;
     p.q_dtype = a->q_dtype;
     p.k_pool = a->k_pool;
@@ -310,6 +323,7 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
     PrefillParams p;
     std::memset(&p, 0, sizeof(p));
     p.rows = row_map(a);
+    p.pos = pos_params(a->rope_theta, a->alibi_slopes);
     p.q = a->q;
     p.k_pool = a->k_pool;
     p.v_pool = a->v_pool;
@@ -336,6 +350,7 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
         if (rg->max_regen_pages > 0) {
             RegenFillParams r;
             std::memset(&r, 0, sizeof(r));
+            r.pos = p.pos;
             r.seed = rg->seed;
             r.layer = rg->layer;
             r.num_kv_heads = a->num_kv_heads;
@@ -521,7 +536,7 @@ atlas_status atlas_gather_pages(const atlas_attn_args *args, int32_t seq, int32_
 
 atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t page_tokens, int32_t kv_dtype,
-                                    const int32_t *logical_pages, const int32_t *dst_blocks,
+                                    float rope_theta, const int32_t *logical_pages, const int32_t *dst_blocks,
                                     int32_t n, int32_t num_blocks, void *k_pool, void *v_pool,
                                     void *stream) {
     if (layer >= (1u << 16)) return fail(ATLAS_EINVAL, "layer %u >= 2^16", layer);
@@ -535,8 +550,11 @@ atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer, int32_t num_k
     if (n < 0 || num_blocks < 0) return fail(ATLAS_EINVAL, "negative n or num_blocks");
     if (n > 0 && (!logical_pages || !dst_blocks || !k_pool || !v_pool))
         return fail(ATLAS_EINVAL, "NULL pointer argument");
+    if (!std::isfinite(rope_theta) || (rope_theta != 0.0f && !(rope_theta > 1.0f)))
+        return fail(ATLAS_EINVAL, "rope_theta must be 0 or a finite value > 1");
     RegenFillParams r;
     std::memset(&r, 0, sizeof(r));
+    r.pos = pos_params(rope_theta, nullptr);
     r.seed = seed;
     r.layer = layer;
     r.num_kv_heads = num_kv_heads;
@@ -653,6 +671,7 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new, cons
     WriteKvParams w;
     std::memset(&w, 0, sizeof(w));
     w.rows = row_map(args);
+    w.pos = pos_params(args->rope_theta, nullptr);
     w.k_new = k_new;
     w.v_new = v_new;
     w.k_pool = const_cast<void *>(args->k_pool);
@@ -665,6 +684,7 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new, cons
     w.num_blocks = args->num_blocks;
     w.total_q = args->total_q;
     w.elem_bytes = args->kv_dtype == ATLAS_F32 ? 4 : 2;
+    w.kv_type = args->kv_dtype;
     return device_status(launch_write_kv(w, reinterpret_cast<hipStream_t>(args->stream)),
                          "write launch");
 }

@@ -52,7 +52,8 @@ struct SlotData {
 template <int KV, int D, int U, int MODE>
 __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry, int g, int tok0,
                                           int lp, int n_regen, int c, float (&kf)[U][D / 16],
-                                          float (&vf)[U][D / 16], SlotData &sd) {
+                                          float (&vf)[U][D / 16], SlotData &sd,
+                                          const double (&rt)[D / 32]) {
     constexpr int E = D / 16;
     const int P = p.page_tokens;
     const int off = tok0 % P;
@@ -69,6 +70,18 @@ __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry,
                     kf[u][e] = regen_value(p.seed, regen_counter(p.layer, g, tok0 + u, dim, 0));
                     vf[u][e] = regen_value(p.seed, regen_counter(p.layer, g, tok0 + u, dim, 1));
                 }
+            }
+            if (p.pos.rope) {
+                // regenerated keys are replayed unrotated; the cached key
+                // they stand for is the rotated key in bf16
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int m = 0; m < E / 2; ++m) {
+                        rope_rotate(kf[u][2 * m], kf[u][2 * m + 1], tok0 + u, rt[m]);
+                        kf[u][2 * m] = bf16_round(kf[u][2 * m]);
+                        kf[u][2 * m + 1] = bf16_round(kf[u][2 * m + 1]);
+                    }
             }
             return true;
         }
@@ -254,12 +267,29 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[kWaves][G];
 
+    // positional policy: the row sits at its own key, qpos
+    const int qpos = nvis - 1;
+    double rt[E / 2];  // rotary turns per position of this lane's dim pairs
+#pragma unroll
+    for (int m = 0; m < E / 2; ++m)
+        rt[m] = p.pos.rope ? rope_turns(c * E / 2 + m, D, p.pos.rope_log2_theta) : 0.0;
+    const bool alibi = p.pos.alibi != nullptr;
+    float ab[G];  // ALiBi slope of each head, log2 units
+#pragma unroll
+    for (int h = 0; h < G; ++h) ab[h] = alibi ? p.pos.alibi[g * G + h] * kLog2e : 0.0f;
+
     float qv[G][E];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const int64_t qo = ((int64_t)row * p.num_heads + g * G + h) * D + c * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) qv[h][e] = load_elem(p.q, qo + e, p.q_dtype) * p.scale_log2;
+        for (int e = 0; e < E; ++e) qv[h][e] = load_elem(p.q, qo + e, p.q_dtype);
+        if (p.pos.rope) {
+#pragma unroll
+            for (int m = 0; m < E / 2; ++m) rope_rotate(qv[h][2 * m], qv[h][2 * m + 1], qpos, rt[m]);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) qv[h][e] *= p.scale_log2;
     }
 
     float m[G], l[G], acc[G][E];
@@ -347,6 +377,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
                         part = fmaf(qv[h][e], widen_word<KV>(R.k[u], e), part);
                     const float dot = row16_sum(part);
                     s[h][u] = valid ? dot : kNegInf;
+                    if (alibi) s[h][u] = fmaf(ab[h], (float)(R.tok0 + u - qpos), s[h][u]);
                 }
             }
 #pragma unroll
@@ -394,7 +425,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
                 uint32_t entry = 0;
                 if (!(MODE == MODE_REGEN && lp < n_regen))
                     entry = (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]);
-                if (!load_slot<KV, D, U, MODE>(p, entry, g, tok0, lp, n_regen, c, kf, vf, sd)) {
+                if (!load_slot<KV, D, U, MODE>(p, entry, g, tok0, lp, n_regen, c, kf, vf, sd, rt)) {
                     bad = true;
                     live = false;
                 }
@@ -418,6 +449,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
                     for (int e = 0; e < E; ++e) part = fmaf(qv[h][e], kf[u][e], part);
                     const float dot = row16_sum(part) * sd.kscale;
                     s[h][u] = valid ? dot : kNegInf;
+                    if (alibi) s[h][u] = fmaf(ab[h], (float)(tok0 + u - qpos), s[h][u]);
                 }
     #pragma unroll
                 for (int e = 0; e < E; ++e) vf[u][e] = valid ? vf[u][e] : 0.0f;

@@ -301,6 +301,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     // within kStagedPages pages)
     __shared__ int32_t s_pages[kStagedPages];
     __shared__ int16_t s_lp[MODE == MODE_TIERED ? kStagedPages : 1];
+    // ALiBi slopes (log2 units) of score rows 0..15, zero past G; read per
+    // tile from LDS (published by the staging barrier below)
+    __shared__ __attribute__((aligned(16))) float s_ab[16];
+    if (tid < 16)
+        s_ab[tid] = (p.pos.alibi != nullptr && tid < G) ? p.pos.alibi[g * G + tid] * kLog2e : 0.0f;
     const int32_t *trow = p.page_table + (int64_t)seq * p.max_pages;
     const int P = p.page_tokens;
     const int lp_first = t0 / P;
@@ -316,22 +321,44 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         __syncthreads();
     }
 
-    // A operand of the scores: query head c (zero for c >= G)
+    // positional policy: the row sits at its own key, qpos
+    const int qpos = nvis - 1;
+    const bool rope = p.pos.rope != 0;
+    const bool alibi = p.pos.alibi != nullptr;
+
+    // A operand of the scores: query head c (zero for c >= G).  A rotated q
+    // is no longer exact in 16 bits: rows G .. 2G - 1 (padding otherwise)
+    // then carry the rounding remainder of heads 0 .. G - 1, and each head's
+    // two score rows are added after the product.
+    const bool lo_row = rope && c >= G && c < 2 * G;
     uint4 qf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         uint32_t w[4] = {0u, 0u, 0u, 0u};
-        if (c < G) {
+        if (c < G || lo_row) {
             // operand ks, lane row r holds dims 32 ks + 8 r (16-bit pages) or
             // 32 r + 8 ks (tiered pages, so each lane's K bytes are one run);
             // a dot product does not depend on how its terms are dealt out
             const int d0 = MODE == MODE_TIERED ? 32 * r + 8 * ks : 32 * ks + 8 * r;
-            const int64_t q0 = ((int64_t)row * p.num_heads + g * G + c) * kD + d0;
+            const int hq = c < G ? c : c - G;
+            const int64_t q0 = ((int64_t)row * p.num_heads + g * G + hq) * kD + d0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x0 = load_elem(p.q, q0 + 2 * i, p.q_dtype);
-                const float x1 = load_elem(p.q, q0 + 2 * i + 1, p.q_dtype);
-                if constexpr (QT == KV_BF16) {  // q is bf16: exact
+                float x0 = load_elem(p.q, q0 + 2 * i, p.q_dtype);
+                float x1 = load_elem(p.q, q0 + 2 * i + 1, p.q_dtype);
+                if (rope) {
+                    rope_rotate(x0, x1, qpos, rope_turns(d0 / 2 + i, kD, p.pos.rope_log2_theta));
+                    if constexpr (QT == KV_BF16) {
+                        const float h0 = bf16_round(x0), h1 = bf16_round(x1);
+                        x0 = lo_row ? bf16_round(x0 - h0) : h0;
+                        x1 = lo_row ? bf16_round(x1 - h1) : h1;
+                    } else {
+                        const float h0 = (float)(_Float16)x0, h1 = (float)(_Float16)x1;
+                        x0 = lo_row ? x0 - h0 : x0;
+                        x1 = lo_row ? x1 - h1 : x1;
+                    }
+                }
+                if constexpr (QT == KV_BF16) {  // bf16-exact here
                     w[i] = (__float_as_uint(x0) >> 16) | (__float_as_uint(x1) & 0xFFFF0000u);
                 } else {
                     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -463,6 +490,27 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) sc[tg] = mfma16<QT>(qf[ks], kb[ks], sc[tg]);
             }
+            if (rope) {  // add the remainder rows G .. 2G - 1 to heads 0 .. G - 1
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) {
+                    if constexpr (G == 2) {
+                        sc[tg][0] += sc[tg][2];
+                        sc[tg][1] += sc[tg][3];
+                    } else if constexpr (G == 4) {  // rows 4..7 sit 16 lanes up
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sc[tg][i] += __int_as_float(
+                                __builtin_amdgcn_ds_swizzle(__float_as_int(sc[tg][i]), 0x401F));
+                    } else {  // rows 8..15 sit 32 lanes up
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t u = __float_as_uint(sc[tg][i]);
+                            const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                            sc[tg][i] += __uint_as_float(sw[1]);  // lane l < 32: lane l + 32
+                        }
+                    }
+                }
+            }
             float kf[4];  // hot pages carry no scale
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg)
@@ -474,6 +522,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             for (int tg = 0; tg < 4; ++tg) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[tg][i] = kvalid[tg] ? sc[tg][i] * kf[tg] : kNegInf;
+                if (alibi) {
+                    const float4 ab = *reinterpret_cast<const float4 *>(&s_ab[4 * r]);
+                    const float dist = (float)(cur.tok[tg] + c - qpos);
+                    sc[tg][0] = fmaf(ab.x, dist, sc[tg][0]);
+                    sc[tg][1] = fmaf(ab.y, dist, sc[tg][1]);
+                    sc[tg][2] = fmaf(ab.z, dist, sc[tg][2]);
+                    sc[tg][3] = fmaf(ab.w, dist, sc[tg][3]);
+                }
             }
 
             // ---- online softmax, one reference max per head (uniform in a row)

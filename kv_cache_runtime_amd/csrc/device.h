@@ -43,6 +43,38 @@ __device__ __forceinline__ float load_elem(const void *base, int64_t idx, int dt
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// ---------------------------------------------------------------------------
+// Rotary position embedding (RoFormer, Su et al. 2021; the CFR-Atlas README
+// lists RoPE as a positional policy).  The pair of dims (2m, 2m + 1) at
+// position i turns by the angle i * theta^(-2m / D).
+// ---------------------------------------------------------------------------
+
+// Turns (angle / 2 pi) per position of pair m, in f64.
+__device__ __forceinline__ double rope_turns(int m, int D, double log2_theta) {
+    return exp2(-(double)(2 * m) / (double)D * log2_theta) * 0.15915494309189535;
+}
+
+// Rotates (x0, x1) by pos * turns full turns.  The angle is reduced to
+// [-1/2, 1/2] turn in f64, then the hardware sine and cosine (which take
+// turns) give about 1e-6 absolute accuracy for any position below 2^31.
+__device__ __forceinline__ void rope_rotate(float &x0, float &x1, int pos, double turns) {
+    double t = (double)pos * turns;
+    t -= rint(t);
+    const float tf = (float)t;
+    const float sn = __builtin_amdgcn_sinf(tf);
+    const float cs = __builtin_amdgcn_cosf(tf);
+    const float y0 = x0 * cs - x1 * sn;
+    const float y1 = x0 * sn + x1 * cs;
+    x0 = y0;
+    x1 = y1;
+}
+
+// f32 rounded to the nearest bf16 value (ties to even), returned as f32.
+__device__ __forceinline__ float bf16_round(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
+}
+
 // Sign-extended bit field: the `bits`-wide field that ends at bit 31 after a
 // left shift by `sh` (shift done unsigned, then an arithmetic right shift).
 __device__ __forceinline__ int32_t sext_field(uint32_t w, int sh, int bits) {

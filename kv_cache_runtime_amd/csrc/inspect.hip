@@ -68,10 +68,15 @@ __global__ __launch_bounds__(256) void regen_fill_kernel(const RegenFillParams r
         const int e = 2 * t;
         const int row = e / D, dim = e % D;
         const int tok = lp * P + row;
-        const uint32_t k0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 0));
-        const uint32_t k1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 0));
+        uint32_t k0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 0));
+        uint32_t k1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 0));
+        float2 kk = make_float2(__uint_as_float(k0 << 16), __uint_as_float(k1 << 16));
+        if (r.pos.rope) {  // stored as a model caches it: rotated by its position
+            rope_rotate(kk.x, kk.y, tok, rope_turns(dim / 2, D, r.pos.rope_log2_theta));
+            k0 = __float_as_uint(bf16_round(kk.x)) >> 16;
+            k1 = __float_as_uint(bf16_round(kk.y)) >> 16;
+        }
         if (r.kv_f32) {
-            float2 kk = make_float2(__uint_as_float(k0 << 16), __uint_as_float(k1 << 16));
             reinterpret_cast<float2 *>(reinterpret_cast<float *>(r.k_dst) + base)[t] = kk;
         } else {
             reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.k_dst) + base)[t] =

@@ -21,8 +21,16 @@ struct RowMap {
     int32_t max_keys;             // max_pages_per_seq * page_tokens
 };
 
+// Positional policy of a call: ALiBi slopes and the rotary embedding.
+struct PosParams {
+    const float *alibi;       // [num_heads] slopes, or nullptr
+    double rope_log2_theta;   // log2 of the rotary base
+    int32_t rope;             // 1: rotate q (and regenerated / new K)
+};
+
 struct DecodeParams {
     RowMap rows;
+    PosParams pos;
     const void *q;            // [total_q][H][D]
     int32_t q_dtype;
     const void *k_pool;       // [num_blocks][Hkv][P][D] (hot pool in tiered mode)
@@ -68,6 +76,7 @@ struct FoldParams {
 
 struct PrefillParams {
     RowMap rows;
+    PosParams pos;
     const void *q;            // [total_q][H][D] bf16 / f16
     const void *k_pool;
     const void *v_pool;
@@ -86,6 +95,7 @@ struct PrefillParams {
 };
 
 struct RegenFillParams {
+    PosParams pos;                 // rope: K written rotated by its token position
     uint64_t seed;
     uint32_t layer;
     int32_t num_kv_heads, head_dim, page_tokens;
@@ -128,11 +138,13 @@ struct ValidateParams {
 // New tokens' K/V rows written into their pages (one row per query row).
 struct WriteKvParams {
     RowMap rows;
+    PosParams pos;              // rope: K rows stored rotated by their position
     const void *k_new, *v_new;  // [total_q][Hkv][D]
     void *k_pool, *v_pool;      // [num_blocks][Hkv][P][D]
     const int32_t *page_table;
     int32_t num_kv_heads, head_dim, page_tokens, max_pages, num_blocks, total_q;
     int32_t elem_bytes;
+    int32_t kv_type;
 };
 
 // Hot pages encoded into int8 / int4 cold-tier slots.

@@ -5,7 +5,8 @@
 // chunk) owns the key at its own position, ctx - n_q + t; its K/V rows go to
 // row pos % P of block page_table[s][pos / P] of every kv head (CFR-Atlas
 // README, PageKey and token ranges; the pages are written in place, never
-// concatenated).
+// concatenated).  Under a rotary embedding the K row is stored rotated by
+// its position, as the attention kernels expect cached keys.
 //
 // Demotion (argus-cache, "Visual Architecture": FP16 -> INT8 -> INT4 tiers):
 // one block per (page, kv head, K|V) gets a symmetric f32 scale max|x| / qmax
@@ -17,6 +18,40 @@
 namespace atlas {
 
 namespace {
+
+// A 16-byte chunk of a K row starting at dim d0 (even), rotated by the row's
+// position (rotary embedding; pairs (2m, 2m + 1) lie inside the chunk) and
+// rounded back to its storage type (nearest, ties to even).
+__device__ uint4 rotate_chunk(const uint4 k, const int kv_type, const int pos, const int d0,
+                              const int D, const double log2_theta) {
+    uint32_t w[4] = {k.x, k.y, k.z, k.w};
+    if (kv_type == KV_F32) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            float x0 = __uint_as_float(w[2 * m]), x1 = __uint_as_float(w[2 * m + 1]);
+            rope_rotate(x0, x1, pos, rope_turns(d0 / 2 + m, D, log2_theta));
+            w[2 * m] = __float_as_uint(x0);
+            w[2 * m + 1] = __float_as_uint(x1);
+        }
+    } else {
+        const bool bf = kv_type == KV_BF16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float x0 = bf ? bf16_lo(w[m]) : f16_lo(w[m]);
+            float x1 = bf ? bf16_hi(w[m]) : f16_hi(w[m]);
+            rope_rotate(x0, x1, pos, rope_turns(d0 / 2 + m, D, log2_theta));
+            if (bf) {
+                w[m] = (__float_as_uint(bf16_round(x0)) >> 16) |
+                       (__float_as_uint(bf16_round(x1)) & 0xFFFF0000u);
+            } else {
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                const h2 h = {(_Float16)x0, (_Float16)x1};
+                w[m] = __builtin_bit_cast(uint32_t, h);
+            }
+        }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 // One thread per 16-byte chunk of a (row, kv head) K or V row.
 __global__ __launch_bounds__(256) void write_kv_kernel(const WriteKvParams w) {
@@ -37,7 +72,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteKvParams w) {
         const int64_t dst = (((int64_t)blk * w.num_kv_heads + g) * w.page_tokens +
                              (pos - lp * w.page_tokens)) * chunks_per_row + ch;
         const int64_t src = ((int64_t)row * w.num_kv_heads + g) * chunks_per_row + ch;
-        reinterpret_cast<uint4 *>(w.k_pool)[dst] = reinterpret_cast<const uint4 *>(w.k_new)[src];
+        uint4 k = reinterpret_cast<const uint4 *>(w.k_new)[src];
+        if (w.pos.rope) k = rotate_chunk(k, w.kv_type, pos, (int)ch * (16 / w.elem_bytes),
+                                         w.head_dim, w.pos.rope_log2_theta);
+        reinterpret_cast<uint4 *>(w.k_pool)[dst] = k;
         reinterpret_cast<uint4 *>(w.v_pool)[dst] = reinterpret_cast<const uint4 *>(w.v_new)[src];
     }
 }

@@ -87,7 +87,10 @@ __device__ __forceinline__ uint32_t page_of(const PrefillParams &p, int key) {
     return (__umulhi((uint32_t)key, p.p_magic) + (uint32_t)key) >> p.p_shift;
 }
 
-template <int KV, int G, int NH>
+// ALIBI: scores gain -slope_h * (pos - key).  ROPE: q is rotated by its
+// position; the rotated row is kept as a 16-bit hi part plus the rounded
+// remainder, and S^T takes one more MFMA per step for the remainder.
+template <int KV, int G, int NH, bool ALIBI, bool ROPE>
 __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParams p) {
     constexpr int kPosHalf = 32 / G;         // positions per 32-row half
     constexpr int kPosWave = NH * kPosHalf;  // a wave owns NH halves of 32 rows
@@ -150,15 +153,46 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
 
     // Q^T operands: k-step ks holds dims 16 ks + 8 half .. + 8 of the row
     uint4 qf[NH][8];
+    uint4 qlo[NH][ROPE ? 8 : 1];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
         const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
                                ((int64_t)(q0 + t[hh]) * p.num_heads + head) * kD + 8 * half;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+        for (int ks = 0; ks < 8; ++ks) {
             qf[hh][ks] = row_ok[hh] ? *reinterpret_cast<const uint4 *>(qrow + 16 * ks)
                                     : make_uint4(0, 0, 0, 0);
+            if constexpr (ROPE) {
+                uint32_t hi[4] = {qf[hh][ks].x, qf[hh][ks].y, qf[hh][ks].z, qf[hh][ks].w};
+                uint32_t lo[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x0 = KV == KV_BF16 ? bf16_lo(hi[i]) : f16_lo(hi[i]);
+                    float x1 = KV == KV_BF16 ? bf16_hi(hi[i]) : f16_hi(hi[i]);
+                    rope_rotate(x0, x1, pos[hh],
+                                rope_turns(8 * ks + 4 * half + i, kD, p.pos.rope_log2_theta));
+                    if constexpr (KV == KV_BF16) {
+                        const float h0 = bf16_round(x0), h1 = bf16_round(x1);
+                        hi[i] = (__float_as_uint(h0) >> 16) | (__float_as_uint(h1) & 0xFFFF0000u);
+                        lo[i] = (__float_as_uint(bf16_round(x0 - h0)) >> 16) |
+                                (__float_as_uint(bf16_round(x1 - h1)) & 0xFFFF0000u);
+                    } else {
+                        const f16x2_t h = {(_Float16)x0, (_Float16)x1};
+                        const f16x2_t l = {(_Float16)(x0 - (float)h[0]), (_Float16)(x1 - (float)h[1])};
+                        hi[i] = __builtin_bit_cast(uint32_t, h);
+                        lo[i] = __builtin_bit_cast(uint32_t, l);
+                    }
+                }
+                qf[hh][ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                qlo[hh][ks] = row_ok[hh] ? make_uint4(lo[0], lo[1], lo[2], lo[3])
+                                         : make_uint4(0, 0, 0, 0);
+            }
+        }
     }
+    // ALiBi slope of this lane's head in raw score units (the scores are
+    // scaled by scale * log2(e) later)
+    float ab = 0.0f;
+    if constexpr (ALIBI) ab = p.pos.alibi[head] / (p.scale_log2 * (1.0f / kLog2e));
 
     f32x16_t o[NH][4];
 #pragma unroll
@@ -290,8 +324,22 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
                 const uint4 a =
                     *reinterpret_cast<const uint4 *>(&cK[(32 * kb + r) * kKStride + 16 * ks + 8 * half]);
 #pragma unroll
-                for (int hh = 0; hh < NH; ++hh) s[hh][kb] = mfma32<KV>(a, qf[hh][ks], s[hh][kb]);
+                for (int hh = 0; hh < NH; ++hh) {
+                    s[hh][kb] = mfma32<KV>(a, qf[hh][ks], s[hh][kb]);
+                    if constexpr (ROPE) s[hh][kb] = mfma32<KV>(a, qlo[hh][ks], s[hh][kb]);
+                }
             }
+        }
+        if constexpr (ALIBI) {
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * half + (j & 3);
+                        s[hh][kb][j] = fmaf(ab, (float)(key - pos[hh]), s[hh][kb][j]);
+                    }
         }
 
         // causal mask only on tiles that reach past some row's position
@@ -409,18 +457,27 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
     }
 }
 
-template <int KV, int NH>
+template <int KV, int NH, bool A, bool R>
 hipError_t by_group(const PrefillParams &p, int group, hipStream_t s) {
     const int64_t blocks = (int64_t)p.num_kv_heads * p.q_blocks * p.rows.num_seqs;
     if (blocks <= 0) return hipSuccess;
     switch (group) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<KV, 1, NH>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<KV, 2, NH>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<KV, 4, NH>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<KV, 8, NH>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<KV, 1, NH, A, R>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<KV, 2, NH, A, R>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<KV, 4, NH, A, R>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<KV, 8, NH, A, R>), dim3((unsigned)blocks), dim3(256), 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int KV>
+hipError_t by_policy(const PrefillParams &p, int group, hipStream_t s) {
+    const bool a = p.pos.alibi != nullptr, r = p.pos.rope != 0;
+    if (a && r) return by_group<KV, kPrefillHalves, true, true>(p, group, s);
+    if (a) return by_group<KV, kPrefillHalves, true, false>(p, group, s);
+    if (r) return by_group<KV, kPrefillHalves, false, true>(p, group, s);
+    return by_group<KV, kPrefillHalves, false, false>(p, group, s);
 }
 
 }  // namespace
@@ -428,8 +485,8 @@ hipError_t by_group(const PrefillParams &p, int group, hipStream_t s) {
 int prefill_rows_per_wave() { return 32 * kPrefillHalves; }
 
 hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream) {
-    if (kv_type == KV_BF16) return by_group<KV_BF16, kPrefillHalves>(p, group, stream);
-    if (kv_type == KV_F16) return by_group<KV_F16, kPrefillHalves>(p, group, stream);
+    if (kv_type == KV_BF16) return by_policy<KV_BF16>(p, group, stream);
+    if (kv_type == KV_F16) return by_policy<KV_F16>(p, group, stream);
     return hipErrorInvalidValue;
 }
 

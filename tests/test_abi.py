@@ -52,7 +52,7 @@ def test_struct_layouts_match_c(tmp_path):
 
 
 def test_abi_version_and_status_strings():
-    assert atlas.atlas_abi_version() == 1
+    assert atlas.atlas_abi_version() == 2
     assert atlas.atlas_status_string(0) == "ok"
     assert atlas.atlas_status_string(3).startswith("workspace")
     assert atlas.atlas_status_string(99) == "unknown status"
@@ -180,12 +180,15 @@ def test_fold_and_inspection_arguments_are_checked():
     a = _args()
     assert L.atlas_gather_pages(ctypes.byref(a), 4, 10, FAKE, FAKE) == atlas.EINVAL
     assert L.atlas_gather_pages(ctypes.byref(a), 0, 64 * 16 + 1, FAKE, FAKE) == atlas.EINVAL
-    assert L.atlas_regenerate_pages(1, 1 << 16, 8, 128, 16, atlas.BF16, FAKE, FAKE, 1, 1,
+    assert L.atlas_regenerate_pages(1, 1 << 16, 8, 128, 16, atlas.BF16, 0.0, FAKE, FAKE, 1, 1,
                                     FAKE, FAKE, None) == atlas.EINVAL
-    assert L.atlas_regenerate_pages(1, 0, 8, 128, 16, atlas.F16, FAKE, FAKE, 1, 1,
+    assert L.atlas_regenerate_pages(1, 0, 8, 128, 16, atlas.F16, 0.0, FAKE, FAKE, 1, 1,
                                     FAKE, FAKE, None) == atlas.EUNSUPPORTED
-    assert L.atlas_regenerate_pages(1, 0, 8, 127, 16, atlas.BF16, FAKE, FAKE, 1, 1,
+    assert L.atlas_regenerate_pages(1, 0, 8, 127, 16, atlas.BF16, 0.0, FAKE, FAKE, 1, 1,
                                     FAKE, FAKE, None) == atlas.EINVAL
+    for theta in (0.5, 1.0, -2.0, float("nan"), float("inf")):
+        assert L.atlas_regenerate_pages(1, 0, 8, 128, 16, atlas.BF16, theta, FAKE, FAKE, 1, 1,
+                                        FAKE, FAKE, None) == atlas.EINVAL
 
 
 def test_validate_tables_arguments_are_checked():
@@ -233,3 +236,20 @@ def test_write_and_demote_arguments_are_checked():
                                 ctypes.byref(pools), FAKE, FAKE, 1, None) == atlas.EUNSUPPORTED
     assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), None, None, 0,
                                 None) == atlas.OK   # nothing to do
+
+
+def test_positional_policy_arguments_are_checked():
+    L = atlas.load()
+    for theta in (0.5, 1.0, -1.0, float("nan"), float("inf")):
+        a = _args()
+        a.rope_theta = theta
+        assert L.atlas_paged_attention(ctypes.byref(a)) == atlas.EINVAL, theta
+        assert "rope_theta" in atlas.atlas_last_error()
+    a = _args()
+    a.reserved = 1
+    assert L.atlas_paged_attention(ctypes.byref(a)) == atlas.EINVAL
+    # a valid policy passes the argument checks
+    a = _args()
+    a.rope_theta = 10000.0
+    a.alibi_slopes = FAKE
+    assert _ws(a)[0] == atlas.OK
