@@ -522,8 +522,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             for (int tg = 0; tg < 4; ++tg) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[tg][i] = kvalid[tg] ? sc[tg][i] * kf[tg] : kNegInf;
-                if (alibi) {
-                    const float4 ab = *reinterpret_cast<const float4 *>(&s_ab[4 * r]);
+            }
+            if (alibi) {  // wave-uniform
+                const float4 ab = *reinterpret_cast<const float4 *>(&s_ab[4 * r]);
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) {
                     const float dist = (float)(cur.tok[tg] + c - qpos);
                     sc[tg][0] = fmaf(ab.x, dist, sc[tg][0]);
                     sc[tg][1] = fmaf(ab.y, dist, sc[tg][1]);

@@ -330,16 +330,24 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
                 }
             }
         }
+        // ALiBi, split as ab * (key - pos) = ab * o_j + rb: o_j = key - (k0 +
+        // 4 half) is a compile-time offset of the register slot, and the
+        // row's tile offset rb = ab * (k0 + 4 half - pos) is added to its max
+        // and to the exponent below, once per row instead of per score
+        float rb[NH];
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) rb[hh] = 0.0f;
         if constexpr (ALIBI) {
 #pragma unroll
-            for (int hh = 0; hh < NH; ++hh)
+            for (int hh = 0; hh < NH; ++hh) {
+                rb[hh] = ab * (float)(k0 + 4 * half - pos[hh]);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * half + (j & 3);
-                        s[hh][kb][j] = fmaf(ab, (float)(key - pos[hh]), s[hh][kb][j]);
-                    }
+                    for (int j = 0; j < 16; ++j)
+                        s[hh][kb][j] = fmaf(ab, (float)(32 * kb + 8 * (j >> 2) + (j & 3)),
+                                            s[hh][kb][j]);
+            }
         }
 
         // causal mask only on tiles that reach past some row's position
@@ -364,6 +372,7 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, s[hh][kb][j]);
+            if constexpr (ALIBI) mraw += rb[hh];
             mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
             mt[hh] = mraw * p.scale_log2;  // scale > 0 keeps the order
             move[hh] = mt[hh] > m_ref[hh] + kSlack;  // also true on the first finite tile
@@ -388,7 +397,8 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
         uint4 pb[NH][4];
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
-            const float m_off = (m_ref[hh] == kNegInf) ? 0.0f : m_ref[hh] - kPScale;
+            float m_off = (m_ref[hh] == kNegInf) ? 0.0f : m_ref[hh] - kPScale;
+            if constexpr (ALIBI) m_off = fmaf(-rb[hh], p.scale_log2, m_off);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int kb = st >> 1, j0 = 8 * (st & 1);
