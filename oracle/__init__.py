@@ -10,11 +10,14 @@ from .oracle import (  # noqa: F401
     attend,
     build,
     dequant_f32,
+    fp8_e4m3_encode,
+    fp8_e4m3_value,
     int4_codes,
     logical_kv,
     merge_splits,
     pack_int4,
     quantize_block,
+    quantize_block_fp8,
     reference,
     rope,
     round_bf16,

@@ -15,9 +15,10 @@ Definitions followed:
     keys 0 .. c - n_q + t (the chunk's own earlier tokens included);
   * paging: logical token j of sequence s lives in block table[s][j // P], row
     j % P (CFR-Atlas README, PageKey + token_range per page);
-  * cold tiers: ARGUS "Visual Architecture" (INT8; INT4 2-way bit-packed),
-    symmetric: value = code * scale, one scale per (page, kv head) for K and
-    one for V; int4 element 2i in the low nibble, two's complement;
+  * cold tiers: ARGUS "Visual Architecture" (FP8; INT8; INT4 2-way
+    bit-packed), symmetric: value = code * scale (FP8: E4M3 value of the code
+    times scale), one scale per (page, kv head) for K and one for V; int4
+    element 2i in the low nibble, two's complement;
   * regenerated pages: the value definition in attention.c;
   * split merge: log-sum-exp combination of normalised partial results
     (attnres AGENTS.md, "online softmax merge").
@@ -248,6 +249,50 @@ def quantize_block(x: np.ndarray, qmax: int):
     return np.clip(q, -qmax, qmax).astype(np.int16), scale
 
 
+def fp8_e4m3_value(code):
+    """Value of an OCP FP8 E4M3 code (the "e4m3fn" variant), the FP8 tier of
+    argus-cache's "Visual Architecture" cascade as read here: sign in bit 7,
+    exponent in bits 6-3 with bias 7, mantissa in bits 2-0; exponent 0 is
+    subnormal (m/8 * 2^-6); 0x7F and 0xFF are NaN; there are no infinities.
+    Largest finite magnitude 448."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 0xF
+    m = (code & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((code & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def fp8_e4m3_encode(y):
+    """E4M3 code nearest to each value of y (f32), by brute force over the 127
+    finite magnitudes: ties go to the even code, magnitudes above 448
+    saturate to 448, and the sign bit is y's sign bit."""
+    y = np.asarray(y, dtype=np.float32)
+    codes = np.arange(0x7F)
+    mags = fp8_e4m3_value(codes)
+    a = np.abs(y.astype(np.float64))[..., None]
+    d = np.abs(a - mags)
+    cand = d == d.min(axis=-1, keepdims=True)
+    first = np.where(cand, codes, 0x7F).min(axis=-1)
+    even = np.where(cand & (codes % 2 == 0), codes, 0x7F).min(axis=-1)
+    mag_code = np.where(cand.sum(axis=-1) > 1, even, first)
+    return (mag_code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_block_fp8(x: np.ndarray):
+    """FP8 (E4M3) encoding of one (page, kv head) block (reading: one f32
+    scale per block, like the integer tiers): scale = f32(max |x|) / 448 and
+    code = nearest E4M3 code to f32(x) / scale, both divisions correctly
+    rounded f32.  An all-zero block gets scale 0 and codes 0.  Returns
+    (uint8 codes of x's shape, np.float32 scale)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    scale = np.float32(amax / np.float32(448.0))
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.uint8), np.float32(0.0)
+    return fp8_e4m3_encode(np.divide(x, scale, dtype=np.float32)), scale
+
+
 def pack_int4(codes: np.ndarray) -> np.ndarray:
     """Two's-complement nibbles, element 2i in the low nibble of byte i (the
     argus-cache INT4 "2-way bit-packed" layout as read here)."""
@@ -328,13 +373,14 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
             V[t0:t1] = widen_bits(va[slot, g, :rows], kind)
             continue
         ta = host.tier_arrays()
-        key = "i8" if tier == 1 else "i4"
+        key = {1: "i8", 2: "i4", 3: "f8"}[tier]
         for dst, kv in ((K, "k"), (V, "v")):
             codes = ta[f"{key}_{kv}"][slot, g, :rows]
             if key == "i4":
                 codes = int4_codes(codes)
             sc = np.float64(ta[f"{key}_{kv}_scale"][slot, g])
-            dst[t0:t1] = codes.astype(np.float64) * sc
+            vals = fp8_e4m3_value(codes) if key == "f8" else codes.astype(np.float64)
+            dst[t0:t1] = vals * sc
     return K, V
 
 

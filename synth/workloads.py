@@ -35,7 +35,7 @@ import numpy as np
 import torch
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
-TIER_HOT, TIER_I8, TIER_I4 = 0, 1, 2
+TIER_HOT, TIER_I8, TIER_I4, TIER_F8 = 0, 1, 2, 3
 TIER_SHIFT = 30
 SLOT_MASK = (1 << TIER_SHIFT) - 1
 
@@ -187,6 +187,17 @@ def _quantize(src: torch.Tensor, qmax: int):
     return codes.to(torch.int8), scale
 
 
+def _quantize_fp8(src: torch.Tensor):
+    """FP8 (E4M3) storage encoding of cold pages: scale = max|x| / 448 (f32) per
+    (page, kv head), codes from torch's float8_e4m3fn conversion of x / scale."""
+    amax = src.abs().amax(dim=(2, 3))
+    scale = (amax / 448.0).to(torch.float32)
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    y = (src / safe[:, :, None, None]).clamp_(-448.0, 448.0)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
 def _pack_int4(codes: torch.Tensor) -> torch.Tensor:
     """Two's-complement nibbles, element 2i in the low nibble of byte i."""
     c = codes.to(torch.int16) & 0xF
@@ -265,25 +276,31 @@ def build(spec: dict, device="cpu", seed: int = 42, name: str = "") -> Paged:
     else:
         # Tiered storage: pages holding any of the newest `hot_tokens` tokens
         # are f16/bf16 (kv_dtype); older pages are int8 or int4 by a seeded
-        # fair coin per (sequence, page), shared by K and V and all kv heads.
+        # fair coin per (sequence, page), shared by K and V and all kv heads
+        # (with p_fp8 > 0, that share of the cold pages is FP8 E4M3).
         hot_tokens = int(tiers_spec.get("hot_tokens", 1024))
         p_i8 = float(tiers_spec.get("p_int8", 0.5))
+        p_f8 = float(tiers_spec.get("p_fp8", 0.0))
         tier_of = []
         for s in range(S):
             first_hot = max(0, int(ctx[s]) - hot_tokens) // P
             t = np.full(int(n_pages[s]), TIER_HOT, dtype=np.int32)
             cold = np.arange(int(n_pages[s])) < first_hot
-            coin = rng.random(int(n_pages[s])) < p_i8
+            u = rng.random(int(n_pages[s]))
+            coin = u < p_i8
+            f8 = ~coin & (u < p_i8 + p_f8)
             t[cold & coin] = TIER_I8
-            t[cold & ~coin] = TIER_I4
+            t[cold & f8] = TIER_F8
+            t[cold & ~coin & ~f8] = TIER_I4
             tier_of.append(t)
-        counts = [sum(int((t == k).sum()) for t in tier_of) for k in range(3)]
+        counts = [sum(int((t == k).sum()) for t in tier_of) for k in range(4)]
         slots = [list(_place(None, counts[k], placement, rng)) for k in range(3)]
+        slots.append(list(_place(None, counts[TIER_F8], placement, rng)) if counts[TIER_F8] else [])
         poison_hot = counts[TIER_HOT]
         # entries are 32-bit words (tier in the top two bits), kept in an
         # int32 array with the same bits
         table = np.full((S, max_pages), poison_hot, dtype=np.uint32)
-        used = [0, 0, 0]
+        used = [0, 0, 0, 0]
         for s in range(S):
             for p, t in enumerate(tier_of[s]):
                 slot = int(slots[t][used[t]])
@@ -309,6 +326,12 @@ def build(spec: dict, device="cpu", seed: int = 42, name: str = "") -> Paged:
                     codes = _pack_int4(codes)
                 tiers[f"{key}_{kv}"] = codes.contiguous()
                 tiers[f"{key}_{kv}_scale"] = sc.contiguous()
+        if counts[TIER_F8]:
+            for kv in ("k", "v"):
+                src = _normal((counts[TIER_F8], Hkv, P, D), gen, device)
+                codes, sc = _quantize_fp8(src)
+                tiers[f"f8_{kv}"] = codes.contiguous()
+                tiers[f"f8_{kv}_scale"] = sc.contiguous()
         tiers["counts"] = counts
 
     # Positional policy (inputs, not arithmetic): the geometric ALiBi slopes

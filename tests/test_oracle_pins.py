@@ -620,3 +620,69 @@ def test_round_bf16_is_nearest_even():
     x = 1 + 2 ** -8 + 2 ** -40
     assert oracle.round_bf16(x) == 1 + 2 ** -7
     assert oracle.round_bf16(1 + 2 ** -8) == 1.0
+
+
+# ---------------------------------------------------------------------------
+# 11. FP8 (E4M3) cold tier
+# ---------------------------------------------------------------------------
+
+def test_fp8_values_match_torch_e4m3fn_and_named_codes():
+    v = oracle.fp8_e4m3_value(np.arange(256))
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t))
+    np.testing.assert_array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    named = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x3C: 1.5, 0x7E: 448.0, 0xC0: -2.0, 0xFE: -448.0}
+    for c, val in named.items():
+        assert v[c] == val, hex(c)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+
+
+def test_fp8_encode_is_nearest_even_and_matches_torch():
+    rng = np.random.default_rng(8)
+    y = (rng.uniform(-448, 448, 20000) * np.exp2(rng.integers(-14, 1, 20000))).astype(np.float32)
+    ties = oracle.fp8_e4m3_value(np.arange(0x7E))  # midpoints between neighbours
+    mids = ((ties[:-1] + ties[1:]) / 2).astype(np.float32)
+    y = np.concatenate([y, mids, -mids, [0.0, -0.0, 448.0, -448.0, 3e-5, -3e-5]]).astype(np.float32)
+    got = oracle.fp8_e4m3_encode(y)
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, want)
+    # every finite code's value encodes to itself; above 448 saturates
+    c = np.array([k for k in range(256) if (k & 0x7F) != 0x7F])
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(oracle.fp8_e4m3_value(c)), c)
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(np.float32([460.0, 1e9, -500.0])),
+                                  [0x7E, 0x7E, 0xFE])
+
+
+def test_fp8_block_scale_extremes_and_round_trip():
+    x = np.random.default_rng(9).standard_normal((16, 64)).astype(np.float32)
+    codes, scale = oracle.quantize_block_fp8(x)
+    assert scale == np.float32(np.float32(np.abs(x).max()) / np.float32(448.0))
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert codes[i] in (0x7E, 0xFE)
+    back = oracle.fp8_e4m3_value(codes) * np.float64(scale)
+    normal = np.abs(x) >= 2.0 ** -6 * scale
+    assert np.all(np.abs(back - x)[normal] <= np.abs(x)[normal] * 2.0 ** -4)
+    assert np.all(np.abs(back - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale))
+    c2, s2 = oracle.quantize_block_fp8(-x)
+    np.testing.assert_array_equal(c2, codes ^ 0x80)
+    z, sz = oracle.quantize_block_fp8(np.zeros((4, 8), np.float32))
+    assert sz == 0 and not z.any()
+
+
+def test_tiered_reference_reads_fp8_pages():
+    w = synth.build(dict(num_seqs=2, context_lens=[70, 130], num_heads=4, num_kv_heads=2,
+                         head_dim=8, page_tokens=16, kv_dtype="f16",
+                         tiers=dict(hot_tokens=16, p_int8=0.3, p_fp8=0.4)), seed=19)
+    assert w.tiers["counts"][3] > 0
+    ta = oracle.HostView(w).tier_arrays()
+    for s in range(2):
+        for p in range(w.pages_of(s)):
+            e = int(w.page_table[s, p]) & 0xFFFFFFFF
+            if e >> 30 != 3:
+                continue
+            slot = e & ((1 << 30) - 1)
+            K, V = oracle.logical_kv(w, s, 1)
+            n = min(16, int(w.context_lens[s]) - 16 * p)
+            want = oracle.fp8_e4m3_value(ta["f8_k"][slot, 1, :n]) * np.float64(ta["f8_k_scale"][slot, 1])
+            np.testing.assert_array_equal(K[16 * p:16 * p + n], want)
