@@ -41,7 +41,7 @@ def algorithmic_work(w):
     ctx = w.context_lens.astype(np.int64)
     kv_bytes = 0
     if w.tiers is not None:
-        per_tok = {0: 2 * D * elem, 1: 2 * D, 2: D}  # K+V bytes per (token, kv head)
+        per_tok = {0: 2 * D * elem, 1: 2 * D, 2: D, 3: 2 * D}  # K+V bytes per (token, kv head)
         for s in range(w.num_seqs):
             for p in range(w.pages_of(s)):
                 tier = (int(w.page_table[s, p]) & 0xFFFFFFFF) >> 30
@@ -377,6 +377,9 @@ def main():
                     help="attention with ALiBi slopes 2^(-8 (h + 1) / H)")
     ap.add_argument("--rope-theta", type=float, default=0.0,
                     help="attention with a rotary embedding of this base (0 = none)")
+    ap.add_argument("--p-fp8", type=float, default=0.0,
+                    help="tiered workload (config 4): share of the cold pages stored as FP8 "
+                         "E4M3, the rest split evenly between int8 and int4")
     ap.add_argument("--op", choices=("attention", "write_kv", "demote"), default="attention",
                     help="attention (default): the attention call of --config; write_kv: "
                          "writing a chunk's new K/V into its pages; demote: encoding every "
@@ -404,8 +407,12 @@ def main():
         positional["alibi"] = True
     if args.rope_theta:
         positional["rope_theta"] = args.rope_theta
-    w = synth.config(args.config, device=dev, seed=42,
-                     **({"positional": positional} if positional else {}))
+    extra = {"positional": positional} if positional else {}
+    if args.p_fp8 > 0:
+        if args.config != 4:
+            sys.exit("--p-fp8 applies to the tiered workload (--config 4)")
+        extra["tiers"] = dict(hot_tokens=1024, p_int8=(1.0 - args.p_fp8) / 2, p_fp8=args.p_fp8)
+    w = synth.config(args.config, device=dev, seed=42, **extra)
     prob = atlas.Problem(w, split_tokens=args.split_tokens)
     if w.regen is not None:
         prob.fill_resident_from_regenerator()
@@ -542,6 +549,9 @@ def main():
     }
     if positional:
         line["config"]["positional"] = positional
+    if args.p_fp8 > 0:
+        line["config"]["cold_fp8_share"] = args.p_fp8
+        line["dtype"] = "f16+fp8+int8+int4"
     if prefill:
         line["tflops"] = round(work["flops"] / t / 1e12, 3)
     print(json.dumps(line), flush=True)

@@ -67,6 +67,7 @@ typedef int32_t atlas_status;
 #define ATLAS_TIER_HOT 0  /* f16 / bf16 page in the hot pool (args k_pool/v_pool) */
 #define ATLAS_TIER_INT8 1 /* int8 codes, one f32 scale per (page, kv head) */
 #define ATLAS_TIER_INT4 2 /* int4 codes, two per byte, same scale layout */
+#define ATLAS_TIER_FP8 3  /* FP8 E4M3 codes (OCP "e4m3fn"), same scale layout */
 
 /*
  * One attention call (decode or chunked prefill).  CFR-Atlas README,
@@ -145,12 +146,14 @@ typedef struct atlas_attn_args {
 
 /*
  * Cold-tier pools of atlas_paged_attention_tiered (ARGUS, "Visual
- * Architecture": FP16 hot pool, INT8, INT4 "2-way Bit-Packed"; pages are
+ * Architecture": FP16 hot pool, FP8, INT8, INT4 "2-way Bit-Packed"; pages are
  * reconstructed in registers just before the dot products, ARGUS "Why It
  * Works: Storage vs. Computation").  Value = code * scale, symmetric, one f32
  * scale per (page, kv head), separately for K and V.  int4 byte i of a row
  * holds element 2i in its low nibble and element 2i+1 in its high nibble,
- * two's complement.  A pool with zero slots may pass NULL pointers.
+ * two's complement.  FP8 codes are OCP E4M3 ("e4m3fn": bias 7, largest
+ * finite 448, 0x7F / 0xFF NaN) and value = e4m3(code) * scale.  A pool with
+ * zero slots may pass NULL pointers.
  */
 typedef struct atlas_tier_pools {
     uint32_t struct_size;       /* = sizeof(atlas_tier_pools) */
@@ -165,6 +168,12 @@ typedef struct atlas_tier_pools {
     const uint8_t *int4_v;
     const float *int4_k_scale;  /* [num_int4][num_kv_heads] */
     const float *int4_v_scale;
+    int32_t num_fp8;            /* slots in the FP8 pool */
+    int32_t reserved2;          /* 0 */
+    const uint8_t *fp8_k;       /* [num_fp8][num_kv_heads][page_tokens][head_dim] */
+    const uint8_t *fp8_v;
+    const float *fp8_k_scale;   /* [num_fp8][num_kv_heads] */
+    const float *fp8_v_scale;
 } atlas_tier_pools;
 
 /*
@@ -235,12 +244,13 @@ atlas_status atlas_paged_attention(const atlas_attn_args *args);
 /*
  * Decode over tiered pages: page_table entries are (tier << 30) | slot.  Hot
  * pages come from args->k_pool / v_pool (kv_dtype F16 or BF16, num_blocks
- * slots); int8 and int4 pages from `pools`.  Decode only (query_start must be
- * NULL).  Codes are decoded in registers and the per-page scales are applied
+ * slots); int8, int4 and FP8 pages from `pools`.  Decode only (query_start must
+ * be NULL).  Codes are decoded in registers and the per-page scales are applied
  * to the dot products and to the probabilities, never written back.  With
  * F16 hot pages, head_dim 128 and 2, 4 or 8 query heads per kv head both
  * products run on matrix cores in f16 (when a split spans at most 510
- * pages): the codes convert exactly, q is rounded to f16 (exact for bf16 q
+ * pages): the codes convert exactly (FP8 through the gfx950 hardware
+ * conversion), q is rounded to f16 (exact for bf16 q
  * with 2^-14 <= |q| <= 65504; smaller magnitudes carry an absolute error of
  * at most 2^-25, larger ones are out of range).
  */
@@ -316,11 +326,12 @@ atlas_status atlas_dequant_pages(const atlas_attn_args *args,
  * sequence.  report_dev: caller-owned device buffer of 4 uint32 counters,
  * overwritten:
  *   [0] page-table entries of visible, non-regenerated pages that name no
- *       page (slot beyond its pool, tier 3);
+ *       page (slot beyond its pool);
  *   [1] sequences whose context length, query range or regenerated-page
  *       count is out of bounds;
- *   [2] non-finite K or V elements among visible tokens of resident pages
- *       (check_values != 0 only; reads every such element);
+ *   [2] non-finite K or V elements among visible tokens of resident pages,
+ *       and FP8 NaN codes of visible FP8 pages (check_values != 0 only;
+ *       reads every such element);
  *   [3] non-finite K or V scales of visible cold pages (check_values only).
  * Asynchronous on args->stream; if report_host != NULL the counters are also
  * copied there and the call waits for the stream.  Allocates nothing.
@@ -351,12 +362,14 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,
 
 /*
  * atlas_demote_pages: encodes hot pages into the cold tiers (argus-cache,
- * "Visual Architecture": FP16 -> INT8 -> INT4).  For i < n, hot block
+ * "Visual Architecture": FP16 -> FP8 -> INT8 -> INT4).  For i < n, hot block
  * src_slots[i] of args->k_pool / v_pool (kv_dtype F16 or BF16, every row
- * finite) is encoded into dst_entries[i] = (tier << 30) | slot, tier 1 (int8)
- * or 2 (int4) of `pools`: for each kv head, K and V separately,
- *     scale = max|x| / qmax            (f32, correctly rounded; qmax 127 / 7)
+ * finite) is encoded into dst_entries[i] = (tier << 30) | slot, tier 1 (int8),
+ * 2 (int4) or 3 (FP8) of `pools`: for each kv head, K and V separately,
+ *     scale = max|x| / qmax            (f32, correctly rounded; qmax 127 / 7 / 448)
  *     code  = clamp(rint(x / scale), -qmax, qmax)   (round half to even)
+ *     FP8:  code = the E4M3 code nearest to x / scale (ties to the even
+ *           code; x / scale is correctly rounded f32)
  * and an all-zero block gets scale 0 and codes 0.  Codes and scales are
  * written through the pools' pointers; the caller then points its page-table
  * entries at dst_entries.  A destination outside its pool rejects the page

@@ -76,6 +76,12 @@ class TierPools(ctypes.Structure):
         ("int4_v", _p),
         ("int4_k_scale", _p),
         ("int4_v_scale", _p),
+        ("num_fp8", _i32),
+        ("reserved2", _i32),
+        ("fp8_k", _p),
+        ("fp8_v", _p),
+        ("fp8_k_scale", _p),
+        ("fp8_v_scale", _p),
     ]
 
 
@@ -236,6 +242,10 @@ def make_tiers(t: dict) -> TierPools:
     p.int8_k_scale, p.int8_v_scale = _ptr(t["i8_k_scale"]), _ptr(t["i8_v_scale"])
     p.int4_k, p.int4_v = _ptr(t["i4_k"]), _ptr(t["i4_v"])
     p.int4_k_scale, p.int4_v_scale = _ptr(t["i4_k_scale"]), _ptr(t["i4_v_scale"])
+    if "f8_k" in t:
+        p.num_fp8 = int(t["f8_k"].shape[0])
+        p.fp8_k, p.fp8_v = _ptr(t["f8_k"]), _ptr(t["f8_v"])
+        p.fp8_k_scale, p.fp8_v_scale = _ptr(t["f8_k_scale"]), _ptr(t["f8_v_scale"])
     return p
 
 

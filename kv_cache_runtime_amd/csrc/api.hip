@@ -225,6 +225,44 @@ PosParams pos_params(float rope_theta, const float *alibi) {
     return q;
 }
 
+// Sizes and pointers of the cold-tier pools (a pool with slots needs all four
+// of its pointers).
+atlas_status check_pools(const atlas_tier_pools *t) {
+    if (!t) return fail(ATLAS_EINVAL, "pools is NULL");
+    if (t->struct_size != sizeof(atlas_tier_pools))
+        return fail(ATLAS_EINVAL, "pools->struct_size %u != %zu", t->struct_size,
+                    sizeof(atlas_tier_pools));
+    if (t->num_int8 < 0 || t->num_int4 < 0 || t->num_fp8 < 0)
+        return fail(ATLAS_EINVAL, "negative tier pool size");
+    if (t->reserved != 0 || t->reserved2 != 0) return fail(ATLAS_EINVAL, "reserved field must be 0");
+    if (t->num_int8 > 0 && (!t->int8_k || !t->int8_v || !t->int8_k_scale || !t->int8_v_scale))
+        return fail(ATLAS_EINVAL, "NULL int8 pool pointer");
+    if (t->num_int4 > 0 && (!t->int4_k || !t->int4_v || !t->int4_k_scale || !t->int4_v_scale))
+        return fail(ATLAS_EINVAL, "NULL int4 pool pointer");
+    if (t->num_fp8 > 0 && (!t->fp8_k || !t->fp8_v || !t->fp8_k_scale || !t->fp8_v_scale))
+        return fail(ATLAS_EINVAL, "NULL fp8 pool pointer");
+    return ok();
+}
+
+template <typename P>
+void set_pools(P &p, const atlas_tier_pools *t) {
+    p.i8_k = t->int8_k;
+    p.i8_v = t->int8_v;
+    p.i8_ks = t->int8_k_scale;
+    p.i8_vs = t->int8_v_scale;
+    p.i4_k = t->int4_k;
+    p.i4_v = t->int4_v;
+    p.i4_ks = t->int4_k_scale;
+    p.i4_vs = t->int4_v_scale;
+    p.f8_k = t->fp8_k;
+    p.f8_v = t->fp8_v;
+    p.f8_ks = t->fp8_k_scale;
+    p.f8_vs = t->fp8_v_scale;
+    p.n_i8 = t->num_int8;
+    p.n_i4 = t->num_int4;
+    p.n_f8 = t->num_fp8;
+}
+
 RowMap row_map(const atlas_attn_args *a) {
     RowMap m;
     m.context_lens = a->context_lens;
@@ -440,34 +478,14 @@ atlas_status atlas_paged_attention_tiered(const atlas_attn_args *args,
     Plan plan;
     atlas_status st = check_common(args, true, nullptr, &plan);
     if (st != ATLAS_OK) return st;
-    if (!pools) return fail(ATLAS_EINVAL, "pools is NULL");
-    if (pools->struct_size != sizeof(atlas_tier_pools))
-        return fail(ATLAS_EINVAL, "pools->struct_size %u != %zu", pools->struct_size,
-                    sizeof(atlas_tier_pools));
+    if ((st = check_pools(pools)) != ATLAS_OK) return st;
     if (args->query_start != nullptr)
         return fail(ATLAS_EUNSUPPORTED, "tiered pages support decode only (query_start NULL)");
     if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
         return fail(ATLAS_EUNSUPPORTED, "tiered hot pages must be F16 or BF16");
-    if (pools->num_int8 < 0 || pools->num_int4 < 0)
-        return fail(ATLAS_EINVAL, "negative tier pool size");
-    if (pools->num_int8 > 0 && (!pools->int8_k || !pools->int8_v || !pools->int8_k_scale ||
-                                !pools->int8_v_scale))
-        return fail(ATLAS_EINVAL, "NULL int8 pool pointer");
-    if (pools->num_int4 > 0 && (!pools->int4_k || !pools->int4_v || !pools->int4_k_scale ||
-                                !pools->int4_v_scale))
-        return fail(ATLAS_EINVAL, "NULL int4 pool pointer");
     if ((st = check_workspace(args, plan)) != ATLAS_OK) return st;
     DecodeParams p = decode_params(args, plan);
-    p.i8_k = pools->int8_k;
-    p.i8_v = pools->int8_v;
-    p.i8_ks = pools->int8_k_scale;
-    p.i8_vs = pools->int8_v_scale;
-    p.i4_k = pools->int4_k;
-    p.i4_v = pools->int4_v;
-    p.i4_ks = pools->int4_k_scale;
-    p.i4_vs = pools->int4_v_scale;
-    p.n_i8 = pools->num_int8;
-    p.n_i4 = pools->num_int4;
+    set_pools(p, pools);
     return run_decode(args, plan, p, MODE_TIERED);
 }
 
@@ -576,23 +594,13 @@ atlas_status atlas_dequant_pages(const atlas_attn_args *args, const atlas_tier_p
     Plan plan;
     atlas_status st = check_common(args, true, nullptr, &plan);
     if (st != ATLAS_OK) return st;
-    if (!pools || pools->struct_size != sizeof(atlas_tier_pools))
-        return fail(ATLAS_EINVAL, "pools NULL or wrong struct_size");
+    if ((st = check_pools(pools)) != ATLAS_OK) return st;
     if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
         return fail(ATLAS_EUNSUPPORTED, "tiered hot pages must be F16 or BF16");
     if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
     if (n > 0 && (!entries || !k_out || !v_out)) return fail(ATLAS_EINVAL, "NULL pointer");
     DecodeParams p = decode_params(args, plan);
-    p.i8_k = pools->int8_k;
-    p.i8_v = pools->int8_v;
-    p.i8_ks = pools->int8_k_scale;
-    p.i8_vs = pools->int8_v_scale;
-    p.i4_k = pools->int4_k;
-    p.i4_v = pools->int4_v;
-    p.i4_ks = pools->int4_k_scale;
-    p.i4_vs = pools->int4_v_scale;
-    p.n_i8 = pools->num_int8;
-    p.n_i4 = pools->num_int4;
+    set_pools(p, pools);
     return device_status(launch_dequant(p, args->kv_dtype, args->head_dim, entries, n, k_out,
                                         v_out, reinterpret_cast<hipStream_t>(args->stream)),
                          "dequant launch");
@@ -608,7 +616,7 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args, const atlas_tier
     if (!report_dev) return fail(ATLAS_EINVAL, "report_dev is NULL");
     if (pools && pools->struct_size != sizeof(atlas_tier_pools))
         return fail(ATLAS_EINVAL, "pools->struct_size mismatch");
-    if (pools && (pools->num_int8 < 0 || pools->num_int4 < 0))
+    if (pools && (pools->num_int8 < 0 || pools->num_int4 < 0 || pools->num_fp8 < 0))
         return fail(ATLAS_EINVAL, "negative tier pool size");
     ValidateParams v;
     std::memset(&v, 0, sizeof(v));
@@ -623,8 +631,14 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args, const atlas_tier
         v.p.i4_vs = pools->int4_v_scale;
         v.p.n_i8 = pools->num_int8;
         v.p.n_i4 = pools->num_int4;
+        v.p.f8_k = pools->fp8_k;
+        v.p.f8_v = pools->fp8_v;
+        v.p.f8_ks = pools->fp8_k_scale;
+        v.p.f8_vs = pools->fp8_v_scale;
+        v.p.n_f8 = pools->num_fp8;
         if (check_values && ((v.p.n_i8 > 0 && (!v.p.i8_ks || !v.p.i8_vs)) ||
-                             (v.p.n_i4 > 0 && (!v.p.i4_ks || !v.p.i4_vs))))
+                             (v.p.n_i4 > 0 && (!v.p.i4_ks || !v.p.i4_vs)) ||
+                             (v.p.n_f8 > 0 && (!v.p.f8_ks || !v.p.f8_vs))))
             return fail(ATLAS_EINVAL, "NULL tier scale pointer");
     }
     if (regen) {
@@ -695,21 +709,12 @@ atlas_status atlas_demote_pages(const atlas_attn_args *args, const atlas_tier_po
     Plan plan;
     atlas_status st = check_common(args, true, nullptr, &plan);
     if (st != ATLAS_OK) return st;
-    if (!pools || pools->struct_size != sizeof(atlas_tier_pools))
-        return fail(ATLAS_EINVAL, "pools NULL or wrong struct_size");
+    if ((st = check_pools(pools)) != ATLAS_OK) return st;
     if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
         return fail(ATLAS_EUNSUPPORTED, "hot pages must be F16 or BF16");
     if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
     if (n == 0) return ok();
     if (!src_slots || !dst_entries) return fail(ATLAS_EINVAL, "NULL src_slots or dst_entries");
-    if (pools->num_int8 < 0 || pools->num_int4 < 0)
-        return fail(ATLAS_EINVAL, "negative tier pool size");
-    if (pools->num_int8 > 0 && (!pools->int8_k || !pools->int8_v || !pools->int8_k_scale ||
-                                !pools->int8_v_scale))
-        return fail(ATLAS_EINVAL, "NULL int8 pool pointer");
-    if (pools->num_int4 > 0 && (!pools->int4_k || !pools->int4_v || !pools->int4_k_scale ||
-                                !pools->int4_v_scale))
-        return fail(ATLAS_EINVAL, "NULL int4 pool pointer");
     if ((int64_t)n * args->num_kv_heads * 2 > INT32_MAX) return fail(ATLAS_EINVAL, "n too large");
     DemoteParams d;
     std::memset(&d, 0, sizeof(d));
@@ -731,8 +736,13 @@ atlas_status atlas_demote_pages(const atlas_attn_args *args, const atlas_tier_po
     d.i4_v = const_cast<uint8_t *>(pools->int4_v);
     d.i4_ks = const_cast<float *>(pools->int4_k_scale);
     d.i4_vs = const_cast<float *>(pools->int4_v_scale);
+    d.f8_k = const_cast<uint8_t *>(pools->fp8_k);
+    d.f8_v = const_cast<uint8_t *>(pools->fp8_v);
+    d.f8_ks = const_cast<float *>(pools->fp8_k_scale);
+    d.f8_vs = const_cast<float *>(pools->fp8_v_scale);
     d.n_i8 = pools->num_int8;
     d.n_i4 = pools->num_int4;
+    d.n_f8 = pools->num_fp8;
     d.rejected = rejected;
     return device_status(launch_demote(d, reinterpret_cast<hipStream_t>(args->stream)),
                          "demote launch");

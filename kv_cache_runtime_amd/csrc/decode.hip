@@ -25,7 +25,7 @@
 // by zero, so NaN poison in page tails cannot leak.
 //
 // Tiered mode (ARGUS "Visual Architecture", "Why It Works"): a page's tier
-// comes from its page-table entry; int8 / int4 codes are widened in
+// comes from its page-table entry; int8 / int4 / FP8 codes are widened in
 // registers, the K scale multiplies the finished dot product and the V scale
 // multiplies the probability, so no dequantised page is ever written.
 // Regen mode (CFR-Atlas README, overview and KvRegenerator): leading pages are
@@ -165,6 +165,40 @@ __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry,
                     const int sh = 28 - 4 * (e & 7);
                     kf[u][e] = (float)sext_field(kw[u][e >> 3], sh, 4);
                     vf[u][e] = (float)sext_field(vw[u][e >> 3], sh, 4);
+                }
+            }
+            return true;
+        }
+        if (tier == 3) {  // FP8 E4M3 codes, widened by the hardware conversion
+            if (slot >= (uint32_t)p.n_f8) return false;
+            const int64_t row0 = ((int64_t)slot * p.num_kv_heads + g) * P + off;
+            const uint8_t *kb = p.f8_k + row0 * D + c * E;
+            const uint8_t *vb = p.f8_v + row0 * D + c * E;
+            uint32_t kw[U][(E + 3) / 4], vw[U][(E + 3) / 4];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                load_words<E>(kw[u], kb + (int64_t)u * D);
+                load_words<E>(vw[u], vb + (int64_t)u * D);
+            }
+            sd.kscale = p.f8_ks[(int64_t)slot * p.num_kv_heads + g];
+            sd.vscale = p.f8_vs[(int64_t)slot * p.num_kv_heads + g];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int wi = 0; wi < E / 4; ++wi) {  // bytes 0, 1 then 2, 3 of each word
+                    typedef float f2 __attribute__((ext_vector_type(2)));
+                    const f2 k01 = __builtin_amdgcn_cvt_pk_f32_fp8(kw[u][wi], false);
+                    const f2 k23 = __builtin_amdgcn_cvt_pk_f32_fp8(kw[u][wi], true);
+                    const f2 v01 = __builtin_amdgcn_cvt_pk_f32_fp8(vw[u][wi], false);
+                    const f2 v23 = __builtin_amdgcn_cvt_pk_f32_fp8(vw[u][wi], true);
+                    kf[u][4 * wi] = k01[0];
+                    kf[u][4 * wi + 1] = k01[1];
+                    kf[u][4 * wi + 2] = k23[0];
+                    kf[u][4 * wi + 3] = k23[1];
+                    vf[u][4 * wi] = v01[0];
+                    vf[u][4 * wi + 1] = v01[1];
+                    vf[u][4 * wi + 2] = v23[0];
+                    vf[u][4 * wi + 3] = v23[1];
                 }
             }
             return true;

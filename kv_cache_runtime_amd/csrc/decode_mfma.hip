@@ -1,5 +1,5 @@
 // Paged decode attention on the matrix cores (gfx950), for 16-bit and tiered
-// (f16 hot + int8 / int4 cold) pages, head_dim 128 and 2, 4 or 8 query heads
+// (f16 hot + int8 / int4 / FP8 cold) pages, head_dim 128 and 2, 4 or 8 query heads
 // per kv head.  Same method and split-K structure as decode.hip: keys folded
 // tile by tile with an online softmax (CFR-Atlas README, overview; ARGUS
 // "Latency & Throughput Impact"), splits merged by log-sum-exp.
@@ -25,8 +25,8 @@
 //
 // Tiered pages: the split's page-table entries are staged in LDS grouped by
 // tier, and each tier's run of pages is padded to whole tiles, so every tile
-// holds one tier and runs straight-line code for it.  K int8 / int4 codes
-// become f16 in registers (exact), the K scale multiplies the finished score
+// holds one tier and runs straight-line code for it.  K int8 / int4 / FP8
+// codes become f16 in registers (exact), the K scale multiplies the finished score
 // and the V scale the probability.  The matrix-core operand type is bf16 for
 // bf16 pages (query used as stored) and f16 otherwise (the query converted to
 // f16: exact for |q| in [2^-14, 65504], smaller magnitudes round with
@@ -98,10 +98,17 @@ __device__ __forceinline__ void i4x8_to_f16x8(uint32_t w, uint32_t (&out)[4]) {
     out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p3) - bias);
 }
 
-constexpr int kHot = 0, kInt8 = 1, kInt4 = 2;
+// FP8 E4M3 codes (4 per word) -> f16 pairs, exact, by the gfx950 hardware
+// conversion (two codes per instruction).
+__device__ __forceinline__ void f8x4_to_f16x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+constexpr int kHot = 0, kInt8 = 1, kInt4 = 2, kFp8 = 3;
 // 16-byte chunks per lane of one 16-token group, for K and for V
 template <int TIER>
-constexpr int chunks() { return TIER == kHot ? 4 : TIER == kInt8 ? 2 : 1; }
+constexpr int chunks() { return TIER == kHot ? 4 : TIER == kInt4 ? 1 : 2; }
 
 // Raw K of row `row` of a page (slot) for this lane (row r of the 16-lane
 // rows).  Resident pages give the four operands directly (operand ks = dims
@@ -127,6 +134,12 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slo
         kscale = p.i8_ks[(int64_t)slot * p.num_kv_heads + g];
         kr[0] = src[0];
         kr[1] = src[1];
+    } else if constexpr (TIER == kFp8) {
+        if (slot >= (uint32_t)p.n_f8) return false;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.f8_k + r0 * kD + 32 * r);
+        kscale = p.f8_ks[(int64_t)slot * p.num_kv_heads + g];
+        kr[0] = src[0];
+        kr[1] = src[1];
     } else {
         if (slot >= (uint32_t)p.n_i4) return false;
         kr[0] = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + 16 * r);
@@ -141,13 +154,18 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
     if constexpr (TIER == kHot) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[ks] = kr[ks];
-    } else if constexpr (TIER == kInt8) {
+    } else if constexpr (TIER == kInt8 || TIER == kFp8) {
         const uint32_t w[8] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w, kr[1].x, kr[1].y, kr[1].z, kr[1].w};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             uint32_t a, b, c, d;
-            i8x4_to_f16x4(w[2 * ks], a, b);
-            i8x4_to_f16x4(w[2 * ks + 1], c, d);
+            if constexpr (TIER == kInt8) {
+                i8x4_to_f16x4(w[2 * ks], a, b);
+                i8x4_to_f16x4(w[2 * ks + 1], c, d);
+            } else {
+                f8x4_to_f16x4(w[2 * ks], a, b);
+                f8x4_to_f16x4(w[2 * ks + 1], c, d);
+            }
             kb[ks] = make_uint4(a, b, c, d);
         }
     } else {
@@ -182,6 +200,12 @@ __device__ __forceinline__ bool load_v_group(const DecodeParams &p, uint32_t slo
         vscale = p.i8_vs[(int64_t)slot * p.num_kv_heads + g];
         vr[0] = src[lane];
         vr[1] = src[64 + lane];
+    } else if constexpr (TIER == kFp8) {
+        if (slot >= (uint32_t)p.n_f8) return false;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.f8_v + r0 * kD);
+        vscale = p.f8_vs[(int64_t)slot * p.num_kv_heads + g];
+        vr[0] = src[lane];
+        vr[1] = src[64 + lane];
     } else {
         if (slot >= (uint32_t)p.n_i4) return false;
         const uint4 *src = reinterpret_cast<const uint4 *>(p.i4_v + r0 * (kD / 2));
@@ -214,7 +238,7 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
             *reinterpret_cast<uint4 *>(vt + (base + tok) * kVPitch + 8 * (lane & 15)) =
                 keep_if(tok_ok(tok), vr[i].x, vr[i].y, vr[i].z, vr[i].w);
         }
-    } else if constexpr (TIER == kInt8) {
+    } else if constexpr (TIER == kInt8 || TIER == kFp8) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {  // chunk 64 i + lane: token 8 i + lane / 8
             const int tok = 8 * i + (lane >> 3);
@@ -222,7 +246,10 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
             const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
             uint32_t h[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) i8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (TIER == kInt8) i8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
+                else f8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
+            }
             uint16_t *dst = vt + (base + tok) * kVPitch + 16 * (lane & 7);
             *reinterpret_cast<uint4 *>(dst) = keep_if(ok, h[0], h[1], h[2], h[3]);
             *reinterpret_cast<uint4 *>(dst + 8) = keep_if(ok, h[4], h[5], h[6], h[7]);
@@ -671,11 +698,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     };
 
     if constexpr (MODE == MODE_TIERED) {
-        // runs of hot, int8 and int4 pages; tier-3 entries name no pool
+        // runs of hot, int8, int4 and FP8 pages
         run(TierC<kHot>{}, TierC<0>{}, 0, tier_count[0]);
         run(TierC<kInt8>{}, TierC<0>{}, tier_count[0], tier_count[1]);
         run(TierC<kInt4>{}, TierC<0>{}, tier_count[0] + tier_count[1], tier_count[2]);
-        if (tier_count[3] > 0 || !staged) bad = true;
+        run(TierC<kFp8>{}, TierC<0>{}, tier_count[0] + tier_count[1] + tier_count[2],
+            tier_count[3]);
+        if (!staged) bad = true;
     } else {
         run(TierC<kHot>{}, TierC<1>{}, 0, 0);
     }

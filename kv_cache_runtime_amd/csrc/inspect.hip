@@ -201,6 +201,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DecodeParams p, int 
             const int sh = (t & 1) ? 24 : 28;  // high nibble for odd elements
             kv = (float)sext_field(bk, sh, 4) * ks;
             vv = (float)sext_field(bv, sh, 4) * vs;
+        } else if (tier == 3 && slot < (uint32_t)p.n_f8) {
+            const float ks = p.f8_ks[(int64_t)slot * p.num_kv_heads + g];
+            const float vs = p.f8_vs[(int64_t)slot * p.num_kv_heads + g];
+            kv = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)p.f8_k[src_row * D + t], false)[0] * ks;
+            vv = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)p.f8_v[src_row * D + t], false)[0] * vs;
         }
         k_out[dst + t] = kv;
         v_out[dst + t] = vv;
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(256) void validate_kernel(const ValidateParams v) {
         const bool ok = tier == 0   ? slot < (uint32_t)p.num_blocks
                         : tier == 1 ? slot < (uint32_t)p.n_i8
                         : tier == 2 ? slot < (uint32_t)p.n_i4
-                                    : false;
+                                    : slot < (uint32_t)p.n_f8;
         if (!ok) {
             if (threadIdx.x == 0) ++bad_entry;
             continue;
@@ -293,8 +298,18 @@ __global__ __launch_bounds__(256) void validate_kernel(const ValidateParams v) {
                 if (!__builtin_isfinite(b)) ++bad_val;
             }
         } else {
-            const float *ks = tier == 1 ? p.i8_ks : p.i4_ks;
-            const float *vs = tier == 1 ? p.i8_vs : p.i4_vs;
+            const float *ks = tier == 1 ? p.i8_ks : tier == 2 ? p.i4_ks : p.f8_ks;
+            const float *vs = tier == 1 ? p.i8_vs : tier == 2 ? p.i4_vs : p.f8_vs;
+            if (tier == 3 && p.f8_k && p.f8_v) {  // FP8 NaN codes (0x7F / 0xFF)
+                const int64_t n = (int64_t)p.num_kv_heads * rows * D;
+                for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+                    const int g = (int)(i / ((int64_t)rows * D));
+                    const int64_t rem = i - (int64_t)g * rows * D;
+                    const int64_t idx = (((int64_t)slot * p.num_kv_heads + g) * P) * D + rem;
+                    if ((p.f8_k[idx] & 0x7F) == 0x7F) ++bad_val;
+                    if ((p.f8_v[idx] & 0x7F) == 0x7F) ++bad_val;
+                }
+            }
             for (int g = threadIdx.x; g < p.num_kv_heads; g += blockDim.x) {
                 const int64_t i = (int64_t)slot * p.num_kv_heads + g;
                 if (!__builtin_isfinite(ks[i])) ++bad_scale;

@@ -51,6 +51,9 @@ struct DecodeParams {
     const uint8_t *i4_k, *i4_v;
     const float *i4_ks, *i4_vs;
     int32_t n_i8, n_i4;
+    const uint8_t *f8_k, *f8_v;   // FP8 E4M3 codes
+    const float *f8_ks, *f8_vs;
+    int32_t n_f8;
     // regenerated pages
     uint64_t seed;
     uint32_t layer;
@@ -160,6 +163,9 @@ struct DemoteParams {
     uint8_t *i4_k, *i4_v;
     float *i4_ks, *i4_vs;
     int32_t n_i8, n_i4;
+    uint8_t *f8_k, *f8_v;
+    float *f8_ks, *f8_vs;
+    int32_t n_f8;
     int32_t *rejected;             // device counter or null
 };
 

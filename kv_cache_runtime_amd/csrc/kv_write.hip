@@ -8,11 +8,12 @@
 // concatenated).  Under a rotary embedding the K row is stored rotated by
 // its position, as the attention kernels expect cached keys.
 //
-// Demotion (argus-cache, "Visual Architecture": FP16 -> INT8 -> INT4 tiers):
-// one block per (page, kv head, K|V) gets a symmetric f32 scale max|x| / qmax
-// and codes rint(x / scale) clamped to [-qmax, qmax]; both divisions are
-// correctly rounded f32 so the integer decisions are reproducible.  int4
-// codes are two's-complement nibbles, element 2i in the low nibble of byte i.
+// Demotion (argus-cache, "Visual Architecture": FP16 -> FP8 -> INT8 -> INT4
+// tiers): one block per (page, kv head, K|V) gets a symmetric f32 scale
+// max|x| / qmax and codes rint(x / scale) clamped to [-qmax, qmax] (FP8: the
+// nearest E4M3 code to x / scale, qmax 448); both divisions are correctly
+// rounded f32 so the code decisions are reproducible.  int4 codes are
+// two's-complement nibbles, element 2i in the low nibble of byte i.
 #include "device.h"
 
 namespace atlas {
@@ -94,8 +95,21 @@ __device__ inline float absmax8(const uint4 w, const bool bf16) {
     return m;
 }
 
-// Codes of the 8 elements of chunk ch, stored at their place in the int8
-// (8 bytes per chunk) or int4 (one 32-bit word per chunk) block.
+// The FP8 E4M3 code nearest to y (ties to the even code), sign from y's sign
+// bit, magnitudes of 448 and above saturating to 448 (0x7E; the next step
+// would be the NaN code).
+__device__ inline uint32_t e4m3_nearest(const float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // subnormal grid 2^-9
+    uint32_t u = __float_as_uint(a);
+    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;  // 3 mantissa bits, ties to even
+    return sign | ((((u >> 23) - 120u) << 3) | ((u >> 20) & 7u));  // exponent bias 127 -> 7
+}
+
+// Codes of the 8 elements of chunk ch, stored at their place in the int8 or
+// FP8 (8 bytes per chunk) or int4 (one 32-bit word per chunk) block.
 __device__ inline void encode8(const uint4 w, const bool bf16, const float scale, const int qmax,
                                const int tier, int8_t *i8, uint8_t *i4, const int64_t ch) {
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -105,10 +119,14 @@ __device__ inline void encode8(const uint4 w, const bool bf16, const float scale
         const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
         const float x = bf16 ? __uint_as_float((uint32_t)b << 16)
                              : (float)__builtin_bit_cast(_Float16, b);
+        if (tier == 3) {
+            c[j] = scale > 0.0f ? (int)e4m3_nearest(__fdiv_rn(x, scale)) : 0;
+            continue;
+        }
         const float q = scale > 0.0f ? rintf(__fdiv_rn(x, scale)) : 0.0f;
         c[j] = (int)fminf(fmaxf(q, (float)-qmax), (float)qmax);
     }
-    if (tier == 1) {
+    if (tier == 1 || tier == 3) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -140,9 +158,13 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     const int32_t src_slot = d.src_slots[i];
     const uint32_t dst = (uint32_t)d.dst_entries[i];
     const uint32_t tier = dst >> 30, slot = dst & ((1u << 30) - 1u);
-    const bool dst_ok = (tier == 1 && slot < (uint32_t)d.n_i8) || (tier == 2 && slot < (uint32_t)d.n_i4);
+    const bool dst_ok = (tier == 1 && slot < (uint32_t)d.n_i8) ||
+                        (tier == 2 && slot < (uint32_t)d.n_i4) ||
+                        (tier == 3 && slot < (uint32_t)d.n_f8);
     const bool src_ok = src_slot >= 0 && src_slot < d.num_blocks;
-    float *sc = tier == 1 ? (kv ? d.i8_vs : d.i8_ks) : (kv ? d.i4_vs : d.i4_ks);
+    float *sc = tier == 1   ? (kv ? d.i8_vs : d.i8_ks)
+                : tier == 2 ? (kv ? d.i4_vs : d.i4_ks)
+                            : (kv ? d.f8_vs : d.f8_ks);
     if (!dst_ok || !src_ok) {
         if (lane == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
         // a bad source: the page turns its rows into NaN
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
         return;
     }
     const bool bf16 = d.kv_type == KV_BF16;
-    const int qmax = tier == 1 ? 127 : 7;
+    const int qmax = tier == 1 ? 127 : tier == 2 ? 7 : 448;
     const int64_t n = (int64_t)d.page_tokens * d.head_dim;  // multiple of 8
     const int64_t nch = n / 8;
     const uint4 *src = reinterpret_cast<const uint4 *>(
@@ -172,7 +194,9 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     const float scale = __fdiv_rn(amax, (float)qmax);
 
     const int64_t dst_base = ((int64_t)slot * d.num_kv_heads + g) * n;  // in elements
-    int8_t *i8 = tier == 1 ? (kv ? d.i8_v : d.i8_k) + dst_base : nullptr;
+    int8_t *i8 = tier == 1   ? (kv ? d.i8_v : d.i8_k) + dst_base
+                 : tier == 3 ? reinterpret_cast<int8_t *>(kv ? d.f8_v : d.f8_k) + dst_base
+                             : nullptr;
     uint8_t *i4 = tier == 2 ? (kv ? d.i4_v : d.i4_k) + dst_base / 2 : nullptr;
 #pragma unroll
     for (int j = 0; j < R; ++j) {

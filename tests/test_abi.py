@@ -232,6 +232,16 @@ def test_write_and_demote_arguments_are_checked():
     pools.num_int4 = 2  # int4 pointers missing
     assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
                                 None) == atlas.EINVAL
+    pools.num_int4 = 0
+    pools.num_fp8 = 2  # fp8 pointers missing
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    assert "fp8" in atlas.atlas_last_error()
+    pools.num_fp8 = 0
+    pools.reserved2 = 1
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    pools.reserved2 = 0
     assert L.atlas_demote_pages(ctypes.byref(_args(kv_dtype=atlas.F32, q_dtype=atlas.F32)),
                                 ctypes.byref(pools), FAKE, FAKE, 1, None) == atlas.EUNSUPPORTED
     assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), None, None, 0,

@@ -481,7 +481,7 @@ def test_validate_tables_tiered_and_regen(gpu):
     scales = w.tiers["i8_k_scale" if tier == 1 else "i4_k_scale"]
     scales[slot, 2] = float("inf")
     assert prob.validate(check_values=True) == [0, 0, 0, 1]
-    prob.table[0, 1] = -(1 << 30)              # 0xC0000000: tier 3, names no pool
+    prob.table[0, 1] = -(1 << 30)              # 0xC0000000: FP8 slot 0, FP8 pool empty
     assert prob.validate()[0] == 1
 
     w5 = synth.config(5, device=gpu, context_lens=3000, query_lens=200, num_heads=16,
