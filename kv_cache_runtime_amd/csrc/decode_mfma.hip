@@ -105,10 +105,12 @@ __device__ __forceinline__ void f8x4_to_f16x4(uint32_t w, uint32_t &lo, uint32_t
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
-constexpr int kHot = 0, kInt8 = 1, kInt4 = 2, kFp8 = 3;
+// Tile kinds.  kByte covers both one-byte code tiers (int8 and FP8): same
+// layout and load path, the pool and the widening chosen per run (f8).
+constexpr int kHot = 0, kByte = 1, kInt4 = 2;
 // 16-byte chunks per lane of one 16-token group, for K and for V
 template <int TIER>
-constexpr int chunks() { return TIER == kHot ? 4 : TIER == kInt4 ? 1 : 2; }
+constexpr int chunks() { return TIER == kHot ? 4 : TIER == kByte ? 2 : 1; }
 
 // Raw K of row `row` of a page (slot) for this lane (row r of the 16-lane
 // rows).  Resident pages give the four operands directly (operand ks = dims
@@ -117,7 +119,8 @@ constexpr int chunks() { return TIER == kHot ? 4 : TIER == kInt4 ? 1 : 2; }
 // scale; false if the slot is outside its pool.
 template <int KV, int MODE, int TIER>
 __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slot, int g, int row,
-                                             int r, uint4 (&kr)[chunks<TIER>()], float &kscale) {
+                                             int r, uint4 (&kr)[chunks<TIER>()], float &kscale,
+                                             bool f8) {
     kscale = 1.0f;
     const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row;
     if constexpr (TIER == kHot) {
@@ -128,16 +131,11 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slo
             const int d0 = MODE == MODE_TIERED ? 32 * r + 8 * ks : 32 * ks + 8 * r;
             kr[ks] = *reinterpret_cast<const uint4 *>(src + d0);
         }
-    } else if constexpr (TIER == kInt8) {
-        if (slot >= (uint32_t)p.n_i8) return false;
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.i8_k + r0 * kD + 32 * r);
-        kscale = p.i8_ks[(int64_t)slot * p.num_kv_heads + g];
-        kr[0] = src[0];
-        kr[1] = src[1];
-    } else if constexpr (TIER == kFp8) {
-        if (slot >= (uint32_t)p.n_f8) return false;
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.f8_k + r0 * kD + 32 * r);
-        kscale = p.f8_ks[(int64_t)slot * p.num_kv_heads + g];
+    } else if constexpr (TIER == kByte) {
+        if (slot >= (uint32_t)(f8 ? p.n_f8 : p.n_i8)) return false;
+        const uint8_t *pool = f8 ? p.f8_k : reinterpret_cast<const uint8_t *>(p.i8_k);
+        const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD + 32 * r);
+        kscale = (f8 ? p.f8_ks : p.i8_ks)[(int64_t)slot * p.num_kv_heads + g];
         kr[0] = src[0];
         kr[1] = src[1];
     } else {
@@ -150,23 +148,29 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slo
 
 // Raw K -> the four 16-bit operands (codes widened to f16, exact).
 template <int TIER>
-__device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4 (&kb)[4]) {
+__device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4 (&kb)[4],
+                                       bool f8) {
     if constexpr (TIER == kHot) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[ks] = kr[ks];
-    } else if constexpr (TIER == kInt8 || TIER == kFp8) {
+    } else if constexpr (TIER == kByte) {
         const uint32_t w[8] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w, kr[1].x, kr[1].y, kr[1].z, kr[1].w};
+        if (f8) {  // run-uniform
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint32_t a, b, c, d;
-            if constexpr (TIER == kInt8) {
-                i8x4_to_f16x4(w[2 * ks], a, b);
-                i8x4_to_f16x4(w[2 * ks + 1], c, d);
-            } else {
+            for (int ks = 0; ks < 4; ++ks) {
+                uint32_t a, b, c, d;
                 f8x4_to_f16x4(w[2 * ks], a, b);
                 f8x4_to_f16x4(w[2 * ks + 1], c, d);
+                kb[ks] = make_uint4(a, b, c, d);
             }
-            kb[ks] = make_uint4(a, b, c, d);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                uint32_t a, b, c, d;
+                i8x4_to_f16x4(w[2 * ks], a, b);
+                i8x4_to_f16x4(w[2 * ks + 1], c, d);
+                kb[ks] = make_uint4(a, b, c, d);
+            }
         }
     } else {
         const uint32_t w[4] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w};
@@ -185,7 +189,7 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
 template <int KV, int TIER>
 __device__ __forceinline__ bool load_v_group(const DecodeParams &p, uint32_t slot, int g, int row0,
                                              int lane, uint4 (&vr)[chunks<TIER>()],
-                                             float &vscale) {
+                                             float &vscale, bool f8) {
     vscale = 1.0f;
     const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row0;
     if constexpr (TIER == kHot) {
@@ -194,16 +198,11 @@ __device__ __forceinline__ bool load_v_group(const DecodeParams &p, uint32_t slo
             reinterpret_cast<const uint16_t *>(p.v_pool) + r0 * kD);
 #pragma unroll
         for (int i = 0; i < 4; ++i) vr[i] = src[64 * i + lane];
-    } else if constexpr (TIER == kInt8) {
-        if (slot >= (uint32_t)p.n_i8) return false;
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.i8_v + r0 * kD);
-        vscale = p.i8_vs[(int64_t)slot * p.num_kv_heads + g];
-        vr[0] = src[lane];
-        vr[1] = src[64 + lane];
-    } else if constexpr (TIER == kFp8) {
-        if (slot >= (uint32_t)p.n_f8) return false;
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.f8_v + r0 * kD);
-        vscale = p.f8_vs[(int64_t)slot * p.num_kv_heads + g];
+    } else if constexpr (TIER == kByte) {
+        if (slot >= (uint32_t)(f8 ? p.n_f8 : p.n_i8)) return false;
+        const uint8_t *pool = f8 ? p.f8_v : reinterpret_cast<const uint8_t *>(p.i8_v);
+        const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD);
+        vscale = (f8 ? p.f8_vs : p.i8_vs)[(int64_t)slot * p.num_kv_heads + g];
         vr[0] = src[lane];
         vr[1] = src[64 + lane];
     } else {
@@ -230,7 +229,7 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint32_t a, uint32_t b, uint32
 template <int TIER, typename TokOk>
 __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
                                               const uint4 (&vr)[chunks<TIER>()], int lane,
-                                              TokOk tok_ok) {
+                                              TokOk tok_ok, bool f8) {
     if constexpr (TIER == kHot) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {  // chunk 64 i + lane: token 4 i + lane / 16
@@ -238,17 +237,19 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
             *reinterpret_cast<uint4 *>(vt + (base + tok) * kVPitch + 8 * (lane & 15)) =
                 keep_if(tok_ok(tok), vr[i].x, vr[i].y, vr[i].z, vr[i].w);
         }
-    } else if constexpr (TIER == kInt8 || TIER == kFp8) {
+    } else if constexpr (TIER == kByte) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {  // chunk 64 i + lane: token 8 i + lane / 8
             const int tok = 8 * i + (lane >> 3);
             const bool ok = tok_ok(tok);
             const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
             uint32_t h[8];
+            if (f8) {  // run-uniform
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (TIER == kInt8) i8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
-                else f8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
+                for (int j = 0; j < 4; ++j) f8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) i8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
             }
             uint16_t *dst = vt + (base + tok) * kVPitch + 16 * (lane & 7);
             *reinterpret_cast<uint4 *>(dst) = keep_if(ok, h[0], h[1], h[2], h[3]);
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     // Walks the tiles of one run of pages with one tier: the whole split in
     // token order (natural), or the sp .. sp + np - 1 staged entries of a
     // tier.  Each wave takes every fourth tile of the run.
-    auto run = [&](auto tier_c, auto natural_c, int sp, int np) {
+    auto run = [&](auto tier_c, auto natural_c, int sp, int np, bool f8) {
         constexpr int TIER = decltype(tier_c)::value;
         constexpr bool natural = decltype(natural_c)::value != 0;
         constexpr int NC = chunks<TIER>();
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             kok[tg] = G_.live[tg];
             kscale[tg] = 1.0f;
             if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.row[tg] + c, r,
-                                                         kr[tg], kscale[tg])) {
+                                                         kr[tg], kscale[tg], f8)) {
                 bad = true;
                 kok[tg] = false;
             }
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             vok[tg] = G_.live[tg];
             vscale[tg] = 1.0f;
             if (vok[tg] && !load_v_group<KV, TIER>(p, G_.slot[tg], g, G_.row[tg], lane,
-                                                   vr[tg], vscale[tg])) {
+                                                   vr[tg], vscale[tg], f8)) {
                 bad = true;
                 vok[tg] = false;
             }
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             for (int tg = 0; tg < 4; ++tg) {
                 kvalid[tg] = kok[tg] && in_range(cur.tok[tg] + c);
                 uint4 kb[4];
-                widen_k<TIER>(kr[tg], kb);
+                widen_k<TIER>(kr[tg], kb, f8);
                 sc[tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) sc[tg] = mfma16<QT>(qf[ks], kb[ks], sc[tg]);
@@ -655,10 +656,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                     const bool live = vok[tg];
                     const int tb = cur.tok[tg];
                     if (live && tb >= t0 && tb + 16 <= t1)  // whole group visible (uniform)
-                        store_v_group<TIER>(vt, 16 * j, vr[tg], lane, [](int) { return true; });
+                        store_v_group<TIER>(vt, 16 * j, vr[tg], lane, [](int) { return true; }, f8);
                     else
                         store_v_group<TIER>(vt, 16 * j, vr[tg], lane,
-                                            [&](int tok) { return live && in_range(tb + tok); });
+                                            [&](int tok) { return live && in_range(tb + tok); }, f8);
                     load_v(nxt, tg);  // this group's registers are free again
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -698,15 +699,20 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     };
 
     if constexpr (MODE == MODE_TIERED) {
-        // runs of hot, int8, int4 and FP8 pages
-        run(TierC<kHot>{}, TierC<0>{}, 0, tier_count[0]);
-        run(TierC<kInt8>{}, TierC<0>{}, tier_count[0], tier_count[1]);
-        run(TierC<kInt4>{}, TierC<0>{}, tier_count[0] + tier_count[1], tier_count[2]);
-        run(TierC<kFp8>{}, TierC<0>{}, tier_count[0] + tier_count[1] + tier_count[2],
-            tier_count[3]);
+        // runs of hot, int4, int8 and FP8 pages; the two one-byte tiers share
+        // one body (a loop the compiler keeps rolled), so the kernel carries
+        // three run bodies rather than four
+        run(TierC<kHot>{}, TierC<0>{}, 0, tier_count[0], false);
+        run(TierC<kInt4>{}, TierC<0>{}, tier_count[0] + tier_count[1], tier_count[2], false);
+#pragma clang loop unroll(disable)
+        for (int pass = 0; pass < 2; ++pass) {
+            const bool f8 = pass == 1;
+            const int sp = f8 ? tier_count[0] + tier_count[1] + tier_count[2] : tier_count[0];
+            run(TierC<kByte>{}, TierC<0>{}, sp, f8 ? tier_count[3] : tier_count[1], f8);
+        }
         if (!staged) bad = true;
     } else {
-        run(TierC<kHot>{}, TierC<1>{}, 0, 0);
+        run(TierC<kHot>{}, TierC<1>{}, 0, 0, false);
     }
 
     // ---- merge the waves: l is summed over the 16 lanes of the row holding
