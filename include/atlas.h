@@ -361,11 +361,14 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,
                             const void *v_new);
 
 /*
- * atlas_demote_pages: encodes hot pages into the cold tiers (argus-cache,
- * "Visual Architecture": FP16 -> FP8 -> INT8 -> INT4).  For i < n, hot block
- * src_slots[i] of args->k_pool / v_pool (kv_dtype F16 or BF16, every row
- * finite) is encoded into dst_entries[i] = (tier << 30) | slot, tier 1 (int8),
- * 2 (int4) or 3 (FP8) of `pools`: for each kv head, K and V separately,
+ * atlas_demote_pages: encodes pages into the cold tiers (argus-cache,
+ * "Visual Architecture": the compression cascade FP16 -> FP8 -> INT8 ->
+ * INT4).  For i < n, the source src_slots[i] is a tiered entry (tier << 30) |
+ * slot: tier 0 is a hot block of args->k_pool / v_pool (kv_dtype F16 or BF16,
+ * every row finite; a plain block id is such an entry), tiers 1-3 a cold slot
+ * of `pools` whose values enter as f32(code * scale).  It is encoded into
+ * dst_entries[i] = (tier << 30) | slot, tier 1 (int8), 2 (int4) or 3 (FP8) of
+ * `pools`: for each kv head, K and V separately,
  *     scale = max|x| / qmax            (f32, correctly rounded; qmax 127 / 7 / 448)
  *     code  = clamp(rint(x / scale), -qmax, qmax)   (round half to even)
  *     FP8:  code = the E4M3 code nearest to x / scale (ties to the even
@@ -373,8 +376,8 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,
  * and an all-zero block gets scale 0 and codes 0.  Codes and scales are
  * written through the pools' pointers; the caller then points its page-table
  * entries at dst_entries.  A destination outside its pool rejects the page
- * (nothing written); a source block outside the hot pool writes NaN scales,
- * so rows reading the page fail loudly.  Each rejected page adds 1 to
+ * (nothing written); a source outside its pool writes NaN scales, so rows
+ * reading the page fail loudly.  Each rejected page adds 1 to
  * *rejected (device int32, optional).  The source and destination sets must
  * not overlap between calls in flight.  Asynchronous on args->stream.
  */

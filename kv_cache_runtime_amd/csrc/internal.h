@@ -155,7 +155,7 @@ struct DemoteParams {
     const void *k_pool, *v_pool;   // hot pool, bf16 or f16
     int32_t kv_type;
     int32_t num_kv_heads, head_dim, page_tokens, num_blocks;
-    const int32_t *src_slots;      // [n] hot blocks
+    const int32_t *src_slots;      // [n] sources: (tier << 30) | slot, tier 0 = hot block
     const int32_t *dst_entries;    // [n] (tier << 30) | slot, tier 1 or 2
     int32_t n;
     int8_t *i8_k, *i8_v;

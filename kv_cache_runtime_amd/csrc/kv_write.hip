@@ -12,7 +12,9 @@
 // tiers): one block per (page, kv head, K|V) gets a symmetric f32 scale
 // max|x| / qmax and codes rint(x / scale) clamped to [-qmax, qmax] (FP8: the
 // nearest E4M3 code to x / scale, qmax 448); both divisions are correctly
-// rounded f32 so the code decisions are reproducible.  int4 codes are
+// rounded f32 so the code decisions are reproducible.  The source is a hot
+// block or a cold slot (the cascade's next step): cold values enter as
+// f32(code * scale).  int4 codes are
 // two's-complement nibbles, element 2i in the low nibble of byte i.
 #include "device.h"
 
@@ -81,17 +83,64 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteKvParams w) {
     }
 }
 
-// max |x| over the 8 16-bit elements of a chunk.
-__device__ inline float absmax8(const uint4 w, const bool bf16) {
+// The source block of a demotion: hot 16-bit rows, or the codes and scale of
+// a cold slot.  A chunk is 8 consecutive elements: 16 bytes hot, 8 bytes
+// int8 / FP8, 4 bytes int4 (loaded into the low words of a uint4).
+struct DemoteSrc {
+    bool bf16;           // hot pool type
+    const uint8_t *base; // the block's first byte
+    float scale;         // cold tiers
+};
+
+template <int ST>  // source tier: 0 hot, 1 int8, 2 int4, 3 FP8
+__device__ inline uint4 load_chunk(const DemoteSrc &s, int64_t ch) {
+    if constexpr (ST == 0) return reinterpret_cast<const uint4 *>(s.base)[ch];
+    if constexpr (ST == 2)
+        return make_uint4(reinterpret_cast<const uint32_t *>(s.base)[ch], 0u, 0u, 0u);
+    const uint2 v = reinterpret_cast<const uint2 *>(s.base)[ch];
+    return make_uint4(v.x, v.y, 0u, 0u);
+}
+
+// The 8 values of a chunk in f32: hot values exactly, cold values as
+// f32(code * scale) (one rounding of the exact product).
+template <int ST>
+__device__ inline void widen8(const DemoteSrc &s, const uint4 w, float (&x)[8]) {
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    if constexpr (ST == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+            x[j] = s.bf16 ? __uint_as_float((uint32_t)b << 16)
+                          : (float)__builtin_bit_cast(_Float16, b);
+        }
+    } else if constexpr (ST == 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = (float)sext_field(ww[j >> 2], 24 - 8 * (j & 3), 8) * s.scale;
+    } else if constexpr (ST == 2) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (float)sext_field(ww[0], 28 - 4 * j, 4) * s.scale;
+    } else {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(ww[q], false);
+            const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(ww[q], true);
+            x[4 * q] = a[0] * s.scale;
+            x[4 * q + 1] = a[1] * s.scale;
+            x[4 * q + 2] = b[0] * s.scale;
+            x[4 * q + 3] = b[1] * s.scale;
+        }
+    }
+}
+
+template <int ST>
+__device__ inline float absmax8(const DemoteSrc &s, const uint4 w) {
+    float x[8];
+    widen8<ST>(s, w, x);
     float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
-        const float x = bf16 ? __uint_as_float((uint32_t)b << 16)
-                             : (float)__builtin_bit_cast(_Float16, b);
-        m = fmaxf(m, fabsf(x));
-    }
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
     return m;
 }
 
@@ -110,23 +159,23 @@ __device__ inline uint32_t e4m3_nearest(const float y) {
 
 // Codes of the 8 elements of chunk ch, stored at their place in the int8 or
 // FP8 (8 bytes per chunk) or int4 (one 32-bit word per chunk) block.
-__device__ inline void encode8(const uint4 w, const bool bf16, const float scale, const int qmax,
-                               const int tier, int8_t *i8, uint8_t *i4, const int64_t ch) {
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+template <int ST, int DT>  // source and destination tiers
+__device__ inline void encode8(const DemoteSrc &src, const uint4 w, const float scale,
+                               int8_t *i8, uint8_t *i4, const int64_t ch) {
+    constexpr int qmax = DT == 1 ? 127 : DT == 2 ? 7 : 448;
+    float x[8];
+    widen8<ST>(src, w, x);
     int c[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
-        const float x = bf16 ? __uint_as_float((uint32_t)b << 16)
-                             : (float)__builtin_bit_cast(_Float16, b);
-        if (tier == 3) {
-            c[j] = scale > 0.0f ? (int)e4m3_nearest(__fdiv_rn(x, scale)) : 0;
-            continue;
+        if constexpr (DT == 3) {
+            c[j] = scale > 0.0f ? (int)e4m3_nearest(__fdiv_rn(x[j], scale)) : 0;
+        } else {
+            const float q = scale > 0.0f ? rintf(__fdiv_rn(x[j], scale)) : 0.0f;
+            c[j] = (int)fminf(fmaxf(q, (float)-qmax), (float)qmax);
         }
-        const float q = scale > 0.0f ? rintf(__fdiv_rn(x, scale)) : 0.0f;
-        c[j] = (int)fminf(fmaxf(q, (float)-qmax), (float)qmax);
     }
-    if (tier == 1 || tier == 3) {
+    if constexpr (DT == 1 || DT == 3) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -142,9 +191,57 @@ __device__ inline void encode8(const uint4 w, const bool bf16, const float scale
     }
 }
 
+// Max |x| pass, then the encoding pass, of one block by one wave.
+template <int R, int ST, int DT>
+__device__ inline void encode_block(const DemoteSrc &src, const int64_t nch, int8_t *i8,
+                                    uint8_t *i4, float *scale_out, const int lane) {
+    constexpr int qmax = DT == 1 ? 127 : DT == 2 ? 7 : 448;
+    uint4 keep[R];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t ch = lane + 64 * j;
+        keep[j] = ch < nch ? load_chunk<ST>(src, ch) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) amax = fmaxf(amax, absmax8<ST>(src, keep[j]));
+    for (int64_t ch = lane + 64 * R; ch < nch; ch += 64)
+        amax = fmaxf(amax, absmax8<ST>(src, load_chunk<ST>(src, ch)));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float scale = __fdiv_rn(amax, (float)qmax);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t ch = lane + 64 * j;
+        if (ch < nch) encode8<ST, DT>(src, keep[j], scale, i8, i4, ch);
+    }
+    for (int64_t ch = lane + 64 * R; ch < nch; ch += 64)
+        encode8<ST, DT>(src, load_chunk<ST>(src, ch), scale, i8, i4, ch);
+    if (lane == 0) *scale_out = scale;
+}
+
+template <int R, int ST>
+__device__ inline void dispatch_dst(uint32_t dt, const DemoteSrc &src, int64_t nch, int8_t *i8,
+                                    uint8_t *i4, float *sdst, int lane) {
+    if (dt == 1) encode_block<R, ST, 1>(src, nch, i8, i4, sdst, lane);
+    else if (dt == 2) encode_block<R, ST, 2>(src, nch, i8, i4, sdst, lane);
+    else encode_block<R, ST, 3>(src, nch, i8, i4, sdst, lane);
+}
+
+template <int R>
+__device__ inline void dispatch_block(uint32_t st, uint32_t dt, const DemoteSrc &src, int64_t nch,
+                                      int8_t *i8, uint8_t *i4, float *sdst, int lane) {
+    switch (st) {
+        case 0: dispatch_dst<R, 0>(dt, src, nch, i8, i4, sdst, lane); break;
+        case 1: dispatch_dst<R, 1>(dt, src, nch, i8, i4, sdst, lane); break;
+        case 2: dispatch_dst<R, 2>(dt, src, nch, i8, i4, sdst, lane); break;
+        default: dispatch_dst<R, 3>(dt, src, nch, i8, i4, sdst, lane); break;
+    }
+}
+
 // One wave per (page i, kv head g, K or V) block, four blocks per
-// workgroup.  Lane l owns the 16-byte chunks l + 64 j.  A block of up to
-// 64 * R chunks (P * D <= 2048 at R = 4) is read once and kept in registers
+// workgroup.  Lane l owns the chunks l + 64 j.  A block of up to 64 * R
+// chunks (P * D <= 2048 at R = 4) is read once and kept in registers
 // between the max |x| pass and the encoding pass; a larger block is read a
 // second time for the encoding.  No barrier: the waves are independent.
 template <int R>
@@ -155,13 +252,17 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     const int kv = (int)(unit & 1);
     const int g = (int)((unit >> 1) % d.num_kv_heads);
     const int i = (int)((unit >> 1) / d.num_kv_heads);
-    const int32_t src_slot = d.src_slots[i];
+    const uint32_t se = (uint32_t)d.src_slots[i];
+    const uint32_t stier = se >> 30, sslot = se & ((1u << 30) - 1u);
     const uint32_t dst = (uint32_t)d.dst_entries[i];
     const uint32_t tier = dst >> 30, slot = dst & ((1u << 30) - 1u);
     const bool dst_ok = (tier == 1 && slot < (uint32_t)d.n_i8) ||
                         (tier == 2 && slot < (uint32_t)d.n_i4) ||
                         (tier == 3 && slot < (uint32_t)d.n_f8);
-    const bool src_ok = src_slot >= 0 && src_slot < d.num_blocks;
+    const bool src_ok = (stier == 0 && sslot < (uint32_t)d.num_blocks) ||
+                        (stier == 1 && sslot < (uint32_t)d.n_i8) ||
+                        (stier == 2 && sslot < (uint32_t)d.n_i4) ||
+                        (stier == 3 && sslot < (uint32_t)d.n_f8);
     float *sc = tier == 1   ? (kv ? d.i8_vs : d.i8_ks)
                 : tier == 2 ? (kv ? d.i4_vs : d.i4_ks)
                             : (kv ? d.f8_vs : d.f8_ks);
@@ -171,41 +272,33 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
         if (dst_ok && lane == 0) sc[(int64_t)slot * d.num_kv_heads + g] = __builtin_nanf("");
         return;
     }
-    const bool bf16 = d.kv_type == KV_BF16;
-    const int qmax = tier == 1 ? 127 : tier == 2 ? 7 : 448;
     const int64_t n = (int64_t)d.page_tokens * d.head_dim;  // multiple of 8
-    const int64_t nch = n / 8;
-    const uint4 *src = reinterpret_cast<const uint4 *>(
-        reinterpret_cast<const uint16_t *>(kv ? d.v_pool : d.k_pool) +
-        ((int64_t)src_slot * d.num_kv_heads + g) * n);
-
-    uint4 keep[R];
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const int64_t ch = lane + 64 * j;
-        keep[j] = ch < nch ? src[ch] : make_uint4(0, 0, 0, 0);
+    const int64_t sblk = ((int64_t)sslot * d.num_kv_heads + g);
+    DemoteSrc src;
+    src.bf16 = d.kv_type == KV_BF16;
+    src.scale = 1.0f;
+    if (stier == 0) {
+        src.base = reinterpret_cast<const uint8_t *>(kv ? d.v_pool : d.k_pool) + sblk * n * 2;
+    } else if (stier == 1) {
+        src.base = reinterpret_cast<const uint8_t *>(kv ? d.i8_v : d.i8_k) + sblk * n;
+        src.scale = (kv ? d.i8_vs : d.i8_ks)[sblk];
+    } else if (stier == 2) {
+        src.base = (kv ? d.i4_v : d.i4_k) + sblk * (n / 2);
+        src.scale = (kv ? d.i4_vs : d.i4_ks)[sblk];
+    } else {
+        src.base = (kv ? d.f8_v : d.f8_k) + sblk * n;
+        src.scale = (kv ? d.f8_vs : d.f8_ks)[sblk];
     }
-#pragma unroll
-    for (int j = 0; j < R; ++j) amax = fmaxf(amax, absmax8(keep[j], bf16));
-    for (int64_t ch = lane + 64 * R; ch < nch; ch += 64) amax = fmaxf(amax, absmax8(src[ch], bf16));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const float scale = __fdiv_rn(amax, (float)qmax);
 
     const int64_t dst_base = ((int64_t)slot * d.num_kv_heads + g) * n;  // in elements
     int8_t *i8 = tier == 1   ? (kv ? d.i8_v : d.i8_k) + dst_base
                  : tier == 3 ? reinterpret_cast<int8_t *>(kv ? d.f8_v : d.f8_k) + dst_base
                              : nullptr;
     uint8_t *i4 = tier == 2 ? (kv ? d.i4_v : d.i4_k) + dst_base / 2 : nullptr;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const int64_t ch = lane + 64 * j;
-        if (ch < nch) encode8(keep[j], bf16, scale, qmax, (int)tier, i8, i4, ch);
-    }
-    for (int64_t ch = lane + 64 * R; ch < nch; ch += 64)
-        encode8(src[ch], bf16, scale, qmax, (int)tier, i8, i4, ch);
-    if (lane == 0) sc[(int64_t)slot * d.num_kv_heads + g] = scale;
+    float *sdst = sc + (int64_t)slot * d.num_kv_heads + g;
+    // one straight-line body per (source, destination) tier pair (the
+    // choice is wave-uniform)
+    dispatch_block<R>(stier, tier, src, n / 8, i8, i4, sdst, lane);
 }
 
 }  // namespace

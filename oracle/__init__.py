@@ -8,6 +8,7 @@ with the GPU path.
 from .oracle import (  # noqa: F401
     HostView,
     attend,
+    block_f32,
     build,
     dequant_f32,
     fp8_e4m3_encode,

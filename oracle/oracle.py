@@ -384,6 +384,25 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
     return K, V
 
 
+def block_f32(w, entry: int, g: int, kv: str, host=None) -> np.ndarray:
+    """The values of one stored (page, kv head) block of K (kv = "k") or V as
+    f32: a hot block (tier 0) widened exactly, a cold slot as f32(code *
+    scale), one rounding of the exact product (FP8: e4m3(code) * scale).
+    This is what a demotion reads when it moves a page down the cascade."""
+    host = host or HostView(w)
+    entry = int(entry) & 0xFFFFFFFF
+    tier, slot = entry >> TIER_SHIFT, entry & SLOT_MASK
+    if tier == 0:
+        (ka, kind), (va, _) = host.pools()
+        return widen_bits((ka if kv == "k" else va)[slot, g], kind).astype(np.float32)
+    ta = host.tier_arrays()
+    key = {1: "i8", 2: "i4", 3: "f8"}[tier]
+    codes = ta[f"{key}_{kv}"][slot, g]
+    vals = fp8_e4m3_value(codes) if key == "f8" else (
+        int4_codes(codes) if key == "i4" else codes).astype(np.float64)
+    return (vals * np.float64(ta[f"{key}_{kv}_scale"][slot, g])).astype(np.float32)
+
+
 def row_info(w):
     """For each query row: (sequence, visible key count)."""
     qs = w.query_start

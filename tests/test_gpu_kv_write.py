@@ -203,3 +203,64 @@ def test_demote_full_size_sampled(gpu):
                 assert got_scale[g].tobytes() == scale.tobytes(), (i, kv, g)
                 want = codes.astype(np.int8) if tier == 1 else oracle.pack_int4(codes)
                 assert np.array_equal(got_codes[g].view(np.uint8), want.view(np.uint8)), (i, kv, g)
+
+
+@pytest.mark.parametrize("hot_dtype", ["f16", "bf16"])
+def test_demote_cascade_transcodes_cold_slots(gpu, hot_dtype):
+    """The compression cascade: hot -> FP8 -> INT8 -> INT4, and hot -> INT8 ->
+    INT4, each step bit-exact against the oracle's encoder applied to the
+    oracle's f32 reading of the source block."""
+    w = _demote_case(gpu, hot_dtype, seed=13)
+    Hkv, P, D = w.num_kv_heads, w.page_tokens, w.head_dim
+    ent = w.page_table[2].view(np.uint32)
+    pages = [p for p in range(int(w.context_lens[2]) // P) if (int(ent[p]) >> 30) == 0][:2]
+    src0 = [int(ent[p]) for p in pages]
+    n8, n4 = w.tiers["i8_k"].shape[0], w.tiers["i4_k"].shape[0]
+    for key, extra in (("i8", 2), ("i4", 2)):
+        for kv in ("k", "v"):
+            t = w.tiers[f"{key}_{kv}"]
+            w.tiers[f"{key}_{kv}"] = torch.cat([t, torch.zeros((extra,) + t.shape[1:],
+                                                               dtype=t.dtype, device=gpu)])
+            sc = w.tiers[f"{key}_{kv}_scale"]
+            w.tiers[f"{key}_{kv}_scale"] = torch.cat([sc, torch.full((extra, Hkv), -1.0,
+                                                                     device=gpu)])
+    for kv in ("k", "v"):
+        w.tiers[f"f8_{kv}"] = torch.zeros((1, Hkv, P, D), dtype=torch.uint8, device=gpu)
+        w.tiers[f"f8_{kv}_scale"] = torch.full((1, Hkv), -1.0, device=gpu)
+    chains = [[src0[0], (3 << 30) | 0, (1 << 30) | n8, (2 << 30) | n4],
+              [src0[1], (1 << 30) | (n8 + 1), (2 << 30) | (n4 + 1)]]
+    qfun = {1: lambda x: oracle.quantize_block(x, 127), 2: lambda x: oracle.quantize_block(x, 7),
+            3: oracle.quantize_block_fp8}
+    for step in range(3):
+        jobs = [(c[step], c[step + 1]) for c in chains if step + 1 < len(c)]
+        prob = atlas.Problem(w)
+        src = torch.tensor(np.array([j[0] for j in jobs], np.uint32).view(np.int32), device=gpu)
+        dst = torch.tensor(np.array([j[1] for j in jobs], np.uint32).view(np.int32), device=gpu)
+        rejected = torch.zeros(1, dtype=torch.int32, device=gpu)
+        # expected from the source as it stands before the step
+        host = oracle.HostView(w)
+        want = {}
+        for s_e, d_e in jobs:
+            for kv in ("k", "v"):
+                for g in range(Hkv):
+                    x = oracle.block_f32(w, s_e, g, kv, host=host)
+                    want[(d_e, kv, g)] = qfun[d_e >> 30](x)
+        atlas.atlas_demote_pages(prob.args, prob.tiers, src, dst, rejected)
+        torch.cuda.synchronize()
+        assert int(rejected) == 0
+        ta = oracle.HostView(w).tier_arrays()
+        for (d_e, kv, g), (codes, scale) in want.items():
+            tier, slot = d_e >> 30, d_e & ((1 << 30) - 1)
+            key = {1: "i8", 2: "i4", 3: "f8"}[tier]
+            assert np.float32(ta[f"{key}_{kv}_scale"][slot, g]).tobytes() == scale.tobytes()
+            got = ta[f"{key}_{kv}"][slot, g]
+            exp = oracle.pack_int4(codes) if tier == 2 else codes.astype(
+                np.int8 if tier == 1 else np.uint8)
+            assert np.array_equal(got.view(np.uint8), exp.view(np.uint8)), (step, d_e, kv, g)
+    # point the pages at the ends of their chains and attend
+    new = ent.copy()
+    for p, c in zip(pages, chains):
+        new[p] = c[-1]
+    w.page_table[2] = new.view(np.int32)
+    out, lse = run(w)
+    check(w, out, lse)

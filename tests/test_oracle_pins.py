@@ -686,3 +686,27 @@ def test_tiered_reference_reads_fp8_pages():
             n = min(16, int(w.context_lens[s]) - 16 * p)
             want = oracle.fp8_e4m3_value(ta["f8_k"][slot, 1, :n]) * np.float64(ta["f8_k_scale"][slot, 1])
             np.testing.assert_array_equal(K[16 * p:16 * p + n], want)
+
+
+def test_block_f32_reads_each_tier():
+    w = synth.build(dict(num_seqs=1, context_lens=200, num_heads=4, num_kv_heads=2,
+                         head_dim=8, page_tokens=16, kv_dtype="bf16",
+                         tiers=dict(hot_tokens=40, p_int8=0.4, p_fp8=0.3)), seed=23)
+    ta = oracle.HostView(w).tier_arrays()
+    seen = set()
+    for e in w.page_table[0, :w.pages_of(0)].view(np.uint32):
+        tier, slot = int(e) >> 30, int(e) & ((1 << 30) - 1)
+        got = oracle.block_f32(w, e, 1, "v")
+        if tier == 0:
+            want = w.v_pool[slot, 1].float().numpy()
+        elif tier == 3:
+            want = (torch.from_numpy(ta["f8_v"][slot, 1]).view(torch.float8_e4m3fn).float()
+                    * float(ta["f8_v_scale"][slot, 1])).numpy()
+        else:
+            key = "i8" if tier == 1 else "i4"
+            c = ta[f"{key}_v"][slot, 1]
+            c = oracle.int4_codes(c) if key == "i4" else c
+            want = oracle.dequant_f32(c[None, None], ta[f"{key}_v_scale"][slot, 1:2][None])[0, 0]
+        np.testing.assert_array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
+        seen.add(tier)
+    assert seen == {0, 1, 2, 3}
