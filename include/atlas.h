@@ -55,6 +55,8 @@ typedef int32_t atlas_status;
 #define ATLAS_EUNSUPPORTED 2 /* valid but not implemented: head_dim, dtype, ... */
 #define ATLAS_EWORKSPACE 3   /* workspace missing or smaller than required */
 #define ATLAS_EDEVICE 4      /* the HIP runtime reported an error */
+#define ATLAS_ECAPACITY 5    /* residency runtime: a pool has no room for what the
+                                policy needs (nothing was changed) */
 
 /* Element types of q and of resident K/V pages. */
 #define ATLAS_F32 0

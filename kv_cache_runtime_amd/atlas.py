@@ -17,7 +17,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libatlas.so")
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EDEVICE = 0, 1, 2, 3, 4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EDEVICE, ECAPACITY = 0, 1, 2, 3, 4, 5
 F32, BF16, F16 = 0, 1, 2
 TIER_SHIFT = 30
 DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -102,9 +102,33 @@ EXPORTS = [
     "atlas_fold_partials", "atlas_gather_pages", "atlas_regenerate_pages",
     "atlas_dequant_pages", "atlas_validate_tables", "atlas_read_probe",
     "atlas_write_kv", "atlas_demote_pages",
+    "atlas_residency_create", "atlas_residency_destroy", "atlas_residency_add_seq",
+    "atlas_residency_remove_seq", "atlas_residency_append", "atlas_residency_plan",
+    "atlas_residency_tables", "atlas_residency_get_stats",
 ]
 
 _lib = None
+
+
+class ResidencyConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32 if n == "struct_size" else _i32) for n in (
+        "struct_size", "mode", "page_tokens", "max_seqs", "max_pages_per_seq", "hot_blocks",
+        "recent_tokens", "sink_tokens", "admit_per_plan", "fp8_pages", "int8_pages",
+        "num_fp8", "num_int8", "num_int4")]
+
+
+class ResidencyStats(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32)] + [(n, _i32) for n in (
+        "sequences", "hot_used", "fp8_used", "int8_used", "int4_used", "regenerated_pages",
+        "reserved")] + [(n, ctypes.c_int64) for n in (
+        "appended_tokens", "demotions", "transcodes", "admissions", "evictions",
+        "capacity_failures")]
+
+
+class ResidencyJobs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("capacity", _i32), ("n_demote", _i32),
+                ("n_admit", _i32), ("demote_src", _p), ("demote_dst", _p),
+                ("admit_page", _p), ("admit_block", _p)]
 
 
 class AtlasError(RuntimeError):
@@ -157,6 +181,21 @@ def load(path: str = LIB_PATH):
                                      _i32, _p]
     L.atlas_read_probe.restype = _i32
     L.atlas_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, _p]
+    L.atlas_residency_create.restype = _i32
+    L.atlas_residency_create.argtypes = [ctypes.POINTER(ResidencyConfig), ctypes.POINTER(_p)]
+    L.atlas_residency_destroy.restype = _i32
+    L.atlas_residency_destroy.argtypes = [_p]
+    for name in ("atlas_residency_add_seq", "atlas_residency_remove_seq"):
+        getattr(L, name).restype = _i32
+        getattr(L, name).argtypes = [_p, _i32]
+    L.atlas_residency_append.restype = _i32
+    L.atlas_residency_append.argtypes = [_p, _i32, _i32]
+    L.atlas_residency_plan.restype = _i32
+    L.atlas_residency_plan.argtypes = [_p, ctypes.POINTER(ResidencyJobs)]
+    L.atlas_residency_tables.restype = _i32
+    L.atlas_residency_tables.argtypes = [_p, _p, _i32, _p, _p, _p]
+    L.atlas_residency_get_stats.restype = _i32
+    L.atlas_residency_get_stats.argtypes = [_p, ctypes.POINTER(ResidencyStats)]
     if L.atlas_abi_version() != 2:
         raise RuntimeError("libatlas ABI version mismatch")
     _lib = L

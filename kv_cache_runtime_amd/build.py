@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libatlas.so")
 
 SOURCES = ["api.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "inspect.hip",
-           "kv_write.hip"]
+           "kv_write.hip", "residency.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -436,6 +436,16 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
 
 }  // namespace
 
+namespace atlas {
+// Error reporting for the library's other host sources (the same
+// thread-local message atlas_last_error returns).
+int32_t report_error(int32_t st, const char *msg) {
+    g_last_error = msg;
+    return st;
+}
+int32_t report_ok() { return ok(); }
+}  // namespace atlas
+
 extern "C" {
 
 uint32_t atlas_abi_version(void) { return ATLAS_ABI_VERSION; }
@@ -447,6 +457,7 @@ const char *atlas_status_string(atlas_status s) {
         case ATLAS_EUNSUPPORTED: return "unsupported configuration";
         case ATLAS_EWORKSPACE: return "workspace missing or too small";
         case ATLAS_EDEVICE: return "device error";
+        case ATLAS_ECAPACITY: return "pool capacity exceeded";
         default: return "unknown status";
     }
 }

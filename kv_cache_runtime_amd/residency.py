@@ -1,0 +1,99 @@
+"""ctypes binding of the host residency runtime (include/atlas_residency.h).
+
+Argument marshalling only: every decision is made by the runtime inside
+libatlas.so.  Host arrays are numpy int32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import atlas
+
+REGEN, TIERED = 0, 1
+
+
+def _arr(a: np.ndarray):
+    assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Residency:
+    """One runtime handle.  Fields of the config as keyword arguments."""
+
+    def __init__(self, *, mode, page_tokens, max_seqs, max_pages_per_seq, hot_blocks,
+                 recent_tokens=0, sink_tokens=0, admit_per_plan=0, fp8_pages=0, int8_pages=0,
+                 num_fp8=0, num_int8=0, num_int4=0, job_capacity=1 << 16):
+        L = atlas.load()
+        c = atlas.ResidencyConfig()
+        c.struct_size = ctypes.sizeof(c)
+        for k, v in dict(mode=mode, page_tokens=page_tokens, max_seqs=max_seqs,
+                         max_pages_per_seq=max_pages_per_seq, hot_blocks=hot_blocks,
+                         recent_tokens=recent_tokens, sink_tokens=sink_tokens,
+                         admit_per_plan=admit_per_plan, fp8_pages=fp8_pages,
+                         int8_pages=int8_pages, num_fp8=num_fp8, num_int8=num_int8,
+                         num_int4=num_int4).items():
+            setattr(c, k, int(v))
+        self.config = c
+        self._h = ctypes.c_void_p()
+        atlas._check(L.atlas_residency_create(ctypes.byref(c), ctypes.byref(self._h)),
+                     "atlas_residency_create")
+        self._L = L
+        self.max_pages = int(max_pages_per_seq)
+        self._cap = int(job_capacity)
+        self._bufs = [np.zeros(self._cap, dtype=np.int32) for _ in range(4)]
+
+    def close(self):
+        if self._h:
+            self._L.atlas_residency_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _call(self, name, *args):
+        st = getattr(self._L, name)(self._h, *args)
+        if st != atlas.OK:
+            raise atlas.AtlasError(st, name, self._L.atlas_last_error().decode())
+
+    def add_seq(self, seq: int):
+        self._call("atlas_residency_add_seq", int(seq))
+
+    def remove_seq(self, seq: int):
+        self._call("atlas_residency_remove_seq", int(seq))
+
+    def append(self, seq: int, n_tokens: int):
+        self._call("atlas_residency_append", int(seq), int(n_tokens))
+
+    def plan(self):
+        """Returns (demote_src, demote_dst, admit_page, admit_block) int32 arrays."""
+        j = atlas.ResidencyJobs()
+        j.struct_size = ctypes.sizeof(j)
+        j.capacity = self._cap
+        j.demote_src, j.demote_dst, j.admit_page, j.admit_block = (_arr(b) for b in self._bufs)
+        self._call("atlas_residency_plan", ctypes.byref(j))
+        nd, na = j.n_demote, j.n_admit
+        return (self._bufs[0][:nd].copy(), self._bufs[1][:nd].copy(),
+                self._bufs[2][:na].copy(), self._bufs[3][:na].copy())
+
+    def tables(self, seqs):
+        """Returns (page_table [n][max_pages], context_lens [n], regen_pages [n])."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = seqs.size
+        table = np.zeros((n, self.max_pages), dtype=np.int32)
+        ctx = np.zeros(n, dtype=np.int32)
+        regen = np.zeros(n, dtype=np.int32)
+        self._call("atlas_residency_tables", _arr(seqs), n, _arr(table), _arr(ctx), _arr(regen))
+        return table, ctx, regen
+
+    def stats(self) -> dict:
+        s = atlas.ResidencyStats()
+        s.struct_size = ctypes.sizeof(s)
+        self._call("atlas_residency_get_stats", ctypes.byref(s))
+        return {name: getattr(s, name) for name, _ in s._fields_ if name not in
+                ("struct_size", "reserved")}

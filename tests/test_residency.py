@@ -1,0 +1,201 @@
+"""CPU tests of the host residency runtime (include/atlas_residency.h): the
+CFR KeepRecent / hot-cache / admission policy and the ARGUS sink / window /
+cascade policy, through the C ABI.  No GPU: the runtime is host code."""
+
+import numpy as np
+import pytest
+
+from kv_cache_runtime_amd import atlas
+from kv_cache_runtime_amd.residency import REGEN, TIERED, Residency
+
+TIER = lambda e: (int(e) & 0xFFFFFFFF) >> 30  # noqa: E731
+SLOT = lambda e: int(e) & ((1 << 30) - 1)  # noqa: E731
+
+
+def _regen(**kw):
+    cfg = dict(mode=REGEN, page_tokens=16, max_seqs=4, max_pages_per_seq=64, hot_blocks=8,
+               recent_tokens=64)
+    cfg.update(kw)
+    return Residency(**cfg)
+
+
+def _tiered(**kw):
+    cfg = dict(mode=TIERED, page_tokens=16, max_seqs=4, max_pages_per_seq=64, hot_blocks=32,
+               recent_tokens=64, sink_tokens=16, fp8_pages=2, int8_pages=3, num_fp8=16,
+               num_int8=16, num_int4=64)
+    cfg.update(kw)
+    return Residency(**cfg)
+
+
+def test_config_is_checked():
+    for bad in (dict(mode=7), dict(page_tokens=0), dict(hot_blocks=-1), dict(recent_tokens=-1),
+                dict(max_seqs=0), dict(num_int4=-3)):
+        with pytest.raises(atlas.AtlasError) as e:
+            _tiered(**bad)
+        assert e.value.status == atlas.EINVAL
+
+
+def test_regen_keep_recent_and_long_prompt():
+    r = _regen()
+    r.add_seq(0)
+    r.append(0, 200)  # 13 pages; window = newest 64 tokens = pages 8..12
+    table, ctx, regen = r.tables([0])
+    assert ctx[0] == 200 and regen[0] == 8
+    blocks = table[0, 8:13]
+    assert len(set(blocks.tolist())) == 5 and blocks.max() < 8
+    assert (table[0, :8] == 8).all() and (table[0, 13:] == 8).all()  # no block there
+    assert r.stats()["hot_used"] == 5 and r.stats()["regenerated_pages"] == 8
+
+
+def test_regen_window_slides_and_lru_evicts_oldest_cached_page():
+    r = _regen()
+    r.add_seq(0)
+    r.append(0, 200)
+    r.append(0, 64)   # 17 pages, window 12..16: needs 4 blocks, 3 free -> one eviction
+    table, ctx, regen = r.tables([0])
+    assert regen[0] == 9 and r.stats()["evictions"] == 1 and r.stats()["hot_used"] == 8
+    assert len(set(table[0, 9:17].tolist())) == 8
+
+
+def test_regen_lru_picks_least_recently_used_sequence():
+    r = _regen(hot_blocks=12)
+    for s in (0, 1):
+        r.add_seq(s)
+        r.append(s, 64)          # 4 pages each, all in the window
+        r.append(s, 32)          # window moves: pages 0, 1 now cached outside it
+    r.tables([0])                # sequence 0 used last
+    r.add_seq(2)
+    r.append(2, 32)              # 2 pages: 12 blocks all in use -> evict 2
+    # the victims are sequence 1's cached pages (least recently used), oldest first
+    _, _, regen = r.tables([0, 1, 2])
+    assert regen.tolist() == [0, 2, 0] and r.stats()["evictions"] == 2
+    r.append(2, 64)              # 4 more pages: sequence 0 (now least recent) gives its 2
+    _, _, regen = r.tables([0, 1, 2])  # cached pages, then sequence 2 its own 2
+    assert regen.tolist() == [2, 2, 2] and r.stats()["evictions"] == 6
+    with pytest.raises(atlas.AtlasError):
+        r.append(2, 200)         # nothing evictable is left for this much
+
+
+def test_regen_capacity_failure_changes_nothing():
+    r = _regen(hot_blocks=4)
+    r.add_seq(0)
+    r.append(0, 64)
+    before = r.tables([0])
+    with pytest.raises(atlas.AtlasError) as e:
+        r.append(0, 8)           # 72 keys: the newest 64 span 5 pages, 4 blocks
+    assert e.value.status == atlas.ECAPACITY
+    after = r.tables([0])
+    assert all(np.array_equal(a, b) for a, b in zip(before, after))
+    assert r.stats()["capacity_failures"] == 1
+
+
+def test_regen_admission_fills_free_blocks_most_recent_first():
+    r = _regen(hot_blocks=16, admit_per_plan=3)
+    for s in (0, 1):
+        r.add_seq(s)
+        r.append(s, 160)         # 10 pages, 4 resident, 6 regenerated
+    r.tables([1])                # sequence 1 most recent
+    src, dst, pages, blocks = r.plan()
+    assert len(src) == 0 and pages.tolist() == [5, 4, 3]
+    _, _, regen = r.tables([0, 1])
+    assert regen.tolist() == [6, 3]
+    assert len(set(blocks.tolist())) == 3 and r.stats()["admissions"] == 3
+
+
+def _tiers(r, seq=0):
+    table, ctx, _ = r.tables([seq])
+    n = -(-int(ctx[0]) // 16)
+    return [TIER(e) for e in table[0, :n]], table[0, :n]
+
+
+def test_tiered_targets_by_position():
+    r = _tiered()
+    r.add_seq(0)
+    r.append(0, 400)             # 25 pages, window 21..24, sink page 0
+    src, dst, _, _ = r.plan()
+    tiers, _ = _tiers(r)
+    want = [0] + [2] * 15 + [1] * 3 + [3] * 2 + [0] * 4
+    assert tiers == want
+    assert all(TIER(e) == 0 for e in src) and len(src) == 20
+    assert len(set(dst.tolist())) == 20
+    st = r.stats()
+    assert st["hot_used"] == 5 and st["fp8_used"] == 2 and st["int8_used"] == 3
+    assert st["int4_used"] == 15 and st["demotions"] == 20
+
+
+def test_tiered_cascade_step_transcodes_and_never_reuses_within_a_plan():
+    # one slot of headroom per tier: a slot freed by a plan returns to its
+    # pool only after the plan
+    r = _tiered(num_fp8=3, num_int8=4)
+    r.add_seq(0)
+    r.append(0, 400)
+    r.plan()
+    r.append(0, 16)              # window 22..25: page 21 -> FP8, 19 -> INT8, 16 -> INT4
+    src, dst, _, _ = r.plan()
+    assert sorted((TIER(s), TIER(d)) for s, d in zip(src, dst)) == [(0, 3), (1, 2), (3, 1)]
+    # a slot freed by one job is not the destination of another in the same plan
+    assert not {(TIER(e), SLOT(e)) for e in src} & {(TIER(e), SLOT(e)) for e in dst}
+    tiers, _ = _tiers(r)
+    assert tiers == [0] + [2] * 16 + [1] * 3 + [3] * 2 + [0] * 4
+    assert r.stats()["transcodes"] == 2
+
+
+def test_tiered_full_pools_fall_through_then_fail_unchanged():
+    r = _tiered(num_fp8=1, num_int8=1, num_int4=64)
+    r.add_seq(0)
+    r.append(0, 400)
+    r.plan()
+    tiers, _ = _tiers(r)
+    assert tiers == [0] + [2] * 18 + [1] + [3] + [0] * 4   # FP8 and INT8 hold one page each
+    r2 = _tiered(num_fp8=0, num_int8=0, num_int4=3)
+    r2.add_seq(0)
+    r2.append(0, 400)
+    before = r2.tables([0])
+    with pytest.raises(atlas.AtlasError) as e:
+        r2.plan()
+    assert e.value.status == atlas.ECAPACITY
+    assert all(np.array_equal(a, b) for a, b in zip(before, r2.tables([0])))
+    assert r2.stats()["int4_used"] == 0
+
+
+def test_tiered_hot_pool_exhaustion_and_remove_frees_everything():
+    r = _tiered(hot_blocks=6)
+    r.add_seq(0)
+    with pytest.raises(atlas.AtlasError) as e:
+        r.append(0, 7 * 16)      # 7 pages before any plan
+    assert e.value.status == atlas.ECAPACITY
+    r.append(0, 6 * 16)          # window 2..5 and sink page 0 hot; page 1 -> FP8
+    r.plan()
+    r.add_seq(1)
+    r.append(1, 16)              # the block page 1 left
+    assert r.stats()["hot_used"] == 6 and r.stats()["fp8_used"] == 1
+    r.remove_seq(0)
+    st = r.stats()
+    assert st["sequences"] == 1 and st["hot_used"] == 1 and st["fp8_used"] == 0
+    with pytest.raises(atlas.AtlasError):
+        r.tables([0])
+
+
+def test_bad_calls_are_rejected():
+    r = _tiered()
+    with pytest.raises(atlas.AtlasError):
+        r.append(0, 5)           # not active
+    r.add_seq(0)
+    with pytest.raises(atlas.AtlasError):
+        r.add_seq(0)             # already active
+    with pytest.raises(atlas.AtlasError):
+        r.add_seq(9)             # out of range
+    with pytest.raises(atlas.AtlasError):
+        r.append(0, 64 * 16 + 1)  # past max_pages_per_seq
+
+
+def test_tiered_without_headroom_falls_through_to_colder_tiers():
+    # exactly full FP8 / INT8 pools: the slots freed by this plan's moves are
+    # not reused within it, so the moved pages go one tier colder
+    r = _tiered(num_fp8=2, num_int8=3)
+    r.add_seq(0)
+    r.append(0, 400)
+    r.plan()
+    r.append(0, 16)
+    src, dst, _, _ = r.plan()
+    assert sorted((TIER(s), TIER(d)) for s, d in zip(src, dst)) == [(0, 2), (1, 2), (3, 2)]
