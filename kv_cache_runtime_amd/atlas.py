@@ -259,11 +259,17 @@ def make_args(*, q, k_pool, v_pool, page_table, context_lens, num_heads, num_kv_
     a.stream = _stream(stream)
     a.alibi_slopes = _ptr(alibi_slopes)
     a.rope_theta = float(rope_theta)
+    # the struct holds raw pointers only: keep the tensors alive with it, so
+    # that a temporary passed here is not recycled before the call runs
+    a.tensors = [t for t in (q, k_pool, v_pool, page_table, context_lens, out, lse,
+                             query_start, workspace, alibi_slopes)
+                 if isinstance(t, torch.Tensor)]
     return a
 
 
 def make_regen(seed, layer, regen_pages, max_regen_pages) -> RegenSpec:
     r = RegenSpec()
+    r.tensors = [regen_pages] if isinstance(regen_pages, torch.Tensor) else []
     r.struct_size = ctypes.sizeof(RegenSpec)
     r.layer = int(layer)
     r.seed = int(seed) & (2**64 - 1)
@@ -274,6 +280,7 @@ def make_regen(seed, layer, regen_pages, max_regen_pages) -> RegenSpec:
 
 def make_tiers(t: dict) -> TierPools:
     p = TierPools()
+    p.tensors = [v for v in t.values() if isinstance(v, torch.Tensor)]
     p.struct_size = ctypes.sizeof(TierPools)
     p.num_int8 = int(t["i8_k"].shape[0])
     p.num_int4 = int(t["i4_k"].shape[0])

@@ -1,0 +1,205 @@
+"""End-to-end decode loops driven by the host residency runtime on the GPU:
+the runtime's tables feed atlas_write_kv and the attention calls, its jobs
+run through atlas_demote_pages / atlas_regenerate_pages, and the attention
+results are checked against the oracle over the pools as they stand."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from kv_cache_runtime_amd import atlas
+from kv_cache_runtime_amd.residency import REGEN, TIERED, Residency
+from tests.test_gpu_parity import check
+
+pytestmark = pytest.mark.gpu
+
+H, HKV, D, P = 8, 2, 128, 16
+
+
+def _args(dev, q, k_pool, v_pool, table, ctx, out, lse, qstart=None, max_q=1, ws=None,
+          kv=atlas.F16, qdt=atlas.BF16):
+    a = atlas.make_args(q=q, k_pool=k_pool, v_pool=v_pool, page_table=table, context_lens=ctx,
+                        num_heads=H, num_kv_heads=HKV, head_dim=D, page_tokens=P,
+                        max_context_len=int(ctx.max()), scale=float(np.float32(D ** -0.5)),
+                        out=out, lse=lse, query_start=qstart, max_query_len=max_q,
+                        total_q=q.shape[0], kv_dtype=kv, q_dtype=qdt)
+    return a
+
+
+def _attend(a, dev, tiers=None, regen=None):
+    n = atlas.atlas_workspace_size(a, regen)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    a.workspace = atlas._ptr(ws)
+    a.workspace_bytes = n
+    a.tensors.append(ws)
+    if tiers is not None:
+        atlas.atlas_paged_attention_tiered(a, tiers)
+    elif regen is not None:
+        atlas.atlas_paged_attention_regen(a, regen)
+    torch.cuda.synchronize()
+
+
+def test_tiered_decode_loop_through_the_runtime(gpu):
+    rt = Residency(mode=TIERED, page_tokens=P, max_seqs=3, max_pages_per_seq=64, hot_blocks=64,
+                   recent_tokens=64, sink_tokens=16, fp8_pages=2, int8_pages=3, num_fp8=16,
+                   num_int8=24, num_int4=160)
+    gen = torch.Generator(device=gpu).manual_seed(1)
+    hot_k = torch.zeros((64, HKV, P, D), dtype=torch.float16, device=gpu)
+    hot_v = torch.zeros_like(hot_k)
+    tiers = {}
+    for key, n, shape_d, dt in (("f8", 16, D, torch.uint8), ("i8", 24, D, torch.int8),
+                                ("i4", 160, D // 2, torch.uint8)):
+        for kv in ("k", "v"):
+            tiers[f"{key}_{kv}"] = torch.zeros((n, HKV, P, shape_d), dtype=dt, device=gpu)
+            tiers[f"{key}_{kv}_scale"] = torch.zeros((n, HKV), device=gpu)
+    pools = atlas.make_tiers(tiers)
+    seqs = [0, 1, 2]
+    prompt = [100, 37, 250]
+    for s in seqs:
+        rt.add_seq(s)
+
+    def write(n_new, qstart, max_q):
+        table, ctx, _ = rt.tables(seqs)
+        rows = int(sum(n_new))
+        k_new = torch.randn((rows, HKV, D), generator=gen, device=gpu).half()
+        v_new = torch.randn((rows, HKV, D), generator=gen, device=gpu).half()
+        q = torch.zeros((rows, H, D), dtype=torch.bfloat16, device=gpu)
+        out = torch.empty((rows, H, D), device=gpu)
+        lse = torch.empty((rows, H), device=gpu)
+        tt, ct = torch.from_numpy(table).to(gpu), torch.from_numpy(ctx).to(gpu)
+        qs = None if qstart is None else torch.from_numpy(qstart).to(gpu)
+        a = _args(gpu, q, hot_k, hot_v, tt, ct, out, lse, qstart=qs, max_q=max_q)
+        a.num_blocks = 64
+        atlas.atlas_write_kv(a, k_new, v_new)
+
+    def run_jobs():
+        src, dst, _, _ = rt.plan()
+        if len(src):
+            a = _args(gpu, torch.zeros((3, H, D), dtype=torch.bfloat16, device=gpu), hot_k, hot_v,
+                      torch.zeros((3, 64), dtype=torch.int32, device=gpu),
+                      torch.ones(3, dtype=torch.int32, device=gpu),
+                      torch.empty((3, H, D), device=gpu), torch.empty((3, H), device=gpu))
+            a.num_blocks = 64
+            rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+            atlas.atlas_demote_pages(a, pools, torch.from_numpy(src).to(gpu),
+                                     torch.from_numpy(dst).to(gpu), rej)
+            torch.cuda.synchronize()
+            assert int(rej) == 0
+        return len(src)
+
+    for s, n in zip(seqs, prompt):
+        rt.append(s, n)
+    qstart = np.concatenate([[0], np.cumsum(prompt)]).astype(np.int32)
+    write(prompt, qstart, max(prompt))
+    run_jobs()
+    checked = 0
+    for step in range(48):
+        for s in seqs:
+            rt.append(s, 1)
+        write([1, 1, 1], None, 1)
+        if step % 12 == 11:
+            table, ctx, _ = rt.tables(seqs)
+            q = torch.randn((3, H, D), generator=gen, device=gpu).bfloat16()
+            out = torch.empty((3, H, D), device=gpu)
+            lse = torch.empty((3, H), device=gpu)
+            a = _args(gpu, q, hot_k, hot_v, torch.from_numpy(table).to(gpu),
+                      torch.from_numpy(ctx).to(gpu), out, lse)
+            a.num_blocks = 64
+            _attend(a, gpu, tiers=pools)
+            counts = [64, tiers["i8_k"].shape[0], tiers["i4_k"].shape[0],
+                      tiers["f8_k"].shape[0]]
+            w = synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
+                            page_tokens=P, q_dtype="bf16", kv_dtype="f16", context_lens=ctx,
+                            query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
+                            q=q, k_pool=hot_k, v_pool=hot_v, page_table=table,
+                            tiers=dict(tiers, counts=counts), name=f"runtime-tiered-{step}")
+            check(w, out.cpu().numpy(), lse.cpu().numpy())
+            checked += 1
+        run_jobs()
+    st = rt.stats()
+    assert checked == 4 and st["demotions"] > 0 and st["transcodes"] > 0
+    assert st["fp8_used"] > 0 and st["int8_used"] > 0 and st["int4_used"] > 0
+
+
+def test_regen_decode_loop_through_the_runtime(gpu):
+    """KeepRecent + LRU hot cache + admission over regenerated pages: the
+    result equals the all-regenerated call bit for bit (CFR-Atlas core
+    contract) and the oracle within tolerance."""
+    seed, layer = 77, 2
+    rt = Residency(mode=REGEN, page_tokens=P, max_seqs=3, max_pages_per_seq=64, hot_blocks=20,
+                   recent_tokens=48, admit_per_plan=2)
+    hot_k = torch.zeros((20, HKV, P, D), dtype=torch.bfloat16, device=gpu)
+    hot_v = torch.zeros_like(hot_k)
+    seqs = [0, 1, 2]
+    prompt = [150, 40, 300]
+    gen = torch.Generator(device=gpu).manual_seed(2)
+    known = {s: set() for s in seqs}  # resident pages already regenerated into their block
+
+    def fill_new_pages():
+        # resident pages hold the generator's values: regenerate every page
+        # that got a block and has not been written yet
+        table, ctx, regen = rt.tables(seqs)
+        pages, blocks = [], []
+        for i, s in enumerate(seqs):
+            n = -(-int(ctx[i]) // P)
+            for p in range(int(regen[i]), n):
+                b = int(table[i, p])
+                if (p, b) not in known[s]:
+                    pages.append(p)
+                    blocks.append(b)
+                    known[s].add((p, b))
+        if pages:
+            atlas.atlas_regenerate_pages(seed, layer, HKV, D, P, atlas.BF16,
+                                         torch.tensor(pages, dtype=torch.int32, device=gpu),
+                                         torch.tensor(blocks, dtype=torch.int32, device=gpu),
+                                         20, hot_k, hot_v)
+
+    def forget_stale():
+        table, ctx, regen = rt.tables(seqs)
+        for i, s in enumerate(seqs):
+            n = -(-int(ctx[i]) // P)
+            live = {(p, int(table[i, p])) for p in range(int(regen[i]), n)}
+            known[s] &= live
+
+    for s, n in zip(seqs, prompt):
+        rt.add_seq(s)
+        rt.append(s, n)
+    fill_new_pages()
+    for step in range(40):
+        for s in seqs:
+            rt.append(s, 1)
+        forget_stale()
+        fill_new_pages()
+        if step % 10 == 9:
+            table, ctx, regen = rt.tables(seqs)
+            q = torch.randn((3, H, D), generator=gen, device=gpu).bfloat16()
+            outs = []
+            for rp in (regen, -(-ctx // P)):  # as planned, then everything regenerated
+                out = torch.empty((3, H, D), device=gpu)
+                lse = torch.empty((3, H), device=gpu)
+                a = _args(gpu, q, hot_k, hot_v, torch.from_numpy(table).to(gpu),
+                          torch.from_numpy(ctx).to(gpu), out, lse, kv=atlas.BF16)
+                a.num_blocks = 20
+                a.split_tokens = 256
+                rpt = torch.from_numpy(np.ascontiguousarray(rp, dtype=np.int32)).to(gpu)
+                spec = atlas.make_regen(seed, layer, rpt, int(rpt.max()))
+                _attend(a, gpu, regen=spec)
+                outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+            w = synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
+                            page_tokens=P, q_dtype="bf16", kv_dtype="bf16", context_lens=ctx,
+                            query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
+                            q=q, k_pool=hot_k, v_pool=hot_v, page_table=table,
+                            regen=dict(seed=seed, layer=layer, regen_pages=regen),
+                            name=f"runtime-regen-{step}")
+            check(w, *outs[1])  # everything regenerated
+            check(w, *outs[0])  # as the runtime planned
+            assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+            assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+        _, _, pages, blocks = rt.plan()
+        if len(pages):
+            atlas.atlas_regenerate_pages(seed, layer, HKV, D, P, atlas.BF16,
+                                         torch.from_numpy(pages).to(gpu),
+                                         torch.from_numpy(blocks).to(gpu), 20, hot_k, hot_v)
+    st = rt.stats()
+    assert st["evictions"] > 0 and st["admissions"] > 0 and st["regenerated_pages"] > 0
