@@ -41,10 +41,12 @@ def algorithmic_work(w):
     ctx = w.context_lens.astype(np.int64)
     kv_bytes = 0
     if w.tiers is not None:
-        per_tok = {0: 2 * D * elem, 1: 2 * D, 2: D, 3: 2 * D}  # K+V bytes per (token, kv head)
+        # K+V bytes per (token, kv head) by entry class: hot, int8, int4, FP8, INT2
+        per_tok = {0: 2 * D * elem, 1: 2 * D, 2: D, 3: 2 * D, 4: D // 2}
         for s in range(w.num_seqs):
             for p in range(w.pages_of(s)):
-                tier = (int(w.page_table[s, p]) & 0xFFFFFFFF) >> 30
+                e = int(w.page_table[s, p]) & 0xFFFFFFFF
+                tier = e >> 30 if e >> 30 < 3 else 3 + ((e >> 28) & 3)
                 ntok = min(P, int(ctx[s]) - p * P)
                 kv_bytes += ntok * Hkv * per_tok[tier]
                 if tier:

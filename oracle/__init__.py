@@ -11,11 +11,14 @@ from .oracle import (  # noqa: F401
     block_f32,
     build,
     dequant_f32,
+    entry_class,
     fp8_e4m3_encode,
     fp8_e4m3_value,
+    int2_codes,
     int4_codes,
     logical_kv,
     merge_splits,
+    pack_int2,
     pack_int4,
     quantize_block,
     quantize_block_fp8,

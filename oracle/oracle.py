@@ -16,9 +16,10 @@ Definitions followed:
   * paging: logical token j of sequence s lives in block table[s][j // P], row
     j % P (CFR-Atlas README, PageKey + token_range per page);
   * cold tiers: ARGUS "Visual Architecture" (FP8; INT8; INT4 2-way
-    bit-packed), symmetric: value = code * scale (FP8: E4M3 value of the code
-    times scale), one scale per (page, kv head) for K and one for V; int4
-    element 2i in the low nibble, two's complement;
+    bit-packed; INT2 4-way bit-packed), symmetric: value = code * scale (FP8:
+    E4M3 value of the code times scale), one scale per (page, kv head) for K
+    and one for V; int4 element 2i in the low nibble, int2 element 4i + j in
+    bits 2j of byte i, two's complement; INT2 and FP8 entries share tier 3;
   * regenerated pages: the value definition in attention.c;
   * split merge: log-sum-exp combination of normalised partial results
     (attnres AGENTS.md, "online softmax merge").
@@ -39,6 +40,20 @@ _lib = None
 
 TIER_SHIFT = 30
 SLOT_MASK = (1 << TIER_SHIFT) - 1
+# tier 3 is the extension tier: bits 29-28 give the kind, bits 27-0 the slot
+EXT_KIND_SHIFT = 28
+EXT_SLOT_MASK = (1 << EXT_KIND_SHIFT) - 1
+
+
+def entry_class(entry: int):
+    """(class, slot) of a tiered page-table entry: class 0 hot, 1 int8, 2 int4,
+    3 FP8 (tier 3, kind 0), 4 INT2 (tier 3, kind 1), 5 names no pool."""
+    e = int(entry) & 0xFFFFFFFF
+    tier = e >> TIER_SHIFT
+    if tier < 3:
+        return tier, e & SLOT_MASK
+    kind = (e >> EXT_KIND_SHIFT) & 3
+    return (3 + kind if kind < 2 else 5), e & EXT_SLOT_MASK
 
 
 def build(force: bool = False) -> str:
@@ -293,6 +308,24 @@ def quantize_block_fp8(x: np.ndarray):
     return fp8_e4m3_encode(np.divide(x, scale, dtype=np.float32)), scale
 
 
+def int2_codes(packed: np.ndarray) -> np.ndarray:
+    """INT2 (argus-cache "4-way Bit-Packed" as read here): element 4i + j is
+    bits 2j, 2j + 1 of byte i, two's complement (-2 .. 1)."""
+    p = np.asarray(packed).astype(np.int16)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 4,), dtype=np.int16)
+    for j in range(4):
+        f = (p >> (2 * j)) & 3
+        out[..., j::4] = np.where(f >= 2, f - 4, f)
+    return out
+
+
+def pack_int2(codes: np.ndarray) -> np.ndarray:
+    """Inverse of int2_codes: 4 codes per byte, element 4i + j in bits 2j, 2j+1."""
+    c = np.asarray(codes).astype(np.int16) & 3
+    return (c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)
+            ).astype(np.uint8)
+
+
 def pack_int4(codes: np.ndarray) -> np.ndarray:
     """Two's-complement nibbles, element 2i in the low nibble of byte i (the
     argus-cache INT4 "2-way bit-packed" layout as read here)."""
@@ -366,18 +399,20 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
             K[t0:t1] = widen_bits(ka[entry, g, :rows], kind)
             V[t0:t1] = widen_bits(va[entry, g, :rows], kind)
             continue
-        tier, slot = entry >> TIER_SHIFT, entry & SLOT_MASK
+        tier, slot = entry_class(entry)
         if tier == 0:
             (ka, kind), (va, _) = host.pools()
             K[t0:t1] = widen_bits(ka[slot, g, :rows], kind)
             V[t0:t1] = widen_bits(va[slot, g, :rows], kind)
             continue
         ta = host.tier_arrays()
-        key = {1: "i8", 2: "i4", 3: "f8"}[tier]
+        key = {1: "i8", 2: "i4", 3: "f8", 4: "i2"}[tier]
         for dst, kv in ((K, "k"), (V, "v")):
             codes = ta[f"{key}_{kv}"][slot, g, :rows]
             if key == "i4":
                 codes = int4_codes(codes)
+            elif key == "i2":
+                codes = int2_codes(codes)
             sc = np.float64(ta[f"{key}_{kv}_scale"][slot, g])
             vals = fp8_e4m3_value(codes) if key == "f8" else codes.astype(np.float64)
             dst[t0:t1] = vals * sc
@@ -390,16 +425,16 @@ def block_f32(w, entry: int, g: int, kv: str, host=None) -> np.ndarray:
     scale), one rounding of the exact product (FP8: e4m3(code) * scale).
     This is what a demotion reads when it moves a page down the cascade."""
     host = host or HostView(w)
-    entry = int(entry) & 0xFFFFFFFF
-    tier, slot = entry >> TIER_SHIFT, entry & SLOT_MASK
+    tier, slot = entry_class(entry)
     if tier == 0:
         (ka, kind), (va, _) = host.pools()
         return widen_bits((ka if kv == "k" else va)[slot, g], kind).astype(np.float32)
     ta = host.tier_arrays()
-    key = {1: "i8", 2: "i4", 3: "f8"}[tier]
+    key = {1: "i8", 2: "i4", 3: "f8", 4: "i2"}[tier]
     codes = ta[f"{key}_{kv}"][slot, g]
     vals = fp8_e4m3_value(codes) if key == "f8" else (
-        int4_codes(codes) if key == "i4" else codes).astype(np.float64)
+        int4_codes(codes) if key == "i4" else int2_codes(codes) if key == "i2" else codes
+    ).astype(np.float64)
     return (vals * np.float64(ta[f"{key}_{kv}_scale"][slot, g])).astype(np.float32)
 
 

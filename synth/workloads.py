@@ -35,7 +35,7 @@ import numpy as np
 import torch
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
-TIER_HOT, TIER_I8, TIER_I4, TIER_F8 = 0, 1, 2, 3
+TIER_HOT, TIER_I8, TIER_I4, TIER_F8, TIER_I2 = 0, 1, 2, 3, 4  # classes; INT2 is tier 3, kind 1
 TIER_SHIFT = 30
 SLOT_MASK = (1 << TIER_SHIFT) - 1
 
@@ -198,6 +198,13 @@ def _quantize_fp8(src: torch.Tensor):
     return codes, scale
 
 
+def _pack_int2(codes: torch.Tensor) -> torch.Tensor:
+    """Two's-complement 2-bit fields, element 4i + j in bits 2j, 2j + 1 of byte i."""
+    c = codes.to(torch.int16) & 0x3
+    return (c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)
+            ).to(torch.uint8)
+
+
 def _pack_int4(codes: torch.Tensor) -> torch.Tensor:
     """Two's-complement nibbles, element 2i in the low nibble of byte i."""
     c = codes.to(torch.int16) & 0xF
@@ -281,6 +288,7 @@ def build(spec: dict, device="cpu", seed: int = 42, name: str = "") -> Paged:
         hot_tokens = int(tiers_spec.get("hot_tokens", 1024))
         p_i8 = float(tiers_spec.get("p_int8", 0.5))
         p_f8 = float(tiers_spec.get("p_fp8", 0.0))
+        p_i2 = float(tiers_spec.get("p_int2", 0.0))
         tier_of = []
         for s in range(S):
             first_hot = max(0, int(ctx[s]) - hot_tokens) // P
@@ -289,23 +297,29 @@ def build(spec: dict, device="cpu", seed: int = 42, name: str = "") -> Paged:
             u = rng.random(int(n_pages[s]))
             coin = u < p_i8
             f8 = ~coin & (u < p_i8 + p_f8)
+            i2 = ~coin & ~f8 & (u < p_i8 + p_f8 + p_i2)
             t[cold & coin] = TIER_I8
             t[cold & f8] = TIER_F8
-            t[cold & ~coin & ~f8] = TIER_I4
+            t[cold & i2] = TIER_I2
+            t[cold & ~coin & ~f8 & ~i2] = TIER_I4
             tier_of.append(t)
-        counts = [sum(int((t == k).sum()) for t in tier_of) for k in range(4)]
+        counts = [sum(int((t == k).sum()) for t in tier_of) for k in range(5)]
         slots = [list(_place(None, counts[k], placement, rng)) for k in range(3)]
-        slots.append(list(_place(None, counts[TIER_F8], placement, rng)) if counts[TIER_F8] else [])
+        for k in (TIER_F8, TIER_I2):
+            slots.append(list(_place(None, counts[k], placement, rng)) if counts[k] else [])
         poison_hot = counts[TIER_HOT]
         # entries are 32-bit words (tier in the top two bits), kept in an
         # int32 array with the same bits
         table = np.full((S, max_pages), poison_hot, dtype=np.uint32)
-        used = [0, 0, 0, 0]
+        used = [0, 0, 0, 0, 0]
         for s in range(S):
             for p, t in enumerate(tier_of[s]):
                 slot = int(slots[t][used[t]])
                 used[t] += 1
-                table[s, p] = (int(t) << TIER_SHIFT) | slot
+                if t == TIER_I2:  # the extension tier, kind 1
+                    table[s, p] = (3 << TIER_SHIFT) | (1 << 28) | slot
+                else:
+                    table[s, p] = (int(t) << TIER_SHIFT) | slot
         table = table.view(np.int32)
         hot_shape = (counts[TIER_HOT] + 1, Hkv, P, D)
         k_pool = _normal(hot_shape, gen, device).to(DTYPES[kv_dtype])
@@ -332,6 +346,12 @@ def build(spec: dict, device="cpu", seed: int = 42, name: str = "") -> Paged:
                 codes, sc = _quantize_fp8(src)
                 tiers[f"f8_{kv}"] = codes.contiguous()
                 tiers[f"f8_{kv}_scale"] = sc.contiguous()
+        if counts[TIER_I2]:
+            for kv in ("k", "v"):
+                src = _normal((counts[TIER_I2], Hkv, P, D), gen, device)
+                codes, sc = _quantize(src, 1)
+                tiers[f"i2_{kv}"] = _pack_int2(codes).contiguous()
+                tiers[f"i2_{kv}_scale"] = sc.contiguous()
         tiers["counts"] = counts
 
     # Positional policy (inputs, not arithmetic): the geometric ALiBi slopes

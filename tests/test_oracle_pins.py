@@ -442,7 +442,7 @@ def test_cfr_bench_byte_accounting():
 # Cold-tier encoding (page demotion)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("qmax", [127, 7])
+@pytest.mark.parametrize("qmax", [127, 7, 1])
 def test_quantize_block_is_the_nearest_code(qmax):
     """Brute force: each code is the integer in [-qmax, qmax] nearest to
     x / scale (ties to even), found by exhaustive search."""
@@ -459,7 +459,7 @@ def test_quantize_block_is_the_nearest_code(qmax):
         assert ci == want
 
 
-@pytest.mark.parametrize("qmax", [127, 7])
+@pytest.mark.parametrize("qmax", [127, 7, 1])
 def test_quantize_block_extremes_symmetry_and_round_trip(qmax):
     rng = np.random.default_rng(3 + qmax)
     x = rng.standard_normal((16, 64)).astype(np.float32)
@@ -710,3 +710,48 @@ def test_block_f32_reads_each_tier():
         np.testing.assert_array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
         seen.add(tier)
     assert seen == {0, 1, 2, 3}
+
+
+
+# ---------------------------------------------------------------------------
+# 12. INT2 cold tier (tier 3, kind 1)
+# ---------------------------------------------------------------------------
+
+def test_int2_packing_by_hand_and_round_trip():
+    # byte 0b01_11_00_10: elements -2, 0, -1, 1 (element 4i + j in bits 2j)
+    assert oracle.int2_codes(np.array([0b01110010], np.uint8)).tolist() == [-2, 0, -1, 1]
+    allb = np.arange(256, dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.pack_int2(oracle.int2_codes(allb)), allb)
+    assert oracle.pack_int2(np.array([1, -1, 0, 1])).tolist() == [0b01001101]
+
+
+def test_entry_classes():
+    assert oracle.entry_class(5) == (0, 5)
+    assert oracle.entry_class((1 << 30) | 7) == (1, 7)
+    assert oracle.entry_class((2 << 30) | 9) == (2, 9)
+    assert oracle.entry_class((3 << 30) | 11) == (3, 11)
+    assert oracle.entry_class((3 << 30) | (1 << 28) | 13) == (4, 13)
+    assert oracle.entry_class((3 << 30) | (2 << 28) | 1)[0] == 5
+    assert oracle.entry_class(np.uint32((3 << 30) | (3 << 28)).view(np.int32))[0] == 5
+
+
+def test_tiered_reference_reads_int2_pages():
+    w = synth.build(dict(num_seqs=2, context_lens=[90, 130], num_heads=4, num_kv_heads=2,
+                         head_dim=8, page_tokens=16, kv_dtype="f16",
+                         tiers=dict(hot_tokens=16, p_int8=0.2, p_fp8=0.2, p_int2=0.4)), seed=29)
+    assert w.tiers["counts"][4] > 0
+    ta = oracle.HostView(w).tier_arrays()
+    seen = 0
+    for s in range(2):
+        K, V = oracle.logical_kv(w, s, 0)
+        for p in range(w.pages_of(s)):
+            cls, slot = oracle.entry_class(w.page_table[s, p])
+            if cls != 4:
+                continue
+            n = min(16, int(w.context_lens[s]) - 16 * p)
+            codes = oracle.int2_codes(ta["i2_v"][slot, 0, :n])
+            assert set(np.unique(codes)) <= {-1, 0, 1}
+            np.testing.assert_array_equal(V[16 * p:16 * p + n],
+                                          codes * np.float64(ta["i2_v_scale"][slot, 0]))
+            seen += 1
+    assert seen > 0
