@@ -119,7 +119,10 @@ def measured_traffic(workload: str):
         for line in f:
             if line.startswith("#") or "=" not in line:
                 continue
-            fields = dict(kv.split("=", 1) for kv in line.split())
+            tokens = line.split()
+            if not all("=" in t for t in tokens):
+                continue
+            fields = dict(t.split("=", 1) for t in tokens)
             if fields.get("workload") == workload and fields.get("sources") == digest:
                 return int(fields["bytes_per_launch"])
     return None
@@ -343,12 +346,12 @@ def write_path(args, torch, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.kv_dtype if args.op == "write_kv" else f"{w.kv_dtype}->int8+int4",
         "data": "synthetic",
-        "config": {"workload": f"{args.op} over {w.name}", "rows": w.total_q,
+        "config": {"workload": f"{args.op}:{w.name}", "rows": w.total_q,
                    "num_kv_heads": Hkv, "head_dim": D, "page_tokens": P,
                    "units": units, "bytes": alg_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(f"{args.op} over {w.name}"),
+                     "traffic": measured_traffic(f"{args.op}:{w.name}"),
                      "kernel": kernel, "kernel_avg_ms": round(kern_avg, 5),
                      "kernel_median_ms": round(kern[K // 2], 5),
                      "algorithmic_per_launch": alg_bytes},
@@ -382,6 +385,8 @@ def main():
     ap.add_argument("--p-fp8", type=float, default=0.0,
                     help="tiered workload (config 4): share of the cold pages stored as FP8 "
                          "E4M3, the rest split evenly between int8 and int4")
+    ap.add_argument("--p-int2", type=float, default=0.0,
+                    help="tiered workload (config 4): share of the cold pages stored as INT2")
     ap.add_argument("--op", choices=("attention", "write_kv", "demote"), default="attention",
                     help="attention (default): the attention call of --config; write_kv: "
                          "writing a chunk's new K/V into its pages; demote: encoding every "
@@ -410,10 +415,12 @@ def main():
     if args.rope_theta:
         positional["rope_theta"] = args.rope_theta
     extra = {"positional": positional} if positional else {}
-    if args.p_fp8 > 0:
+    if args.p_fp8 > 0 or args.p_int2 > 0:
         if args.config != 4:
-            sys.exit("--p-fp8 applies to the tiered workload (--config 4)")
-        extra["tiers"] = dict(hot_tokens=1024, p_int8=(1.0 - args.p_fp8) / 2, p_fp8=args.p_fp8)
+            sys.exit("--p-fp8 / --p-int2 apply to the tiered workload (--config 4)")
+        rest = 1.0 - args.p_fp8 - args.p_int2
+        extra["tiers"] = dict(hot_tokens=1024, p_int8=rest / 2, p_fp8=args.p_fp8,
+                              p_int2=args.p_int2)
     w = synth.config(args.config, device=dev, seed=42, **extra)
     prob = atlas.Problem(w, split_tokens=args.split_tokens)
     if w.regen is not None:
@@ -551,9 +558,10 @@ def main():
     }
     if positional:
         line["config"]["positional"] = positional
-    if args.p_fp8 > 0:
+    if args.p_fp8 > 0 or args.p_int2 > 0:
         line["config"]["cold_fp8_share"] = args.p_fp8
-        line["dtype"] = "f16+fp8+int8+int4"
+        line["config"]["cold_int2_share"] = args.p_int2
+        line["dtype"] = "f16+fp8+int8+int4+int2"
     if prefill:
         line["tflops"] = round(work["flops"] / t / 1e12, 3)
     print(json.dumps(line), flush=True)

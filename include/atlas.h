@@ -70,6 +70,12 @@ typedef int32_t atlas_status;
 #define ATLAS_TIER_INT8 1 /* int8 codes, one f32 scale per (page, kv head) */
 #define ATLAS_TIER_INT4 2 /* int4 codes, two per byte, same scale layout */
 #define ATLAS_TIER_FP8 3  /* FP8 E4M3 codes (OCP "e4m3fn"), same scale layout */
+/* Tier 3 is the extension tier: bits 29-28 of its entries give the kind and
+ * bits 27-0 the slot (so FP8 slots stay below 2^28).  Kinds 2 and 3 name no
+ * pool. */
+#define ATLAS_EXT_KIND_SHIFT 28
+#define ATLAS_EXT_FP8 0   /* (3 << 30) | (0 << 28) | slot: FP8 pool */
+#define ATLAS_EXT_INT2 1  /* (3 << 30) | (1 << 28) | slot: INT2 codes, four per byte */
 
 /*
  * One attention call (decode or chunked prefill).  CFR-Atlas README,
@@ -154,8 +160,10 @@ typedef struct atlas_attn_args {
  * scale per (page, kv head), separately for K and V.  int4 byte i of a row
  * holds element 2i in its low nibble and element 2i+1 in its high nibble,
  * two's complement.  FP8 codes are OCP E4M3 ("e4m3fn": bias 7, largest
- * finite 448, 0x7F / 0xFF NaN) and value = e4m3(code) * scale.  A pool with
- * zero slots may pass NULL pointers.
+ * finite 448, 0x7F / 0xFF NaN) and value = e4m3(code) * scale.  INT2 ("4-way
+ * Bit-Packed"): byte i of a row holds elements 4i .. 4i+3, element 4i+j in
+ * bits 2j, 2j+1, two's complement; codes -1, 0, 1 (scale = max|x| / 1).  A
+ * pool with zero slots may pass NULL pointers.
  */
 typedef struct atlas_tier_pools {
     uint32_t struct_size;       /* = sizeof(atlas_tier_pools) */
@@ -176,6 +184,12 @@ typedef struct atlas_tier_pools {
     const uint8_t *fp8_v;
     const float *fp8_k_scale;   /* [num_fp8][num_kv_heads] */
     const float *fp8_v_scale;
+    int32_t num_int2;           /* slots in the INT2 pool */
+    int32_t reserved3;          /* 0 */
+    const uint8_t *int2_k;      /* [num_int2][num_kv_heads][page_tokens][head_dim/4] */
+    const uint8_t *int2_v;
+    const float *int2_k_scale;  /* [num_int2][num_kv_heads] */
+    const float *int2_v_scale;
 } atlas_tier_pools;
 
 /*
@@ -246,7 +260,7 @@ atlas_status atlas_paged_attention(const atlas_attn_args *args);
 /*
  * Decode over tiered pages: page_table entries are (tier << 30) | slot.  Hot
  * pages come from args->k_pool / v_pool (kv_dtype F16 or BF16, num_blocks
- * slots); int8, int4 and FP8 pages from `pools`.  Decode only (query_start must
+ * slots); int8, int4, FP8 and INT2 pages from `pools`.  Decode only (query_start must
  * be NULL).  Codes are decoded in registers and the per-page scales are applied
  * to the dot products and to the probabilities, never written back.  With
  * F16 hot pages, head_dim 128 and 2, 4 or 8 query heads per kv head both
@@ -367,11 +381,11 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,
  * "Visual Architecture": the compression cascade FP16 -> FP8 -> INT8 ->
  * INT4).  For i < n, the source src_slots[i] is a tiered entry (tier << 30) |
  * slot: tier 0 is a hot block of args->k_pool / v_pool (kv_dtype F16 or BF16,
- * every row finite; a plain block id is such an entry), tiers 1-3 a cold slot
- * of `pools` whose values enter as f32(code * scale).  It is encoded into
- * dst_entries[i] = (tier << 30) | slot, tier 1 (int8), 2 (int4) or 3 (FP8) of
- * `pools`: for each kv head, K and V separately,
- *     scale = max|x| / qmax            (f32, correctly rounded; qmax 127 / 7 / 448)
+ * every row finite; a plain block id is such an entry), any other entry a
+ * cold slot of `pools` whose values enter as f32(code * scale).  It is
+ * encoded into dst_entries[i], an int8, int4, FP8 or INT2 entry of `pools`:
+ * for each kv head, K and V separately,
+ *     scale = max|x| / qmax    (f32, correctly rounded; qmax 127 / 7 / 448 / 1)
  *     code  = clamp(rint(x / scale), -qmax, qmax)   (round half to even)
  *     FP8:  code = the E4M3 code nearest to x / scale (ties to the even
  *           code; x / scale is correctly rounded f32)

@@ -82,6 +82,12 @@ class TierPools(ctypes.Structure):
         ("fp8_v", _p),
         ("fp8_k_scale", _p),
         ("fp8_v_scale", _p),
+        ("num_int2", _i32),
+        ("reserved3", _i32),
+        ("int2_k", _p),
+        ("int2_v", _p),
+        ("int2_k_scale", _p),
+        ("int2_v_scale", _p),
     ]
 
 
@@ -292,6 +298,10 @@ def make_tiers(t: dict) -> TierPools:
         p.num_fp8 = int(t["f8_k"].shape[0])
         p.fp8_k, p.fp8_v = _ptr(t["f8_k"]), _ptr(t["f8_v"])
         p.fp8_k_scale, p.fp8_v_scale = _ptr(t["f8_k_scale"]), _ptr(t["f8_v_scale"])
+    if "i2_k" in t:
+        p.num_int2 = int(t["i2_k"].shape[0])
+        p.int2_k, p.int2_v = _ptr(t["i2_k"]), _ptr(t["i2_v"])
+        p.int2_k_scale, p.int2_v_scale = _ptr(t["i2_k_scale"]), _ptr(t["i2_v_scale"])
     return p
 
 

@@ -232,15 +232,20 @@ atlas_status check_pools(const atlas_tier_pools *t) {
     if (t->struct_size != sizeof(atlas_tier_pools))
         return fail(ATLAS_EINVAL, "pools->struct_size %u != %zu", t->struct_size,
                     sizeof(atlas_tier_pools));
-    if (t->num_int8 < 0 || t->num_int4 < 0 || t->num_fp8 < 0)
+    if (t->num_int8 < 0 || t->num_int4 < 0 || t->num_fp8 < 0 || t->num_int2 < 0)
         return fail(ATLAS_EINVAL, "negative tier pool size");
-    if (t->reserved != 0 || t->reserved2 != 0) return fail(ATLAS_EINVAL, "reserved field must be 0");
+    if (t->num_fp8 > (1 << 28) || t->num_int2 > (1 << 28))
+        return fail(ATLAS_EINVAL, "FP8 / INT2 pools hold at most 2^28 slots");
+    if (t->reserved != 0 || t->reserved2 != 0 || t->reserved3 != 0)
+        return fail(ATLAS_EINVAL, "reserved field must be 0");
     if (t->num_int8 > 0 && (!t->int8_k || !t->int8_v || !t->int8_k_scale || !t->int8_v_scale))
         return fail(ATLAS_EINVAL, "NULL int8 pool pointer");
     if (t->num_int4 > 0 && (!t->int4_k || !t->int4_v || !t->int4_k_scale || !t->int4_v_scale))
         return fail(ATLAS_EINVAL, "NULL int4 pool pointer");
     if (t->num_fp8 > 0 && (!t->fp8_k || !t->fp8_v || !t->fp8_k_scale || !t->fp8_v_scale))
         return fail(ATLAS_EINVAL, "NULL fp8 pool pointer");
+    if (t->num_int2 > 0 && (!t->int2_k || !t->int2_v || !t->int2_k_scale || !t->int2_v_scale))
+        return fail(ATLAS_EINVAL, "NULL int2 pool pointer");
     return ok();
 }
 
@@ -258,9 +263,14 @@ void set_pools(P &p, const atlas_tier_pools *t) {
     p.f8_v = t->fp8_v;
     p.f8_ks = t->fp8_k_scale;
     p.f8_vs = t->fp8_v_scale;
+    p.i2_k = t->int2_k;
+    p.i2_v = t->int2_v;
+    p.i2_ks = t->int2_k_scale;
+    p.i2_vs = t->int2_v_scale;
     p.n_i8 = t->num_int8;
     p.n_i4 = t->num_int4;
     p.n_f8 = t->num_fp8;
+    p.n_i2 = t->num_int2;
 }
 
 RowMap row_map(const atlas_attn_args *a) {
@@ -627,7 +637,8 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args, const atlas_tier
     if (!report_dev) return fail(ATLAS_EINVAL, "report_dev is NULL");
     if (pools && pools->struct_size != sizeof(atlas_tier_pools))
         return fail(ATLAS_EINVAL, "pools->struct_size mismatch");
-    if (pools && (pools->num_int8 < 0 || pools->num_int4 < 0 || pools->num_fp8 < 0))
+    if (pools && (pools->num_int8 < 0 || pools->num_int4 < 0 || pools->num_fp8 < 0 ||
+                  pools->num_int2 < 0))
         return fail(ATLAS_EINVAL, "negative tier pool size");
     ValidateParams v;
     std::memset(&v, 0, sizeof(v));
@@ -647,9 +658,13 @@ atlas_status atlas_validate_tables(const atlas_attn_args *args, const atlas_tier
         v.p.f8_ks = pools->fp8_k_scale;
         v.p.f8_vs = pools->fp8_v_scale;
         v.p.n_f8 = pools->num_fp8;
+        v.p.i2_ks = pools->int2_k_scale;
+        v.p.i2_vs = pools->int2_v_scale;
+        v.p.n_i2 = pools->num_int2;
         if (check_values && ((v.p.n_i8 > 0 && (!v.p.i8_ks || !v.p.i8_vs)) ||
                              (v.p.n_i4 > 0 && (!v.p.i4_ks || !v.p.i4_vs)) ||
-                             (v.p.n_f8 > 0 && (!v.p.f8_ks || !v.p.f8_vs))))
+                             (v.p.n_f8 > 0 && (!v.p.f8_ks || !v.p.f8_vs)) ||
+                             (v.p.n_i2 > 0 && (!v.p.i2_ks || !v.p.i2_vs))))
             return fail(ATLAS_EINVAL, "NULL tier scale pointer");
     }
     if (regen) {
@@ -751,9 +766,14 @@ atlas_status atlas_demote_pages(const atlas_attn_args *args, const atlas_tier_po
     d.f8_v = const_cast<uint8_t *>(pools->fp8_v);
     d.f8_ks = const_cast<float *>(pools->fp8_k_scale);
     d.f8_vs = const_cast<float *>(pools->fp8_v_scale);
+    d.i2_k = const_cast<uint8_t *>(pools->int2_k);
+    d.i2_v = const_cast<uint8_t *>(pools->int2_v);
+    d.i2_ks = const_cast<float *>(pools->int2_k_scale);
+    d.i2_vs = const_cast<float *>(pools->int2_v_scale);
     d.n_i8 = pools->num_int8;
     d.n_i4 = pools->num_int4;
     d.n_f8 = pools->num_fp8;
+    d.n_i2 = pools->num_int2;
     d.rejected = rejected;
     return device_status(launch_demote(d, reinterpret_cast<hipStream_t>(args->stream)),
                          "demote launch");

@@ -25,8 +25,8 @@
 // by zero, so NaN poison in page tails cannot leak.
 //
 // Tiered mode (ARGUS "Visual Architecture", "Why It Works"): a page's tier
-// comes from its page-table entry; int8 / int4 / FP8 codes are widened in
-// registers, the K scale multiplies the finished dot product and the V scale
+// comes from its page-table entry; int8 / int4 / FP8 / INT2 codes are
+// widened in registers, the K scale multiplies the finished dot product and the V scale
 // multiplies the probability, so no dequantised page is ever written.
 // Regen mode (CFR-Atlas README, overview and KvRegenerator): leading pages are
 // regenerated inside the kernel from the counter-based SplitMix64 definition,
@@ -88,10 +88,7 @@ __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry,
     }
 
     uint32_t tier = 0, slot = entry;
-    if constexpr (MODE == MODE_TIERED) {
-        tier = entry >> 30;
-        slot = entry & ((1u << 30) - 1u);
-    }
+    if constexpr (MODE == MODE_TIERED) tier = (uint32_t)entry_class(entry, slot);
 
     if (tier == 0) {
         if (slot >= (uint32_t)p.num_blocks) return false;
@@ -169,7 +166,31 @@ __device__ __forceinline__ bool load_slot(const DecodeParams &p, uint32_t entry,
             }
             return true;
         }
-        if (tier == 3) {  // FP8 E4M3 codes, widened by the hardware conversion
+        if (tier == CLS_I2) {  // INT2 codes, four per byte
+            if (slot >= (uint32_t)p.n_i2) return false;
+            constexpr int NB = E / 4;
+            const int64_t row0 = ((int64_t)slot * p.num_kv_heads + g) * P + off;
+            const uint8_t *kb = p.i2_k + row0 * (D / 4) + c * NB;
+            const uint8_t *vb = p.i2_v + row0 * (D / 4) + c * NB;
+            uint32_t kw[U][1], vw[U][1];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                load_words<NB>(kw[u], kb + (int64_t)u * (D / 4));
+                load_words<NB>(vw[u], vb + (int64_t)u * (D / 4));
+            }
+            sd.kscale = p.i2_ks[(int64_t)slot * p.num_kv_heads + g];
+            sd.vscale = p.i2_vs[(int64_t)slot * p.num_kv_heads + g];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {  // element e: bits 2e, 2e + 1
+                    kf[u][e] = (float)sext_field(kw[u][0], 30 - 2 * e, 2);
+                    vf[u][e] = (float)sext_field(vw[u][0], 30 - 2 * e, 2);
+                }
+            }
+            return true;
+        }
+        if (tier == CLS_F8) {  // FP8 E4M3 codes, widened by the hardware conversion
             if (slot >= (uint32_t)p.n_f8) return false;
             const int64_t row0 = ((int64_t)slot * p.num_kv_heads + g) * P + off;
             const uint8_t *kb = p.f8_k + row0 * D + c * E;

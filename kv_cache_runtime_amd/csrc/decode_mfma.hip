@@ -105,10 +105,27 @@ __device__ __forceinline__ void f8x4_to_f16x4(uint32_t w, uint32_t &lo, uint32_t
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
-// Tile kinds.  kByte covers both one-byte code tiers (int8 and FP8): same
-// layout and load path, the pool and the widening chosen per run (f8).
-constexpr int kHot = 0, kByte = 1, kInt4 = 2;
-// 16-byte chunks per lane of one 16-token group, for K and for V
+// INT2 codes (16 per word, element j in bits 2j, 2j + 1, two's complement)
+// -> f16 pairs (2m, 2m + 1), exact: bias each field to unsigned (f + 2),
+// place it under the f16 1024 and subtract 1026.
+__device__ __forceinline__ void i2x16_to_f16x16(uint32_t w, uint32_t (&out)[8]) {
+    const uint32_t u = w ^ 0xAAAAAAAAu;
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 bias = {(_Float16)1026.0f, (_Float16)1026.0f};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const uint32_t b = 0x64006400u | ((u >> (4 * m)) & 3u) | (((u >> (4 * m + 2)) & 3u) << 16);
+        out[m] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - bias);
+    }
+}
+
+// Tile kinds.  kByte covers the one-byte code tiers (int8, FP8 when alt) and
+// kSub the sub-byte ones (int4, INT2 when alt): same layout within a kind;
+// alt is a compile-time constant of each run, so every class gets its own
+// straight-line body.
+constexpr int kHot = 0, kByte = 1, kSub = 2;
+// 16-byte chunks per lane of one 16-token group, for K and for V (INT2 uses
+// the low half of its one chunk)
 template <int TIER>
 constexpr int chunks() { return TIER == kHot ? 4 : TIER == kByte ? 2 : 1; }
 
@@ -120,7 +137,7 @@ constexpr int chunks() { return TIER == kHot ? 4 : TIER == kByte ? 2 : 1; }
 template <int KV, int MODE, int TIER>
 __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slot, int g, int row,
                                              int r, uint4 (&kr)[chunks<TIER>()], float &kscale,
-                                             bool f8) {
+                                             bool alt) {
     kscale = 1.0f;
     const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row;
     if constexpr (TIER == kHot) {
@@ -132,12 +149,17 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slo
             kr[ks] = *reinterpret_cast<const uint4 *>(src + d0);
         }
     } else if constexpr (TIER == kByte) {
-        if (slot >= (uint32_t)(f8 ? p.n_f8 : p.n_i8)) return false;
-        const uint8_t *pool = f8 ? p.f8_k : reinterpret_cast<const uint8_t *>(p.i8_k);
+        if (slot >= (uint32_t)(alt ? p.n_f8 : p.n_i8)) return false;
+        const uint8_t *pool = alt ? p.f8_k : reinterpret_cast<const uint8_t *>(p.i8_k);
         const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD + 32 * r);
-        kscale = (f8 ? p.f8_ks : p.i8_ks)[(int64_t)slot * p.num_kv_heads + g];
+        kscale = (alt ? p.f8_ks : p.i8_ks)[(int64_t)slot * p.num_kv_heads + g];
         kr[0] = src[0];
         kr[1] = src[1];
+    } else if (alt) {  // INT2: dims 32 r .. 32 r + 31 are 8 bytes
+        if (slot >= (uint32_t)p.n_i2) return false;
+        const uint2 v = *reinterpret_cast<const uint2 *>(p.i2_k + r0 * (kD / 4) + 8 * r);
+        kr[0] = make_uint4(v.x, v.y, 0u, 0u);
+        kscale = p.i2_ks[(int64_t)slot * p.num_kv_heads + g];
     } else {
         if (slot >= (uint32_t)p.n_i4) return false;
         kr[0] = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + 16 * r);
@@ -149,13 +171,13 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slo
 // Raw K -> the four 16-bit operands (codes widened to f16, exact).
 template <int TIER>
 __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4 (&kb)[4],
-                                       bool f8) {
+                                       bool alt) {
     if constexpr (TIER == kHot) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[ks] = kr[ks];
     } else if constexpr (TIER == kByte) {
         const uint32_t w[8] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w, kr[1].x, kr[1].y, kr[1].z, kr[1].w};
-        if (f8) {  // run-uniform
+        if (alt) {  // FP8, run-uniform
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 uint32_t a, b, c, d;
@@ -171,6 +193,14 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
                 i8x4_to_f16x4(w[2 * ks + 1], c, d);
                 kb[ks] = make_uint4(a, b, c, d);
             }
+        }
+    } else if (alt) {  // INT2, run-uniform: 16 codes per word, two operands
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t o[8];
+            i2x16_to_f16x16(h ? kr[0].y : kr[0].x, o);
+            kb[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
+            kb[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
         }
     } else {
         const uint32_t w[4] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w};
@@ -189,7 +219,7 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
 template <int KV, int TIER>
 __device__ __forceinline__ bool load_v_group(const DecodeParams &p, uint32_t slot, int g, int row0,
                                              int lane, uint4 (&vr)[chunks<TIER>()],
-                                             float &vscale, bool f8) {
+                                             float &vscale, bool alt) {
     vscale = 1.0f;
     const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row0;
     if constexpr (TIER == kHot) {
@@ -199,12 +229,17 @@ __device__ __forceinline__ bool load_v_group(const DecodeParams &p, uint32_t slo
 #pragma unroll
         for (int i = 0; i < 4; ++i) vr[i] = src[64 * i + lane];
     } else if constexpr (TIER == kByte) {
-        if (slot >= (uint32_t)(f8 ? p.n_f8 : p.n_i8)) return false;
-        const uint8_t *pool = f8 ? p.f8_v : reinterpret_cast<const uint8_t *>(p.i8_v);
+        if (slot >= (uint32_t)(alt ? p.n_f8 : p.n_i8)) return false;
+        const uint8_t *pool = alt ? p.f8_v : reinterpret_cast<const uint8_t *>(p.i8_v);
         const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD);
-        vscale = (f8 ? p.f8_vs : p.i8_vs)[(int64_t)slot * p.num_kv_heads + g];
+        vscale = (alt ? p.f8_vs : p.i8_vs)[(int64_t)slot * p.num_kv_heads + g];
         vr[0] = src[lane];
         vr[1] = src[64 + lane];
+    } else if (alt) {  // INT2: 8 bytes per lane
+        if (slot >= (uint32_t)p.n_i2) return false;
+        const uint2 v = reinterpret_cast<const uint2 *>(p.i2_v + r0 * (kD / 4))[lane];
+        vscale = p.i2_vs[(int64_t)slot * p.num_kv_heads + g];
+        vr[0] = make_uint4(v.x, v.y, 0u, 0u);
     } else {
         if (slot >= (uint32_t)p.n_i4) return false;
         const uint4 *src = reinterpret_cast<const uint4 *>(p.i4_v + r0 * (kD / 2));
@@ -229,7 +264,7 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint32_t a, uint32_t b, uint32
 template <int TIER, typename TokOk>
 __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
                                               const uint4 (&vr)[chunks<TIER>()], int lane,
-                                              TokOk tok_ok, bool f8) {
+                                              TokOk tok_ok, bool alt) {
     if constexpr (TIER == kHot) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {  // chunk 64 i + lane: token 4 i + lane / 16
@@ -244,7 +279,7 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
             const bool ok = tok_ok(tok);
             const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
             uint32_t h[8];
-            if (f8) {  // run-uniform
+            if (alt) {  // FP8, run-uniform
 #pragma unroll
                 for (int j = 0; j < 4; ++j) f8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
             } else {
@@ -258,13 +293,23 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
     } else {
         const int tok = lane >> 2;  // chunk lane: token lane / 4, dims 32 (lane % 4) ..
         const bool ok = tok_ok(tok);
-        const uint32_t w[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
         uint16_t *dst = vt + (base + tok) * kVPitch + 32 * (lane & 3);
+        if (alt) {  // INT2, run-uniform
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t o[4];
-            i4x8_to_f16x8(w[j], o);
-            *reinterpret_cast<uint4 *>(dst + 8 * j) = keep_if(ok, o[0], o[1], o[2], o[3]);
+            for (int h = 0; h < 2; ++h) {
+                uint32_t o[8];
+                i2x16_to_f16x16(h ? vr[0].y : vr[0].x, o);
+                *reinterpret_cast<uint4 *>(dst + 16 * h) = keep_if(ok, o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4 *>(dst + 16 * h + 8) = keep_if(ok, o[4], o[5], o[6], o[7]);
+            }
+        } else {
+            const uint32_t w[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t o[4];
+                i4x8_to_f16x8(w[j], o);
+                *reinterpret_cast<uint4 *>(dst + 8 * j) = keep_if(ok, o[0], o[1], o[2], o[3]);
+            }
         }
     }
 }
@@ -339,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     const int lp_first = t0 / P;
     const int lp_count = t1 > t0 ? (t1 - 1) / P - lp_first + 1 : 0;
     const bool staged = lp_count <= kStagedPages;
-    int tier_count[4] = {0, 0, 0, 0};
+    int tier_count[kClasses] = {0, 0, 0, 0, 0, 0};
     if constexpr (MODE == MODE_TIERED) {
         stage_pages_by_tier(trow + lp_first, min(lp_count, kStagedPages), s_pages, s_lp,
                             tier_count);
@@ -419,8 +464,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     // Walks the tiles of one run of pages with one tier: the whole split in
     // token order (natural), or the sp .. sp + np - 1 staged entries of a
     // tier.  Each wave takes every fourth tile of the run.
-    auto run = [&](auto tier_c, auto natural_c, int sp, int np, bool f8) {
+    auto run = [&](auto tier_c, auto alt_c, auto natural_c, int sp, int np) {
         constexpr int TIER = decltype(tier_c)::value;
+        constexpr bool alt = decltype(alt_c)::value != 0;  // FP8 / INT2 of a code width
         constexpr bool natural = decltype(natural_c)::value != 0;
         constexpr int NC = chunks<TIER>();
         const int n_pos = natural ? t1 - t0 : np * P;
@@ -458,7 +504,6 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                     tok = lp * P + row0;
                     ent = live ? (uint32_t)s_pages[sp + pi] : 0u;
                 }
-                if constexpr (MODE == MODE_TIERED) ent &= (1u << 30) - 1u;
                 G_.tok[tg] = __builtin_amdgcn_readfirstlane(tok);
                 G_.row[tg] = __builtin_amdgcn_readfirstlane(row0);
                 G_.slot[tg] = __builtin_amdgcn_readfirstlane(ent);
@@ -472,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             kok[tg] = G_.live[tg];
             kscale[tg] = 1.0f;
             if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.row[tg] + c, r,
-                                                         kr[tg], kscale[tg], f8)) {
+                                                         kr[tg], kscale[tg], alt)) {
                 bad = true;
                 kok[tg] = false;
             }
@@ -485,7 +530,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             vok[tg] = G_.live[tg];
             vscale[tg] = 1.0f;
             if (vok[tg] && !load_v_group<KV, TIER>(p, G_.slot[tg], g, G_.row[tg], lane,
-                                                   vr[tg], vscale[tg], f8)) {
+                                                   vr[tg], vscale[tg], alt)) {
                 bad = true;
                 vok[tg] = false;
             }
@@ -513,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             for (int tg = 0; tg < 4; ++tg) {
                 kvalid[tg] = kok[tg] && in_range(cur.tok[tg] + c);
                 uint4 kb[4];
-                widen_k<TIER>(kr[tg], kb, f8);
+                widen_k<TIER>(kr[tg], kb, alt);
                 sc[tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) sc[tg] = mfma16<QT>(qf[ks], kb[ks], sc[tg]);
@@ -656,10 +701,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                     const bool live = vok[tg];
                     const int tb = cur.tok[tg];
                     if (live && tb >= t0 && tb + 16 <= t1)  // whole group visible (uniform)
-                        store_v_group<TIER>(vt, 16 * j, vr[tg], lane, [](int) { return true; }, f8);
+                        store_v_group<TIER>(vt, 16 * j, vr[tg], lane, [](int) { return true; }, alt);
                     else
                         store_v_group<TIER>(vt, 16 * j, vr[tg], lane,
-                                            [&](int tok) { return live && in_range(tb + tok); }, f8);
+                                            [&](int tok) { return live && in_range(tb + tok); }, alt);
                     load_v(nxt, tg);  // this group's registers are free again
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -699,20 +744,19 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     };
 
     if constexpr (MODE == MODE_TIERED) {
-        // runs of hot, int4, int8 and FP8 pages; the two one-byte tiers share
-        // one body (a loop the compiler keeps rolled), so the kernel carries
-        // three run bodies rather than four
-        run(TierC<kHot>{}, TierC<0>{}, 0, tier_count[0], false);
-        run(TierC<kInt4>{}, TierC<0>{}, tier_count[0] + tier_count[1], tier_count[2], false);
-#pragma clang loop unroll(disable)
-        for (int pass = 0; pass < 2; ++pass) {
-            const bool f8 = pass == 1;
-            const int sp = f8 ? tier_count[0] + tier_count[1] + tier_count[2] : tier_count[0];
-            run(TierC<kByte>{}, TierC<0>{}, sp, f8 ? tier_count[3] : tier_count[1], f8);
-        }
-        if (!staged) bad = true;
+        // one straight-line run body per class: hot, int8, int4, FP8, INT2
+        // (a run-time choice between two classes inside one body costs more
+        // than the larger code)
+        const int c01 = tier_count[0] + tier_count[1];
+        const int c012 = c01 + tier_count[2];
+        run(TierC<kHot>{}, TierC<0>{}, TierC<0>{}, 0, tier_count[0]);
+        run(TierC<kByte>{}, TierC<0>{}, TierC<0>{}, tier_count[0], tier_count[1]);
+        run(TierC<kSub>{}, TierC<0>{}, TierC<0>{}, c01, tier_count[2]);
+        run(TierC<kByte>{}, TierC<1>{}, TierC<0>{}, c012, tier_count[3]);
+        run(TierC<kSub>{}, TierC<1>{}, TierC<0>{}, c012 + tier_count[3], tier_count[4]);
+        if (tier_count[5] > 0 || !staged) bad = true;
     } else {
-        run(TierC<kHot>{}, TierC<1>{}, 0, 0, false);
+        run(TierC<kHot>{}, TierC<0>{}, TierC<1>{}, 0, 0);
     }
 
     // ---- merge the waves: l is summed over the 16 lanes of the row holding

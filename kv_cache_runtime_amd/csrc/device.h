@@ -82,7 +82,7 @@ __device__ __forceinline__ int32_t sext_field(uint32_t w, int sh, int bits) {
 }
 
 // ---------------------------------------------------------------------------
-// Vector loads of NB bytes (NB in {2, 4, 8, 16, 32}) into 32-bit words.
+// Vector loads of NB bytes (NB in {1, 2, 4, 8, 16, 32}) into 32-bit words.
 // ---------------------------------------------------------------------------
 template <int NB>
 __device__ __forceinline__ void load_words(uint32_t *dst, const void *src) {
@@ -99,9 +99,11 @@ __device__ __forceinline__ void load_words(uint32_t *dst, const void *src) {
         dst[0] = a.x; dst[1] = a.y;
     } else if constexpr (NB == 4) {
         dst[0] = *reinterpret_cast<const uint32_t *>(src);
-    } else {
-        static_assert(NB == 2, "unsupported load width");
+    } else if constexpr (NB == 2) {
         dst[0] = *reinterpret_cast<const uint16_t *>(src);
+    } else {
+        static_assert(NB == 1, "unsupported load width");
+        dst[0] = *reinterpret_cast<const uint8_t *>(src);
     }
 }
 
@@ -180,29 +182,30 @@ __device__ __forceinline__ bool map_row(const RowMap &m, int row, int &seq, int 
     return ok;
 }
 
-// Stages the page-table entries lp_first .. lp_first + n - 1 of a split into
-// LDS grouped by tier (entry >> 30: hot, int8, int4, and 3 = invalid), keeping
-// the logical order inside a tier; s_lp receives each staged entry's offset
-// from lp_first and count[t] (every thread) the number of entries of tier t.
-// The ranks come from wave ballots, so the order is fixed (no atomics).
-// Whole workgroup of 256 threads, n <= 512; ends with a barrier.
-// Folding keys with an online softmax does not depend on their order, so a
-// split may visit its pages in this order: the waves then mostly meet pages of
-// one tier and take one load path.
-__device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, int32_t *s_entry,
-                                                    int16_t *s_lp, int (&count)[4]) {
-    __shared__ int s_cnt[2][4][4];  // chunk, wave, tier
+// Stages n page-table entries of a tiered split in LDS grouped by entry
+// class (hot, int8, int4, FP8, INT2, then entries that name no pool),
+// keeping the logical order inside a class.  s_slot receives each staged
+// page's slot in its pool, s_lp its offset from lp_first, and count[c]
+// (every thread) the number of entries of class c.  The ranks come from wave
+// ballots, so the order is fixed (no atomics).  Whole workgroup of 256
+// threads, n <= 512; ends with a barrier.  Folding keys with an online
+// softmax does not depend on their order, so a split may visit its pages in
+// this order: the waves then mostly meet pages of one class and take one
+// load path.
+constexpr int kClasses = 6;
+__device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, int32_t *s_slot,
+                                                    int16_t *s_lp, int (&count)[kClasses]) {
+    __shared__ int s_cnt[2][4][kClasses];  // chunk, wave, class
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int32_t e[2];
+    uint32_t slot[2];
     int t[2], rank[2];
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const int i = ch * 256 + tid;
-        e[ch] = i < n ? trow[i] : 0;
-        t[ch] = i < n ? (int)((uint32_t)e[ch] >> 30) : 4;
+        t[ch] = i < n ? entry_class((uint32_t)trow[i], slot[ch]) : kClasses;
         rank[ch] = 0;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < kClasses; ++tt) {
             const uint64_t m = __ballot(t[ch] == tt);
             if (lane == 0) s_cnt[ch][wave][tt] = __popcll(m);
             if (t[ch] == tt)
@@ -212,7 +215,7 @@ __device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, 
     }
     __syncthreads();
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < kClasses; ++tt) {
         int sum = 0;
         for (int c2 = 0; c2 < 2; ++c2)
             for (int w2 = 0; w2 < 4; ++w2) sum += s_cnt[c2][w2][tt];
@@ -229,7 +232,7 @@ __device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, 
                 for (int u = 0; u < tt; ++u) pos += s_cnt[c2][w2][u];
                 if (c2 < ch || (c2 == ch && w2 < wave)) pos += s_cnt[c2][w2][tt];
             }
-        s_entry[pos] = e[ch];
+        s_slot[pos] = (int32_t)slot[ch];
         s_lp[pos] = (int16_t)i;
     }
     __syncthreads();

@@ -177,8 +177,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DecodeParams p, int 
     const int i = blockIdx.x / p.num_kv_heads;
     const int g = blockIdx.x % p.num_kv_heads;
     if (i >= n) return;
-    const uint32_t e = (uint32_t)entries[i];
-    const uint32_t tier = e >> 30, slot = e & ((1u << 30) - 1u);
+    uint32_t slot;
+    const int tier = entry_class((uint32_t)entries[i], slot);
     const int P = p.page_tokens;
     const int64_t dst = (((int64_t)i * p.num_kv_heads + g) * P) * D;
     const int64_t src_row = ((int64_t)slot * p.num_kv_heads + g) * P;
@@ -201,7 +201,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DecodeParams p, int 
             const int sh = (t & 1) ? 24 : 28;  // high nibble for odd elements
             kv = (float)sext_field(bk, sh, 4) * ks;
             vv = (float)sext_field(bv, sh, 4) * vs;
-        } else if (tier == 3 && slot < (uint32_t)p.n_f8) {
+        } else if (tier == CLS_I2 && slot < (uint32_t)p.n_i2) {
+            const float ks = p.i2_ks[(int64_t)slot * p.num_kv_heads + g];
+            const float vs = p.i2_vs[(int64_t)slot * p.num_kv_heads + g];
+            const uint32_t bk = p.i2_k[src_row * (D / 4) + t / 4];
+            const uint32_t bv = p.i2_v[src_row * (D / 4) + t / 4];
+            const int sh = 30 - 2 * (t & 3);  // element 4i + j: bits 2j, 2j + 1
+            kv = (float)sext_field(bk, sh, 2) * ks;
+            vv = (float)sext_field(bv, sh, 2) * vs;
+        } else if (tier == CLS_F8 && slot < (uint32_t)p.n_f8) {
             const float ks = p.f8_ks[(int64_t)slot * p.num_kv_heads + g];
             const float vs = p.f8_vs[(int64_t)slot * p.num_kv_heads + g];
             kv = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)p.f8_k[src_row * D + t], false)[0] * ks;
@@ -271,15 +279,15 @@ __global__ __launch_bounds__(256) void validate_kernel(const ValidateParams v) {
     uint32_t bad_entry = 0, bad_val = 0, bad_scale = 0;
     for (int lp = max(lp0, n_regen); lp < lp_end; ++lp) {
         const uint32_t e = (uint32_t)trow[lp];
-        uint32_t tier = 0, slot = e;
-        if (v.mode == MODE_TIERED) {
-            tier = e >> 30;
-            slot = e & ((1u << 30) - 1u);
-        }
-        const bool ok = tier == 0   ? slot < (uint32_t)p.num_blocks
-                        : tier == 1 ? slot < (uint32_t)p.n_i8
-                        : tier == 2 ? slot < (uint32_t)p.n_i4
-                                    : slot < (uint32_t)p.n_f8;
+        uint32_t slot = e;
+        int tier = 0;
+        if (v.mode == MODE_TIERED) tier = entry_class(e, slot);
+        const bool ok = tier == CLS_HOT  ? slot < (uint32_t)p.num_blocks
+                        : tier == CLS_I8 ? slot < (uint32_t)p.n_i8
+                        : tier == CLS_I4 ? slot < (uint32_t)p.n_i4
+                        : tier == CLS_F8 ? slot < (uint32_t)p.n_f8
+                        : tier == CLS_I2 ? slot < (uint32_t)p.n_i2
+                                         : false;
         if (!ok) {
             if (threadIdx.x == 0) ++bad_entry;
             continue;
@@ -298,9 +306,11 @@ __global__ __launch_bounds__(256) void validate_kernel(const ValidateParams v) {
                 if (!__builtin_isfinite(b)) ++bad_val;
             }
         } else {
-            const float *ks = tier == 1 ? p.i8_ks : tier == 2 ? p.i4_ks : p.f8_ks;
-            const float *vs = tier == 1 ? p.i8_vs : tier == 2 ? p.i4_vs : p.f8_vs;
-            if (tier == 3 && p.f8_k && p.f8_v) {  // FP8 NaN codes (0x7F / 0xFF)
+            const float *ks = tier == CLS_I8 ? p.i8_ks : tier == CLS_I4 ? p.i4_ks
+                              : tier == CLS_F8 ? p.f8_ks : p.i2_ks;
+            const float *vs = tier == CLS_I8 ? p.i8_vs : tier == CLS_I4 ? p.i4_vs
+                              : tier == CLS_F8 ? p.f8_vs : p.i2_vs;
+            if (tier == CLS_F8 && p.f8_k && p.f8_v) {  // FP8 NaN codes (0x7F / 0xFF)
                 const int64_t n = (int64_t)p.num_kv_heads * rows * D;
                 for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
                     const int g = (int)(i / ((int64_t)rows * D));

@@ -54,6 +54,9 @@ struct DecodeParams {
     const uint8_t *f8_k, *f8_v;   // FP8 E4M3 codes
     const float *f8_ks, *f8_vs;
     int32_t n_f8;
+    const uint8_t *i2_k, *i2_v;   // INT2 codes, four per byte
+    const float *i2_ks, *i2_vs;
+    int32_t n_i2;
     // regenerated pages
     uint64_t seed;
     uint32_t layer;
@@ -166,8 +169,25 @@ struct DemoteParams {
     uint8_t *f8_k, *f8_v;
     float *f8_ks, *f8_vs;
     int32_t n_f8;
+    uint8_t *i2_k, *i2_v;
+    float *i2_ks, *i2_vs;
+    int32_t n_i2;
     int32_t *rejected;             // device counter or null
 };
+
+// Classes of a tiered page-table entry: tiers 0-2 as they are, tier 3 split
+// by its kind bits (29-28) into FP8 and INT2; other kinds name no pool.
+enum EntryClass : int { CLS_HOT = 0, CLS_I8 = 1, CLS_I4 = 2, CLS_F8 = 3, CLS_I2 = 4, CLS_BAD = 5 };
+__host__ __device__ inline int entry_class(uint32_t e, uint32_t &slot) {
+    const uint32_t tier = e >> 30;
+    if (tier < 3) {
+        slot = e & ((1u << 30) - 1u);
+        return (int)tier;
+    }
+    const uint32_t kind = (e >> 28) & 3u;
+    slot = e & ((1u << 28) - 1u);
+    return kind < 2 ? CLS_F8 + (int)kind : CLS_BAD;
+}
 
 // Page-table entries a decode workgroup stages in LDS for its split.
 constexpr int kDecodeStagedPages = 512;

@@ -92,11 +92,13 @@ struct DemoteSrc {
     float scale;         // cold tiers
 };
 
-template <int ST>  // source tier: 0 hot, 1 int8, 2 int4, 3 FP8
+template <int ST>  // source class: 0 hot, 1 int8, 2 int4, 3 FP8, 4 INT2
 __device__ inline uint4 load_chunk(const DemoteSrc &s, int64_t ch) {
     if constexpr (ST == 0) return reinterpret_cast<const uint4 *>(s.base)[ch];
     if constexpr (ST == 2)
         return make_uint4(reinterpret_cast<const uint32_t *>(s.base)[ch], 0u, 0u, 0u);
+    if constexpr (ST == 4)
+        return make_uint4(reinterpret_cast<const uint16_t *>(s.base)[ch], 0u, 0u, 0u);
     const uint2 v = reinterpret_cast<const uint2 *>(s.base)[ch];
     return make_uint4(v.x, v.y, 0u, 0u);
 }
@@ -120,6 +122,9 @@ __device__ inline void widen8(const DemoteSrc &s, const uint4 w, float (&x)[8]) 
     } else if constexpr (ST == 2) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = (float)sext_field(ww[0], 28 - 4 * j, 4) * s.scale;
+    } else if constexpr (ST == 4) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (float)sext_field(ww[0], 30 - 2 * j, 2) * s.scale;
     } else {
         typedef float f2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -158,11 +163,11 @@ __device__ inline uint32_t e4m3_nearest(const float y) {
 }
 
 // Codes of the 8 elements of chunk ch, stored at their place in the int8 or
-// FP8 (8 bytes per chunk) or int4 (one 32-bit word per chunk) block.
-template <int ST, int DT>  // source and destination tiers
+// FP8 (8 bytes per chunk), int4 (one 32-bit word) or INT2 (16 bits) block.
+template <int ST, int DT>  // source and destination classes
 __device__ inline void encode8(const DemoteSrc &src, const uint4 w, const float scale,
-                               int8_t *i8, uint8_t *i4, const int64_t ch) {
-    constexpr int qmax = DT == 1 ? 127 : DT == 2 ? 7 : 448;
+                               int8_t *i8, uint8_t *i4, uint8_t *i2, const int64_t ch) {
+    constexpr int qmax = DT == 1 ? 127 : DT == 2 ? 7 : DT == 3 ? 448 : 1;
     float x[8];
     widen8<ST>(src, w, x);
     int c[8];
@@ -183,19 +188,24 @@ __device__ inline void encode8(const DemoteSrc &src, const uint4 w, const float 
             hi |= (uint32_t)(c[4 + j] & 0xFF) << (8 * j);
         }
         reinterpret_cast<uint2 *>(i8)[ch] = make_uint2(lo, hi);
-    } else {
+    } else if constexpr (DT == 2) {
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) word |= (uint32_t)(c[j] & 0xF) << (4 * j);
         reinterpret_cast<uint32_t *>(i4)[ch] = word;
+    } else {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bits |= (uint32_t)(c[j] & 0x3) << (2 * j);
+        reinterpret_cast<uint16_t *>(i2)[ch] = (uint16_t)bits;
     }
 }
 
 // Max |x| pass, then the encoding pass, of one block by one wave.
 template <int R, int ST, int DT>
 __device__ inline void encode_block(const DemoteSrc &src, const int64_t nch, int8_t *i8,
-                                    uint8_t *i4, float *scale_out, const int lane) {
-    constexpr int qmax = DT == 1 ? 127 : DT == 2 ? 7 : 448;
+                                    uint8_t *i4, uint8_t *i2, float *scale_out, const int lane) {
+    constexpr int qmax = DT == 1 ? 127 : DT == 2 ? 7 : DT == 3 ? 448 : 1;
     uint4 keep[R];
     float amax = 0.0f;
 #pragma unroll
@@ -213,29 +223,32 @@ __device__ inline void encode_block(const DemoteSrc &src, const int64_t nch, int
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t ch = lane + 64 * j;
-        if (ch < nch) encode8<ST, DT>(src, keep[j], scale, i8, i4, ch);
+        if (ch < nch) encode8<ST, DT>(src, keep[j], scale, i8, i4, i2, ch);
     }
     for (int64_t ch = lane + 64 * R; ch < nch; ch += 64)
-        encode8<ST, DT>(src, load_chunk<ST>(src, ch), scale, i8, i4, ch);
+        encode8<ST, DT>(src, load_chunk<ST>(src, ch), scale, i8, i4, i2, ch);
     if (lane == 0) *scale_out = scale;
 }
 
 template <int R, int ST>
-__device__ inline void dispatch_dst(uint32_t dt, const DemoteSrc &src, int64_t nch, int8_t *i8,
-                                    uint8_t *i4, float *sdst, int lane) {
-    if (dt == 1) encode_block<R, ST, 1>(src, nch, i8, i4, sdst, lane);
-    else if (dt == 2) encode_block<R, ST, 2>(src, nch, i8, i4, sdst, lane);
-    else encode_block<R, ST, 3>(src, nch, i8, i4, sdst, lane);
+__device__ inline void dispatch_dst(int dt, const DemoteSrc &src, int64_t nch, int8_t *i8,
+                                    uint8_t *i4, uint8_t *i2, float *sdst, int lane) {
+    if (dt == CLS_I8) encode_block<R, ST, CLS_I8>(src, nch, i8, i4, i2, sdst, lane);
+    else if (dt == CLS_I4) encode_block<R, ST, CLS_I4>(src, nch, i8, i4, i2, sdst, lane);
+    else if (dt == CLS_F8) encode_block<R, ST, CLS_F8>(src, nch, i8, i4, i2, sdst, lane);
+    else encode_block<R, ST, CLS_I2>(src, nch, i8, i4, i2, sdst, lane);
 }
 
 template <int R>
-__device__ inline void dispatch_block(uint32_t st, uint32_t dt, const DemoteSrc &src, int64_t nch,
-                                      int8_t *i8, uint8_t *i4, float *sdst, int lane) {
+__device__ inline void dispatch_block(int st, int dt, const DemoteSrc &src, int64_t nch,
+                                      int8_t *i8, uint8_t *i4, uint8_t *i2, float *sdst,
+                                      int lane) {
     switch (st) {
-        case 0: dispatch_dst<R, 0>(dt, src, nch, i8, i4, sdst, lane); break;
-        case 1: dispatch_dst<R, 1>(dt, src, nch, i8, i4, sdst, lane); break;
-        case 2: dispatch_dst<R, 2>(dt, src, nch, i8, i4, sdst, lane); break;
-        default: dispatch_dst<R, 3>(dt, src, nch, i8, i4, sdst, lane); break;
+        case CLS_HOT: dispatch_dst<R, CLS_HOT>(dt, src, nch, i8, i4, i2, sdst, lane); break;
+        case CLS_I8: dispatch_dst<R, CLS_I8>(dt, src, nch, i8, i4, i2, sdst, lane); break;
+        case CLS_I4: dispatch_dst<R, CLS_I4>(dt, src, nch, i8, i4, i2, sdst, lane); break;
+        case CLS_F8: dispatch_dst<R, CLS_F8>(dt, src, nch, i8, i4, i2, sdst, lane); break;
+        default: dispatch_dst<R, CLS_I2>(dt, src, nch, i8, i4, i2, sdst, lane); break;
     }
 }
 
@@ -252,20 +265,20 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     const int kv = (int)(unit & 1);
     const int g = (int)((unit >> 1) % d.num_kv_heads);
     const int i = (int)((unit >> 1) / d.num_kv_heads);
-    const uint32_t se = (uint32_t)d.src_slots[i];
-    const uint32_t stier = se >> 30, sslot = se & ((1u << 30) - 1u);
-    const uint32_t dst = (uint32_t)d.dst_entries[i];
-    const uint32_t tier = dst >> 30, slot = dst & ((1u << 30) - 1u);
-    const bool dst_ok = (tier == 1 && slot < (uint32_t)d.n_i8) ||
-                        (tier == 2 && slot < (uint32_t)d.n_i4) ||
-                        (tier == 3 && slot < (uint32_t)d.n_f8);
-    const bool src_ok = (stier == 0 && sslot < (uint32_t)d.num_blocks) ||
-                        (stier == 1 && sslot < (uint32_t)d.n_i8) ||
-                        (stier == 2 && sslot < (uint32_t)d.n_i4) ||
-                        (stier == 3 && sslot < (uint32_t)d.n_f8);
-    float *sc = tier == 1   ? (kv ? d.i8_vs : d.i8_ks)
-                : tier == 2 ? (kv ? d.i4_vs : d.i4_ks)
-                            : (kv ? d.f8_vs : d.f8_ks);
+    uint32_t sslot, slot;
+    const int stier = entry_class((uint32_t)d.src_slots[i], sslot);
+    const int tier = entry_class((uint32_t)d.dst_entries[i], slot);
+    auto in_pool = [&](int cls, uint32_t s) {
+        return (cls == CLS_HOT && s < (uint32_t)d.num_blocks) ||
+               (cls == CLS_I8 && s < (uint32_t)d.n_i8) || (cls == CLS_I4 && s < (uint32_t)d.n_i4) ||
+               (cls == CLS_F8 && s < (uint32_t)d.n_f8) || (cls == CLS_I2 && s < (uint32_t)d.n_i2);
+    };
+    const bool dst_ok = tier != CLS_HOT && in_pool(tier, slot);
+    const bool src_ok = in_pool(stier, sslot);
+    float *sc = tier == CLS_I8   ? (kv ? d.i8_vs : d.i8_ks)
+                : tier == CLS_I4 ? (kv ? d.i4_vs : d.i4_ks)
+                : tier == CLS_F8 ? (kv ? d.f8_vs : d.f8_ks)
+                                 : (kv ? d.i2_vs : d.i2_ks);
     if (!dst_ok || !src_ok) {
         if (lane == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
         // a bad source: the page turns its rows into NaN
@@ -285,6 +298,9 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     } else if (stier == 2) {
         src.base = (kv ? d.i4_v : d.i4_k) + sblk * (n / 2);
         src.scale = (kv ? d.i4_vs : d.i4_ks)[sblk];
+    } else if (stier == CLS_I2) {
+        src.base = (kv ? d.i2_v : d.i2_k) + sblk * (n / 4);
+        src.scale = (kv ? d.i2_vs : d.i2_ks)[sblk];
     } else {
         src.base = (kv ? d.f8_v : d.f8_k) + sblk * n;
         src.scale = (kv ? d.f8_vs : d.f8_ks)[sblk];
@@ -295,10 +311,11 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
                  : tier == 3 ? reinterpret_cast<int8_t *>(kv ? d.f8_v : d.f8_k) + dst_base
                              : nullptr;
     uint8_t *i4 = tier == 2 ? (kv ? d.i4_v : d.i4_k) + dst_base / 2 : nullptr;
+    uint8_t *i2 = tier == CLS_I2 ? (kv ? d.i2_v : d.i2_k) + dst_base / 4 : nullptr;
     float *sdst = sc + (int64_t)slot * d.num_kv_heads + g;
     // one straight-line body per (source, destination) tier pair (the
     // choice is wave-uniform)
-    dispatch_block<R>(stier, tier, src, n / 8, i8, i4, sdst, lane);
+    dispatch_block<R>(stier, tier, src, n / 8, i8, i4, i2, sdst, lane);
 }
 
 }  // namespace

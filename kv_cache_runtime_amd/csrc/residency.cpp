@@ -177,9 +177,9 @@ atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_resid
         c->fp8_pages < 0 || c->int8_pages < 0)
         return fail(ATLAS_EINVAL, "negative policy field");
     if (c->num_fp8 < 0 || c->num_int8 < 0 || c->num_int4 < 0 ||
-        c->num_fp8 > (int32_t)kSlotMask || c->num_int8 > (int32_t)kSlotMask ||
+        c->num_fp8 > (1 << ATLAS_EXT_KIND_SHIFT) || c->num_int8 > (int32_t)kSlotMask ||
         c->num_int4 > (int32_t)kSlotMask)
-        return fail(ATLAS_EINVAL, "cold pool size outside [0, 2^30)");
+        return fail(ATLAS_EINVAL, "cold pool size outside [0, 2^30) (FP8: 2^28)");
     if ((int64_t)c->max_seqs * c->max_pages_per_seq > ((int64_t)1 << 31))
         return fail(ATLAS_EINVAL, "max_seqs * max_pages_per_seq too large");
     atlas_residency *rt = new (std::nothrow) atlas_residency();

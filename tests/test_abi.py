@@ -243,6 +243,15 @@ def test_write_and_demote_arguments_are_checked():
                                 None) == atlas.EINVAL
     assert "fp8" in atlas.atlas_last_error()
     pools.num_fp8 = 0
+    pools.num_int2 = 2  # int2 pointers missing
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    assert "int2" in atlas.atlas_last_error()
+    pools.num_int2 = 0
+    pools.reserved3 = 1
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    pools.reserved3 = 0
     pools.reserved2 = 1
     assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
                                 None) == atlas.EINVAL
