@@ -9,7 +9,7 @@
  * regenerated pages into the hot cache, runtime counters.  argus-cache,
  * "Visual Architecture" and its configuration (max_active_pages,
  * max_fp8_pages, sink_tokens): an FP16 active pool for recent pages, the
- * compression cascade FP8 -> INT8 -> INT4 for older ones, attention sinks
+ * compression cascade FP8 -> INT8 -> INT4 -> INT2 for older ones, attention sinks
  * that stay in FP16.
  *
  * The runtime is plain host code: it reads and writes no device memory and
@@ -66,6 +66,9 @@ typedef struct atlas_residency_config {
     int32_t num_fp8;           /* tiered: cold pool capacities in slots (slots 0 .. n-1) */
     int32_t num_int8;
     int32_t num_int4;
+    int32_t int4_pages;        /* tiered, with num_int2 > 0: the next this many cold pages
+                                  in INT4, older pages INT2 */
+    int32_t num_int2;          /* tiered: INT2 pool capacity (0: INT4 is the last tier) */
 } atlas_residency_config;
 
 typedef struct atlas_residency_stats {
@@ -75,8 +78,8 @@ typedef struct atlas_residency_stats {
     int32_t fp8_used;          /* cold slots in use, per tier */
     int32_t int8_used;
     int32_t int4_used;
+    int32_t int2_used;
     int32_t regenerated_pages; /* regen: pages now served by regeneration */
-    int32_t reserved;
     int64_t appended_tokens;   /* counters since creation */
     int64_t demotions;         /* jobs whose source was a hot block */
     int64_t transcodes;        /* jobs whose source was a cold slot */
@@ -127,7 +130,8 @@ atlas_status atlas_residency_append(atlas_residency *rt, int32_t seq, int32_t n_
 /* Applies the policy to every active sequence and fills `jobs`.  Tiered mode:
  * each page's target is hot for sink and KeepRecent pages; counting back
  * from the window, fp8_pages FP8 pages, then int8_pages INT8 pages, then
- * INT4; a full pool falls through to the next colder tier.  Each page that
+ * INT4 (with an INT2 pool: int4_pages INT4 pages, then INT2); a full pool
+ * falls through to the next colder tier.  Each page that
  * is hotter than its target gets one job (its current entry -> a new slot of
  * the target tier); its old block or slot is freed after the plan, so no
  * job of a plan writes where another reads (give each cold pool headroom of

@@ -120,13 +120,13 @@ class ResidencyConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32 if n == "struct_size" else _i32) for n in (
         "struct_size", "mode", "page_tokens", "max_seqs", "max_pages_per_seq", "hot_blocks",
         "recent_tokens", "sink_tokens", "admit_per_plan", "fp8_pages", "int8_pages",
-        "num_fp8", "num_int8", "num_int4")]
+        "num_fp8", "num_int8", "num_int4", "int4_pages", "num_int2")]
 
 
 class ResidencyStats(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32)] + [(n, _i32) for n in (
-        "sequences", "hot_used", "fp8_used", "int8_used", "int4_used", "regenerated_pages",
-        "reserved")] + [(n, ctypes.c_int64) for n in (
+        "sequences", "hot_used", "fp8_used", "int8_used", "int4_used", "int2_used",
+        "regenerated_pages")] + [(n, ctypes.c_int64) for n in (
         "appended_tokens", "demotions", "transcodes", "admissions", "evictions",
         "capacity_failures")]
 

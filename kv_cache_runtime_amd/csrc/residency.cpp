@@ -35,8 +35,8 @@ namespace {
 
 constexpr uint32_t kShift = ATLAS_TIER_SHIFT;
 constexpr uint32_t kSlotMask = (1u << kShift) - 1u;
-constexpr int kTierHot = ATLAS_TIER_HOT, kTierI8 = ATLAS_TIER_INT8, kTierI4 = ATLAS_TIER_INT4,
-              kTierF8 = ATLAS_TIER_FP8;
+// Page classes: the tiers, with the extension tier split into FP8 and INT2.
+constexpr int kTierHot = 0, kTierI8 = 1, kTierI4 = 2, kTierF8 = 3, kTierI2 = 4;
 
 int32_t fail(int32_t st, const char *fmt, ...) {
     char buf[256];
@@ -47,17 +47,33 @@ int32_t fail(int32_t st, const char *fmt, ...) {
     return atlas::report_error(st, buf);
 }
 
-// Coldness order of the tiers: hot < FP8 < INT8 < INT4.
-int coldness(int tier) {
-    switch (tier) {
+// Coldness order of the classes: hot < FP8 < INT8 < INT4 < INT2.
+int coldness(int cls) {
+    switch (cls) {
         case kTierHot: return 0;
         case kTierF8: return 1;
         case kTierI8: return 2;
-        default: return 3;
+        case kTierI4: return 3;
+        default: return 4;
     }
 }
 
-uint32_t entry(int tier, int32_t slot) { return ((uint32_t)tier << kShift) | (uint32_t)slot; }
+// Page-table entry of a class and slot (FP8 and INT2 share tier 3).
+uint32_t entry(int cls, int32_t slot) {
+    if (cls == kTierI2)
+        return (3u << kShift) | ((uint32_t)ATLAS_EXT_INT2 << ATLAS_EXT_KIND_SHIFT) | (uint32_t)slot;
+    return ((uint32_t)cls << kShift) | (uint32_t)slot;
+}
+
+int class_of(uint32_t e) {
+    const uint32_t tier = e >> kShift;
+    if (tier < 3) return (int)tier;
+    return ((e >> ATLAS_EXT_KIND_SHIFT) & 3u) == ATLAS_EXT_INT2 ? kTierI2 : kTierF8;
+}
+
+int32_t slot_of(uint32_t e) {
+    return (int32_t)(e & ((e >> kShift) == 3u ? (1u << ATLAS_EXT_KIND_SHIFT) - 1u : kSlotMask));
+}
 
 // A pool of numbered slots; freed slots are reused lowest-first so the
 // allocation order is deterministic.
@@ -94,7 +110,7 @@ struct Seq {
 struct atlas_residency {
     atlas_residency_config cfg;
     std::vector<Seq> seqs;
-    SlotPool hot, f8, i8, i4;
+    SlotPool hot, f8, i8, i4, i2;
     uint64_t tick = 0;
     atlas_residency_stats st;
 
@@ -103,7 +119,8 @@ struct atlas_residency {
             case kTierHot: return hot;
             case kTierF8: return f8;
             case kTierI8: return i8;
-            default: return i4;
+            case kTierI4: return i4;
+            default: return i2;
         }
     }
     int32_t pages_of(const Seq &s) const {
@@ -124,6 +141,8 @@ struct atlas_residency {
         const int32_t r = wf - 1 - p;  // 0 = the newest cold page
         if (r < cfg.fp8_pages) return kTierF8;
         if (r < cfg.fp8_pages + cfg.int8_pages) return kTierI8;
+        if (cfg.num_int2 > 0 && r >= cfg.fp8_pages + cfg.int8_pages + cfg.int4_pages)
+            return kTierI2;
         return kTierI4;
     }
     // Regen mode: resident pages of a sequence that may be dropped back to
@@ -174,7 +193,8 @@ atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_resid
     if (c->hot_blocks < 0 || c->hot_blocks > (int32_t)kSlotMask)
         return fail(ATLAS_EINVAL, "hot_blocks %d outside [0, 2^30)", c->hot_blocks);
     if (c->recent_tokens < 0 || c->sink_tokens < 0 || c->admit_per_plan < 0 ||
-        c->fp8_pages < 0 || c->int8_pages < 0)
+        c->fp8_pages < 0 || c->int8_pages < 0 || c->int4_pages < 0 || c->num_int2 < 0 ||
+        c->num_int2 > (1 << ATLAS_EXT_KIND_SHIFT))
         return fail(ATLAS_EINVAL, "negative policy field");
     if (c->num_fp8 < 0 || c->num_int8 < 0 || c->num_int4 < 0 ||
         c->num_fp8 > (1 << ATLAS_EXT_KIND_SHIFT) || c->num_int8 > (int32_t)kSlotMask ||
@@ -190,6 +210,7 @@ atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_resid
     rt->f8.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_fp8 : 0);
     rt->i8.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int8 : 0);
     rt->i4.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int4 : 0);
+    rt->i2.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int2 : 0);
     std::memset(&rt->st, 0, sizeof(rt->st));
     rt->st.struct_size = sizeof(atlas_residency_stats);
     *out = rt;
@@ -218,8 +239,8 @@ atlas_status atlas_residency_remove_seq(atlas_residency *rt, int32_t seq) {
     const bool tiered = rt->cfg.mode == ATLAS_RESIDENCY_TIERED;
     for (int32_t p = tiered ? 0 : s.first_resident; p < (int32_t)s.pages.size(); ++p) {
         const uint32_t e = s.pages[p];
-        const int tier = tiered ? (int)(e >> kShift) : kTierHot;
-        rt->pool(tier).give((int32_t)(e & kSlotMask));
+        const int tier = tiered ? class_of(e) : kTierHot;
+        rt->pool(tier).give(tiered ? slot_of(e) : (int32_t)e);
     }
     s = Seq();
     return atlas::report_ok();
@@ -329,7 +350,7 @@ atlas_status atlas_residency_plan(atlas_residency *rt, atlas_residency_jobs *job
         // newest pages first: when a warm pool runs short, the newest pages
         // keep the warmer tiers
         for (int32_t p = (int32_t)s.pages.size() - 1; p >= 0; --p) {
-            const int cur = (int)(s.pages[p] >> kShift);
+            const int cur = class_of(s.pages[p]);
             const int want = rt->target_tier(p, wf);
             if (coldness(want) > coldness(cur)) moves.push_back({i, p, s.pages[p], (uint32_t)want});
         }
@@ -342,9 +363,12 @@ atlas_status atlas_residency_plan(atlas_residency *rt, atlas_residency_jobs *job
     for (Move &m : moves) {
         int tier = (int)m.to;
         while (tier != -1 && rt->pool(tier).empty()) {  // fall through to colder tiers
-            tier = tier == kTierF8 ? kTierI8 : tier == kTierI8 ? kTierI4 : -1;
+            tier = tier == kTierF8   ? kTierI8
+                   : tier == kTierI8 ? kTierI4
+                   : tier == kTierI4 && rt->cfg.num_int2 > 0 ? kTierI2
+                                     : -1;
             // a fallback must still be colder than where the page is now
-            if (tier != -1 && coldness(tier) <= coldness((int)(m.from >> kShift))) tier = -1;
+            if (tier != -1 && coldness(tier) <= coldness(class_of(m.from))) tier = -1;
         }
         if (tier == -1) {
             for (auto &t : taken) rt->pool(t.first).give(t.second);
@@ -364,10 +388,10 @@ atlas_status atlas_residency_plan(atlas_residency *rt, atlas_residency_jobs *job
         jobs->demote_src[n] = (int32_t)m.from;
         jobs->demote_dst[n] = (int32_t)m.to;
         ++n;
-        if ((m.from >> kShift) == (uint32_t)kTierHot) ++rt->st.demotions;
+        if (class_of(m.from) == kTierHot) ++rt->st.demotions;
         else ++rt->st.transcodes;
     }
-    for (const Move &m : moves) rt->pool((int)(m.from >> kShift)).give((int32_t)(m.from & kSlotMask));
+    for (const Move &m : moves) rt->pool(class_of(m.from)).give(slot_of(m.from));
     jobs->n_demote = n;
     return atlas::report_ok();
 }
@@ -421,6 +445,7 @@ atlas_status atlas_residency_get_stats(const atlas_residency *rt, atlas_residenc
     out->fp8_used = rt->f8.used();
     out->int8_used = rt->i8.used();
     out->int4_used = rt->i4.used();
+    out->int2_used = rt->i2.used();
     return atlas::report_ok();
 }
 

@@ -25,7 +25,8 @@ class Residency:
 
     def __init__(self, *, mode, page_tokens, max_seqs, max_pages_per_seq, hot_blocks,
                  recent_tokens=0, sink_tokens=0, admit_per_plan=0, fp8_pages=0, int8_pages=0,
-                 num_fp8=0, num_int8=0, num_int4=0, job_capacity=1 << 16):
+                 num_fp8=0, num_int8=0, num_int4=0, int4_pages=0, num_int2=0,
+                 job_capacity=1 << 16):
         L = atlas.load()
         c = atlas.ResidencyConfig()
         c.struct_size = ctypes.sizeof(c)
@@ -34,7 +35,7 @@ class Residency:
                          recent_tokens=recent_tokens, sink_tokens=sink_tokens,
                          admit_per_plan=admit_per_plan, fp8_pages=fp8_pages,
                          int8_pages=int8_pages, num_fp8=num_fp8, num_int8=num_int8,
-                         num_int4=num_int4).items():
+                         num_int4=num_int4, int4_pages=int4_pages, num_int2=num_int2).items():
             setattr(c, k, int(v))
         self.config = c
         self._h = ctypes.c_void_p()
@@ -95,5 +96,4 @@ class Residency:
         s = atlas.ResidencyStats()
         s.struct_size = ctypes.sizeof(s)
         self._call("atlas_residency_get_stats", ctypes.byref(s))
-        return {name: getattr(s, name) for name, _ in s._fields_ if name not in
-                ("struct_size", "reserved")}
+        return {name: getattr(s, name) for name, _ in s._fields_ if name != "struct_size"}

@@ -43,13 +43,13 @@ def _attend(a, dev, tiers=None, regen=None):
 def test_tiered_decode_loop_through_the_runtime(gpu):
     rt = Residency(mode=TIERED, page_tokens=P, max_seqs=3, max_pages_per_seq=64, hot_blocks=64,
                    recent_tokens=64, sink_tokens=16, fp8_pages=2, int8_pages=3, num_fp8=16,
-                   num_int8=24, num_int4=160)
+                   num_int8=24, num_int4=40, int4_pages=3, num_int2=160)
     gen = torch.Generator(device=gpu).manual_seed(1)
     hot_k = torch.zeros((64, HKV, P, D), dtype=torch.float16, device=gpu)
     hot_v = torch.zeros_like(hot_k)
     tiers = {}
     for key, n, shape_d, dt in (("f8", 16, D, torch.uint8), ("i8", 24, D, torch.int8),
-                                ("i4", 160, D // 2, torch.uint8)):
+                                ("i4", 40, D // 2, torch.uint8), ("i2", 160, D // 4, torch.uint8)):
         for kv in ("k", "v"):
             tiers[f"{key}_{kv}"] = torch.zeros((n, HKV, P, shape_d), dtype=dt, device=gpu)
             tiers[f"{key}_{kv}_scale"] = torch.zeros((n, HKV), device=gpu)
@@ -108,7 +108,7 @@ def test_tiered_decode_loop_through_the_runtime(gpu):
             a.num_blocks = 64
             _attend(a, gpu, tiers=pools)
             counts = [64, tiers["i8_k"].shape[0], tiers["i4_k"].shape[0],
-                      tiers["f8_k"].shape[0]]
+                      tiers["f8_k"].shape[0], tiers["i2_k"].shape[0]]
             w = synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
                             page_tokens=P, q_dtype="bf16", kv_dtype="f16", context_lens=ctx,
                             query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
@@ -120,6 +120,7 @@ def test_tiered_decode_loop_through_the_runtime(gpu):
     st = rt.stats()
     assert checked == 4 and st["demotions"] > 0 and st["transcodes"] > 0
     assert st["fp8_used"] > 0 and st["int8_used"] > 0 and st["int4_used"] > 0
+    assert st["int2_used"] > 0
 
 
 def test_regen_decode_loop_through_the_runtime(gpu):

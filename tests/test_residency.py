@@ -5,6 +5,7 @@ cascade policy, through the C ABI.  No GPU: the runtime is host code."""
 import numpy as np
 import pytest
 
+import oracle
 from kv_cache_runtime_amd import atlas
 from kv_cache_runtime_amd.residency import REGEN, TIERED, Residency
 
@@ -199,3 +200,20 @@ def test_tiered_without_headroom_falls_through_to_colder_tiers():
     r.append(0, 16)
     src, dst, _, _ = r.plan()
     assert sorted((TIER(s), TIER(d)) for s, d in zip(src, dst)) == [(0, 2), (1, 2), (3, 2)]
+
+
+def test_tiered_cascade_ends_in_int2_when_it_has_a_pool():
+    r = _tiered(int4_pages=4, num_int2=32)
+    r.add_seq(0)
+    r.append(0, 400)             # 25 pages, window 21..24, sink page 0
+    r.plan()
+    table, ctx, _ = r.tables([0])
+    cls = [oracle.entry_class(e)[0] for e in table[0, :25]]
+    # newest cold first: 2 FP8, 3 INT8, 4 INT4, the rest (pages 1..11) INT2
+    assert cls == [0] + [4] * 11 + [2] * 4 + [1] * 3 + [3] * 2 + [0] * 4
+    st = r.stats()
+    assert st["int2_used"] == 11 and st["int4_used"] == 4
+    r.append(0, 16)
+    src, dst, _, _ = r.plan()
+    moves = sorted((oracle.entry_class(s)[0], oracle.entry_class(d)[0]) for s, d in zip(src, dst))
+    assert moves == [(0, 3), (1, 2), (2, 4), (3, 1)]
