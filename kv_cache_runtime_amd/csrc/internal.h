@@ -178,15 +178,13 @@ struct DemoteParams {
 // Classes of a tiered page-table entry: tiers 0-2 as they are, tier 3 split
 // by its kind bits (29-28) into FP8 and INT2; other kinds name no pool.
 enum EntryClass : int { CLS_HOT = 0, CLS_I8 = 1, CLS_I4 = 2, CLS_F8 = 3, CLS_I2 = 4, CLS_BAD = 5 };
+// Branch-free, so callers can issue several entry loads before decoding any.
 __host__ __device__ inline int entry_class(uint32_t e, uint32_t &slot) {
     const uint32_t tier = e >> 30;
-    if (tier < 3) {
-        slot = e & ((1u << 30) - 1u);
-        return (int)tier;
-    }
     const uint32_t kind = (e >> 28) & 3u;
-    slot = e & ((1u << 28) - 1u);
-    return kind < 2 ? CLS_F8 + (int)kind : CLS_BAD;
+    const bool ext = tier == 3u;
+    slot = e & (ext ? ((1u << 28) - 1u) : ((1u << 30) - 1u));
+    return ext ? (kind < 2u ? CLS_F8 + (int)kind : CLS_BAD) : (int)tier;
 }
 
 // Page-table entries a decode workgroup stages in LDS for its split.

@@ -260,14 +260,18 @@ __device__ inline void dispatch_block(int st, int dt, const DemoteSrc &src, int6
 template <int R>
 __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // the wave's block index, held in scalar registers
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= (int64_t)d.n * d.num_kv_heads * 2) return;
     const int kv = (int)(unit & 1);
     const int g = (int)((unit >> 1) % d.num_kv_heads);
     const int i = (int)((unit >> 1) / d.num_kv_heads);
+    // both entries are loaded before either is decoded
+    const uint32_t se = (uint32_t)d.src_slots[i];
+    const uint32_t de = (uint32_t)d.dst_entries[i];
     uint32_t sslot, slot;
-    const int stier = entry_class((uint32_t)d.src_slots[i], sslot);
-    const int tier = entry_class((uint32_t)d.dst_entries[i], slot);
+    const int stier = entry_class(se, sslot);
+    const int tier = entry_class(de, slot);
     auto in_pool = [&](int cls, uint32_t s) {
         return (cls == CLS_HOT && s < (uint32_t)d.num_blocks) ||
                (cls == CLS_I8 && s < (uint32_t)d.n_i8) || (cls == CLS_I4 && s < (uint32_t)d.n_i4) ||
