@@ -8,10 +8,14 @@ with the GPU path.
 from .oracle import (  # noqa: F401
     HostView,
     attend,
+    B1_MAX_OUTLIERS,
     block_f32,
     build,
+    decode_1bit,
     dequant_f32,
+    encode_1bit,
     entry_class,
+    f16_bits,
     fp8_e4m3_encode,
     fp8_e4m3_value,
     int2_codes,

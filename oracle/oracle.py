@@ -20,6 +20,10 @@ Definitions followed:
     E4M3 value of the code times scale), one scale per (page, kv head) for K
     and one for V; int4 element 2i in the low nibble, int2 element 4i + j in
     bits 2j of byte i, two's complement; INT2 and FP8 entries share tier 3;
+  * the 1-bit archival tier: ARGUS "Visual Architecture" and its heatmap
+    legend (8-way sign-packed with FP16 outlier preservation) and its
+    "Limitations" (archival pages are not attended directly; the overview's
+    transient FP16 reconstruction brings them back first);
   * regenerated pages: the value definition in attention.c;
   * split merge: log-sum-exp combination of normalised partial results
     (attnres AGENTS.md, "online softmax merge").
@@ -47,13 +51,14 @@ EXT_SLOT_MASK = (1 << EXT_KIND_SHIFT) - 1
 
 def entry_class(entry: int):
     """(class, slot) of a tiered page-table entry: class 0 hot, 1 int8, 2 int4,
-    3 FP8 (tier 3, kind 0), 4 INT2 (tier 3, kind 1), 5 names no pool."""
+    3 FP8 (tier 3, kind 0), 4 INT2 (tier 3, kind 1), 5 1-bit (tier 3, kind 2),
+    6 names no pool (tier 3, kind 3)."""
     e = int(entry) & 0xFFFFFFFF
     tier = e >> TIER_SHIFT
     if tier < 3:
         return tier, e & SLOT_MASK
     kind = (e >> EXT_KIND_SHIFT) & 3
-    return (3 + kind if kind < 2 else 5), e & EXT_SLOT_MASK
+    return 3 + kind, e & EXT_SLOT_MASK
 
 
 def build(force: bool = False) -> str:
@@ -326,6 +331,62 @@ def pack_int2(codes: np.ndarray) -> np.ndarray:
             ).astype(np.uint8)
 
 
+B1_MAX_OUTLIERS = 64
+
+
+def f16_bits(x) -> np.ndarray:
+    """IEEE half-precision bit patterns of x (f32), round to nearest even."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def encode_1bit(x: np.ndarray, n_out: int):
+    """The 1-bit archival encoding of one (page, kv head) block, as read here
+    from ARGUS's "8-way sign-packed with FP16 outlier preservation":
+
+      * outliers: the n_out elements of largest magnitude (ordered by the bit
+        pattern of f32 |x|, so NaN ranks above inf; ties go to the lower
+        index), kept as (index, FP16 value) pairs, one uint32 each: index in
+        bits 0-15, the FP16 bits (round to nearest even) in bits 16-31,
+        sorted by index;
+      * signs: bit j of byte i is 1 iff element 8 i + j is negative (x < 0;
+        -0.0 and NaN give 0), for every element, outliers included;
+      * scale: the mean |x| over the other elements (the scale that minimises
+        the squared error of x ~ scale * sign), the sum taken in f64 and the
+        quotient rounded to f32; 0 when every element is an outlier.
+
+    x is the block flattened in storage order (row-major [P][D]).  Returns
+    (uint8 signs [n / 8], np.float32 scale, uint32 outliers [min(n_out, n)]).
+    """
+    x = np.asarray(x, dtype=np.float32).ravel()
+    n = x.size
+    k = min(int(n_out), n)
+    key = np.abs(x).view(np.uint32).astype(np.int64)
+    order = np.lexsort((np.arange(n), -key))  # magnitude down, index up
+    idx = np.sort(order[:k])
+    is_out = np.zeros(n, dtype=bool)
+    is_out[idx] = True
+    rest = np.abs(x[~is_out]).astype(np.float64)
+    scale = np.float32(rest.sum() / rest.size) if rest.size else np.float32(0.0)
+    signs = np.packbits((x < 0).astype(np.uint8), bitorder="little")
+    outliers = idx.astype(np.uint32) | (f16_bits(x[idx]).astype(np.uint32) << 16)
+    return signs, scale, outliers
+
+
+def decode_1bit(signs: np.ndarray, scale, outliers: np.ndarray, n: int) -> np.ndarray:
+    """Values of a 1-bit block as f32: -scale where the sign bit is set,
+    +scale elsewhere, then each outlier entry in list order writes its FP16
+    value at its index (an index >= n is ignored; a later entry for the same
+    index wins)."""
+    bits = np.unpackbits(np.asarray(signs, dtype=np.uint8), bitorder="little")[:n]
+    sc = np.float32(scale)
+    out = np.where(bits == 1, -sc, sc).astype(np.float32)
+    for e in np.asarray(outliers, dtype=np.uint32).ravel():
+        i = int(e) & 0xFFFF
+        if i < n:
+            out[i] = np.float32(np.uint16(int(e) >> 16).view(np.float16))
+    return out
+
+
 def pack_int4(codes: np.ndarray) -> np.ndarray:
     """Two's-complement nibbles, element 2i in the low nibble of byte i (the
     argus-cache INT4 "2-way bit-packed" layout as read here)."""
@@ -405,6 +466,12 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
             K[t0:t1] = widen_bits(ka[slot, g, :rows], kind)
             V[t0:t1] = widen_bits(va[slot, g, :rows], kind)
             continue
+        if tier >= 5:
+            # 1-bit archival pages are reconstructed before attention, never
+            # read by it; a row that reaches one is undefined (NaN)
+            K[t0:t1] = np.nan
+            V[t0:t1] = np.nan
+            continue
         ta = host.tier_arrays()
         key = {1: "i8", 2: "i4", 3: "f8", 4: "i2"}[tier]
         for dst, kv in ((K, "k"), (V, "v")):
@@ -422,7 +489,8 @@ def logical_kv(w, s: int, g: int, n_tokens: int | None = None, host=None):
 def block_f32(w, entry: int, g: int, kv: str, host=None) -> np.ndarray:
     """The values of one stored (page, kv head) block of K (kv = "k") or V as
     f32: a hot block (tier 0) widened exactly, a cold slot as f32(code *
-    scale), one rounding of the exact product (FP8: e4m3(code) * scale).
+    scale), one rounding of the exact product (FP8: e4m3(code) * scale), a
+    1-bit slot as decode_1bit gives it.
     This is what a demotion reads when it moves a page down the cascade."""
     host = host or HostView(w)
     tier, slot = entry_class(entry)
@@ -430,6 +498,11 @@ def block_f32(w, entry: int, g: int, kv: str, host=None) -> np.ndarray:
         (ka, kind), (va, _) = host.pools()
         return widen_bits((ka if kv == "k" else va)[slot, g], kind).astype(np.float32)
     ta = host.tier_arrays()
+    if tier == 5:
+        signs = ta[f"b1_{kv}"][slot, g]
+        n = signs.size * 8
+        vals = decode_1bit(signs, ta[f"b1_{kv}_scale"][slot, g], ta[f"b1_{kv}_out"][slot, g], n)
+        return vals.reshape(w.page_tokens, w.head_dim)
     key = {1: "i8", 2: "i4", 3: "f8", 4: "i2"}[tier]
     codes = ta[f"{key}_{kv}"][slot, g]
     vals = fp8_e4m3_value(codes) if key == "f8" else (

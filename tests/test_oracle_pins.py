@@ -732,7 +732,7 @@ def test_entry_classes():
     assert oracle.entry_class((3 << 30) | 11) == (3, 11)
     assert oracle.entry_class((3 << 30) | (1 << 28) | 13) == (4, 13)
     assert oracle.entry_class((3 << 30) | (2 << 28) | 1)[0] == 5
-    assert oracle.entry_class(np.uint32((3 << 30) | (3 << 28)).view(np.int32))[0] == 5
+    assert oracle.entry_class(np.uint32((3 << 30) | (3 << 28)).view(np.int32))[0] == 6
 
 
 def test_tiered_reference_reads_int2_pages():
@@ -755,3 +755,101 @@ def test_tiered_reference_reads_int2_pages():
                                           codes * np.float64(ta["i2_v_scale"][slot, 0]))
             seen += 1
     assert seen > 0
+
+
+# ---------------------------------------------------------------------------
+# 13. 1-bit archival tier (tier 3, kind 2): signs + FP16 outliers
+# ---------------------------------------------------------------------------
+
+def test_1bit_hand_decoded_block():
+    # 16 elements; the two largest magnitudes (3.0 at 2, 10.0 at 8) are the
+    # outliers, listed by index with their FP16 bits (3.0 = 0x4200, 10.0 =
+    # 0x4900); signs: elements 1, 3, 7 and 9 are negative (-0.0 is not)
+    x = np.array([0.5, -2.0, 3.0, -0.25, 0.0, -0.0, 1.0, -1.0,
+                  10.0, -0.5, 0, 0, 0, 0, 0, 0], np.float32)
+    signs, scale, out = oracle.encode_1bit(x, 2)
+    assert signs.tolist() == [0b10001010, 0b00000010]
+    assert out.tolist() == [0x42000002, 0x49000008]
+    # mean |x| of the 14 other elements: (0.5+2+0.25+1+1+0.5) / 14
+    assert scale == np.float32(5.25 / 14)
+    dec = oracle.decode_1bit(signs, scale, out, 16)
+    s = np.float32(5.25 / 14)
+    want = np.array([s, -s, 3.0, -s, s, s, s, -s, 10.0, -s, s, s, s, s, s, s], np.float32)
+    np.testing.assert_array_equal(dec, want)
+
+
+def test_1bit_outliers_are_the_largest_magnitudes_ties_to_lower_index():
+    x = np.array([1, -1, 1, -1, 1, -1, 1, -1], np.float32)
+    _, scale, out = oracle.encode_1bit(x, 3)
+    assert [int(e) & 0xFFFF for e in out] == [0, 1, 2]
+    assert scale == 1.0
+    rng = np.random.default_rng(7)
+    for n_out in (0, 1, 5, 64):
+        x = (rng.standard_normal(512) * rng.choice([0.1, 1, 30], 512)).astype(np.float32)
+        x[rng.integers(0, 512, 40)] = 0.75  # ties
+        _, _, out = oracle.encode_1bit(x, n_out)
+        idx = np.array([int(e) & 0xFFFF for e in out], dtype=np.int64)
+        assert len(idx) == n_out and np.all(np.diff(idx) > 0)
+        rest = np.setdiff1d(np.arange(512), idx)
+        if n_out:
+            # brute force: every kept magnitude >= every dropped one, and a
+            # dropped element equal to the smallest kept one has a higher index
+            lo = np.abs(x[idx]).min()
+            assert np.all(np.abs(x[rest]) <= lo)
+            tied_rest = rest[np.abs(x[rest]) == lo]
+            tied_kept = idx[np.abs(x[idx]) == lo]
+            assert tied_rest.size == 0 or tied_rest.min() > tied_kept.max()
+        # the FP16 values are the nearest-even halves of the elements
+        vals = np.array([np.uint16(int(e) >> 16).view(np.float16) for e in out], np.float16)
+        np.testing.assert_array_equal(vals, x[idx].astype(np.float16))
+
+
+def test_1bit_scale_minimises_the_sign_code_error():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(1024) * 2).astype(np.float32)
+    signs, scale, out = oracle.encode_1bit(x, 16)
+    idx = np.array([int(e) & 0xFFFF for e in out])
+    rest = np.delete(x, idx).astype(np.float64)
+    err = lambda s: np.sum((np.abs(rest) - s) ** 2)  # noqa: E731
+    grid = np.linspace(0.5 * scale, 1.5 * scale, 2001)
+    assert abs(grid[np.argmin([err(g) for g in grid])] - scale) <= (grid[1] - grid[0])
+    # decoded error on the non-outliers equals err(scale); signs follow x
+    dec = oracle.decode_1bit(signs, scale, out, 1024)
+    keep = np.ones(1024, bool)
+    keep[idx] = False
+    np.testing.assert_array_equal(np.signbit(dec[keep]) & (x[keep] != 0), x[keep] < 0)
+    assert np.all(np.abs(dec[keep]) == scale)
+
+
+def test_1bit_exact_when_the_outliers_cover_every_nonzero():
+    rng = np.random.default_rng(11)
+    x = np.zeros(256, np.float32)
+    pos = rng.choice(256, 20, replace=False)
+    x[pos] = rng.standard_normal(20).astype(np.float16).astype(np.float32)
+    signs, scale, out = oracle.encode_1bit(x, 20)
+    assert scale == 0.0
+    np.testing.assert_array_equal(oracle.decode_1bit(signs, scale, out, 256), x)
+
+
+def test_1bit_special_cases():
+    z = np.zeros(64, np.float32)
+    signs, scale, out = oracle.encode_1bit(z, 4)
+    assert scale == 0 and not signs.any() and out.tolist() == [0, 1, 2, 3]
+    # no outliers: a pure sign code with the mean |x| of the whole block
+    x = np.array([1, -3, 2, -2, 0, 4, -4, 4], np.float32)
+    signs, scale, out = oracle.encode_1bit(x, 0)
+    assert out.size == 0 and scale == np.float32(20 / 8) and signs.tolist() == [0b01001010]
+    # NaN outranks every magnitude; inf too
+    x = np.array([1, np.nan, -np.inf, 2, 0, 0, 0, 0], np.float32)
+    _, _, out = oracle.encode_1bit(x, 2)
+    assert [int(e) & 0xFFFF for e in out] == [1, 2]
+    # decoder rules: an out-of-range index is ignored, a later duplicate wins
+    dec = oracle.decode_1bit(np.array([0], np.uint8), 1.0,
+                             np.array([3 | (0x3C00 << 16), 9 | (0x4000 << 16),
+                                       3 | (0xC000 << 16)], np.uint32), 8)
+    assert dec.tolist() == [1, 1, 1, -2, 1, 1, 1, 1]
+
+
+def test_entry_classes_with_archival_kind():
+    assert oracle.entry_class((3 << 30) | (2 << 28) | 5) == (5, 5)
+    assert oracle.entry_class((3 << 30) | (3 << 28) | 5)[0] == 6
