@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATLAS_ABI_VERSION 2u
+#define ATLAS_ABI_VERSION 3u
 
 typedef int32_t atlas_status;
 #define ATLAS_OK 0           /* success (work enqueued) */
@@ -71,11 +71,17 @@ typedef int32_t atlas_status;
 #define ATLAS_TIER_INT4 2 /* int4 codes, two per byte, same scale layout */
 #define ATLAS_TIER_FP8 3  /* FP8 E4M3 codes (OCP "e4m3fn"), same scale layout */
 /* Tier 3 is the extension tier: bits 29-28 of its entries give the kind and
- * bits 27-0 the slot (so FP8 slots stay below 2^28).  Kinds 2 and 3 name no
- * pool. */
+ * bits 27-0 the slot (so FP8 slots stay below 2^28).  Kind 3 names no pool. */
 #define ATLAS_EXT_KIND_SHIFT 28
 #define ATLAS_EXT_FP8 0   /* (3 << 30) | (0 << 28) | slot: FP8 pool */
 #define ATLAS_EXT_INT2 1  /* (3 << 30) | (1 << 28) | slot: INT2 codes, four per byte */
+/* (3 << 30) | (2 << 28) | slot: 1-bit archival pool (argus-cache, heatmap
+ * legend: "8-way sign-packed with FP16 outlier preservation"; its limitations
+ * section keeps such pages out of attention).  Attention calls treat these
+ * entries like entries that name no page (NaN rows; atlas_validate_tables
+ * counts them); atlas_promote_pages reconstructs them into hot blocks first. */
+#define ATLAS_EXT_1BIT 2
+#define ATLAS_1BIT_MAX_OUTLIERS 64
 
 /*
  * One attention call (decode or chunked prefill).  CFR-Atlas README,
@@ -190,6 +196,26 @@ typedef struct atlas_tier_pools {
     const uint8_t *int2_v;
     const float *int2_k_scale;  /* [num_int2][num_kv_heads] */
     const float *int2_v_scale;
+    /* 1-bit archival pool.  A (page, kv head) block of n = page_tokens *
+     * head_dim elements (row-major) is stored as
+     *   signs: bit j of byte i set iff element 8 i + j is negative (x < 0);
+     *   scale: f32, the mean |x| of the elements that are not outliers (0 if
+     *          there are none);
+     *   outliers: the `outliers_1bit` elements of largest |x| (ordered by the
+     *          bit pattern of f32 |x|, ties to the lower index), sorted by
+     *          index, one uint32 each: index in bits 0-15, FP16 value bits
+     *          (round to nearest even) in bits 16-31.
+     * Element e decodes to the FP16 value of an outlier entry with index e (a
+     * later entry wins; indices >= n are ignored), else -scale if its sign
+     * bit is set, else +scale.  Needs n <= 65536. */
+    int32_t num_1bit;           /* slots in the 1-bit pool */
+    int32_t outliers_1bit;      /* outliers per block, 0 .. ATLAS_1BIT_MAX_OUTLIERS */
+    const uint8_t *bit_k;       /* [num_1bit][num_kv_heads][page_tokens * head_dim / 8] */
+    const uint8_t *bit_v;
+    const float *bit_k_scale;   /* [num_1bit][num_kv_heads] */
+    const float *bit_v_scale;
+    const uint32_t *bit_k_out;  /* [num_1bit][num_kv_heads][outliers_1bit] */
+    const uint32_t *bit_v_out;
 } atlas_tier_pools;
 
 /*
@@ -379,29 +405,53 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,
 /*
  * atlas_demote_pages: encodes pages into the cold tiers (argus-cache,
  * "Visual Architecture": the compression cascade FP16 -> FP8 -> INT8 ->
- * INT4).  For i < n, the source src_slots[i] is a tiered entry (tier << 30) |
- * slot: tier 0 is a hot block of args->k_pool / v_pool (kv_dtype F16 or BF16,
- * every row finite; a plain block id is such an entry), any other entry a
- * cold slot of `pools` whose values enter as f32(code * scale).  It is
- * encoded into dst_entries[i], an int8, int4, FP8 or INT2 entry of `pools`:
- * for each kv head, K and V separately,
+ * INT4 -> INT2 -> 1-bit).  For i < n, the source src_slots[i] is a tiered
+ * entry (tier << 30) | slot: tier 0 is a hot block of args->k_pool / v_pool
+ * (kv_dtype F16 or BF16, every row finite; a plain block id is such an
+ * entry), an int8, int4, FP8 or INT2 entry a cold slot of `pools` whose values
+ * enter as f32(code * scale).  It is encoded into dst_entries[i], an int8,
+ * int4, FP8, INT2 or 1-bit entry of `pools`: for each kv head, K and V
+ * separately,
  *     scale = max|x| / qmax    (f32, correctly rounded; qmax 127 / 7 / 448 / 1)
  *     code  = clamp(rint(x / scale), -qmax, qmax)   (round half to even)
  *     FP8:  code = the E4M3 code nearest to x / scale (ties to the even
  *           code; x / scale is correctly rounded f32)
- * and an all-zero block gets scale 0 and codes 0.  Codes and scales are
- * written through the pools' pointers; the caller then points its page-table
- * entries at dst_entries.  A destination outside its pool rejects the page
- * (nothing written); a source outside its pool writes NaN scales, so rows
- * reading the page fail loudly.  Each rejected page adds 1 to
- * *rejected (device int32, optional).  The source and destination sets must
- * not overlap between calls in flight.  Asynchronous on args->stream.
+ * and an all-zero block gets scale 0 and codes 0; a 1-bit destination takes
+ * the encoding described at atlas_tier_pools (its scale sums |x| in f64, so
+ * it can differ from the exactly rounded mean by one f32 ulp).  Codes and
+ * scales are written through the pools' pointers; the caller then points its
+ * page-table entries at dst_entries.  A destination outside its pool, or a
+ * 1-bit source (use atlas_promote_pages), rejects the page (nothing written);
+ * a source outside its pool writes NaN scales, so rows reading the page fail
+ * loudly.  Each rejected page adds 1 to *rejected (device int32, optional).
+ * The source and destination sets must not overlap between calls in flight.
+ * Asynchronous on args->stream.
  */
 atlas_status atlas_demote_pages(const atlas_attn_args *args,
                                 const atlas_tier_pools *pools,
                                 const int32_t *src_slots,
                                 const int32_t *dst_entries, int32_t n,
                                 int32_t *rejected);
+
+/*
+ * atlas_promote_pages: the transient reconstruction of argus-cache's
+ * overview (cold or archived pages restored to FP16 when a query needs
+ * them).  For i < n, the page of the tiered entry src_entries[i] (any class:
+ * hot, int8, int4, FP8, INT2 or 1-bit; device int32) is written into hot block
+ * dst_blocks[i] of args->k_pool / v_pool (device int32): every element's value
+ * (f32(code * scale), the 1-bit decoding, or the hot value itself) rounded to
+ * kv_dtype (F32, F16 or BF16; round to nearest even), K and V, every kv head.
+ * A destination block outside [0, num_blocks) rejects the page (nothing
+ * written); a source outside its pool, or of kind 3, fills the destination
+ * block with NaN.  Each such page adds 1 to *rejected (device int32,
+ * optional).  Sources and destinations must not overlap within a call or
+ * with calls in flight.  Asynchronous on args->stream; allocates nothing.
+ */
+atlas_status atlas_promote_pages(const atlas_attn_args *args,
+                                 const atlas_tier_pools *pools,
+                                 const int32_t *src_entries,
+                                 const int32_t *dst_blocks, int32_t n,
+                                 int32_t *rejected);
 
 /*
  * Measurement helper (not part of the attention method): reads `bytes`

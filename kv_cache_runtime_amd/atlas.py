@@ -88,6 +88,14 @@ class TierPools(ctypes.Structure):
         ("int2_v", _p),
         ("int2_k_scale", _p),
         ("int2_v_scale", _p),
+        ("num_1bit", _i32),
+        ("outliers_1bit", _i32),
+        ("bit_k", _p),
+        ("bit_v", _p),
+        ("bit_k_scale", _p),
+        ("bit_v_scale", _p),
+        ("bit_k_out", _p),
+        ("bit_v_out", _p),
     ]
 
 
@@ -107,7 +115,7 @@ EXPORTS = [
     "atlas_paged_attention", "atlas_paged_attention_tiered", "atlas_paged_attention_regen",
     "atlas_fold_partials", "atlas_gather_pages", "atlas_regenerate_pages",
     "atlas_dequant_pages", "atlas_validate_tables", "atlas_read_probe",
-    "atlas_write_kv", "atlas_demote_pages",
+    "atlas_write_kv", "atlas_demote_pages", "atlas_promote_pages",
     "atlas_residency_create", "atlas_residency_destroy", "atlas_residency_add_seq",
     "atlas_residency_remove_seq", "atlas_residency_append", "atlas_residency_plan",
     "atlas_residency_tables", "atlas_residency_get_stats",
@@ -185,6 +193,9 @@ def load(path: str = LIB_PATH):
     L.atlas_demote_pages.restype = _i32
     L.atlas_demote_pages.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools), _p, _p,
                                      _i32, _p]
+    L.atlas_promote_pages.restype = _i32
+    L.atlas_promote_pages.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools), _p, _p,
+                                      _i32, _p]
     L.atlas_read_probe.restype = _i32
     L.atlas_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, _p]
     L.atlas_residency_create.restype = _i32
@@ -202,7 +213,7 @@ def load(path: str = LIB_PATH):
     L.atlas_residency_tables.argtypes = [_p, _p, _i32, _p, _p, _p]
     L.atlas_residency_get_stats.restype = _i32
     L.atlas_residency_get_stats.argtypes = [_p, ctypes.POINTER(ResidencyStats)]
-    if L.atlas_abi_version() != 2:
+    if L.atlas_abi_version() != 3:
         raise RuntimeError("libatlas ABI version mismatch")
     _lib = L
     return L
@@ -302,6 +313,12 @@ def make_tiers(t: dict) -> TierPools:
         p.num_int2 = int(t["i2_k"].shape[0])
         p.int2_k, p.int2_v = _ptr(t["i2_k"]), _ptr(t["i2_v"])
         p.int2_k_scale, p.int2_v_scale = _ptr(t["i2_k_scale"]), _ptr(t["i2_v_scale"])
+    if "b1_k" in t:  # 1-bit archive: signs, scales and [.., outliers] entries
+        p.num_1bit = int(t["b1_k"].shape[0])
+        p.outliers_1bit = int(t["b1_k_out"].shape[-1])
+        p.bit_k, p.bit_v = _ptr(t["b1_k"]), _ptr(t["b1_v"])
+        p.bit_k_scale, p.bit_v_scale = _ptr(t["b1_k_scale"]), _ptr(t["b1_v_scale"])
+        p.bit_k_out, p.bit_v_out = _ptr(t["b1_k_out"]), _ptr(t["b1_v_out"])
     return p
 
 
@@ -400,6 +417,14 @@ def atlas_demote_pages(args: AttnArgs, pools: TierPools, src_slots, dst_entries,
     _check(load().atlas_demote_pages(ctypes.byref(args), ctypes.byref(pools), _ptr(src_slots),
                                      _ptr(dst_entries), int(src_slots.numel()), _ptr(rejected)),
            "atlas_demote_pages")
+
+
+def atlas_promote_pages(args: AttnArgs, pools: TierPools, src_entries, dst_blocks,
+                        rejected=None):
+    """Reconstruct the pages of src_entries[i] into hot blocks dst_blocks[i]."""
+    _check(load().atlas_promote_pages(ctypes.byref(args), ctypes.byref(pools), _ptr(src_entries),
+                                      _ptr(dst_blocks), int(src_entries.numel()), _ptr(rejected)),
+           "atlas_promote_pages")
 
 
 def atlas_read_probe(src, out, blocks: int, stream=None):

@@ -246,6 +246,21 @@ atlas_status check_pools(const atlas_tier_pools *t) {
         return fail(ATLAS_EINVAL, "NULL fp8 pool pointer");
     if (t->num_int2 > 0 && (!t->int2_k || !t->int2_v || !t->int2_k_scale || !t->int2_v_scale))
         return fail(ATLAS_EINVAL, "NULL int2 pool pointer");
+    if (t->num_1bit < 0 || t->num_1bit > (1 << 28))
+        return fail(ATLAS_EINVAL, "1-bit pool size %d outside [0, 2^28]", t->num_1bit);
+    if (t->outliers_1bit < 0 || t->outliers_1bit > ATLAS_1BIT_MAX_OUTLIERS)
+        return fail(ATLAS_EINVAL, "outliers_1bit %d outside [0, %d]", t->outliers_1bit,
+                    ATLAS_1BIT_MAX_OUTLIERS);
+    if (t->num_1bit > 0 && (!t->bit_k || !t->bit_v || !t->bit_k_scale || !t->bit_v_scale ||
+                            (t->outliers_1bit > 0 && (!t->bit_k_out || !t->bit_v_out))))
+        return fail(ATLAS_EINVAL, "NULL 1-bit pool pointer");
+    return ok();
+}
+
+// 1-bit blocks index their elements with 16 bits.
+atlas_status check_1bit_block(const atlas_attn_args *a, const atlas_tier_pools *t) {
+    if (t->num_1bit > 0 && (int64_t)a->page_tokens * a->head_dim > 65536)
+        return fail(ATLAS_EUNSUPPORTED, "1-bit pages need page_tokens * head_dim <= 65536");
     return ok();
 }
 
@@ -271,6 +286,17 @@ void set_pools(P &p, const atlas_tier_pools *t) {
     p.n_i4 = t->num_int4;
     p.n_f8 = t->num_fp8;
     p.n_i2 = t->num_int2;
+}
+
+void set_1bit(DecodeParams &p, const atlas_tier_pools *t) {
+    p.b1_k = t->bit_k;
+    p.b1_v = t->bit_v;
+    p.b1_ks = t->bit_k_scale;
+    p.b1_vs = t->bit_v_scale;
+    p.b1_ko = t->bit_k_out;
+    p.b1_vo = t->bit_v_out;
+    p.n_b1 = t->num_1bit;
+    p.b1_nout = t->outliers_1bit;
 }
 
 RowMap row_map(const atlas_attn_args *a) {
@@ -616,12 +642,14 @@ atlas_status atlas_dequant_pages(const atlas_attn_args *args, const atlas_tier_p
     atlas_status st = check_common(args, true, nullptr, &plan);
     if (st != ATLAS_OK) return st;
     if ((st = check_pools(pools)) != ATLAS_OK) return st;
+    if ((st = check_1bit_block(args, pools)) != ATLAS_OK) return st;
     if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
         return fail(ATLAS_EUNSUPPORTED, "tiered hot pages must be F16 or BF16");
     if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
     if (n > 0 && (!entries || !k_out || !v_out)) return fail(ATLAS_EINVAL, "NULL pointer");
     DecodeParams p = decode_params(args, plan);
     set_pools(p, pools);
+    set_1bit(p, pools);
     return device_status(launch_dequant(p, args->kv_dtype, args->head_dim, entries, n, k_out,
                                         v_out, reinterpret_cast<hipStream_t>(args->stream)),
                          "dequant launch");
@@ -736,6 +764,7 @@ atlas_status atlas_demote_pages(const atlas_attn_args *args, const atlas_tier_po
     atlas_status st = check_common(args, true, nullptr, &plan);
     if (st != ATLAS_OK) return st;
     if ((st = check_pools(pools)) != ATLAS_OK) return st;
+    if ((st = check_1bit_block(args, pools)) != ATLAS_OK) return st;
     if (args->kv_dtype != ATLAS_F16 && args->kv_dtype != ATLAS_BF16)
         return fail(ATLAS_EUNSUPPORTED, "hot pages must be F16 or BF16");
     if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
@@ -774,9 +803,52 @@ atlas_status atlas_demote_pages(const atlas_attn_args *args, const atlas_tier_po
     d.n_i4 = pools->num_int4;
     d.n_f8 = pools->num_fp8;
     d.n_i2 = pools->num_int2;
+    d.b1_k = const_cast<uint8_t *>(pools->bit_k);
+    d.b1_v = const_cast<uint8_t *>(pools->bit_v);
+    d.b1_ks = const_cast<float *>(pools->bit_k_scale);
+    d.b1_vs = const_cast<float *>(pools->bit_v_scale);
+    d.b1_ko = const_cast<uint32_t *>(pools->bit_k_out);
+    d.b1_vo = const_cast<uint32_t *>(pools->bit_v_out);
+    d.n_b1 = pools->num_1bit;
+    d.b1_nout = pools->outliers_1bit;
     d.rejected = rejected;
     return device_status(launch_demote(d, reinterpret_cast<hipStream_t>(args->stream)),
                          "demote launch");
+}
+
+atlas_status atlas_promote_pages(const atlas_attn_args *args, const atlas_tier_pools *pools,
+                                 const int32_t *src_entries, const int32_t *dst_blocks, int32_t n,
+                                 int32_t *rejected) {
+    Plan plan;
+    atlas_status st = check_common(args, true, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if ((st = check_pools(pools)) != ATLAS_OK) return st;
+    if ((st = check_1bit_block(args, pools)) != ATLAS_OK) return st;
+    if (args->num_blocks < 1 || !args->k_pool || !args->v_pool)
+        return fail(ATLAS_EINVAL, "promotion needs a hot pool (num_blocks >= 1)");
+    if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
+    if (n == 0) return ok();
+    if (!src_entries || !dst_blocks) return fail(ATLAS_EINVAL, "NULL src_entries or dst_blocks");
+    if ((int64_t)n * args->num_kv_heads * 2 > INT32_MAX) return fail(ATLAS_EINVAL, "n too large");
+    PromoteParams q;
+    std::memset(&q, 0, sizeof(q));
+    q.p.k_pool = args->k_pool;
+    q.p.v_pool = args->v_pool;
+    q.p.num_kv_heads = args->num_kv_heads;
+    q.p.page_tokens = args->page_tokens;
+    q.p.num_blocks = args->num_blocks;
+    set_pools(q.p, pools);
+    set_1bit(q.p, pools);
+    q.k_dst = const_cast<void *>(args->k_pool);
+    q.v_dst = const_cast<void *>(args->v_pool);
+    q.kv_type = args->kv_dtype;
+    q.head_dim = args->head_dim;
+    q.src_entries = src_entries;
+    q.dst_blocks = dst_blocks;
+    q.n = n;
+    q.rejected = rejected;
+    return device_status(launch_promote(q, reinterpret_cast<hipStream_t>(args->stream)),
+                         "promote launch");
 }
 
 }  // extern "C"

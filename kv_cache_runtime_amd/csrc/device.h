@@ -192,7 +192,7 @@ __device__ __forceinline__ bool map_row(const RowMap &m, int row, int &seq, int 
 // softmax does not depend on their order, so a split may visit its pages in
 // this order: the waves then mostly meet pages of one class and take one
 // load path.
-constexpr int kClasses = 6;
+constexpr int kClasses = 6;  // the attended classes, then one bin for every other entry
 __device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, int32_t *s_slot,
                                                     int16_t *s_lp, int (&count)[kClasses]) {
     __shared__ int s_cnt[2][4][kClasses];  // chunk, wave, class
@@ -202,7 +202,7 @@ __device__ __forceinline__ void stage_pages_by_tier(const int32_t *trow, int n, 
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const int i = ch * 256 + tid;
-        t[ch] = i < n ? entry_class((uint32_t)trow[i], slot[ch]) : kClasses;
+        t[ch] = i < n ? min(entry_class((uint32_t)trow[i], slot[ch]), kClasses - 1) : kClasses;
         rank[ch] = 0;
 #pragma unroll
         for (int tt = 0; tt < kClasses; ++tt) {

@@ -214,6 +214,22 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DecodeParams p, int 
             const float vs = p.f8_vs[(int64_t)slot * p.num_kv_heads + g];
             kv = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)p.f8_k[src_row * D + t], false)[0] * ks;
             vv = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)p.f8_v[src_row * D + t], false)[0] * vs;
+        } else if (tier == CLS_B1 && slot < (uint32_t)p.n_b1) {
+            // sign bit -> -scale / +scale, then the outlier entries in order
+            const int64_t blk = (int64_t)slot * p.num_kv_heads + g;
+            const int64_t nb = (int64_t)P * D / 8;
+            const float ks = p.b1_ks[blk], vs = p.b1_vs[blk];
+            kv = ((p.b1_k[blk * nb + t / 8] >> (t & 7)) & 1) ? -ks : ks;
+            vv = ((p.b1_v[blk * nb + t / 8] >> (t & 7)) & 1) ? -vs : vs;
+            const uint32_t *ko = p.b1_ko + blk * p.b1_nout;
+            const uint32_t *vo = p.b1_vo + blk * p.b1_nout;
+            for (int o = 0; o < p.b1_nout; ++o) {
+                const uint32_t a = ko[o], b = vo[o];
+                if ((a & 0xFFFFu) == (uint32_t)t)
+                    kv = (float)__builtin_bit_cast(_Float16, (uint16_t)(a >> 16));
+                if ((b & 0xFFFFu) == (uint32_t)t)
+                    vv = (float)__builtin_bit_cast(_Float16, (uint16_t)(b >> 16));
+            }
         }
         k_out[dst + t] = kv;
         v_out[dst + t] = vv;

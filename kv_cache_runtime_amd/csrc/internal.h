@@ -57,6 +57,10 @@ struct DecodeParams {
     const uint8_t *i2_k, *i2_v;   // INT2 codes, four per byte
     const float *i2_ks, *i2_vs;
     int32_t n_i2;
+    const uint8_t *b1_k, *b1_v;   // 1-bit archive: sign bits, eight per byte
+    const float *b1_ks, *b1_vs;
+    const uint32_t *b1_ko, *b1_vo;  // outliers: index | f16 bits << 16
+    int32_t n_b1, b1_nout;
     // regenerated pages
     uint64_t seed;
     uint32_t layer;
@@ -172,19 +176,38 @@ struct DemoteParams {
     uint8_t *i2_k, *i2_v;
     float *i2_ks, *i2_vs;
     int32_t n_i2;
+    uint8_t *b1_k, *b1_v;
+    float *b1_ks, *b1_vs;
+    uint32_t *b1_ko, *b1_vo;
+    int32_t n_b1, b1_nout;
+    int32_t *rejected;             // device counter or null
+};
+
+// Cold (or hot) pages reconstructed into hot blocks.  `p` describes every
+// source pool (its hot pool pointers are the destination too).
+struct PromoteParams {
+    DecodeParams p;
+    void *k_dst, *v_dst;           // the hot pool, written
+    int32_t kv_type, head_dim;
+    const int32_t *src_entries;    // [n] tiered entries
+    const int32_t *dst_blocks;     // [n] hot block ids
+    int32_t n;
     int32_t *rejected;             // device counter or null
 };
 
 // Classes of a tiered page-table entry: tiers 0-2 as they are, tier 3 split
-// by its kind bits (29-28) into FP8 and INT2; other kinds name no pool.
-enum EntryClass : int { CLS_HOT = 0, CLS_I8 = 1, CLS_I4 = 2, CLS_F8 = 3, CLS_I2 = 4, CLS_BAD = 5 };
+// by its kind bits (29-28) into FP8, INT2 and the 1-bit archive; kind 3
+// names no pool.  Attention reads classes below CLS_B1 only.
+enum EntryClass : int {
+    CLS_HOT = 0, CLS_I8 = 1, CLS_I4 = 2, CLS_F8 = 3, CLS_I2 = 4, CLS_B1 = 5, CLS_BAD = 6
+};
 // Branch-free, so callers can issue several entry loads before decoding any.
 __host__ __device__ inline int entry_class(uint32_t e, uint32_t &slot) {
     const uint32_t tier = e >> 30;
     const uint32_t kind = (e >> 28) & 3u;
     const bool ext = tier == 3u;
     slot = e & (ext ? ((1u << 28) - 1u) : ((1u << 30) - 1u));
-    return ext ? (kind < 2u ? CLS_F8 + (int)kind : CLS_BAD) : (int)tier;
+    return ext ? (kind < 3u ? CLS_F8 + (int)kind : CLS_BAD) : (int)tier;
 }
 
 // Page-table entries a decode workgroup stages in LDS for its split.
@@ -215,6 +238,7 @@ hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *
 hipError_t launch_validate(const ValidateParams &v, hipStream_t stream);
 hipError_t launch_write_kv(const WriteKvParams &w, hipStream_t stream);
 hipError_t launch_demote(const DemoteParams &d, hipStream_t stream);
+hipError_t launch_promote(const PromoteParams &q, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int blocks,
                              hipStream_t stream);
 hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,

@@ -272,6 +272,7 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     uint32_t sslot, slot;
     const int stier = entry_class(se, sslot);
     const int tier = entry_class(de, slot);
+    if (tier == CLS_B1 && d.n_b1 > 0) return;  // archive_kernel's page
     auto in_pool = [&](int cls, uint32_t s) {
         return (cls == CLS_HOT && s < (uint32_t)d.num_blocks) ||
                (cls == CLS_I8 && s < (uint32_t)d.n_i8) || (cls == CLS_I4 && s < (uint32_t)d.n_i4) ||
@@ -285,8 +286,10 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
                                  : (kv ? d.i2_vs : d.i2_ks);
     if (!dst_ok || !src_ok) {
         if (lane == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
-        // a bad source: the page turns its rows into NaN
-        if (dst_ok && lane == 0) sc[(int64_t)slot * d.num_kv_heads + g] = __builtin_nanf("");
+        // a bad source: the page turns its rows into NaN (a 1-bit source is
+        // refused without writing)
+        if (dst_ok && stier != CLS_B1 && lane == 0)
+            sc[(int64_t)slot * d.num_kv_heads + g] = __builtin_nanf("");
         return;
     }
     const int64_t n = (int64_t)d.page_tokens * d.head_dim;  // multiple of 8
@@ -322,6 +325,314 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
     dispatch_block<R>(stier, tier, src, n / 8, i8, i4, i2, sdst, lane);
 }
 
+// ---- 1-bit archive (sign bits, mean-|x| scale, FP16 outliers) -------------
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Sum of v over the lanes below this one.
+__device__ inline int wave_excl_scan(const int v, const int lane) {
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(x, d);
+        if (lane >= d) x += t;
+    }
+    return x - v;
+}
+
+__device__ inline uint32_t mag_key(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// Encodes one block into the 1-bit format (one wave).  The outlier
+// threshold T is the k-th largest magnitude key, found bit by bit from the
+// top (31 counting passes); elements above T are outliers, and of those
+// equal to T the lowest-indexed ones fill the remaining places.  Chunks of
+// the first R rounds stay in registers; later ones are read again per pass.
+template <int R, int ST>
+__device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *signs,
+                              float *scale_out, uint32_t *outs, const int kout, const int lane) {
+    const int64_t n = nch * 8;
+    const int k = (int)min((int64_t)kout, n);
+    const int rounds = (int)((nch + 63) / 64);
+    uint4 keep[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t ch = lane + 64 * j;
+        keep[j] = ch < nch ? load_chunk<ST>(src, ch) : make_uint4(0, 0, 0, 0);
+    }
+    // fn(chunk bits, round, valid) for every round of this lane, in order
+    auto for_each_chunk = [&](auto &&fn) {
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            if (j < rounds) fn(keep[j], j, lane + 64 * j < nch);
+        for (int r = R; r < rounds; ++r) {
+            const int64_t ch = lane + 64 * (int64_t)r;
+            fn(ch < nch ? load_chunk<ST>(src, ch) : make_uint4(0, 0, 0, 0), r, ch < nch);
+        }
+    };
+
+    uint32_t T = 0;
+    int need = 0;
+    if (k > 0) {
+        for (int b = 30; b >= 0; --b) {
+            const uint32_t cand = T | (1u << b);
+            int cnt = 0;
+            for_each_chunk([&](const uint4 w, int, bool valid) {
+                float x[8];
+                widen8<ST>(src, w, x);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cnt += (valid && mag_key(x[j]) >= cand) ? 1 : 0;
+            });
+            if (wave_sum(cnt) >= k) T = cand;
+        }
+        int gt = 0;
+        for_each_chunk([&](const uint4 w, int, bool valid) {
+            float x[8];
+            widen8<ST>(src, w, x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) gt += (valid && mag_key(x[j]) > T) ? 1 : 0;
+        });
+        need = k - wave_sum(gt);  // >= 1 elements equal to T are kept
+    }
+
+    int eq_base = 0, out_base = 0;
+    double sum = 0.0;
+    for_each_chunk([&](const uint4 w, int r, bool valid) {
+        float x[8];
+        widen8<ST>(src, w, x);
+        const int64_t ch = lane + 64 * (int64_t)r;
+        int eqc = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) eqc += (k > 0 && valid && mag_key(x[j]) == T) ? 1 : 0;
+        const int eq_pre = wave_excl_scan(eqc, lane);
+        int rank = eq_base + eq_pre;
+        eq_base += __shfl(eq_pre + eqc, 63);
+        bool is_out[8];
+        int oc = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t kj = mag_key(x[j]);
+            const bool tie = k > 0 && valid && kj == T;
+            is_out[j] = k > 0 && valid && (kj > T || (tie && rank < need));
+            rank += tie ? 1 : 0;
+            oc += is_out[j] ? 1 : 0;
+        }
+        const int o_pre = wave_excl_scan(oc, lane);
+        int pos = out_base + o_pre;
+        out_base += __shfl(o_pre + oc, 63);
+        uint32_t byte = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (is_out[j]) {
+                const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)x[j]);
+                outs[pos++] = (uint32_t)(ch * 8 + j) | ((uint32_t)h << 16);
+            } else if (valid) {
+                sum += (double)fabsf(x[j]);
+            }
+            byte |= (x[j] < 0.0f ? 1u : 0u) << j;
+        }
+        if (valid) signs[ch] = (uint8_t)byte;
+    });
+    sum = wave_sum(sum);
+    const int64_t m = n - k;
+    if (lane == 0) *scale_out = m > 0 ? (float)(sum / (double)m) : 0.0f;
+}
+
+// One wave per (page i, kv head g, K or V) block whose destination is a
+// 1-bit entry; every other page is demote_kernel's.
+template <int R>
+__global__ __launch_bounds__(256) void archive_kernel(const DemoteParams d) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= (int64_t)d.n * d.num_kv_heads * 2) return;
+    const int kv = (int)(unit & 1);
+    const int g = (int)((unit >> 1) % d.num_kv_heads);
+    const int i = (int)((unit >> 1) / d.num_kv_heads);
+    const uint32_t se = (uint32_t)d.src_slots[i];
+    const uint32_t de = (uint32_t)d.dst_entries[i];
+    uint32_t sslot, slot;
+    const int stier = entry_class(se, sslot);
+    const int tier = entry_class(de, slot);
+    if (tier != CLS_B1) return;
+    const bool dst_ok = slot < (uint32_t)d.n_b1;
+    const bool src_ok = (stier == CLS_HOT && sslot < (uint32_t)d.num_blocks) ||
+                        (stier == CLS_I8 && sslot < (uint32_t)d.n_i8) ||
+                        (stier == CLS_I4 && sslot < (uint32_t)d.n_i4) ||
+                        (stier == CLS_F8 && sslot < (uint32_t)d.n_f8) ||
+                        (stier == CLS_I2 && sslot < (uint32_t)d.n_i2);
+    const int64_t dblk = (int64_t)slot * d.num_kv_heads + g;
+    float *sdst = (kv ? d.b1_vs : d.b1_ks) + dblk;
+    if (!dst_ok || !src_ok) {
+        if (lane == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
+        if (dst_ok && stier != CLS_B1 && lane == 0) *sdst = __builtin_nanf("");
+        return;
+    }
+    const int64_t n = (int64_t)d.page_tokens * d.head_dim;
+    const int64_t sblk = (int64_t)sslot * d.num_kv_heads + g;
+    DemoteSrc src;
+    src.bf16 = d.kv_type == KV_BF16;
+    src.scale = 1.0f;
+    if (stier == CLS_HOT) {
+        src.base = reinterpret_cast<const uint8_t *>(kv ? d.v_pool : d.k_pool) + sblk * n * 2;
+    } else if (stier == CLS_I8) {
+        src.base = reinterpret_cast<const uint8_t *>(kv ? d.i8_v : d.i8_k) + sblk * n;
+        src.scale = (kv ? d.i8_vs : d.i8_ks)[sblk];
+    } else if (stier == CLS_I4) {
+        src.base = (kv ? d.i4_v : d.i4_k) + sblk * (n / 2);
+        src.scale = (kv ? d.i4_vs : d.i4_ks)[sblk];
+    } else if (stier == CLS_I2) {
+        src.base = (kv ? d.i2_v : d.i2_k) + sblk * (n / 4);
+        src.scale = (kv ? d.i2_vs : d.i2_ks)[sblk];
+    } else {
+        src.base = (kv ? d.f8_v : d.f8_k) + sblk * n;
+        src.scale = (kv ? d.f8_vs : d.f8_ks)[sblk];
+    }
+    uint8_t *signs = (kv ? d.b1_v : d.b1_k) + dblk * (n / 8);
+    uint32_t *outs = (kv ? d.b1_vo : d.b1_ko) + dblk * d.b1_nout;
+    switch (stier) {
+        case CLS_HOT: archive_block<R, CLS_HOT>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
+        case CLS_I8: archive_block<R, CLS_I8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
+        case CLS_I4: archive_block<R, CLS_I4>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
+        case CLS_F8: archive_block<R, CLS_F8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
+        default: archive_block<R, CLS_I2>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
+    }
+}
+
+// ---- reconstruction of pages into hot blocks --------------------------------
+
+// Stores the 8 values of chunk ch of a hot block as kv_type (round to
+// nearest even).
+__device__ inline void store_hot8(void *dst, int64_t ch, int kv_type, const float (&x)[8]) {
+    if (kv_type == KV_F32) {
+        float4 *o = reinterpret_cast<float4 *>(dst) + 2 * ch;
+        o[0] = make_float4(x[0], x[1], x[2], x[3]);
+        o[1] = make_float4(x[4], x[5], x[6], x[7]);
+        return;
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint16_t a, b;
+        if (kv_type == KV_BF16) {
+            a = __builtin_bit_cast(uint16_t, (__bf16)x[2 * j]);
+            b = __builtin_bit_cast(uint16_t, (__bf16)x[2 * j + 1]);
+        } else {
+            a = __builtin_bit_cast(uint16_t, (_Float16)x[2 * j]);
+            b = __builtin_bit_cast(uint16_t, (_Float16)x[2 * j + 1]);
+        }
+        w[j] = (uint32_t)a | ((uint32_t)b << 16);
+    }
+    reinterpret_cast<uint4 *>(dst)[ch] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int ST>
+__device__ void promote_codes(const DemoteSrc &src, int64_t nch, void *dst, int kv_type, int lane) {
+    for (int64_t ch = lane; ch < nch; ch += 64) {
+        float x[8];
+        widen8<ST>(src, load_chunk<ST>(src, ch), x);
+        store_hot8(dst, ch, kv_type, x);
+    }
+}
+
+// One wave per (page i, kv head g, K or V) block.
+__global__ __launch_bounds__(256) void promote_kernel(const PromoteParams q) {
+    const DecodeParams &p = q.p;
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= (int64_t)q.n * p.num_kv_heads * 2) return;
+    const int kv = (int)(unit & 1);
+    const int g = (int)((unit >> 1) % p.num_kv_heads);
+    const int i = (int)((unit >> 1) / p.num_kv_heads);
+    const uint32_t se = (uint32_t)q.src_entries[i];
+    const int32_t db = q.dst_blocks[i];
+    uint32_t slot;
+    const int cls = entry_class(se, slot);
+    const bool dst_ok = db >= 0 && db < p.num_blocks;
+    const bool src_ok = (cls == CLS_HOT && slot < (uint32_t)p.num_blocks) ||
+                        (cls == CLS_I8 && slot < (uint32_t)p.n_i8) ||
+                        (cls == CLS_I4 && slot < (uint32_t)p.n_i4) ||
+                        (cls == CLS_F8 && slot < (uint32_t)p.n_f8) ||
+                        (cls == CLS_I2 && slot < (uint32_t)p.n_i2) ||
+                        (cls == CLS_B1 && slot < (uint32_t)p.n_b1);
+    if (!dst_ok || !src_ok) {
+        if (lane == 0 && g == 0 && kv == 0 && q.rejected) atomicAdd(q.rejected, 1);
+        if (!dst_ok) return;
+    }
+    const int64_t n = (int64_t)p.page_tokens * q.head_dim;  // multiple of 8
+    const int64_t nch = n / 8;
+    const int eb = q.kv_type == KV_F32 ? 4 : 2;
+    void *dst = reinterpret_cast<uint8_t *>(kv ? q.v_dst : q.k_dst) +
+                ((int64_t)db * p.num_kv_heads + g) * n * eb;
+    if (!src_ok) {  // a NaN block, so that rows reading it fail loudly
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = __builtin_nanf("");
+        for (int64_t ch = lane; ch < nch; ch += 64) store_hot8(dst, ch, q.kv_type, x);
+        return;
+    }
+    const int64_t sblk = (int64_t)slot * p.num_kv_heads + g;
+    if (cls == CLS_HOT) {  // a copy
+        const uint4 *s4 = reinterpret_cast<const uint4 *>(
+            reinterpret_cast<const uint8_t *>(kv ? p.v_pool : p.k_pool) + sblk * n * eb);
+        uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+        for (int64_t c = lane; c < n * eb / 16; c += 64) d4[c] = s4[c];
+        return;
+    }
+    if (cls == CLS_B1) {
+        const uint8_t *signs = (kv ? p.b1_v : p.b1_k) + sblk * nch;
+        const float sc = (kv ? p.b1_vs : p.b1_ks)[sblk];
+        const uint32_t *outs = (kv ? p.b1_vo : p.b1_ko) + sblk * p.b1_nout;
+        // lane l holds outlier entry l; entries are applied in list order
+        const uint32_t mine = lane < p.b1_nout ? outs[lane] : 0xFFFFu;
+        for (int64_t r = 0; 64 * r < nch; ++r) {
+            const int64_t ch = lane + 64 * r;
+            const uint32_t byte = ch < nch ? signs[ch] : 0u;
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = ((byte >> j) & 1u) ? -sc : sc;
+            for (int o = 0; o < p.b1_nout; ++o) {
+                const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)mine, o);
+                const uint32_t idx = e & 0xFFFFu;
+                if ((int64_t)(idx >> 3) < 64 * r || (int64_t)(idx >> 3) >= 64 * (r + 1)) continue;
+                const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
+                const bool hit = (int64_t)(idx >> 3) == ch;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = (hit && (int)(idx & 7u) == j) ? v : x[j];
+            }
+            if (ch < nch) store_hot8(dst, ch, q.kv_type, x);
+        }
+        return;
+    }
+    DemoteSrc src;
+    src.bf16 = false;
+    if (cls == CLS_I8) {
+        src.base = reinterpret_cast<const uint8_t *>(kv ? p.i8_v : p.i8_k) + sblk * n;
+        src.scale = (kv ? p.i8_vs : p.i8_ks)[sblk];
+        promote_codes<CLS_I8>(src, nch, dst, q.kv_type, lane);
+    } else if (cls == CLS_I4) {
+        src.base = (kv ? p.i4_v : p.i4_k) + sblk * (n / 2);
+        src.scale = (kv ? p.i4_vs : p.i4_ks)[sblk];
+        promote_codes<CLS_I4>(src, nch, dst, q.kv_type, lane);
+    } else if (cls == CLS_F8) {
+        src.base = (kv ? p.f8_v : p.f8_k) + sblk * n;
+        src.scale = (kv ? p.f8_vs : p.f8_ks)[sblk];
+        promote_codes<CLS_F8>(src, nch, dst, q.kv_type, lane);
+    } else {
+        src.base = (kv ? p.i2_v : p.i2_k) + sblk * (n / 4);
+        src.scale = (kv ? p.i2_vs : p.i2_ks)[sblk];
+        promote_codes<CLS_I2>(src, nch, dst, q.kv_type, lane);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_write_kv(const WriteKvParams &w, hipStream_t stream) {
@@ -337,6 +648,19 @@ hipError_t launch_demote(const DemoteParams &d, hipStream_t stream) {
     if (waves <= 0) return hipSuccess;
     hipLaunchKernelGGL(demote_kernel<4>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
                        d);
+    if (d.n_b1 > 0) {  // pages bound for the 1-bit archive
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(archive_kernel<4>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                           stream, d);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_promote(const PromoteParams &q, hipStream_t stream) {
+    const int64_t waves = (int64_t)q.n * q.p.num_kv_heads * 2;  // one per block
+    if (waves <= 0) return hipSuccess;
+    hipLaunchKernelGGL(promote_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, q);
     return hipGetLastError();
 }
 

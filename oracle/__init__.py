@@ -16,6 +16,7 @@ from .oracle import (  # noqa: F401
     encode_1bit,
     entry_class,
     f16_bits,
+    hot_bits,
     fp8_e4m3_encode,
     fp8_e4m3_value,
     int2_codes,

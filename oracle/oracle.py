@@ -380,11 +380,25 @@ def decode_1bit(signs: np.ndarray, scale, outliers: np.ndarray, n: int) -> np.nd
     bits = np.unpackbits(np.asarray(signs, dtype=np.uint8), bitorder="little")[:n]
     sc = np.float32(scale)
     out = np.where(bits == 1, -sc, sc).astype(np.float32)
-    for e in np.asarray(outliers, dtype=np.uint32).ravel():
+    for e in np.asarray(outliers).astype(np.int64).ravel() & 0xFFFFFFFF:  # uint32 bits
         i = int(e) & 0xFFFF
         if i < n:
             out[i] = np.float32(np.uint16(int(e) >> 16).view(np.float16))
     return out
+
+
+def hot_bits(x, kind: str) -> np.ndarray:
+    """Bits of f32 values x stored in a hot pool of element type kind ("f32",
+    "f16" or "bf16"), rounded to nearest even: what reconstructing a page
+    into a hot block writes.  bf16 rounding goes through round_bf16 (normal
+    range, which is all it is fed here)."""
+    x = np.asarray(x, dtype=np.float32)
+    if kind == "f32":
+        return x.view(np.uint32)
+    if kind == "f16":
+        return f16_bits(x)
+    r = round_bf16(x.astype(np.float64)).astype(np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def pack_int4(codes: np.ndarray) -> np.ndarray:

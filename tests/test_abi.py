@@ -57,7 +57,7 @@ def test_struct_layouts_match_c(tmp_path):
 
 
 def test_abi_version_and_status_strings():
-    assert atlas.atlas_abi_version() == 2
+    assert atlas.atlas_abi_version() == 3
     assert atlas.atlas_status_string(0) == "ok"
     assert atlas.atlas_status_string(3).startswith("workspace")
     assert atlas.atlas_status_string(99) == "unknown status"
@@ -260,6 +260,48 @@ def test_write_and_demote_arguments_are_checked():
                                 ctypes.byref(pools), FAKE, FAKE, 1, None) == atlas.EUNSUPPORTED
     assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), None, None, 0,
                                 None) == atlas.OK   # nothing to do
+    # 1-bit archive: pointers, outlier count and the 16-bit element index
+    pools.num_1bit = 2
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    assert "1-bit" in atlas.atlas_last_error()
+    pools.bit_k = pools.bit_v = pools.bit_k_scale = pools.bit_v_scale = FAKE
+    pools.outliers_1bit = 65
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    pools.outliers_1bit = 4  # outlier pointers missing
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    pools.bit_k_out = pools.bit_v_out = FAKE
+    big = _args(kv_dtype=atlas.F16, head_dim=128, page_tokens=1024, max_pages_per_seq=4)
+    assert L.atlas_demote_pages(ctypes.byref(big), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EUNSUPPORTED
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), None, None, 0,
+                                None) == atlas.OK
+    pools.num_1bit = -1
+    assert L.atlas_demote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                None) == atlas.EINVAL
+    pools.num_1bit = 0
+
+
+def test_promote_arguments_are_checked():
+    L = atlas.load()
+    pools = atlas.TierPools()
+    pools.struct_size = ctypes.sizeof(atlas.TierPools)
+    f16 = _args(kv_dtype=atlas.F16)
+    assert L.atlas_promote_pages(ctypes.byref(f16), None, FAKE, FAKE, 1, None) == atlas.EINVAL
+    assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, -1,
+                                 None) == atlas.EINVAL
+    assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), None, FAKE, 1,
+                                 None) == atlas.EINVAL
+    assert L.atlas_promote_pages(ctypes.byref(_args(kv_dtype=atlas.F16, num_blocks=0)),
+                                 ctypes.byref(pools), FAKE, FAKE, 1, None) == atlas.EINVAL
+    pools.num_int8 = 1  # int8 pointers missing
+    assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
+                                 None) == atlas.EINVAL
+    pools.num_int8 = 0
+    assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), None, None, 0,
+                                 None) == atlas.OK
 
 
 def test_positional_policy_arguments_are_checked():

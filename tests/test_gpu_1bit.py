@@ -1,0 +1,237 @@
+"""GPU parity of the 1-bit archival tier (the extension tier, kind 2) and of
+page reconstruction (atlas_promote_pages) through the C ABI.
+
+Archiving: sign bits and outlier entries bit-exact against the oracle's
+encoder, the scale within one f32 ulp (the device sums |x| in f64 in its own
+order; the oracle's sum is exact to f64 rounding, then both round the mean to
+f32).  Promotion of every class into hot blocks: bit-exact against the
+oracle's values rounded to the hot type.  Attention and the validator refuse
+1-bit entries (NaN rows, counted)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from kv_cache_runtime_amd import atlas
+from tests.test_gpu_parity import check, run
+
+pytestmark = pytest.mark.gpu
+
+B1 = (3 << 30) | (2 << 28)
+KIND3 = (3 << 30) | (3 << 28)
+
+
+def _case(gpu, hot="f16", Hkv=2, P=16, D=128, ctx=(900, 1700), seed=41, H=None):
+    return synth.build(dict(num_seqs=len(ctx), context_lens=list(ctx), num_heads=H or 8 * Hkv,
+                            num_kv_heads=Hkv, head_dim=D, page_tokens=P, q_dtype="bf16",
+                            kv_dtype=hot, placement="permuted",
+                            tiers=dict(hot_tokens=max(ctx) // 2, p_int8=0.3, p_fp8=0.2,
+                                       p_int2=0.2)),
+                       device=gpu, seed=seed, name=f"1bit-{hot}-P{P}-D{D}")
+
+
+def _add_b1_pool(w, n, n_out, gpu):
+    Hkv, P, D = w.num_kv_heads, w.page_tokens, w.head_dim
+    for kv in ("k", "v"):
+        w.tiers[f"b1_{kv}"] = torch.full((n, Hkv, P * D // 8), 0xAA, dtype=torch.uint8, device=gpu)
+        w.tiers[f"b1_{kv}_scale"] = torch.full((n, Hkv), -1.0, device=gpu)
+        w.tiers[f"b1_{kv}_out"] = torch.full((n, Hkv, n_out), -1, dtype=torch.int32, device=gpu)
+
+
+def _full_pages_by_class(w, per_class=2):
+    """(seq, page, entry) of full pages, up to per_class of each class 0-4."""
+    picked = {c: [] for c in range(5)}
+    for s in range(w.num_seqs):
+        full = int(w.context_lens[s]) // w.page_tokens
+        for p in range(full):
+            e = int(w.page_table[s, p]) & 0xFFFFFFFF
+            c = oracle.entry_class(e)[0]
+            if c < 5 and len(picked[c]) < per_class:
+                picked[c].append((s, p, e))
+    return [x for c in range(5) for x in picked[c]]
+
+
+def _scale_close(got, want):
+    want = np.float32(want)
+    return got == want or abs(np.float64(got) - np.float64(want)) <= np.spacing(np.abs(want))
+
+
+@pytest.mark.parametrize("hot,P,D,n_out", [("f16", 16, 128, 8), ("bf16", 16, 128, 64),
+                                           ("f16", 64, 128, 64), ("bf16", 16, 64, 0),
+                                           ("f16", 256, 64, 16)])
+def test_archive_matches_oracle(gpu, hot, P, D, n_out):
+    w = _case(gpu, hot=hot, P=P, D=D, ctx=(1300, 2700), seed=P + D + n_out)
+    pages = _full_pages_by_class(w)
+    classes = {oracle.entry_class(e)[0] for _, _, e in pages}
+    assert 0 in classes and len(classes) >= (5 if P == 16 else 2), classes
+    n = len(pages)
+    _add_b1_pool(w, n, n_out, gpu)
+    src_np = np.array([e for _, _, e in pages], dtype=np.uint32)
+    dst_np = np.array([B1 | i for i in range(n)], dtype=np.uint32)
+    host = oracle.HostView(w)
+    want = {}
+    for i, e in enumerate(src_np):
+        for kv in ("k", "v"):
+            for g in range(w.num_kv_heads):
+                want[(i, kv, g)] = oracle.encode_1bit(
+                    oracle.block_f32(w, int(e), g, kv, host=host).ravel(), n_out)
+    prob = atlas.Problem(w)
+    rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+    print(f"[archive {hot} P{P} D{D} K{n_out}] {n} pages", flush=True)
+    atlas.atlas_demote_pages(prob.args, prob.tiers,
+                             torch.from_numpy(src_np.view(np.int32)).to(gpu),
+                             torch.from_numpy(dst_np.view(np.int32)).to(gpu), rej)
+    torch.cuda.synchronize()
+    assert int(rej) == 0
+    for kv in ("k", "v"):
+        signs = w.tiers[f"b1_{kv}"].cpu().numpy()
+        scales = w.tiers[f"b1_{kv}_scale"].cpu().numpy()
+        outs = w.tiers[f"b1_{kv}_out"].cpu().numpy().view(np.uint32)
+        for i in range(n):
+            for g in range(w.num_kv_heads):
+                ws, wscale, wout = want[(i, kv, g)]
+                assert np.array_equal(signs[i, g], ws), (i, kv, g)
+                assert np.array_equal(outs[i, g], wout), (i, kv, g)
+                assert _scale_close(scales[i, g], wscale), (i, kv, g, scales[i, g], wscale)
+
+
+def _oracle_b1_pool(w, n, n_out, gpu, seed):
+    """A 1-bit pool written on the host by the oracle's encoder from seeded
+    blocks (normal values with a few large outliers and some exact ties)."""
+    rng = np.random.default_rng(seed)
+    Hkv, P, D = w.num_kv_heads, w.page_tokens, w.head_dim
+    for kv in ("k", "v"):
+        signs = np.zeros((n, Hkv, P * D // 8), np.uint8)
+        scales = np.zeros((n, Hkv), np.float32)
+        outs = np.zeros((n, Hkv, n_out), np.uint32)
+        for i in range(n):
+            for g in range(Hkv):
+                x = rng.standard_normal(P * D).astype(np.float16).astype(np.float32)
+                x[rng.integers(0, P * D, 12)] *= 40
+                x[rng.integers(0, P * D, 30)] = 0.5
+                signs[i, g], scales[i, g], outs[i, g] = oracle.encode_1bit(x, n_out)
+        w.tiers[f"b1_{kv}"] = torch.from_numpy(signs).to(gpu)
+        w.tiers[f"b1_{kv}_scale"] = torch.from_numpy(scales).to(gpu)
+        w.tiers[f"b1_{kv}_out"] = torch.from_numpy(outs.view(np.int32)).to(gpu)
+
+
+def _with_spare_blocks(w, extra):
+    """Appends `extra` blocks (zeros) to the hot pool; returns their ids."""
+    nb = w.num_blocks
+    z = torch.zeros((extra,) + tuple(w.k_pool.shape[1:]), dtype=w.k_pool.dtype,
+                    device=w.k_pool.device)
+    w.k_pool = torch.cat([w.k_pool, z]).contiguous()
+    w.v_pool = torch.cat([w.v_pool, z]).contiguous()
+    return list(range(nb, nb + extra))
+
+
+@pytest.mark.parametrize("hot", ["f16", "bf16"])
+def test_promote_every_class_bit_exact(gpu, hot):
+    w = _case(gpu, hot=hot, seed=17)
+    n_out = 16
+    _oracle_b1_pool(w, 3, n_out, gpu, seed=5)
+    pages = [e for _, _, e in _full_pages_by_class(w)] + [B1 | 0, B1 | 2]
+    dst = _with_spare_blocks(w, len(pages))
+    host = oracle.HostView(w)
+    want = {(i, kv, g): oracle.hot_bits(oracle.block_f32(w, e, g, kv, host=host), hot)
+            for i, e in enumerate(pages) for kv in ("k", "v") for g in range(w.num_kv_heads)}
+    prob = atlas.Problem(w)
+    rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+    src = torch.from_numpy(np.array(pages, dtype=np.uint32).view(np.int32)).to(gpu)
+    atlas.atlas_promote_pages(prob.args, prob.tiers, src,
+                              torch.tensor(dst, dtype=torch.int32, device=gpu), rej)
+    torch.cuda.synchronize()
+    assert int(rej) == 0
+    for kv, pool in (("k", w.k_pool), ("v", w.v_pool)):
+        got = pool.cpu().view(torch.int16).numpy().view(np.uint16)
+        for i, b in enumerate(dst):
+            for g in range(w.num_kv_heads):
+                assert np.array_equal(got[b, g], want[(i, kv, g)]), (i, kv, g)
+
+
+def test_promote_rejections(gpu):
+    w = _case(gpu, seed=23)
+    _oracle_b1_pool(w, 1, 4, gpu, seed=1)
+    dst = _with_spare_blocks(w, 3)
+    before = w.k_pool[dst[2]].clone()
+    prob = atlas.Problem(w)
+    n_b1 = w.tiers["b1_k"].shape[0]
+    src = np.array([B1 | n_b1, KIND3 | 0, B1 | 0], dtype=np.uint32)  # past the pool, kind 3, ok
+    blocks = [dst[0], dst[1], w.num_blocks]  # the last names no block
+    rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+    atlas.atlas_promote_pages(prob.args, prob.tiers, torch.from_numpy(src.view(np.int32)).to(gpu),
+                              torch.tensor(blocks, dtype=torch.int32, device=gpu), rej)
+    torch.cuda.synchronize()
+    assert int(rej) == 3
+    assert torch.isnan(w.k_pool[dst[0]].float()).all() and torch.isnan(w.v_pool[dst[1]].float()).all()
+    assert torch.equal(w.k_pool[dst[2]], before)
+
+
+def test_dequant_1bit_bit_exact(gpu):
+    w = _case(gpu, seed=31)
+    _oracle_b1_pool(w, 4, 64, gpu, seed=9)
+    prob = atlas.Problem(w)
+    ent = np.array([B1 | i for i in range(4)], dtype=np.uint32)
+    k = torch.empty((4, w.num_kv_heads, w.page_tokens, w.head_dim), device=gpu)
+    v = torch.empty_like(k)
+    atlas.atlas_dequant_pages(prob.args, prob.tiers, torch.from_numpy(ent.view(np.int32)).to(gpu),
+                              k, v)
+    torch.cuda.synchronize()
+    host = oracle.HostView(w)
+    for i, e in enumerate(ent):
+        for got, kv in ((k[i], "k"), (v[i], "v")):
+            want = np.stack([oracle.block_f32(w, int(e), g, kv, host=host)
+                             for g in range(w.num_kv_heads)])
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32)), i
+
+
+@pytest.mark.parametrize("kernel", ["default", "valu"])
+def test_attention_refuses_1bit_entries(gpu, monkeypatch, kernel):
+    if kernel == "valu":
+        monkeypatch.setenv("ATLAS_DECODE_VALU", "1")
+    w = _case(gpu, seed=47)
+    _oracle_b1_pool(w, 2, 8, gpu, seed=2)
+    prob = atlas.Problem(w)
+    assert prob.validate() == [0, 0, 0, 0]
+    prob.table[0, 3] = int(np.uint32(B1 | 1).view(np.int32))
+    assert prob.validate()[0] == 1
+    out, lse = prob.run()
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.isfinite(out[1]).all()
+
+
+@pytest.mark.parametrize("hot", ["f16", "bf16"])
+def test_archive_then_promote_then_attend(gpu, hot):
+    """The ARGUS loop for deep-cold pages: archive hot and cold pages into
+    1-bit slots, reconstruct them into hot blocks, attend.  Reconstruction is
+    bit-exact against the oracle's decoding of the archived bytes, and the
+    attention over the reconstructed pages matches the oracle."""
+    w = _case(gpu, hot=hot, ctx=(1100, 2300), seed=53)
+    pages = _full_pages_by_class(w, per_class=3)
+    n = len(pages)
+    _add_b1_pool(w, n, 16, gpu)
+    dst = _with_spare_blocks(w, n)
+    prob = atlas.Problem(w)
+    rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+    src = torch.from_numpy(np.array([e for _, _, e in pages], np.uint32).view(np.int32)).to(gpu)
+    b1 = torch.from_numpy(np.array([B1 | i for i in range(n)], np.uint32).view(np.int32)).to(gpu)
+    atlas.atlas_demote_pages(prob.args, prob.tiers, src, b1, rej)
+    atlas.atlas_promote_pages(prob.args, prob.tiers, b1,
+                              torch.tensor(dst, dtype=torch.int32, device=gpu), rej)
+    torch.cuda.synchronize()
+    assert int(rej) == 0
+    host = oracle.HostView(w)
+    for i in range(n):
+        for kv, pool in (("k", w.k_pool), ("v", w.v_pool)):
+            for g in range(w.num_kv_heads):
+                want = oracle.hot_bits(oracle.block_f32(w, B1 | i, g, kv, host=host), hot)
+                got = pool[dst[i], g].cpu().view(torch.int16).numpy().view(np.uint16)
+                assert np.array_equal(got, want), (i, kv, g)
+    table = w.page_table.copy()
+    for i, (s, p, _) in enumerate(pages):
+        table[s, p] = dst[i]
+    w.page_table = table
+    out, lse = run(w)
+    check(w, out, lse)

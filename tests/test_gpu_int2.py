@@ -119,7 +119,7 @@ def test_validate_counts_unknown_kinds_and_bad_int2_slots(gpu):
     w.tiers["i2_k_scale"][slot, 3] = float("nan")
     assert prob.validate(check_values=True) == [0, 0, 0, 1]
     prob.table[s, p] = int(np.uint32(I2 | w.tiers["i2_k"].shape[0]).view(np.int32))
-    prob.table[1 - s, 0] = int(np.uint32((3 << 30) | (2 << 28)).view(np.int32))  # kind 2
+    prob.table[1 - s, 0] = int(np.uint32((3 << 30) | (3 << 28)).view(np.int32))  # kind 3
     assert prob.validate()[0] == 2
     out, lse = prob.run()
     torch.cuda.synchronize()

@@ -853,3 +853,13 @@ def test_1bit_special_cases():
 def test_entry_classes_with_archival_kind():
     assert oracle.entry_class((3 << 30) | (2 << 28) | 5) == (5, 5)
     assert oracle.entry_class((3 << 30) | (3 << 28) | 5)[0] == 6
+
+
+def test_hot_bits_rounds_to_nearest_even():
+    # 1 + 2^-11 is halfway between two f16 values: ties to even (1.0); 1 +
+    # 3 * 2^-11 rounds up to 1 + 2^-9; bf16 keeps 8 significant bits
+    x = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -2.5], np.float32)
+    assert oracle.hot_bits(x, "f16").tolist() == [0x3C00, 0x3C02, 0xC100]
+    y = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -2.5], np.float32)
+    assert oracle.hot_bits(y, "bf16").tolist() == [0x3F80, 0x3F82, 0xC020]
+    assert oracle.hot_bits(np.float32(1.5), "f32").tolist() == 0x3FC00000
