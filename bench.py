@@ -226,17 +226,18 @@ def demote_plan(w, seed: int = 7):
 
 def write_path(args, torch, dev):
     """Time the KV write path: atlas_write_kv (a chunk's new K/V rows into
-    their pages) or atlas_demote_pages (hot pages encoded into int8 / int4),
-    each against its HBM roofline, with the oracle's encoder timed on the host
-    for demotion."""
+    their pages), atlas_demote_pages (hot pages encoded into int8 / int4, or
+    into the 1-bit archive) or atlas_promote_pages (archived pages rebuilt
+    into hot blocks), each against its HBM roofline, with the oracle's encoder
+    or decoder timed on the host.""" 
     import numpy as np
 
     import synth
     from kv_cache_runtime_amd import atlas
 
     w = synth.config(args.config, device=dev, seed=42)
-    if w.kv_dtype not in ("bf16", "f16") and args.op == "demote":
-        sys.exit("demote needs a bf16 or f16 hot pool (configs 3 and 5)")
+    if w.kv_dtype not in ("bf16", "f16") and args.op != "write_kv":
+        sys.exit(f"{args.op} needs a bf16 or f16 hot pool (configs 3 and 5)")
     prob = atlas.Problem(w)
     D, Hkv, P = w.head_dim, w.num_kv_heads, w.page_tokens
     eb = w.k_pool.element_size()
@@ -252,6 +253,34 @@ def write_path(args, torch, dev):
             atlas.atlas_write_kv(prob.args, k_new, v_new)
         sample = None
         kernel = "write_kv_kernel"
+    elif args.op in ("archive", "promote"):
+        src, _, _, _ = demote_plan(w)
+        n, K = len(src), args.outliers
+        tiers = {}
+        for kv in ("k", "v"):
+            for t8 in ("i8", "i4"):
+                tiers[f"{t8}_{kv}"] = torch.empty((0,), dtype=torch.uint8, device=dev)
+                tiers[f"{t8}_{kv}_scale"] = torch.empty((0,), dtype=torch.float32, device=dev)
+            tiers[f"b1_{kv}"] = torch.empty((n, Hkv, P * D // 8), dtype=torch.uint8, device=dev)
+            tiers[f"b1_{kv}_scale"] = torch.empty((n, Hkv), dtype=torch.float32, device=dev)
+            tiers[f"b1_{kv}_out"] = torch.empty((n, Hkv, K), dtype=torch.int32, device=dev)
+        pools = atlas.make_tiers(tiers)
+        src_t = torch.from_numpy(src).to(dev)
+        b1_t = torch.from_numpy((np.arange(n, dtype=np.int64) | (0xE << 28)).astype(np.uint32)
+                                .view(np.int32)).to(dev)
+        rejected = torch.zeros(1, dtype=torch.int32, device=dev)
+        units = n * Hkv
+        per_unit = 2 * (P * D * eb + P * D // 8 + 4 + 4 * K)  # K and V: hot + archived bytes
+        atlas.atlas_demote_pages(prob.args, pools, src_t, b1_t, rejected)  # fills the archive
+        if args.op == "archive":
+            def call():
+                atlas.atlas_demote_pages(prob.args, pools, src_t, b1_t, rejected)
+            kernel = "archive_kernel"
+        else:
+            def call():  # back into the blocks they came from
+                atlas.atlas_promote_pages(prob.args, pools, b1_t, src_t, rejected)
+            kernel = "promote_kernel"
+        code_bytes = 0
     else:
         src, dst, n8, n4 = demote_plan(w)
         tiers = {}
@@ -295,7 +324,7 @@ def write_path(args, torch, dev):
     torch.cuda.synchronize()
     kern = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     kern_avg = sum(kern) / K
-    if args.op == "demote":
+    if args.op != "write_kv":
         assert int(rejected) == 0
 
     if args.op == "demote" and not args.no_cpu:
@@ -323,6 +352,30 @@ def write_path(args, torch, dev):
                "sample": f"{n_blocks} of {len(src)} pages (all {Hkv} kv heads, K and V), "
                          f"numpy f32 encoder, one host thread"}
 
+    if args.op in ("archive", "promote") and not args.no_cpu:
+        import oracle
+        host = oracle.HostView(w)
+        (ka, kind), (va, _) = host.pools()
+        order = np.random.default_rng(0).permutation(len(src))
+        t0, n_blocks, n_bytes = time.perf_counter(), 0, 0
+        for i in order:
+            for arr in (ka, va):
+                for g in range(Hkv):
+                    x = oracle.widen_bits(arr[int(src[i]), g], kind).astype(np.float32).ravel()
+                    enc = oracle.encode_1bit(x, args.outliers)
+                    if args.op == "promote":
+                        oracle.hot_bits(oracle.decode_1bit(*enc, x.size), w.kv_dtype)
+                    n_bytes += P * D * eb + P * D // 8 + 4 + 4 * args.outliers
+            n_blocks += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        dt = time.perf_counter() - t0
+        what = "encoder" if args.op == "archive" else "encoder + decoder"
+        cpu = {"value": round(n_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "seconds": round(dt, 3),
+               "sample": f"{n_blocks} of {len(src)} pages (all {Hkv} kv heads, K and V), "
+                         f"numpy 1-bit {what}, one host thread"}
+
     # context: a plain device copy (read + write bytes), the practical roof of
     # a kernel that streams reads and writes together
     src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -340,11 +393,15 @@ def write_path(args, torch, dev):
     achieved = alg_bytes / (kern_avg / 1e3) / 1e9
     line = {
         "metric": {"write_kv": "KV write: bytes/s moved into the pages",
-                   "demote": "KV demotion: bytes/s of hot pages read + codes written"}[args.op],
+                   "demote": "KV demotion: bytes/s of hot pages read + codes written",
+                   "archive": "KV archiving: bytes/s of hot pages read + 1-bit pages written",
+                   "promote": "KV reconstruction: bytes/s of 1-bit pages read + hot pages "
+                              "written"}[args.op],
         "value": round(alg_bytes / (ms / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.kv_dtype if args.op == "write_kv" else f"{w.kv_dtype}->int8+int4",
+        "dtype": {"write_kv": w.kv_dtype, "demote": f"{w.kv_dtype}->int8+int4",
+                  "archive": f"{w.kv_dtype}->1bit", "promote": f"1bit->{w.kv_dtype}"}[args.op],
         "data": "synthetic",
         "config": {"workload": f"{args.op}:{w.name}", "rows": w.total_q,
                    "num_kv_heads": Hkv, "head_dim": D, "page_tokens": P,
@@ -387,10 +444,15 @@ def main():
                          "E4M3, the rest split evenly between int8 and int4")
     ap.add_argument("--p-int2", type=float, default=0.0,
                     help="tiered workload (config 4): share of the cold pages stored as INT2")
-    ap.add_argument("--op", choices=("attention", "write_kv", "demote"), default="attention",
+    ap.add_argument("--op", choices=("attention", "write_kv", "demote", "archive", "promote"),
+                    default="attention",
                     help="attention (default): the attention call of --config; write_kv: "
                          "writing a chunk's new K/V into its pages; demote: encoding every "
-                         "full hot page of --config into the int8 / int4 tiers")
+                         "full hot page of --config into the int8 / int4 tiers; archive: "
+                         "encoding them into the 1-bit archive; promote: rebuilding the "
+                         "archived pages into hot blocks")
+    ap.add_argument("--outliers", type=int, default=16,
+                    help="FP16 outliers per (page, kv head) block for archive / promote")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -327,121 +327,126 @@ __global__ __launch_bounds__(256) void demote_kernel(const DemoteParams d) {
 
 // ---- 1-bit archive (sign bits, mean-|x| scale, FP16 outliers) -------------
 
-__device__ inline int wave_sum(int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 __device__ inline double wave_sum(double v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return v;
 }
 
-// Sum of v over the lanes below this one.
-__device__ inline int wave_excl_scan(const int v, const int lane) {
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(x, d);
-        if (lane >= d) x += t;
-    }
-    return x - v;
-}
-
 __device__ inline uint32_t mag_key(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// Set bits of a wave mask in the lanes below this one / in all lanes.
+__device__ inline int below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 // Encodes one block into the 1-bit format (one wave).  The outlier
 // threshold T is the k-th largest magnitude key, found bit by bit from the
-// top (31 counting passes); elements above T are outliers, and of those
-// equal to T the lowest-indexed ones fill the remaining places.  Chunks of
-// the first R rounds stay in registers; later ones are read again per pass.
+// top; each pass counts the keys >= a candidate with one ballot per element
+// (no cross-lane data movement), and the search stops early once a prefix
+// selects exactly k keys.  Elements above T are outliers, and of those equal
+// to T the lowest-indexed ones fill the remaining places (ranks in index
+// order from lane-prefix bit counts).  The keys of the first R rounds of
+// chunks stay in registers; later rounds are read again per pass.
 template <int R, int ST>
 __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *signs,
                               float *scale_out, uint32_t *outs, const int kout, const int lane) {
     const int64_t n = nch * 8;
     const int k = (int)min((int64_t)kout, n);
     const int rounds = (int)((nch + 63) / 64);
-    uint4 keep[R];
+    uint32_t key[R][8];  // 0 past the block: never >= a candidate (>= 1)
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t ch = lane + 64 * j;
-        keep[j] = ch < nch ? load_chunk<ST>(src, ch) : make_uint4(0, 0, 0, 0);
+        float x[8];
+        if (ch < nch) {
+            widen8<ST>(src, load_chunk<ST>(src, ch), x);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) key[j][e] = ch < nch ? mag_key(x[e]) : 0u;
     }
-    // fn(chunk bits, round, valid) for every round of this lane, in order
-    auto for_each_chunk = [&](auto &&fn) {
+    // keys >= c over the block (c >= 1; wave-uniform)
+    auto count_at_least = [&](uint32_t c) {
+        int cnt = 0;
 #pragma unroll
         for (int j = 0; j < R; ++j)
-            if (j < rounds) fn(keep[j], j, lane + 64 * j < nch);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cnt += __popcll(__ballot(key[j][e] >= c));
         for (int r = R; r < rounds; ++r) {
             const int64_t ch = lane + 64 * (int64_t)r;
-            fn(ch < nch ? load_chunk<ST>(src, ch) : make_uint4(0, 0, 0, 0), r, ch < nch);
+            float x[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+            if (ch < nch) widen8<ST>(src, load_chunk<ST>(src, ch), x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cnt += __popcll(__ballot(ch < nch && mag_key(x[e]) >= c));
         }
+        return cnt;
     };
 
-    uint32_t T = 0;
+    uint32_t T = 0;  // count(key >= T) >= k throughout
     int need = 0;
     if (k > 0) {
-        for (int b = 30; b >= 0; --b) {
+        bool exact = false;
+        for (int b = 30; b >= 0 && !exact; --b) {
             const uint32_t cand = T | (1u << b);
-            int cnt = 0;
-            for_each_chunk([&](const uint4 w, int, bool valid) {
-                float x[8];
-                widen8<ST>(src, w, x);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) cnt += (valid && mag_key(x[j]) >= cand) ? 1 : 0;
-            });
-            if (wave_sum(cnt) >= k) T = cand;
+            const int c = count_at_least(cand);
+            if (c >= k) T = cand;
+            exact = c == k;
         }
-        int gt = 0;
-        for_each_chunk([&](const uint4 w, int, bool valid) {
-            float x[8];
-            widen8<ST>(src, w, x);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) gt += (valid && mag_key(x[j]) > T) ? 1 : 0;
-        });
-        need = k - wave_sum(gt);  // >= 1 elements equal to T are kept
+        if (exact) --T;  // then key > T selects exactly the k outliers
+        need = k - (T == 0x7FFFFFFFu ? 0 : count_at_least(T + 1));
     }
 
+    // final pass, the chunks read again (the threshold passes keep only keys)
     int eq_base = 0, out_base = 0;
     double sum = 0.0;
-    for_each_chunk([&](const uint4 w, int r, bool valid) {
-        float x[8];
-        widen8<ST>(src, w, x);
+    for (int r = 0; r < rounds; ++r) {
         const int64_t ch = lane + 64 * (int64_t)r;
-        int eqc = 0;
+        const bool valid = ch < nch;
+        float x[8];
+        if (valid) {
+            widen8<ST>(src, load_chunk<ST>(src, ch), x);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) eqc += (k > 0 && valid && mag_key(x[j]) == T) ? 1 : 0;
-        const int eq_pre = wave_excl_scan(eqc, lane);
-        int rank = eq_base + eq_pre;
-        eq_base += __shfl(eq_pre + eqc, 63);
-        bool is_out[8];
-        int oc = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t kj = mag_key(x[j]);
-            const bool tie = k > 0 && valid && kj == T;
-            is_out[j] = k > 0 && valid && (kj > T || (tie && rank < need));
-            rank += tie ? 1 : 0;
-            oc += is_out[j] ? 1 : 0;
+            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
         }
-        const int o_pre = wave_excl_scan(oc, lane);
-        int pos = out_base + o_pre;
-        out_base += __shfl(o_pre + oc, 63);
+        bool tie[8];
+        int rank = eq_base, eq_tot = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tie[e] = k > 0 && valid && mag_key(x[e]) == T;
+            const uint64_t m = __ballot(tie[e]);
+            rank += below(m);
+            eq_tot += __popcll(m);
+        }
+        eq_base += eq_tot;
+        bool is_out[8];
+        int pos = out_base, out_tot = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            is_out[e] = k > 0 && valid && (mag_key(x[e]) > T || (tie[e] && rank < need));
+            rank += tie[e] ? 1 : 0;
+            const uint64_t m = __ballot(is_out[e]);
+            pos += below(m);
+            out_tot += __popcll(m);
+        }
+        out_base += out_tot;
         uint32_t byte = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (is_out[j]) {
-                const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)x[j]);
-                outs[pos++] = (uint32_t)(ch * 8 + j) | ((uint32_t)h << 16);
+        for (int e = 0; e < 8; ++e) {
+            if (is_out[e]) {
+                const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)x[e]);
+                outs[pos++] = (uint32_t)(ch * 8 + e) | ((uint32_t)h << 16);
             } else if (valid) {
-                sum += (double)fabsf(x[j]);
+                sum += (double)fabsf(x[e]);
             }
-            byte |= (x[j] < 0.0f ? 1u : 0u) << j;
+            byte |= (x[e] < 0.0f ? 1u : 0u) << e;
         }
         if (valid) signs[ch] = (uint8_t)byte;
-    });
+    }
     sum = wave_sum(sum);
     const int64_t m = n - k;
     if (lane == 0) *scale_out = m > 0 ? (float)(sum / (double)m) : 0.0f;
@@ -591,24 +596,40 @@ __global__ __launch_bounds__(256) void promote_kernel(const PromoteParams q) {
         const uint8_t *signs = (kv ? p.b1_v : p.b1_k) + sblk * nch;
         const float sc = (kv ? p.b1_vs : p.b1_ks)[sblk];
         const uint32_t *outs = (kv ? p.b1_vo : p.b1_ko) + sblk * p.b1_nout;
-        // lane l holds outlier entry l; entries are applied in list order
+        // lane l holds outlier entry l; entries are applied in list order.
+        // Four rounds of chunks are decoded into registers, then one scan of
+        // the entries patches them (each entry's round and element are
+        // wave-uniform).
         const uint32_t mine = lane < p.b1_nout ? outs[lane] : 0xFFFFu;
-        for (int64_t r = 0; 64 * r < nch; ++r) {
-            const int64_t ch = lane + 64 * r;
-            const uint32_t byte = ch < nch ? signs[ch] : 0u;
-            float x[8];
+        for (int64_t r0 = 0; 64 * r0 < nch; r0 += 4) {
+            float x[4][8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = ((byte >> j) & 1u) ? -sc : sc;
+            for (int u = 0; u < 4; ++u) {
+                const int64_t ch = lane + 64 * (r0 + u);
+                const uint32_t byte = ch < nch ? signs[ch] : 0u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[u][j] = ((byte >> j) & 1u) ? -sc : sc;
+            }
             for (int o = 0; o < p.b1_nout; ++o) {
                 const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)mine, o);
-                const uint32_t idx = e & 0xFFFFu;
-                if ((int64_t)(idx >> 3) < 64 * r || (int64_t)(idx >> 3) >= 64 * (r + 1)) continue;
+                const int64_t c = (int64_t)((e & 0xFFFFu) >> 3);
+                const int64_t u = c / 64 - r0;
+                if (u < 0 || u >= 4) continue;  // uniform: another group of rounds
                 const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
-                const bool hit = (int64_t)(idx >> 3) == ch;
+                // this lane's element that the entry names (8: none)
+                const int t = (c % 64) == lane ? (int)(e & 7u) : 8;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = (hit && (int)(idx & 7u) == j) ? v : x[j];
+                for (int uu = 0; uu < 4; ++uu) {
+                    if (uu != u) continue;  // uniform
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[uu][j] = t == j ? v : x[uu][j];
+                }
             }
-            if (ch < nch) store_hot8(dst, ch, q.kv_type, x);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t ch = lane + 64 * (r0 + u);
+                if (ch < nch) store_hot8(dst, ch, q.kv_type, x[u]);
+            }
         }
         return;
     }
