@@ -237,7 +237,7 @@ def write_path(args, torch, dev):
 
     w = synth.config(args.config, device=dev, seed=42)
     if w.kv_dtype not in ("bf16", "f16") and args.op != "write_kv":
-        sys.exit(f"{args.op} needs a bf16 or f16 hot pool (configs 3 and 5)")
+        sys.exit(f"{args.op} needs a bf16 or f16 hot pool (--config 3 or 5)")
     prob = atlas.Problem(w)
     D, Hkv, P = w.head_dim, w.num_kv_heads, w.page_tokens
     eb = w.k_pool.element_size()
@@ -423,7 +423,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload: 1 one-head f32 decode over 4,096 keys; 2 (default) 32-head "
+                         "f32 decode over 65,536 keys; 3 64-sequence bf16 GQA decode over "
+                         "1k-32k keys; 4 the same with f16 hot and int8/int4 cold pages; 5 a "
+                         "2,048-query bf16 prefill over 131,072 keys, 75 %% regenerated")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--stream", type=int, default=1,
@@ -440,10 +444,10 @@ def main():
     ap.add_argument("--rope-theta", type=float, default=0.0,
                     help="attention with a rotary embedding of this base (0 = none)")
     ap.add_argument("--p-fp8", type=float, default=0.0,
-                    help="tiered workload (config 4): share of the cold pages stored as FP8 "
+                    help="tiered 64-sequence workload (--config 4): share of the cold pages stored as FP8 "
                          "E4M3, the rest split evenly between int8 and int4")
     ap.add_argument("--p-int2", type=float, default=0.0,
-                    help="tiered workload (config 4): share of the cold pages stored as INT2")
+                    help="tiered 64-sequence workload (--config 4): share of the cold pages stored as INT2")
     ap.add_argument("--op", choices=("attention", "write_kv", "demote", "archive", "promote"),
                     default="attention",
                     help="attention (default): the attention call of --config; write_kv: "

@@ -312,7 +312,7 @@ def test_regenerate_pages_bit_exact(gpu, kv_name, code):
 
 
 def test_regenerate_config5_pages_bit_exact(gpu):
-    # every value of four of config 5's regenerated pages, all kv heads
+    # every value of four regenerated pages of the 2,048-query prefill, all kv heads
     Hkv, D, P = 8, 128, 256
     lps = [0, 1, 200, 383]
     logical = torch.tensor(lps, dtype=torch.int32, device=gpu)
