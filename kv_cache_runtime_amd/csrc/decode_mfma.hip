@@ -499,10 +499,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                 } else {
                     const int pi = page_div(q);
                     live = tile < n_tiles && pi < np;
-                    const int lp = lp_first + (live ? s_lp[sp + pi] : 0);
+                    // unconditional reads (index kept inside the staged table), so the
+                    // four groups' LDS reads are in flight together
+                    const int si = min(sp + (live ? pi : 0), kStagedPages - 1);
+                    const int lpv = s_lp[si];
+                    const uint32_t entv = (uint32_t)s_pages[si];
+                    const int lp = lp_first + (live ? lpv : 0);
                     row0 = q - pi * P;
                     tok = lp * P + row0;
-                    ent = live ? (uint32_t)s_pages[sp + pi] : 0u;
+                    ent = live ? entv : 0u;
                 }
                 G_.tok[tg] = __builtin_amdgcn_readfirstlane(tok);
                 G_.row[tg] = __builtin_amdgcn_readfirstlane(row0);
