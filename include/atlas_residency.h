@@ -9,8 +9,9 @@
  * regenerated pages into the hot cache, runtime counters.  argus-cache,
  * "Visual Architecture" and its configuration (max_active_pages,
  * max_fp8_pages, sink_tokens): an FP16 active pool for recent pages, the
- * compression cascade FP8 -> INT8 -> INT4 -> INT2 for older ones, attention sinks
- * that stay in FP16.
+ * compression cascade FP8 -> INT8 -> INT4 -> INT2 -> 1-bit for older ones,
+ * attention sinks that stay in FP16, and the transient FP16 reconstruction of
+ * archived pages when a query needs them.
  *
  * The runtime is plain host code: it reads and writes no device memory and
  * launches nothing.  It hands out block and slot numbers of pools the caller
@@ -25,7 +26,9 @@
  *   1. atlas_residency_append(seq, n) for each sequence that grows (new
  *      pages get hot blocks);
  *   2. atlas_residency_tables -> page table, context lengths, regenerated
- *      page counts for the attention call; atlas_write_kv the new tokens;
+ *      page counts for the attention call (with a 1-bit archive:
+ *      atlas_residency_tables_transient, then atlas_promote_pages on its
+ *      jobs); atlas_write_kv the new tokens;
  *   3. the attention call;
  *   4. atlas_residency_plan -> demotions (tiered) or admissions (regen);
  *      run them (atlas_demote_pages, atlas_regenerate_pages).
@@ -69,6 +72,13 @@ typedef struct atlas_residency_config {
     int32_t int4_pages;        /* tiered, with num_int2 > 0: the next this many cold pages
                                   in INT4, older pages INT2 */
     int32_t num_int2;          /* tiered: INT2 pool capacity (0: INT4 is the last tier) */
+    int32_t int2_pages;        /* tiered, with num_1bit > 0: the next this many cold pages
+                                  in INT2 (or INT4 without an INT2 pool); older pages go to
+                                  the 1-bit archive */
+    int32_t num_1bit;          /* tiered: 1-bit archive capacity in slots (0: no archive) */
+    int32_t transient_blocks;  /* tiered: hot blocks hot_blocks .. hot_blocks +
+                                  transient_blocks - 1, reserved for archived pages rebuilt
+                                  for one attention call (atlas_residency_tables_transient) */
 } atlas_residency_config;
 
 typedef struct atlas_residency_stats {
@@ -86,6 +96,8 @@ typedef struct atlas_residency_stats {
     int64_t admissions;        /* regenerated pages admitted into the hot pool */
     int64_t evictions;         /* resident pages dropped back to regeneration (LRU) */
     int64_t capacity_failures; /* calls refused with ATLAS_ECAPACITY */
+    int64_t archive_used;      /* 1-bit archive slots in use */
+    int64_t reconstructions;   /* promotion jobs handed out by tables_transient */
 } atlas_residency_stats;
 
 /* Job lists filled by atlas_residency_plan.  The caller provides the arrays
@@ -99,6 +111,10 @@ typedef struct atlas_residency_jobs {
     int32_t *demote_dst;       /* destination entries */
     int32_t *admit_page;       /* logical page to regenerate ... */
     int32_t *admit_block;      /* ... into this hot block */
+    int32_t n_promote;         /* out: jobs for atlas_promote_pages (tables_transient) */
+    int32_t reserved;          /* 0 */
+    int32_t *promote_src;      /* archived entries ... */
+    int32_t *promote_dst;      /* ... rebuilt into these transient hot blocks */
 } atlas_residency_jobs;
 
 typedef struct atlas_residency atlas_residency; /* opaque */
@@ -130,8 +146,10 @@ atlas_status atlas_residency_append(atlas_residency *rt, int32_t seq, int32_t n_
 /* Applies the policy to every active sequence and fills `jobs`.  Tiered mode:
  * each page's target is hot for sink and KeepRecent pages; counting back
  * from the window, fp8_pages FP8 pages, then int8_pages INT8 pages, then
- * INT4 (with an INT2 pool: int4_pages INT4 pages, then INT2); a full pool
- * falls through to the next colder tier.  Each page that
+ * INT4 (with an INT2 pool: int4_pages INT4 pages, then INT2; with a 1-bit
+ * archive the last of these bands is int4_pages or int2_pages long and the
+ * rest is archived); a full pool falls through to the next colder tier.
+ * Archiving jobs have 1-bit destinations (atlas_demote_pages).  Each page that
  * is hotter than its target gets one job (its current entry -> a new slot of
  * the target tier); its old block or slot is freed after the plan, so no
  * job of a plan writes where another reads (give each cold pool headroom of
@@ -139,19 +157,35 @@ atlas_status atlas_residency_append(atlas_residency *rt, int32_t seq, int32_t n_
  * admit_per_plan regenerated pages just before a resident run (most recently
  * used sequences first) get free hot blocks as admission jobs.  Fails with
  * ATLAS_ECAPACITY (every cold pool full) or ATLAS_EINVAL (jobs capacity too
- * small), changing nothing. */
+ * small), changing nothing.  n_promote is set to 0. */
 atlas_status atlas_residency_plan(atlas_residency *rt, atlas_residency_jobs *jobs);
 
 /* Host arrays for an attention call over the sequences seqs[0..n-1]:
  * page_table [n][max_pages_per_seq] (hot block ids, or tiered entries in
  * tiered mode; entries of regenerated pages and past the context name block
- * hot_blocks, which the runtime never hands out: with a pool of exactly
- * hot_blocks blocks atlas_write_kv skips rows of such pages),
+ * hot_blocks + transient_blocks, which the runtime never hands out: with a
+ * pool of exactly that many blocks atlas_write_kv skips rows of such pages;
+ * archived pages keep their 1-bit entries, which attention refuses),
  * context_lens [n], regen_pages [n] (regen mode; may be NULL otherwise).
  * Marks the sequences as used (LRU). */
 atlas_status atlas_residency_tables(atlas_residency *rt, const int32_t *seqs, int32_t n,
                                     int32_t *page_table, int32_t *context_lens,
                                     int32_t *regen_pages);
+
+/* atlas_residency_tables plus the transient reconstruction of archived
+ * pages: the k-th 1-bit page of the listed sequences (in sequence, then page
+ * order) is given transient block hot_blocks + k in page_table, and jobs gets
+ * the promotion (promote_src = its 1-bit entry, promote_dst = that block) for
+ * atlas_promote_pages, to run before the attention call.  The transient
+ * blocks hold these pages until the next tables_transient call.  jobs
+ * (capacity >= the archived pages) is required; its n_demote and n_admit are
+ * set to 0.  Fails with ATLAS_ECAPACITY when the archived pages outnumber
+ * transient_blocks, or ATLAS_EINVAL for a small jobs capacity; the runtime
+ * is then unchanged and the outputs are unspecified. */
+atlas_status atlas_residency_tables_transient(atlas_residency *rt, const int32_t *seqs,
+                                              int32_t n, int32_t *page_table,
+                                              int32_t *context_lens, int32_t *regen_pages,
+                                              atlas_residency_jobs *jobs);
 
 /* Current counters. */
 atlas_status atlas_residency_get_stats(const atlas_residency *rt, atlas_residency_stats *out);

@@ -118,7 +118,7 @@ EXPORTS = [
     "atlas_write_kv", "atlas_demote_pages", "atlas_promote_pages",
     "atlas_residency_create", "atlas_residency_destroy", "atlas_residency_add_seq",
     "atlas_residency_remove_seq", "atlas_residency_append", "atlas_residency_plan",
-    "atlas_residency_tables", "atlas_residency_get_stats",
+    "atlas_residency_tables", "atlas_residency_tables_transient", "atlas_residency_get_stats",
 ]
 
 _lib = None
@@ -128,7 +128,8 @@ class ResidencyConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32 if n == "struct_size" else _i32) for n in (
         "struct_size", "mode", "page_tokens", "max_seqs", "max_pages_per_seq", "hot_blocks",
         "recent_tokens", "sink_tokens", "admit_per_plan", "fp8_pages", "int8_pages",
-        "num_fp8", "num_int8", "num_int4", "int4_pages", "num_int2")]
+        "num_fp8", "num_int8", "num_int4", "int4_pages", "num_int2", "int2_pages", "num_1bit",
+        "transient_blocks")]
 
 
 class ResidencyStats(ctypes.Structure):
@@ -136,13 +137,14 @@ class ResidencyStats(ctypes.Structure):
         "sequences", "hot_used", "fp8_used", "int8_used", "int4_used", "int2_used",
         "regenerated_pages")] + [(n, ctypes.c_int64) for n in (
         "appended_tokens", "demotions", "transcodes", "admissions", "evictions",
-        "capacity_failures")]
+        "capacity_failures", "archive_used", "reconstructions")]
 
 
 class ResidencyJobs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("capacity", _i32), ("n_demote", _i32),
                 ("n_admit", _i32), ("demote_src", _p), ("demote_dst", _p),
-                ("admit_page", _p), ("admit_block", _p)]
+                ("admit_page", _p), ("admit_block", _p), ("n_promote", _i32),
+                ("reserved", _i32), ("promote_src", _p), ("promote_dst", _p)]
 
 
 class AtlasError(RuntimeError):
@@ -211,6 +213,9 @@ def load(path: str = LIB_PATH):
     L.atlas_residency_plan.argtypes = [_p, ctypes.POINTER(ResidencyJobs)]
     L.atlas_residency_tables.restype = _i32
     L.atlas_residency_tables.argtypes = [_p, _p, _i32, _p, _p, _p]
+    L.atlas_residency_tables_transient.restype = _i32
+    L.atlas_residency_tables_transient.argtypes = [_p, _p, _i32, _p, _p, _p,
+                                                   ctypes.POINTER(ResidencyJobs)]
     L.atlas_residency_get_stats.restype = _i32
     L.atlas_residency_get_stats.argtypes = [_p, ctypes.POINTER(ResidencyStats)]
     if L.atlas_abi_version() != 3:

@@ -5,8 +5,9 @@
 // KeepRecent { recent_tokens } policy and the admission of regenerated pages
 // into the cache.  argus-cache, "Visual Architecture" and its configuration
 // (max_active_pages, max_fp8_pages, sink_tokens): an FP16 active pool, the
-// compression cascade FP8 -> INT8 -> INT4 for older pages, attention sinks
-// kept in FP16.
+// compression cascade FP8 -> INT8 -> INT4 -> INT2 -> 1-bit for older pages,
+// attention sinks kept in FP16, and archived pages rebuilt in FP16 for the
+// call that needs them (its overview: transient FP16 reconstruction).
 //
 // Regen mode keeps, per sequence, a resident suffix of pages (the kernels
 // regenerate a leading run of pages, so the regenerated set is always a
@@ -15,7 +16,8 @@
 // stay as long as the hot pool has room and are the LRU victims when it has
 // not.  Tiered mode gives every page a target tier from its position (sink
 // and window pages hot; counting back from the window, FP8, then INT8, then
-// INT4) and moves each page that is hotter than its target in one job.
+// INT4, INT2 and the 1-bit archive) and moves each page that is hotter than
+// its target in one job.
 #include <algorithm>
 #include <cstdarg>
 #include <cstdint>
@@ -35,8 +37,9 @@ namespace {
 
 constexpr uint32_t kShift = ATLAS_TIER_SHIFT;
 constexpr uint32_t kSlotMask = (1u << kShift) - 1u;
-// Page classes: the tiers, with the extension tier split into FP8 and INT2.
-constexpr int kTierHot = 0, kTierI8 = 1, kTierI4 = 2, kTierF8 = 3, kTierI2 = 4;
+// Page classes: the tiers, with the extension tier split into FP8, INT2 and
+// the 1-bit archive.
+constexpr int kTierHot = 0, kTierI8 = 1, kTierI4 = 2, kTierF8 = 3, kTierI2 = 4, kTierB1 = 5;
 
 int32_t fail(int32_t st, const char *fmt, ...) {
     char buf[256];
@@ -47,28 +50,32 @@ int32_t fail(int32_t st, const char *fmt, ...) {
     return atlas::report_error(st, buf);
 }
 
-// Coldness order of the classes: hot < FP8 < INT8 < INT4 < INT2.
+// Coldness order of the classes: hot < FP8 < INT8 < INT4 < INT2 < 1-bit.
 int coldness(int cls) {
     switch (cls) {
         case kTierHot: return 0;
         case kTierF8: return 1;
         case kTierI8: return 2;
         case kTierI4: return 3;
-        default: return 4;
+        case kTierI2: return 4;
+        default: return 5;
     }
 }
 
-// Page-table entry of a class and slot (FP8 and INT2 share tier 3).
+// Page-table entry of a class and slot (FP8, INT2 and 1-bit share tier 3).
 uint32_t entry(int cls, int32_t slot) {
-    if (cls == kTierI2)
-        return (3u << kShift) | ((uint32_t)ATLAS_EXT_INT2 << ATLAS_EXT_KIND_SHIFT) | (uint32_t)slot;
+    if (cls == kTierI2 || cls == kTierB1)
+        return (3u << kShift) |
+               ((uint32_t)(cls == kTierI2 ? ATLAS_EXT_INT2 : ATLAS_EXT_1BIT) << ATLAS_EXT_KIND_SHIFT) |
+               (uint32_t)slot;
     return ((uint32_t)cls << kShift) | (uint32_t)slot;
 }
 
 int class_of(uint32_t e) {
     const uint32_t tier = e >> kShift;
     if (tier < 3) return (int)tier;
-    return ((e >> ATLAS_EXT_KIND_SHIFT) & 3u) == ATLAS_EXT_INT2 ? kTierI2 : kTierF8;
+    const uint32_t kind = (e >> ATLAS_EXT_KIND_SHIFT) & 3u;
+    return kind == ATLAS_EXT_INT2 ? kTierI2 : kind == ATLAS_EXT_1BIT ? kTierB1 : kTierF8;
 }
 
 int32_t slot_of(uint32_t e) {
@@ -110,7 +117,7 @@ struct Seq {
 struct atlas_residency {
     atlas_residency_config cfg;
     std::vector<Seq> seqs;
-    SlotPool hot, f8, i8, i4, i2;
+    SlotPool hot, f8, i8, i4, i2, b1;
     uint64_t tick = 0;
     atlas_residency_stats st;
 
@@ -120,7 +127,8 @@ struct atlas_residency {
             case kTierF8: return f8;
             case kTierI8: return i8;
             case kTierI4: return i4;
-            default: return i2;
+            case kTierI2: return i2;
+            default: return b1;
         }
     }
     int32_t pages_of(const Seq &s) const {
@@ -138,13 +146,20 @@ struct atlas_residency {
     // start wf should be in.
     int target_tier(int32_t p, int32_t wf) const {
         if (p < sink_pages() || p >= wf) return kTierHot;
-        const int32_t r = wf - 1 - p;  // 0 = the newest cold page
-        if (r < cfg.fp8_pages) return kTierF8;
-        if (r < cfg.fp8_pages + cfg.int8_pages) return kTierI8;
-        if (cfg.num_int2 > 0 && r >= cfg.fp8_pages + cfg.int8_pages + cfg.int4_pages)
-            return kTierI2;
-        return kTierI4;
+        const int64_t r = wf - 1 - p;  // 0 = the newest cold page
+        int64_t edge = cfg.fp8_pages;
+        if (r < edge) return kTierF8;
+        if (r < (edge += cfg.int8_pages)) return kTierI8;
+        const bool i2 = cfg.num_int2 > 0, b1 = cfg.num_1bit > 0;
+        if (!i2 && !b1) return kTierI4;
+        if (r < (edge += cfg.int4_pages)) return kTierI4;
+        if (!b1) return kTierI2;
+        if (i2 && r < edge + cfg.int2_pages) return kTierI2;
+        return kTierB1;
     }
+    // The table entry of pages the runtime does not hand out: regenerated
+    // pages and pages past the context.
+    int32_t filler() const { return cfg.hot_blocks + cfg.transient_blocks; }
     // Regen mode: resident pages of a sequence that may be dropped back to
     // regeneration (in front of its window).
     int32_t evictable(const Seq &s) const {
@@ -179,6 +194,77 @@ bool evict_one(atlas_residency *rt) {
 
 }  // namespace
 
+namespace {
+
+atlas_status fill_tables(atlas_residency *rt, const int32_t *seqs, int32_t n, int32_t *page_table,
+                         int32_t *context_lens, int32_t *regen_pages,
+                         atlas_residency_jobs *jobs) {
+    if (!rt) return fail(ATLAS_EINVAL, "runtime is NULL");
+    if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
+    if (n > 0 && (!seqs || !page_table || !context_lens))
+        return fail(ATLAS_EINVAL, "NULL seqs, page_table or context_lens");
+    if (n > 0 && rt->cfg.mode == ATLAS_RESIDENCY_REGEN && !regen_pages)
+        return fail(ATLAS_EINVAL, "regen mode needs regen_pages");
+    for (int32_t i = 0; i < n; ++i)
+        if (!valid_seq(rt, seqs[i]) || !rt->seqs[seqs[i]].active)
+            return fail(ATLAS_EINVAL, "sequence %d is not active", seqs[i]);
+    for (int32_t i = 0; i < n; ++i)
+        if (rt->seqs[seqs[i]].tokens > INT32_MAX) return fail(ATLAS_EINVAL, "context too long");
+    if (jobs) {  // archived pages of the listed sequences get transient blocks
+        if (jobs->struct_size != sizeof(atlas_residency_jobs))
+            return fail(ATLAS_EINVAL, "jobs->struct_size %u != %zu", jobs->struct_size,
+                        sizeof(atlas_residency_jobs));
+        int64_t archived = 0;
+        for (int32_t i = 0; i < n; ++i)
+            for (uint32_t e : rt->seqs[seqs[i]].pages)
+                if (rt->cfg.mode == ATLAS_RESIDENCY_TIERED && class_of(e) == kTierB1) ++archived;
+        if (archived > rt->cfg.transient_blocks) {
+            ++rt->st.capacity_failures;
+            return fail(ATLAS_ECAPACITY, "%lld archived pages, %d transient blocks",
+                        (long long)archived, rt->cfg.transient_blocks);
+        }
+        if (archived > jobs->capacity)
+            return fail(ATLAS_EINVAL, "jobs capacity %d < %lld archived pages", jobs->capacity,
+                        (long long)archived);
+        if (archived > 0 && (!jobs->promote_src || !jobs->promote_dst))
+            return fail(ATLAS_EINVAL, "NULL promote arrays");
+        jobs->n_demote = 0;
+        jobs->n_admit = 0;
+        jobs->n_promote = 0;
+    }
+    const int32_t M = rt->cfg.max_pages_per_seq;
+    int32_t k = 0;  // transient blocks handed out
+    for (int32_t i = 0; i < n; ++i) {
+        Seq &s = rt->seqs[seqs[i]];
+        int32_t *row = page_table + (int64_t)i * M;
+        // regenerated pages and pages past the context name a block the
+        // runtime never hands out (atlas_write_kv skips such rows when the
+        // pool has no block there)
+        std::fill(row, row + M, rt->filler());
+        for (int32_t p = (rt->cfg.mode == ATLAS_RESIDENCY_REGEN ? s.first_resident : 0);
+             p < (int32_t)s.pages.size(); ++p) {
+            row[p] = (int32_t)s.pages[p];
+            if (jobs && rt->cfg.mode == ATLAS_RESIDENCY_TIERED && class_of(s.pages[p]) == kTierB1) {
+                const int32_t blk = rt->cfg.hot_blocks + k;
+                jobs->promote_src[k] = (int32_t)s.pages[p];
+                jobs->promote_dst[k] = blk;
+                row[p] = blk;
+                ++k;
+            }
+        }
+        context_lens[i] = (int32_t)s.tokens;
+        if (regen_pages) regen_pages[i] = rt->cfg.mode == ATLAS_RESIDENCY_REGEN ? s.first_resident : 0;
+        s.last_use = ++rt->tick;
+    }
+    if (jobs) {
+        jobs->n_promote = k;
+        rt->st.reconstructions += k;
+    }
+    return atlas::report_ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_residency **out) {
@@ -200,6 +286,9 @@ atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_resid
         c->num_fp8 > (1 << ATLAS_EXT_KIND_SHIFT) || c->num_int8 > (int32_t)kSlotMask ||
         c->num_int4 > (int32_t)kSlotMask)
         return fail(ATLAS_EINVAL, "cold pool size outside [0, 2^30) (FP8: 2^28)");
+    if (c->int2_pages < 0 || c->num_1bit < 0 || c->num_1bit > (1 << ATLAS_EXT_KIND_SHIFT) ||
+        c->transient_blocks < 0 || (int64_t)c->hot_blocks + c->transient_blocks > (int64_t)kSlotMask)
+        return fail(ATLAS_EINVAL, "1-bit archive or transient block field out of range");
     if ((int64_t)c->max_seqs * c->max_pages_per_seq > ((int64_t)1 << 31))
         return fail(ATLAS_EINVAL, "max_seqs * max_pages_per_seq too large");
     atlas_residency *rt = new (std::nothrow) atlas_residency();
@@ -211,6 +300,7 @@ atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_resid
     rt->i8.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int8 : 0);
     rt->i4.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int4 : 0);
     rt->i2.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int2 : 0);
+    rt->b1.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_1bit : 0);
     std::memset(&rt->st, 0, sizeof(rt->st));
     rt->st.struct_size = sizeof(atlas_residency_stats);
     *out = rt;
@@ -304,6 +394,7 @@ atlas_status atlas_residency_plan(atlas_residency *rt, atlas_residency_jobs *job
     if (jobs->capacity < 0) return fail(ATLAS_EINVAL, "jobs capacity < 0");
     jobs->n_demote = 0;
     jobs->n_admit = 0;
+    jobs->n_promote = 0;
 
     if (rt->cfg.mode == ATLAS_RESIDENCY_REGEN) {
         if (rt->cfg.admit_per_plan > 0 && jobs->capacity > 0 &&
@@ -366,6 +457,7 @@ atlas_status atlas_residency_plan(atlas_residency *rt, atlas_residency_jobs *job
             tier = tier == kTierF8   ? kTierI8
                    : tier == kTierI8 ? kTierI4
                    : tier == kTierI4 && rt->cfg.num_int2 > 0 ? kTierI2
+                   : (tier == kTierI4 || tier == kTierI2) && rt->cfg.num_1bit > 0 ? kTierB1
                                      : -1;
             // a fallback must still be colder than where the page is now
             if (tier != -1 && coldness(tier) <= coldness(class_of(m.from))) tier = -1;
@@ -399,32 +491,15 @@ atlas_status atlas_residency_plan(atlas_residency *rt, atlas_residency_jobs *job
 atlas_status atlas_residency_tables(atlas_residency *rt, const int32_t *seqs, int32_t n,
                                     int32_t *page_table, int32_t *context_lens,
                                     int32_t *regen_pages) {
-    if (!rt) return fail(ATLAS_EINVAL, "runtime is NULL");
-    if (n < 0) return fail(ATLAS_EINVAL, "n %d < 0", n);
-    if (n > 0 && (!seqs || !page_table || !context_lens))
-        return fail(ATLAS_EINVAL, "NULL seqs, page_table or context_lens");
-    if (n > 0 && rt->cfg.mode == ATLAS_RESIDENCY_REGEN && !regen_pages)
-        return fail(ATLAS_EINVAL, "regen mode needs regen_pages");
-    for (int32_t i = 0; i < n; ++i)
-        if (!valid_seq(rt, seqs[i]) || !rt->seqs[seqs[i]].active)
-            return fail(ATLAS_EINVAL, "sequence %d is not active", seqs[i]);
-    const int32_t M = rt->cfg.max_pages_per_seq;
-    for (int32_t i = 0; i < n; ++i) {
-        Seq &s = rt->seqs[seqs[i]];
-        if (s.tokens > INT32_MAX) return fail(ATLAS_EINVAL, "context too long");
-        int32_t *row = page_table + (int64_t)i * M;
-        // regenerated pages and pages past the context name block hot_blocks,
-        // which the runtime never hands out (atlas_write_kv skips such rows
-        // when the pool has no block there)
-        std::fill(row, row + M, rt->cfg.hot_blocks);
-        for (int32_t p = (rt->cfg.mode == ATLAS_RESIDENCY_REGEN ? s.first_resident : 0);
-             p < (int32_t)s.pages.size(); ++p)
-            row[p] = (int32_t)s.pages[p];
-        context_lens[i] = (int32_t)s.tokens;
-        if (regen_pages) regen_pages[i] = rt->cfg.mode == ATLAS_RESIDENCY_REGEN ? s.first_resident : 0;
-        s.last_use = ++rt->tick;
-    }
-    return atlas::report_ok();
+    return fill_tables(rt, seqs, n, page_table, context_lens, regen_pages, nullptr);
+}
+
+atlas_status atlas_residency_tables_transient(atlas_residency *rt, const int32_t *seqs,
+                                              int32_t n, int32_t *page_table,
+                                              int32_t *context_lens, int32_t *regen_pages,
+                                              atlas_residency_jobs *jobs) {
+    if (!jobs) return fail(ATLAS_EINVAL, "jobs is NULL");
+    return fill_tables(rt, seqs, n, page_table, context_lens, regen_pages, jobs);
 }
 
 atlas_status atlas_residency_get_stats(const atlas_residency *rt, atlas_residency_stats *out) {
@@ -446,6 +521,7 @@ atlas_status atlas_residency_get_stats(const atlas_residency *rt, atlas_residenc
     out->int8_used = rt->i8.used();
     out->int4_used = rt->i4.used();
     out->int2_used = rt->i2.used();
+    out->archive_used = rt->b1.used();
     return atlas::report_ok();
 }
 

@@ -26,7 +26,7 @@ class Residency:
     def __init__(self, *, mode, page_tokens, max_seqs, max_pages_per_seq, hot_blocks,
                  recent_tokens=0, sink_tokens=0, admit_per_plan=0, fp8_pages=0, int8_pages=0,
                  num_fp8=0, num_int8=0, num_int4=0, int4_pages=0, num_int2=0,
-                 job_capacity=1 << 16):
+                 int2_pages=0, num_1bit=0, transient_blocks=0, job_capacity=1 << 16):
         L = atlas.load()
         c = atlas.ResidencyConfig()
         c.struct_size = ctypes.sizeof(c)
@@ -35,7 +35,9 @@ class Residency:
                          recent_tokens=recent_tokens, sink_tokens=sink_tokens,
                          admit_per_plan=admit_per_plan, fp8_pages=fp8_pages,
                          int8_pages=int8_pages, num_fp8=num_fp8, num_int8=num_int8,
-                         num_int4=num_int4, int4_pages=int4_pages, num_int2=num_int2).items():
+                         num_int4=num_int4, int4_pages=int4_pages, num_int2=num_int2,
+                         int2_pages=int2_pages, num_1bit=num_1bit,
+                         transient_blocks=transient_blocks).items():
             setattr(c, k, int(v))
         self.config = c
         self._h = ctypes.c_void_p()
@@ -44,7 +46,7 @@ class Residency:
         self._L = L
         self.max_pages = int(max_pages_per_seq)
         self._cap = int(job_capacity)
-        self._bufs = [np.zeros(self._cap, dtype=np.int32) for _ in range(4)]
+        self._bufs = [np.zeros(self._cap, dtype=np.int32) for _ in range(6)]
 
     def close(self):
         if self._h:
@@ -71,12 +73,17 @@ class Residency:
     def append(self, seq: int, n_tokens: int):
         self._call("atlas_residency_append", int(seq), int(n_tokens))
 
-    def plan(self):
-        """Returns (demote_src, demote_dst, admit_page, admit_block) int32 arrays."""
+    def _jobs(self):
         j = atlas.ResidencyJobs()
         j.struct_size = ctypes.sizeof(j)
         j.capacity = self._cap
-        j.demote_src, j.demote_dst, j.admit_page, j.admit_block = (_arr(b) for b in self._bufs)
+        (j.demote_src, j.demote_dst, j.admit_page, j.admit_block, j.promote_src,
+         j.promote_dst) = (_arr(b) for b in self._bufs)
+        return j
+
+    def plan(self):
+        """Returns (demote_src, demote_dst, admit_page, admit_block) int32 arrays."""
+        j = self._jobs()
         self._call("atlas_residency_plan", ctypes.byref(j))
         nd, na = j.n_demote, j.n_admit
         return (self._bufs[0][:nd].copy(), self._bufs[1][:nd].copy(),
@@ -91,6 +98,20 @@ class Residency:
         regen = np.zeros(n, dtype=np.int32)
         self._call("atlas_residency_tables", _arr(seqs), n, _arr(table), _arr(ctx), _arr(regen))
         return table, ctx, regen
+
+    def tables_transient(self, seqs):
+        """tables() with archived pages given transient blocks; returns
+        (page_table, context_lens, regen_pages, promote_src, promote_dst)."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = seqs.size
+        table = np.zeros((n, self.max_pages), dtype=np.int32)
+        ctx = np.zeros(n, dtype=np.int32)
+        regen = np.zeros(n, dtype=np.int32)
+        j = self._jobs()
+        self._call("atlas_residency_tables_transient", _arr(seqs), n, _arr(table), _arr(ctx),
+                   _arr(regen), ctypes.byref(j))
+        k = j.n_promote
+        return table, ctx, regen, self._bufs[4][:k].copy(), self._bufs[5][:k].copy()
 
     def stats(self) -> dict:
         s = atlas.ResidencyStats()

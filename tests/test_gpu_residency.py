@@ -123,6 +123,110 @@ def test_tiered_decode_loop_through_the_runtime(gpu):
     assert st["int2_used"] > 0
 
 
+def test_tiered_decode_loop_with_the_1bit_archive(gpu):
+    """The full ARGUS loop through the runtime: plans archive the oldest cold
+    pages into 1-bit slots, and before each checked attention call the
+    transient tables rebuild them into reserved hot blocks
+    (atlas_promote_pages); the result matches the oracle over the pools."""
+    HOT, TRANS, K_OUT = 48, 40, 16
+    rt = Residency(mode=TIERED, page_tokens=P, max_seqs=3, max_pages_per_seq=64, hot_blocks=HOT,
+                   recent_tokens=48, sink_tokens=16, fp8_pages=1, int8_pages=2, num_fp8=8,
+                   num_int8=16, num_int4=24, int4_pages=2, num_int2=24, int2_pages=2,
+                   num_1bit=96, transient_blocks=TRANS)
+    gen = torch.Generator(device=gpu).manual_seed(3)
+    hot_k = torch.zeros((HOT + TRANS, HKV, P, D), dtype=torch.float16, device=gpu)
+    hot_v = torch.zeros_like(hot_k)
+    tiers = {}
+    for key, n, shape_d, dt in (("f8", 8, D, torch.uint8), ("i8", 16, D, torch.int8),
+                                ("i4", 24, D // 2, torch.uint8), ("i2", 24, D // 4, torch.uint8)):
+        for kv in ("k", "v"):
+            tiers[f"{key}_{kv}"] = torch.zeros((n, HKV, P, shape_d), dtype=dt, device=gpu)
+            tiers[f"{key}_{kv}_scale"] = torch.zeros((n, HKV), device=gpu)
+    for kv in ("k", "v"):
+        tiers[f"b1_{kv}"] = torch.zeros((96, HKV, P * D // 8), dtype=torch.uint8, device=gpu)
+        tiers[f"b1_{kv}_scale"] = torch.zeros((96, HKV), device=gpu)
+        tiers[f"b1_{kv}_out"] = torch.zeros((96, HKV, K_OUT), dtype=torch.int32, device=gpu)
+    pools = atlas.make_tiers(tiers)
+    seqs = [0, 1, 2]
+    prompt = [120, 45, 260]
+    for s in seqs:
+        rt.add_seq(s)
+
+    def dummy_args():
+        a = _args(gpu, torch.zeros((3, H, D), dtype=torch.bfloat16, device=gpu), hot_k, hot_v,
+                  torch.zeros((3, 64), dtype=torch.int32, device=gpu),
+                  torch.ones(3, dtype=torch.int32, device=gpu),
+                  torch.empty((3, H, D), device=gpu), torch.empty((3, H), device=gpu))
+        a.num_blocks = HOT + TRANS
+        return a
+
+    def tables():
+        table, ctx, _, psrc, pdst = rt.tables_transient(seqs)
+        if len(psrc):
+            rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+            atlas.atlas_promote_pages(dummy_args(), pools, torch.from_numpy(psrc).to(gpu),
+                                      torch.from_numpy(pdst).to(gpu), rej)
+            torch.cuda.synchronize()
+            assert int(rej) == 0
+        return table, ctx, len(psrc)
+
+    def write(n_new, qstart, max_q):
+        table, ctx, _ = rt.tables(seqs)
+        rows = int(sum(n_new))
+        k_new = torch.randn((rows, HKV, D), generator=gen, device=gpu).half()
+        v_new = torch.randn((rows, HKV, D), generator=gen, device=gpu).half()
+        q = torch.zeros((rows, H, D), dtype=torch.bfloat16, device=gpu)
+        tt, ct = torch.from_numpy(table).to(gpu), torch.from_numpy(ctx).to(gpu)
+        qs = None if qstart is None else torch.from_numpy(qstart).to(gpu)
+        a = _args(gpu, q, hot_k, hot_v, tt, ct, torch.empty((rows, H, D), device=gpu),
+                  torch.empty((rows, H), device=gpu), qstart=qs, max_q=max_q)
+        a.num_blocks = HOT + TRANS
+        atlas.atlas_write_kv(a, k_new, v_new)
+
+    def run_jobs():
+        src, dst, _, _ = rt.plan()
+        if len(src):
+            rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+            atlas.atlas_demote_pages(dummy_args(), pools, torch.from_numpy(src).to(gpu),
+                                     torch.from_numpy(dst).to(gpu), rej)
+            torch.cuda.synchronize()
+            assert int(rej) == 0
+
+    for s, n in zip(seqs, prompt):
+        rt.append(s, n)
+    qstart = np.concatenate([[0], np.cumsum(prompt)]).astype(np.int32)
+    write(prompt, qstart, max(prompt))
+    run_jobs()
+    checked, rebuilt = 0, 0
+    for step in range(40):
+        for s in seqs:
+            rt.append(s, 1)
+        write([1, 1, 1], None, 1)
+        if step % 10 == 9:
+            table, ctx, n_promoted = tables()
+            rebuilt += n_promoted
+            q = torch.randn((3, H, D), generator=gen, device=gpu).bfloat16()
+            out = torch.empty((3, H, D), device=gpu)
+            lse = torch.empty((3, H), device=gpu)
+            a = _args(gpu, q, hot_k, hot_v, torch.from_numpy(table).to(gpu),
+                      torch.from_numpy(ctx).to(gpu), out, lse)
+            a.num_blocks = HOT + TRANS
+            print(f"[archive loop] step {step}: {n_promoted} pages rebuilt", flush=True)
+            _attend(a, gpu, tiers=pools)
+            counts = [HOT + TRANS, 16, 24, 8, 24]
+            w = synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
+                            page_tokens=P, q_dtype="bf16", kv_dtype="f16", context_lens=ctx,
+                            query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
+                            q=q, k_pool=hot_k, v_pool=hot_v, page_table=table,
+                            tiers=dict(tiers, counts=counts), name=f"runtime-archive-{step}")
+            check(w, out.cpu().numpy(), lse.cpu().numpy())
+            checked += 1
+        run_jobs()
+    st = rt.stats()
+    assert checked == 4 and rebuilt > 0 and st["archive_used"] > 0
+    assert st["reconstructions"] == rebuilt and st["int2_used"] > 0
+
+
 def test_regen_decode_loop_through_the_runtime(gpu):
     """KeepRecent + LRU hot cache + admission over regenerated pages: the
     result equals the all-regenerated call bit for bit (CFR-Atlas core

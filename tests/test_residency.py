@@ -217,3 +217,77 @@ def test_tiered_cascade_ends_in_int2_when_it_has_a_pool():
     src, dst, _, _ = r.plan()
     moves = sorted((oracle.entry_class(s)[0], oracle.entry_class(d)[0]) for s, d in zip(src, dst))
     assert moves == [(0, 3), (1, 2), (2, 4), (3, 1)]
+
+
+def test_tiered_cascade_ends_in_the_1bit_archive():
+    r = _tiered(int4_pages=4, num_int2=32, int2_pages=3, num_1bit=16, transient_blocks=16)
+    r.add_seq(0)
+    r.append(0, 400)             # 25 pages, window 21..24, sink page 0
+    src, dst, _, _ = r.plan()
+    assert sum(oracle.entry_class(d)[0] == 5 for d in dst) == 8
+    table, ctx, _ = r.tables([0])
+    cls = [oracle.entry_class(e)[0] for e in table[0, :25]]
+    # newest cold first: 2 FP8, 3 INT8, 4 INT4, 3 INT2, the rest (pages 1..8) archived
+    assert cls == [0] + [5] * 8 + [4] * 3 + [2] * 4 + [1] * 3 + [3] * 2 + [0] * 4
+    assert r.stats()["archive_used"] == 8
+    # without an INT2 pool the INT4 band comes last before the archive
+    r2 = _tiered(int4_pages=4, int2_pages=3, num_1bit=16)
+    r2.add_seq(0)
+    r2.append(0, 400)
+    r2.plan()
+    t2, _, _ = r2.tables([0])
+    assert [oracle.entry_class(e)[0] for e in t2[0, :25]] == (
+        [0] + [5] * 11 + [2] * 4 + [1] * 3 + [3] * 2 + [0] * 4)
+
+
+def test_transient_tables_rebuild_archived_pages():
+    r = _tiered(int4_pages=4, num_int2=32, int2_pages=3, num_1bit=16, transient_blocks=16)
+    for s in (0, 1):
+        r.add_seq(s)
+    r.append(0, 400)
+    r.append(1, 60)              # no archived page
+    r.plan()
+    plain, _, _ = r.tables([1, 0])
+    table, ctx, _, psrc, pdst = r.tables_transient([1, 0])
+    assert list(ctx) == [60, 400]
+    np.testing.assert_array_equal(table[0], plain[0])
+    archived = [p for p in range(25) if oracle.entry_class(plain[1, p])[0] == 5]
+    assert archived == list(range(1, 9))
+    # the k-th archived page (sequence, then page order) gets block hot_blocks + k
+    assert list(pdst) == list(range(32, 40))
+    assert list(psrc) == [int(plain[1, p]) for p in archived]
+    assert [int(table[1, p]) for p in archived] == list(range(32, 40))
+    others = [p for p in range(25) if p not in archived]
+    np.testing.assert_array_equal(table[1, others], plain[1, others])
+    # past the context: the block the runtime never hands out
+    assert set(table[1, 25:].tolist()) == {32 + 16} and set(table[0, 4:].tolist()) == {48}
+    assert r.stats()["reconstructions"] == 8
+
+
+def test_transient_capacity_failure_and_archive_fall_through():
+    r = _tiered(int4_pages=4, num_int2=32, int2_pages=3, num_1bit=16, transient_blocks=5)
+    r.add_seq(0)
+    r.append(0, 400)
+    r.plan()
+    with pytest.raises(atlas.AtlasError) as e:
+        r.tables_transient([0])
+    assert e.value.status == atlas.ECAPACITY
+    assert r.stats()["reconstructions"] == 0 and r.stats()["capacity_failures"] == 1
+    table, _, _ = r.tables([0])           # the plain tables still work
+    assert sum(oracle.entry_class(x)[0] == 5 for x in table[0, :25]) == 8
+    # a full INT2 pool sends its band to the archive
+    r3 = _tiered(int4_pages=4, num_int2=1, int2_pages=3, num_1bit=16)
+    r3.add_seq(0)
+    r3.append(0, 400)
+    r3.plan()
+    t3, _, _ = r3.tables([0])
+    assert [oracle.entry_class(x)[0] for x in t3[0, 1:12]].count(4) == 1
+    assert r3.stats()["archive_used"] == 10
+
+
+def test_archive_config_is_checked():
+    for bad in (dict(num_1bit=-1), dict(int2_pages=-2), dict(transient_blocks=-1),
+                dict(num_1bit=(1 << 28) + 1)):
+        with pytest.raises(atlas.AtlasError) as e:
+            _tiered(**bad)
+        assert e.value.status == atlas.EINVAL
