@@ -112,9 +112,13 @@ __device__ __forceinline__ void load_words(uint32_t *dst, const void *src) {
 // 2 and 1 leave the full row sum in every lane, and every lane adds the same
 // pairs in the same tree, so all 16 lanes hold bit-identical sums.
 // ---------------------------------------------------------------------------
+// Lane permutation within 16-lane rows (row_ror only: every lane reads a
+// lane of its own row, so bound_ctrl never applies; setting it lets the
+// compiler fold the move into the instruction that consumes it).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+    static_assert(CTRL >= 0x121 && CTRL <= 0x12F, "row_ror controls only");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_f<0x128>(x);  // row_ror:8
