@@ -618,11 +618,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             float alpha[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float mx = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
-                mx = fmaxf(mx, dpp_f<0x128>(mx));
-                mx = fmaxf(mx, dpp_f<0x124>(mx));
-                mx = fmaxf(mx, dpp_f<0x122>(mx));
-                mx = fmaxf(mx, dpp_f<0x121>(mx));
+                // IEEE maximum (v_maximum3_f32): no operand canonicalisation,
+                // and a NaN score (from NaN keys) propagates into the row
+                float mx = __builtin_elementwise_maximum(
+                    __builtin_elementwise_maximum(sc[0][i], sc[1][i]),
+                    __builtin_elementwise_maximum(sc[2][i], sc[3][i]));
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x128>(mx));
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x124>(mx));
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x122>(mx));
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x121>(mx));
                 const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
                 const float m_new = move ? mx : m_ref[i];
                 alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;
