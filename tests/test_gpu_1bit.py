@@ -235,3 +235,39 @@ def test_archive_then_promote_then_attend(gpu, hot):
     w.page_table = table
     out, lse = run(w)
     check(w, out, lse)
+
+
+def test_promote_into_an_f32_hot_pool(gpu):
+    """Reconstruction into f32 blocks: every class's values exactly (no
+    rounding step), through a pool of another element type than the one the
+    pages were demoted from."""
+    w = _case(gpu, seed=61)
+    _oracle_b1_pool(w, 2, 8, gpu, seed=4)
+    pages = [e for _, _, e in _full_pages_by_class(w) if oracle.entry_class(e)[0] != 0]
+    pages += [B1 | 0, B1 | 1]
+    n = len(pages)
+    pool_k = torch.zeros((n, w.num_kv_heads, w.page_tokens, w.head_dim), device=gpu)
+    pool_v = torch.zeros_like(pool_k)
+    dummy_q = torch.zeros((1, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=gpu)
+    args = atlas.make_args(q=dummy_q, k_pool=pool_k, v_pool=pool_v,
+                           page_table=torch.zeros((1, 4), dtype=torch.int32, device=gpu),
+                           context_lens=torch.ones(1, dtype=torch.int32, device=gpu),
+                           num_heads=w.num_heads, num_kv_heads=w.num_kv_heads,
+                           head_dim=w.head_dim, page_tokens=w.page_tokens, max_context_len=1,
+                           scale=0.1, out=torch.empty((1, w.num_heads, w.head_dim), device=gpu),
+                           lse=torch.empty((1, w.num_heads), device=gpu), kv_dtype=atlas.F32,
+                           q_dtype=atlas.BF16)
+    tiers = atlas.make_tiers(w.tiers)
+    rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+    atlas.atlas_promote_pages(args, tiers,
+                              torch.from_numpy(np.array(pages, np.uint32).view(np.int32)).to(gpu),
+                              torch.arange(n, dtype=torch.int32, device=gpu), rej)
+    torch.cuda.synchronize()
+    assert int(rej) == 0
+    host = oracle.HostView(w)
+    for kv, pool in (("k", pool_k), ("v", pool_v)):
+        got = pool.cpu().numpy()
+        for i, e in enumerate(pages):
+            for g in range(w.num_kv_heads):
+                want = oracle.hot_bits(oracle.block_f32(w, e, g, kv, host=host), "f32")
+                assert np.array_equal(got[i, g].view(np.uint32), want), (i, kv, g)
