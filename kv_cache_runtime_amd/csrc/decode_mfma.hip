@@ -461,6 +461,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto in_range = [&](int tok) { return tok >= t0 && tok < t1; };
 
+    if constexpr (G == 4) {  // the P columns of heads 4-15 are never written
+#pragma unroll
+        for (int part = 0; part < NP; ++part)
+#pragma unroll
+            for (int j = 0; j < kTileTok * 16 / (64 * 8); ++j)
+                *reinterpret_cast<uint4 *>(pt + part * kTileTok * 16 + 8 * (lane + 64 * j)) =
+                    make_uint4(0u, 0u, 0u, 0u);
+    }
+
     // Walks the tiles of one run of pages with one tier: the whole split in
     // token order (natural), or the sp .. sp + np - 1 staged entries of a
     // tier.  Each wave takes every fourth tile of the run.
@@ -518,6 +527,124 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         uint4 kr[4][NC], vr[4][NC];
         float kscale[4], vscale[4];
         bool kok[4], vok[4];
+
+        // Four query heads per kv head: the score tiles hold them in the first
+        // 16 lanes only.  The softmax of a 64-token tile then runs on one packed
+        // register per head instead of four: lane (r, c) holds token 16 r + c
+        // (group r), moved there by two 16-lane swaps and a 32-lane swap.  The
+        // head max and the rescale factors are wave-uniform; P is written for
+        // heads 0-3 (the other columns of the P tile stay zero).
+        auto softmax_packed = [&](const f32x4_t (&sc)[4], const float (&kf)[4],
+                                  const bool (&kvalid)[4], const int (&tok)[4]) {
+            float ps[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const auto s01 = __builtin_amdgcn_permlane16_swap(
+                    __float_as_uint(sc[0][i]), __float_as_uint(sc[1][i]), false, false);
+                const auto s23 = __builtin_amdgcn_permlane16_swap(
+                    __float_as_uint(sc[2][i]), __float_as_uint(sc[3][i]), false, false);
+                const auto sw = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+                ps[i] = __uint_as_float(sw[0]);
+            }
+            // this lane's group r: K scale, visibility, V scale, first token.
+            // Two-level selects on the bits of r, from values held one by one (a
+            // select chain over an array would become an indexed stack load).
+            const bool r1 = (r & 1) != 0, r2 = (r & 2) != 0;
+            auto pick = [&](auto a0, auto a1, auto a2, auto a3) {
+                return r2 ? (r1 ? a3 : a2) : (r1 ? a1 : a0);
+            };
+            const float kf0 = kf[0], kf1 = kf[1], kf2 = kf[2], kf3 = kf[3];
+            const float kfl = pick(kf0, kf1, kf2, kf3);
+            const bool v0 = kvalid[0], v1 = kvalid[1], v2 = kvalid[2], v3 = kvalid[3];
+            const bool vis = pick(v0, v1, v2, v3);
+            float vsl = 1.0f;
+            if constexpr (TIER != kHot) {
+                const float vs0 = vscale[0], vs1 = vscale[1], vs2 = vscale[2], vs3 = vscale[3];
+                vsl = pick(vs0, vs1, vs2, vs3);
+            }
+            const int tk0 = tok[0], tk1 = tok[1], tk2 = tok[2], tk3 = tok[3];
+            const int tokl = pick(tk0, tk1, tk2, tk3);
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) ps[i] = vis ? ps[i] * kfl : kNegInf;
+            if (alibi) {  // wave-uniform
+                const float4 ab = *reinterpret_cast<const float4 *>(&s_ab[0]);
+                const float dist = (float)(tokl + c - qpos);
+                ps[0] = fmaf(ab.x, dist, ps[0]);
+                ps[1] = fmaf(ab.y, dist, ps[1]);
+                ps[2] = fmaf(ab.z, dist, ps[2]);
+                ps[3] = fmaf(ab.w, dist, ps[3]);
+            }
+            bool move_any = false;
+            float alpha[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float mx = ps[i];
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x128>(mx));
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x124>(mx));
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x122>(mx));
+                mx = __builtin_elementwise_maximum(mx, dpp_f<0x121>(mx));
+                const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                                __float_as_uint(mx), false, false);
+                mx = __builtin_elementwise_maximum(__uint_as_float(h[0]), __uint_as_float(h[1]));
+                const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx),
+                                                                __float_as_uint(mx), false, false);
+                mx = __builtin_elementwise_maximum(__uint_as_float(q[0]), __uint_as_float(q[1]));
+                const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
+                const float m_new = move ? mx : m_ref[i];
+                alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;
+                move_any = move_any || move;
+                m_ref[i] = m_new;
+            }
+            if (__any(move_any)) {  // wave-uniform
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) l[i] *= alpha[i];
+                const float ac = c == 0 ? alpha[0] : c == 1 ? alpha[1] : c == 2 ? alpha[2]
+                                 : c == 3 ? alpha[3] : 1.0f;
+    #pragma unroll
+                for (int mb = 0; mb < 8; ++mb) acc[mb] *= ac;
+            }
+            float pr[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float m_off = (m_ref[i] == kNegInf) ? 0.0f : m_ref[i] - kPScale;
+                pr[i] = __builtin_amdgcn_exp2f(ps[i] - m_off);
+                if constexpr (TIER != kHot) {
+                    l[i] += pr[i];
+                    pr[i] *= vsl;
+                }
+            }
+            uint2 hi, lo;
+            if constexpr (QT == KV_BF16) {
+                uint32_t hb[4], lb[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t u = __float_as_uint(pr[i]);
+                    const uint32_t h16 = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                    const float hf = __uint_as_float(h16 << 16);
+                    const uint32_t v = __float_as_uint(pr[i] - hf);
+                    const uint32_t l16 = (v + 0x7FFFu + ((v >> 16) & 1u)) >> 16;
+                    hb[i] = h16;
+                    lb[i] = l16;
+                    l[i] += hf + __uint_as_float(l16 << 16);
+                }
+                hi = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                lo = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+            } else {
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                const h2 a = {(_Float16)pr[0], (_Float16)pr[1]};
+                const h2 b = {(_Float16)pr[2], (_Float16)pr[3]};
+                if constexpr (TIER == kHot) {
+                    l[0] += (float)a[0];
+                    l[1] += (float)a[1];
+                    l[2] += (float)b[0];
+                    l[3] += (float)b[1];
+                }
+                hi = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+                lo = make_uint2(0u, 0u);
+            }
+            *reinterpret_cast<uint2 *>(pt + (16 * r + c) * 16) = hi;
+            if constexpr (NP == 2) *reinterpret_cast<uint2 *>(pt + kTileTok * 16 + (16 * r + c) * 16) = lo;
+        };
         auto load_k = [&](const Groups &G_, int tg) {
             kok[tg] = G_.live[tg];
             kscale[tg] = 1.0f;
@@ -596,109 +723,113 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             // next tile's K (its registers are free once the scores are issued)
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) load_k(nxt, tg);
-#pragma unroll
-            for (int tg = 0; tg < 4; ++tg) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sc[tg][i] = kvalid[tg] ? sc[tg][i] * kf[tg] : kNegInf;
-            }
-            if (alibi) {  // wave-uniform
-                const float4 ab = *reinterpret_cast<const float4 *>(&s_ab[4 * r]);
-#pragma unroll
+            if constexpr (G == 4) {
+                softmax_packed(sc, kf, kvalid, cur.tok);
+            } else {
+    #pragma unroll
                 for (int tg = 0; tg < 4; ++tg) {
-                    const float dist = (float)(cur.tok[tg] + c - qpos);
-                    sc[tg][0] = fmaf(ab.x, dist, sc[tg][0]);
-                    sc[tg][1] = fmaf(ab.y, dist, sc[tg][1]);
-                    sc[tg][2] = fmaf(ab.z, dist, sc[tg][2]);
-                    sc[tg][3] = fmaf(ab.w, dist, sc[tg][3]);
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) sc[tg][i] = kvalid[tg] ? sc[tg][i] * kf[tg] : kNegInf;
                 }
-            }
+                if (alibi) {  // wave-uniform
+                    const float4 ab = *reinterpret_cast<const float4 *>(&s_ab[4 * r]);
+    #pragma unroll
+                    for (int tg = 0; tg < 4; ++tg) {
+                        const float dist = (float)(cur.tok[tg] + c - qpos);
+                        sc[tg][0] = fmaf(ab.x, dist, sc[tg][0]);
+                        sc[tg][1] = fmaf(ab.y, dist, sc[tg][1]);
+                        sc[tg][2] = fmaf(ab.z, dist, sc[tg][2]);
+                        sc[tg][3] = fmaf(ab.w, dist, sc[tg][3]);
+                    }
+                }
 
-            // ---- online softmax, one reference max per head (uniform in a row)
-            bool move_any = false;
-            float alpha[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // IEEE maximum (v_maximum3_f32): no operand canonicalisation,
-                // and a NaN score (from NaN keys) propagates into the row
-                float mx = __builtin_elementwise_maximum(
-                    __builtin_elementwise_maximum(sc[0][i], sc[1][i]),
-                    __builtin_elementwise_maximum(sc[2][i], sc[3][i]));
-                mx = __builtin_elementwise_maximum(mx, dpp_f<0x128>(mx));
-                mx = __builtin_elementwise_maximum(mx, dpp_f<0x124>(mx));
-                mx = __builtin_elementwise_maximum(mx, dpp_f<0x122>(mx));
-                mx = __builtin_elementwise_maximum(mx, dpp_f<0x121>(mx));
-                const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
-                const float m_new = move ? mx : m_ref[i];
-                alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;
-                move_any = move_any || move;
-                m_ref[i] = m_new;
-            }
-            if (__any(move_any)) {  // wave-uniform
-#pragma unroll
-                for (int i = 0; i < 4; ++i) l[i] *= alpha[i];
-                // alpha of head c, from the score layout (row c / 4, register c % 4)
-                float ac = 1.0f;
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float ah = __int_as_float(
-                        __builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
-                    ac = c == h ? ah : ac;
-                }
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb) acc[mb] *= ac;
-            }
-            // probabilities of token tok[tg] + c, heads 4 r .. 4 r + 3 -> P
-            // tile (token-major, 16 heads), scaled by the group's V scale.
-            // Resident pages add the rounded weights the matrix cores use to
-            // l, so the normalisation matches them exactly (a constant V row
-            // comes back unchanged); cold pages add the unscaled weights.
-#pragma unroll
-            for (int tg = 0; tg < 4; ++tg) {
-                float pr[4];
-#pragma unroll
+                // ---- online softmax, one reference max per head (uniform in a row)
+                bool move_any = false;
+                float alpha[4];
+    #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float m_off = (m_ref[i] == kNegInf) ? 0.0f : m_ref[i] - kPScale;
-                    pr[i] = __builtin_amdgcn_exp2f(sc[tg][i] - m_off);
-                    if constexpr (TIER != kHot) {
-                        l[i] += pr[i];
-                        pr[i] *= vscale[tg];
-                    }
+                    // IEEE maximum (v_maximum3_f32): no operand canonicalisation,
+                    // and a NaN score (from NaN keys) propagates into the row
+                    float mx = __builtin_elementwise_maximum(
+                        __builtin_elementwise_maximum(sc[0][i], sc[1][i]),
+                        __builtin_elementwise_maximum(sc[2][i], sc[3][i]));
+                    mx = __builtin_elementwise_maximum(mx, dpp_f<0x128>(mx));
+                    mx = __builtin_elementwise_maximum(mx, dpp_f<0x124>(mx));
+                    mx = __builtin_elementwise_maximum(mx, dpp_f<0x122>(mx));
+                    mx = __builtin_elementwise_maximum(mx, dpp_f<0x121>(mx));
+                    const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
+                    const float m_new = move ? mx : m_ref[i];
+                    alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;
+                    move_any = move_any || move;
+                    m_ref[i] = m_new;
                 }
-                uint2 hi, lo;
-                if constexpr (QT == KV_BF16) {
-                    uint32_t hb[4], lb[4];
-#pragma unroll
+                if (__any(move_any)) {  // wave-uniform
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) l[i] *= alpha[i];
+                    // alpha of head c, from the score layout (row c / 4, register c % 4)
+                    float ac = 1.0f;
+    #pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float ah = __int_as_float(
+                            __builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+                        ac = c == h ? ah : ac;
+                    }
+    #pragma unroll
+                    for (int mb = 0; mb < 8; ++mb) acc[mb] *= ac;
+                }
+                // probabilities of token tok[tg] + c, heads 4 r .. 4 r + 3 -> P
+                // tile (token-major, 16 heads), scaled by the group's V scale.
+                // Resident pages add the rounded weights the matrix cores use to
+                // l, so the normalisation matches them exactly (a constant V row
+                // comes back unchanged); cold pages add the unscaled weights.
+    #pragma unroll
+                for (int tg = 0; tg < 4; ++tg) {
+                    float pr[4];
+    #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        // round to nearest even; the remainder is exact in
-                        // f32, and so is hi + lo
-                        const uint32_t u = __float_as_uint(pr[i]);
-                        const uint32_t h16 = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-                        const float hf = __uint_as_float(h16 << 16);
-                        const uint32_t v = __float_as_uint(pr[i] - hf);
-                        const uint32_t l16 = (v + 0x7FFFu + ((v >> 16) & 1u)) >> 16;
-                        hb[i] = h16;
-                        lb[i] = l16;
-                        l[i] += hf + __uint_as_float(l16 << 16);
+                        const float m_off = (m_ref[i] == kNegInf) ? 0.0f : m_ref[i] - kPScale;
+                        pr[i] = __builtin_amdgcn_exp2f(sc[tg][i] - m_off);
+                        if constexpr (TIER != kHot) {
+                            l[i] += pr[i];
+                            pr[i] *= vscale[tg];
+                        }
                     }
-                    hi = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-                    lo = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
-                } else {
-                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                    const h2 a = {(_Float16)pr[0], (_Float16)pr[1]};
-                    const h2 b = {(_Float16)pr[2], (_Float16)pr[3]};
-                    if constexpr (TIER == kHot) {
-                        l[0] += (float)a[0];
-                        l[1] += (float)a[1];
-                        l[2] += (float)b[0];
-                        l[3] += (float)b[1];
+                    uint2 hi, lo;
+                    if constexpr (QT == KV_BF16) {
+                        uint32_t hb[4], lb[4];
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            // round to nearest even; the remainder is exact in
+                            // f32, and so is hi + lo
+                            const uint32_t u = __float_as_uint(pr[i]);
+                            const uint32_t h16 = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                            const float hf = __uint_as_float(h16 << 16);
+                            const uint32_t v = __float_as_uint(pr[i] - hf);
+                            const uint32_t l16 = (v + 0x7FFFu + ((v >> 16) & 1u)) >> 16;
+                            hb[i] = h16;
+                            lb[i] = l16;
+                            l[i] += hf + __uint_as_float(l16 << 16);
+                        }
+                        hi = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                        lo = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+                    } else {
+                        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                        const h2 a = {(_Float16)pr[0], (_Float16)pr[1]};
+                        const h2 b = {(_Float16)pr[2], (_Float16)pr[3]};
+                        if constexpr (TIER == kHot) {
+                            l[0] += (float)a[0];
+                            l[1] += (float)a[1];
+                            l[2] += (float)b[0];
+                            l[3] += (float)b[1];
+                        }
+                        hi = make_uint2(__builtin_bit_cast(uint32_t, a),
+                                        __builtin_bit_cast(uint32_t, b));
+                        lo = make_uint2(0u, 0u);
                     }
-                    hi = make_uint2(__builtin_bit_cast(uint32_t, a),
-                                    __builtin_bit_cast(uint32_t, b));
-                    lo = make_uint2(0u, 0u);
+                    *reinterpret_cast<uint2 *>(pt + (16 * tg + c) * 16 + 4 * r) = hi;
+                    if constexpr (NP == 2)
+                        *reinterpret_cast<uint2 *>(pt + kTileTok * 16 + (16 * tg + c) * 16 + 4 * r) = lo;
                 }
-                *reinterpret_cast<uint2 *>(pt + (16 * tg + c) * 16 + 4 * r) = hi;
-                if constexpr (NP == 2)
-                    *reinterpret_cast<uint2 *>(pt + kTileTok * 16 + (16 * tg + c) * 16 + 4 * r) = lo;
             }
 
             // ---- P.V on the matrix cores, one 32-token half at a time
@@ -771,7 +902,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     // ---- merge the waves: l is summed over the 16 lanes of the row holding
     // the head; the wave's accumulators go to its own (now unused) V tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l[i] = row16_sum(l[i]);
+    for (int i = 0; i < 4; ++i) {
+        l[i] = row16_sum(l[i]);
+        if constexpr (G == 4) {  // packed softmax: the head's sum spans all four rows
+            const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[i]),
+                                                            __float_as_uint(l[i]), false, false);
+            l[i] = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+            const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(l[i]),
+                                                            __float_as_uint(l[i]), false, false);
+            l[i] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+        }
+    }
     __builtin_amdgcn_wave_barrier();
     float *s_acc = reinterpret_cast<float *>(vt);  // [G][kD] of this wave
     if (c < G) {
