@@ -13,7 +13,10 @@
 //    every K load is 16 tokens x 64 contiguous bytes; the result has token
 //    l % 16 in lane l and heads 4 (l / 16) .. + 3 in its four registers.
 //  * Softmax: one reference max per head, moved only when a tile's max
-//    exceeds it by 2^8, reduced within 16-lane rows by DPP.
+//    exceeds it by 2^8, reduced within 16-lane rows by DPP.  With four query
+//    heads per kv head the heads sit in the first row only, so the four
+//    16-token groups are first packed into the four rows (lane swaps) and
+//    the softmax runs on one register per head.
 //  * P.V: O^T[dim][head] += V^T[dim][token] P^T[token][head], also on
 //    v_mfma_f32_16x16x32.  V rows are written to LDS as they are stored
 //    (token-major, int codes widened to f16 on the way) and read back as the
