@@ -138,34 +138,37 @@ constexpr int chunks() { return TIER == kHot ? 4 : TIER == kByte ? 2 : 1; }
 // (hot: 64 bytes, int8: 32, int4: 16), widened by widen_k.  Returns the K
 // scale; false if the slot is outside its pool.
 template <int KV, int MODE, int TIER>
-__device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slot, int g, int row,
-                                             int r, uint4 (&kr)[chunks<TIER>()], float &kscale,
-                                             bool alt) {
+__device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slot, int g, int row0,
+                                             int c, int r, uint4 (&kr)[chunks<TIER>()],
+                                             float &kscale, bool alt) {
     kscale = 1.0f;
-    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row;
+    // the group's first row (wave-uniform) and this lane's row c within it,
+    // kept apart so that the address is a scalar base plus a lane offset
+    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row0;
     if constexpr (TIER == kHot) {
         if (slot >= (uint32_t)p.num_blocks) return false;
         const uint16_t *src = reinterpret_cast<const uint16_t *>(p.k_pool) + r0 * kD;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int d0 = MODE == MODE_TIERED ? 32 * r + 8 * ks : 32 * ks + 8 * r;
-            kr[ks] = *reinterpret_cast<const uint4 *>(src + d0);
+            kr[ks] = *reinterpret_cast<const uint4 *>(src + (c * kD + d0));
         }
     } else if constexpr (TIER == kByte) {
         if (slot >= (uint32_t)(alt ? p.n_f8 : p.n_i8)) return false;
         const uint8_t *pool = alt ? p.f8_k : reinterpret_cast<const uint8_t *>(p.i8_k);
-        const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD + 32 * r);
+        const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD + (c * kD + 32 * r));
         kscale = (alt ? p.f8_ks : p.i8_ks)[(int64_t)slot * p.num_kv_heads + g];
         kr[0] = src[0];
         kr[1] = src[1];
     } else if (alt) {  // INT2: dims 32 r .. 32 r + 31 are 8 bytes
         if (slot >= (uint32_t)p.n_i2) return false;
-        const uint2 v = *reinterpret_cast<const uint2 *>(p.i2_k + r0 * (kD / 4) + 8 * r);
+        const uint2 v = *reinterpret_cast<const uint2 *>(p.i2_k + r0 * (kD / 4) +
+                                                          (c * (kD / 4) + 8 * r));
         kr[0] = make_uint4(v.x, v.y, 0u, 0u);
         kscale = p.i2_ks[(int64_t)slot * p.num_kv_heads + g];
     } else {
         if (slot >= (uint32_t)p.n_i4) return false;
-        kr[0] = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + 16 * r);
+        kr[0] = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + (c * (kD / 2) + 16 * r));
         kscale = p.i4_ks[(int64_t)slot * p.num_kv_heads + g];
     }
     return true;
@@ -651,7 +654,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         auto load_k = [&](const Groups &G_, int tg) {
             kok[tg] = G_.live[tg];
             kscale[tg] = 1.0f;
-            if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.row[tg] + c, r,
+            if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.row[tg], c, r,
                                                          kr[tg], kscale[tg], alt)) {
                 bad = true;
                 kok[tg] = false;
