@@ -461,8 +461,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the attention path has no multi-GPU "
-              "mode in this build (each GPU would run its own shard of sequences or "
-              "kv heads independently); run with --gpus 1.", file=sys.stderr)
+              "mode (each GPU would run its own shard of sequences or kv heads "
+              "independently); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
