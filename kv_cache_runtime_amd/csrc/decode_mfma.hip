@@ -132,21 +132,19 @@ constexpr int kHot = 0, kByte = 1, kSub = 2;
 template <int TIER>
 constexpr int chunks() { return TIER == kHot ? 4 : TIER == kByte ? 2 : 1; }
 
-// Raw K of row `row` of a page (slot) for this lane (row r of the 16-lane
-// rows).  Resident pages give the four operands directly (operand ks = dims
-// 32 ks + 8 r .. + 8); tiered pages give dims 32 r .. 32 r + 31 as one run
-// (hot: 64 bytes, int8: 32, int4: 16), widened by widen_k.  Returns the K
-// scale; false if the slot is outside its pool.
+// Raw K of row row0 + c of a group for this lane (row r of the 16-lane
+// rows).  `base` is the first row of the group's (slot, kv head) block in its
+// pool, negative for an entry outside its pool (then nothing is read and the
+// call returns false).  Resident pages give the four operands directly
+// (operand ks = dims 32 ks + 8 r .. + 8); tiered pages give dims 32 r .. 32 r
+// + 31 as one run (hot: 64 bytes, int8: 32, int4: 16), widened by widen_k.
+// The row is a wave-uniform base plus this lane's offset c.
 template <int KV, int MODE, int TIER>
-__device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slot, int g, int row0,
-                                             int c, int r, uint4 (&kr)[chunks<TIER>()],
-                                             float &kscale, bool alt) {
-    kscale = 1.0f;
-    // the group's first row (wave-uniform) and this lane's row c within it,
-    // kept apart so that the address is a scalar base plus a lane offset
-    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row0;
+__device__ __forceinline__ bool load_k_group(const DecodeParams &p, int64_t base, int row0, int c,
+                                             int r, uint4 (&kr)[chunks<TIER>()], bool alt) {
+    if (base < 0) return false;
+    const int64_t r0 = base + row0;
     if constexpr (TIER == kHot) {
-        if (slot >= (uint32_t)p.num_blocks) return false;
         const uint16_t *src = reinterpret_cast<const uint16_t *>(p.k_pool) + r0 * kD;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -154,22 +152,16 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, uint32_t slo
             kr[ks] = *reinterpret_cast<const uint4 *>(src + (c * kD + d0));
         }
     } else if constexpr (TIER == kByte) {
-        if (slot >= (uint32_t)(alt ? p.n_f8 : p.n_i8)) return false;
         const uint8_t *pool = alt ? p.f8_k : reinterpret_cast<const uint8_t *>(p.i8_k);
         const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD + (c * kD + 32 * r));
-        kscale = (alt ? p.f8_ks : p.i8_ks)[(int64_t)slot * p.num_kv_heads + g];
         kr[0] = src[0];
         kr[1] = src[1];
     } else if (alt) {  // INT2: dims 32 r .. 32 r + 31 are 8 bytes
-        if (slot >= (uint32_t)p.n_i2) return false;
         const uint2 v = *reinterpret_cast<const uint2 *>(p.i2_k + r0 * (kD / 4) +
                                                           (c * (kD / 4) + 8 * r));
         kr[0] = make_uint4(v.x, v.y, 0u, 0u);
-        kscale = p.i2_ks[(int64_t)slot * p.num_kv_heads + g];
     } else {
-        if (slot >= (uint32_t)p.n_i4) return false;
         kr[0] = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + (c * (kD / 2) + 16 * r));
-        kscale = p.i4_ks[(int64_t)slot * p.num_kv_heads + g];
     }
     return true;
 }
@@ -220,36 +212,28 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
 }
 
 // Raw V of one 16-token group (rows row0 .. row0 + 15 of a page, one
-// contiguous slab): lane l takes 16-byte chunks l, l + 64, ...  Returns the V
-// scale; false if the slot is outside its pool.
+// contiguous slab): lane l takes 16-byte chunks l, l + 64, ...  `base` as for
+// load_k_group (false, nothing read, when negative).
 template <int KV, int TIER>
-__device__ __forceinline__ bool load_v_group(const DecodeParams &p, uint32_t slot, int g, int row0,
-                                             int lane, uint4 (&vr)[chunks<TIER>()],
-                                             float &vscale, bool alt) {
-    vscale = 1.0f;
-    const int64_t r0 = ((int64_t)slot * p.num_kv_heads + g) * p.page_tokens + row0;
+__device__ __forceinline__ bool load_v_group(const DecodeParams &p, int64_t base, int row0,
+                                             int lane, uint4 (&vr)[chunks<TIER>()], bool alt) {
+    if (base < 0) return false;
+    const int64_t r0 = base + row0;
     if constexpr (TIER == kHot) {
-        if (slot >= (uint32_t)p.num_blocks) return false;
         const uint4 *src = reinterpret_cast<const uint4 *>(
             reinterpret_cast<const uint16_t *>(p.v_pool) + r0 * kD);
 #pragma unroll
         for (int i = 0; i < 4; ++i) vr[i] = src[64 * i + lane];
     } else if constexpr (TIER == kByte) {
-        if (slot >= (uint32_t)(alt ? p.n_f8 : p.n_i8)) return false;
         const uint8_t *pool = alt ? p.f8_v : reinterpret_cast<const uint8_t *>(p.i8_v);
         const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD);
-        vscale = (alt ? p.f8_vs : p.i8_vs)[(int64_t)slot * p.num_kv_heads + g];
         vr[0] = src[lane];
         vr[1] = src[64 + lane];
     } else if (alt) {  // INT2: 8 bytes per lane
-        if (slot >= (uint32_t)p.n_i2) return false;
         const uint2 v = reinterpret_cast<const uint2 *>(p.i2_v + r0 * (kD / 4))[lane];
-        vscale = p.i2_vs[(int64_t)slot * p.num_kv_heads + g];
         vr[0] = make_uint4(v.x, v.y, 0u, 0u);
     } else {
-        if (slot >= (uint32_t)p.n_i4) return false;
         const uint4 *src = reinterpret_cast<const uint4 *>(p.i4_v + r0 * (kD / 2));
-        vscale = p.i4_vs[(int64_t)slot * p.num_kv_heads + g];
         vr[0] = src[lane];
     }
     return true;
@@ -391,9 +375,40 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
     const int lp_count = t1 > t0 ? (t1 - 1) / P - lp_first + 1 : 0;
     const bool staged = lp_count <= kStagedPages;
     int tier_count[kClasses] = {0, 0, 0, 0, 0, 0};
+    // tiered splits: per staged page, the first row of its (slot, kv head)
+    // block in its pool (-1 outside the pool) and its K and V scales, computed
+    // once here instead of per tile and group
+    __shared__ int64_t s_base[MODE == MODE_TIERED ? kStagedPages : 1];
+    __shared__ float s_ksc[MODE == MODE_TIERED ? kStagedPages : 1];
+    __shared__ float s_vsc[MODE == MODE_TIERED ? kStagedPages : 1];
     if constexpr (MODE == MODE_TIERED) {
-        stage_pages_by_tier(trow + lp_first, min(lp_count, kStagedPages), s_pages, s_lp,
-                            tier_count);
+        const int n_st = min(lp_count, kStagedPages);
+        stage_pages_by_tier(trow + lp_first, n_st, s_pages, s_lp, tier_count);
+        // staged positions are sorted by class: hot, int8, int4, FP8, INT2, other
+        const int b1 = tier_count[0], b2 = b1 + tier_count[1], b3 = b2 + tier_count[2];
+        const int b4 = b3 + tier_count[3], b5 = b4 + tier_count[4];
+        for (int i = tid; i < n_st; i += 256) {
+            const uint32_t sl = (uint32_t)s_pages[i];
+            uint32_t cap = 0;
+            const float *ksp = nullptr, *vsp = nullptr;
+            if (i < b1) {
+                cap = (uint32_t)p.num_blocks;
+            } else if (i < b2) {
+                cap = (uint32_t)p.n_i8, ksp = p.i8_ks, vsp = p.i8_vs;
+            } else if (i < b3) {
+                cap = (uint32_t)p.n_i4, ksp = p.i4_ks, vsp = p.i4_vs;
+            } else if (i < b4) {
+                cap = (uint32_t)p.n_f8, ksp = p.f8_ks, vsp = p.f8_vs;
+            } else if (i < b5) {
+                cap = (uint32_t)p.n_i2, ksp = p.i2_ks, vsp = p.i2_vs;
+            }
+            const bool ok = sl < cap;  // cap 0 past the attended classes
+            const int64_t blk = (int64_t)sl * p.num_kv_heads + g;
+            s_base[i] = ok ? blk * P : (int64_t)-1;
+            s_ksc[i] = ok && ksp ? ksp[blk] : 1.0f;
+            s_vsc[i] = ok && vsp ? vsp[blk] : 1.0f;
+        }
+        __syncthreads();
     } else {
         if (staged)
             for (int i = tid; i < lp_count; i += 256) s_pages[i] = trow[lp_first + i];
@@ -492,7 +507,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         struct Groups {
             int tok[4];       // first token
             int row[4];       // its row in the page
-            uint32_t slot[4];
+            int64_t base[4];  // first row of the (slot, kv head) block, -1 outside the pool
+            float ks[4], vs[4];  // K and V scales (1 for resident pages)
             bool live[4];
         };
         auto page_div = [&](int x) {  // x / P, x < 2^31
@@ -504,13 +520,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                 const int q = tile * kTileTok + 16 * tg;
                 bool live;
                 int tok, row0;
-                uint32_t ent;
                 if constexpr (natural) {
                     tok = t0 + q;
                     live = tile < n_tiles && tok < t1;
                     const int lp = page_div(tok);
                     row0 = tok - lp * P;
-                    ent = live ? (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]) : 0u;
+                    const uint32_t ent = __builtin_amdgcn_readfirstlane(
+                        live ? (uint32_t)(staged ? s_pages[lp - lp_first] : trow[lp]) : 0u);
+                    G_.base[tg] = ent < (uint32_t)p.num_blocks
+                                      ? ((int64_t)ent * p.num_kv_heads + g) * P : (int64_t)-1;
+                    G_.ks[tg] = 1.0f;
+                    G_.vs[tg] = 1.0f;
                 } else {
                     const int pi = page_div(q);
                     live = tile < n_tiles && pi < np;
@@ -518,15 +538,20 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                     // four groups' LDS reads are in flight together
                     const int si = min(sp + (live ? pi : 0), kStagedPages - 1);
                     const int lpv = s_lp[si];
-                    const uint32_t entv = (uint32_t)s_pages[si];
+                    const int64_t bv = s_base[si];
+                    const float ksv = s_ksc[si], vsv = s_vsc[si];
                     const int lp = lp_first + (live ? lpv : 0);
                     row0 = q - pi * P;
                     tok = lp * P + row0;
-                    ent = live ? entv : 0u;
+                    const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)bv);
+                    const uint32_t bhi =
+                        __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)bv >> 32));
+                    G_.base[tg] = (int64_t)(((uint64_t)bhi << 32) | blo);
+                    G_.ks[tg] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ksv)));
+                    G_.vs[tg] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vsv)));
                 }
                 G_.tok[tg] = __builtin_amdgcn_readfirstlane(tok);
                 G_.row[tg] = __builtin_amdgcn_readfirstlane(row0);
-                G_.slot[tg] = __builtin_amdgcn_readfirstlane(ent);
                 G_.live[tg] = live;
             }
         };
@@ -653,9 +678,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         };
         auto load_k = [&](const Groups &G_, int tg) {
             kok[tg] = G_.live[tg];
-            kscale[tg] = 1.0f;
-            if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.slot[tg], g, G_.row[tg], c, r,
-                                                         kr[tg], kscale[tg], alt)) {
+            kscale[tg] = G_.ks[tg];
+            if (kok[tg] && !load_k_group<KV, MODE, TIER>(p, G_.base[tg], G_.row[tg], c, r,
+                                                         kr[tg], alt)) {
                 bad = true;
                 kok[tg] = false;
             }
@@ -666,9 +691,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         };
         auto load_v = [&](const Groups &G_, int tg) {
             vok[tg] = G_.live[tg];
-            vscale[tg] = 1.0f;
-            if (vok[tg] && !load_v_group<KV, TIER>(p, G_.slot[tg], g, G_.row[tg], lane,
-                                                   vr[tg], vscale[tg], alt)) {
+            vscale[tg] = G_.vs[tg];
+            if (vok[tg] && !load_v_group<KV, TIER>(p, G_.base[tg], G_.row[tg], lane, vr[tg],
+                                                   alt)) {
                 bad = true;
                 vok[tg] = false;
             }
