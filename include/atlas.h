@@ -422,8 +422,9 @@ atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new,
  * scales are written through the pools' pointers; the caller then points its
  * page-table entries at dst_entries.  A destination outside its pool, or a
  * 1-bit source (use atlas_promote_pages), rejects the page (nothing written);
- * a source outside its pool writes NaN scales, so rows reading the page fail
- * loudly.  Each rejected page adds 1 to *rejected (device int32, optional).
+ * a source outside its pool writes NaN scales (and, into a 1-bit slot, NaN
+ * outlier values at index 0), so every value read from the page is NaN.
+ * Each rejected page adds 1 to *rejected (device int32, optional).
  * The source and destination sets must not overlap between calls in flight.
  * Asynchronous on args->stream.
  */

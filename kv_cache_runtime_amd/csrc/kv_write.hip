@@ -478,7 +478,12 @@ __global__ __launch_bounds__(256) void archive_kernel(const DemoteParams d) {
     float *sdst = (kv ? d.b1_vs : d.b1_ks) + dblk;
     if (!dst_ok || !src_ok) {
         if (lane == 0 && g == 0 && kv == 0 && d.rejected) atomicAdd(d.rejected, 1);
-        if (dst_ok && stier != CLS_B1 && lane == 0) *sdst = __builtin_nanf("");
+        if (dst_ok && stier != CLS_B1) {
+            // poison the slot: NaN scale, and every outlier a NaN at index 0,
+            // so no stale outlier decodes to a finite value
+            if (lane == 0) *sdst = __builtin_nanf("");
+            if (lane < d.b1_nout) ((kv ? d.b1_vo : d.b1_ko) + dblk * d.b1_nout)[lane] = 0x7E00u << 16;
+        }
         return;
     }
     const int64_t n = (int64_t)d.page_tokens * d.head_dim;

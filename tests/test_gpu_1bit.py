@@ -169,6 +169,45 @@ def test_promote_rejections(gpu):
     assert torch.equal(w.k_pool[dst[2]], before)
 
 
+def test_archive_rejections(gpu):
+    """A source outside its pool poisons the 1-bit slot: after a valid
+    archive into slot 1, archiving a bad source there makes every value of
+    the slot NaN (no stale outlier survives).  A 1-bit source and a slot
+    outside the pool are rejected with nothing written."""
+    w = _case(gpu, seed=29)
+    n_b1 = 3
+    _add_b1_pool(w, n_b1, 8, gpu)
+    hot = next(e for _, _, e in _full_pages_by_class(w) if oracle.entry_class(e)[0] == 0)
+    prob = atlas.Problem(w)
+    rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+
+    def demote(src, dst):
+        atlas.atlas_demote_pages(
+            prob.args, prob.tiers,
+            torch.from_numpy(np.array(src, np.uint32).view(np.int32)).to(gpu),
+            torch.from_numpy(np.array(dst, np.uint32).view(np.int32)).to(gpu), rej)
+
+    demote([hot, hot], [B1 | 1, B1 | 2])
+    torch.cuda.synchronize()
+    assert int(rej) == 0
+    before = {kv: [w.tiers[f"b1_{kv}{x}"][2].clone() for x in ("", "_scale", "_out")]
+              for kv in ("k", "v")}
+    demote([w.num_blocks, B1 | 0, hot], [B1 | 1, B1 | 2, B1 | n_b1])
+    torch.cuda.synchronize()
+    assert int(rej) == 3
+    for kv in ("k", "v"):
+        assert torch.isnan(w.tiers[f"b1_{kv}_scale"][1]).all()
+        for t, x in zip(before[kv], ("", "_scale", "_out")):
+            assert torch.equal(w.tiers[f"b1_{kv}{x}"][2], t), (kv, x)
+    k = torch.empty((2, w.num_kv_heads, w.page_tokens, w.head_dim), device=gpu)
+    v = torch.empty_like(k)
+    ent = torch.from_numpy(np.array([B1 | 1, B1 | 2], np.uint32).view(np.int32)).to(gpu)
+    atlas.atlas_dequant_pages(prob.args, prob.tiers, ent, k, v)
+    torch.cuda.synchronize()
+    assert torch.isnan(k[0]).all() and torch.isnan(v[0]).all()
+    assert torch.isfinite(k[1]).all() and torch.isfinite(v[1]).all()
+
+
 def test_dequant_1bit_bit_exact(gpu):
     w = _case(gpu, seed=31)
     _oracle_b1_pool(w, 4, 64, gpu, seed=9)
