@@ -67,22 +67,36 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // code byte u under it gives the f16 0x64uu = 1024 + u.
 constexpr uint32_t kMagic64 = 0x64646464u;
 
+// The f16 offsets that the code widenings below subtract.  With BIASED set
+// a widening leaves the offset in (code + offset, still exact in f16); the
+// score kernel then starts its dot products from -offset * sum(q) instead.
+constexpr uint32_t kBiasI8 = 0x6480u;  // 1152
+constexpr uint32_t kBiasI4 = 0x6408u;  // 1032
+constexpr uint32_t kBiasI2 = 0x6402u;  // 1026
+
 // int8 codes (4 per word) -> f16 pairs, exact: bias to unsigned (u = c + 128),
 // form 0x64uu (= 1024 + u) with one byte permute per pair, subtract 1152.
+template <bool BIASED = false>
 __device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
     const uint32_t u = w ^ 0x80808080u;
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const uint32_t a = __builtin_amdgcn_perm(kMagic64, u, 0x05010400u);  // bytes 0, 1
     const uint32_t b = __builtin_amdgcn_perm(kMagic64, u, 0x05030402u);  // bytes 2, 3
-    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) - bias);
-    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - bias);
+    if constexpr (BIASED) {
+        lo = a;
+        hi = b;
+    } else {
+        const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+        lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) - bias);
+        hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - bias);
+    }
 }
 
 // int4 codes (8 per word, element e in nibble e, two's complement) -> f16
 // pairs (e, e + 1), exact: bias to unsigned nibbles, gather the even and the
 // odd elements into bytes, interleave them, place each byte under 0x64 and
 // subtract 1032.
+template <bool BIASED = false>
 __device__ __forceinline__ void i4x8_to_f16x8(uint32_t w, uint32_t (&out)[4]) {
     const uint32_t u = w ^ 0x88888888u;
     const uint32_t ev = u & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
@@ -95,10 +109,17 @@ __device__ __forceinline__ void i4x8_to_f16x8(uint32_t w, uint32_t (&out)[4]) {
     const uint32_t p1 = __builtin_amdgcn_perm(kMagic64, e03, 0x05030402u);
     const uint32_t p2 = __builtin_amdgcn_perm(kMagic64, e47, 0x05010400u);
     const uint32_t p3 = __builtin_amdgcn_perm(kMagic64, e47, 0x05030402u);
-    out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p0) - bias);
-    out[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p1) - bias);
-    out[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p2) - bias);
-    out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p3) - bias);
+    if constexpr (BIASED) {
+        out[0] = p0;
+        out[1] = p1;
+        out[2] = p2;
+        out[3] = p3;
+    } else {
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p0) - bias);
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p1) - bias);
+        out[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p2) - bias);
+        out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p3) - bias);
+    }
 }
 
 // FP8 E4M3 codes (4 per word) -> f16 pairs, exact, by the gfx950 hardware
@@ -111,6 +132,7 @@ __device__ __forceinline__ void f8x4_to_f16x4(uint32_t w, uint32_t &lo, uint32_t
 // INT2 codes (16 per word, element j in bits 2j, 2j + 1, two's complement)
 // -> f16 pairs (2m, 2m + 1), exact: bias each field to unsigned (f + 2),
 // place it under the f16 1024 and subtract 1026.
+template <bool BIASED = false>
 __device__ __forceinline__ void i2x16_to_f16x16(uint32_t w, uint32_t (&out)[8]) {
     const uint32_t u = w ^ 0xAAAAAAAAu;
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -118,7 +140,7 @@ __device__ __forceinline__ void i2x16_to_f16x16(uint32_t w, uint32_t (&out)[8]) 
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const uint32_t b = 0x64006400u | ((u >> (4 * m)) & 3u) | (((u >> (4 * m + 2)) & 3u) << 16);
-        out[m] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - bias);
+        out[m] = BIASED ? b : __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - bias);
     }
 }
 
@@ -131,6 +153,11 @@ constexpr int kHot = 0, kByte = 1, kSub = 2;
 // the low half of its one chunk)
 template <int TIER>
 constexpr int chunks() { return TIER == kHot ? 4 : TIER == kByte ? 2 : 1; }
+// f16 offset that widen_k leaves in the K operands of a class (0: none)
+template <int TIER, bool ALT>
+constexpr uint32_t k_offset() {
+    return TIER == kHot ? 0u : TIER == kByte ? (ALT ? 0u : kBiasI8) : (ALT ? kBiasI2 : kBiasI4);
+}
 
 // Raw K of row row0 + c of a group for this lane (row r of the 16-lane
 // rows).  `base` is the first row of the group's (slot, kv head) block in its
@@ -166,7 +193,8 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, int64_t base
     return true;
 }
 
-// Raw K -> the four 16-bit operands (codes widened to f16, exact).
+// Raw K -> the four 16-bit operands (codes widened to f16, exact; int8,
+// int4 and INT2 codes keep their offset, see k_offset_scores).
 template <int TIER>
 __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4 (&kb)[4],
                                        bool alt) {
@@ -187,8 +215,8 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 uint32_t a, b, c, d;
-                i8x4_to_f16x4(w[2 * ks], a, b);
-                i8x4_to_f16x4(w[2 * ks + 1], c, d);
+                i8x4_to_f16x4<true>(w[2 * ks], a, b);
+                i8x4_to_f16x4<true>(w[2 * ks + 1], c, d);
                 kb[ks] = make_uint4(a, b, c, d);
             }
         }
@@ -196,7 +224,7 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint32_t o[8];
-            i2x16_to_f16x16(h ? kr[0].y : kr[0].x, o);
+            i2x16_to_f16x16<true>(h ? kr[0].y : kr[0].x, o);
             kb[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
             kb[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
         }
@@ -205,7 +233,7 @@ __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             uint32_t o[4];
-            i4x8_to_f16x8(w[ks], o);
+            i4x8_to_f16x8<true>(w[ks], o);
             kb[ks] = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
@@ -501,6 +529,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         constexpr int NC = chunks<TIER>();
         const int n_pos = natural ? t1 - t0 : np * P;
         const int n_tiles = n_pos > 0 ? (n_pos + kTileTok - 1) / kTileTok : 0;
+        if (n_tiles == 0) return;
+
+        // Integer-code K operands carry the f16 offset b (code + b is exact),
+        // so each score starts from -b * sum(q) of its row instead of zero:
+        // one product of q with a constant-b operand, in the score layout
+        // (the remainder rows of a rotated q included).  This saves the
+        // subtraction of b from every widened code.
+        f32x4_t s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        constexpr uint32_t kOff = k_offset<TIER, alt>();
+        if constexpr (kOff != 0u) {
+            static_assert(QT == KV_F16, "the offsets are f16 values");
+            const uint32_t bb = kOff | (kOff << 16);
+            const uint4 ob = make_uint4(bb, bb, bb, bb);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) s0 = mfma16<QT>(qf[ks], ob, s0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s0[i] = -s0[i];
+        }
 
         // the 16-position groups of a tile: first token, slot and liveness,
         // all wave-uniform (a group lies in one page)
@@ -722,7 +768,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                 kvalid[tg] = kok[tg] && in_range(cur.tok[tg] + c);
                 uint4 kb[4];
                 widen_k<TIER>(kr[tg], kb, alt);
-                sc[tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                sc[tg] = s0;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) sc[tg] = mfma16<QT>(qf[ks], kb[ks], sc[tg]);
             }
