@@ -1,12 +1,17 @@
 """End-to-end decode loops driven by the host residency runtime on the GPU:
 the runtime's tables feed atlas_write_kv and the attention calls, its jobs
-run through atlas_demote_pages / atlas_regenerate_pages, and the attention
-results are checked against the oracle over the pools as they stand."""
+run through atlas_demote_pages / atlas_promote_pages /
+atlas_regenerate_pages, and the attention results are checked against the
+oracle.  The oracle never reads a device-written pool: tiered loops keep
+host shadow pools that the oracle writes (the same rows, encodings and
+reconstructions the runtime asks of the device), and the regenerated loop
+is checked on the call whose every page is regenerated."""
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from kv_cache_runtime_amd import atlas
 from kv_cache_runtime_amd.residency import REGEN, TIERED, Residency
@@ -25,6 +30,87 @@ def _args(dev, q, k_pool, v_pool, table, ctx, out, lse, qstart=None, max_q=1, ws
                         out=out, lse=lse, query_start=qstart, max_query_len=max_q,
                         total_q=q.shape[0], kv_dtype=kv, q_dtype=qdt)
     return a
+
+
+_NP = {torch.int8: np.int8, torch.uint8: np.uint8, torch.float32: np.float32,
+       torch.int32: np.int32}
+
+
+class _Shadow:
+    """Host copies of the f16 hot pool and the cold pools, written by the
+    oracle alone: new rows go where the runtime's table puts them, each
+    demotion is the oracle's encoding of its reading of the source block
+    (sources are all read before any destination is written, as the device
+    does within one call), and each reconstruction is the oracle's reading
+    of the entry rounded to f16."""
+
+    def __init__(self, n_hot, tiers, n_out=0):
+        self.k = np.zeros((n_hot, HKV, P, D), np.float16)
+        self.v = np.zeros_like(self.k)
+        self.t = {key: np.zeros(tuple(a.shape), _NP[a.dtype]) for key, a in tiers.items()}
+        self.n_out = n_out
+
+    def paged(self, q, table, ctx, counts, name=""):
+        tiers = {key: torch.from_numpy(a) for key, a in self.t.items()}
+        return synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
+                           page_tokens=P, q_dtype="bf16", kv_dtype="f16", context_lens=ctx,
+                           query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
+                           q=q, k_pool=torch.from_numpy(self.k), v_pool=torch.from_numpy(self.v),
+                           page_table=table, tiers=dict(tiers, counts=counts), name=name)
+
+    def write(self, table, ctx, n_new, k_new, v_new):
+        """Rows of the last n_new[i] tokens of sequence i, in row order."""
+        k, v = k_new.cpu().numpy(), v_new.cpu().numpy()
+        j = 0
+        for i, n in enumerate(n_new):
+            for t in range(n):
+                pos = int(ctx[i]) - n + t
+                b = int(np.uint32(table[i, pos // P]))
+                assert b < self.k.shape[0], (i, pos, b)  # a hot page
+                self.k[b, :, pos % P] = k[j]
+                self.v[b, :, pos % P] = v[j]
+                j += 1
+
+    def _reader(self):
+        w = self.paged(None, np.zeros((3, 1), np.int32), np.ones(3, np.int32), None)
+        return w, oracle.HostView(w)
+
+    def demote(self, src, dst):
+        w, host = self._reader()
+        new = []
+        for se, de in zip(np.asarray(src).view(np.uint32), np.asarray(dst).view(np.uint32)):
+            cls, slot = oracle.entry_class(int(de))
+            for kv in ("k", "v"):
+                for g in range(HKV):
+                    x = oracle.block_f32(w, int(se), g, kv, host=host)
+                    if cls == 5:
+                        enc = oracle.encode_1bit(x.ravel(), self.n_out)
+                    elif cls == 3:
+                        enc = oracle.quantize_block_fp8(x)
+                    else:
+                        codes, sc = oracle.quantize_block(x, {1: 127, 2: 7, 4: 1}[cls])
+                        codes = (codes.astype(np.int8) if cls == 1 else
+                                 oracle.pack_int4(codes) if cls == 2 else oracle.pack_int2(codes))
+                        enc = (codes, sc)
+                    new.append((cls, slot, kv, g, enc))
+        for cls, slot, kv, g, enc in new:
+            if cls == 5:
+                signs, sc, outs = enc
+                self.t[f"b1_{kv}"][slot, g] = signs
+                self.t[f"b1_{kv}_scale"][slot, g] = sc
+                self.t[f"b1_{kv}_out"][slot, g] = np.asarray(outs, np.uint32).view(np.int32)
+            else:
+                key = {1: "i8", 2: "i4", 3: "f8", 4: "i2"}[cls]
+                self.t[f"{key}_{kv}"][slot, g] = enc[0]
+                self.t[f"{key}_{kv}_scale"][slot, g] = enc[1]
+
+    def promote(self, src, dst):
+        w, host = self._reader()
+        new = [(int(b), kv, g, oracle.hot_bits(oracle.block_f32(w, int(e), g, kv, host=host), "f16"))
+               for e, b in zip(np.asarray(src).view(np.uint32), dst)
+               for kv in ("k", "v") for g in range(HKV)]
+        for b, kv, g, bits in new:
+            (self.k if kv == "k" else self.v)[b, g] = bits.reshape(P, D).view(np.float16)
 
 
 def _attend(a, dev, tiers=None, regen=None):
@@ -54,6 +140,7 @@ def test_tiered_decode_loop_through_the_runtime(gpu):
             tiers[f"{key}_{kv}"] = torch.zeros((n, HKV, P, shape_d), dtype=dt, device=gpu)
             tiers[f"{key}_{kv}_scale"] = torch.zeros((n, HKV), device=gpu)
     pools = atlas.make_tiers(tiers)
+    shadow = _Shadow(64, tiers)
     seqs = [0, 1, 2]
     prompt = [100, 37, 250]
     for s in seqs:
@@ -72,6 +159,7 @@ def test_tiered_decode_loop_through_the_runtime(gpu):
         a = _args(gpu, q, hot_k, hot_v, tt, ct, out, lse, qstart=qs, max_q=max_q)
         a.num_blocks = 64
         atlas.atlas_write_kv(a, k_new, v_new)
+        shadow.write(table, ctx, n_new, k_new, v_new)
 
     def run_jobs():
         src, dst, _, _ = rt.plan()
@@ -86,6 +174,7 @@ def test_tiered_decode_loop_through_the_runtime(gpu):
                                      torch.from_numpy(dst).to(gpu), rej)
             torch.cuda.synchronize()
             assert int(rej) == 0
+            shadow.demote(src, dst)
         return len(src)
 
     for s, n in zip(seqs, prompt):
@@ -109,11 +198,7 @@ def test_tiered_decode_loop_through_the_runtime(gpu):
             _attend(a, gpu, tiers=pools)
             counts = [64, tiers["i8_k"].shape[0], tiers["i4_k"].shape[0],
                       tiers["f8_k"].shape[0], tiers["i2_k"].shape[0]]
-            w = synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
-                            page_tokens=P, q_dtype="bf16", kv_dtype="f16", context_lens=ctx,
-                            query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
-                            q=q, k_pool=hot_k, v_pool=hot_v, page_table=table,
-                            tiers=dict(tiers, counts=counts), name=f"runtime-tiered-{step}")
+            w = shadow.paged(q, table, ctx, counts, name=f"runtime-tiered-{step}")
             check(w, out.cpu().numpy(), lse.cpu().numpy())
             checked += 1
         run_jobs()
@@ -147,6 +232,7 @@ def test_tiered_decode_loop_with_the_1bit_archive(gpu):
         tiers[f"b1_{kv}_scale"] = torch.zeros((96, HKV), device=gpu)
         tiers[f"b1_{kv}_out"] = torch.zeros((96, HKV, K_OUT), dtype=torch.int32, device=gpu)
     pools = atlas.make_tiers(tiers)
+    shadow = _Shadow(HOT + TRANS, tiers, n_out=K_OUT)
     seqs = [0, 1, 2]
     prompt = [120, 45, 260]
     for s in seqs:
@@ -168,6 +254,7 @@ def test_tiered_decode_loop_with_the_1bit_archive(gpu):
                                       torch.from_numpy(pdst).to(gpu), rej)
             torch.cuda.synchronize()
             assert int(rej) == 0
+            shadow.promote(psrc, pdst)
         return table, ctx, len(psrc)
 
     def write(n_new, qstart, max_q):
@@ -182,6 +269,7 @@ def test_tiered_decode_loop_with_the_1bit_archive(gpu):
                   torch.empty((rows, H), device=gpu), qstart=qs, max_q=max_q)
         a.num_blocks = HOT + TRANS
         atlas.atlas_write_kv(a, k_new, v_new)
+        shadow.write(table, ctx, n_new, k_new, v_new)
 
     def run_jobs():
         src, dst, _, _ = rt.plan()
@@ -191,6 +279,7 @@ def test_tiered_decode_loop_with_the_1bit_archive(gpu):
                                      torch.from_numpy(dst).to(gpu), rej)
             torch.cuda.synchronize()
             assert int(rej) == 0
+            shadow.demote(src, dst)
 
     for s, n in zip(seqs, prompt):
         rt.append(s, n)
@@ -214,11 +303,7 @@ def test_tiered_decode_loop_with_the_1bit_archive(gpu):
             print(f"[archive loop] step {step}: {n_promoted} pages rebuilt", flush=True)
             _attend(a, gpu, tiers=pools)
             counts = [HOT + TRANS, 16, 24, 8, 24]
-            w = synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
-                            page_tokens=P, q_dtype="bf16", kv_dtype="f16", context_lens=ctx,
-                            query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
-                            q=q, k_pool=hot_k, v_pool=hot_v, page_table=table,
-                            tiers=dict(tiers, counts=counts), name=f"runtime-archive-{step}")
+            w = shadow.paged(q, table, ctx, counts, name=f"runtime-archive-{step}")
             check(w, out.cpu().numpy(), lse.cpu().numpy())
             checked += 1
         run_jobs()
@@ -291,11 +376,15 @@ def test_regen_decode_loop_through_the_runtime(gpu):
                 spec = atlas.make_regen(seed, layer, rpt, int(rpt.max()))
                 _attend(a, gpu, regen=spec)
                 outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+            # the oracle reads no pool here: every page of the reference
+            # problem is regenerated (its pool is a host placeholder)
+            all_regen = (-(-ctx // P)).astype(np.int32)
+            zeros = torch.zeros((1, HKV, P, D), dtype=torch.bfloat16)
             w = synth.Paged(num_seqs=3, num_heads=H, num_kv_heads=HKV, head_dim=D,
                             page_tokens=P, q_dtype="bf16", kv_dtype="bf16", context_lens=ctx,
                             query_lens=np.ones(3, np.int32), scale=float(np.float32(D ** -0.5)),
-                            q=q, k_pool=hot_k, v_pool=hot_v, page_table=table,
-                            regen=dict(seed=seed, layer=layer, regen_pages=regen),
+                            q=q, k_pool=zeros, v_pool=zeros, page_table=np.zeros_like(table),
+                            regen=dict(seed=seed, layer=layer, regen_pages=all_regen),
                             name=f"runtime-regen-{step}")
             check(w, *outs[1])  # everything regenerated
             check(w, *outs[0])  # as the runtime planned
