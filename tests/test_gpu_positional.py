@@ -5,6 +5,8 @@ matrix-core and vector-ALU chunked prefill; plus the rotation of new keys in
 the write path.  Tolerances as for the plain paths (2e-5 f32, 2e-3 16-bit,
 dequantised or regenerated K/V)."""
 
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -115,6 +117,11 @@ def test_write_kv_stores_rotated_keys(gpu, kv):
     shape = (w.total_q, w.num_kv_heads, w.head_dim)
     k_new = torch.randn(shape, generator=gen, device=gpu).to(w.k_pool.dtype)
     v_new = torch.randn(shape, generator=gen, device=gpu).to(w.v_pool.dtype)
+    # the oracle's cache: the generated pool with the oracle's own rotation of
+    # each new K row (rounded to the pool's type) and the new V rows placed in
+    # it; the attention reference is computed over it, not over the pool the
+    # device wrote
+    ref_k, ref_v = w.k_pool.clone(), w.v_pool.clone()
     prob = atlas.Problem(w)
     atlas.atlas_write_kv(prob.args, k_new, v_new)
     torch.cuda.synchronize()
@@ -136,10 +143,16 @@ def test_write_kv_stores_rotated_keys(gpu, kv):
             assert np.all(err <= bound), (s, t, float(err.max()))
             worst = max(worst, float((err / (1 + np.abs(want))).max()))
             assert torch.equal(w.v_pool[blk, :, off], v_new[r])
+            bits = oracle.hot_bits(want, kv)
+            bits = bits.view(np.int32) if kv == "f32" else bits.view(np.int16)
+            ref_k[blk, :, off] = torch.from_numpy(bits).to(gpu).view(ref_k.dtype)
+            ref_v[blk, :, off] = v_new[r]
             r += 1
     print(f"[write-rope-{kv}] worst relative error {worst:.3e}")
     out, lse = run(w)
-    check(w, out, lse)
+    ref = copy.copy(w)
+    ref.k_pool, ref.v_pool = ref_k, ref_v
+    check(ref, out, lse)
 
 
 @pytest.mark.parametrize("prefill", [False, True])
