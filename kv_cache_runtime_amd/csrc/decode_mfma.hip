@@ -153,7 +153,7 @@ constexpr int kHot = 0, kByte = 1, kSub = 2;
 // the low half of its one chunk)
 template <int TIER>
 constexpr int chunks() { return TIER == kHot ? 4 : TIER == kByte ? 2 : 1; }
-// f16 offset that widen_k leaves in the K operands of a class (0: none)
+// f16 offset that the K and V widenings leave in a class's operands (0: none)
 template <int TIER, bool ALT>
 constexpr uint32_t k_offset() {
     return TIER == kHot ? 0u : TIER == kByte ? (ALT ? 0u : kBiasI8) : (ALT ? kBiasI2 : kBiasI4);
@@ -194,7 +194,7 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, int64_t base
 }
 
 // Raw K -> the four 16-bit operands (codes widened to f16, exact; int8,
-// int4 and INT2 codes keep their offset, see k_offset_scores).
+// int4 and INT2 codes keep their offset k_offset).
 template <int TIER>
 __device__ __forceinline__ void widen_k(const uint4 (&kr)[chunks<TIER>()], uint4 (&kb)[4],
                                        bool alt) {
@@ -278,7 +278,8 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint32_t a, uint32_t b, uint32
 // Writes the group's V rows, as 16-bit operands, into rows base .. base + 15
 // of the wave's LDS V tile; rows whose token is not visible (tok_ok false)
 // are written as zeros, so NaN garbage in page tails never meets a zero
-// probability.
+// probability.  Integer codes keep their f16 offset (k_offset), which the
+// P.V step takes out again.
 template <int TIER, typename TokOk>
 __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
                                               const uint4 (&vr)[chunks<TIER>()], int lane,
@@ -302,7 +303,7 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
                 for (int j = 0; j < 4; ++j) f8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) i8x4_to_f16x4(w[j], h[2 * j], h[2 * j + 1]);
+                for (int j = 0; j < 4; ++j) i8x4_to_f16x4<true>(w[j], h[2 * j], h[2 * j + 1]);
             }
             uint16_t *dst = vt + (base + tok) * kVPitch + 16 * (lane & 7);
             *reinterpret_cast<uint4 *>(dst) = keep_if(ok, h[0], h[1], h[2], h[3]);
@@ -316,7 +317,7 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 uint32_t o[8];
-                i2x16_to_f16x16(h ? vr[0].y : vr[0].x, o);
+                i2x16_to_f16x16<true>(h ? vr[0].y : vr[0].x, o);
                 *reinterpret_cast<uint4 *>(dst + 16 * h) = keep_if(ok, o[0], o[1], o[2], o[3]);
                 *reinterpret_cast<uint4 *>(dst + 16 * h + 8) = keep_if(ok, o[4], o[5], o[6], o[7]);
             }
@@ -325,7 +326,7 @@ __device__ __forceinline__ void store_v_group(uint16_t *vt, int base,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32_t o[4];
-                i4x8_to_f16x8(w[j], o);
+                i4x8_to_f16x8<true>(w[j], o);
                 *reinterpret_cast<uint4 *>(dst + 8 * j) = keep_if(ok, o[0], o[1], o[2], o[3]);
             }
         }
@@ -531,10 +532,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         const int n_tiles = n_pos > 0 ? (n_pos + kTileTok - 1) / kTileTok : 0;
         if (n_tiles == 0) return;
 
-        // Integer-code K operands carry the f16 offset b (code + b is exact),
-        // so each score starts from -b * sum(q) of its row instead of zero:
+        // Integer-code K and V operands carry the f16 offset b (code + b is
+        // exact).  Each score starts from -b * sum(q) of its row instead of zero:
         // one product of q with a constant-b operand, in the score layout
-        // (the remainder rows of a rotated q included).  This saves the
+        // (the remainder rows of a rotated q included).  The P.V step removes
+        // b * sum(P) with a second product per 32 tokens.  This saves the
         // subtraction of b from every widened code.
         f32x4_t s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         constexpr uint32_t kOff = k_offset<TIER, alt>();
@@ -547,6 +549,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
 #pragma unroll
             for (int i = 0; i < 4; ++i) s0[i] = -s0[i];
         }
+        // the P.V operand that removes the V offset: -b in every element
+        constexpr uint32_t kNeg = kOff | 0x8000u;
+        const uint4 vneg = make_uint4(kNeg | (kNeg << 16), kNeg | (kNeg << 16),
+                                      kNeg | (kNeg << 16), kNeg | (kNeg << 16));
 
         // the 16-position groups of a tile: first token, slot and liveness,
         // all wave-uniform (a group lies in one page)
@@ -953,6 +959,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
 #pragma unroll
                     for (int part = 0; part < NP; ++part)
                         acc[mb] = mfma16<QT>(av, bp[part], acc[mb]);
+                    // integer V codes carry the offset b: take b * sum(P) of
+                    // these 32 tokens out at once (a constant -b operand), so
+                    // the offset never accumulates across tiles
+                    if constexpr (kOff != 0u) acc[mb] = mfma16<QT>(vneg, bp[0], acc[mb]);
                 }
             }
             __builtin_amdgcn_wave_barrier();  // P and V tiles are rewritten by the next tile
