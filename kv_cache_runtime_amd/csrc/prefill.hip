@@ -373,7 +373,11 @@ __global__ __launch_bounds__(256, 3 - NH) void prefill_kernel(const PrefillParam
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, s[hh][kb][j]);
             if constexpr (ALIBI) mraw += rb[hh];
-            mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+            {  // the row's other half (lane r + 32) by a VALU swap, no LDS trip
+                const auto h = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(mraw), __float_as_uint(mraw), false, false);
+                mraw = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+            }
             mt[hh] = mraw * p.scale_log2;  // scale > 0 keeps the order
             move[hh] = mt[hh] > m_ref[hh] + kSlack;  // also true on the first finite tile
             any_move = any_move || move[hh];
