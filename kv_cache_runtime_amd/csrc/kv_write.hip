@@ -389,8 +389,24 @@ __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *
     uint32_t T = 0;  // count(key >= T) >= k throughout
     int need = 0;
     if (k > 0) {
+        // A bit that no key has set never moves T: no key lies in [T + 2^b,
+        // T + 2^(b+1)), so its count equals that of the higher candidate,
+        // which fell short of k.  Its pass is skipped (16-bit sources leave
+        // the low 13 to 16 bits of every key clear).
+        uint32_t any = 0x7FFFFFFFu;
+        if (rounds <= R) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o |= key[j][e];
+#pragma unroll
+            for (int sh = 32; sh >= 1; sh >>= 1) o |= (uint32_t)__shfl_xor((int)o, sh);
+            any = __builtin_amdgcn_readfirstlane(o);
+        }
         bool exact = false;
         for (int b = 30; b >= 0 && !exact; --b) {
+            if (((any >> b) & 1u) == 0u) continue;  // uniform
             const uint32_t cand = T | (1u << b);
             const int c = count_at_least(cand);
             if (c >= k) T = cand;
