@@ -133,7 +133,8 @@ typedef struct atlas_attn_args {
     int32_t max_context_len;    /* host: >= every context_lens[s] */
     int32_t max_query_len;      /* host: >= every chunk length (1 for decode) */
     int32_t total_q;            /* query rows (== num_seqs for decode) */
-    int32_t split_tokens;       /* keys per split-K work item (multiple of 64);
+    int32_t split_tokens;       /* keys per split-K work item of decode, or per
+                                   window of a regenerating prefill (multiple of 64);
                                    0 = the library chooses from the shape */
     float scale;                /* softmax scale, finite (e.g. 1/sqrt(head_dim)) */
     const void *q;              /* [total_q][num_heads][head_dim], q_dtype */
@@ -255,13 +256,18 @@ const char *atlas_last_error(void);
  * Workspace bytes needed by atlas_paged_attention (regen == NULL) or
  * atlas_paged_attention_regen (regen != NULL) for these arguments.  Reads host
  * fields only.  The workspace holds the split-K partials of decode (one f32
- * vector of head_dim plus one lse per (row, head, split)); for matrix-core
- * chunked prefill it holds an f16 copy of every page's V transposed to
- * [head_dim][page_tokens] (num_seqs * max_pages_per_seq pages) and, with
- * regenerated pages, one bf16 copy of every regenerated K page (each
- * regenerated value is computed once per call and shared by every query
- * tile).  Its contents need no initialisation and are not meaningful between
- * calls; two calls in flight at the same time must not share a workspace.
+ * vector of head_dim plus one lse per (row, head, split)).  Matrix-core
+ * chunked prefill needs none without regenerated pages; with them it takes
+ * the keys in windows of W tokens (W = split_tokens, or 16384 when
+ * split_tokens is 0, cut to the context rounded up to 64) and regenerates each
+ * window's regenerated keys into one ring that every window reuses (CFR-Atlas
+ * README, overview: scratch buffers that are reused), so the workspace is
+ *     2 * num_seqs * num_kv_heads * W * head_dim * 2 bytes
+ * (bf16 K and V; 64 MiB for 8 kv heads, head_dim 128 and W = 16384), at
+ * most that for any context length.  Each regenerated value is still
+ * computed once per call.  Its contents need no initialisation and are not
+ * meaningful between calls; two calls in flight at the same time must not
+ * share a workspace.
  */
 atlas_status atlas_workspace_size(const atlas_attn_args *args,
                                   const atlas_regen_spec *regen,
@@ -302,9 +308,12 @@ atlas_status atlas_paged_attention_tiered(const atlas_attn_args *args,
 /*
  * Attention with regenerated leading pages (see atlas_regen_spec).  Decode
  * rows regenerate each value inside the attention kernel, where it is used
- * once.  Chunked prefill first regenerates every value of the regenerated
- * pages once into the workspace and then runs the matrix-core kernel over
- * resident and regenerated pages alike.
+ * once.  Chunked prefill walks the keys window by window (see
+ * atlas_workspace_size): the window's regenerated keys are written once into
+ * the workspace ring, the matrix-core kernel folds the window over resident
+ * and regenerated pages alike and merges it into out / lse by log-sum-exp.
+ * The windows are fixed in tokens, so the result bits do not depend on which
+ * pages are regenerated or on the page size.
  */
 atlas_status atlas_paged_attention_regen(const atlas_attn_args *args,
                                          const atlas_regen_spec *regen);

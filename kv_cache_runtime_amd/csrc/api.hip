@@ -55,8 +55,9 @@ struct Plan {
     int q_blocks = 0;        // query tiles per sequence (matrix-core prefill)
     size_t part_o_bytes = 0;
     size_t part_lse_bytes = 0;
-    size_t regen_bytes = 0;  // K copy of the regenerated pages (matrix-core prefill)
-    size_t vt_bytes = 0;     // transposed f16 V of every page (matrix-core prefill)
+    int window_tokens = 0;   // matrix-core prefill with regeneration: keys per window
+    int windows = 1;
+    size_t ring_bytes = 0;   // K (and V) ring of one window's regenerated keys
     size_t total = 0;
 };
 
@@ -185,22 +186,28 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
         if (rg->max_regen_pages < 0 || rg->max_regen_pages > a->max_pages_per_seq)
             return fail(ATLAS_EINVAL, "max_regen_pages %d outside [0, max_pages_per_seq]",
                         rg->max_regen_pages);
-        if (plan->mfma) {
-            plan->regen_bytes = align_up((size_t)a->num_seqs * rg->max_regen_pages *
-                                         a->num_kv_heads * a->page_tokens * a->head_dim * 2);
-        }
     }
     if (plan->mfma) {
-        // transposed f16 copy of every page's V, written once per call
-        plan->vt_bytes = align_up((size_t)a->num_seqs * a->max_pages_per_seq * a->num_kv_heads *
-                                  a->page_tokens * a->head_dim * 2);
-        const int pos_per_block = 4 * 32 * kPrefillHalves / group;
+        const int pos_per_block = kPrefillRows / group;
         plan->q_blocks = (a->max_query_len + pos_per_block - 1) / pos_per_block;
         const int64_t blocks = (int64_t)a->num_kv_heads * plan->q_blocks * a->num_seqs;
         if (blocks > INT32_MAX)
             return fail(ATLAS_EUNSUPPORTED, "too many prefill workgroups (%lld)", (long long)blocks);
+        if (rg) {
+            // Regenerated keys are produced window by window into one ring
+            // that every window reuses, so the scratch does not grow with
+            // the context; the windows are fixed in tokens, so the result
+            // bits do not depend on how many pages are regenerated.
+            int w = a->split_tokens > 0 ? a->split_tokens : kPrefillWindow;
+            const int ctx64 = (a->max_context_len + 63) / 64 * 64;
+            if (ctx64 > 0 && w > ctx64) w = ctx64;  // one window holds the whole context
+            plan->window_tokens = w;
+            plan->windows = a->max_context_len > 0 ? (a->max_context_len + w - 1) / w : 1;
+            plan->ring_bytes = align_up((size_t)a->num_seqs * a->num_kv_heads * w *
+                                        a->head_dim * 2);
+        }
     }
-    plan->total = plan->part_o_bytes + plan->part_lse_bytes + plan->regen_bytes + plan->vt_bytes;
+    plan->total = plan->part_o_bytes + plan->part_lse_bytes + 2 * plan->ring_bytes;
     return ok();
 }
 
@@ -390,8 +397,9 @@ atlas_status run_decode(const atlas_attn_args *a, const Plan &plan, DecodeParams
     return ok();
 }
 
-// Chunked prefill on the matrix cores, after regenerating the regenerated
-// pages once into the workspace.
+// Chunked prefill on the matrix cores.  With regenerated pages the keys are
+// taken window by window: the window's regenerated keys go into the ring,
+// then the prefill kernel folds the window and merges it into out / lse.
 atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas_regen_spec *rg) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
     PrefillParams p;
@@ -414,57 +422,52 @@ atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas
     p.scale_log2 = a->scale * 1.4426950408889634f;
     p.out = a->out;
     p.lse = a->lse;
-    hipError_t e;
-    char *ws = reinterpret_cast<char *>(a->workspace);
-    p.vt = ws + plan.regen_bytes;
-    if (rg) {
-        p.regen_k = ws;
+    p.key_begin = 0;
+    p.key_end = INT32_MAX;
+    p.carry = 0;
+    hipError_t e = mark(a, 0, stream);
+    if (e != hipSuccess) return device_status(e, "profile event record");
+    if (!rg) {
+        e = launch_prefill(p, a->kv_dtype, plan.group, stream);
+        if (e != hipSuccess) return device_status(e, "prefill launch");
+    } else {
+        char *ws = reinterpret_cast<char *>(a->workspace);
+        p.ring_k = ws;
+        p.ring_v = ws + plan.ring_bytes;
+        p.ring_tokens = plan.window_tokens;
         p.regen_pages = rg->regen_pages;
         p.max_regen = rg->max_regen_pages;
-        if (rg->max_regen_pages > 0) {
-            RegenFillParams r;
-            std::memset(&r, 0, sizeof(r));
-            r.pos = p.pos;
-            r.seed = rg->seed;
-            r.layer = rg->layer;
-            r.num_kv_heads = a->num_kv_heads;
-            r.head_dim = a->head_dim;
-            r.page_tokens = a->page_tokens;
-            r.regen_pages = rg->regen_pages;
-            r.pages_per_seq = rg->max_regen_pages;
-            r.n = a->num_seqs * rg->max_regen_pages;
-            r.num_blocks = r.n;
-            r.kv_f32 = 0;
-            r.k_dst = ws;
-            r.vt_dst = const_cast<void *>(p.vt);
-            r.vt_pages_per_seq = a->max_pages_per_seq;
-            e = launch_regen_fill(r, stream);
-            if (e != hipSuccess) return device_status(e, "regenerate launch");
+        RegenWindowParams r;
+        std::memset(&r, 0, sizeof(r));
+        r.pos = p.pos;
+        r.seed = rg->seed;
+        r.layer = rg->layer;
+        r.num_seqs = a->num_seqs;
+        r.num_kv_heads = a->num_kv_heads;
+        r.page_tokens = a->page_tokens;
+        r.regen_pages = rg->regen_pages;
+        r.max_regen = rg->max_regen_pages;
+        r.context_lens = a->context_lens;
+        r.max_context_len = a->max_context_len;
+        r.max_keys = a->max_pages_per_seq * a->page_tokens;
+        r.window_tokens = plan.window_tokens;
+        r.ring_k = ws;
+        r.ring_v = ws + plan.ring_bytes;
+        const int64_t regen_keys = (int64_t)rg->max_regen_pages * a->page_tokens;
+        for (int w = 0; w < plan.windows; ++w) {
+            const int64_t k0 = (int64_t)w * plan.window_tokens;
+            if (k0 < regen_keys) {  // some sequence may regenerate keys of this window
+                r.key_begin = (int32_t)k0;
+                e = launch_regen_window(r, stream);
+                if (e != hipSuccess) return device_status(e, "regenerate launch");
+            }
+            p.key_begin = (int32_t)k0;
+            p.key_end = (int32_t)std::min<int64_t>(k0 + plan.window_tokens, INT32_MAX);
+            p.carry = w > 0 ? 1 : 0;
+            e = launch_prefill(p, a->kv_dtype, plan.group, stream);
+            if (e != hipSuccess) return device_status(e, "prefill launch");
         }
     }
-    {
-        VtCopyParams v;
-        std::memset(&v, 0, sizeof(v));
-        v.v_pool = a->v_pool;
-        v.v_bf16 = a->kv_dtype == ATLAS_BF16;
-        v.page_table = a->page_table;
-        v.context_lens = a->context_lens;
-        v.regen_pages = rg ? rg->regen_pages : nullptr;
-        v.num_seqs = a->num_seqs;
-        v.num_kv_heads = a->num_kv_heads;
-        v.page_tokens = a->page_tokens;
-        v.max_pages = a->max_pages_per_seq;
-        v.num_blocks = a->num_blocks;
-        v.max_context_len = a->max_context_len;
-        v.max_regen = rg ? rg->max_regen_pages : 0;
-        v.vt = const_cast<void *>(p.vt);
-        e = launch_vt_copy(v, stream);
-        if (e != hipSuccess) return device_status(e, "V transpose launch");
-    }
-    e = mark(a, 0, stream);
-    if (e != hipSuccess) return device_status(e, "profile event record");
-    e = launch_prefill(p, a->kv_dtype, plan.group, stream);
-    if (e != hipSuccess) return device_status(e, "prefill launch");
     e = mark(a, 1, stream);
     if (e != hipSuccess) return device_status(e, "profile event record");
     return ok();

@@ -1,7 +1,7 @@
 // Page-walk, regeneration and decode kernels without attention arithmetic:
 // the page gather (inspection), the page regenerator that writes bf16 values
-// into pools or into the workspace copy used by chunked prefill, and the
-// tier decoder (inspection).
+// into pools or into the ring of regenerated keys a chunked prefill reads
+// window by window, and the tier decoder (inspection).
 #include "device.h"
 
 namespace atlas {
@@ -40,27 +40,14 @@ __global__ __launch_bounds__(128) void gather_kernel(const char *k_pool, const c
 }
 
 // One workgroup per (page entry, kv head); each thread writes pairs of
-// consecutive elements (one 32-bit bf16x2 / f16x2 or two f32 stores).  With
-// vt_dst set, V is written transposed ([D][P]) as f16 -- every regenerated
-// value is a multiple of 2^-23 in [-1, 1] with at most 8 significant bits, so
-// f16 holds it exactly.
+// consecutive elements (one 32-bit bf16x2 / f16x2 or two f32 stores).
 __global__ __launch_bounds__(256) void regen_fill_kernel(const RegenFillParams r) {
     const int i = blockIdx.x / r.num_kv_heads;
     const int g = blockIdx.x % r.num_kv_heads;
     if (i >= r.n) return;
-    int lp, blk, seq = 0;
-    if (r.regen_pages != nullptr) {
-        // workspace copy: block i holds logical page i % pages_per_seq of
-        // sequence i / pages_per_seq, if that page is regenerated
-        seq = i / r.pages_per_seq;
-        lp = i % r.pages_per_seq;
-        if (lp >= r.regen_pages[seq]) return;
-        blk = i;
-    } else {
-        lp = r.logical_pages[i];
-        blk = r.dst_blocks[i];
-        if (lp < 0 || blk < 0 || blk >= r.num_blocks) return;
-    }
+    const int lp = r.logical_pages[i];
+    const int blk = r.dst_blocks[i];
+    if (lp < 0 || blk < 0 || blk >= r.num_blocks) return;
     const int P = r.page_tokens, D = r.head_dim;
     const int64_t base = (((int64_t)blk * r.num_kv_heads + g) * P) * D;
     const int pairs = P * D / 2;
@@ -76,97 +63,64 @@ __global__ __launch_bounds__(256) void regen_fill_kernel(const RegenFillParams r
             k0 = __float_as_uint(bf16_round(kk.x)) >> 16;
             k1 = __float_as_uint(bf16_round(kk.y)) >> 16;
         }
+        const uint32_t v0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1));
+        const uint32_t v1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 1));
         if (r.kv_f32) {
             reinterpret_cast<float2 *>(reinterpret_cast<float *>(r.k_dst) + base)[t] = kk;
+            reinterpret_cast<float2 *>(reinterpret_cast<float *>(r.v_dst) + base)[t] =
+                make_float2(__uint_as_float(v0 << 16), __uint_as_float(v1 << 16));
         } else {
             reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.k_dst) + base)[t] =
                 k0 | (k1 << 16);
-        }
-        if (r.vt_dst == nullptr) {
-            const uint32_t v0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1));
-            const uint32_t v1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 1));
-            if (r.kv_f32) {
-                float2 vv = make_float2(__uint_as_float(v0 << 16), __uint_as_float(v1 << 16));
-                reinterpret_cast<float2 *>(reinterpret_cast<float *>(r.v_dst) + base)[t] = vv;
-            } else {
-                reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.v_dst) + base)[t] =
-                    v0 | (v1 << 16);
-            }
-        }
-    }
-    if (r.vt_dst != nullptr) {
-        // V^T: element pair (dim, rows row, row + 1)
-        const int64_t vbase =
-            (((int64_t)seq * r.vt_pages_per_seq + lp) * r.num_kv_heads + g) * (int64_t)D * P;
-        for (int t = threadIdx.x; t < pairs; t += blockDim.x) {
-            const int e = 2 * t;
-            const int dim = e / P, row = e % P;
-            const int tok = lp * P + row;
-            const float v0 = __uint_as_float(
-                regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1)) << 16);
-            const float v1 = __uint_as_float(
-                regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok + 1, dim, 1)) << 16);
-            typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-            const f16x2_t h = {(_Float16)v0, (_Float16)v1};
-            reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.vt_dst) + vbase)[t] =
-                __builtin_bit_cast(uint32_t, h);
+            reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.v_dst) + base)[t] =
+                v0 | (v1 << 16);
         }
     }
 }
 
-// Transposed f16 copy of resident V pages: one workgroup per (sequence,
-// logical page, kv head), 64 rows at a time through LDS.  Rows past the
-// context end are written as zeros (a page's tail may hold anything), and a
-// block id outside the pool writes NaN so the rows that read it fail loudly.
-__global__ __launch_bounds__(256) void vt_copy_kernel(const VtCopyParams v) {
+// The regenerated keys of one window of a chunked prefill, into the ring the
+// prefill kernel reads (the CFR-Atlas README's scratch buffers that are
+// reused: every window overwrites the same ring).  One workgroup per (seq,
+// kv head, 64 keys of the window); thread t writes dim pairs of keys
+// t / 64 + 4 i, so each key row is written by 64 consecutive lanes.  Keys past
+// the sequence's regenerated pages or its context are left alone; the
+// prefill kernel reads those from the pool or not at all.
+__global__ __launch_bounds__(256) void regen_window_kernel(const RegenWindowParams r) {
     constexpr int D = 128;
-    constexpr int kRows = 64;
-    __shared__ uint16_t tile[kRows][D + 2];
-    const int g = blockIdx.x % v.num_kv_heads;
-    const int rest = blockIdx.x / v.num_kv_heads;
-    const int lp = rest % v.max_pages;
-    const int seq = rest / v.max_pages;
-    const int P = v.page_tokens;
-    const int ctx = v.context_lens[seq];
-    if (ctx < 0 || ctx > v.max_context_len || ctx > v.max_pages * P) return;
-    if (lp * P >= ctx) return;
-    if (v.regen_pages != nullptr) {
-        const int nr = v.regen_pages[seq];
-        if (nr >= 0 && nr <= v.max_regen && lp < nr) return;  // regenerated page
-    }
-    const int blk = v.page_table[(int64_t)seq * v.max_pages + lp];
-    const bool ok = blk >= 0 && blk < v.num_blocks;
-    const uint16_t *src = reinterpret_cast<const uint16_t *>(v.v_pool) +
-                          (((int64_t)(ok ? blk : 0) * v.num_kv_heads + g) * P) * D;
-    uint16_t *dst = reinterpret_cast<uint16_t *>(v.vt) +
-                    (((int64_t)seq * v.max_pages + lp) * v.num_kv_heads + g) * (int64_t)D * P;
-    const int valid = min(P, ctx - lp * P);
-    const uint16_t qnan = 0x7E00u;
-    for (int r0 = 0; r0 < P; r0 += kRows) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < kRows * D / 2; e += blockDim.x) {
-            const int row = (2 * e) / D, dim = (2 * e) % D;
-            uint32_t w = 0;
-            if (r0 + row < valid) {
-                w = *reinterpret_cast<const uint32_t *>(src + (int64_t)(r0 + row) * D + dim);
-                if (v.v_bf16) {
-                    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-                    const f16x2_t h = {(_Float16)__uint_as_float(w << 16),
-                                       (_Float16)__uint_as_float(w & 0xFFFF0000u)};
-                    w = __builtin_bit_cast(uint32_t, h);
-                }
-                if (!ok) w = qnan | ((uint32_t)qnan << 16);
-            }
-            tile[row][dim] = (uint16_t)w;
-            tile[row][dim + 1] = (uint16_t)(w >> 16);
+    const int groups = r.window_tokens / 64;
+    const int gi = blockIdx.x % groups;
+    const int rest = blockIdx.x / groups;
+    const int g = rest % r.num_kv_heads;
+    const int seq = rest / r.num_kv_heads;
+    const int n_regen = r.regen_pages[seq];
+    const int ctx = r.context_lens[seq];
+    // sequences the prefill kernel rejects (NaN rows) need no values
+    if (n_regen < 0 || n_regen > r.max_regen) return;
+    if (ctx < 0 || ctx > r.max_context_len || ctx > r.max_keys) return;
+    const int lim = min((int)min((int64_t)n_regen * r.page_tokens, (int64_t)INT32_MAX), ctx);
+    const int k_lo = r.key_begin + 64 * gi;
+    if (k_lo >= lim) return;
+    const int64_t ring0 = (((int64_t)seq * r.num_kv_heads + g) * r.window_tokens + 64 * gi) * D;
+    const int dp = threadIdx.x & 63;  // dim pair
+    const int dim = 2 * dp;
+    const double turns = r.pos.rope ? rope_turns(dp, D, r.pos.rope_log2_theta) : 0.0;
+#pragma unroll 4
+    for (int kr = threadIdx.x >> 6; kr < 64; kr += 4) {
+        const int tok = k_lo + kr;
+        if (tok >= lim) break;  // uniform in the wave
+        uint32_t k0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 0));
+        uint32_t k1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 0));
+        if (r.pos.rope) {
+            float x0 = __uint_as_float(k0 << 16), x1 = __uint_as_float(k1 << 16);
+            rope_rotate(x0, x1, tok, turns);
+            k0 = __float_as_uint(bf16_round(x0)) >> 16;
+            k1 = __float_as_uint(bf16_round(x1)) >> 16;
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < kRows * D / 2; e += blockDim.x) {
-            const int dim = (2 * e) / kRows, row = (2 * e) % kRows;
-            if (r0 + row >= P) continue;  // pages shorter than the staging tile
-            const uint32_t w = (uint32_t)tile[row][dim] | ((uint32_t)tile[row + 1][dim] << 16);
-            *reinterpret_cast<uint32_t *>(dst + (int64_t)dim * P + r0 + row) = w;
-        }
+        const uint32_t v0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1));
+        const uint32_t v1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 1));
+        const int64_t at = ring0 + (int64_t)kr * D + dim;
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.ring_k) + at) = k0 | (k1 << 16);
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.ring_v) + at) = v0 | (v1 << 16);
     }
 }
 
@@ -399,10 +353,10 @@ hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_vt_copy(const VtCopyParams &v, hipStream_t stream) {
-    const int64_t blocks = (int64_t)v.num_seqs * v.max_pages * v.num_kv_heads;
+hipError_t launch_regen_window(const RegenWindowParams &r, hipStream_t stream) {
+    const int64_t blocks = (int64_t)r.num_seqs * r.num_kv_heads * (r.window_tokens / 64);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(vt_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, v);
+    hipLaunchKernelGGL(regen_window_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, r);
     return hipGetLastError();
 }
 

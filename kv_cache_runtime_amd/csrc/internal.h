@@ -91,13 +91,19 @@ struct PrefillParams {
     const void *k_pool;
     const void *v_pool;
     const int32_t *page_table;
-    const void *regen_k;      // [num_seqs][max_regen][Hkv][P][D] regenerated K pages, or null
-    const void *vt;           // [num_seqs][max_pages][Hkv][D][P] f16: V of every page, transposed
+    // regenerated pages of the current key window: ring_k / ring_v
+    // [num_seqs][Hkv][ring_tokens][D] bf16, row = key - key_begin (or null)
+    const void *ring_k;
+    const void *ring_v;
+    int32_t ring_tokens;
     const int32_t *regen_pages;
     int32_t max_regen;
     int32_t num_heads, num_kv_heads, page_tokens, max_pages, num_blocks, total_q;
     int32_t max_query_len;
     int32_t q_blocks;         // query tiles per sequence (grid)
+    int32_t key_begin;        // keys of this launch: [key_begin, key_end), key_begin a
+    int32_t key_end;          // multiple of 64, window length <= ring_tokens with a ring
+    int32_t carry;            // 1: merge into the out / lse an earlier window wrote
     uint32_t p_magic, p_shift;  // key / page_tokens == (umulhi(key, p_magic) + key) >> p_shift
     float scale_log2;
     float *out;
@@ -109,30 +115,30 @@ struct RegenFillParams {
     uint64_t seed;
     uint32_t layer;
     int32_t num_kv_heads, head_dim, page_tokens;
-    const int32_t *logical_pages;  // [n] or null (then page index = i % pages_per_seq)
-    const int32_t *dst_blocks;     // [n] or null (then block = i)
-    const int32_t *regen_pages;    // per-sequence limit for scratch fills, or null
-    int32_t pages_per_seq;         // scratch fill: max_regen
+    const int32_t *logical_pages;  // [n]
+    const int32_t *dst_blocks;     // [n]
     int32_t n;
     int32_t num_blocks;
     int32_t kv_f32;                // 1: write f32 values, 0: bf16
     void *k_dst;
     void *v_dst;
-    void *vt_dst;                  // if set: V goes here transposed, as f16
-                                   // [seq][vt_pages_per_seq][Hkv][D][P], not to v_dst
-    int32_t vt_pages_per_seq;
 };
 
-// Transposed f16 copy of the resident V pages of a chunked prefill.
-struct VtCopyParams {
-    const void *v_pool;            // [num_blocks][Hkv][P][D] bf16 or f16
-    int32_t v_bf16;
-    const int32_t *page_table;
-    const int32_t *context_lens;
-    const int32_t *regen_pages;    // pages below this count are skipped (regenerated), or null
-    int32_t num_seqs, num_kv_heads, page_tokens, max_pages, num_blocks, max_context_len;
+// Regenerated K/V of one key window of a chunked prefill, written into the
+// ring the prefill kernel reads: ring[seq][Hkv][window_tokens][128] bf16.
+struct RegenWindowParams {
+    PosParams pos;                 // rope: K written rotated by its token position
+    uint64_t seed;
+    uint32_t layer;
+    int32_t num_seqs, num_kv_heads, page_tokens;
+    const int32_t *regen_pages;    // [num_seqs]
     int32_t max_regen;
-    void *vt;                      // [num_seqs][max_pages][Hkv][D][P] f16
+    const int32_t *context_lens;   // [num_seqs]
+    int32_t max_context_len, max_keys;
+    int32_t key_begin;             // first key of the window (multiple of 64)
+    int32_t window_tokens;         // ring rows per (seq, kv head), multiple of 64
+    void *ring_k;
+    void *ring_v;
 };
 
 // Debug check of the tables and pools behind a call.
@@ -223,14 +229,14 @@ bool decode_mfma_supported(int kv_type, int head_dim, int group, int mode, int p
                            int split_tokens);
 hipError_t launch_decode_mfma(const DecodeParams &p, int kv_type, int group, int mode,
                               hipStream_t stream);
-// 32-row halves per wave of the matrix-core prefill kernel (1 or 2).
-#ifndef ATLAS_PREFILL_HALVES
-#define ATLAS_PREFILL_HALVES 1
-#endif
-constexpr int kPrefillHalves = ATLAS_PREFILL_HALVES;
+// Query rows per workgroup of the matrix-core prefill kernel.
+constexpr int kPrefillRows = 256;
+// Keys per window of a chunked prefill with regenerated pages (the default
+// when the caller leaves split_tokens at 0).
+constexpr int kPrefillWindow = 16384;
 hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream);
 hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream);
-hipError_t launch_vt_copy(const VtCopyParams &v, hipStream_t stream);
+hipError_t launch_regen_window(const RegenWindowParams &r, hipStream_t stream);
 hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
                          int32_t num_kv_heads, int32_t head_dim, int32_t page_tokens,
                          int32_t num_blocks, int32_t elem_bytes, int32_t num_tokens,
