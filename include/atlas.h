@@ -153,7 +153,10 @@ typedef struct atlas_attn_args {
                                    `stream` just before and just after the main
                                    attention kernel, so a caller can time that
                                    kernel alone (the split merge and a
-                                   regeneration pre-pass fall outside the pair) */
+                                   regeneration pre-pass fall outside the pair;
+                                   a windowed matrix-core prefill has the pair
+                                   around all its windows, each a preparation
+                                   and a fold kernel) */
     const float *alibi_slopes;  /* [num_heads] f32 ALiBi slopes, finite, or NULL */
     float rope_theta;           /* rotary base (e.g. 10000), finite and > 1, or 0 */
     int32_t reserved;           /* 0 */
@@ -257,17 +260,18 @@ const char *atlas_last_error(void);
  * atlas_paged_attention_regen (regen != NULL) for these arguments.  Reads host
  * fields only.  The workspace holds the split-K partials of decode (one f32
  * vector of head_dim plus one lse per (row, head, split)).  Matrix-core
- * chunked prefill needs none without regenerated pages; with them it takes
- * the keys in windows of W tokens (W = split_tokens, or 16384 when
- * split_tokens is 0, cut to the context rounded up to 64) and regenerates each
- * window's regenerated keys into one ring that every window reuses (CFR-Atlas
- * README, overview: scratch buffers that are reused), so the workspace is
+ * chunked prefill takes the keys in windows of W tokens (W = split_tokens,
+ * or 16384 when split_tokens is 0, cut to the longest context rounded up to
+ * 64) and gathers each window -- regenerated keys from the regenerator,
+ * resident keys through the page table -- into one ring that every window
+ * reuses (CFR-Atlas README, overview: scratch buffers that are reused), so
+ * its workspace is
  *     2 * num_seqs * num_kv_heads * W * head_dim * 2 bytes
- * (bf16 K and V; 64 MiB for 8 kv heads, head_dim 128 and W = 16384), at
- * most that for any context length.  Each regenerated value is still
- * computed once per call.  Its contents need no initialisation and are not
- * meaningful between calls; two calls in flight at the same time must not
- * share a workspace.
+ * (K in the kv dtype and V in f16; 64 MiB for one sequence, 8 kv heads,
+ * head_dim 128 and W = 16384), at most that for any context length.  Each
+ * regenerated value is still computed once per call.  Its contents need no
+ * initialisation and are not meaningful between calls; two calls in flight
+ * at the same time must not share a workspace.
  */
 atlas_status atlas_workspace_size(const atlas_attn_args *args,
                                   const atlas_regen_spec *regen,

@@ -193,19 +193,16 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
         const int64_t blocks = (int64_t)a->num_kv_heads * plan->q_blocks * a->num_seqs;
         if (blocks > INT32_MAX)
             return fail(ATLAS_EUNSUPPORTED, "too many prefill workgroups (%lld)", (long long)blocks);
-        if (rg) {
-            // Regenerated keys are produced window by window into one ring
-            // that every window reuses, so the scratch does not grow with
-            // the context; the windows are fixed in tokens, so the result
-            // bits do not depend on how many pages are regenerated.
-            int w = a->split_tokens > 0 ? a->split_tokens : kPrefillWindow;
-            const int ctx64 = (a->max_context_len + 63) / 64 * 64;
-            if (ctx64 > 0 && w > ctx64) w = ctx64;  // one window holds the whole context
-            plan->window_tokens = w;
-            plan->windows = a->max_context_len > 0 ? (a->max_context_len + w - 1) / w : 1;
-            plan->ring_bytes = align_up((size_t)a->num_seqs * a->num_kv_heads * w *
-                                        a->head_dim * 2);
-        }
+        // The keys are taken in windows fixed in tokens, each gathered (or
+        // regenerated) into one ring that every window reuses, so the scratch
+        // does not grow with the context and the result bits do not depend
+        // on the page size or on which pages are regenerated.
+        int w = a->split_tokens > 0 ? a->split_tokens : kPrefillWindow;
+        const int ctx64 = (a->max_context_len + 63) / 64 * 64;
+        if (ctx64 > 0 && w > ctx64) w = ctx64;  // one window holds the whole context
+        plan->window_tokens = w;
+        plan->windows = a->max_context_len > 0 ? (a->max_context_len + w - 1) / w : 1;
+        plan->ring_bytes = align_up((size_t)a->num_seqs * a->num_kv_heads * w * a->head_dim * 2);
     }
     plan->total = plan->part_o_bytes + plan->part_lse_bytes + 2 * plan->ring_bytes;
     return ok();
@@ -397,76 +394,64 @@ atlas_status run_decode(const atlas_attn_args *a, const Plan &plan, DecodeParams
     return ok();
 }
 
-// Chunked prefill on the matrix cores.  With regenerated pages the keys are
-// taken window by window: the window's regenerated keys go into the ring,
-// then the prefill kernel folds the window and merges it into out / lse.
+// Chunked prefill on the matrix cores, window by window: the window's keys
+// are gathered (or regenerated) into the ring, then the prefill kernel folds
+// the window and merges it into out / lse.
 atlas_status run_prefill(const atlas_attn_args *a, const Plan &plan, const atlas_regen_spec *rg) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
+    char *ws = reinterpret_cast<char *>(a->workspace);
     PrefillParams p;
     std::memset(&p, 0, sizeof(p));
     p.rows = row_map(a);
     p.pos = pos_params(a->rope_theta, a->alibi_slopes);
     p.q = a->q;
-    p.k_pool = a->k_pool;
-    p.v_pool = a->v_pool;
-    p.page_table = a->page_table;
+    p.ring_k = ws;
+    p.ring_v = ws + plan.ring_bytes;
+    p.ring_tokens = plan.window_tokens;
+    p.regen_pages = rg ? rg->regen_pages : nullptr;
+    p.max_regen = rg ? rg->max_regen_pages : 0;
     p.num_heads = a->num_heads;
     p.num_kv_heads = a->num_kv_heads;
-    p.page_tokens = a->page_tokens;
-    p.max_pages = a->max_pages_per_seq;
-    p.num_blocks = a->num_blocks;
     p.total_q = a->total_q;
     p.max_query_len = a->max_query_len;
     p.q_blocks = plan.q_blocks;
-    page_divider(a->page_tokens, p.p_magic, p.p_shift);
     p.scale_log2 = a->scale * 1.4426950408889634f;
     p.out = a->out;
     p.lse = a->lse;
-    p.key_begin = 0;
-    p.key_end = INT32_MAX;
-    p.carry = 0;
+    WindowParams r;
+    std::memset(&r, 0, sizeof(r));
+    r.pos = p.pos;
+    r.seed = rg ? rg->seed : 0;
+    r.layer = rg ? rg->layer : 0;
+    r.num_seqs = a->num_seqs;
+    r.num_kv_heads = a->num_kv_heads;
+    r.page_tokens = a->page_tokens;
+    r.max_pages = a->max_pages_per_seq;
+    r.num_blocks = a->num_blocks;
+    r.k_pool = a->k_pool;
+    r.v_pool = a->v_pool;
+    r.page_table = a->page_table;
+    r.kv_f16 = a->kv_dtype == ATLAS_F16 ? 1 : 0;
+    r.regen_pages = p.regen_pages;
+    r.max_regen = p.max_regen;
+    r.context_lens = a->context_lens;
+    r.max_context_len = a->max_context_len;
+    r.max_keys = a->max_pages_per_seq * a->page_tokens;
+    r.window_tokens = plan.window_tokens;
+    r.ring_k = ws;
+    r.ring_v = ws + plan.ring_bytes;
     hipError_t e = mark(a, 0, stream);
     if (e != hipSuccess) return device_status(e, "profile event record");
-    if (!rg) {
+    for (int w = 0; w < plan.windows; ++w) {
+        const int64_t k0 = (int64_t)w * plan.window_tokens;
+        r.key_begin = (int32_t)k0;
+        e = launch_window_prepare(r, stream);
+        if (e != hipSuccess) return device_status(e, "window preparation launch");
+        p.key_begin = (int32_t)k0;
+        p.key_end = (int32_t)std::min<int64_t>(k0 + plan.window_tokens, INT32_MAX);
+        p.carry = w > 0 ? 1 : 0;
         e = launch_prefill(p, a->kv_dtype, plan.group, stream);
         if (e != hipSuccess) return device_status(e, "prefill launch");
-    } else {
-        char *ws = reinterpret_cast<char *>(a->workspace);
-        p.ring_k = ws;
-        p.ring_v = ws + plan.ring_bytes;
-        p.ring_tokens = plan.window_tokens;
-        p.regen_pages = rg->regen_pages;
-        p.max_regen = rg->max_regen_pages;
-        RegenWindowParams r;
-        std::memset(&r, 0, sizeof(r));
-        r.pos = p.pos;
-        r.seed = rg->seed;
-        r.layer = rg->layer;
-        r.num_seqs = a->num_seqs;
-        r.num_kv_heads = a->num_kv_heads;
-        r.page_tokens = a->page_tokens;
-        r.regen_pages = rg->regen_pages;
-        r.max_regen = rg->max_regen_pages;
-        r.context_lens = a->context_lens;
-        r.max_context_len = a->max_context_len;
-        r.max_keys = a->max_pages_per_seq * a->page_tokens;
-        r.window_tokens = plan.window_tokens;
-        r.ring_k = ws;
-        r.ring_v = ws + plan.ring_bytes;
-        const int64_t regen_keys = (int64_t)rg->max_regen_pages * a->page_tokens;
-        for (int w = 0; w < plan.windows; ++w) {
-            const int64_t k0 = (int64_t)w * plan.window_tokens;
-            if (k0 < regen_keys) {  // some sequence may regenerate keys of this window
-                r.key_begin = (int32_t)k0;
-                e = launch_regen_window(r, stream);
-                if (e != hipSuccess) return device_status(e, "regenerate launch");
-            }
-            p.key_begin = (int32_t)k0;
-            p.key_end = (int32_t)std::min<int64_t>(k0 + plan.window_tokens, INT32_MAX);
-            p.carry = w > 0 ? 1 : 0;
-            e = launch_prefill(p, a->kv_dtype, plan.group, stream);
-            if (e != hipSuccess) return device_status(e, "prefill launch");
-        }
     }
     e = mark(a, 1, stream);
     if (e != hipSuccess) return device_status(e, "profile event record");

@@ -1,7 +1,6 @@
 // Page-walk, regeneration and decode kernels without attention arithmetic:
 // the page gather (inspection), the page regenerator that writes bf16 values
-// into pools or into the ring of regenerated keys a chunked prefill reads
-// window by window, and the tier decoder (inspection).
+// into pools, and the tier decoder (inspection).
 #include "device.h"
 
 namespace atlas {
@@ -75,52 +74,6 @@ __global__ __launch_bounds__(256) void regen_fill_kernel(const RegenFillParams r
             reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.v_dst) + base)[t] =
                 v0 | (v1 << 16);
         }
-    }
-}
-
-// The regenerated keys of one window of a chunked prefill, into the ring the
-// prefill kernel reads (the CFR-Atlas README's scratch buffers that are
-// reused: every window overwrites the same ring).  One workgroup per (seq,
-// kv head, 64 keys of the window); thread t writes dim pairs of keys
-// t / 64 + 4 i, so each key row is written by 64 consecutive lanes.  Keys past
-// the sequence's regenerated pages or its context are left alone; the
-// prefill kernel reads those from the pool or not at all.
-__global__ __launch_bounds__(256) void regen_window_kernel(const RegenWindowParams r) {
-    constexpr int D = 128;
-    const int groups = r.window_tokens / 64;
-    const int gi = blockIdx.x % groups;
-    const int rest = blockIdx.x / groups;
-    const int g = rest % r.num_kv_heads;
-    const int seq = rest / r.num_kv_heads;
-    const int n_regen = r.regen_pages[seq];
-    const int ctx = r.context_lens[seq];
-    // sequences the prefill kernel rejects (NaN rows) need no values
-    if (n_regen < 0 || n_regen > r.max_regen) return;
-    if (ctx < 0 || ctx > r.max_context_len || ctx > r.max_keys) return;
-    const int lim = min((int)min((int64_t)n_regen * r.page_tokens, (int64_t)INT32_MAX), ctx);
-    const int k_lo = r.key_begin + 64 * gi;
-    if (k_lo >= lim) return;
-    const int64_t ring0 = (((int64_t)seq * r.num_kv_heads + g) * r.window_tokens + 64 * gi) * D;
-    const int dp = threadIdx.x & 63;  // dim pair
-    const int dim = 2 * dp;
-    const double turns = r.pos.rope ? rope_turns(dp, D, r.pos.rope_log2_theta) : 0.0;
-#pragma unroll 4
-    for (int kr = threadIdx.x >> 6; kr < 64; kr += 4) {
-        const int tok = k_lo + kr;
-        if (tok >= lim) break;  // uniform in the wave
-        uint32_t k0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 0));
-        uint32_t k1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 0));
-        if (r.pos.rope) {
-            float x0 = __uint_as_float(k0 << 16), x1 = __uint_as_float(k1 << 16);
-            rope_rotate(x0, x1, tok, turns);
-            k0 = __float_as_uint(bf16_round(x0)) >> 16;
-            k1 = __float_as_uint(bf16_round(x1)) >> 16;
-        }
-        const uint32_t v0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim, 1));
-        const uint32_t v1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, tok, dim + 1, 1));
-        const int64_t at = ring0 + (int64_t)kr * D + dim;
-        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.ring_k) + at) = k0 | (k1 << 16);
-        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(r.ring_v) + at) = v0 | (v1 << 16);
     }
 }
 
@@ -353,12 +306,6 @@ hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_regen_window(const RegenWindowParams &r, hipStream_t stream) {
-    const int64_t blocks = (int64_t)r.num_seqs * r.num_kv_heads * (r.window_tokens / 64);
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(regen_window_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, r);
-    return hipGetLastError();
-}
 
 hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,
                           const int32_t *entries, int32_t n, float *k_out, float *v_out,

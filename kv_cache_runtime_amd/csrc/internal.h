@@ -91,20 +91,19 @@ struct PrefillParams {
     const void *k_pool;
     const void *v_pool;
     const int32_t *page_table;
-    // regenerated pages of the current key window: ring_k / ring_v
-    // [num_seqs][Hkv][ring_tokens][D] bf16, row = key - key_begin (or null)
+    // the keys of the current window, gathered: ring_k (kv type) / ring_v
+    // (f16) [num_seqs][Hkv][ring_tokens][D], row = key - key_begin
     const void *ring_k;
     const void *ring_v;
     int32_t ring_tokens;
-    const int32_t *regen_pages;
+    const int32_t *regen_pages;   // validated only (the window preparation reads them)
     int32_t max_regen;
-    int32_t num_heads, num_kv_heads, page_tokens, max_pages, num_blocks, total_q;
+    int32_t num_heads, num_kv_heads, total_q;
     int32_t max_query_len;
     int32_t q_blocks;         // query tiles per sequence (grid)
     int32_t key_begin;        // keys of this launch: [key_begin, key_end), key_begin a
     int32_t key_end;          // multiple of 64, window length <= ring_tokens with a ring
     int32_t carry;            // 1: merge into the out / lse an earlier window wrote
-    uint32_t p_magic, p_shift;  // key / page_tokens == (umulhi(key, p_magic) + key) >> p_shift
     float scale_log2;
     float *out;
     float *lse;
@@ -124,14 +123,19 @@ struct RegenFillParams {
     void *v_dst;
 };
 
-// Regenerated K/V of one key window of a chunked prefill, written into the
-// ring the prefill kernel reads: ring[seq][Hkv][window_tokens][128] bf16.
-struct RegenWindowParams {
-    PosParams pos;                 // rope: K written rotated by its token position
+// One key window of a chunked prefill gathered into the ring the prefill
+// kernel reads: ring[seq][Hkv][window_tokens][128], K in the kv type, V in
+// f16; regenerated keys from the page regenerator, other keys through the
+// page table.
+struct WindowParams {
+    PosParams pos;                 // rope: regenerated K rotated by its token position
     uint64_t seed;
     uint32_t layer;
-    int32_t num_seqs, num_kv_heads, page_tokens;
-    const int32_t *regen_pages;    // [num_seqs]
+    int32_t num_seqs, num_kv_heads, page_tokens, max_pages, num_blocks;
+    const void *k_pool, *v_pool;   // [num_blocks][Hkv][P][128]
+    const int32_t *page_table;
+    int32_t kv_f16;                // 1: f16 pools, 0: bf16 pools
+    const int32_t *regen_pages;    // [num_seqs] or null
     int32_t max_regen;
     const int32_t *context_lens;   // [num_seqs]
     int32_t max_context_len, max_keys;
@@ -231,12 +235,12 @@ hipError_t launch_decode_mfma(const DecodeParams &p, int kv_type, int group, int
                               hipStream_t stream);
 // Query rows per workgroup of the matrix-core prefill kernel.
 constexpr int kPrefillRows = 256;
-// Keys per window of a chunked prefill with regenerated pages (the default
-// when the caller leaves split_tokens at 0).
+// Keys per window of a matrix-core chunked prefill (the default when the
+// caller leaves split_tokens at 0).
 constexpr int kPrefillWindow = 16384;
 hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream);
 hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream);
-hipError_t launch_regen_window(const RegenWindowParams &r, hipStream_t stream);
+hipError_t launch_window_prepare(const WindowParams &r, hipStream_t stream);
 hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
                          int32_t num_kv_heads, int32_t head_dim, int32_t page_tokens,
                          int32_t num_blocks, int32_t elem_bytes, int32_t num_tokens,

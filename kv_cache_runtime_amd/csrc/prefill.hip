@@ -22,22 +22,26 @@
 //                                                  read, B = P^T in VGPRs)
 // so each row lives in one lane pair (r, r + 32) for the softmax.
 //
-// Phases.  The waves of a workgroup are dealt to the four SIMDs round-robin,
-// so waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 run the same
-// sequence of clusters -- matrix cluster M_a (P.V of tile a - 1 and the scores
-// of tile a), vector cluster V_a (the softmax of tile a and the staging of the
-// next tiles) -- but waves 4-7 run one slot behind.  Every slot ends with a
-// workgroup barrier, so on each SIMD one wave issues matrix instructions while
-// the other runs the exponentials, and the matrix cores do not wait for the
-// softmax.
+// Schedule.  The waves of a workgroup are dealt to the four SIMDs
+// round-robin, so two waves share each SIMD and its matrix core.  An
+// exponential in one wave holds up the matrix instructions of the other, so
+// each wave interleaves its own work instead: keys are folded in units of 32,
+// and while the matrix core computes the scores of unit u + 1 the wave takes
+// the exponentials of unit u between the products; the P.V products of unit
+// u then run beside the row max of unit u + 1.  The issue order inside a
+// unit is fixed with scheduling barriers.
 //
-// Staging.  LDS holds two buffers, each a 64-key K tile (row-major) and a
-// 64-key V tile (row-major, f16: bf16 values are converted while staged, so
-// P.V runs with f16 probabilities).  Buffer x % 2 holds K of tile x and V of
-// tile x - 1, read by M_x; each wave group stages its 32 keys of the next
-// buffer in its vector clusters, from registers loaded one cluster earlier.
+// Staging.  The keys of the call come from a ring the window preparation
+// kernel fills (K in the kv type, V in f16), 64 contiguous rows per tile.
+// They move from memory straight into LDS by DMA (global_load_lds), with no
+// registers in between.  LDS holds four buffers of one K tile and one V tile
+// each; a tile is issued three tiles ahead and the workgroup meets once per
+// tile.  Rows are not padded: the 16-byte chunks of each row are permuted
+// so that the fragment reads of the matrix operands hit distinct banks.
 // P is kept relative to the reference max minus 7 and is at most 2^15, so
 // P * V stays finite for |v| <= 65504, the f16 range that bf16 V must lie in.
+#include <type_traits>
+
 #include "device.h"
 
 namespace atlas {
@@ -49,12 +53,13 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;          // head_dim
 constexpr int kTile = 64;        // keys per tile
 constexpr int kWaves = 8;        // waves per workgroup
-constexpr int kKPitch = 136;     // K tile row pitch, 16-bit elements (68 dwords)
-constexpr int kVPitch = 160;     // V tile row pitch, 16-bit elements (80 dwords)
+constexpr int kRowBytes = kD * 2;             // one staged K or V row
+constexpr int kTileBytes = kTile * kRowBytes;  // one staged K or V tile
 
 template <int KV>
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
@@ -86,11 +91,30 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// Barrier between slots: LDS traffic settled, global loads left in flight.
-__device__ __forceinline__ void slot_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l writes bytes 16 l .. 16 l + 15 after the
+// wave-uniform LDS address dst.  Counted by vmcnt like any load.
+__device__ __forceinline__ void lds_dma16(const void *src, uint16_t *dst) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(src),
+                                     reinterpret_cast<uint4 *>(dst), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): the tile DMAs issued before the last N
+// loads have landed in LDS and this wave's LDS reads have returned.
+template <int N>
+__device__ __forceinline__ void tile_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Barrier between tiles.  Inside the key loop LDS is written only by the
+// tile DMAs, whose completion tile_wait establishes, so no fence is used (a
+// workgroup fence would also wait for the DMA still in flight).  The empty
+// asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    asm volatile("" ::: "memory");
 }
 
 // ALIBI: scores gain -slope_h * (pos - key).  ROPE: q is rotated by its
@@ -107,14 +131,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     constexpr float kPScale = 7.0f;
     const float kNegInf = -__builtin_inff();
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTile * kKPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kTile * kVPitch];
+    // four LDS buffers, each a K tile and a V tile; separate objects, so
+    // that the compiler sees a DMA into one buffer does not alias reads of
+    // another and adds no wait for it
+    __shared__ __attribute__((aligned(1024))) uint16_t sB0[2 * kTile * kD], sB1[2 * kTile * kD],
+        sB2[2 * kTile * kD], sB3[2 * kTile * kD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wave-uniform (scalar) so that the cluster branches below are uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2;   // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
     const int r = lane & 31, half = lane >> 5;
 
     const int g = blockIdx.x % p.num_kv_heads;
@@ -142,14 +168,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     const int wave_min_pos = ctx - n_q + t_base + wave * kPosWave;
     const bool wave_rows_ok = __all(row_ok);
 
-    int n_regen = 0;
+    // a regenerated-page count outside the host bound fails loudly (the
+    // window preparation leaves such a sequence's ring rows alone)
     bool regen_bad = false;
     if (p.regen_pages != nullptr && ctx_ok) {
-        n_regen = p.regen_pages[seq];
-        if (n_regen < 0 || n_regen > p.max_regen) {  // outside the host bound: fail loudly
-            regen_bad = true;
-            n_regen = 0;
-        }
+        const int n_regen = p.regen_pages[seq];
+        regen_bad = n_regen < 0 || n_regen > p.max_regen;
     }
 
     // keys of this call: the window, cut at the last key any row here sees
@@ -215,241 +239,310 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[b][j] = 0.0f;
-    f32x16_t s[2];
-    uint4 pb[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) pb[st] = make_uint4(0, 0, 0, 0);
     float m_ref = kNegInf, l = 0.0f;
-    bool bad = false;
+    float alpha = 1.0f;     // rescale of o and l owed before the next P.V
+    bool owe = false;       // some lane of the wave moved its reference max
 
-    // ---- staging: this thread moves 16 dims of key 32 grp + tg / 8 of a
-    // tile, for K and for V.  K dims 16 cp .. 16 cp + 15; V dims of chunks c0
-    // and c0 + 4 (8 dims each), which keeps the 16 lanes of one LDS write
-    // phase on distinct banks with the 80-dword V pitch.
-    const int tg = tid & 255;
-    const int srow = 32 * grp + (tg >> 3);
-    const int cp = tg & 7;
-    const int vc0 = (cp & 3) + 8 * (cp >> 2);
-    const int P = p.page_tokens;
-    const int64_t trow = (int64_t)seq * p.max_pages;
-    const int64_t ring_row0 = ((int64_t)seq * p.num_kv_heads + g) * p.ring_tokens;
-    // Element offset of key `key`'s row of this kv head, in the ring or in the
-    // pool through the page table.  `ent` is the page-table entry of the key's
-    // page (read ahead by the caller).
-    auto row_offset = [&](int key, int ent, const uint16_t *&base) -> int64_t {
-        const int lp = (int)((__umulhi((uint32_t)key, p.p_magic) + (uint32_t)key) >> p.p_shift);
-        if (lp < n_regen) {
-            base = reinterpret_cast<const uint16_t *>(p.ring_k);
-            return (ring_row0 + (key - kb0)) * kD;
-        }
-        int blk = ent;
-        if (blk < 0 || blk >= p.num_blocks) {
-            bad = true;
-            blk = 0;
-        }
-        base = nullptr;
-        return (((int64_t)blk * p.num_kv_heads + g) * P + (key - lp * P)) * kD;
+    // ---- staging.  Tiles come from the window's ring [seq][kv head][key -
+    // key_begin][D] (K in the kv type, V in f16, rows past the context zero),
+    // so a tile is 64 contiguous rows of 256 bytes.  They go straight from
+    // memory into LDS by DMA (global_load_lds_dwordx4: lane l of a wave's
+    // load fills bytes 16 l .. 16 l + 15 of a 1 KiB stretch, from any address
+    // it names), four loads per thread per tile pair.  Rows are not padded;
+    // instead the 16-byte chunks of a row are permuted so that the matrix
+    // operand reads hit distinct banks: chunk c of K row k sits at position
+    // c ^ (k % 16), chunk c of V row k at c ^ (4 (k % 4) + 2 ((k / 4) % 2)).
+    // Content x is K of tile x and V of tile x - 1; it lives in buffer x % 4
+    // and is issued three tiles before it is read.
+    // buffer B: K tile at element 0, V tile at element kTile * kD
+    auto kbuf = [&](auto b_c) __attribute__((always_inline)) -> uint16_t * {
+        constexpr int B = decltype(b_c)::value & 3;
+        if constexpr (B == 0) return sB0;
+        else if constexpr (B == 1) return sB1;
+        else if constexpr (B == 2) return sB2;
+        else return sB3;
     };
-    auto entry_of = [&](int key) -> int {
-        const int lp = (int)((__umulhi((uint32_t)key, p.p_magic) + (uint32_t)key) >> p.p_shift);
-        return lp >= n_regen ? p.page_table[trow + lp] : 0;
+    auto vbuf = [&](auto b_c) __attribute__((always_inline)) -> uint16_t * {
+        return kbuf(b_c) + kTile * kD;
     };
-    uint4 kst[2], vst[2];
-    int ent_k = 0, ent_v = 0;  // entries of the next content's keys
-    // Loads this group's half of content x (K of tile x, V of tile x - 1)
-    // into kst / vst; keys past the visible range load zeros.
-    auto load_content = [&](int x) {
-        const int kk = kb0 + kTile * x + srow;
-        const int kv = kk - kTile;
-        if (x < n_tiles && kk < kb1) {
-            const uint16_t *base;
-            int64_t off = row_offset(kk, ent_k, base);
-            const uint16_t *src = (base ? base : reinterpret_cast<const uint16_t *>(p.k_pool)) +
-                                  off + 16 * cp;
-            kst[0] = *reinterpret_cast<const uint4 *>(src);
-            kst[1] = *reinterpret_cast<const uint4 *>(src + 8);
-        } else {
-            kst[0] = kst[1] = make_uint4(0, 0, 0, 0);
+    const int64_t ring0 = ((int64_t)seq * p.num_kv_heads + g) * p.ring_tokens * kD;
+    const char *const rk = reinterpret_cast<const char *>(p.ring_k) + 2 * ring0;
+    const char *const rv = reinterpret_cast<const char *>(p.ring_v) + 2 * ring0;
+    // thread's DMA rows: 8 wave + 4 i + lane / 16 (i = 0, 1), position
+    // lane % 16; the byte offsets within a tile are recomputed at each use
+    // from a lane index the compiler cannot hoist (keeping them costs
+    // registers the products need)
+    auto dma_offsets = [&](uint32_t (&ko)[2], uint32_t (&vo)[2]) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = 8 * wave + 4 * i + (ln >> 4), at = ln & 15;
+            ko[i] = row * kRowBytes + ((at ^ (row & 15)) << 4);
+            vo[i] = row * kRowBytes + ((at ^ (4 * (row & 3) + 2 * ((row >> 2) & 1))) << 4);
         }
-        if (x >= 1 && x <= n_tiles && kv < kb1) {
-            const uint16_t *base;
-            int64_t off = row_offset(kv, ent_v, base);
-            const uint16_t *src = (base ? reinterpret_cast<const uint16_t *>(p.ring_v)
-                                        : reinterpret_cast<const uint16_t *>(p.v_pool)) +
-                                  off + 8 * vc0;
-            vst[0] = *reinterpret_cast<const uint4 *>(src);
-            vst[1] = *reinterpret_cast<const uint4 *>(src + 32);
-        } else {
-            vst[0] = vst[1] = make_uint4(0, 0, 0, 0);
-        }
-        // entries of content x + 1 (the next call), read ahead
-        const int nk = kk + kTile, nv = kv + kTile;
-        ent_k = (x + 1 < n_tiles && nk < kb1) ? entry_of(nk) : 0;
-        ent_v = (x + 1 <= n_tiles && nv < kb1) ? entry_of(nv) : 0;
     };
-    auto write_content = [&](int x) {
-        const int buf = x & 1;
-        uint16_t *kd = &sK[buf][srow * kKPitch + 16 * cp];
-        *reinterpret_cast<uint4 *>(kd) = kst[0];
-        *reinterpret_cast<uint4 *>(kd + 8) = kst[1];
-        uint4 v0 = vst[0], v1 = vst[1];
-        if constexpr (KV == KV_BF16) {
-            v0 = make_uint4(bf16x2_to_f16x2(v0.x), bf16x2_to_f16x2(v0.y), bf16x2_to_f16x2(v0.z),
-                            bf16x2_to_f16x2(v0.w));
-            v1 = make_uint4(bf16x2_to_f16x2(v1.x), bf16x2_to_f16x2(v1.y), bf16x2_to_f16x2(v1.z),
-                            bf16x2_to_f16x2(v1.w));
-        }
-        uint16_t *vd = &sV[buf][srow * kVPitch + 8 * vc0];
-        *reinterpret_cast<uint4 *>(vd) = v0;
-        *reinterpret_cast<uint4 *>(vd + 32) = v1;
+    // Every content issues exactly four loads (past the tiles of the call
+    // they read a clamped, valid tile that is never used), so a wait for
+    // "all but the last four" means "all but the newest content".
+    auto dma_content = [&](int x, auto b_c) __attribute__((always_inline)) {
+        const int xk = min(x, n_tiles - 1);
+        const int xv = max(min(x - 1, n_tiles - 1), 0);
+        uint32_t kofs[2], vofs[2];
+        dma_offsets(kofs, vofs);
+        const char *ks = rk + (int64_t)xk * kTileBytes;
+        const char *vs = rv + (int64_t)xv * kTileBytes;
+        // opaque scalar tile bases: each load is then a scalar base plus the
+        // lane's 32-bit offset, not a 64-bit lane address kept in VGPRs
+        asm("" : "+s"(ks));
+        asm("" : "+s"(vs));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16(ks + kofs[i], kbuf(b_c) + (8 * wave + 4 * i) * kD);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16(vs + vofs[i], vbuf(b_c) + (8 * wave + 4 * i) * kD);
     };
 
-    // prologue: content 0 (K of tile 0) from both groups, then the first
-    // content each group writes inside the loop (content 1)
-    {
-        ent_k = kb0 + srow < kb1 ? entry_of(kb0 + srow) : 0;
-        load_content(0);
-        write_content(0);
-        load_content(1);
-    }
-    slot_barrier();
-
-    // ---- matrix cluster M_a: P.V of tile a - 1, scores of tile a
-    auto matrix_cluster = [&](int a) {
-        const uint16_t *cK = sK[a & 1];
-        const uint16_t *cV = sV[a & 1];
-        if (a >= 1) {
-            // A = V^T: lane (dim 32 b + r, half) takes keys 16 st + 4 half ..
-            // + 3 and 16 st + 8 + 4 half .. + 3 (two transposing reads), the
-            // key order of P^T's registers
-            const int q16 = lane >> 4, s16 = lane & 15;
-            const int kq = 4 * (q16 >> 1) + (s16 >> 2);     // row within the 16-key step
-            const int nq = 16 * (q16 & 1) + 4 * (s16 & 3);  // dim within the 32-dim block
+    // The keys are folded in units of 32 (unit u = keys 32 u .. 32 u + 31 of
+    // the call, half u % 2 of tile u / 2), one 32 x 32 score block each.
+    // ---- scores of unit u (K of tile u / 2, buffer B = (u / 2) % 4).  Lane
+    // (r, half) reads chunk 2 ks + half of row 32 (u % 2) + r, which sits at
+    // byte (r * 256 + ((half ^ r % 16) << 4)) ^ (ks << 5) of its half tile.
+    const uint32_t kaddr = r * kRowBytes + ((half ^ (r & 15)) << 4);
+    auto scores = [&](int u, f32x16_t &dst, auto b_c) __attribute__((always_inline)) {
+        const char *cK = reinterpret_cast<const char *>(kbuf(b_c)) + (u & 1) * (32 * kRowBytes);
+        // the eight read addresses are rebuilt here from an opaque copy of
+        // kaddr: hoisted out of the loop they would take eight registers
+        uint32_t ka = kaddr;
+        asm volatile("" : "+v"(ka));
+        uint4 kf[2];
+        kf[0] = *reinterpret_cast<const uint4 *>(cK + ka);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint16_t *vp = cV + (16 * st + kq) * kVPitch + 32 * b + nq;
-                    const uint2 x0 = lds_read_tr16(vp);
-                    const uint2 x1 = lds_read_tr16(vp + 8 * kVPitch);
-                    o[b] = mfma32<KV_F16>(make_uint4(x0.x, x0.y, x1.x, x1.y), pb[st], o[b]);
-                }
-            }
-        }
-        if (a < n_tiles) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const uint4 av = *reinterpret_cast<const uint4 *>(
-                        &cK[(32 * kb + r) * kKPitch + 16 * ks + 8 * half]);
-                    s[kb] = mfma32<KV>(av, qf[ks], s[kb]);
-                    if constexpr (ROPE) s[kb] = mfma32<KV>(av, qlo[ks], s[kb]);
-                }
-            }
+        for (int ks = 0; ks < 8; ++ks) {
+            if (ks < 7)
+                kf[(ks + 1) & 1] = *reinterpret_cast<const uint4 *>(cK + (ka ^ ((ks + 1) << 5)));
+            // the first step starts from a zero accumulator operand
+            dst = mfma32<KV>(kf[ks & 1], qf[ks], ks == 0 ? f32x16_t{} : dst);
+            if constexpr (ROPE) dst = mfma32<KV>(kf[ks & 1], qlo[ks], dst);
         }
     };
-    // ---- vector cluster V_a: staging (group 0 writes content a + 1, group 1
-    // content a + 2), then the softmax of tile a (a = -1: staging only)
-    auto vector_cluster = [&](int a) {
-        const int x = a + 1 + grp;
-        if (x <= n_tiles) {
-            write_content(x);
-            load_content(x + 1);
-        }
-        if (a < 0) return;
-        // S^T register j of block kb holds key k0 + 32 kb + 8 (j / 4) +
-        // 4 half + j % 4 of row r
-        const int k0 = kb0 + kTile * a;
-        float rb = 0.0f;
+    // ---- P.V of unit u (V of tile u / 2, content u / 2 + 1, buffer B).  A =
+    // V^T: lane (dim 32 b + r, half) takes keys 16 st + 4 half .. + 3 and
+    // 16 st + 8 + 4 half .. + 3 (two transposing reads), the key order of
+    // P^T's registers.  The read of lane (q16, s16) starts at row kq, dims
+    // 32 b + nq .. + 3; with the chunk permutation that is byte vaddr ^ (b << 6)
+    // of the 8-row stretch.
+    const int q16 = lane >> 4, s16 = lane & 15;
+    const int kq = 4 * (q16 >> 1) + (s16 >> 2);     // row within the 8-row stretch
+    const int nq = 16 * (q16 & 1) + 4 * (s16 & 3);  // dim within the 32-dim block
+    const uint32_t vaddr =
+        kq * kRowBytes + (((nq >> 3) ^ (4 * (kq & 3) + 2 * (kq >> 2))) << 4) + (nq & 7) * 2;
+    uint4 pb[2];  // P^T operands of the unit being folded
+    // ---- softmax, part 1 (unit u): ALiBi, the causal mask (mask: the unit
+    // reaches past some row's position), the row max and the new reference;
+    // the rescale it implies is owed to the accumulators.  Score register j
+    // holds key k0 + 8 (j / 4) + 4 half + j % 4 of row r.
+    auto alibi_bias = [&](f32x16_t &sx) __attribute__((always_inline)) {
         if constexpr (ALIBI) {
-            // ab * (key - pos) = ab * o_j + rb with o_j a fixed offset of the
-            // register slot and rb the row's tile offset
-            rb = ab * (float)(k0 + 4 * half - pos);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    s[kb][j] = fmaf(ab, (float)(32 * kb + 8 * (j >> 2) + (j & 3)), s[kb][j]);
+            for (int j = 0; j < 16; ++j) sx[j] = fmaf(ab, (float)(8 * (j >> 2) + (j & 3)), sx[j]);
         }
-        if (!wave_rows_ok || k0 + kTile - 1 > wave_min_pos) {
+    };
+    auto causal_mask = [&](int u, f32x16_t &sx) __attribute__((always_inline)) {
+        // register j is visible when its key offset 8 (j / 4) + j % 4 stays
+        // within lim (a row outside the chunk sees nothing)
+        const int lim = row_ok ? pos - kb0 - 32 * u - 4 * half : -1;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * half + (j & 3);
-                    s[kb][j] = (row_ok && key <= pos) ? s[kb][j] : kNegInf;
-                }
-        }
-        float mraw = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, s[kb][j]);
-        if constexpr (ALIBI) mraw += rb;
+        for (int j = 0; j < 16; ++j) sx[j] = 8 * (j >> 2) + (j & 3) <= lim ? sx[j] : kNegInf;
+    };
+    // mraw: the max of this lane's (biased, masked) scores of unit u
+    auto new_reference = [&](int u, float mraw) __attribute__((always_inline)) {
+        if constexpr (ALIBI) mraw += ab * (float)(kb0 + 32 * u + 4 * half - pos);
         {  // the row's other half (lane r + 32)
             const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw),
                                                             __float_as_uint(mraw), false, false);
             mraw = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
         }
         const float mt = mraw * p.scale_log2;    // scale > 0 keeps the order
-        const bool move = mt > m_ref + kSlack;  // also true on the first finite tile
-        if (__any(move)) {
-            const float m_new = move ? mt : m_ref;
-            const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-            m_ref = m_new;
+        const bool move = mt > m_ref + kSlack;  // also true on the first finite unit
+        const float m_new = move ? mt : m_ref;
+        alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+        m_ref = m_new;
+        owe = __any(move);
+    };
+    auto row_max = [&](int u, f32x16_t &sx, bool mask) __attribute__((always_inline)) {
+        if (mask) causal_mask(u, sx);  // wave-uniform
+        float mraw = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, sx[j]);
+        new_reference(u, mraw);
+    };
+    auto settle = [&]() __attribute__((always_inline)) {  // pay a rescale owed to the accumulators
+        if (owe) {
             l *= alpha;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
         }
-        // P^T operands (f16, relative to m_ref - 7); step st covers keys 16 st
-        // .. 16 st + 15 of the tile: registers 8 (st % 2) .. + 7 of block st / 2
-        float m_off = (m_ref == kNegInf) ? 0.0f : m_ref - kPScale;
-        if constexpr (ALIBI) m_off = fmaf(-rb, p.scale_log2, m_off);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int kb = st >> 1, j0 = 8 * (st & 1);
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p0 =
-                    __builtin_amdgcn_exp2f(fmaf(s[kb][j0 + 2 * i], p.scale_log2, -m_off));
-                const float p1 =
-                    __builtin_amdgcn_exp2f(fmaf(s[kb][j0 + 2 * i + 1], p.scale_log2, -m_off));
-                const f16x2_t h = {(_Float16)p0, (_Float16)p1};
-                // l sums the f16 weights the matrix cores use
-                l = __builtin_amdgcn_fdot2(h, f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, l, false);
-                w[i] = __builtin_bit_cast(uint32_t, h);
-            }
-            pb[st] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
     };
+    // a unit needs the causal mask when it reaches past the first position of
+    // the wave (or the wave holds rows past the chunk)
+    auto masked = [&](int u) { return !wave_rows_ok || kb0 + 32 * u + 31 > wave_min_pos; };
+    // One unit, in an explicit issue order (the compiler may not move code
+    // across the scheduling barriers): the scores of unit u + 1 on the matrix
+    // cores, each product beside one exponential pair of unit u and the read
+    // of a K fragment four products ahead; then the P.V products of unit u,
+    // the first four beside the reads of the last V fragments, the last four
+    // beside the row max of unit u + 1.  sc holds unit u's scores, sn
+    // receives unit u + 1's.  MORE: a unit follows; KB / VB: the buffers of
+    // the K tile of unit u + 1 and of the V tile of unit u.
+    auto unit = [&](int u, f32x16_t &sc, f32x16_t &sn, auto more_c, auto kb_c,
+                    auto vb_c) __attribute__((always_inline)) {
+        constexpr bool MORE = decltype(more_c)::value;
+        constexpr int kAhead = 4;  // K fragments in flight
+        settle();
+        const char *cK =
+            reinterpret_cast<const char *>(kbuf(kb_c)) + ((u + 1) & 1) * (32 * kRowBytes);
+        const char *cV = reinterpret_cast<const char *>(vbuf(vb_c)) + (u & 1) * (32 * kRowBytes);
+        // the read addresses are rebuilt here from opaque copies: hoisted out
+        // of the loop they would take a dozen registers
+        uint32_t ka = kaddr, va = vaddr;
+        asm volatile("" : "+v"(ka), "+v"(va));
+        uint4 kf[8];
+        uint4 vf[2][4];
+        auto kread = [&](int ks) __attribute__((always_inline)) {
+            kf[ks] = *reinterpret_cast<const uint4 *>(cK + (ka ^ (ks << 5)));
+        };
+        auto vread = [&](int st, int b) __attribute__((always_inline)) {
+            const char *vp = cV + (va ^ (b << 6)) + 16 * st * kRowBytes;
+            const uint2 x0 = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp));
+            const uint2 x1 = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp + 8 * kRowBytes));
+            vf[st][b] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        };
+        // probabilities of unit u as f16 P^T operands, relative to m_ref - 7;
+        // pair i is registers 2 i, 2 i + 1 (step i / 4 of the P.V).  l sums
+        // the f16 weights the matrix cores use.
+        float m_off = (m_ref == kNegInf) ? 0.0f : m_ref - kPScale;
+        if constexpr (ALIBI)
+            m_off = fmaf(-ab * (float)(kb0 + 32 * u + 4 * half - pos), p.scale_log2, m_off);
+        uint32_t w[8];
+        auto pexp = [&](int i) __attribute__((always_inline)) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i], p.scale_log2, -m_off));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i + 1], p.scale_log2, -m_off));
+            const f16x2_t h = {(_Float16)p0, (_Float16)p1};
+            l = __builtin_amdgcn_fdot2(h, f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, l, false);
+            w[i] = __builtin_bit_cast(uint32_t, h);
+            // keep the pair here, beside its matrix product (the compiler
+            // would otherwise sink it to its use after the mask branch)
+            asm volatile("" : "+v"(w[i]), "+v"(l));
+        };
+        if constexpr (MORE) {
+#pragma unroll
+            for (int ks = 0; ks < kAhead; ++ks) kread(ks);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) vread(0, b);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (MORE) {
+                // the first step starts from a zero accumulator operand
+                sn = mfma32<KV>(kf[i], qf[i], i == 0 ? f32x16_t{} : sn);
+                if constexpr (ROPE) sn = mfma32<KV>(kf[i], qlo[i], sn);
+                if (i + kAhead < 8) kread(i + kAhead);
+            }
+            pexp(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pb[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        pb[1] = make_uint4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            o[b] = mfma32<KV_F16>(vf[0][b], pb[0], o[b]);
+            vread(1, b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MORE) {
+            alibi_bias(sn);
+            if (masked(u + 1)) causal_mask(u + 1, sn);
+        }
+        // the row max of unit u + 1 beside the last four products
+        float mraw = kNegInf;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            o[b] = mfma32<KV_F16>(vf[1][b], pb[1], o[b]);
+            if constexpr (MORE) {
+#pragma unroll
+                for (int j = 4 * b; j < 4 * b + 4; ++j) mraw = fmaxf(mraw, sn[j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MORE) new_reference(u + 1, mraw);
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
+    using B3 = std::integral_constant<int, 3>;
 
-    // ---- slots: M_0, V_0, M_1, ..., V_{n-1}, M_n, each followed by a
-    // barrier; waves 4-7 run one slot behind (a staging-only slot first),
-    // waves 0-3 end with an empty slot, so every wave passes 2 n + 2 barriers
-    if (grp == 1) {
-        vector_cluster(-1);
-        slot_barrier();
+    // ---- prologue: contents 0, 1 and 2 in LDS, the scores of unit 0.  All
+    // three have landed before the loop, so that its first tile starts from
+    // the same pending state as every later one (the compiler tracks the LDS
+    // DMAs for the waits it adds to LDS reads, and a DMA of unknown age
+    // there would cost a full wait).
+    f32x16_t sa, sb;
+    dma_content(0, B0{});
+    dma_content(1, B1{});
+    dma_content(2, B2{});
+    tile_wait<0>();
+    tile_barrier();
+    scores(0, sa, B0{});
+    alibi_bias(sa);
+    row_max(0, sa, masked(0));
+
+    // ---- iteration t folds tile t (units 2t, 2t + 1) from contents t and
+    // t + 1 (buffers P = t % 4 and P + 1).
+    auto iteration = [&](int t, auto ph_c, auto more_c) __attribute__((always_inline)) {
+        constexpr int P = decltype(ph_c)::value;
+        using BK = std::integral_constant<int, P>;
+        using BN = std::integral_constant<int, (P + 1) & 3>;
+        unit(2 * t, sa, sb, std::true_type{}, BK{}, BN{});
+        unit(2 * t + 1, sb, sa, more_c, BN{}, BN{});
+    };
+    // Every tile but the last issues content t + 3 into the buffer of content
+    // t - 1, free since the last barrier, and ends once content t + 2 has
+    // landed: one barrier per tile.  The loop is unrolled by the four buffer
+    // phases and holds one DMA per phase, with no branch around a DMA, so the
+    // compiler tells the buffers apart and adds no wait of its own.
+    auto step = [&](int t, auto ph_c) __attribute__((always_inline)) {
+        constexpr int P = decltype(ph_c)::value;
+        dma_content(t + 3, std::integral_constant<int, (P + 3) & 3>{});
+        iteration(t, ph_c, std::true_type{});
+        tile_wait<4>();
+        tile_barrier();
+    };
+    int tl = 0;  // tiles folded so far
+    for (; tl + 4 < n_tiles; tl += 4) {
+        step(tl, B0{});
+        step(tl + 1, B1{});
+        step(tl + 2, B2{});
+        step(tl + 3, B3{});
     }
-    for (int a = 0; a < n_tiles; ++a) {
-        matrix_cluster(a);
-        slot_barrier();
-        vector_cluster(a);
-        slot_barrier();
+    // the remaining 1 .. 4 tiles: all but the last as above, then the last
+    const int rem = n_tiles - tl;
+    if (rem > 1) step(tl, B0{});
+    if (rem > 2) step(tl + 1, B1{});
+    if (rem > 3) step(tl + 2, B2{});
+    switch (rem) {
+        case 1: iteration(tl, B0{}, std::false_type{}); break;
+        case 2: iteration(tl + 1, B1{}, std::false_type{}); break;
+        case 3: iteration(tl + 2, B2{}, std::false_type{}); break;
+        default: iteration(tl + 3, B3{}, std::false_type{}); break;
     }
-    matrix_cluster(n_tiles);
-    slot_barrier();
-    if (grp == 0) slot_barrier();
+    tile_wait<0>();  // no DMA may still be writing LDS when the wave ends
 
     // ---- combine the two halves of each row and write (or merge) out / lse
-    const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0 || !ctx_ok || regen_bad;
+    __syncthreads();
+    const bool any_bad = !ctx_ok || regen_bad;
     const float l_row = l + __shfl_xor(l, 32);
     if (t >= n_q) return;
     float *dst = p.out + orow0 * kD;
@@ -475,6 +568,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         }
         if (lse_p != lse_p) lse_new = qnan;  // an earlier window failed
     }
+    float4 prev[16];  // the earlier windows' output, all loads issued together
+    if (p.carry) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            prev[i] = *reinterpret_cast<const float4 *>(dst + 32 * (i >> 2) + 8 * (i & 3) + 4 * half);
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -483,7 +582,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
             float4 v = make_float4(o[b][4 * jj] * wb, o[b][4 * jj + 1] * wb,
                                    o[b][4 * jj + 2] * wb, o[b][4 * jj + 3] * wb);
             if (p.carry) {
-                const float4 op = *reinterpret_cast<const float4 *>(dst + d0);
+                const float4 op = prev[4 * b + jj];
                 v = make_float4(fmaf(op.x, wa, v.x), fmaf(op.y, wa, v.y), fmaf(op.z, wa, v.z),
                                 fmaf(op.w, wa, v.w));
             }
@@ -492,6 +591,93 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         }
     }
     if (half == 0) p.lse[orow0] = any_bad ? qnan : lse_new;
+}
+
+// Window preparation: every key of the window [key_begin, key_begin +
+// window_tokens) of every (sequence, kv head) is written into the ring the
+// prefill kernel reads, K in the kv type and V in f16: regenerated keys from
+// the SplitMix64 regenerator (once per call; K rotated by its position under
+// RoPE), other keys gathered through the page table (CFR-Atlas README: cold
+// pages regenerated into scratch buffers that are reused, here one ring per
+// window), keys past the context as zeros, and the keys of a page whose block
+// id lies outside the pool as NaN, so the rows that see them fail loudly.
+// One workgroup per (sequence, kv head, 64 keys); four lanes per key row, each
+// moving 32 dims (64 contiguous bytes of K and of V).
+__global__ __launch_bounds__(256) void window_prepare_kernel(const WindowParams r) {
+    constexpr int D = kD;
+    const int groups = r.window_tokens / 64;
+    const int gi = blockIdx.x % groups;
+    const int rest = blockIdx.x / groups;
+    const int g = rest % r.num_kv_heads;
+    const int seq = rest / r.num_kv_heads;
+    const int ctx = r.context_lens[seq];
+    // sequences the prefill kernel turns into NaN rows need no ring rows
+    if (ctx < 0 || ctx > r.max_context_len || ctx > r.max_keys) return;
+    const int n_regen = r.regen_pages != nullptr ? r.regen_pages[seq] : 0;
+    if (n_regen < 0 || n_regen > r.max_regen) return;
+    const int P = r.page_tokens;
+    const int64_t regen_keys = (int64_t)n_regen * P;
+    const int row = threadIdx.x >> 2;      // key row within the 64
+    const int d0 = 32 * (threadIdx.x & 3);  // first dim of this lane
+    const int key = r.key_begin + 64 * gi + row;
+    const int64_t at = (((int64_t)seq * r.num_kv_heads + g) * r.window_tokens + 64 * gi + row) * D + d0;
+    uint32_t kw[16], vw[16];  // 32 dims of K and V as 16-bit pairs
+    if (key >= ctx) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kw[i] = vw[i] = 0u;
+    } else if ((int64_t)key < regen_keys) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int dim = d0 + 2 * i;
+            uint32_t k0 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, key, dim, 0));
+            uint32_t k1 = regen_bf16_bits(r.seed, regen_counter(r.layer, g, key, dim + 1, 0));
+            if (r.pos.rope) {  // cached keys are rotated by their position
+                float x0 = __uint_as_float(k0 << 16), x1 = __uint_as_float(k1 << 16);
+                rope_rotate(x0, x1, key, rope_turns(dim / 2, D, r.pos.rope_log2_theta));
+                k0 = __float_as_uint(bf16_round(x0)) >> 16;
+                k1 = __float_as_uint(bf16_round(x1)) >> 16;
+            }
+            kw[i] = k0 | (k1 << 16);
+            // f16 holds a regenerated value exactly (at most 8 significant
+            // bits, within [-1, 1])
+            const float v0 = regen_value(r.seed, regen_counter(r.layer, g, key, dim, 1));
+            const float v1 = regen_value(r.seed, regen_counter(r.layer, g, key, dim + 1, 1));
+            const f16x2_t vh = {(_Float16)v0, (_Float16)v1};
+            vw[i] = __builtin_bit_cast(uint32_t, vh);
+        }
+    } else {
+        const int lp = key / P;
+        const int blk = r.page_table[(int64_t)seq * r.max_pages + lp];
+        if (blk < 0 || blk >= r.num_blocks) {
+            const uint32_t knan = r.kv_f16 ? 0x7E007E00u : 0x7FC07FC0u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                kw[i] = knan;
+                vw[i] = 0x7E007E00u;
+            }
+        } else {
+            const int64_t src = (((int64_t)blk * r.num_kv_heads + g) * P + (key - lp * P)) * D + d0;
+            const uint4 *ks = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(r.k_pool) + src);
+            const uint4 *vs = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(r.v_pool) + src);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint4 a = ks[c], b = vs[c];
+                kw[4 * c] = a.x; kw[4 * c + 1] = a.y; kw[4 * c + 2] = a.z; kw[4 * c + 3] = a.w;
+                vw[4 * c] = b.x; vw[4 * c + 1] = b.y; vw[4 * c + 2] = b.z; vw[4 * c + 3] = b.w;
+            }
+            if (!r.kv_f16) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) vw[i] = bf16x2_to_f16x2(vw[i]);
+            }
+        }
+    }
+    uint4 *kd = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(r.ring_k) + at);
+    uint4 *vd = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(r.ring_v) + at);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        kd[c] = make_uint4(kw[4 * c], kw[4 * c + 1], kw[4 * c + 2], kw[4 * c + 3]);
+        vd[c] = make_uint4(vw[4 * c], vw[4 * c + 1], vw[4 * c + 2], vw[4 * c + 3]);
+    }
 }
 
 template <int KV, bool A, bool R>
@@ -519,7 +705,12 @@ hipError_t by_policy(const PrefillParams &p, int group, hipStream_t s) {
 
 }  // namespace
 
-int prefill_rows_per_workgroup() { return 32 * kWaves; }
+hipError_t launch_window_prepare(const WindowParams &r, hipStream_t stream) {
+    const int64_t blocks = (int64_t)r.num_seqs * r.num_kv_heads * (r.window_tokens / 64);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(window_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, r);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream) {
     if (kv_type == KV_BF16) return by_policy<KV_BF16>(p, group, stream);
