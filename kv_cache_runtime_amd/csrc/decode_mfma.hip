@@ -610,6 +610,23 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
         uint4 kr[4][NC], vr[4][NC];
         float kscale[4], vscale[4];
         bool kok[4], vok[4];
+        // A cold page's V scale multiplies the probabilities before they
+        // become f16 operands.  The reference max of a tile is taken as its
+        // score max plus lv = max(0, ceil(log2(largest V scale of the tile))):
+        // the lazy rescale then bounds p by 2^(15 - lv), so p * scale <= 2^15
+        // stays finite.  Integer steps on the (wave-uniform) scale bits.
+        auto v_headroom = [&]() -> float {
+            if constexpr (TIER == kHot) {
+                return 0.0f;
+            } else {
+                float vm = 0.0f;
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) vm = vok[tg] ? fmaxf(vm, fabsf(vscale[tg])) : vm;
+                const uint32_t b = __float_as_uint(vm);
+                const int e = (int)(b >> 23) - 127 + ((b & 0x7FFFFFu) != 0u ? 1 : 0);
+                return (float)max(e, 0);
+            }
+        };
 
         // Four query heads per kv head: the score tiles hold them in the first
         // 16 lanes only.  The softmax of a 64-token tile then runs on one packed
@@ -659,6 +676,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
             }
             bool move_any = false;
             float alpha[4];
+            const float lv = v_headroom();
     #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float mx = ps[i];
@@ -672,6 +690,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                 const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx),
                                                                 __float_as_uint(mx), false, false);
                 mx = __builtin_elementwise_maximum(__uint_as_float(q[0]), __uint_as_float(q[1]));
+                mx += lv;
                 const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
                 const float m_new = move ? mx : m_ref[i];
                 alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;
@@ -829,6 +848,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                 // ---- online softmax, one reference max per head (uniform in a row)
                 bool move_any = false;
                 float alpha[4];
+                const float lv = v_headroom();
     #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     // IEEE maximum (v_maximum3_f32): no operand canonicalisation,
@@ -840,6 +860,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams 
                     mx = __builtin_elementwise_maximum(mx, dpp_f<0x124>(mx));
                     mx = __builtin_elementwise_maximum(mx, dpp_f<0x122>(mx));
                     mx = __builtin_elementwise_maximum(mx, dpp_f<0x121>(mx));
+                    mx += lv;
                     const bool move = mx > m_ref[i] + kSlack;  // also true on the first tile
                     const float m_new = move ? mx : m_ref[i];
                     alpha[i] = move ? __builtin_amdgcn_exp2f(m_ref[i] - m_new) : 1.0f;

@@ -185,6 +185,51 @@ def test_tiered_page_walk(gpu, monkeypatch, kernel, P, split, H, Hkv, hot):
     assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
+@pytest.mark.parametrize("H,cold", [(8, "i4"), (16, "i4"), (8, "i8"), (16, "i8")])
+def test_tiered_cold_spike_large_v_scale(gpu, H, cold):
+    """A cold key scoring 7.5 log2 units above every earlier key (just under
+    the lazy-rescale threshold) on a page with a V scale far above 1: p *
+    scale must stay a finite f16 operand.  q is the unit vector of dim 0, so
+    each score is dim 0 of its key; hot keys and all but one cold page score
+    about 0."""
+    w = synth.build(dict(num_seqs=1, context_lens=[4096], num_heads=H, num_kv_heads=2,
+                         head_dim=128, page_tokens=64, q_dtype="bf16", kv_dtype="f16",
+                         placement="permuted",
+                         tiers=dict(hot_tokens=1024, p_int8=1.0 if cold == "i8" else 0.0)),
+                    device=gpu, seed=5, name=f"tiered-spike-{cold}-H{H}")
+    t = w.tiers
+    w.q.zero_()
+    w.q[..., 0] = 1.0
+    w.k_pool[..., 0] = 0.0  # hot scores 0 (poisoned rows keep NaN elsewhere)
+    # dim-0 codes of every cold slot, [n][Hkv][P]
+    raw = t[f"{cold}_k"][..., 0].to(torch.int16)
+    code0 = ((raw & 0xF) ^ 0x8) - 0x8 if cold == "i4" else raw
+    cold_tier = 2 if cold == "i4" else 1
+    ent = w.page_table[0].view(np.uint32)
+    cold_slots = [int(e & ((1 << 30) - 1)) for e in ent if (e >> 30) == cold_tier]
+    assert len(cold_slots) > 4
+    spike = cold_slots[-1]  # the newest cold page
+    c = w.scale * np.log2(np.e)  # score (log2 units) per unit of q.k
+    ks = t[f"{cold}_k_scale"]
+    ks.mul_(1e-3)  # other cold pages score about 0
+    for h in range(2):
+        top = float(code0[spike, h].max())
+        assert top > 0
+        ks[spike, h] = 7.5 / (top * c)
+    vmul = 64.0 if cold == "i4" else 256.0
+    t[f"{cold}_v_scale"].mul_(vmul)
+    out, lse = run(w, split_tokens=8192)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    ref_o, ref_l = oracle.reference(w)
+    vmax = float(t[f"{cold}_v_scale"].max()) * (7 if cold == "i4" else 127)
+    tol_o = 2e-3 * max(1.0, vmax / 4.0)
+    eo = float(np.max(np.abs(out - ref_o)))
+    el = float(np.max(np.abs(lse - ref_l)))
+    print(f"[{w.name}] max|out-ref|={eo:.3e} (tol {tol_o:.3g}, max|v| {vmax:.1f}) "
+          f"max|lse-ref|={el:.3e}", flush=True)
+    assert eo <= tol_o and el <= 2e-3
+
+
 def test_determinism_bitwise(gpu):
     w = synth.config(3, device=gpu, num_seqs=6, context_lens=("uniform", 100, 5000))
     o1, l1 = run(w)
