@@ -323,6 +323,24 @@ atlas_status atlas_paged_attention_regen(const atlas_attn_args *args,
                                          const atlas_regen_spec *regen);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as atlas_paged_attention, with its workspace taken from a
+ * scratch array built into the library instead of args->workspace (which is
+ * ignored).  The array holds ATLAS_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU;
+ * each GPU the library runs on keeps its own copy until the process ends.
+ * A call whose plan needs more (atlas_workspace_size with regen NULL) fails
+ * with ATLAS_EWORKSPACE before any launch.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); its first call on a device
+ * looks up that device's array address.  Every call on one GPU shares the
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  The array's contents need no
+ * initialisation and carry nothing from one call to the next.
+ */
+#define ATLAS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+atlas_status atlas_paged_attention_noalloc(const atlas_attn_args *args);
+
+/*
  * Log-sum-exp merge of split-K partials (attnres AGENTS.md, "online softmax
  * merge"):  lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * o_s.
  *   part_out [splits][rows][head_dim] f32: normalised partial outputs

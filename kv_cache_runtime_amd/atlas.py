@@ -112,7 +112,8 @@ class RegenSpec(ctypes.Structure):
 
 EXPORTS = [
     "atlas_abi_version", "atlas_status_string", "atlas_last_error", "atlas_workspace_size",
-    "atlas_paged_attention", "atlas_paged_attention_tiered", "atlas_paged_attention_regen",
+    "atlas_paged_attention", "atlas_paged_attention_noalloc", "atlas_paged_attention_tiered",
+    "atlas_paged_attention_regen",
     "atlas_fold_partials", "atlas_gather_pages", "atlas_regenerate_pages",
     "atlas_dequant_pages", "atlas_validate_tables", "atlas_read_probe",
     "atlas_write_kv", "atlas_demote_pages", "atlas_promote_pages",
@@ -173,6 +174,8 @@ def load(path: str = LIB_PATH):
                                        ctypes.POINTER(ctypes.c_size_t)]
     L.atlas_paged_attention.restype = _i32
     L.atlas_paged_attention.argtypes = [ctypes.POINTER(AttnArgs)]
+    L.atlas_paged_attention_noalloc.restype = _i32
+    L.atlas_paged_attention_noalloc.argtypes = [ctypes.POINTER(AttnArgs)]
     L.atlas_paged_attention_tiered.restype = _i32
     L.atlas_paged_attention_tiered.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools)]
     L.atlas_paged_attention_regen.restype = _i32
@@ -356,6 +359,13 @@ def atlas_paged_attention(args: AttnArgs):
     _check(load().atlas_paged_attention(ctypes.byref(args)), "atlas_paged_attention")
 
 
+def atlas_paged_attention_noalloc(args: AttnArgs):
+    """atlas_paged_attention with the library's built-in device scratch in
+    place of args.workspace (for callers that cannot allocate)."""
+    _check(load().atlas_paged_attention_noalloc(ctypes.byref(args)),
+           "atlas_paged_attention_noalloc")
+
+
 def atlas_paged_attention_tiered(args: AttnArgs, pools: TierPools):
     _check(load().atlas_paged_attention_tiered(ctypes.byref(args), ctypes.byref(pools)),
            "atlas_paged_attention_tiered")
@@ -508,6 +518,13 @@ class Problem:
 
     def validate(self, check_values: bool = False):
         return atlas_validate_tables(self.args, self.tiers, self.regen, check_values)
+
+    def run_noalloc(self):
+        """The same call through atlas_paged_attention_noalloc (plain pages
+        only): the library's built-in scratch instead of self.workspace."""
+        assert self.kind == "plain"
+        atlas_paged_attention_noalloc(self.args)
+        return self.out, self.lse
 
     def run(self):
         if self.kind == "tiered":

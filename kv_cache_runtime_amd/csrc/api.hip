@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "atlas.h"
@@ -18,9 +19,18 @@
 
 using namespace atlas;
 
+// Device scratch of atlas_paged_attention_noalloc: a file-scope device array,
+// one copy per GPU.  Host code never uses the name as an address; it keeps
+// the address hipGetSymbolAddress reports for each device.
+static __device__ __align__(256) char scratch[ATLAS_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // per device, set on its first call
 
 atlas_status fail(atlas_status st, const char *fmt, ...) {
     char buf[512];
@@ -506,6 +516,38 @@ atlas_status atlas_paged_attention(const atlas_attn_args *args) {
     if (plan.mfma) return run_prefill(args, plan, nullptr);
     DecodeParams p = decode_params(args, plan);
     return run_decode(args, plan, p, MODE_PLAIN);
+}
+
+atlas_status atlas_paged_attention_noalloc(const atlas_attn_args *args) {
+    Plan plan;
+    atlas_status st = check_common(args, false, nullptr, &plan);
+    if (st != ATLAS_OK) return st;
+    if (plan.total > ATLAS_NOALLOC_SCRATCH_BYTES)
+        return fail(ATLAS_EWORKSPACE,
+                    "the call needs %zu workspace bytes, the built-in scratch holds %zu",
+                    plan.total, (size_t)ATLAS_NOALLOC_SCRATCH_BYTES);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATLAS_EUNSUPPORTED, "device %d", dev);
+    void *ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        if (!g_scratch_ptr[dev]) {  // first call on this device, with it current
+            e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+            if (e != hipSuccess) {
+                g_scratch_ptr[dev] = nullptr;
+                return device_status(e, "scratch address lookup");
+            }
+        }
+        ptr = g_scratch_ptr[dev];
+    }
+    atlas_attn_args a = *args;
+    a.workspace = ptr;
+    a.workspace_bytes = ATLAS_NOALLOC_SCRATCH_BYTES;
+    if (plan.mfma) return run_prefill(&a, plan, nullptr);
+    DecodeParams p = decode_params(&a, plan);
+    return run_decode(&a, plan, p, MODE_PLAIN);
 }
 
 atlas_status atlas_paged_attention_tiered(const atlas_attn_args *args,

@@ -319,3 +319,15 @@ def test_positional_policy_arguments_are_checked():
     a.rope_theta = 10000.0
     a.alibi_slopes = FAKE
     assert _ws(a)[0] == atlas.OK
+
+
+def test_noalloc_rejects_a_plan_beyond_its_scratch():
+    """The no-allocation entry point refuses, before any device call, a call
+    whose workspace would exceed the built-in scratch (64 MiB)."""
+    a = _args(num_seqs=64, total_q=64, max_context_len=32768, max_pages_per_seq=2048,
+              num_blocks=65536, split_tokens=64)
+    st, need = _ws(a)
+    assert st == atlas.OK and need > (64 << 20)
+    st = atlas.load().atlas_paged_attention_noalloc(ctypes.byref(a))
+    assert st == atlas.EWORKSPACE
+    assert b"scratch" in atlas.load().atlas_last_error()
