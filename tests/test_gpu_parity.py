@@ -185,7 +185,8 @@ def test_tiered_page_walk(gpu, monkeypatch, kernel, P, split, H, Hkv, hot):
     assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
-@pytest.mark.parametrize("H,cold", [(8, "i4"), (16, "i4"), (8, "i8"), (16, "i8")])
+@pytest.mark.parametrize("H,cold", [(8, "i4"), (16, "i4"), (8, "i8"), (16, "i8"), (8, "i2"),
+                                    (16, "i2")])
 def test_tiered_cold_spike_large_v_scale(gpu, H, cold):
     """A cold key scoring 7.5 log2 units above every earlier key (just under
     the lazy-rescale threshold) on a page with a V scale far above 1: p *
@@ -195,7 +196,8 @@ def test_tiered_cold_spike_large_v_scale(gpu, H, cold):
     w = synth.build(dict(num_seqs=1, context_lens=[4096], num_heads=H, num_kv_heads=2,
                          head_dim=128, page_tokens=64, q_dtype="bf16", kv_dtype="f16",
                          placement="permuted",
-                         tiers=dict(hot_tokens=1024, p_int8=1.0 if cold == "i8" else 0.0)),
+                         tiers=dict(hot_tokens=1024, p_int8=1.0 if cold == "i8" else 0.0,
+                                    p_int2=1.0 if cold == "i2" else 0.0)),
                     device=gpu, seed=5, name=f"tiered-spike-{cold}-H{H}")
     t = w.tiers
     w.q.zero_()
@@ -203,10 +205,19 @@ def test_tiered_cold_spike_large_v_scale(gpu, H, cold):
     w.k_pool[..., 0] = 0.0  # hot scores 0 (poisoned rows keep NaN elsewhere)
     # dim-0 codes of every cold slot, [n][Hkv][P]
     raw = t[f"{cold}_k"][..., 0].to(torch.int16)
-    code0 = ((raw & 0xF) ^ 0x8) - 0x8 if cold == "i4" else raw
-    cold_tier = 2 if cold == "i4" else 1
+    if cold == "i4":
+        code0 = ((raw & 0xF) ^ 0x8) - 0x8
+    elif cold == "i2":
+        code0 = ((raw & 0x3) ^ 0x2) - 0x2
+    else:
+        code0 = raw
     ent = w.page_table[0].view(np.uint32)
-    cold_slots = [int(e & ((1 << 30) - 1)) for e in ent if (e >> 30) == cold_tier]
+    if cold == "i2":  # extension tier 3, kind 1, 28-bit slot
+        cold_slots = [int(e & ((1 << 28) - 1)) for e in ent
+                      if (e >> 30) == 3 and ((e >> 28) & 3) == 1]
+    else:
+        tier = 2 if cold == "i4" else 1
+        cold_slots = [int(e & ((1 << 30) - 1)) for e in ent if (e >> 30) == tier]
     assert len(cold_slots) > 4
     spike = cold_slots[-1]  # the newest cold page
     c = w.scale * np.log2(np.e)  # score (log2 units) per unit of q.k
@@ -216,12 +227,13 @@ def test_tiered_cold_spike_large_v_scale(gpu, H, cold):
         top = float(code0[spike, h].max())
         assert top > 0
         ks[spike, h] = 7.5 / (top * c)
-    vmul = 64.0 if cold == "i4" else 256.0
+    vmul = {"i4": 64.0, "i8": 256.0, "i2": 8.0}[cold]
+    qmax = {"i4": 7, "i8": 127, "i2": 1}[cold]
     t[f"{cold}_v_scale"].mul_(vmul)
     out, lse = run(w, split_tokens=8192)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     ref_o, ref_l = oracle.reference(w)
-    vmax = float(t[f"{cold}_v_scale"].max()) * (7 if cold == "i4" else 127)
+    vmax = float(t[f"{cold}_v_scale"].max()) * qmax
     tol_o = 2e-3 * max(1.0, vmax / 4.0)
     eo = float(np.max(np.abs(out - ref_o)))
     el = float(np.max(np.abs(lse - ref_l)))
