@@ -65,9 +65,9 @@ struct Plan {
     int q_blocks = 0;        // query tiles per sequence (matrix-core prefill)
     size_t part_o_bytes = 0;
     size_t part_lse_bytes = 0;
-    int window_tokens = 0;   // matrix-core prefill with regeneration: keys per window
+    int window_tokens = 0;   // matrix-core prefill: keys per window
     int windows = 1;
-    size_t ring_bytes = 0;   // K (and V) ring of one window's regenerated keys
+    size_t ring_bytes = 0;   // the K ring (and the V ring) of one window's keys
     size_t total = 0;
 };
 
