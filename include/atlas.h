@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATLAS_ABI_VERSION 3u
+#define ATLAS_ABI_VERSION 4u
 
 typedef int32_t atlas_status;
 #define ATLAS_OK 0           /* success (work enqueued) */
@@ -372,7 +372,14 @@ atlas_status atlas_gather_pages(const atlas_attn_args *args, int32_t seq,
  * embedding the values are bf16-exact either way).  Both index arrays are device int32.  With
  * rope_theta > 0 the K rows are stored rotated by their token position (see
  * the positional policy of atlas_attn_args), rounded to kv_dtype, so that
- * resident pages hold what the regenerating kernels compute. */
+ * resident pages hold what the regenerating kernels compute.
+ * nonfinite (device int32 [n], optional; CFR-Atlas README, hardening
+ * baseline: finite-value validation before hot-cache admission): after the
+ * call, nonfinite[i] is the number of non-finite K and V values stored in
+ * block dst_blocks[i], or -1 if that block id is outside [0, num_blocks)
+ * (nothing written); atlas_residency_refuse_admissions takes the flagged
+ * pages back.  Needs page_tokens * head_dim * element bytes to be a
+ * multiple of 16. */
 atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer,
                                     int32_t num_kv_heads, int32_t head_dim,
                                     int32_t page_tokens, int32_t kv_dtype,
@@ -380,7 +387,8 @@ atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer,
                                     const int32_t *logical_pages,
                                     const int32_t *dst_blocks, int32_t n,
                                     int32_t num_blocks, void *k_pool,
-                                    void *v_pool, void *stream);
+                                    void *v_pool, void *stream,
+                                    int32_t *nonfinite);
 
 /* Decode tier-tagged pages entries[i] (i < n, device int32, (tier << 30) |
  * slot) to f32 K/V [n][num_kv_heads][page_tokens][head_dim]: hot pages are
@@ -476,14 +484,18 @@ atlas_status atlas_demote_pages(const atlas_attn_args *args,
  * A destination block outside [0, num_blocks) rejects the page (nothing
  * written); a source outside its pool, or of kind 3, fills the destination
  * block with NaN.  Each such page adds 1 to *rejected (device int32,
- * optional).  Sources and destinations must not overlap within a call or
- * with calls in flight.  Asynchronous on args->stream; allocates nothing.
+ * optional).  nonfinite (device int32 [n], optional): after the call,
+ * nonfinite[i] counts the non-finite K and V values now in block
+ * dst_blocks[i] (-1 for a rejected destination), so a caller can see which
+ * rebuilt pages would turn rows NaN.  Sources and destinations must not
+ * overlap within a call or with calls in flight.  Asynchronous on
+ * args->stream; allocates nothing.
  */
 atlas_status atlas_promote_pages(const atlas_attn_args *args,
                                  const atlas_tier_pools *pools,
                                  const int32_t *src_entries,
                                  const int32_t *dst_blocks, int32_t n,
-                                 int32_t *rejected);
+                                 int32_t *rejected, int32_t *nonfinite);
 
 /*
  * Measurement helper (not part of the attention method): reads `bytes`

@@ -31,7 +31,9 @@
  *      jobs); atlas_write_kv the new tokens;
  *   3. the attention call;
  *   4. atlas_residency_plan -> demotions (tiered) or admissions (regen);
- *      run them (atlas_demote_pages, atlas_regenerate_pages).
+ *      run them (atlas_demote_pages, atlas_regenerate_pages with its
+ *      non-finite counts), then hand the counts to
+ *      atlas_residency_refuse_admissions.
  */
 #ifndef ATLAS_RESIDENCY_H
 #define ATLAS_RESIDENCY_H
@@ -79,6 +81,11 @@ typedef struct atlas_residency_config {
     int32_t transient_blocks;  /* tiered: hot blocks hot_blocks .. hot_blocks +
                                   transient_blocks - 1, reserved for archived pages rebuilt
                                   for one attention call (atlas_residency_tables_transient) */
+    struct atlas_residency_budget *budget; /* optional shared (global) budget: hot blocks
+                                  that all runtimes naming it may hold together, or NULL.
+                                  A runtime serves one layer, so hot_blocks is that
+                                  layer's budget (CFR-Atlas README, test list: global and
+                                  per-layer budgets) */
 } atlas_residency_config;
 
 typedef struct atlas_residency_stats {
@@ -98,6 +105,8 @@ typedef struct atlas_residency_stats {
     int64_t capacity_failures; /* calls refused with ATLAS_ECAPACITY */
     int64_t archive_used;      /* 1-bit archive slots in use */
     int64_t reconstructions;   /* promotion jobs handed out by tables_transient */
+    int64_t refused_admissions; /* admitted pages taken back by
+                                   atlas_residency_refuse_admissions */
 } atlas_residency_stats;
 
 /* Job lists filled by atlas_residency_plan.  The caller provides the arrays
@@ -118,6 +127,17 @@ typedef struct atlas_residency_jobs {
 } atlas_residency_jobs;
 
 typedef struct atlas_residency atlas_residency; /* opaque */
+typedef struct atlas_residency_budget atlas_residency_budget; /* opaque */
+
+/* A shared budget of `blocks` hot blocks (host memory only).  Runtimes that
+ * name it in their config take a hot block only while it has room; blocks
+ * return to it when freed or when their runtime is destroyed.  Destroy the
+ * runtimes before their budget.  Runtimes sharing a budget are used from one
+ * host thread at a time. */
+atlas_status atlas_residency_budget_create(int64_t blocks, atlas_residency_budget **out);
+atlas_status atlas_residency_budget_destroy(atlas_residency_budget *budget);
+/* Hot blocks currently held by the runtimes that share the budget. */
+atlas_status atlas_residency_budget_used(const atlas_residency_budget *budget, int64_t *used);
 
 /* Creates a runtime (host memory only).  Checks every field; *out is set on
  * success only. */
@@ -186,6 +206,20 @@ atlas_status atlas_residency_tables_transient(atlas_residency *rt, const int32_t
                                               int32_t n, int32_t *page_table,
                                               int32_t *context_lens, int32_t *regen_pages,
                                               atlas_residency_jobs *jobs);
+
+/* Finite-value validation before admission (CFR-Atlas README, hardening
+ * baseline).  Regen mode, right after the admission jobs of the last
+ * atlas_residency_plan ran through atlas_regenerate_pages with its
+ * `nonfinite` output copied back to the host: every job j with
+ * nonfinite[j] != 0 (non-finite values stored, or -1: the job was rejected)
+ * is taken back -- its page is regenerated again and its block freed -- and
+ * so are the pages the same plan admitted below it in that sequence (the
+ * resident pages stay a suffix).  Call it before the next tables call.
+ * Fails with ATLAS_EINVAL, changing nothing, when a job is not a current
+ * admission. */
+atlas_status atlas_residency_refuse_admissions(atlas_residency *rt,
+                                               const atlas_residency_jobs *jobs,
+                                               const int32_t *nonfinite);
 
 /* Current counters. */
 atlas_status atlas_residency_get_stats(const atlas_residency *rt, atlas_residency_stats *out);

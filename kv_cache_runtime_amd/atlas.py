@@ -120,6 +120,8 @@ EXPORTS = [
     "atlas_residency_create", "atlas_residency_destroy", "atlas_residency_add_seq",
     "atlas_residency_remove_seq", "atlas_residency_append", "atlas_residency_plan",
     "atlas_residency_tables", "atlas_residency_tables_transient", "atlas_residency_get_stats",
+    "atlas_residency_budget_create", "atlas_residency_budget_destroy",
+    "atlas_residency_budget_used", "atlas_residency_refuse_admissions",
 ]
 
 _lib = None
@@ -130,7 +132,7 @@ class ResidencyConfig(ctypes.Structure):
         "struct_size", "mode", "page_tokens", "max_seqs", "max_pages_per_seq", "hot_blocks",
         "recent_tokens", "sink_tokens", "admit_per_plan", "fp8_pages", "int8_pages",
         "num_fp8", "num_int8", "num_int4", "int4_pages", "num_int2", "int2_pages", "num_1bit",
-        "transient_blocks")]
+        "transient_blocks")] + [("budget", ctypes.c_void_p)]
 
 
 class ResidencyStats(ctypes.Structure):
@@ -138,7 +140,7 @@ class ResidencyStats(ctypes.Structure):
         "sequences", "hot_used", "fp8_used", "int8_used", "int4_used", "int2_used",
         "regenerated_pages")] + [(n, ctypes.c_int64) for n in (
         "appended_tokens", "demotions", "transcodes", "admissions", "evictions",
-        "capacity_failures", "archive_used", "reconstructions")]
+        "capacity_failures", "archive_used", "reconstructions", "refused_admissions")]
 
 
 class ResidencyJobs(ctypes.Structure):
@@ -186,7 +188,7 @@ def load(path: str = LIB_PATH):
     L.atlas_gather_pages.argtypes = [ctypes.POINTER(AttnArgs), _i32, _i32, _p, _p]
     L.atlas_regenerate_pages.restype = _i32
     L.atlas_regenerate_pages.argtypes = [ctypes.c_uint64, ctypes.c_uint32, _i32, _i32, _i32, _i32,
-                                         ctypes.c_float, _p, _p, _i32, _i32, _p, _p, _p]
+                                         ctypes.c_float, _p, _p, _i32, _i32, _p, _p, _p, _p]
     L.atlas_dequant_pages.restype = _i32
     L.atlas_dequant_pages.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools), _p,
                                       _i32, _p, _p]
@@ -200,7 +202,7 @@ def load(path: str = LIB_PATH):
                                      _i32, _p]
     L.atlas_promote_pages.restype = _i32
     L.atlas_promote_pages.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(TierPools), _p, _p,
-                                      _i32, _p]
+                                      _i32, _p, _p]
     L.atlas_read_probe.restype = _i32
     L.atlas_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, _p]
     L.atlas_residency_create.restype = _i32
@@ -219,9 +221,17 @@ def load(path: str = LIB_PATH):
     L.atlas_residency_tables_transient.restype = _i32
     L.atlas_residency_tables_transient.argtypes = [_p, _p, _i32, _p, _p, _p,
                                                    ctypes.POINTER(ResidencyJobs)]
+    L.atlas_residency_budget_create.restype = _i32
+    L.atlas_residency_budget_create.argtypes = [ctypes.c_int64, ctypes.POINTER(_p)]
+    L.atlas_residency_budget_destroy.restype = _i32
+    L.atlas_residency_budget_destroy.argtypes = [_p]
+    L.atlas_residency_budget_used.restype = _i32
+    L.atlas_residency_budget_used.argtypes = [_p, ctypes.POINTER(ctypes.c_int64)]
+    L.atlas_residency_refuse_admissions.restype = _i32
+    L.atlas_residency_refuse_admissions.argtypes = [_p, ctypes.POINTER(ResidencyJobs), _p]
     L.atlas_residency_get_stats.restype = _i32
     L.atlas_residency_get_stats.argtypes = [_p, ctypes.POINTER(ResidencyStats)]
-    if L.atlas_abi_version() != 3:
+    if L.atlas_abi_version() != 4:
         raise RuntimeError("libatlas ABI version mismatch")
     _lib = L
     return L
@@ -391,13 +401,16 @@ def atlas_gather_pages(args: AttnArgs, seq: int, num_tokens: int, k_out, v_out):
 
 def atlas_regenerate_pages(seed, layer, num_kv_heads, head_dim, page_tokens, kv_dtype,
                            logical_pages, dst_blocks, num_blocks, k_pool, v_pool, stream=None,
-                           rope_theta: float = 0.0):
+                           rope_theta: float = 0.0, nonfinite=None):
+    """nonfinite: optional device int32 tensor [n], the non-finite values
+    stored per page (-1: rejected block id)."""
     n = int(logical_pages.numel())
     _check(load().atlas_regenerate_pages(int(seed) & (2**64 - 1), int(layer), int(num_kv_heads),
                                          int(head_dim), int(page_tokens), int(kv_dtype),
                                          float(rope_theta), _ptr(logical_pages), _ptr(dst_blocks), n,
                                          int(num_blocks), _ptr(k_pool), _ptr(v_pool),
-                                         _stream(stream)), "atlas_regenerate_pages")
+                                         _stream(stream), _ptr(nonfinite)),
+           "atlas_regenerate_pages")
 
 
 def atlas_dequant_pages(args: AttnArgs, pools: TierPools, entries, k_out, v_out):
@@ -435,10 +448,11 @@ def atlas_demote_pages(args: AttnArgs, pools: TierPools, src_slots, dst_entries,
 
 
 def atlas_promote_pages(args: AttnArgs, pools: TierPools, src_entries, dst_blocks,
-                        rejected=None):
+                        rejected=None, nonfinite=None):
     """Reconstruct the pages of src_entries[i] into hot blocks dst_blocks[i]."""
     _check(load().atlas_promote_pages(ctypes.byref(args), ctypes.byref(pools), _ptr(src_entries),
-                                      _ptr(dst_blocks), int(src_entries.numel()), _ptr(rejected)),
+                                      _ptr(dst_blocks), int(src_entries.numel()), _ptr(rejected),
+                                      _ptr(nonfinite)),
            "atlas_promote_pages")
 
 

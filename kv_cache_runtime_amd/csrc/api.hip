@@ -633,7 +633,7 @@ atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer, int32_t num_k
                                     int32_t head_dim, int32_t page_tokens, int32_t kv_dtype,
                                     float rope_theta, const int32_t *logical_pages, const int32_t *dst_blocks,
                                     int32_t n, int32_t num_blocks, void *k_pool, void *v_pool,
-                                    void *stream) {
+                                    void *stream, int32_t *nonfinite) {
     if (layer >= (1u << 16)) return fail(ATLAS_EINVAL, "layer %u >= 2^16", layer);
     if (num_kv_heads < 1 || num_kv_heads > 256)
         return fail(ATLAS_EINVAL, "num_kv_heads %d outside [1, 256]", num_kv_heads);
@@ -662,8 +662,17 @@ atlas_status atlas_regenerate_pages(uint64_t seed, uint32_t layer, int32_t num_k
     r.kv_f32 = kv_dtype == ATLAS_F32;
     r.k_dst = k_pool;
     r.v_dst = v_pool;
-    return device_status(launch_regen_fill(r, reinterpret_cast<hipStream_t>(stream)),
-                         "regenerate launch");
+    const int eb = kv_dtype == ATLAS_F32 ? 4 : 2;
+    if (nonfinite && ((int64_t)page_tokens * head_dim * eb) % 16)
+        return fail(ATLAS_EINVAL, "nonfinite counts need page_tokens * head_dim * %d "
+                                  "to be a multiple of 16 bytes", eb);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch_regen_fill(r, st);
+    if (e != hipSuccess) return device_status(e, "regenerate launch");
+    if (nonfinite)
+        e = launch_count_nonfinite(k_pool, v_pool, dst_blocks, n, num_blocks, num_kv_heads,
+                                   page_tokens, head_dim, eb, 0, nonfinite, st);
+    return device_status(e, "finite check launch");
 }
 
 atlas_status atlas_dequant_pages(const atlas_attn_args *args, const atlas_tier_pools *pools,
@@ -848,7 +857,7 @@ atlas_status atlas_demote_pages(const atlas_attn_args *args, const atlas_tier_po
 
 atlas_status atlas_promote_pages(const atlas_attn_args *args, const atlas_tier_pools *pools,
                                  const int32_t *src_entries, const int32_t *dst_blocks, int32_t n,
-                                 int32_t *rejected) {
+                                 int32_t *rejected, int32_t *nonfinite) {
     Plan plan;
     atlas_status st = check_common(args, true, nullptr, &plan);
     if (st != ATLAS_OK) return st;
@@ -877,8 +886,16 @@ atlas_status atlas_promote_pages(const atlas_attn_args *args, const atlas_tier_p
     q.dst_blocks = dst_blocks;
     q.n = n;
     q.rejected = rejected;
-    return device_status(launch_promote(q, reinterpret_cast<hipStream_t>(args->stream)),
-                         "promote launch");
+    hipStream_t stream = reinterpret_cast<hipStream_t>(args->stream);
+    hipError_t e = launch_promote(q, stream);
+    if (e != hipSuccess) return device_status(e, "promote launch");
+    if (nonfinite) {
+        const int eb = args->kv_dtype == ATLAS_F32 ? 4 : 2;
+        e = launch_count_nonfinite(args->k_pool, args->v_pool, dst_blocks, n, args->num_blocks,
+                                   args->num_kv_heads, args->page_tokens, args->head_dim, eb,
+                                   args->kv_dtype == ATLAS_F16 ? 1 : 0, nonfinite, stream);
+    }
+    return device_status(e, "finite check launch");
 }
 
 }  // extern "C"

@@ -77,6 +77,47 @@ __global__ __launch_bounds__(256) void regen_fill_kernel(const RegenFillParams r
     }
 }
 
+// Finite-value check of written pages: zero the counts, then one workgroup
+// per (job, kv head) counts the non-finite elements of K and V (an exponent
+// field of all ones) with 16-byte loads and adds them to its job's count.
+__global__ __launch_bounds__(256) void zero_counts_kernel(int32_t *out, int32_t n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void count_nonfinite_kernel(
+    const uint4 *k_pool, const uint4 *v_pool, const int32_t *dst_blocks, int32_t n,
+    int32_t num_blocks, int32_t num_kv_heads, int64_t chunks, int32_t elem_bytes,
+    int32_t f16_bits, int32_t *out) {
+    const int i = blockIdx.x / num_kv_heads;
+    const int g = blockIdx.x % num_kv_heads;
+    if (i >= n) return;
+    const int32_t blk = dst_blocks[i];
+    if (blk < 0 || blk >= num_blocks) {
+        if (g == 0 && threadIdx.x == 0) out[i] = -1;
+        return;
+    }
+    const int64_t base = ((int64_t)blk * num_kv_heads + g) * chunks;  // 16-byte chunks
+    int cnt = 0;
+    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
+        const uint4 a = k_pool[base + c], b = v_pool[base + c];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (elem_bytes == 4) {
+                cnt += (w[j] & 0x7F800000u) == 0x7F800000u;
+            } else if (f16_bits) {
+                cnt += (w[j] & 0x7C00u) == 0x7C00u;
+                cnt += (w[j] & 0x7C000000u) == 0x7C000000u;
+            } else {
+                cnt += (w[j] & 0x7F80u) == 0x7F80u;
+                cnt += (w[j] & 0x7F800000u) == 0x7F800000u;
+            }
+        }
+    }
+    if (cnt) atomicAdd(&out[i], cnt);
+}
+
 // One workgroup per (entry, kv head): f32 values of every element of the page.
 __global__ __launch_bounds__(256) void dequant_kernel(const DecodeParams p, int kv_type, int D,
                                                       const int32_t *entries, int32_t n,
@@ -306,6 +347,24 @@ hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream) {
     return hipGetLastError();
 }
 
+
+hipError_t launch_count_nonfinite(const void *k_pool, const void *v_pool,
+                                  const int32_t *dst_blocks, int32_t n, int32_t num_blocks,
+                                  int32_t num_kv_heads, int32_t page_tokens, int32_t head_dim,
+                                  int32_t elem_bytes, int32_t f16_bits, int32_t *out,
+                                  hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, out, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t chunks = (int64_t)page_tokens * head_dim * elem_bytes / 16;
+    hipLaunchKernelGGL(count_nonfinite_kernel, dim3((unsigned)((int64_t)n * num_kv_heads)),
+                       dim3(256), 0, stream, reinterpret_cast<const uint4 *>(k_pool),
+                       reinterpret_cast<const uint4 *>(v_pool), dst_blocks, n, num_blocks,
+                       num_kv_heads, chunks, elem_bytes, f16_bits, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,
                           const int32_t *entries, int32_t n, float *k_out, float *v_out,

@@ -240,6 +240,15 @@ constexpr int kPrefillRows = 256;
 constexpr int kPrefillWindow = 16384;
 hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream);
 hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream);
+// Per job i: the non-finite K and V values now stored in block dst_blocks[i]
+// of the pools ([*][num_kv_heads][page_tokens][head_dim], elem_bytes 2 or 4;
+// f16_bits: 2-byte elements are f16, else bf16), or -1 when the block id is
+// outside [0, num_blocks).  Writes out[0 .. n-1].
+hipError_t launch_count_nonfinite(const void *k_pool, const void *v_pool,
+                                  const int32_t *dst_blocks, int32_t n, int32_t num_blocks,
+                                  int32_t num_kv_heads, int32_t page_tokens, int32_t head_dim,
+                                  int32_t elem_bytes, int32_t f16_bits, int32_t *out,
+                                  hipStream_t stream);
 hipError_t launch_window_prepare(const WindowParams &r, hipStream_t stream);
 hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
                          int32_t num_kv_heads, int32_t head_dim, int32_t page_tokens,

@@ -18,6 +18,19 @@
 // and window pages hot; counting back from the window, FP8, then INT8, then
 // INT4, INT2 and the 1-bit archive) and moves each page that is hotter than
 // its target in one job.
+//
+// Budgets (CFR-Atlas README, test list: global and per-layer budgets).  A
+// runtime serves one layer: hot_blocks is that layer's budget.  Runtimes
+// may also share an atlas_residency_budget, a count of hot blocks that all
+// of them together may hold (the global budget); a hot block is taken only
+// when both the layer's pool and the shared budget have room.
+//
+// Admission check (CFR-Atlas README, hardening baseline: finite-value
+// validation before hot-cache admission).  atlas_regenerate_pages reports
+// the non-finite values it stored per job; the caller hands the counts to
+// atlas_residency_refuse_admissions, which takes back every flagged page
+// (and the pages admitted below it in the same plan, so the resident run
+// stays a suffix) before its block can be named by a page table.
 #include <algorithm>
 #include <cstdarg>
 #include <cstdint>
@@ -82,24 +95,45 @@ int32_t slot_of(uint32_t e) {
     return (int32_t)(e & ((e >> kShift) == 3u ? (1u << ATLAS_EXT_KIND_SHIFT) - 1u : kSlotMask));
 }
 
+}  // namespace
+
+// Hot blocks that several runtimes (layers) may hold together.
+struct atlas_residency_budget {
+    int64_t limit = 0;
+    int64_t used = 0;
+};
+
+namespace {
+
 // A pool of numbered slots; freed slots are reused lowest-first so the
-// allocation order is deterministic.
+// allocation order is deterministic.  The hot pool may also draw on a
+// shared budget: a slot is available only while the budget has room.
 struct SlotPool {
     std::vector<int32_t> free_;  // kept sorted descending: back() is the lowest
     int32_t capacity = 0;
-    void init(int32_t n) {
+    atlas_residency_budget *budget = nullptr;
+    void init(int32_t n, atlas_residency_budget *b = nullptr) {
         capacity = n;
+        budget = b;
         free_.clear();
         for (int32_t i = n - 1; i >= 0; --i) free_.push_back(i);
     }
-    bool empty() const { return free_.empty(); }
+    // slots that can be taken now
+    int64_t available() const {
+        int64_t a = (int64_t)free_.size();
+        if (budget) a = std::min<int64_t>(a, std::max<int64_t>(0, budget->limit - budget->used));
+        return a;
+    }
+    bool empty() const { return available() == 0; }
     int32_t take() {
         const int32_t s = free_.back();
         free_.pop_back();
+        if (budget) ++budget->used;
         return s;
     }
     void give(int32_t s) {
         free_.insert(std::upper_bound(free_.begin(), free_.end(), s, std::greater<int32_t>()), s);
+        if (budget) --budget->used;
     }
     int32_t used() const { return capacity - (int32_t)free_.size(); }
 };
@@ -295,7 +329,7 @@ atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_resid
     if (!rt) return fail(ATLAS_EINVAL, "out of host memory");
     rt->cfg = *c;
     rt->seqs.resize(c->max_seqs);
-    rt->hot.init(c->hot_blocks);
+    rt->hot.init(c->hot_blocks, c->budget);
     rt->f8.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_fp8 : 0);
     rt->i8.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int8 : 0);
     rt->i4.init(c->mode == ATLAS_RESIDENCY_TIERED ? c->num_int4 : 0);
@@ -308,7 +342,78 @@ atlas_status atlas_residency_create(const atlas_residency_config *c, atlas_resid
 }
 
 atlas_status atlas_residency_destroy(atlas_residency *rt) {
+    if (rt && rt->hot.budget) rt->hot.budget->used -= rt->hot.used();  // its blocks go back
     delete rt;
+    return atlas::report_ok();
+}
+
+atlas_status atlas_residency_budget_create(int64_t blocks, atlas_residency_budget **out) {
+    if (!out) return fail(ATLAS_EINVAL, "out is NULL");
+    if (blocks < 0) return fail(ATLAS_EINVAL, "blocks %lld < 0", (long long)blocks);
+    atlas_residency_budget *b = new (std::nothrow) atlas_residency_budget();
+    if (!b) return fail(ATLAS_EINVAL, "out of host memory");
+    b->limit = blocks;
+    *out = b;
+    return atlas::report_ok();
+}
+
+atlas_status atlas_residency_budget_destroy(atlas_residency_budget *b) {
+    delete b;
+    return atlas::report_ok();
+}
+
+atlas_status atlas_residency_budget_used(const atlas_residency_budget *b, int64_t *used) {
+    if (!b || !used) return fail(ATLAS_EINVAL, "budget or used is NULL");
+    *used = b->used;
+    return atlas::report_ok();
+}
+
+atlas_status atlas_residency_refuse_admissions(atlas_residency *rt,
+                                               const atlas_residency_jobs *jobs,
+                                               const int32_t *nonfinite) {
+    if (!rt || !jobs) return fail(ATLAS_EINVAL, "runtime or jobs is NULL");
+    if (jobs->struct_size != sizeof(atlas_residency_jobs))
+        return fail(ATLAS_EINVAL, "jobs->struct_size %u != %zu", jobs->struct_size,
+                    sizeof(atlas_residency_jobs));
+    if (rt->cfg.mode != ATLAS_RESIDENCY_REGEN)
+        return fail(ATLAS_EINVAL, "admissions exist in regen mode only");
+    const int32_t n = jobs->n_admit;
+    if (n < 0 || n > jobs->capacity) return fail(ATLAS_EINVAL, "n_admit %d out of range", n);
+    if (n == 0) return atlas::report_ok();
+    if (!nonfinite || !jobs->admit_page || !jobs->admit_block)
+        return fail(ATLAS_EINVAL, "NULL admission arrays or counts");
+    // the owner of every job: the sequence whose page admit_page names the
+    // job's block inside its resident suffix (checked before any change)
+    std::vector<int> owner(n, -1);
+    for (int32_t j = 0; j < n; ++j) {
+        const int32_t pg = jobs->admit_page[j], blk = jobs->admit_block[j];
+        for (int i = 0; i < (int)rt->seqs.size() && owner[j] < 0; ++i) {
+            const Seq &s = rt->seqs[i];
+            if (s.active && pg >= s.first_resident && pg < (int32_t)s.pages.size() &&
+                s.pages[pg] == (uint32_t)blk)
+                owner[j] = i;
+        }
+        if (owner[j] < 0)
+            return fail(ATLAS_EINVAL, "job %d (page %d, block %d) is not a current admission", j,
+                        pg, blk);
+    }
+    // per sequence, the highest flagged page; every page of this plan at or
+    // below it goes back to regeneration
+    std::vector<int32_t> cut(rt->seqs.size(), -1);
+    for (int32_t j = 0; j < n; ++j)
+        if (nonfinite[j] != 0) cut[owner[j]] = std::max(cut[owner[j]], jobs->admit_page[j]);
+    for (int32_t j = 0; j < n; ++j) {
+        Seq &s = rt->seqs[owner[j]];
+        const int32_t pg = jobs->admit_page[j];
+        if (pg > cut[owner[j]]) continue;
+        rt->hot.give(jobs->admit_block[j]);
+        s.pages[pg] = 0u;
+        ++rt->st.refused_admissions;
+        --rt->st.admissions;
+    }
+    for (int i = 0; i < (int)rt->seqs.size(); ++i)
+        if (cut[i] >= 0) rt->seqs[i].first_resident = std::max(rt->seqs[i].first_resident,
+                                                               cut[i] + 1);
     return atlas::report_ok();
 }
 
@@ -357,7 +462,7 @@ atlas_status atlas_residency_append(atlas_residency *rt, int32_t seq, int32_t n_
         skip = std::max(0, std::min(wf, (int32_t)pages) - old_pages);
     const int32_t need = (int32_t)pages - old_pages - skip;
     // capacity check before any change (transactional)
-    int64_t room = (int64_t)rt->hot.free_.size();
+    int64_t room = rt->hot.available();
     if (regen && room < need) {
         for (const Seq &o : rt->seqs) {
             if (!o.active) continue;

@@ -20,13 +20,38 @@ def _arr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+class Budget:
+    """A shared hot-block budget (the global budget of several layers'
+    runtimes)."""
+
+    def __init__(self, blocks: int):
+        self._L = atlas.load()
+        self._h = ctypes.c_void_p()
+        atlas._check(self._L.atlas_residency_budget_create(int(blocks), ctypes.byref(self._h)),
+                     "atlas_residency_budget_create")
+
+    @property
+    def used(self) -> int:
+        v = ctypes.c_int64(0)
+        atlas._check(self._L.atlas_residency_budget_used(self._h, ctypes.byref(v)),
+                     "atlas_residency_budget_used")
+        return v.value
+
+    def close(self):
+        if self._h:
+            self._L.atlas_residency_budget_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+
 class Residency:
-    """One runtime handle.  Fields of the config as keyword arguments."""
+    """One runtime handle (one layer).  Fields of the config as keyword
+    arguments; budget: an optional shared Budget."""
 
     def __init__(self, *, mode, page_tokens, max_seqs, max_pages_per_seq, hot_blocks,
                  recent_tokens=0, sink_tokens=0, admit_per_plan=0, fp8_pages=0, int8_pages=0,
                  num_fp8=0, num_int8=0, num_int4=0, int4_pages=0, num_int2=0,
-                 int2_pages=0, num_1bit=0, transient_blocks=0, job_capacity=1 << 16):
+                 int2_pages=0, num_1bit=0, transient_blocks=0, job_capacity=1 << 16,
+                 budget: Budget | None = None):
         L = atlas.load()
         c = atlas.ResidencyConfig()
         c.struct_size = ctypes.sizeof(c)
@@ -39,6 +64,8 @@ class Residency:
                          int2_pages=int2_pages, num_1bit=num_1bit,
                          transient_blocks=transient_blocks).items():
             setattr(c, k, int(v))
+        c.budget = budget._h.value if budget is not None else None
+        self._budget = budget  # kept alive while the runtime uses it
         self.config = c
         self._h = ctypes.c_void_p()
         atlas._check(L.atlas_residency_create(ctypes.byref(c), ctypes.byref(self._h)),
@@ -88,6 +115,20 @@ class Residency:
         nd, na = j.n_demote, j.n_admit
         return (self._bufs[0][:nd].copy(), self._bufs[1][:nd].copy(),
                 self._bufs[2][:na].copy(), self._bufs[3][:na].copy())
+
+    def refuse_admissions(self, admit_page, admit_block, nonfinite):
+        """Take back the admissions of the last plan whose nonfinite count
+        (host int32, from atlas_regenerate_pages) is not 0."""
+        page = np.ascontiguousarray(admit_page, dtype=np.int32)
+        block = np.ascontiguousarray(admit_block, dtype=np.int32)
+        counts = np.ascontiguousarray(nonfinite, dtype=np.int32)
+        assert page.size == block.size == counts.size
+        j = atlas.ResidencyJobs()
+        j.struct_size = ctypes.sizeof(j)
+        j.capacity = max(1, page.size)
+        j.n_admit = page.size
+        j.admit_page, j.admit_block = _arr(page), _arr(block)
+        self._call("atlas_residency_refuse_admissions", ctypes.byref(j), _arr(counts))
 
     def tables(self, seqs):
         """Returns (page_table [n][max_pages], context_lens [n], regen_pages [n])."""

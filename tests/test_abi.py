@@ -57,7 +57,7 @@ def test_struct_layouts_match_c(tmp_path):
 
 
 def test_abi_version_and_status_strings():
-    assert atlas.atlas_abi_version() == 3
+    assert atlas.atlas_abi_version() == 4
     assert atlas.atlas_status_string(0) == "ok"
     assert atlas.atlas_status_string(3).startswith("workspace")
     assert atlas.atlas_status_string(99) == "unknown status"
@@ -186,14 +186,14 @@ def test_fold_and_inspection_arguments_are_checked():
     assert L.atlas_gather_pages(ctypes.byref(a), 4, 10, FAKE, FAKE) == atlas.EINVAL
     assert L.atlas_gather_pages(ctypes.byref(a), 0, 64 * 16 + 1, FAKE, FAKE) == atlas.EINVAL
     assert L.atlas_regenerate_pages(1, 1 << 16, 8, 128, 16, atlas.BF16, 0.0, FAKE, FAKE, 1, 1,
-                                    FAKE, FAKE, None) == atlas.EINVAL
+                                    FAKE, FAKE, None, None) == atlas.EINVAL
     assert L.atlas_regenerate_pages(1, 0, 8, 128, 16, atlas.F16, 0.0, FAKE, FAKE, 1, 1,
-                                    FAKE, FAKE, None) == atlas.EUNSUPPORTED
+                                    FAKE, FAKE, None, None) == atlas.EUNSUPPORTED
     assert L.atlas_regenerate_pages(1, 0, 8, 127, 16, atlas.BF16, 0.0, FAKE, FAKE, 1, 1,
-                                    FAKE, FAKE, None) == atlas.EINVAL
+                                    FAKE, FAKE, None, None) == atlas.EINVAL
     for theta in (0.5, 1.0, -2.0, float("nan"), float("inf")):
         assert L.atlas_regenerate_pages(1, 0, 8, 128, 16, atlas.BF16, theta, FAKE, FAKE, 1, 1,
-                                        FAKE, FAKE, None) == atlas.EINVAL
+                                        FAKE, FAKE, None, None) == atlas.EINVAL
 
 
 def test_validate_tables_arguments_are_checked():
@@ -289,19 +289,19 @@ def test_promote_arguments_are_checked():
     pools = atlas.TierPools()
     pools.struct_size = ctypes.sizeof(atlas.TierPools)
     f16 = _args(kv_dtype=atlas.F16)
-    assert L.atlas_promote_pages(ctypes.byref(f16), None, FAKE, FAKE, 1, None) == atlas.EINVAL
+    assert L.atlas_promote_pages(ctypes.byref(f16), None, FAKE, FAKE, 1, None, None) == atlas.EINVAL
     assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, -1,
-                                 None) == atlas.EINVAL
+                                 None, None) == atlas.EINVAL
     assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), None, FAKE, 1,
-                                 None) == atlas.EINVAL
+                                 None, None) == atlas.EINVAL
     assert L.atlas_promote_pages(ctypes.byref(_args(kv_dtype=atlas.F16, num_blocks=0)),
-                                 ctypes.byref(pools), FAKE, FAKE, 1, None) == atlas.EINVAL
+                                 ctypes.byref(pools), FAKE, FAKE, 1, None, None) == atlas.EINVAL
     pools.num_int8 = 1  # int8 pointers missing
     assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), FAKE, FAKE, 1,
-                                 None) == atlas.EINVAL
+                                 None, None) == atlas.EINVAL
     pools.num_int8 = 0
     assert L.atlas_promote_pages(ctypes.byref(f16), ctypes.byref(pools), None, None, 0,
-                                 None) == atlas.OK
+                                 None, None) == atlas.OK
 
 
 def test_positional_policy_arguments_are_checked():

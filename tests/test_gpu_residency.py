@@ -7,6 +7,8 @@ host shadow pools that the oracle writes (the same rows, encodings and
 reconstructions the runtime asks of the device), and the regenerated loop
 is checked on the call whose every page is regenerated."""
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -356,6 +358,7 @@ def test_regen_decode_loop_through_the_runtime(gpu):
         rt.add_seq(s)
         rt.append(s, n)
     fill_new_pages()
+    planted = [0]
     for step in range(40):
         for s in seqs:
             rt.append(s, 1)
@@ -392,8 +395,58 @@ def test_regen_decode_loop_through_the_runtime(gpu):
             assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
         _, _, pages, blocks = rt.plan()
         if len(pages):
+            # finite-value validation before admission: the regenerator counts
+            # the non-finite values it stored per page
+            nf = torch.full((len(pages),), 99, dtype=torch.int32, device=gpu)
             atlas.atlas_regenerate_pages(seed, layer, HKV, D, P, atlas.BF16,
                                          torch.from_numpy(pages).to(gpu),
-                                         torch.from_numpy(blocks).to(gpu), 20, hot_k, hot_v)
+                                         torch.from_numpy(blocks).to(gpu), 20, hot_k, hot_v,
+                                         nonfinite=nf)
+            counts = nf.cpu().numpy()
+            assert (counts == 0).all()
+            if step >= 1 and planted[0] < 2:  # a flagged block (planted on the host)
+                counts[0] = 3                  # is taken back
+                planted[0] += 1
+            rt.refuse_admissions(pages, blocks, counts)
+            forget_stale()
     st = rt.stats()
     assert st["evictions"] > 0 and st["admissions"] > 0 and st["regenerated_pages"] > 0
+    assert st["refused_admissions"] >= 1
+
+
+def test_promote_and_regenerate_count_nonfinite_values(gpu):
+    """The finite check behind admission: a rebuilt page whose source has a
+    NaN scale is all NaN (every element counted), a rejected destination
+    reports -1, and regenerated pages count 0."""
+    hot = torch.zeros((6, HKV, P, D), dtype=torch.float16, device=gpu)
+    hot_v = torch.zeros_like(hot)
+    pools = atlas.TierPools()
+    pools.struct_size = ctypes.sizeof(atlas.TierPools)
+    codes = torch.randint(-127, 128, (2, HKV, P, D), dtype=torch.int8, device=gpu)
+    scales = torch.ones((2, HKV), dtype=torch.float32, device=gpu)
+    scales[1, 1] = float("nan")  # slot 1, kv head 1: a corrupt scale
+    pools.num_int8 = 2
+    pools.int8_k, pools.int8_v = atlas._ptr(codes), atlas._ptr(codes)
+    pools.int8_k_scale, pools.int8_v_scale = atlas._ptr(scales), atlas._ptr(scales)
+    a = _args(gpu, torch.zeros((1, H, D), dtype=torch.bfloat16, device=gpu), hot, hot_v,
+              torch.zeros((1, 4), dtype=torch.int32, device=gpu),
+              torch.ones(1, dtype=torch.int32, device=gpu), torch.empty((1, H, D), device=gpu),
+              torch.empty((1, H), device=gpu), kv=atlas.F16)
+    a.num_blocks = 6
+    src = torch.tensor([(1 << 30) | 0, (1 << 30) | 1, (1 << 30) | 0], dtype=torch.int32,
+                       device=gpu)
+    dst = torch.tensor([2, 3, 9], dtype=torch.int32, device=gpu)  # block 9 is outside
+    nf = torch.full((3,), 99, dtype=torch.int32, device=gpu)
+    atlas.atlas_promote_pages(a, pools, src, dst, nonfinite=nf)
+    torch.cuda.synchronize()
+    assert nf.cpu().tolist() == [0, 2 * P * D, -1]  # K and V of kv head 1
+    kp = torch.empty((3, HKV, P, D), dtype=torch.bfloat16, device=gpu)
+    vp = torch.empty_like(kp)
+    nf2 = torch.full((2,), 99, dtype=torch.int32, device=gpu)
+    atlas.atlas_regenerate_pages(9, 1, HKV, D, P, atlas.BF16,
+                                 torch.tensor([0, 7], dtype=torch.int32, device=gpu),
+                                 torch.tensor([2, 5], dtype=torch.int32, device=gpu), 3, kp, vp,
+                                 nonfinite=nf2)
+    torch.cuda.synchronize()
+    assert nf2.cpu().tolist() == [0, -1]
+

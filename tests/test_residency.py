@@ -291,3 +291,97 @@ def test_archive_config_is_checked():
         with pytest.raises(atlas.AtlasError) as e:
             _tiered(**bad)
         assert e.value.status == atlas.EINVAL
+
+
+# ---------------------------------------------------------------------------
+# Hardening: finite-value validation before admission, global and per-layer
+# budgets (CFR-Atlas README, hardening baseline and test list)
+# ---------------------------------------------------------------------------
+
+def test_refused_admission_goes_back_to_regeneration():
+    r = _regen(hot_blocks=16, admit_per_plan=3)
+    for s in (0, 1):
+        r.add_seq(s)
+        r.append(s, 160)         # 10 pages, 4 resident, 6 regenerated
+    r.tables([1])
+    _, _, pages, blocks = r.plan()
+    assert pages.tolist() == [5, 4, 3]          # all for sequence 1
+    used = r.stats()["hot_used"]
+    # the regenerator found non-finite values in page 4's block: pages 4 and
+    # 3 (admitted below it) go back; page 5 stays resident
+    r.refuse_admissions(pages, blocks, [0, 7, 0])
+    st = r.stats()
+    assert st["refused_admissions"] == 2 and st["admissions"] == 1
+    assert st["hot_used"] == used - 2
+    table, _, regen = r.tables([0, 1])
+    assert regen.tolist() == [6, 5]
+    assert table[1, 5] == blocks[0]
+    # a rejected job (-1) is refused too, and refusing nothing changes nothing
+    _, _, pages, blocks = r.plan()
+    assert pages.tolist() == [4, 3, 2]
+    r.refuse_admissions(pages, blocks, [0, 0, 0])
+    assert r.tables([1])[2].tolist() == [2]
+    _, _, pages, blocks = r.plan()
+    r.refuse_admissions(pages, blocks, [-1] * len(pages))
+    assert r.tables([1])[2].tolist() == [2]
+
+
+def test_refuse_checks_its_jobs_before_changing_anything():
+    r = _regen(hot_blocks=16, admit_per_plan=2)
+    r.add_seq(0)
+    r.append(0, 160)
+    _, _, pages, blocks = r.plan()
+    before = r.stats()
+    with pytest.raises(atlas.AtlasError) as e:
+        r.refuse_admissions(pages, blocks[::-1].copy(), [1, 1])  # blocks do not match
+    assert e.value.status == atlas.EINVAL
+    assert r.stats() == before
+    t = _tiered()
+    t.add_seq(0)
+    t.append(0, 10)
+    with pytest.raises(atlas.AtlasError):
+        t.refuse_admissions([0], [0], [1])  # no admissions in tiered mode
+
+
+def test_shared_budget_caps_layers_together():
+    from kv_cache_runtime_amd.residency import Budget
+    b = Budget(10)
+    layers = [_regen(hot_blocks=8, recent_tokens=64, budget=b) for _ in range(2)]
+    for r in layers:
+        r.add_seq(0)
+    layers[0].append(0, 100)             # 7 pages: window 64 tokens -> 5 resident
+    assert b.used == layers[0].stats()["hot_used"] == 7 - 2
+    layers[1].append(0, 64)              # 4 pages, all in the window
+    assert b.used == 9
+    # layer 1 has 4 free blocks of its own, the shared budget only 1: the
+    # layer evicts its own least recently used page outside its window
+    layers[1].append(0, 32)              # 6 pages, window 64 tokens: pages 2..5
+    assert b.used == 10 and layers[1].stats()["hot_used"] == 5
+    with pytest.raises(atlas.AtlasError) as e:   # a sequence with no evictable page
+        layers[1].add_seq(1)
+        layers[1].append(1, 64)
+    assert e.value.status == atlas.ECAPACITY
+    assert b.used == 10
+    # freeing a layer's pages returns them to the budget
+    layers[0].remove_seq(0)
+    assert b.used == 5
+    layers[1].append(1, 64)  # 3 free blocks of its own, then its oldest evictable page
+    assert b.used == 8 and layers[1].stats()["evictions"] == 2
+    for r in layers:
+        r.close()
+    assert b.used == 0
+    b.close()
+
+
+def test_per_layer_budget_is_the_runtime_pool():
+    from kv_cache_runtime_amd.residency import Budget
+    b = Budget(1000)  # a global budget far above the layer's
+    r = _regen(hot_blocks=4, recent_tokens=128, budget=b)
+    r.add_seq(0)
+    with pytest.raises(atlas.AtlasError) as e:
+        r.append(0, 80)  # 5 pages in the window > 4 blocks
+    assert e.value.status == atlas.ECAPACITY and b.used == 0
+    r.append(0, 64)
+    assert b.used == 4
+    r.close()
+    b.close()
