@@ -15,7 +15,9 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libatlas.so")
+# ATLAS_LIBRARY selects another build of the same library (the host
+# sanitizer build of build.py --sanitize); there is no fallback.
+LIB_PATH = os.environ.get("ATLAS_LIBRARY") or os.path.join(HERE, "libatlas.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EDEVICE, ECAPACITY = 0, 1, 2, 3, 4, 5
 F32, BF16, F16 = 0, 1, 2

@@ -354,8 +354,10 @@ DecodeParams decode_params(const atlas_attn_args *a, const Plan &plan) {
     page_divider(a->page_tokens, p.p_magic, p.p_shift);
     p.scale_log2 = a->scale * 1.4426950408889634f;
     char *ws = reinterpret_cast<char *>(a->workspace);
-    p.part_o = plan.direct ? nullptr : reinterpret_cast<float *>(ws);
-    p.part_lse = plan.direct ? nullptr : reinterpret_cast<float *>(ws + plan.part_o_bytes);
+    // (callers that launch nothing, such as the validator, may pass no
+    // workspace: no pointer is formed from a null base)
+    p.part_o = plan.direct || !ws ? nullptr : reinterpret_cast<float *>(ws);
+    p.part_lse = plan.direct || !ws ? nullptr : reinterpret_cast<float *>(ws + plan.part_o_bytes);
     p.out = a->out;
     p.lse = a->lse;
     p.direct = plan.direct ? 1 : 0;
