@@ -257,8 +257,10 @@ const char *atlas_last_error(void);
 
 /*
  * Workspace bytes needed by atlas_paged_attention (regen == NULL) or
- * atlas_paged_attention_regen (regen != NULL) for these arguments.  Reads host
- * fields only.  The workspace holds the split-K partials of decode (one f32
+ * atlas_paged_attention_regen (regen != NULL) for these arguments, and of
+ * atlas_paged_attention_tiered (regen NULL; its pools do not change the
+ * size, and the hot-pool fields are not checked here, so an all-cold call
+ * with num_blocks 0 can be sized).  Reads host fields only.  The workspace holds the split-K partials of decode (one f32
  * vector of head_dim plus one lse per (row, head, split)).  Matrix-core
  * chunked prefill takes the keys in windows of W tokens (W = split_tokens,
  * or 16384 when split_tokens is 0, cut to the longest context rounded up to

@@ -98,8 +98,10 @@ int choose_split_tokens(const atlas_attn_args *a) {
 
 bool dtype_ok(int32_t d) { return d == ATLAS_F32 || d == ATLAS_BF16 || d == ATLAS_F16; }
 
+// sizing: atlas_workspace_size, which serves plain and tiered calls alike,
+// so the hot-pool checks that only a plain call needs are left to the call.
 atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_regen_spec *rg,
-                          Plan *plan) {
+                          Plan *plan, bool sizing = false) {
     if (!a) return fail(ATLAS_EINVAL, "args is NULL");
     if (a->struct_size != sizeof(atlas_attn_args))
         return fail(ATLAS_EINVAL, "args->struct_size %u != %zu", a->struct_size,
@@ -124,7 +126,7 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
         return fail(ATLAS_EUNSUPPORTED, "page_tokens %d is not a multiple of 16", a->page_tokens);
     if (a->max_pages_per_seq < 1)
         return fail(ATLAS_EINVAL, "max_pages_per_seq %d < 1", a->max_pages_per_seq);
-    if (a->num_blocks < (tiered ? 0 : 1))
+    if (a->num_blocks < (tiered || sizing ? 0 : 1))
         return fail(ATLAS_EINVAL, "num_blocks %d out of range", a->num_blocks);
     const int64_t max_keys = (int64_t)a->max_pages_per_seq * a->page_tokens;
     if (max_keys > INT32_MAX)
@@ -152,7 +154,7 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
                     a->split_tokens);
     if (!a->q || !a->page_table || !a->context_lens || !a->out || !a->lse)
         return fail(ATLAS_EINVAL, "NULL q, page_table, context_lens, out or lse");
-    if (!tiered && (!a->k_pool || !a->v_pool))
+    if (!tiered && !sizing && (!a->k_pool || !a->v_pool))
         return fail(ATLAS_EINVAL, "NULL k_pool or v_pool");
     if (tiered && a->num_blocks > 0 && (!a->k_pool || !a->v_pool))
         return fail(ATLAS_EINVAL, "NULL hot k_pool or v_pool with num_blocks > 0");
@@ -504,7 +506,7 @@ atlas_status atlas_workspace_size(const atlas_attn_args *args, const atlas_regen
                                   size_t *bytes) {
     if (!bytes) return fail(ATLAS_EINVAL, "bytes is NULL");
     Plan plan;
-    atlas_status st = check_common(args, false, regen, &plan);
+    atlas_status st = check_common(args, false, regen, &plan, /*sizing=*/true);
     if (st != ATLAS_OK) return st;
     *bytes = plan.total;
     return ok();

@@ -112,7 +112,6 @@ def test_workspace_size_of_a_valid_call():
     (dict(page_tokens=0), atlas.EINVAL),
     (dict(page_tokens=24), atlas.EUNSUPPORTED),
     (dict(max_pages_per_seq=0), atlas.EINVAL),
-    (dict(num_blocks=0), atlas.EINVAL),
     (dict(max_context_len=64 * 16 + 1), atlas.EINVAL),
     (dict(max_context_len=-1), atlas.EINVAL),
     (dict(total_q=5), atlas.EINVAL),
@@ -331,3 +330,20 @@ def test_noalloc_rejects_a_plan_beyond_its_scratch():
     st = atlas.load().atlas_paged_attention_noalloc(ctypes.byref(a))
     assert st == atlas.EWORKSPACE
     assert b"scratch" in atlas.load().atlas_last_error()
+
+
+def test_workspace_size_serves_an_all_cold_tiered_call():
+    """A tiered decode whose pages are all cold has no hot pool (num_blocks 0,
+    NULL pools); the sizing call accepts it and gives the split-K bytes the
+    tiered call needs, while the plain call still refuses it."""
+    a = _args(num_blocks=0, split_tokens=64)
+    a.k_pool = None
+    a.v_pool = None
+    st, need = _ws(a)
+    assert st == atlas.OK and need > 0
+    b = _args(split_tokens=64)
+    assert _ws(b) == (atlas.OK, need)
+    assert atlas.load().atlas_paged_attention(ctypes.byref(a)) == atlas.EINVAL
+    c = _args(num_blocks=0)  # pools present, no blocks: the plain call refuses too
+    assert atlas.load().atlas_paged_attention(ctypes.byref(c)) == atlas.EINVAL
+
