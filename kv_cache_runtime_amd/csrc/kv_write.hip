@@ -139,13 +139,18 @@ __device__ inline void widen8(const DemoteSrc &s, const uint4 w, float (&x)[8]) 
     }
 }
 
+// max |x| of the 8 elements, +inf if any of them is NaN or infinite (a
+// plain fmaxf would drop a NaN)
 template <int ST>
 __device__ inline float absmax8(const DemoteSrc &s, const uint4 w) {
     float x[8];
     widen8<ST>(s, w, x);
     float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+    for (int j = 0; j < 8; ++j) {
+        const float a = fabsf(x[j]);
+        m = fmaxf(m, a == a ? a : __builtin_inff());
+    }
     return m;
 }
 
@@ -219,7 +224,11 @@ __device__ inline void encode_block(const DemoteSrc &src, const int64_t nch, int
         amax = fmaxf(amax, absmax8<ST>(src, load_chunk<ST>(src, ch)));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const float scale = __fdiv_rn(amax, (float)qmax);
+    // a block holding a non-finite value gets a NaN scale (and codes 0, since
+    // no code is formed from a NaN scale), so every value read back from it
+    // is NaN instead of a finite stand-in
+    const float scale = amax == __builtin_inff() ? __builtin_nanf("")
+                                                  : __fdiv_rn(amax, (float)qmax);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t ch = lane + 64 * j;

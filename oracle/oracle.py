@@ -258,9 +258,14 @@ def quantize_block(x: np.ndarray, qmax: int):
     scale = f32(max |x|) / qmax and code = clamp(rint(f32(x) / scale), -qmax,
     qmax), both divisions in f32 with correct rounding, so that a device
     computing in f32 takes the same integer decisions.  An all-zero block gets
-    scale 0 and codes 0.  Returns (int16 codes of x's shape, np.float32 scale).
+    scale 0 and codes 0.  A block holding a NaN or an infinity gets a NaN scale
+    and codes 0, so that every value read back from it is NaN (reading: bad
+    values fail loudly, attnres AGENTS.md, "Non-Negotiable Invariants").
+    Returns (int16 codes of x's shape, np.float32 scale).
     """
     x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        return np.zeros(x.shape, dtype=np.int16), np.float32(np.nan)
     amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
     scale = np.float32(amax / np.float32(qmax))
     if scale == 0:
@@ -303,9 +308,12 @@ def quantize_block_fp8(x: np.ndarray):
     """FP8 (E4M3) encoding of one (page, kv head) block (reading: one f32
     scale per block, like the integer tiers): scale = f32(max |x|) / 448 and
     code = nearest E4M3 code to f32(x) / scale, both divisions correctly
-    rounded f32.  An all-zero block gets scale 0 and codes 0.  Returns
-    (uint8 codes of x's shape, np.float32 scale)."""
+    rounded f32.  An all-zero block gets scale 0 and codes 0; a block holding
+    a NaN or an infinity a NaN scale and codes 0 (as for the integer tiers).
+    Returns (uint8 codes of x's shape, np.float32 scale)."""
     x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        return np.zeros(x.shape, dtype=np.uint8), np.float32(np.nan)
     amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
     scale = np.float32(amax / np.float32(448.0))
     if scale == 0:

@@ -143,6 +143,59 @@ def test_demote_pages_bit_exact_and_attention(gpu, hot_dtype):
     check(w, out, lse)
 
 
+def test_demote_block_with_non_finite_value_gets_nan_scale(gpu):
+    """A hot block holding a NaN (or an infinity) is demoted to a NaN scale
+    with codes 0 -- every value read back is NaN -- while the other blocks of
+    the same pages encode as usual; codes and scales match the oracle's
+    encoder, NaN for NaN."""
+    w = _demote_case(gpu, "f16", seed=13)
+    Hkv, P = w.num_kv_heads, w.page_tokens
+    s = 2
+    ctx = int(w.context_lens[s])
+    ent = w.page_table[s].view(np.uint32)
+    pages = [p for p in range(ctx // P) if (int(ent[p]) >> 30) == 0][:2]
+    assert len(pages) == 2
+    src = [int(ent[p]) & ((1 << 30) - 1) for p in pages]
+    w.k_pool[src[0], 0, 3, 17] = float("nan")
+    w.v_pool[src[1], Hkv - 1, 5, 2] = float("inf")
+    n8, n4 = w.tiers["i8_k"].shape[0], w.tiers["i4_k"].shape[0]
+    for key in ("i8", "i4"):
+        for kv in ("k", "v"):
+            t = w.tiers[f"{key}_{kv}"]
+            w.tiers[f"{key}_{kv}"] = torch.cat([t, torch.zeros((1,) + t.shape[1:],
+                                                               dtype=t.dtype, device=gpu)])
+            sc = w.tiers[f"{key}_{kv}_scale"]
+            w.tiers[f"{key}_{kv}_scale"] = torch.cat([sc, torch.full((1, Hkv), -1.0, device=gpu)])
+    dst = [(1 << 30) | n8, (2 << 30) | n4]
+    prob = atlas.Problem(w)
+    atlas.atlas_demote_pages(prob.args, prob.tiers, torch.tensor(src, dtype=torch.int32,
+                                                                 device=gpu),
+                             torch.tensor(np.array(dst, dtype=np.uint32).view(np.int32),
+                                          device=gpu))
+    torch.cuda.synchronize()
+    host = oracle.HostView(w)
+    (ka, kind), (va, _) = host.pools()
+    ta = host.tier_arrays()
+    nan_blocks = 0
+    for b, e in zip(src, dst):
+        tier, slot = e >> 30, e & ((1 << 30) - 1)
+        key, qmax = ("i8", 127) if tier == 1 else ("i4", 7)
+        for arr, kv in ((ka, "k"), (va, "v")):
+            for g in range(Hkv):
+                x = oracle.widen_bits(arr[b, g], kind).astype(np.float32)
+                codes, scale = oracle.quantize_block(x, qmax)
+                got_scale = np.float32(ta[f"{key}_{kv}_scale"][slot, g])
+                if np.isnan(scale):
+                    nan_blocks += 1
+                    assert np.isnan(got_scale), (b, kv, g)
+                else:
+                    assert got_scale.tobytes() == scale.tobytes(), (b, kv, g)
+                want = codes.astype(np.int8) if tier == 1 else oracle.pack_int4(codes)
+                got = ta[f"{key}_{kv}"][slot, g]
+                assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (b, kv, g)
+    assert nan_blocks == 2
+
+
 def test_demote_rejects_bad_destinations_and_poisons_bad_sources(gpu):
     w = _demote_case(gpu, "f16", seed=12)
     Hkv = w.num_kv_heads

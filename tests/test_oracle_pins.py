@@ -475,6 +475,22 @@ def test_quantize_block_extremes_symmetry_and_round_trip(qmax):
     assert ps == scale * np.float32(8.0) and np.array_equal(pc, codes)
 
 
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_quantize_block_with_a_non_finite_value_gives_nan(bad):
+    """A block holding a NaN or an infinity encodes to a NaN scale with codes
+    0, integer tiers and FP8 alike, so every value decoded from it is NaN:
+    f32(code * NaN) is NaN for every code, the E4M3 values included."""
+    x = np.linspace(-3, 3, 64, dtype=np.float32).reshape(8, 8)
+    x[5, 3] = bad
+    for qmax in (127, 7, 1):
+        codes, scale = oracle.quantize_block(x, qmax)
+        assert np.isnan(scale) and not codes.any()
+        assert np.isnan(codes.astype(np.float32) * scale).all()
+    codes, scale = oracle.quantize_block_fp8(x)
+    assert np.isnan(scale) and not codes.any()
+    assert np.isnan(oracle.fp8_e4m3_value(codes) * np.float64(scale)).all()
+
+
 def test_quantize_block_zero_and_int4_packing():
     codes, scale = oracle.quantize_block(np.zeros((4, 8), np.float32), 7)
     assert scale == 0 and not codes.any()
