@@ -130,13 +130,16 @@ def measured_traffic(workload: str):
 
 def cpu_baseline(w, work, budget_s: float = 20.0):
     """Time the f64 oracle on a bounded sample of the same workload, running
-    independent (sequence, kv head) groups on the host cores."""
+    independent (sequence, kv head) groups on every host core this process
+    may use (one worker thread per core; inside a worker the oracle's own
+    OpenMP regions run single-threaded, so the cores are not oversubscribed)."""
+    import ctypes
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
 
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = max(1, len(os.sched_getaffinity(0)))
     host = oracle.HostView(w)
     host.pools()
     host.tier_arrays()
@@ -175,8 +178,15 @@ def cpu_baseline(w, work, budget_s: float = 20.0):
         oracle.reference(w, rows=rows, heads=heads, host=host)
 
     cores = min(cores, len(chosen))  # threads actually used
+    from oracle import oracle as oracle_impl
+    oracle_impl.lib()  # loads the oracle and its OpenMP runtime
+    gomp = ctypes.CDLL("libgomp.so.1")
+
+    def one_thread_omp():
+        gomp.omp_set_num_threads(1)
+
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=cores) as ex:
+    with ThreadPoolExecutor(max_workers=cores, initializer=one_thread_omp) as ex:
         list(ex.map(task, chosen))
     dt = time.perf_counter() - t0
     done_pairs = sum(c[3] for c in chosen)
