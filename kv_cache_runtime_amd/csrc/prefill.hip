@@ -27,15 +27,18 @@
 // exponential in one wave holds up the matrix instructions of the other, so
 // each wave interleaves its own work instead: keys are folded in units of 32,
 // and while the matrix core computes the scores of unit u + 1 the wave takes
-// the exponentials of unit u between the products; the P.V products of unit
-// u then run beside the row max of unit u + 1.  The issue order inside a
-// unit is fixed with scheduling barriers.
+// the exponentials of unit u between the products, whose second half
+// alternates with the first P.V products of unit u.  The issue order inside
+// a unit is fixed with scheduling barriers.  No row max is taken per unit:
+// the reference max moves only when a half unit's f16 weights overflow
+// (a score more than 9 log2 units above it), which the sum of that half's
+// weights shows; the half is then redone.
 //
 // Staging.  The keys of the call come from a ring the window preparation
 // kernel fills (K in the kv type, V in f16), 64 contiguous rows per tile.
 // They move from memory straight into LDS by DMA (global_load_lds), with no
-// registers in between.  LDS holds four buffers of one K tile and one V tile
-// each; a tile is issued three tiles ahead and the workgroup meets once per
+// registers in between.  LDS holds five buffers of one K tile and one V tile
+// each; a tile is issued four tiles ahead and the workgroup meets once per
 // tile.  Rows are not padded: the 16-byte chunks of each row are permuted
 // so that the fragment reads of the matrix operands hit distinct banks.
 // P is kept relative to the reference max minus 7 and is at most 2^15, so
@@ -131,11 +134,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     constexpr float kPScale = 7.0f;
     const float kNegInf = -__builtin_inff();
 
-    // four LDS buffers, each a K tile and a V tile; separate objects, so
+    // five LDS buffers, each a K tile and a V tile; separate objects, so
     // that the compiler sees a DMA into one buffer does not alias reads of
     // another and adds no wait for it
     __shared__ __attribute__((aligned(1024))) uint16_t sB0[2 * kTile * kD], sB1[2 * kTile * kD],
-        sB2[2 * kTile * kD], sB3[2 * kTile * kD];
+        sB2[2 * kTile * kD], sB3[2 * kTile * kD], sB4[2 * kTile * kD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -240,8 +243,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[b][j] = 0.0f;
     float m_ref = kNegInf, l = 0.0f;
-    float alpha = 1.0f;     // rescale of o and l owed before the next P.V
-    bool owe = false;       // some lane of the wave moved its reference max
 
     // ---- staging.  Tiles come from the window's ring [seq][kv head][key -
     // key_begin][D] (K in the kv type, V in f16, rows past the context zero),
@@ -252,15 +253,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     // instead the 16-byte chunks of a row are permuted so that the matrix
     // operand reads hit distinct banks: chunk c of K row k sits at position
     // c ^ (k % 16), chunk c of V row k at c ^ (4 (k % 4) + 2 ((k / 4) % 2)).
-    // Content x is K of tile x and V of tile x - 1; it lives in buffer x % 4
+    // Content x is K of tile x and V of tile x - 1; it lives in buffer x % 5
     // and is issued three tiles before it is read.
     // buffer B: K tile at element 0, V tile at element kTile * kD
     auto kbuf = [&](auto b_c) __attribute__((always_inline)) -> uint16_t * {
-        constexpr int B = decltype(b_c)::value & 3;
+        constexpr int B = decltype(b_c)::value % 5;
         if constexpr (B == 0) return sB0;
         else if constexpr (B == 1) return sB1;
         else if constexpr (B == 2) return sB2;
-        else return sB3;
+        else if constexpr (B == 3) return sB3;
+        else return sB4;
     };
     auto vbuf = [&](auto b_c) __attribute__((always_inline)) -> uint16_t * {
         return kbuf(b_c) + kTile * kD;
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
 
     // The keys are folded in units of 32 (unit u = keys 32 u .. 32 u + 31 of
     // the call, half u % 2 of tile u / 2), one 32 x 32 score block each.
-    // ---- scores of unit u (K of tile u / 2, buffer B = (u / 2) % 4).  Lane
+    // ---- scores of unit u (K of tile u / 2, buffer B = (u / 2) % 5).  Lane
     // (r, half) reads chunk 2 ks + half of row 32 (u % 2) + r, which sits at
     // byte (r * 256 + ((half ^ r % 16) << 4)) ^ (ks << 5) of its half tile.
     const uint32_t kaddr = r * kRowBytes + ((half ^ (r & 15)) << 4);
@@ -354,36 +356,20 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
         for (int j = 0; j < 16; ++j) sx[j] = 8 * (j >> 2) + (j & 3) <= lim ? sx[j] : kNegInf;
     };
-    // mraw: the max of this lane's (biased, masked) scores of unit u
-    auto new_reference = [&](int u, float mraw) __attribute__((always_inline)) {
-        if constexpr (ALIBI) mraw += ab * (float)(kb0 + 32 * u + 4 * half - pos);
+    // the first unit's reference: its row max (nothing is accumulated yet,
+    // so nothing is rescaled)
+    auto first_reference = [&](f32x16_t &sx, bool mask) __attribute__((always_inline)) {
+        if (mask) causal_mask(0, sx);  // wave-uniform
+        float mraw = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, sx[j]);
+        if constexpr (ALIBI) mraw += ab * (float)(kb0 + 4 * half - pos);
         {  // the row's other half (lane r + 32)
             const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw),
                                                             __float_as_uint(mraw), false, false);
             mraw = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
         }
-        const float mt = mraw * p.scale_log2;    // scale > 0 keeps the order
-        const bool move = mt > m_ref + kSlack;  // also true on the first finite unit
-        const float m_new = move ? mt : m_ref;
-        alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-        m_ref = m_new;
-        owe = __any(move);
-    };
-    auto row_max = [&](int u, f32x16_t &sx, bool mask) __attribute__((always_inline)) {
-        if (mask) causal_mask(u, sx);  // wave-uniform
-        float mraw = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, sx[j]);
-        new_reference(u, mraw);
-    };
-    auto settle = [&]() __attribute__((always_inline)) {  // pay a rescale owed to the accumulators
-        if (owe) {
-            l *= alpha;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
-        }
+        m_ref = mraw * p.scale_log2;  // scale > 0 keeps the order
     };
     // a unit needs the causal mask when it reaches past the first position of
     // the wave (or the wave holds rows past the chunk)
@@ -391,16 +377,17 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     // One unit, in an explicit issue order (the compiler may not move code
     // across the scheduling barriers): the scores of unit u + 1 on the matrix
     // cores, each product beside one exponential pair of unit u and the read
-    // of a K fragment four products ahead; then the P.V products of unit u,
-    // the first four beside the reads of the last V fragments, the last four
-    // beside the row max of unit u + 1.  sc holds unit u's scores, sn
-    // receives unit u + 1's.  MORE: a unit follows; KB / VB: the buffers of
-    // the K tile of unit u + 1 and of the V tile of unit u.
+    // of a K fragment two products ahead; the last four alternate with the
+    // first four P.V products of unit u; then the other four P.V products.
+    // sc holds unit u's scores, sn receives unit u + 1's.  MORE: a unit
+    // follows; KB / VB: the buffers of the K tile of unit u + 1 and of the V
+    // tile of unit u.
     auto unit = [&](int u, f32x16_t &sc, f32x16_t &sn, auto more_c, auto kb_c,
                     auto vb_c) __attribute__((always_inline)) {
         constexpr bool MORE = decltype(more_c)::value;
-        constexpr int kAhead = 4;  // K fragments in flight
-        settle();
+        constexpr int kAhead = 2;  // K fragments in flight
+        // (no rescale is owed here: the reference moves only inside a unit,
+        // which rescales at once; the first unit's reference finds o = 0)
         const char *cK =
             reinterpret_cast<const char *>(kbuf(kb_c)) + ((u + 1) & 1) * (32 * kRowBytes);
         const char *cV = reinterpret_cast<const char *>(vbuf(vb_c)) + (u & 1) * (32 * kRowBytes);
@@ -426,63 +413,101 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         if constexpr (ALIBI)
             m_off = fmaf(-ab * (float)(kb0 + 32 * u + 4 * half - pos), p.scale_log2, m_off);
         uint32_t w[8];
+        float lh = 0.0f;  // the f16 weights of the current half unit
         auto pexp = [&](int i) __attribute__((always_inline)) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i], p.scale_log2, -m_off));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * i + 1], p.scale_log2, -m_off));
             const f16x2_t h = {(_Float16)p0, (_Float16)p1};
-            l = __builtin_amdgcn_fdot2(h, f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, l, false);
+            lh = __builtin_amdgcn_fdot2(h, f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, lh, false);
             w[i] = __builtin_bit_cast(uint32_t, h);
             // keep the pair here, beside its matrix product (the compiler
             // would otherwise sink it to its use after the mask branch)
-            asm volatile("" : "+v"(w[i]), "+v"(l));
+            asm volatile("" : "+v"(w[i]), "+v"(lh));
+        };
+        // A half unit whose weights overflowed f16 (a key more than 9 log2
+        // units above the reference) is redone: the reference moves to the
+        // unit's row max, the accumulators are rescaled, and the half's
+        // weights are recomputed.  Rare: it needs a score far above every
+        // earlier one of the row.
+        auto check_half = [&](int h) __attribute__((always_inline)) {
+            if (__any(!(lh < __builtin_inff()))) {  // wave-uniform; NaN lands here too
+                float mraw = kNegInf;  // over this half's scores (the other half
+#pragma unroll                                 // checks its own)
+                for (int j = 8 * h; j < 8 * h + 8; ++j) mraw = fmaxf(mraw, sc[j]);
+                if constexpr (ALIBI) mraw += ab * (float)(kb0 + 32 * u + 4 * half - pos);
+                const auto hm = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(mraw), __float_as_uint(mraw), false, false);
+                mraw = fmaxf(__uint_as_float(hm[0]), __uint_as_float(hm[1]));
+                const float mt = mraw * p.scale_log2;
+                const bool move = mt > m_ref + kSlack;
+                const float m_new = move ? mt : m_ref;
+                const float a = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+                m_ref = m_new;
+                l *= a;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[b][j] *= a;
+                m_off = (m_ref == kNegInf) ? 0.0f : m_ref - kPScale;
+                if constexpr (ALIBI)
+                    m_off = fmaf(-ab * (float)(kb0 + 32 * u + 4 * half - pos), p.scale_log2, m_off);
+                lh = 0.0f;
+#pragma unroll
+                for (int i = 4 * h; i < 4 * h + 4; ++i) pexp(i);
+            }
+            l += lh;
+            lh = 0.0f;
         };
         if constexpr (MORE) {
 #pragma unroll
             for (int ks = 0; ks < kAhead; ++ks) kread(ks);
         }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) vread(0, b);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        // the score products of unit u + 1 (a chain through sn) alternate
+        // with the P.V products of unit u (independent accumulators) from the
+        // fifth on, so that a score product never waits for the one before
+        auto score = [&](int i) __attribute__((always_inline)) {
             if constexpr (MORE) {
                 // the first step starts from a zero accumulator operand
                 sn = mfma32<KV>(kf[i], qf[i], i == 0 ? f32x16_t{} : sn);
                 if constexpr (ROPE) sn = mfma32<KV>(kf[i], qlo[i], sn);
                 if (i + kAhead < 8) kread(i + kAhead);
             }
-            pexp(i);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        pb[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        pb[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        };
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            o[b] = mfma32<KV_F16>(vf[0][b], pb[0], o[b]);
-            vread(1, b);
+        for (int i = 0; i < 4; ++i) {
+            score(i);
+            pexp(i);
+            vread(0, i);
             __builtin_amdgcn_sched_barrier(0);
         }
+        check_half(0);
+        pb[0] = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+        for (int i = 4; i < 8; ++i) {
+            score(i);
+            o[i - 4] = mfma32<KV_F16>(vf[0][i - 4], pb[0], o[i - 4]);
+            pexp(i);
+            vread(1, i - 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        check_half(1);
+        pb[1] = make_uint4(w[4], w[5], w[6], w[7]);
         if constexpr (MORE) {
             alibi_bias(sn);
             if (masked(u + 1)) causal_mask(u + 1, sn);
         }
-        // the row max of unit u + 1 beside the last four products
-        float mraw = kNegInf;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             o[b] = mfma32<KV_F16>(vf[1][b], pb[1], o[b]);
-            if constexpr (MORE) {
-#pragma unroll
-                for (int j = 4 * b; j < 4 * b + 4; ++j) mraw = fmaxf(mraw, sn[j]);
-            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (MORE) new_reference(u + 1, mraw);
     };
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     using B2 = std::integral_constant<int, 2>;
     using B3 = std::integral_constant<int, 3>;
+    using B4 = std::integral_constant<int, 4>;
 
     // ---- prologue: contents 0, 1 and 2 in LDS, the scores of unit 0.  All
     // three have landed before the loop, so that its first tile starts from
@@ -493,50 +518,54 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     dma_content(0, B0{});
     dma_content(1, B1{});
     dma_content(2, B2{});
+    dma_content(3, B3{});
     tile_wait<0>();
     tile_barrier();
     scores(0, sa, B0{});
     alibi_bias(sa);
-    row_max(0, sa, masked(0));
+    first_reference(sa, masked(0));
 
     // ---- iteration t folds tile t (units 2t, 2t + 1) from contents t and
-    // t + 1 (buffers P = t % 4 and P + 1).
+    // t + 1 (buffers P = t % 5 and P + 1).
     auto iteration = [&](int t, auto ph_c, auto more_c) __attribute__((always_inline)) {
         constexpr int P = decltype(ph_c)::value;
         using BK = std::integral_constant<int, P>;
-        using BN = std::integral_constant<int, (P + 1) & 3>;
+        using BN = std::integral_constant<int, (P + 1) % 5>;
         unit(2 * t, sa, sb, std::true_type{}, BK{}, BN{});
         unit(2 * t + 1, sb, sa, more_c, BN{}, BN{});
     };
-    // Every tile but the last issues content t + 3 into the buffer of content
+    // Every tile but the last issues content t + 4 into the buffer of content
     // t - 1, free since the last barrier, and ends once content t + 2 has
-    // landed: one barrier per tile.  The loop is unrolled by the four buffer
+    // landed: one barrier per tile.  The loop is unrolled by the five buffer
     // phases and holds one DMA per phase, with no branch around a DMA, so the
     // compiler tells the buffers apart and adds no wait of its own.
     auto step = [&](int t, auto ph_c) __attribute__((always_inline)) {
         constexpr int P = decltype(ph_c)::value;
-        dma_content(t + 3, std::integral_constant<int, (P + 3) & 3>{});
+        dma_content(t + 4, std::integral_constant<int, (P + 4) % 5>{});
         iteration(t, ph_c, std::true_type{});
-        tile_wait<4>();
+        tile_wait<8>();
         tile_barrier();
     };
     int tl = 0;  // tiles folded so far
-    for (; tl + 4 < n_tiles; tl += 4) {
+    for (; tl + 5 < n_tiles; tl += 5) {
         step(tl, B0{});
         step(tl + 1, B1{});
         step(tl + 2, B2{});
         step(tl + 3, B3{});
+        step(tl + 4, B4{});
     }
-    // the remaining 1 .. 4 tiles: all but the last as above, then the last
+    // the remaining 1 .. 5 tiles: all but the last as above, then the last
     const int rem = n_tiles - tl;
     if (rem > 1) step(tl, B0{});
     if (rem > 2) step(tl + 1, B1{});
     if (rem > 3) step(tl + 2, B2{});
+    if (rem > 4) step(tl + 3, B3{});
     switch (rem) {
         case 1: iteration(tl, B0{}, std::false_type{}); break;
         case 2: iteration(tl + 1, B1{}, std::false_type{}); break;
         case 3: iteration(tl + 2, B2{}, std::false_type{}); break;
-        default: iteration(tl + 3, B3{}, std::false_type{}); break;
+        case 4: iteration(tl + 3, B3{}, std::false_type{}); break;
+        default: iteration(tl + 4, B4{}, std::false_type{}); break;
     }
     tile_wait<0>();  // no DMA may still be writing LDS when the wave ends
 
