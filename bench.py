@@ -128,6 +128,32 @@ def measured_traffic(workload: str):
     return None
 
 
+def measured_valu_busy(workload: str):
+    """Fraction of the main kernel's resident-wave time spent issuing vector
+    (VALU, MFMA included) instructions, SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES,
+    from the committed rocprofv3 instruction-mix summary, or None when that
+    summary was taken with other kernel sources or does not cover the
+    workload."""
+    path = os.path.join(ROOT, "profiles", "instruction_mix.txt")
+    if not os.path.exists(path):
+        return None
+    digest, cur, vals = None, None, {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("# kernel sources digest"):
+                digest = line.split()[-1]
+            elif line.startswith("workload="):
+                cur = line.split()[0].split("=", 1)[1]
+                vals[cur] = {}
+            elif cur and line.startswith("  SQ_"):
+                name, value = line.split()
+                vals[cur][name] = float(value)
+    v = vals.get(workload)
+    if digest != kernel_sources_digest() or not v:
+        return None
+    return round(v["SQ_ACTIVE_INST_VALU"] / v["SQ_WAVE_CYCLES"], 3)
+
+
 def cpu_baseline(w, work, budget_s: float = 20.0):
     """Time the f64 oracle on a bounded sample of the same workload, running
     independent (sequence, kv head) groups on every host core this process
@@ -552,6 +578,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None}
     roof["traffic"] = measured_traffic(w.name)
+    # issue-side view of the same kernel (rocprofv3 SQ counters, committed summary)
+    roof["valu_busy"] = measured_valu_busy(w.name)
     roof["kernel_avg_ms"] = round(kern_avg, 5)
     roof["kernel_median_ms"] = round(kern_ms[K // 2], 5)
     roof["kernel_min_ms"] = round(kern_ms[0], 5)
