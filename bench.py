@@ -154,6 +154,20 @@ def measured_valu_busy(workload: str):
     return round(v["SQ_ACTIVE_INST_VALU"] / v["SQ_WAVE_CYCLES"], 3)
 
 
+def alias_slots(w, n: int):
+    """Rewrite the page table so that every entry names slot mod n of its own
+    pool (tier bits kept): the same kernels and the same call shape, with
+    every page read from a few cached blocks.  Diagnostic only; the results
+    are not those of the workload."""
+    import numpy as np
+    t = w.page_table.astype(np.int64) & 0xFFFFFFFF
+    tier = t >> 30
+    low = np.where(tier == 3, (1 << 28) - 1, (1 << 30) - 1)
+    slot = t & low
+    out = (t & ~low) | (slot % n)
+    w.page_table = out.astype(np.uint32).view(np.int32).copy()
+
+
 def cpu_baseline(w, work, budget_s: float = 20.0):
     """Time the f64 oracle on a bounded sample of the same workload, running
     independent (sequence, kv head) groups on every host core this process
@@ -484,6 +498,10 @@ def main():
                          "E4M3, the rest split evenly between int8 and int4")
     ap.add_argument("--p-int2", type=float, default=0.0,
                     help="tiered 64-sequence workload (--config 4): share of the cold pages stored as INT2")
+    ap.add_argument("--alias-slots", type=int, default=0,
+                    help="diagnostic: map every page-table entry's slot to slot mod N in "
+                         "its own pool, so the call reads N blocks per pool from cache "
+                         "instead of HBM (the kernel's floor without memory traffic)")
     ap.add_argument("--op", choices=("attention", "write_kv", "demote", "archive", "promote"),
                     default="attention",
                     help="attention (default): the attention call of --config; write_kv: "
@@ -524,6 +542,8 @@ def main():
         extra["tiers"] = dict(hot_tokens=1024, p_int8=rest / 2, p_fp8=args.p_fp8,
                               p_int2=args.p_int2)
     w = synth.config(args.config, device=dev, seed=42, **extra)
+    if args.alias_slots > 0:
+        alias_slots(w, args.alias_slots)
     prob = atlas.Problem(w, split_tokens=args.split_tokens)
     if w.regen is not None:
         prob.fill_resident_from_regenerator()
@@ -662,6 +682,10 @@ def main():
     }
     if positional:
         line["config"]["positional"] = positional
+    if args.alias_slots > 0:
+        # the same calls over N blocks per pool: achieved bytes/s are not HBM's
+        line["config"]["alias_slots"] = args.alias_slots
+        line["metric"] += " (diagnostic: slots aliased, reads served from cache)"
     if args.p_fp8 > 0 or args.p_int2 > 0:
         line["config"]["cold_fp8_share"] = args.p_fp8
         line["config"]["cold_int2_share"] = args.p_int2

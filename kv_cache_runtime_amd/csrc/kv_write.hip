@@ -140,18 +140,43 @@ __device__ inline void widen8(const DemoteSrc &s, const uint4 w, float (&x)[8]) 
 }
 
 // max |x| of the 8 elements, +inf if any of them is NaN or infinite (a
-// plain fmaxf would drop a NaN)
+// plain fmaxf would drop a NaN).  Hot (16-bit) values are compared as their
+// bit patterns without the sign: in both formats the patterns of
+// non-negative values order like the values, and every infinity or NaN
+// pattern lies above every finite one, so one packed integer max per two
+// elements does the work.  Integer codes are finite; a block whose scale is
+// not finite is caught by the caller (scale_not_finite).
 template <int ST>
 __device__ inline float absmax8(const DemoteSrc &s, const uint4 w) {
-    float x[8];
-    widen8<ST>(s, w, x);
-    float m = 0.0f;
+    if constexpr (ST == 0) {
+        typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+        auto mag = [](uint32_t x) { return __builtin_bit_cast(u16x2_t, x & 0x7FFF7FFFu); };
+        const u16x2_t m2 = __builtin_elementwise_max(__builtin_elementwise_max(mag(w.x), mag(w.y)),
+                                                     __builtin_elementwise_max(mag(w.z), mag(w.w)));
+        const uint32_t mb = max((uint32_t)m2[0], (uint32_t)m2[1]);
+        if (s.bf16) return mb >= 0x7F80u ? __builtin_inff() : __uint_as_float(mb << 16);
+        return mb >= 0x7C00u ? __builtin_inff()
+                             : (float)__builtin_bit_cast(_Float16, (uint16_t)mb);
+    } else {
+        float x[8];
+        widen8<ST>(s, w, x);
+        float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float a = fabsf(x[j]);
-        m = fmaxf(m, a == a ? a : __builtin_inff());
+        for (int j = 0; j < 8; ++j) {
+            const float a = fabsf(x[j]);
+            // FP8 codes include NaN codes; integer codes times a finite
+            // scale give no NaN
+            m = fmaxf(m, ST == 3 && a != a ? __builtin_inff() : a);
+        }
+        return m;
     }
-    return m;
+}
+
+// a cold source block whose scale is NaN or infinite decodes to non-finite
+// values (0 * inf is NaN), so it demotes like a block holding them
+template <int ST>
+__device__ inline bool scale_not_finite(const DemoteSrc &s) {
+    return ST != 0 && !(fabsf(s.scale) < __builtin_inff());
 }
 
 // The FP8 E4M3 code nearest to y (ties to the even code), sign from y's sign
@@ -224,6 +249,7 @@ __device__ inline void encode_block(const DemoteSrc &src, const int64_t nch, int
         amax = fmaxf(amax, absmax8<ST>(src, load_chunk<ST>(src, ch)));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (scale_not_finite<ST>(src)) amax = __builtin_inff();
     // a block holding a non-finite value gets a NaN scale (and codes 0, since
     // no code is formed from a NaN scale), so every value read back from it
     // is NaN instead of a finite stand-in

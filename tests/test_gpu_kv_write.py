@@ -143,12 +143,13 @@ def test_demote_pages_bit_exact_and_attention(gpu, hot_dtype):
     check(w, out, lse)
 
 
-def test_demote_block_with_non_finite_value_gets_nan_scale(gpu):
+@pytest.mark.parametrize("hot_dtype", ["f16", "bf16"])
+def test_demote_block_with_non_finite_value_gets_nan_scale(gpu, hot_dtype):
     """A hot block holding a NaN (or an infinity) is demoted to a NaN scale
     with codes 0 -- every value read back is NaN -- while the other blocks of
     the same pages encode as usual; codes and scales match the oracle's
     encoder, NaN for NaN."""
-    w = _demote_case(gpu, "f16", seed=13)
+    w = _demote_case(gpu, hot_dtype, seed=13)
     Hkv, P = w.num_kv_heads, w.page_tokens
     s = 2
     ctx = int(w.context_lens[s])
@@ -194,6 +195,53 @@ def test_demote_block_with_non_finite_value_gets_nan_scale(gpu):
                 got = ta[f"{key}_{kv}"][slot, g]
                 assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (b, kv, g)
     assert nan_blocks == 2
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_demote_cold_source_with_non_finite_scale(gpu, bad):
+    """A cold source block whose scale is NaN or infinite reads back as
+    non-finite values, so moving it down the cascade (int8 -> int4) gives a
+    NaN scale and codes 0, like a hot block holding them; the block's other
+    (kv, kv head) blocks encode as usual.  Expected values: the oracle's
+    encoder on the oracle's reading of the source."""
+    w = _demote_case(gpu, "bf16", seed=14)
+    Hkv = w.num_kv_heads
+    s = 2
+    ent = w.page_table[s].view(np.uint32)
+    n_full = int(w.context_lens[s]) // w.page_tokens
+    src = [int(e) for e in ent[:n_full] if (int(e) >> 30) == 1][0]
+    w.tiers["i8_k_scale"][src & ((1 << 30) - 1), 1] = bad
+    n4 = w.tiers["i4_k"].shape[0]
+    for kv in ("k", "v"):
+        t = w.tiers[f"i4_{kv}"]
+        w.tiers[f"i4_{kv}"] = torch.cat([t, torch.zeros((1,) + t.shape[1:], dtype=t.dtype,
+                                                        device=gpu)])
+        sc = w.tiers[f"i4_{kv}_scale"]
+        w.tiers[f"i4_{kv}_scale"] = torch.cat([sc, torch.full((1, Hkv), -1.0, device=gpu)])
+    dst = (2 << 30) | n4
+    host = oracle.HostView(w)
+    want = {(kv, g): oracle.quantize_block(oracle.block_f32(w, src, g, kv, host=host), 7)
+            for kv in ("k", "v") for g in range(Hkv)}
+    prob = atlas.Problem(w)
+    rejected = torch.zeros(1, dtype=torch.int32, device=gpu)
+    atlas.atlas_demote_pages(
+        prob.args, prob.tiers,
+        torch.tensor(np.array([src], np.uint32).view(np.int32), device=gpu),
+        torch.tensor(np.array([dst], np.uint32).view(np.int32), device=gpu), rejected)
+    torch.cuda.synchronize()
+    assert int(rejected) == 0
+    ta = oracle.HostView(w).tier_arrays()
+    nan_blocks = 0
+    for (kv, g), (codes, scale) in want.items():
+        got_scale = np.float32(ta[f"i4_{kv}_scale"][n4, g])
+        if np.isnan(scale):
+            nan_blocks += 1
+            assert np.isnan(got_scale), (kv, g)
+        else:
+            assert got_scale.tobytes() == scale.tobytes(), (kv, g)
+        got = ta[f"i4_{kv}"][n4, g]
+        assert np.array_equal(got.view(np.uint8), oracle.pack_int4(codes).view(np.uint8)), (kv, g)
+    assert nan_blocks == 1
 
 
 def test_demote_rejects_bad_destinations_and_poisons_bad_sources(gpu):
