@@ -263,8 +263,8 @@ const char *atlas_last_error(void);
  * with num_blocks 0 can be sized).  Reads host fields only.  The workspace holds the split-K partials of decode (one f32
  * vector of head_dim plus one lse per (row, head, split)).  Matrix-core
  * chunked prefill takes the keys in windows of W tokens (W = split_tokens,
- * or 16384 when split_tokens is 0, cut to the longest context rounded up to
- * 64) and gathers each window -- regenerated keys from the regenerator,
+ * or 16384 when split_tokens is 0, at most 4194304, cut to the longest
+ * context rounded up to 64) and gathers each window -- regenerated keys from the regenerator,
  * resident keys through the page table -- into one ring that every window
  * reuses (CFR-Atlas README, overview: scratch buffers that are reused), so
  * its workspace is

@@ -210,6 +210,7 @@ atlas_status check_common(const atlas_attn_args *a, bool tiered, const atlas_reg
         // does not grow with the context and the result bits do not depend
         // on the page size or on which pages are regenerated.
         int w = a->split_tokens > 0 ? a->split_tokens : kPrefillWindow;
+        if (w > kPrefillMaxWindow) w = kPrefillMaxWindow;
         const int ctx64 = (a->max_context_len + 63) / 64 * 64;
         if (ctx64 > 0 && w > ctx64) w = ctx64;  // one window holds the whole context
         plan->window_tokens = w;

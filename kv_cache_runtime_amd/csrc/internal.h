@@ -238,6 +238,9 @@ constexpr int kPrefillRows = 256;
 // Keys per window of a matrix-core chunked prefill (the default when the
 // caller leaves split_tokens at 0).
 constexpr int kPrefillWindow = 16384;
+// largest window: the ring rows of one (sequence, kv head) stay within the
+// 32-bit byte range of the buffer loads that stage them
+constexpr int kPrefillMaxWindow = 1 << 22;
 hipError_t launch_prefill(const PrefillParams &p, int kv_type, int group, hipStream_t stream);
 hipError_t launch_regen_fill(const RegenFillParams &r, hipStream_t stream);
 // Per job i: the non-finite K and V values now stored in block dst_blocks[i]

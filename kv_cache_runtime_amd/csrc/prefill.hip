@@ -94,12 +94,23 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane l writes bytes 16 l .. 16 l + 15 after the
-// wave-uniform LDS address dst.  Counted by vmcnt like any load.
-__device__ __forceinline__ void lds_dma16(const void *src, uint16_t *dst) {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(src),
-                                     reinterpret_cast<uint4 *>(dst), 16, 0, 0);
+// 16 bytes per lane from memory straight into LDS (buffer_load_dwordx4 ...
+// lds): lane l reads the buffer at byte soffset + voffset and writes bytes
+// 16 l .. 16 l + 15 after the wave-uniform LDS address dst; reads past the
+// buffer's byte count return zeros.  Counted by vmcnt like any load.  The
+// buffer form (not the global one) matters: the compiler treats a pending
+// global-to-LDS load as an access of both memory kinds and then waits for
+// every outstanding LDS read at each use of one, while a pending buffer load
+// leaves its in-order LDS-read waits alone.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void *base, uint32_t bytes) {
+    // last word: 32-bit data format (the untyped loads used here ignore it)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
+                                          uint32_t soffset, uint16_t *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void *)(dst), 16, voffset,
+        soffset, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0): the tile DMAs issued before the last N
@@ -268,8 +279,13 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         return kbuf(b_c) + kTile * kD;
     };
     const int64_t ring0 = ((int64_t)seq * p.num_kv_heads + g) * p.ring_tokens * kD;
-    const char *const rk = reinterpret_cast<const char *>(p.ring_k) + 2 * ring0;
-    const char *const rv = reinterpret_cast<const char *>(p.ring_v) + 2 * ring0;
+    // this (sequence, kv head)'s ring rows as buffers (tile byte offsets go
+    // in the scalar offset)
+    const uint32_t ring_bytes = (uint32_t)p.ring_tokens * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rk =
+        ring_rsrc(reinterpret_cast<const char *>(p.ring_k) + 2 * ring0, ring_bytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        ring_rsrc(reinterpret_cast<const char *>(p.ring_v) + 2 * ring0, ring_bytes);
     // thread's DMA rows: 8 wave + 4 i + lane / 16 (i = 0, 1), position
     // lane % 16; the byte offsets within a tile are recomputed at each use
     // from a lane index the compiler cannot hoist (keeping them costs
@@ -292,16 +308,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         const int xv = max(min(x - 1, n_tiles - 1), 0);
         uint32_t kofs[2], vofs[2];
         dma_offsets(kofs, vofs);
-        const char *ks = rk + (int64_t)xk * kTileBytes;
-        const char *vs = rv + (int64_t)xv * kTileBytes;
-        // opaque scalar tile bases: each load is then a scalar base plus the
-        // lane's 32-bit offset, not a 64-bit lane address kept in VGPRs
-        asm("" : "+s"(ks));
-        asm("" : "+s"(vs));
+        const uint32_t ks = (uint32_t)xk * kTileBytes, vs = (uint32_t)xv * kTileBytes;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16(ks + kofs[i], kbuf(b_c) + (8 * wave + 4 * i) * kD);
+        for (int i = 0; i < 2; ++i) lds_dma16(rk, kofs[i], ks, kbuf(b_c) + (8 * wave + 4 * i) * kD);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16(vs + vofs[i], vbuf(b_c) + (8 * wave + 4 * i) * kD);
+        for (int i = 0; i < 2; ++i) lds_dma16(rv, vofs[i], vs, vbuf(b_c) + (8 * wave + 4 * i) * kD);
     };
 
     // The keys are folded in units of 32 (unit u = keys 32 u .. 32 u + 31 of
