@@ -417,6 +417,32 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
             const uint2 x1 = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp + 8 * kRowBytes));
             vf[st][b] = make_uint4(x0.x, x0.y, x1.x, x1.y);
         };
+        if constexpr (ALIBI) {
+            // The bias makes a row's scores climb toward its own position, so
+            // the overflow check below would fire (and redo a half) in most
+            // units.  Under ALiBi the reference instead follows the unit's
+            // row max, lazily (only past the slack), with a rescale that
+            // costs no exponential of the unit's weights.
+            float mraw = kNegInf;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mraw = fmaxf(mraw, sc[j]);
+            mraw += ab * (float)(kb0 + 32 * u + 4 * half - pos);
+            const auto hm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw),
+                                                             __float_as_uint(mraw), false, false);
+            mraw = fmaxf(__uint_as_float(hm[0]), __uint_as_float(hm[1]));
+            const float mt = mraw * p.scale_log2;
+            const bool move = mt > m_ref + kSlack;
+            if (__any(move)) {  // wave-uniform
+                const float m_new = move ? mt : m_ref;
+                const float a = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+                m_ref = m_new;
+                l *= a;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[b][j] *= a;
+            }
+        }
         // probabilities of unit u as f16 P^T operands, relative to m_ref - 7;
         // pair i is registers 2 i, 2 i + 1 (step i / 4 of the P.V).  l sums
         // the f16 weights the matrix cores use.
