@@ -321,6 +321,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     // (r, half) reads chunk 2 ks + half of row 32 (u % 2) + r, which sits at
     // byte (r * 256 + ((half ^ r % 16) << 4)) ^ (ks << 5) of its half tile.
     const uint32_t kaddr = r * kRowBytes + ((half ^ (r & 15)) << 4);
+    // the eight K read addresses of the key loop, kept (eight registers, one
+    // XOR per read less); the V ones are rebuilt at each use
+    uint32_t kaddrs[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kaddrs[ks] = kaddr ^ (ks << 5);
     auto scores = [&](int u, f32x16_t &dst, auto b_c) __attribute__((always_inline)) {
         const char *cK = reinterpret_cast<const char *>(kbuf(b_c)) + (u & 1) * (32 * kRowBytes);
         // the eight read addresses are rebuilt here from an opaque copy of
@@ -402,14 +407,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         const char *cK =
             reinterpret_cast<const char *>(kbuf(kb_c)) + ((u + 1) & 1) * (32 * kRowBytes);
         const char *cV = reinterpret_cast<const char *>(vbuf(vb_c)) + (u & 1) * (32 * kRowBytes);
-        // the read addresses are rebuilt here from opaque copies: hoisted out
-        // of the loop they would take a dozen registers
-        uint32_t ka = kaddr, va = vaddr;
-        asm volatile("" : "+v"(ka), "+v"(va));
+        // the V read addresses are rebuilt here from an opaque copy: hoisted
+        // out of the loop they would take four more registers than are left
+        uint32_t va = vaddr;
+        asm volatile("" : "+v"(va));
         uint4 kf[8];
         uint4 vf[2][4];
         auto kread = [&](int ks) __attribute__((always_inline)) {
-            kf[ks] = *reinterpret_cast<const uint4 *>(cK + (ka ^ (ks << 5)));
+            kf[ks] = *reinterpret_cast<const uint4 *>(cK + kaddrs[ks]);
         };
         auto vread = [&](int st, int b) __attribute__((always_inline)) {
             const char *vp = cV + (va ^ (b << 6)) + 16 * st * kRowBytes;
