@@ -3,6 +3,7 @@
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -46,27 +47,54 @@ def sanitize_env() -> dict:
     return env
 
 
-def build(verbose: bool = False, sanitize: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False, incremental: bool = False) -> str:
     """Compile every HIP source into kv_cache_runtime_amd/libatlas.so (or,
-    with sanitize, the host-sanitizer build libatlas_san.so)."""
+    with sanitize, the host-sanitizer build libatlas_san.so).
+
+    Each source is compiled to its own object in parallel (no relocatable
+    device code: every kernel and its launch live in one file), then the
+    objects are linked into the shared library.  With incremental, a source
+    whose object is newer than it and than every header is not recompiled."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     target = SAN_LIB if sanitize else LIB
     tmp = target + ".tmp"
-    cmd = [hipcc, *FLAGS, *(SAN_FLAGS if sanitize else []), "-I", INCLUDE, "-I", CSRC, *srcs,
-           "-o", tmp]
+    objdir = os.path.join(HERE, "_build", "san" if sanitize else "rel")
+    os.makedirs(objdir, exist_ok=True)
+    extra = SAN_FLAGS if sanitize else []
+
+    headers = [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d)
+               if f.endswith(".h")]
+    newest_header = max(os.path.getmtime(h) for h in headers)
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        if (incremental and os.path.exists(obj) and
+                os.path.getmtime(obj) > max(os.path.getmtime(src), newest_header)):
+            return obj, subprocess.CompletedProcess([], 0, "")
+        cmd = [hipcc, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        return obj, res
+
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as pool:
+        results = list(pool.map(compile_one, srcs))
+    for _, res in results:
+        out = "\n".join(l for l in res.stdout.splitlines()
+                        if "packed-fp32-ops" not in l)  # host-pass notice about the feature flag
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+        if verbose and out.strip():
+            print(out)
+    cmd = [hipcc, *FLAGS, *extra, *[o for o, _ in results], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in res.stdout.splitlines()
-                    if "packed-fp32-ops" not in l)  # host-pass notice about the feature flag
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
+        raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{res.stdout}")
     os.replace(tmp, target)
     return target
-
 
 if __name__ == "__main__":
     if "--sanitize" in sys.argv:
@@ -76,5 +104,5 @@ if __name__ == "__main__":
         res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-m", "not gpu", *tests],
                              env=sanitize_env(), cwd=ROOT)
         sys.exit(res.returncode)
-    build(verbose="-v" in sys.argv)
+    build(verbose="-v" in sys.argv, incremental="-i" in sys.argv)
     print(LIB)
