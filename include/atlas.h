@@ -269,7 +269,8 @@ const char *atlas_last_error(void);
  * reuses (CFR-Atlas README, overview: scratch buffers that are reused), so
  * its workspace is
  *     2 * num_seqs * num_kv_heads * W * head_dim * 2 bytes
- * (K in the kv dtype and V in f16; 64 MiB for one sequence, 8 kv heads,
+ * (K in the kv dtype and V in f16, V stored per 64-key tile dims-major;
+ * 64 MiB for one sequence, 8 kv heads,
  * head_dim 128 and W = 16384), at most that for any context length.  Each
  * regenerated value is still computed once per call.  Its contents need no
  * initialisation and are not meaningful between calls; two calls in flight

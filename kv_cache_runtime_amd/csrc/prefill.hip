@@ -18,7 +18,7 @@
 //   S^T[key][row]  = K[key][:] . Q[row][:]        (v_mfma_f32_32x32x16_{bf16,f16};
 //                                                  A = K from LDS, B = Q^T in VGPRs)
 //   O^T[d][row]   += V^T[d][key] . P^T[key][row]  (v_mfma_f32_32x32x16_f16;
-//                                                  A = V from LDS by the transposing
+//                                                  A = V^T from LDS, one 16-byte
 //                                                  read, B = P^T in VGPRs)
 // so each row lives in one lane pair (r, r + 32) for the softmax.
 //
@@ -35,7 +35,12 @@
 // weights shows; the half is then redone.
 //
 // Staging.  The keys of the call come from a ring the window preparation
-// kernel fills (K in the kv type, V in f16), 64 contiguous rows per tile.
+// kernel fills: K in the kv type, 64 contiguous key rows per tile, and V in
+// f16, each 64-key tile stored dims-major (V^T, 128 rows of 64 keys) with
+// the keys of every 16 ordered so that the eight a lane's P.V operand takes
+// are adjacent.  A single 16-byte LDS read then yields that operand, where
+// the key-major layout took two transposing 8-byte reads; the 16-byte reads
+// sustain a higher LDS rate.
 // They move from memory straight into LDS by DMA (global_load_lds), with no
 // registers in between.  LDS holds five buffers of one K tile and one V tile
 // each; a tile is issued four tiles ahead and the workgroup meets once per
@@ -55,7 +60,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;          // head_dim
@@ -63,6 +67,7 @@ constexpr int kTile = 64;        // keys per tile
 constexpr int kWaves = 8;        // waves per workgroup
 constexpr int kRowBytes = kD * 2;             // one staged K or V row
 constexpr int kTileBytes = kTile * kRowBytes;  // one staged K or V tile
+constexpr int kVtRowBytes = kTile * 2;         // one dim of a staged V^T tile
 
 template <int KV>
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
@@ -74,16 +79,6 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
     }
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
-// s gives the address of 4 consecutive 16-bit elements; with lane s pointing
-// at row k0 + s / 4, column n0 + 4 (s % 4) of a row-major tile, lane i
-// receives column n0 + i of rows k0 .. k0 + 3.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *ptr) {
-    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t *)(ptr));
-    return __builtin_bit_cast(uint2, v);
 }
 
 // Two packed bf16 values -> two packed f16 values (round to nearest even;
@@ -256,14 +251,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     float m_ref = kNegInf, l = 0.0f;
 
     // ---- staging.  Tiles come from the window's ring [seq][kv head][key -
-    // key_begin][D] (K in the kv type, V in f16, rows past the context zero),
-    // so a tile is 64 contiguous rows of 256 bytes.  They go straight from
+    // key_begin][D] (K in the kv type, rows past the context zero), so a K
+    // tile is 64 contiguous rows of 256 bytes; the V ring holds the same
+    // 16 KiB per tile as V^T, 128 dim rows of 64 f16 keys in the order
+    // described at the window preparation kernel.  Tiles go straight from
     // memory into LDS by DMA (global_load_lds_dwordx4: lane l of a wave's
     // load fills bytes 16 l .. 16 l + 15 of a 1 KiB stretch, from any address
     // it names), four loads per thread per tile pair.  Rows are not padded;
     // instead the 16-byte chunks of a row are permuted so that the matrix
     // operand reads hit distinct banks: chunk c of K row k sits at position
-    // c ^ (k % 16), chunk c of V row k at c ^ (4 (k % 4) + 2 ((k / 4) % 2)).
+    // c ^ (k % 16), chunk c of V^T row d at c ^ (d % 8).
     // Content x is K of tile x and V of tile x - 1; it lives in buffer x % 5
     // and is issued three tiles before it is read.
     // buffer B: K tile at element 0, V tile at element kTile * kD
@@ -286,10 +283,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         ring_rsrc(reinterpret_cast<const char *>(p.ring_k) + 2 * ring0, ring_bytes);
     const __amdgpu_buffer_rsrc_t rv =
         ring_rsrc(reinterpret_cast<const char *>(p.ring_v) + 2 * ring0, ring_bytes);
-    // thread's DMA rows: 8 wave + 4 i + lane / 16 (i = 0, 1), position
-    // lane % 16; the byte offsets within a tile are recomputed at each use
-    // from a lane index the compiler cannot hoist (keeping them costs
-    // registers the products need)
+    // thread's DMA rows: K row 8 wave + 4 i + lane / 16 (i = 0, 1), position
+    // lane % 16; V^T row (dim) 16 wave + 8 i + lane / 8, position lane % 8.
+    // The byte offsets within a tile are recomputed at each use from a lane
+    // index the compiler cannot hoist (keeping them costs registers the
+    // products need)
     auto dma_offsets = [&](uint32_t (&ko)[2], uint32_t (&vo)[2]) __attribute__((always_inline)) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
@@ -297,7 +295,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         for (int i = 0; i < 2; ++i) {
             const int row = 8 * wave + 4 * i + (ln >> 4), at = ln & 15;
             ko[i] = row * kRowBytes + ((at ^ (row & 15)) << 4);
-            vo[i] = row * kRowBytes + ((at ^ (4 * (row & 3) + 2 * ((row >> 2) & 1))) << 4);
+            const int dim = 16 * wave + 8 * i + (ln >> 3), vat = ln & 7;
+            vo[i] = dim * kVtRowBytes + ((vat ^ (dim & 7)) << 4);
         }
     };
     // Every content issues exactly four loads (past the tiles of the call
@@ -312,7 +311,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
         for (int i = 0; i < 2; ++i) lds_dma16(rk, kofs[i], ks, kbuf(b_c) + (8 * wave + 4 * i) * kD);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16(rv, vofs[i], vs, vbuf(b_c) + (8 * wave + 4 * i) * kD);
+        for (int i = 0; i < 2; ++i)
+            lds_dma16(rv, vofs[i], vs, vbuf(b_c) + (16 * wave + 8 * i) * kTile);
     };
 
     // The keys are folded in units of 32 (unit u = keys 32 u .. 32 u + 31 of
@@ -345,15 +345,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     };
     // ---- P.V of unit u (V of tile u / 2, content u / 2 + 1, buffer B).  A =
     // V^T: lane (dim 32 b + r, half) takes keys 16 st + 4 half .. + 3 and
-    // 16 st + 8 + 4 half .. + 3 (two transposing reads), the key order of
-    // P^T's registers.  The read of lane (q16, s16) starts at row kq, dims
-    // 32 b + nq .. + 3; with the chunk permutation that is byte vaddr ^ (b << 6)
-    // of the 8-row stretch.
-    const int q16 = lane >> 4, s16 = lane & 15;
-    const int kq = 4 * (q16 >> 1) + (s16 >> 2);     // row within the 8-row stretch
-    const int nq = 16 * (q16 & 1) + 4 * (s16 & 3);  // dim within the 32-dim block
-    const uint32_t vaddr =
-        kq * kRowBytes + (((nq >> 3) ^ (4 * (kq & 3) + 2 * (kq >> 2))) << 4) + (nq & 7) * 2;
+    // 16 st + 8 + 4 half .. + 3 of the unit, the key order of P^T's
+    // registers.  The V^T tile holds those eight keys in one 16-byte chunk:
+    // chunk 4 (u % 2) + 2 st + half of row 32 b + r, stored at chunk position
+    // c ^ (row % 8), i.e. byte vaddr ^ (st << 5) ^ ((u % 2) << 6) + 32 b * 128.
+    const uint32_t vaddr = r * kVtRowBytes + ((half ^ (r & 7)) << 4);
     uint4 pb[2];  // P^T operands of the unit being folded
     // ---- softmax, part 1 (unit u): ALiBi, the causal mask (mask: the unit
     // reaches past some row's position), the row max and the new reference;
@@ -406,10 +402,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         // which rescales at once; the first unit's reference finds o = 0)
         const char *cK =
             reinterpret_cast<const char *>(kbuf(kb_c)) + ((u + 1) & 1) * (32 * kRowBytes);
-        const char *cV = reinterpret_cast<const char *>(vbuf(vb_c)) + (u & 1) * (32 * kRowBytes);
+        const char *cV = reinterpret_cast<const char *>(vbuf(vb_c));
         // the V read addresses are rebuilt here from an opaque copy: hoisted
-        // out of the loop they would take four more registers than are left
-        uint32_t va = vaddr;
+        // out of the loop they would take more registers than are left
+        uint32_t va = vaddr ^ ((u & 1) << 6);
         asm volatile("" : "+v"(va));
         uint4 kf[8];
         uint4 vf[2][4];
@@ -417,10 +413,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
             kf[ks] = *reinterpret_cast<const uint4 *>(cK + kaddrs[ks]);
         };
         auto vread = [&](int st, int b) __attribute__((always_inline)) {
-            const char *vp = cV + (va ^ (b << 6)) + 16 * st * kRowBytes;
-            const uint2 x0 = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp));
-            const uint2 x1 = lds_read_tr16(reinterpret_cast<const uint16_t *>(vp + 8 * kRowBytes));
-            vf[st][b] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+            vf[st][b] = *reinterpret_cast<const uint4 *>(cV + (va ^ (st << 5)) + 32 * b * kVtRowBytes);
         };
         if constexpr (ALIBI) {
             // The bias makes a row's scores climb toward its own position, so
@@ -673,8 +666,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
 // window), keys past the context as zeros, and the keys of a page whose block
 // id lies outside the pool as NaN, so the rows that see them fail loudly.
 // One workgroup per (sequence, kv head, 64 keys); four lanes per key row, each
-// moving 32 dims (64 contiguous bytes of K and of V).
+// moving 32 dims (64 contiguous bytes of K).  V is written per 64-key tile as
+// V^T, 128 dim rows of 64 keys (128 bytes each), key k of the tile in slot
+// 16 (k / 16) + s(k % 16), where s swaps bits 2 and 3 (keys 0-3, 8-11, 4-7,
+// 12-15 of every 16): the order in which a lane of the prefill kernel holds
+// its eight keys of a P.V step.  The tile is transposed through LDS and
+// stored in 16-byte chunks.
 __global__ __launch_bounds__(256) void window_prepare_kernel(const WindowParams r) {
+    __shared__ uint16_t vt[kD * kTile];  // [dim][slot]
     constexpr int D = kD;
     const int groups = r.window_tokens / 64;
     const int gi = blockIdx.x % groups;
@@ -743,12 +742,23 @@ __global__ __launch_bounds__(256) void window_prepare_kernel(const WindowParams 
         }
     }
     uint4 *kd = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(r.ring_k) + at);
-    uint4 *vd = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(r.ring_v) + at);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 4; ++c)
         kd[c] = make_uint4(kw[4 * c], kw[4 * c + 1], kw[4 * c + 2], kw[4 * c + 3]);
-        vd[c] = make_uint4(vw[4 * c], vw[4 * c + 1], vw[4 * c + 2], vw[4 * c + 3]);
+    // V^T: this lane's 32 dims of key `row` into its slot of each dim row
+    const int slot = (row & ~15) | (row & 3) | ((row & 4) << 1) | ((row & 8) >> 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        vt[(d0 + 2 * i) * kTile + slot] = (uint16_t)(vw[i] & 0xFFFFu);
+        vt[(d0 + 2 * i + 1) * kTile + slot] = (uint16_t)(vw[i] >> 16);
     }
+    __syncthreads();
+    // the tile's 1,024 chunks of 16 bytes, four per lane, row-major
+    const int64_t tile0 = (((int64_t)seq * r.num_kv_heads + g) * r.window_tokens + 64 * gi) * D;
+    uint4 *vd = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(r.ring_v) + tile0);
+    const uint4 *vs = reinterpret_cast<const uint4 *>(vt);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vd[threadIdx.x + 256 * c] = vs[threadIdx.x + 256 * c];
 }
 
 template <int KV, bool A, bool R>

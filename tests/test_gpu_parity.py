@@ -410,11 +410,13 @@ def test_regenerate_config5_all_pages_bit_exact(gpu):
 def test_prefill_window_ring_holds_regenerated_values(gpu):
     """The values the matrix-core prefill folds: with one window covering the
     whole 131,072-token context of the 2,048-query workload, the workspace
-    ring holds every key of the window after the call -- [kv head][key][dim],
-    K as stored (bf16) and V converted to f16.  Its regenerated rows (the
-    oldest 98,304 keys) must equal the oracle's stream bit for bit (V through
-    a round-to-nearest f16 conversion of the oracle's value).  The ring
-    layout is internal to the library; this test reads it on purpose."""
+    ring holds every key of the window after the call -- K as stored (bf16)
+    [kv head][key][dim], V converted to f16 and stored per 64-key tile
+    dims-major, [kv head][tile][dim][slot], key 16 (s / 16) + t(s % 16) in
+    slot s, t swapping bits 2 and 3.  Its regenerated rows (the oldest 98,304
+    keys) must equal the oracle's stream bit for bit (V through a
+    round-to-nearest f16 conversion of the oracle's value).  The ring layout
+    is internal to the library; this test reads it on purpose."""
     w = synth.config(5, device=gpu)
     ctx = int(w.context_lens[0])
     prob = atlas.Problem(w, split_tokens=ctx)
@@ -426,7 +428,10 @@ def test_prefill_window_ring_holds_regenerated_values(gpu):
     ring = prob.args.workspace_bytes // 2
     ws = prob.workspace
     rk = ws[:Hkv * ctx * D * 2].view(torch.int16).view(Hkv, ctx, D)
-    rv = ws[ring:ring + Hkv * ctx * D * 2].view(torch.float16).view(Hkv, ctx, D)
+    rvt = ws[ring:ring + Hkv * ctx * D * 2].view(torch.float16).view(Hkv, ctx // 64, D, 64)
+    slot = np.arange(64)
+    slot = (slot & ~12) | ((slot & 4) << 1) | ((slot & 8) >> 1)  # key k sits in slot slot[k]
+    rv = rvt.permute(0, 1, 3, 2)[:, :, torch.from_numpy(slot).to(gpu), :].reshape(Hkv, ctx, D)
     for g in range(Hkv):
         ref_k = oracle.regen_values(42, 0, g, 0, n_regen, D, 0)
         ref_v = oracle.regen_values(42, 0, g, 0, n_regen, D, 1)
