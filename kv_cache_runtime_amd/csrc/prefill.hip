@@ -260,7 +260,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     // it names), four loads per thread per tile pair.  Rows are not padded;
     // instead the 16-byte chunks of a row are permuted so that the matrix
     // operand reads hit distinct banks: chunk c of K row k sits at position
-    // c ^ (k % 16), chunk c of V^T row d at c ^ (d % 8).
+    // c ^ (k % 16), chunk c of V^T row d at c ^ ((d / 2) % 8).
     // Content x is K of tile x and V of tile x - 1; it lives in buffer x % 5
     // and is issued three tiles before it is read.
     // buffer B: K tile at element 0, V tile at element kTile * kD
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
             const int row = 8 * wave + 4 * i + (ln >> 4), at = ln & 15;
             ko[i] = row * kRowBytes + ((at ^ (row & 15)) << 4);
             const int dim = 16 * wave + 8 * i + (ln >> 3), vat = ln & 7;
-            vo[i] = dim * kVtRowBytes + ((vat ^ (dim & 7)) << 4);
+            vo[i] = dim * kVtRowBytes + ((vat ^ ((dim >> 1) & 7)) << 4);
         }
     };
     // Every content issues exactly four loads (past the tiles of the call
@@ -348,8 +348,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
     // 16 st + 8 + 4 half .. + 3 of the unit, the key order of P^T's
     // registers.  The V^T tile holds those eight keys in one 16-byte chunk:
     // chunk 4 (u % 2) + 2 st + half of row 32 b + r, stored at chunk position
-    // c ^ (row % 8), i.e. byte vaddr ^ (st << 5) ^ ((u % 2) << 6) + 32 b * 128.
-    const uint32_t vaddr = r * kVtRowBytes + ((half ^ (r & 7)) << 4);
+    // c ^ ((row / 2) % 8), i.e. byte vaddr ^ (st << 5) ^ ((u % 2) << 6) + 32 b * 128.
+    // The LDS has 64 banks and serves a 16-byte read 16 lanes at a time: rows
+    // r = 0 .. 15 of 128 bytes then land on bank groups 8 (r % 2) + position,
+    // all distinct.
+    const uint32_t vaddr = r * kVtRowBytes + ((half ^ ((r >> 1) & 7)) << 4);
     uint4 pb[2];  // P^T operands of the unit being folded
     // ---- softmax, part 1 (unit u): ALiBi, the causal mask (mask: the unit
     // reaches past some row's position), the row max and the new reference;
