@@ -72,6 +72,46 @@ def algorithmic_work(w):
                 regen_elems=regen_elems)
 
 
+PROBE_MIXES = {  # mix: (products, exponentials, multiply-adds, LDS bytes) per wave-iteration
+    0: (0, 16, 0, 0), 1: (0, 0, 16, 0), 2: (16, 0, 0, 0), 3: (16, 16, 16, 0),
+    4: (0, 0, 0, 16384), 5: (16, 0, 0, 16384), 6: (16, 0, 0, 16384), 7: (32, 0, 0, 16384)}
+
+
+def issue_probe(torch, dev, iters: int = 2048) -> None:
+    """Times each mix of atlas_issue_probe at one and two waves per SIMD and
+    prints one JSON line per (mix, waves): the shader clock of the run, the
+    SIMD cycles one wave-iteration takes, the fraction of them the matrix core
+    is busy (32 cycles per 32x32x16 product) and the LDS bytes a CU reads per
+    cycle."""
+    from kv_cache_runtime_amd import atlas
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    sink = torch.zeros(1024, dtype=torch.float32, device=dev)
+    blocks, cus, simds = 1024, 256, 1024
+    for wps in (1, 2):
+        for mix, (nm, ne, nf, lds) in PROBE_MIXES.items():
+            atlas.atlas_issue_probe(mix, wps, iters, clocks, sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            atlas.atlas_issue_probe(mix, wps, iters, clocks, sink)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            ticks, real = (int(v) for v in clocks.cpu())
+            ghz = ticks / real * 0.1 if real else 0.0
+            cycles = ms * 1e-3 * ghz * 1e9
+            wave_iters_per_simd = blocks * 4 * wps / simds * iters
+            row = {"metric": "issue probe", "mix": mix, "waves_per_simd": wps,
+                   "per_wave_iteration": {"mfma_32x32x16": nm, "exp": ne, "fma": nf,
+                                          "lds_bytes": lds},
+                   "ms": round(ms, 4), "clock_GHz": round(ghz, 3),
+                   "simd_cycles_per_wave_iteration": round(cycles / wave_iters_per_simd, 2),
+                   "mfma_busy": round(wave_iters_per_simd * nm * 32 / cycles, 3) if nm else None,
+                   "lds_bytes_per_cu_cycle":
+                       round(blocks * 4 * wps * iters * lds / cus / cycles, 1) if lds else None}
+            print(json.dumps(row), flush=True)
+
+
 def stream_read_gbps(torch, dev, nbytes: int = 2 << 30, reps: int = 10) -> float:
     """Read bandwidth of the library's plain streaming-read probe over nbytes
     (context for the fraction of the 8 TB/s peak)."""
@@ -502,13 +542,16 @@ def main():
                     help="diagnostic: map every page-table entry's slot to slot mod N in "
                          "its own pool, so the call reads N blocks per pool from cache "
                          "instead of HBM (the kernel's floor without memory traffic)")
-    ap.add_argument("--op", choices=("attention", "write_kv", "demote", "archive", "promote"),
+    ap.add_argument("--op", choices=("attention", "write_kv", "demote", "archive", "promote",
+                                     "probe"),
                     default="attention",
                     help="attention (default): the attention call of --config; write_kv: "
                          "writing a chunk's new K/V into its pages; demote: encoding every "
                          "full hot page of --config into the int8 / int4 tiers; archive: "
                          "encoding them into the 1-bit archive; promote: rebuilding the "
-                         "archived pages into hot blocks")
+                         "archived pages into hot blocks; probe: the issue rates of "
+                         "matrix products, exponentials, multiply-adds and LDS reads the "
+                         "matrix-core prefill is built from (one JSON line per mix)")
     ap.add_argument("--outliers", type=int, default=16,
                     help="FP16 outliers per (page, kv head) block for archive / promote")
     args = ap.parse_args()
@@ -526,6 +569,9 @@ def main():
 
     dev = torch.device("cuda:0")
     atlas.load()
+    if args.op == "probe":
+        issue_probe(torch, dev)
+        return
     if args.op != "attention":
         write_path(args, torch, dev)
         return

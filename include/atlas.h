@@ -511,6 +511,29 @@ atlas_status atlas_promote_pages(const atlas_attn_args *args,
 atlas_status atlas_read_probe(const void *src, size_t bytes, uint32_t *out,
                               int32_t blocks, void *stream);
 
+/*
+ * Measurement helper (not part of the attention method): the issue rates the
+ * matrix-core prefill is built from.  Launches 1024 workgroups, one per CU at
+ * a time (each holds 96 KiB of LDS), of 256 * waves_per_simd threads
+ * (waves_per_simd 1 or 2); every wave repeats `iters` (1 .. 2^20) times one
+ * fixed mix of 32x32x16 bf16 matrix products on four independent
+ * accumulators, f32 exponentials and fused multiply-adds, and LDS reads:
+ *   mix 0: 16 exponentials          mix 4: 8 16-byte + 16 8-byte transposing reads
+ *   mix 1: 16 multiply-adds         mix 5: 16 products + the reads of mix 4
+ *   mix 2: 16 products              mix 6: 16 products + 16 16-byte reads
+ *   mix 3: 16 products, 16 exponentials and 16 multiply-adds
+ *   mix 7: 32 products + 16 16-byte reads
+ * (mixes 5 and 6 read 1 KiB of LDS per product, mix 7 0.5 KiB).  Writes the
+ * shader-clock ticks and the 100 MHz constant-clock ticks of workgroup 0's
+ * loop to clocks[0..1] (device, caller-owned); sink (device, 1024 floats,
+ * caller-owned) keeps the work from being dropped and is normally left
+ * unwritten.  Timing the launch gives the cycles each mix takes per SIMD.
+ * EINVAL for NULL pointers or arguments outside the ranges above.
+ * Asynchronous on `stream`.
+ */
+atlas_status atlas_issue_probe(int32_t mix, int32_t waves_per_simd, int32_t iters,
+                               uint64_t *clocks, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -117,7 +117,7 @@ EXPORTS = [
     "atlas_paged_attention", "atlas_paged_attention_noalloc", "atlas_paged_attention_tiered",
     "atlas_paged_attention_regen",
     "atlas_fold_partials", "atlas_gather_pages", "atlas_regenerate_pages",
-    "atlas_dequant_pages", "atlas_validate_tables", "atlas_read_probe",
+    "atlas_dequant_pages", "atlas_validate_tables", "atlas_read_probe", "atlas_issue_probe",
     "atlas_write_kv", "atlas_demote_pages", "atlas_promote_pages",
     "atlas_residency_create", "atlas_residency_destroy", "atlas_residency_add_seq",
     "atlas_residency_remove_seq", "atlas_residency_append", "atlas_residency_plan",
@@ -207,6 +207,8 @@ def load(path: str = LIB_PATH):
                                       _i32, _p, _p]
     L.atlas_read_probe.restype = _i32
     L.atlas_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, _p]
+    L.atlas_issue_probe.restype = _i32
+    L.atlas_issue_probe.argtypes = [_i32, _i32, _i32, _p, _p, _p]
     L.atlas_residency_create.restype = _i32
     L.atlas_residency_create.argtypes = [ctypes.POINTER(ResidencyConfig), ctypes.POINTER(_p)]
     L.atlas_residency_destroy.restype = _i32
@@ -462,6 +464,13 @@ def atlas_read_probe(src, out, blocks: int, stream=None):
     """Streaming read of the whole tensor `src` (measurement helper)."""
     _check(load().atlas_read_probe(_ptr(src), int(src.numel() * src.element_size()), _ptr(out),
                                    int(blocks), _stream(stream)), "atlas_read_probe")
+
+
+def atlas_issue_probe(mix: int, waves_per_simd: int, iters: int, clocks, sink, stream=None):
+    """One launch of the issue-rate probe (measurement helper); clocks: 2
+    int64 on the device, sink: 1024 float32 on the device."""
+    _check(load().atlas_issue_probe(int(mix), int(waves_per_simd), int(iters), _ptr(clocks),
+                                    _ptr(sink), _stream(stream)), "atlas_issue_probe")
 
 
 # ---------------------------------------------------------------------------

@@ -771,6 +771,18 @@ atlas_status atlas_read_probe(const void *src, size_t bytes, uint32_t *out, int3
                          "read probe launch");
 }
 
+atlas_status atlas_issue_probe(int32_t mix, int32_t waves_per_simd, int32_t iters,
+                               uint64_t *clocks, float *sink, void *stream) {
+    if (!clocks || !sink) return fail(ATLAS_EINVAL, "NULL pointer argument");
+    if (mix < 0 || mix > 7) return fail(ATLAS_EINVAL, "mix %d outside [0, 7]", mix);
+    if (waves_per_simd != 1 && waves_per_simd != 2)
+        return fail(ATLAS_EINVAL, "waves_per_simd %d is not 1 or 2", waves_per_simd);
+    if (iters < 1 || iters > (1 << 20)) return fail(ATLAS_EINVAL, "iters %d outside [1, 2^20]", iters);
+    return device_status(launch_issue_probe(mix, waves_per_simd, iters, clocks, sink,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                         "issue probe launch");
+}
+
 atlas_status atlas_write_kv(const atlas_attn_args *args, const void *k_new, const void *v_new) {
     Plan plan;
     atlas_status st = check_common(args, false, nullptr, &plan);

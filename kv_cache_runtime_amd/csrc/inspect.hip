@@ -325,6 +325,87 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4 *src, int64
     }
 }
 
+
+// ---- issue-rate probe (measurement helper) ---------------------------------
+// Each wave repeats a fixed mix of matrix products (v_mfma_f32_32x32x16_bf16
+// on four independent accumulators), exponentials, fused multiply-adds and
+// LDS reads (16-byte reads, and 8-byte transposing reads) for `iters`
+// iterations; workgroup 0 records the shader clock and the 100 MHz constant
+// clock around its loop.  96 KiB of LDS per workgroup keep one workgroup per
+// CU, so a workgroup of 64 W x 4 threads puts W waves on each SIMD.  Every
+// LDS address stays inside the first 64 KiB.  One word per workgroup is
+// stored only when its value equals `magic` (never, for the magic the host
+// passes), so no work can be dropped.
+template <int NMFMA, int NEXP, int NFMA, int NB128, int NTR>
+__global__ __launch_bounds__(512) void issue_probe_kernel(int iters, uint32_t magic,
+                                                          uint64_t *clocks, float *sink) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    typedef float f32x16_t __attribute__((ext_vector_type(16)));
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint16_t buf[49152];
+    for (int i = threadIdx.x; i < 32768; i += blockDim.x) buf[i] = (uint16_t)(i * 7);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    f32x16_t acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[b][j] = 0.0f;
+    bf16x8_t a, bb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (threadIdx.x & 7));
+        bb[i] = (__bf16)(0.002f * i);
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = 0.001f * (threadIdx.x + i);
+    uint32_t h = 0;
+    const uint32_t wave_off = (threadIdx.x >> 6) * 4096u;
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        uint32_t base = (wave_off + (uint32_t)it * 2048u) & 0xFFF0u;
+        asm volatile("" : "+v"(base));
+        uint4 rd[NB128 > 0 ? NB128 : 1];
+        uint2 tr[NTR > 0 ? NTR : 1];
+#pragma unroll
+        for (int k = 0; k < NB128; ++k)
+            rd[k] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(buf) +
+                                                     ((base + lane * 16 + k * 1024) & 0xFFF0u));
+#pragma unroll
+        for (int k = 0; k < NTR; ++k) {
+            const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t *)(reinterpret_cast<char *>(buf) +
+                                                               ((base + lane * 8 + k * 512) & 0xFFF8u)));
+            tr[k] = __builtin_bit_cast(uint2, v);
+        }
+        // the products and the vector work interleaved, one product in turn
+#pragma unroll
+        for (int k = 0; k < (NMFMA > 16 ? NMFMA : 16); ++k) {
+            if (k < NMFMA) acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[k & 3], 0, 0, 0);
+            if (k < NEXP) x[k & 7] = __builtin_amdgcn_exp2f(-x[k & 7]);
+            if (k < NFMA) x[(k + 4) & 7] = fmaf(x[(k + 4) & 7], 0.5f, 0.25f);
+        }
+#pragma unroll
+        for (int k = 0; k < NB128; ++k) h ^= rd[k].x ^ rd[k].y ^ rd[k].z ^ rd[k].w;
+#pragma unroll
+        for (int k = 0; k < NTR; ++k) h ^= tr[k].x ^ tr[k].y;
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    float sum = (float)h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += x[i];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum += acc[b][j];
+    if (__float_as_uint(sum) == magic) sink[blockIdx.x] = sum;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        clocks[0] = t1 - t0;
+        clocks[1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gather(const void *k_pool, const void *v_pool, const int32_t *table_row,
@@ -392,6 +473,24 @@ hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int 
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const uint4 *>(src), bytes / 16, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_issue_probe(int mix, int waves_per_simd, int iters, uint64_t *clocks,
+                              float *sink, hipStream_t stream) {
+    const dim3 grid(kIssueProbeBlocks), block(256 * waves_per_simd);
+    const uint32_t magic = 0xFFFFFFFFu;
+    switch (mix) {
+        case 0: hipLaunchKernelGGL((issue_probe_kernel<0, 16, 0, 0, 0>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        case 1: hipLaunchKernelGGL((issue_probe_kernel<0, 0, 16, 0, 0>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        case 2: hipLaunchKernelGGL((issue_probe_kernel<16, 0, 0, 0, 0>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        case 3: hipLaunchKernelGGL((issue_probe_kernel<16, 16, 16, 0, 0>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        case 4: hipLaunchKernelGGL((issue_probe_kernel<0, 0, 0, 8, 16>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        case 5: hipLaunchKernelGGL((issue_probe_kernel<16, 0, 0, 8, 16>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        case 6: hipLaunchKernelGGL((issue_probe_kernel<16, 0, 0, 16, 0>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        case 7: hipLaunchKernelGGL((issue_probe_kernel<32, 0, 0, 16, 0>), grid, block, 0, stream, iters, magic, clocks, sink); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

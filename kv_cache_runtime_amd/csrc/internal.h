@@ -263,6 +263,10 @@ hipError_t launch_demote(const DemoteParams &d, hipStream_t stream);
 hipError_t launch_promote(const PromoteParams &q, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int blocks,
                              hipStream_t stream);
+// workgroups of the issue probe: four rounds of one workgroup per CU
+constexpr int kIssueProbeBlocks = 1024;
+hipError_t launch_issue_probe(int mix, int waves_per_simd, int iters, uint64_t *clocks,
+                              float *sink, hipStream_t stream);
 hipError_t launch_dequant(const DecodeParams &p, int kv_type, int head_dim,
                           const int32_t *entries, int32_t n, float *k_out, float *v_out,
                           hipStream_t stream);

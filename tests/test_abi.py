@@ -219,6 +219,17 @@ def test_read_probe_arguments_are_checked():
     assert L.atlas_read_probe(FAKE, 32, FAKE, 0, None) == atlas.EINVAL
 
 
+def test_issue_probe_arguments_are_checked():
+    L = atlas.load()
+    assert L.atlas_issue_probe(0, 1, 16, None, FAKE, None) == atlas.EINVAL
+    assert L.atlas_issue_probe(0, 1, 16, FAKE, None, None) == atlas.EINVAL
+    assert L.atlas_issue_probe(8, 1, 16, FAKE, FAKE, None) == atlas.EINVAL
+    assert L.atlas_issue_probe(-1, 1, 16, FAKE, FAKE, None) == atlas.EINVAL
+    assert L.atlas_issue_probe(0, 3, 16, FAKE, FAKE, None) == atlas.EINVAL
+    assert L.atlas_issue_probe(0, 2, 0, FAKE, FAKE, None) == atlas.EINVAL
+    assert L.atlas_issue_probe(0, 2, (1 << 20) + 1, FAKE, FAKE, None) == atlas.EINVAL
+
+
 def test_write_and_demote_arguments_are_checked():
     L = atlas.load()
     a = _args()
