@@ -643,9 +643,15 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None}
-    roof["traffic"] = measured_traffic(w.name)
+    # the committed counter summaries describe the default call of each
+    # workload: a positional policy, another cold mix, aliased slots, another
+    # window or an environment-selected kernel runs other code or other bytes
+    variant = bool(positional or "tiers" in extra or args.alias_slots > 0 or args.split_tokens
+                   or any(k in os.environ for k in ("ATLAS_DECODE_VALU", "ATLAS_NO_MFMA",
+                                                    "ATLAS_SPLIT_TOKENS")))
+    roof["traffic"] = None if variant else measured_traffic(w.name)
     # issue-side view of the same kernel (rocprofv3 SQ counters, committed summary)
-    roof["valu_busy"] = measured_valu_busy(w.name)
+    roof["valu_busy"] = None if variant else measured_valu_busy(w.name)
     roof["kernel_avg_ms"] = round(kern_avg, 5)
     roof["kernel_median_ms"] = round(kern_ms[K // 2], 5)
     roof["kernel_min_ms"] = round(kern_ms[0], 5)
