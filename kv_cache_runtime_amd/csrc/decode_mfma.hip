@@ -176,19 +176,23 @@ __device__ __forceinline__ bool load_k_group(const DecodeParams &p, int64_t base
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int d0 = MODE == MODE_TIERED ? 32 * r + 8 * ks : 32 * ks + 8 * r;
-            kr[ks] = *reinterpret_cast<const uint4 *>(src + (c * kD + d0));
+            // the tiered layout spreads a lane's 64-byte run over four loads,
+            // each touching a quarter of every 64-byte stretch of the row: those
+            // stay ordinary loads, so the later ones find the lines cached
+            kr[ks] = MODE == MODE_TIERED ? *reinterpret_cast<const uint4 *>(src + (c * kD + d0))
+                                         : ld_stream16(src + (c * kD + d0));
         }
     } else if constexpr (TIER == kByte) {
         const uint8_t *pool = alt ? p.f8_k : reinterpret_cast<const uint8_t *>(p.i8_k);
+        // two loads per 32-byte run, each touching half of it: ordinary loads
         const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD + (c * kD + 32 * r));
         kr[0] = src[0];
         kr[1] = src[1];
     } else if (alt) {  // INT2: dims 32 r .. 32 r + 31 are 8 bytes
-        const uint2 v = *reinterpret_cast<const uint2 *>(p.i2_k + r0 * (kD / 4) +
-                                                          (c * (kD / 4) + 8 * r));
+        const uint2 v = ld_stream8(p.i2_k + r0 * (kD / 4) + (c * (kD / 4) + 8 * r));
         kr[0] = make_uint4(v.x, v.y, 0u, 0u);
     } else {
-        kr[0] = *reinterpret_cast<const uint4 *>(p.i4_k + r0 * (kD / 2) + (c * (kD / 2) + 16 * r));
+        kr[0] = ld_stream16(p.i4_k + r0 * (kD / 2) + (c * (kD / 2) + 16 * r));
     }
     return true;
 }
@@ -251,18 +255,18 @@ __device__ __forceinline__ bool load_v_group(const DecodeParams &p, int64_t base
         const uint4 *src = reinterpret_cast<const uint4 *>(
             reinterpret_cast<const uint16_t *>(p.v_pool) + r0 * kD);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = src[64 * i + lane];
+        for (int i = 0; i < 4; ++i) vr[i] = ld_stream16(src + 64 * i + lane);
     } else if constexpr (TIER == kByte) {
         const uint8_t *pool = alt ? p.f8_v : reinterpret_cast<const uint8_t *>(p.i8_v);
         const uint4 *src = reinterpret_cast<const uint4 *>(pool + r0 * kD);
-        vr[0] = src[lane];
-        vr[1] = src[64 + lane];
+        vr[0] = ld_stream16(src + lane);
+        vr[1] = ld_stream16(src + 64 + lane);
     } else if (alt) {  // INT2: 8 bytes per lane
-        const uint2 v = reinterpret_cast<const uint2 *>(p.i2_v + r0 * (kD / 4))[lane];
+        const uint2 v = ld_stream8(reinterpret_cast<const uint2 *>(p.i2_v + r0 * (kD / 4)) + lane);
         vr[0] = make_uint4(v.x, v.y, 0u, 0u);
     } else {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.i4_v + r0 * (kD / 2));
-        vr[0] = src[lane];
+        vr[0] = ld_stream16(src + lane);
     }
     return true;
 }

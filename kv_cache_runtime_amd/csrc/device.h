@@ -82,28 +82,45 @@ __device__ __forceinline__ int32_t sext_field(uint32_t w, int sh, int bits) {
 }
 
 // ---------------------------------------------------------------------------
-// Vector loads of NB bytes (NB in {1, 2, 4, 8, 16, 32}) into 32-bit words.
+// Streaming loads of K/V pages.  Every page byte an attention call reads is
+// read once (the query heads of a kv head share the registers), so the loads
+// carry the non-temporal hint (global_load_* ... nt).  On MI355X a plain
+// streaming read of 2 GiB measured 5.85 TB/s with ordinary 16-byte loads and
+// 6.66 TB/s with non-temporal ones.
 // ---------------------------------------------------------------------------
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void *src) {
+    const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(src));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void *src) {
+    const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2 *>(src));
+    return make_uint2(v.x, v.y);
+}
+
+// Vector loads of NB bytes (NB in {1, 2, 4, 8, 16, 32}) of a K/V page into
+// 32-bit words, non-temporal.
 template <int NB>
 __device__ __forceinline__ void load_words(uint32_t *dst, const void *src) {
     if constexpr (NB == 32) {
-        const uint4 *s = reinterpret_cast<const uint4 *>(src);
-        uint4 a = s[0], b = s[1];
+        const char *s = reinterpret_cast<const char *>(src);
+        const uint4 a = ld_stream16(s), b = ld_stream16(s + 16);
         dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
         dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
     } else if constexpr (NB == 16) {
-        uint4 a = *reinterpret_cast<const uint4 *>(src);
+        const uint4 a = ld_stream16(src);
         dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
     } else if constexpr (NB == 8) {
-        uint2 a = *reinterpret_cast<const uint2 *>(src);
+        const uint2 a = ld_stream8(src);
         dst[0] = a.x; dst[1] = a.y;
     } else if constexpr (NB == 4) {
-        dst[0] = *reinterpret_cast<const uint32_t *>(src);
+        dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src));
     } else if constexpr (NB == 2) {
-        dst[0] = *reinterpret_cast<const uint16_t *>(src);
+        dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(src));
     } else {
         static_assert(NB == 1, "unsupported load width");
-        dst[0] = *reinterpret_cast<const uint8_t *>(src);
+        dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint8_t *>(src));
     }
 }
 

@@ -300,15 +300,17 @@ __global__ __launch_bounds__(256) void validate_kernel(const ValidateParams v) {
 
 
 // ---- streaming read probe (measurement helper) ------------------------------
-// Every thread reads 16-byte words with a grid stride and folds them into one
-// xor; one word per workgroup is written so the loads cannot be dropped.
+// Every thread reads 16-byte words with a grid stride (non-temporal loads, as
+// the attention kernels read their pages) and folds them into one xor; one
+// word per workgroup is written so the loads cannot be dropped.
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4 *src, int64_t n16,
                                                          uint32_t *out) {
     uint32_t x = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        const uint4 a = ld_stream16(src + i), b = ld_stream16(src + i + stride),
+                    c = ld_stream16(src + i + 2 * stride), d = ld_stream16(src + i + 3 * stride);
         x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
     }
     for (; i < n16; i += stride) {
