@@ -92,14 +92,23 @@ struct DemoteSrc {
     float scale;         // cold tiers
 };
 
-template <int ST>  // source class: 0 hot, 1 int8, 2 int4, 3 FP8, 4 INT2
+// ONCE: the chunk is read only this time (non-temporal load); chunks a kernel
+// reads again stay ordinary loads, so the second read finds them cached.
+template <int ST, bool ONCE = false>  // source class: 0 hot, 1 int8, 2 int4, 3 FP8, 4 INT2
 __device__ inline uint4 load_chunk(const DemoteSrc &s, int64_t ch) {
-    if constexpr (ST == 0) return reinterpret_cast<const uint4 *>(s.base)[ch];
-    if constexpr (ST == 2)
-        return make_uint4(reinterpret_cast<const uint32_t *>(s.base)[ch], 0u, 0u, 0u);
-    if constexpr (ST == 4)
-        return make_uint4(reinterpret_cast<const uint16_t *>(s.base)[ch], 0u, 0u, 0u);
-    const uint2 v = reinterpret_cast<const uint2 *>(s.base)[ch];
+    if constexpr (ST == 0)
+        return ONCE ? ld_stream16(reinterpret_cast<const uint4 *>(s.base) + ch)
+                    : reinterpret_cast<const uint4 *>(s.base)[ch];
+    if constexpr (ST == 2) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(s.base) + ch;
+        return make_uint4(ONCE ? __builtin_nontemporal_load(p) : *p, 0u, 0u, 0u);
+    }
+    if constexpr (ST == 4) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(s.base) + ch;
+        return make_uint4(ONCE ? __builtin_nontemporal_load(p) : *p, 0u, 0u, 0u);
+    }
+    const uint2 v = ONCE ? ld_stream8(reinterpret_cast<const uint2 *>(s.base) + ch)
+                         : reinterpret_cast<const uint2 *>(s.base)[ch];
     return make_uint4(v.x, v.y, 0u, 0u);
 }
 
@@ -241,7 +250,7 @@ __device__ inline void encode_block(const DemoteSrc &src, const int64_t nch, int
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t ch = lane + 64 * j;
-        keep[j] = ch < nch ? load_chunk<ST>(src, ch) : make_uint4(0, 0, 0, 0);
+        keep[j] = ch < nch ? load_chunk<ST, true>(src, ch) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < R; ++j) amax = fmaxf(amax, absmax8<ST>(src, keep[j]));
@@ -592,14 +601,16 @@ __device__ inline void store_hot8(void *dst, int64_t ch, int kv_type, const floa
         }
         w[j] = (uint32_t)a | ((uint32_t)b << 16);
     }
-    reinterpret_cast<uint4 *>(dst)[ch] = make_uint4(w[0], w[1], w[2], w[3]);
+    // streaming store: a promoted block is written once, whole
+    const nt_u32x4 v = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x4 *>(dst) + ch);
 }
 
 template <int ST>
 __device__ void promote_codes(const DemoteSrc &src, int64_t nch, void *dst, int kv_type, int lane) {
     for (int64_t ch = lane; ch < nch; ch += 64) {
         float x[8];
-        widen8<ST>(src, load_chunk<ST>(src, ch), x);
+        widen8<ST>(src, load_chunk<ST, true>(src, ch), x);
         store_hot8(dst, ch, kv_type, x);
     }
 }
@@ -645,7 +656,11 @@ __global__ __launch_bounds__(256) void promote_kernel(const PromoteParams q) {
         const uint4 *s4 = reinterpret_cast<const uint4 *>(
             reinterpret_cast<const uint8_t *>(kv ? p.v_pool : p.k_pool) + sblk * n * eb);
         uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-        for (int64_t c = lane; c < n * eb / 16; c += 64) d4[c] = s4[c];
+        for (int64_t c = lane; c < n * eb / 16; c += 64) {
+            const uint4 x = ld_stream16(s4 + c);
+            const nt_u32x4 v = {x.x, x.y, x.z, x.w};
+            __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x4 *>(d4) + c);
+        }
         return;
     }
     if (cls == CLS_B1) {
