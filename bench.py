@@ -116,7 +116,7 @@ def stream_read_gbps(torch, dev, nbytes: int = 2 << 30, reps: int = 10) -> float
     """Read bandwidth of the library's plain streaming-read probe over nbytes
     (context for the fraction of the 8 TB/s peak)."""
     from kv_cache_runtime_amd import atlas
-    blocks = 65536  # best of 1024 .. 65536 workgroups on MI355X (5.4-5.7 TB/s)
+    blocks = 65536  # the best of 1024 .. 65536 workgroups on MI355X
     x = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
     out = torch.empty(blocks, dtype=torch.int32, device=dev)
     for _ in range(2):
