@@ -385,17 +385,47 @@ __device__ inline int below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Threshold search over one key per lane (0 < k <= 64), bit by bit from the
+// top; bits that no lane's key has set are skipped, as they cannot move t.
+// Returns t with at least k lanes holding v >= t.  When a prefix t >= floor
+// selects exactly k lanes the search stops there and `exact` is set: then
+// exactly k lanes hold v >= t.  Otherwise t is the k-th largest v.  (Counts
+// below `floor` may be incomplete, so no exit is taken there.)
+__device__ inline uint32_t kth_largest_lane(uint32_t v, int k, uint32_t floor, bool &exact) {
+    uint32_t o = v;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) o |= (uint32_t)__shfl_xor((int)o, sh);
+    const uint32_t any = __builtin_amdgcn_readfirstlane(o);
+    uint32_t t = 0;
+    exact = false;
+    for (int b = 30; b >= 0 && !exact; --b) {
+        if (((any >> b) & 1u) == 0u) continue;  // uniform
+        const uint32_t cand = t | (1u << b);
+        const int c = (int)__popcll(__ballot(v >= cand));
+        if (c >= k) t = cand;
+        exact = c == k && cand >= floor;
+    }
+    return t;
+}
+
 // Encodes one block into the 1-bit format (one wave).  The outlier
-// threshold T is the k-th largest magnitude key, found bit by bit from the
-// top; each pass counts the keys >= a candidate with one ballot per element
-// (no cross-lane data movement), and the search stops early once a prefix
-// selects exactly k keys.  Elements above T are outliers, and of those equal
+// threshold T is the k-th largest magnitude key.  When the block's keys are
+// held in registers, a lower bound t0 comes first: a threshold that at least
+// k of the 64 lane maxima reach (then at least k keys do).  If at most 64
+// keys reach t0, they are compacted into this wave's 64 words of LDS
+// (`cand`), one per lane, and T is searched bit by bit over those alone.
+// Otherwise T is found bit by bit from the top over the whole block; each
+// pass counts the keys >= a candidate with one ballot per element (no
+// cross-lane data movement).  Both searches stop early once a prefix selects
+// exactly k keys, and both give the same outliers: the k largest keys, ties
+// taken in index order.  Elements above T are outliers, and of those equal
 // to T the lowest-indexed ones fill the remaining places (ranks in index
 // order from lane-prefix bit counts).  The keys of the first R rounds of
 // chunks stay in registers; later rounds are read again per pass.
 template <int R, int ST>
 __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *signs,
-                              float *scale_out, uint32_t *outs, const int kout, const int lane) {
+                              float *scale_out, uint32_t *outs, const int kout, const int lane,
+                              uint32_t *cand) {
     const int64_t n = nch * 8;
     const int k = (int)min((int64_t)kout, n);
     const int rounds = (int)((nch + 63) / 64);
@@ -432,7 +462,46 @@ __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *
 
     uint32_t T = 0;  // count(key >= T) >= k throughout
     int need = 0;
-    if (k > 0) {
+    bool selected = false;
+    if (k > 0 && rounds <= R) {
+        uint32_t lmax = 0;
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lmax = max(lmax, key[j][e]);
+        bool ex;
+        // at least k lane maxima reach t0, so at least k keys do
+        const uint32_t t0 = kth_largest_lane(lmax, k, 0u, ex);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c += key[j][e] >= t0 ? 1 : 0;
+        int incl = c;  // inclusive prefix sum of c over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d);
+            if (lane >= d) incl += t;
+        }
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        // t0 >= 1 keeps the zero keys past the block out of the candidates
+        if (t0 >= 1u && total <= 64) {
+            int at = incl - c;
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (key[j][e] >= t0) cand[at++] = key[j][e];
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t mine = lane < total ? cand[lane] : 0u;
+            // only keys >= t0 were gathered: counts below t0 are short
+            T = kth_largest_lane(mine, k, t0, ex);
+            if (ex) --T;  // then key > T selects exactly the k outliers
+            need = k - (int)__popcll(__ballot(mine > T));
+            selected = true;
+        }
+    }
+    if (k > 0 && !selected) {
         // A bit that no key has set never moves T: no key lies in [T + 2^b,
         // T + 2^(b+1)), so its count equals that of the higher candidate,
         // which fell short of k.  Its pass is skipped (16-bit sources leave
@@ -516,6 +585,7 @@ __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *
 // 1-bit entry; every other page is demote_kernel's.
 template <int R>
 __global__ __launch_bounds__(256) void archive_kernel(const DemoteParams d) {
+    __shared__ uint32_t s_cand[4][64];  // each wave's outlier candidates
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= (int64_t)d.n * d.num_kv_heads * 2) return;
@@ -569,11 +639,11 @@ __global__ __launch_bounds__(256) void archive_kernel(const DemoteParams d) {
     uint8_t *signs = (kv ? d.b1_v : d.b1_k) + dblk * (n / 8);
     uint32_t *outs = (kv ? d.b1_vo : d.b1_ko) + dblk * d.b1_nout;
     switch (stier) {
-        case CLS_HOT: archive_block<R, CLS_HOT>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
-        case CLS_I8: archive_block<R, CLS_I8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
-        case CLS_I4: archive_block<R, CLS_I4>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
-        case CLS_F8: archive_block<R, CLS_F8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
-        default: archive_block<R, CLS_I2>(src, n / 8, signs, sdst, outs, d.b1_nout, lane); break;
+        case CLS_HOT: archive_block<R, CLS_HOT>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
+        case CLS_I8: archive_block<R, CLS_I8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
+        case CLS_I4: archive_block<R, CLS_I4>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
+        case CLS_F8: archive_block<R, CLS_F8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
+        default: archive_block<R, CLS_I2>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
     }
 }
 
