@@ -512,9 +512,23 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
                 if (i + kAhead < 8) kread(i + kAhead);
             }
         };
+        // The two waves of a SIMD contend for its issue slots.  A wave takes
+        // a higher priority while it issues its matrix products and drops it
+        // for its exponentials, so that a product ready to go is not held
+        // behind the other wave's vector work (about 1 % on the 2,048 x
+        // 131,072 prefill).
+        auto prio = [&](auto v_c) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_setprio(decltype(v_c)::value);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        using Hi = std::integral_constant<int, 1>;
+        using Lo = std::integral_constant<int, 0>;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            prio(Hi{});
             score(i);
+            __builtin_amdgcn_sched_barrier(0);
+            prio(Lo{});
             pexp(i);
             vread(0, i);
             __builtin_amdgcn_sched_barrier(0);
@@ -523,8 +537,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
         pb[0] = make_uint4(w[0], w[1], w[2], w[3]);
 #pragma unroll
         for (int i = 4; i < 8; ++i) {
+            prio(Hi{});
             score(i);
             o[i - 4] = mfma32<KV_F16>(vf[0][i - 4], pb[0], o[i - 4]);
+            __builtin_amdgcn_sched_barrier(0);
+            prio(Lo{});
             pexp(i);
             vread(1, i - 4);
             __builtin_amdgcn_sched_barrier(0);
@@ -535,11 +552,13 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(const PrefillParams p) 
             alibi_bias(sn);
             if (masked(u + 1)) causal_mask(u + 1, sn);
         }
+        prio(Hi{});
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             o[b] = mfma32<KV_F16>(vf[1][b], pb[1], o[b]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        prio(Lo{});
     };
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
