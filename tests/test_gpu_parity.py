@@ -531,6 +531,22 @@ def test_mfma_prefill_shapes(gpu, kv, H, Hkv):
     check(w, out, lse)
 
 
+@pytest.mark.parametrize("kv,split", [("bf16", 64), ("bf16", 192), ("f16", 128), ("bf16", 1024)])
+def test_mfma_prefill_small_windows(gpu, kv, split):
+    """The keys folded window by window through the ring (split_tokens keys
+    per window, each window after the first merged into out / lse), with
+    ragged contexts and chunks: a window shorter than the query chunk, windows
+    that end inside a chunk's causal diagonal, and (bf16, the regenerator's
+    type) a regenerated prefix."""
+    spec = dict(num_seqs=3, context_lens=[1000, 333, 1777], query_lens=[200, 333, 77],
+                num_heads=16, num_kv_heads=2, head_dim=128, page_tokens=16, kv_dtype=kv)
+    if kv == "bf16":
+        spec["regen"] = dict(seed=11, layer=1, fraction=0.5)
+    w = synth.build(spec, device=gpu, seed=split + 3, name=f"mfma-window{split}-{kv}")
+    out, lse = run(w, split_tokens=split)
+    check(w, out, lse)
+
+
 @pytest.mark.parametrize("P", [16, 64, 256])
 def test_mfma_prefill_regen_page_sizes(gpu, P):
     w = synth.build(dict(num_seqs=2, context_lens=[2000, 900], query_lens=[257, 64],
