@@ -99,6 +99,96 @@ def test_archive_matches_oracle(gpu, hot, P, D, n_out):
                 assert _scale_close(scales[i, g], wscale), (i, kv, g, scales[i, g], wscale)
 
 
+def _edge_blocks(n_elem, rng):
+    """Hot blocks that steer the encoder's threshold search into each of its
+    paths: spikes well above the rest, ties at the threshold among a few
+    dozen keys, more than 64 keys tied, an all-zero block, and signed zeros."""
+    base = lambda: (0.1 * rng.standard_normal(n_elem)).astype(np.float32)
+    out = []
+    x = base(); x[rng.choice(n_elem, 16, replace=False)] = 40.0 + np.arange(16); out.append(x)
+    x = base(); idx = rng.choice(n_elem, 30, replace=False)
+    x[idx[:10]] = 9.0; x[idx[10:]] = -5.0; out.append(x)
+    x = base(); x[rng.choice(n_elem, 100, replace=False)] = 5.0; out.append(x)
+    out.append(np.zeros(n_elem, np.float32))
+    x = base(); x[::7] = -0.0; x[rng.choice(n_elem, 70, replace=False)] = -3.0
+    x[rng.choice(n_elem, 8, replace=False)] = 6.0; out.append(x)
+    return out
+
+
+def _encoder_path(x, k):
+    """Which threshold search the encoder takes for a 2,048-element block of
+    f32 values x (lane l holds chunks l + 64 j, j < 4, of 8 elements): its
+    lower bound t0 is found over the 64 lane maxima, bit by bit from the top
+    and stopping at the first prefix that exactly k maxima reach; the
+    candidate search follows when t0 >= 1 and at most 64 keys reach t0, else
+    the full-block search.  (Coverage bookkeeping for this test only.)"""
+    keys = (x.astype(np.float32).view(np.uint32) & 0x7FFFFFFF).reshape(4, 64, 8)
+    lane_max = keys.max(axis=(0, 2))
+    any_bits = int(np.bitwise_or.reduce(lane_max))
+    t0 = 0
+    for b in range(30, -1, -1):
+        if not (any_bits >> b) & 1:
+            continue
+        cand = t0 | (1 << b)
+        c = int((lane_max >= cand).sum())
+        if c >= k:
+            t0 = cand
+        if c == k:
+            break
+    return "candidates" if t0 >= 1 and int((keys >= t0).sum()) <= 64 else "full"
+
+
+@pytest.mark.parametrize("hot,n_out", [("f16", 16), ("bf16", 16), ("bf16", 64), ("f16", 1)])
+def test_archive_threshold_edge_cases(gpu, hot, n_out):
+    """Constructed 2,048-element hot blocks, encoded into 1-bit slots, against
+    the oracle's encoder: the outliers are the n_out largest magnitudes, ties
+    taken in index order, whichever search the encoder takes."""
+    w = _case(gpu, hot=hot, Hkv=2, P=16, D=128, ctx=(1300, 700), seed=5 + n_out)
+    P, D, Hkv = w.page_tokens, w.head_dim, w.num_kv_heads
+    hot_pages = [e for _, _, e in _full_pages_by_class(w, per_class=3)
+                 if oracle.entry_class(e)[0] == 0]
+    assert len(hot_pages) == 3
+    rng = np.random.default_rng(17 + n_out)
+    cases = _edge_blocks(P * D, rng)
+    dt = torch.float16 if hot == "f16" else torch.bfloat16
+    k = 0
+    for e in hot_pages:
+        slot = oracle.entry_class(e)[1]
+        for pool in (w.k_pool, w.v_pool):
+            for g in range(Hkv):
+                x = torch.from_numpy(cases[k % len(cases)].reshape(P, D)).to(dt)
+                pool[slot, g] = x.to(gpu)
+                k += 1
+    n = len(hot_pages)
+    _add_b1_pool(w, n, n_out, gpu)
+    src_np = np.array(hot_pages, dtype=np.uint32)
+    dst_np = np.array([B1 | i for i in range(n)], dtype=np.uint32)
+    host = oracle.HostView(w)
+    paths = {_encoder_path(oracle.block_f32(w, int(e), g, kv, host=host).ravel(), n_out)
+             for e in src_np for kv in ("k", "v") for g in range(Hkv)}
+    if n_out == 16:
+        assert paths == {"candidates", "full"}, paths
+    prob = atlas.Problem(w)
+    rej = torch.zeros(1, dtype=torch.int32, device=gpu)
+    print(f"[archive edge cases {hot} K{n_out}] {n} pages, paths {sorted(paths)}", flush=True)
+    atlas.atlas_demote_pages(prob.args, prob.tiers,
+                             torch.from_numpy(src_np.view(np.int32)).to(gpu),
+                             torch.from_numpy(dst_np.view(np.int32)).to(gpu), rej)
+    torch.cuda.synchronize()
+    assert int(rej) == 0
+    for kv in ("k", "v"):
+        signs = w.tiers[f"b1_{kv}"].cpu().numpy()
+        scales = w.tiers[f"b1_{kv}_scale"].cpu().numpy()
+        outs = w.tiers[f"b1_{kv}_out"].cpu().numpy().view(np.uint32)
+        for i, e in enumerate(src_np):
+            for g in range(Hkv):
+                ws, wscale, wout = oracle.encode_1bit(
+                    oracle.block_f32(w, int(e), g, kv, host=host).ravel(), n_out)
+                assert np.array_equal(signs[i, g], ws), (i, kv, g)
+                assert np.array_equal(outs[i, g], wout), (i, kv, g)
+                assert _scale_close(scales[i, g], wscale), (i, kv, g, scales[i, g], wscale)
+
+
 def _oracle_b1_pool(w, n, n_out, gpu, seed):
     """A 1-bit pool written on the host by the oracle's encoder from seeded
     blocks (normal values with a few large outliers and some exact ties)."""
