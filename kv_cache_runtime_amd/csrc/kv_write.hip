@@ -421,11 +421,13 @@ __device__ inline uint32_t kth_largest_lane(uint32_t v, int k, uint32_t floor, b
 // taken in index order.  Elements above T are outliers, and of those equal
 // to T the lowest-indexed ones fill the remaining places (ranks in index
 // order from lane-prefix bit counts).  The keys of the first R rounds of
-// chunks stay in registers; later rounds are read again per pass.
+// chunks stay in registers and their raw chunks in this wave's LDS (`stage`,
+// R * 64 chunks, each lane reading back only what it wrote); later rounds are
+// read again from memory per pass.
 template <int R, int ST>
 __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *signs,
                               float *scale_out, uint32_t *outs, const int kout, const int lane,
-                              uint32_t *cand) {
+                              uint32_t *cand, uint4 *stage) {
     const int64_t n = nch * 8;
     const int k = (int)min((int64_t)kout, n);
     const int rounds = (int)((nch + 63) / 64);
@@ -435,7 +437,9 @@ __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *
         const int64_t ch = lane + 64 * j;
         float x[8];
         if (ch < nch) {
-            widen8<ST>(src, load_chunk<ST>(src, ch), x);
+            const uint4 w = load_chunk<ST>(src, ch);
+            stage[64 * j + lane] = w;
+            widen8<ST>(src, w, x);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.0f;
@@ -529,7 +533,8 @@ __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *
         need = k - (T == 0x7FFFFFFFu ? 0 : count_at_least(T + 1));
     }
 
-    // final pass, the chunks read again (the threshold passes keep only keys)
+    // final pass over the chunks again: the first R rounds from LDS, later
+    // ones from memory (the threshold passes keep only keys)
     int eq_base = 0, out_base = 0;
     double sum = 0.0;
     for (int r = 0; r < rounds; ++r) {
@@ -537,21 +542,30 @@ __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *
         const bool valid = ch < nch;
         float x[8];
         if (valid) {
-            widen8<ST>(src, load_chunk<ST>(src, ch), x);
+            widen8<ST>(src, r < R ? stage[64 * r + lane] : load_chunk<ST>(src, ch), x);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.0f;
         }
-        bool tie[8];
-        int rank = eq_base, eq_tot = 0;
+        // ties at T matter only while places are left for them (need > 0), and
+        // their ranks only in rounds that hold one
+        bool tie[8], any_tie = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            tie[e] = k > 0 && valid && mag_key(x[e]) == T;
-            const uint64_t m = __ballot(tie[e]);
-            rank += below(m);
-            eq_tot += __popcll(m);
+            tie[e] = need > 0 && valid && mag_key(x[e]) == T;
+            any_tie |= tie[e];
         }
-        eq_base += eq_tot;
+        int rank = eq_base;
+        if (__ballot(any_tie) != 0) {  // uniform
+            int eq_tot = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint64_t m = __ballot(tie[e]);
+                rank += below(m);
+                eq_tot += __popcll(m);
+            }
+            eq_base += eq_tot;
+        }
         bool is_out[8];
         int pos = out_base, out_tot = 0;
 #pragma unroll
@@ -586,6 +600,7 @@ __device__ void archive_block(const DemoteSrc &src, const int64_t nch, uint8_t *
 template <int R>
 __global__ __launch_bounds__(256) void archive_kernel(const DemoteParams d) {
     __shared__ uint32_t s_cand[4][64];  // each wave's outlier candidates
+    __shared__ uint4 s_stage[4][R * 64];  // each wave's register-round chunks
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= (int64_t)d.n * d.num_kv_heads * 2) return;
@@ -639,11 +654,11 @@ __global__ __launch_bounds__(256) void archive_kernel(const DemoteParams d) {
     uint8_t *signs = (kv ? d.b1_v : d.b1_k) + dblk * (n / 8);
     uint32_t *outs = (kv ? d.b1_vo : d.b1_ko) + dblk * d.b1_nout;
     switch (stier) {
-        case CLS_HOT: archive_block<R, CLS_HOT>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
-        case CLS_I8: archive_block<R, CLS_I8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
-        case CLS_I4: archive_block<R, CLS_I4>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
-        case CLS_F8: archive_block<R, CLS_F8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
-        default: archive_block<R, CLS_I2>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6]); break;
+        case CLS_HOT: archive_block<R, CLS_HOT>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6], s_stage[threadIdx.x >> 6]); break;
+        case CLS_I8: archive_block<R, CLS_I8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6], s_stage[threadIdx.x >> 6]); break;
+        case CLS_I4: archive_block<R, CLS_I4>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6], s_stage[threadIdx.x >> 6]); break;
+        case CLS_F8: archive_block<R, CLS_F8>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6], s_stage[threadIdx.x >> 6]); break;
+        default: archive_block<R, CLS_I2>(src, n / 8, signs, sdst, outs, d.b1_nout, lane, s_cand[threadIdx.x >> 6], s_stage[threadIdx.x >> 6]); break;
     }
 }
 
