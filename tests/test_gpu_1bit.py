@@ -62,7 +62,7 @@ def _scale_close(got, want):
 
 @pytest.mark.parametrize("hot,P,D,n_out", [("f16", 16, 128, 8), ("bf16", 16, 128, 64),
                                            ("f16", 64, 128, 64), ("bf16", 16, 64, 0),
-                                           ("f16", 256, 64, 16)])
+                                           ("f16", 256, 64, 16), ("bf16", 48, 64, 16)])
 def test_archive_matches_oracle(gpu, hot, P, D, n_out):
     w = _case(gpu, hot=hot, P=P, D=D, ctx=(1300, 2700), seed=P + D + n_out)
     pages = _full_pages_by_class(w)
